@@ -1,0 +1,136 @@
+/*
+ * dust.h -- C ABI of the MI355X (gfx950) Dust gradient-estimator library.
+ *
+ * Dust (Q Labs, 2026) estimates the gradient of a Transformer linear layer
+ * y_t = W x_t without backprop: every token's layer output gets K independent
+ * Gaussian perturbations sigma * a_t^(i); the loss downstream of the layer is
+ * recomputed per draw; the reward r_t^(i) is the clean per-token cross-entropy
+ * minus the perturbed one; the output-error estimate is
+ *     g_hat_t = -(1/(K sigma)) sum_i r_t^(i) a_t^(i)
+ * and the weight-gradient estimate is G_W = sum_t g_hat_t x_t^T.
+ *   - TL;DR page "Dust: zeroth-order Transformer pretraining without backprop"
+ *     (agentlenshq.com), section 1, "activation-space perturbation" and
+ *     "credit assignment without backprop" (the equations for g_hat_t, G_W).
+ *   - same page, section 1, "reducing interference": the LM head is jittered
+ *     on cached logits; the rest of the network stays cached.
+ *   - news article on tahou.com, mechanism paragraph: cache the unperturbed
+ *     intermediates; head perturbed on cached logits, only the loss recomputed.
+ *
+ * Conventions for every entry point
+ *   - Tensors are caller-owned DEVICE memory, row-major, contiguous, aligned to
+ *     at least 16 bytes.  The library keeps no pointer after a call returns.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     on it and the call returns at once; outputs are valid once the stream
+ *     has completed the work.
+ *   - All argument checks run on the host before anything is enqueued.  A
+ *     failed check returns DUST_E_INVALID / DUST_E_UNSUPPORTED /
+ *     DUST_E_WORKSPACE with a message (dust_last_error) and has no side
+ *     effect.  A failed launch returns DUST_E_DEVICE.
+ *   - The library allocates no device memory: scratch space comes from the
+ *     caller's `workspace`, sized by the matching *_workspace_bytes query.
+ *   - Labels are trusted: an out-of-range label never causes an out-of-bounds
+ *     access, but the result is then meaningless.  With DUST_DEBUG_CHECKS=1 in
+ *     the environment the labels are copied back and checked (synchronising).
+ *   - Results are bitwise deterministic run to run (no floating-point atomics).
+ *
+ * Noise stream (the pages say only "independent Gaussian noise per token";
+ * this library fixes one stream so that results are reproducible):
+ *   Philox4x32-10 (Salmon et al., SC'11), key = (lo32(seed), hi32(seed)),
+ *   counter = (token_offset + t, c >> 2, draw_offset + i, layer), followed by
+ *   Box-Muller on each pair of output words:
+ *     u1 = ((w[2p] >> 8) + 1) 2^-24, u2 = (w[2p+1] >> 8) 2^-24,
+ *     a[4q+2p] = sqrt(-2 ln u1) cos(2 pi u2), a[4q+2p+1] = sqrt(-2 ln u1) sin(2 pi u2).
+ *   The noise is regenerated in registers wherever it is needed, never stored.
+ *   Because the counters are global, a run split over draws or tokens (the
+ *   offsets) reproduces a single run:  K G_W[0,K) = K1 G_W[0,K1) + (K-K1) G_W[K1,K).
+ */
+#ifndef DUST_H
+#define DUST_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DUST_ABI_VERSION 1
+
+typedef enum {
+    DUST_OK = 0,
+    DUST_E_INVALID = 1,      /* bad pointer, size, sigma, offset range ...          */
+    DUST_E_UNSUPPORTED = 2,  /* valid but not implemented (e.g. a vocabulary too large) */
+    DUST_E_WORKSPACE = 3,    /* workspace missing or smaller than the query says   */
+    DUST_E_DEVICE = 4        /* a HIP call failed                                   */
+} dust_status;
+
+typedef enum { DUST_F32 = 0, DUST_BF16 = 1 } dust_dtype;
+
+/* ABI version of the loaded library (DUST_ABI_VERSION at build time). */
+int dust_abi_version(void);
+
+/* Message of the last failed call on this thread ("" if none).  Valid until
+ * the next call into the library on the same thread. */
+const char *dust_last_error(void);
+
+/*
+ * Profiling hook: while set, `event` (a hipEvent_t) is recorded on the call's
+ * stream right after the given stage of every estimator call made from this
+ * thread.  stage 0 = after the per-token estimator kernel (g_hat ready),
+ * stage 1 = after the weight-gradient outer product.  Pass NULL to clear.
+ * The caller owns the events.  Used to time the stages of one call.
+ */
+dust_status dust_set_stage_event(int stage, void *event);
+
+/*
+ * Noise export: the exact Gaussian values (and optionally the raw Philox words)
+ * that the estimators use, for draws [draw_offset, draw_offset+K) x tokens
+ * [token_offset, token_offset+T) x channels [0, n).
+ *   raw   : uint32 [K, T, 4*ceil(n/4)] or NULL -- the Philox output words of
+ *           quad q of (draw, token) at [.., .., 4q .. 4q+3].
+ *   gauss : float  [K, T, n] or NULL.
+ * Requires draw_offset + K <= 2^32 and token_offset + T <= 2^32.
+ */
+dust_status dust_noise(uint64_t seed, uint32_t layer, uint32_t draw_offset, int64_t K,
+                       uint32_t token_offset, int64_t T, int64_t n,
+                       uint32_t *raw, float *gauss, void *stream);
+
+/*
+ * Weight-gradient outer product  grad_w = ghat^T x  =  sum_t ghat_t x_t^T
+ * (TL;DR page, section 1, equation for G_W).
+ *   ghat   : float [T, n];  x : float [T, d];  grad_w : float [n, d] (overwritten).
+ * Workspace: dust_outer_workspace_bytes(T, n, d) bytes (split-K partial sums).
+ */
+size_t dust_outer_workspace_bytes(int64_t T, int64_t n, int64_t d);
+dust_status dust_outer_product(const float *ghat, const float *x, int64_t T, int64_t n, int64_t d,
+                               float *grad_w, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * LM-head estimator on cached logits (full vocabulary per draw).
+ *   logits       : [T, V] cached clean logits z_t = W x_t, fp32 or bf16 bits
+ *                  (logits_dtype = DUST_F32 / DUST_BF16).
+ *   x            : float [T, d] cached input of the head (the x_t of G_W).
+ *   labels       : int32 [T] next-token ids in [0, V).
+ *   K >= 1 draws, sigma > 0 finite.
+ *   seed, layer  : noise stream; token_offset/draw_offset: global ids of token 0 / draw 0.
+ *   grad_w       : OUT float [V, d]  G_W = sum_t g_hat_t x_t^T (overwritten).
+ *   ghat         : OUT float [T, V]  g_hat_t, or NULL.
+ *   rewards      : OUT float [K, T]  r_t^(i) = CE_clean - CE_perturbed (nats), or NULL.
+ * Per draw the perturbed loss is evaluated as log1p(sum_v p_v expm1(sigma a_v)) -
+ * sigma a_y with p = softmax(z_t): equal to CE(z + sigma a) - CE(z) in exact
+ * arithmetic, without the cancellation of subtracting two losses of order ln V.
+ * Supported: V <= 65536.
+ */
+size_t dust_head_workspace_bytes(int64_t T, int64_t V, int64_t d, int64_t K);
+dust_status dust_estimate_head(const void *logits, int logits_dtype, const float *x,
+                               const int32_t *labels, int64_t T, int64_t V, int64_t d,
+                               int64_t K, float sigma, uint64_t seed, uint32_t layer,
+                               uint32_t token_offset, uint32_t draw_offset,
+                               float *grad_w, float *ghat, float *rewards,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DUST_H */

@@ -84,8 +84,14 @@ def _lib():
                                         ctypes.c_int64, ctypes.c_double, ctypes.c_uint64,
                                         ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
                                         _f64p, ctypes.c_void_p, ctypes.c_void_p]
+        L.orc_num_threads.restype = ctypes.c_int
         _lib_handle = L
     return _lib_handle
+
+
+def num_threads() -> int:
+    """Host threads the oracle's OpenMP loops use."""
+    return int(_lib().orc_num_threads())
 
 
 # --------------------------------------------------------------------------

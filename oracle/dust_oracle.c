@@ -38,11 +38,24 @@
 #include <stddef.h>
 #include <math.h>
 #include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define PHILOX_M0 0xD2511F53u
 #define PHILOX_M1 0xCD9E8D57u
 #define PHILOX_W0 0x9E3779B9u
 #define PHILOX_W1 0xBB67AE85u
+
+/* Threads the OpenMP loops below use. */
+int orc_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* One Philox4x32 round: two 32x32->64 products, the high halves xored with
  * the other two counter words and the round key (SC'11, section 3.3). */

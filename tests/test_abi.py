@@ -1,0 +1,95 @@
+"""The C-ABI library loads on a host without a GPU, exports every entry point the
+header declares, and rejects bad arguments on the host before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import zeroth_order_activation_amd as dust
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # an aligned address; every call below must fail before using it
+FAKE_MIS = 0x10004
+
+
+def _declared():
+    names = set()
+    for f in os.listdir(os.path.join(ROOT, "include")):
+        if f.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", f)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(dust_\w+)\s*\(", src))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    L = dust.lib()
+    names = _declared()
+    assert {"dust_estimate_head", "dust_noise", "dust_outer_product", "dust_last_error"} <= names
+    for n in sorted(names):
+        assert hasattr(L, n), n
+    assert L.dust_abi_version() == 1
+
+
+def _head(**kw):
+    a = dict(logits=FAKE, dt=0, x=FAKE, labels=FAKE, T=4, V=8, d=2, K=3, sigma=0.01, seed=1, layer=0,
+             tok=0, draw=0, gw=FAKE, ghat=FAKE, rew=None, ws=None, wsb=0)
+    a.update(kw)
+    L = dust.lib()
+    st = L.dust_estimate_head(a["logits"], a["dt"], a["x"], a["labels"], a["T"], a["V"], a["d"], a["K"],
+                              ctypes.c_float(a["sigma"]), a["seed"], a["layer"], a["tok"], a["draw"], a["gw"],
+                              a["ghat"], a["rew"], a["ws"], a["wsb"], None)
+    return st, L.dust_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(logits=None), 1, "non-NULL"),
+    (dict(gw=None), 1, "non-NULL"),
+    (dict(dt=7), 2, "logits_dtype"),
+    (dict(x=FAKE_MIS), 1, "aligned"),
+    (dict(T=0), 1, "T must be"),
+    (dict(K=0), 1, "K must be"),
+    (dict(V=0), 1, "V must be"),
+    (dict(d=-1), 1, "d must be"),
+    (dict(sigma=0.0), 1, "sigma"),
+    (dict(sigma=-1.0), 1, "sigma"),
+    (dict(sigma=float("nan")), 1, "sigma"),
+    (dict(sigma=float("inf")), 1, "sigma"),
+    (dict(tok=2**32 - 2), 1, "token counter"),
+    (dict(draw=2**32 - 1), 1, "draw counter"),
+    (dict(V=70000), 2, "65536"),
+    (dict(V=50000, dt=0), 2, "LDS"),
+    (dict(ghat=None), 3, "workspace"),
+    (dict(ghat=None, ws=FAKE, wsb=16), 3, "workspace"),
+])
+def test_head_rejects_bad_arguments_on_host(kw, status, msg):
+    st, err = _head(**kw)
+    assert st == status, err
+    assert msg in err
+
+
+def test_outer_and_noise_reject_bad_arguments():
+    L = dust.lib()
+    assert L.dust_outer_product(None, FAKE, 4, 4, 4, FAKE, None, 0, None) == 1
+    assert L.dust_outer_product(FAKE, FAKE, 0, 4, 4, FAKE, None, 0, None) == 1
+    # a shape that needs split partial sums, without workspace
+    assert L.dust_outer_workspace_bytes(4096, 2048, 512) > 0
+    assert L.dust_outer_product(FAKE, FAKE, 4096, 2048, 512, FAKE, None, 0, None) == 3
+    assert L.dust_noise(1, 0, 0, 1, 0, 1, 4, None, None, None) == 1
+    assert L.dust_noise(1, 0, 2**32 - 1, 2, 0, 1, 4, None, FAKE, None) == 1
+    assert L.dust_noise(1, 0, 0, 0, 0, 1, 4, None, FAKE, None) == 1
+
+
+def test_workspace_queries():
+    L = dust.lib()
+    T, V, d = 4096, 8192, 512
+    need = L.dust_head_workspace_bytes(T, V, d, 256)
+    assert need >= 4 * T * V + L.dust_outer_workspace_bytes(T, V, d)
+    assert L.dust_head_workspace_bytes(0, V, d, 1) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(TypeError):
+        dust.estimate_head(torch.zeros(2, 4), torch.zeros(2, 3), torch.zeros(2, dtype=torch.int32), 1, 0.1, 0, 0)

@@ -1,0 +1,129 @@
+"""GPU parity of the LM-head estimator against the oracle.
+
+Small cases (every output element, ragged and degenerate shapes, every kernel
+variant) and the named workloads at full size in the benchmark's launch
+configuration: g_hat rows and rewards of sampled tokens against the oracle,
+every grad_w row sampled against the fp64 identity G_W = G_hat^T X, plus
+determinism and the draw/token split invariants.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import zeroth_order_activation_amd as dust
+from gpu_cases import dev, gpu_matmul, logits_to_device, logits_values, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+TOL_GW = 1e-3      # relative L2 on G_W (fp32 path)
+TOL_GHAT = 1e-4    # relative L2 on g_hat rows
+TOL_REW = 1e-4     # relative L2 on rewards
+
+
+def _run(case, K, sigma, seed, layer, tok0=0, draw0=0, want_ghat=True):
+    T, V = case["T"], case["V"]
+    z = logits_to_device(case)
+    x = dev(case["x"])
+    y = dev(case["labels"])
+    ghat = torch.empty((T, V), dtype=torch.float32, device="cuda") if want_ghat else None
+    rew = torch.empty((K, T), dtype=torch.float32, device="cuda")
+    gw = dust.estimate_head(z, x, y, K, sigma, seed, layer, tok0, draw0, ghat=ghat, rewards=rew)
+    torch.cuda.synchronize()
+    return gw, ghat, rew
+
+
+SMALL = [
+    # T, V, d, K, sigma, dtype, labels
+    (16, 4, 3, 3, 0.05, "f32", "uniform"),
+    (37, 1001, 13, 5, 1e-2, "f32", "zipf"),      # V % 4 != 0, Q = 1
+    (20, 2050, 9, 4, 1e-2, "bf16", "zipf"),      # Q = 4, ragged bf16
+    (24, 8192, 32, 4, 1e-2, "f32", "zipf"),      # Q = 8, p in registers
+    (8, 8193, 16, 3, 1e-2, "bf16", "zipf"),      # LDS row, 1024 lanes, Q = 4
+    (6, 20000, 8, 2, 5e-3, "f32", "zipf"),       # LDS row fp32, Q = 8
+    (4, 50304, 8, 2, 5e-3, "bf16", "zipf"),      # 768 lanes, Q = 17
+    (3, 60001, 8, 2, 5e-3, "bf16", "zipf"),      # 1024 lanes, Q = 16
+    (9, 500, 8, 3, 0.1, "f32", "uniform"),       # large sigma: library expm1 variant
+    (5, 20000, 8, 2, 0.5, "bf16", "zipf"),       # large sigma, LDS row
+]
+
+
+@pytest.mark.parametrize("T,V,d,K,sigma,dt,lab", SMALL)
+def test_head_small_cases_elementwise(T, V, d, K, sigma, dt, lab):
+    case = synth.head_case(T, V, d, seed=7 + V, labels=lab, logits_dtype=dt)
+    seed, layer, tok0, draw0 = 0x4455535400000000 + V, 1, 5, 3
+    gw, ghat, rew = _run(case, K, sigma, seed, layer, tok0, draw0)
+    og, orew, _ = oracle.head_estimate(logits_values(case), case["labels"], K, sigma, seed, layer, tok0, draw0)
+    e_g, e_r = rel_l2(ghat.cpu().numpy(), og), rel_l2(rew.cpu().numpy(), orew)
+    ogw = oracle.grad_w(og, case["x"])
+    e_w = rel_l2(gw.cpu().numpy(), ogw)
+    print(f"T={T} V={V} K={K} sigma={sigma} {dt}: ghat {e_g:.2e} rewards {e_r:.2e} grad_w {e_w:.2e}")
+    assert e_r < TOL_REW and e_g < TOL_GHAT and e_w < TOL_GW
+
+
+def test_single_class_vocabulary_gives_zero():
+    case = synth.head_case(7, 1, 3, seed=3, labels="uniform")
+    gw, ghat, rew = _run(case, 4, 0.2, 9, 1)
+    assert torch.all(rew == 0) and torch.all(ghat == 0) and torch.all(gw == 0)
+
+
+def test_workload1_full_parity():
+    c = synth.workload(1)
+    gw, ghat, rew = _run(c, c["K"], c["sigma"], c["seed_noise"], c["layer"])
+    og, orew, _ = oracle.head_estimate(logits_values(c), c["labels"], c["K"], c["sigma"], c["seed_noise"], c["layer"])
+    e_w = rel_l2(gw.cpu().numpy(), oracle.grad_w(og, c["x"]))
+    print(f"workload 1: grad_w rel L2 {e_w:.2e}")
+    assert e_w < TOL_GW
+    assert rel_l2(ghat.cpu().numpy(), og) < TOL_GHAT
+    assert rel_l2(rew.cpu().numpy(), orew) < TOL_REW
+
+
+@pytest.mark.parametrize("wid,ntok", [(2, 12), (4, 6)])
+def test_named_workload_full_size(wid, ntok):
+    """Full-size workload in the benchmark's configuration (g_hat kept in the workspace)."""
+    c = synth.workload(wid, matmul=gpu_matmul)
+    T, V, K, sigma = c["T"], c["V"], c["K"], c["sigma"]
+    z, x, y = logits_to_device(c), dev(c["x"]), dev(c["labels"])
+    gw_bench = dust.estimate_head(z, x, y, K, sigma, c["seed_noise"], c["layer"])
+    ghat = torch.empty((T, V), dtype=torch.float32, device="cuda")
+    rew = torch.empty((K, T), dtype=torch.float32, device="cuda")
+    gw = dust.estimate_head(z, x, y, K, sigma, c["seed_noise"], c["layer"], ghat=ghat, rewards=rew)
+    torch.cuda.synchronize()
+    assert torch.equal(gw, gw_bench)  # same result with or without the g_hat output
+    toks = np.random.default_rng(wid).choice(T, ntok, replace=False)
+    toks[0] = int(np.argmax(c["labels"] > 0))  # include a token whose label is not 0
+    zv = logits_values({k: (v[toks] if k in ("logits", "logits_bf16") else v) for k, v in c.items()})
+    og_rows = []
+    for t in toks:  # tokens one by one, with their global token ids
+        g1, r1, _ = oracle.head_estimate(zv[list(toks).index(t)][None], c["labels"][[t]], K, sigma,
+                                         c["seed_noise"], c["layer"], token_offset=int(t))
+        og_rows.append((g1[0], r1[:, 0]))
+    gh = ghat[toks].cpu().numpy()
+    rw = rew[:, toks].cpu().numpy()
+    e_g = rel_l2(gh, np.stack([g for g, _ in og_rows]))
+    e_r = rel_l2(rw, np.stack([r for _, r in og_rows], axis=1))
+    rows = np.random.default_rng(wid + 1).choice(V, 64, replace=False)
+    ref_rows = ghat[:, rows].cpu().numpy().astype(np.float64).T @ c["x"].astype(np.float64)
+    e_w = rel_l2(gw[rows].cpu().numpy(), ref_rows)
+    print(f"workload {wid}: sampled ghat {e_g:.2e} rewards {e_r:.2e}; grad_w rows vs G^T X {e_w:.2e}")
+    assert e_g < TOL_GHAT and e_r < TOL_REW and e_w < 1e-5
+
+
+def test_deterministic_and_split_invariants():
+    case = synth.head_case(33, 3000, 24, seed=11, labels="zipf")
+    K, K1, sigma, seed = 12, 5, 1e-2, 77
+    gw, _, rew = _run(case, K, sigma, seed, 1)
+    gw2, _, rew2 = _run(case, K, sigma, seed, 1)
+    assert torch.equal(gw, gw2) and torch.equal(rew, rew2)
+    g1, _, r1 = _run(case, K1, sigma, seed, 1)
+    g2, _, r2 = _run(case, K - K1, sigma, seed, 1, draw0=K1)
+    comb = (K1 * g1.double() + (K - K1) * g2.double()) / K
+    assert rel_l2(comb.cpu().numpy(), gw.cpu().numpy()) < 1e-5
+    assert torch.equal(torch.cat([r1, r2]), rew)
+    # token shard: the last 13 tokens alone with token_offset 20
+    sub = {k: (v[20:] if isinstance(v, np.ndarray) else v) for k, v in case.items()}
+    sub["T"] = 13
+    _, gs, rs = _run(sub, K, sigma, seed, 1, tok0=20)
+    _, gfull, _ = _run(case, K, sigma, seed, 1)
+    assert torch.equal(gs, gfull[20:])

@@ -1,0 +1,55 @@
+"""GPU parity: the exported noise stream and the outer-product GEMM.
+
+- raw Philox words: bit-exact against the oracle;
+- Gaussians: within an absolute tolerance of the oracle's fp64 Box-Muller
+  (the kernel uses the hardware log2/sqrt/sin/cos in fp32);
+- grad_w = ghat^T x: against an fp64 product, ragged shapes and split token ranges.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import zeroth_order_activation_amd as dust
+from gpu_cases import dev, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+GAUSS_ABS_TOL = 2e-5
+
+
+@pytest.mark.parametrize("seed,layer,d0,K,t0,T,n", [
+    (0, 0, 0, 2, 0, 3, 8),
+    (0x4455535400000002, 1, 7, 3, 100, 5, 37),
+    (0xFFFFFFFFFFFFFFFF, 2**32 - 1, 2**32 - 4, 4, 2**32 - 6, 6, 130),
+])
+def test_noise_raw_words_bit_exact(seed, layer, d0, K, t0, T, n):
+    g, w = dust.noise(seed, layer, d0, K, t0, T, n, raw=True)
+    w = w.cpu().numpy().view(np.uint32)
+    for i in range(K):
+        for t in range(T):
+            np.testing.assert_array_equal(w[i, t], oracle.noise_raw(seed, layer, d0 + i, t0 + t, n))
+
+
+def test_noise_gaussians_match_oracle():
+    K, T, n = 4, 128, 1024
+    g = dust.noise(0x4455535400000004, 1, 3, K, 11, T, n).cpu().numpy().astype(np.float64)
+    ref = oracle.noise_block(0x4455535400000004, 1, 3, K, 11, T, n)
+    err = np.abs(g - ref)
+    print(f"gaussian max abs err {err.max():.3e}, rms {np.sqrt((err ** 2).mean()):.3e}")
+    assert err.max() < GAUSS_ABS_TOL
+    assert np.abs(g).max() <= 5.7684
+
+
+@pytest.mark.parametrize("T,n,d", [(1, 1, 1), (37, 130, 70), (1000, 512, 64), (4096, 2048, 512), (300, 8192, 16)])
+def test_outer_product_matches_fp64(T, n, d):
+    rng = np.random.default_rng(T * 7 + n)
+    G = rng.standard_normal((T, n)).astype(np.float32)
+    X = rng.standard_normal((T, d)).astype(np.float32)
+    out = dust.outer_product(dev(G), dev(X)).cpu().numpy()
+    ref = G.astype(np.float64).T @ X.astype(np.float64)
+    assert rel_l2(out, ref) < 1e-5
+    scale = np.sqrt(T)  # entries are sums of T unit-variance products
+    assert np.abs(out - ref).max() < 1e-4 * scale
+    out2 = dust.outer_product(dev(G), dev(X)).cpu().numpy()
+    np.testing.assert_array_equal(out, out2)

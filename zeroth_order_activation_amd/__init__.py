@@ -1,0 +1,169 @@
+"""Dust per-token activation-perturbation gradient estimator for MI355X (gfx950).
+
+Thin Python binding of ``libdust.so`` (C ABI declared in ``include/dust.h``):
+argument marshalling only.  Every step of the estimator runs in the library's
+HIP kernels; torch provides device memory and the current stream.  There is no
+CPU fallback: if the library is missing, every call raises.
+
+Method (the Dust pages, Q Labs 2026; TL;DR page "Dust: zeroth-order
+Transformer pretraining without backprop", section 1): each token's layer
+output y_t = W x_t gets K Gaussian perturbations sigma a_t^(i); the loss is
+recomputed per draw; r_t^(i) = CE_clean - CE_perturbed;
+g_hat_t = -(1/(K sigma)) sum_i r_t^(i) a_t^(i); G_W = sum_t g_hat_t x_t^T.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdust.so")
+F32, BF16 = 0, 1
+_lib = None
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_u32 = ctypes.c_uint32
+_u64 = ctypes.c_uint64
+_f32 = ctypes.c_float
+
+
+class DustError(RuntimeError):
+    """A non-OK dust_status; ``status`` holds the code."""
+
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"dust status {status}: {msg}")
+        self.status = status
+
+
+def lib():
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m zeroth_order_activation_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.dust_abi_version.restype = ctypes.c_int
+        L.dust_last_error.restype = ctypes.c_char_p
+        L.dust_set_stage_event.restype = ctypes.c_int
+        L.dust_set_stage_event.argtypes = [ctypes.c_int, _vp]
+        L.dust_noise.restype = ctypes.c_int
+        L.dust_noise.argtypes = [_u64, _u32, _u32, _i64, _u32, _i64, _i64, _vp, _vp, _vp]
+        L.dust_outer_workspace_bytes.restype = ctypes.c_size_t
+        L.dust_outer_workspace_bytes.argtypes = [_i64, _i64, _i64]
+        L.dust_outer_product.restype = ctypes.c_int
+        L.dust_outer_product.argtypes = [_vp, _vp, _i64, _i64, _i64, _vp, _vp, ctypes.c_size_t, _vp]
+        L.dust_head_workspace_bytes.restype = ctypes.c_size_t
+        L.dust_head_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64]
+        L.dust_estimate_head.restype = ctypes.c_int
+        L.dust_estimate_head.argtypes = [_vp, ctypes.c_int, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _u64, _u32,
+                                         _u32, _u32, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        if hasattr(L, "dust_estimate_linear"):
+            L.dust_linear_workspace_bytes.restype = ctypes.c_size_t
+            L.dust_linear_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _i64]
+            L.dust_estimate_linear.restype = ctypes.c_int
+            L.dust_estimate_linear.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32,
+                                               _f32, _u64, _u32, _u32, _u32, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                                               _vp]
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise DustError(status, lib().dust_last_error().decode())
+
+
+def _p(t):
+    return None if t is None else _vp(t.data_ptr())
+
+
+def _dev_tensor(t, name, dtypes):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(t):
+    return _vp(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _workspace(nbytes, device, workspace):
+    if nbytes == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def set_stage_event(stage: int, event) -> None:
+    """Record ``event`` (a torch.cuda.Event) after ``stage`` of each estimator call
+    from this thread (0: estimator kernel, 1: outer product); None clears it."""
+    if event is None:
+        ptr = None
+    else:
+        ptr = _vp(event.cuda_event)
+    _check(lib().dust_set_stage_event(stage, ptr))
+
+
+def noise(seed: int, layer: int, draw_offset: int, K: int, token_offset: int, T: int, n: int,
+          device="cuda", raw: bool = False):
+    """The Gaussian noise a[K,T,n] the estimators use (and the raw Philox words if ``raw``)."""
+    g = torch.empty((K, T, n), dtype=torch.float32, device=device)
+    w = torch.empty((K, T, 4 * ((n + 3) // 4)), dtype=torch.int32, device=device) if raw else None
+    _check(lib().dust_noise(seed, layer, draw_offset, K, token_offset, T, n, _p(w), _p(g), _stream(g)))
+    return (g, w.view(torch.uint32) if hasattr(torch, "uint32") else w) if raw else g
+
+
+def outer_product(ghat, x, grad_w=None, workspace=None):
+    """grad_w = ghat^T x for ghat [T,n], x [T,d] (fp32)."""
+    _dev_tensor(ghat, "ghat", (torch.float32,))
+    _dev_tensor(x, "x", (torch.float32,))
+    T, n = ghat.shape
+    d = x.shape[1]
+    if x.shape[0] != T:
+        raise ValueError("ghat and x must have the same number of rows")
+    if grad_w is None:
+        grad_w = torch.empty((n, d), dtype=torch.float32, device=ghat.device)
+    ws, nb = _workspace(lib().dust_outer_workspace_bytes(T, n, d), ghat.device, workspace)
+    _check(lib().dust_outer_product(_p(ghat), _p(x), T, n, d, _p(grad_w), _p(ws), nb, _stream(ghat)))
+    return grad_w
+
+
+def head_workspace_bytes(T: int, V: int, d: int, K: int) -> int:
+    return int(lib().dust_head_workspace_bytes(T, V, d, K))
+
+
+def estimate_head(logits, x, labels, K: int, sigma: float, seed: int, layer: int,
+                  token_offset: int = 0, draw_offset: int = 0, *, grad_w=None, ghat=None,
+                  rewards=None, workspace=None):
+    """LM-head estimator on cached logits [T,V] (fp32 or bf16).  Returns grad_w [V,d].
+
+    Pass preallocated ``ghat`` [T,V] / ``rewards`` [K,T] fp32 tensors to receive
+    g_hat and the rewards as well.
+    """
+    _dev_tensor(logits, "logits", (torch.float32, torch.bfloat16))
+    _dev_tensor(x, "x", (torch.float32,))
+    _dev_tensor(labels, "labels", (torch.int32,))
+    T, V = logits.shape
+    d = x.shape[1]
+    if x.shape[0] != T or labels.numel() != T:
+        raise ValueError("logits, x and labels disagree on T")
+    dt = F32 if logits.dtype == torch.float32 else BF16
+    if grad_w is None:
+        grad_w = torch.empty((V, d), dtype=torch.float32, device=logits.device)
+    # with ghat given, only the outer product's split partial sums need scratch space
+    need = (lib().dust_outer_workspace_bytes(T, V, d) if ghat is not None
+            else lib().dust_head_workspace_bytes(T, V, d, K))
+    ws, nb = _workspace(need, logits.device, workspace)
+    _check(lib().dust_estimate_head(_p(logits), dt, _p(x), _p(labels), T, V, d, K, sigma, seed, layer,
+                                    token_offset, draw_offset, _p(grad_w), _p(ghat), _p(rewards), _p(ws), nb,
+                                    _stream(logits)))
+    return grad_w

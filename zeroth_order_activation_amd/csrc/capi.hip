@@ -1,0 +1,204 @@
+// C ABI of the Dust estimator library: argument checks, workspace layout and
+// dispatch.  Every check runs on the host before anything is enqueued.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+#include <vector>
+
+#include "dust.h"
+#include "dust_internal.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+thread_local hipEvent_t g_stage_event[2] = {nullptr, nullptr};
+
+hipError_t record_stage(int stage, hipStream_t s) {
+    return g_stage_event[stage] ? hipEventRecord(g_stage_event[stage], s) : hipSuccess;
+}
+
+dust_status fail(dust_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+dust_status ok() {
+    g_err.clear();
+    return DUST_OK;
+}
+
+dust_status device_fail(const char* what, hipError_t e) {
+    return fail(DUST_E_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool env_flag(const char* name) {
+    const char* v = std::getenv(name);
+    return v && v[0] && v[0] != '0';
+}
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Checks shared by the estimators.  Returns DUST_OK or a failure with message.
+dust_status check_common(int64_t T, int64_t K, float sigma, uint32_t token_offset, uint32_t draw_offset) {
+    if (T <= 0 || T > (int64_t)INT32_MAX) return fail(DUST_E_INVALID, "T must be in [1, 2^31): got %lld", (long long)T);
+    if (K <= 0 || K > (int64_t)INT32_MAX) return fail(DUST_E_INVALID, "K must be in [1, 2^31): got %lld", (long long)K);
+    if (!std::isfinite(sigma) || !(sigma > 0.f)) return fail(DUST_E_INVALID, "sigma must be finite and > 0: got %g", (double)sigma);
+    if ((uint64_t)token_offset + (uint64_t)T > (1ull << 32))
+        return fail(DUST_E_INVALID, "token_offset + T exceeds the 32-bit token counter");
+    if ((uint64_t)draw_offset + (uint64_t)K > (1ull << 32))
+        return fail(DUST_E_INVALID, "draw_offset + K exceeds the 32-bit draw counter");
+    return DUST_OK;
+}
+
+dust_status check_labels(const int32_t* labels, int64_t T, int64_t V, hipStream_t stream) {
+    if (!env_flag("DUST_DEBUG_CHECKS")) return DUST_OK;
+    std::vector<int32_t> h((size_t)T);
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e == hipSuccess) e = hipMemcpy(h.data(), labels, (size_t)T * sizeof(int32_t), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return device_fail("label check copy", e);
+    for (int64_t t = 0; t < T; ++t)
+        if (h[(size_t)t] < 0 || h[(size_t)t] >= V)
+            return fail(DUST_E_INVALID, "label[%lld] = %d is outside [0, %lld)", (long long)t, h[(size_t)t], (long long)V);
+    return DUST_OK;
+}
+
+size_t head_ghat_bytes(int64_t T, int64_t V) { return round_up((size_t)T * (size_t)V * sizeof(float)); }
+
+}  // namespace
+
+extern "C" {
+
+int dust_abi_version(void) { return DUST_ABI_VERSION; }
+
+const char* dust_last_error(void) { return g_err.c_str(); }
+
+dust_status dust_set_stage_event(int stage, void* event) {
+    if (stage < 0 || stage > 1) return fail(DUST_E_INVALID, "dust_set_stage_event: stage must be 0 or 1");
+    g_stage_event[stage] = static_cast<hipEvent_t>(event);
+    return ok();
+}
+
+dust_status dust_noise(uint64_t seed, uint32_t layer, uint32_t draw_offset, int64_t K, uint32_t token_offset,
+                       int64_t T, int64_t n, uint32_t* raw, float* gauss, void* stream) {
+    if (!raw && !gauss) return fail(DUST_E_INVALID, "dust_noise: raw and gauss are both NULL");
+    if (T <= 0 || K <= 0 || n <= 0) return fail(DUST_E_INVALID, "dust_noise: K, T, n must be >= 1");
+    if ((uint64_t)token_offset + (uint64_t)T > (1ull << 32) || (uint64_t)draw_offset + (uint64_t)K > (1ull << 32))
+        return fail(DUST_E_INVALID, "dust_noise: offset + count exceeds the 32-bit counter");
+    const int64_t threads = K * T * ((n + 3) / 4);
+    if (K > (int64_t)INT32_MAX || T > (int64_t)INT32_MAX || threads > ((int64_t)1 << 32) - 256)
+        return fail(DUST_E_UNSUPPORTED, "dust_noise: K*T*ceil(n/4) must stay below 2^32");
+    hipError_t e = dust::launch_noise_export(seed, layer, draw_offset, K, token_offset, T, n, raw, gauss,
+                                             static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_fail("dust_noise launch", e);
+    return ok();
+}
+
+size_t dust_outer_workspace_bytes(int64_t T, int64_t n, int64_t d) {
+    if (T <= 0 || n <= 0 || d <= 0) return 0;
+    return dust::outer_workspace_bytes(T, n, d);
+}
+
+dust_status dust_outer_product(const float* ghat, const float* x, int64_t T, int64_t n, int64_t d, float* grad_w,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    if (!ghat || !x || !grad_w) return fail(DUST_E_INVALID, "dust_outer_product: null tensor pointer");
+    if (!aligned16(ghat) || !aligned16(x) || !aligned16(grad_w))
+        return fail(DUST_E_INVALID, "dust_outer_product: tensors must be 16-byte aligned");
+    if (T <= 0 || n <= 0 || d <= 0) return fail(DUST_E_INVALID, "dust_outer_product: T, n, d must be >= 1");
+    if (n > 65535LL * 128 || d > 65535LL * 128) return fail(DUST_E_UNSUPPORTED, "dust_outer_product: n or d too large");
+    const size_t need = dust::outer_workspace_bytes(T, n, d);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+        return fail(DUST_E_WORKSPACE, "dust_outer_product: workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (workspace && !aligned16(workspace)) return fail(DUST_E_INVALID, "dust_outer_product: workspace must be 16-byte aligned");
+    hipError_t e = dust::launch_outer(ghat, x, T, n, d, grad_w, workspace, workspace_bytes,
+                                      static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_fail("dust_outer_product launch", e);
+    return ok();
+}
+
+size_t dust_head_workspace_bytes(int64_t T, int64_t V, int64_t d, int64_t K) {
+    (void)K;
+    if (T <= 0 || V <= 0 || d <= 0) return 0;
+    return head_ghat_bytes(T, V) + dust::outer_workspace_bytes(T, V, d);
+}
+
+dust_status dust_estimate_head(const void* logits, int logits_dtype, const float* x, const int32_t* labels,
+                               int64_t T, int64_t V, int64_t d, int64_t K, float sigma, uint64_t seed,
+                               uint32_t layer, uint32_t token_offset, uint32_t draw_offset, float* grad_w,
+                               float* ghat, float* rewards, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+    if (!logits || !x || !labels || !grad_w)
+        return fail(DUST_E_INVALID, "dust_estimate_head: logits, x, labels and grad_w must be non-NULL");
+    if (logits_dtype != DUST_F32 && logits_dtype != DUST_BF16)
+        return fail(DUST_E_UNSUPPORTED, "dust_estimate_head: logits_dtype %d is not DUST_F32 or DUST_BF16", logits_dtype);
+    if (!aligned16(logits) || !aligned16(x) || !aligned16(labels) || !aligned16(grad_w) ||
+        (ghat && !aligned16(ghat)) || (rewards && !aligned16(rewards)) || (workspace && !aligned16(workspace)))
+        return fail(DUST_E_INVALID, "dust_estimate_head: every pointer must be 16-byte aligned");
+    dust_status s = check_common(T, K, sigma, token_offset, draw_offset);
+    if (s != DUST_OK) return s;
+    if (V <= 0) return fail(DUST_E_INVALID, "dust_estimate_head: V must be >= 1");
+    if (d <= 0) return fail(DUST_E_INVALID, "dust_estimate_head: d must be >= 1");
+    if (V > 65535LL * 128 || d > 65535LL * 128) return fail(DUST_E_UNSUPPORTED, "dust_estimate_head: V or d too large");
+    const dust::HeadPlan plan = dust::plan_head(V, logits_dtype, sigma);
+    if (!plan.ok) return fail(DUST_E_UNSUPPORTED, "dust_estimate_head: %s", plan.why);
+
+    const size_t ghat_ws = ghat ? 0 : head_ghat_bytes(T, V);
+    const size_t outer_ws = dust::outer_workspace_bytes(T, V, d);
+    const size_t need = ghat_ws + outer_ws;
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+        return fail(DUST_E_WORKSPACE, "dust_estimate_head: workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    s = check_labels(labels, T, V, st);
+    if (s != DUST_OK) return s;
+
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    float* g = ghat ? ghat : reinterpret_cast<float*>(ws);
+    void* ows = outer_ws ? ws + ghat_ws : nullptr;
+
+    dust::HeadArgs A{};
+    A.logits = logits;
+    A.labels = labels;
+    A.ghat = g;
+    A.rewards = rewards;
+    A.T = (int32_t)T;
+    A.V = (int32_t)V;
+    A.K = (int32_t)K;
+    A.sigma = sigma;
+    const double sd = sigma;
+    A.smul = plan.deg == 5 ? sigma : 1.0f;
+    A.gscale = (float)(-1.0 / ((double)K * sd));
+    A.coef[0] = 1.0f;
+    A.coef[1] = (float)(sd / 2.0);
+    A.coef[2] = (float)(sd * sd / 6.0);
+    A.coef[3] = (float)(sd * sd * sd / 24.0);
+    A.coef[4] = (float)(sd * sd * sd * sd / 120.0);
+    A.k0 = (uint32_t)seed;
+    A.k1 = (uint32_t)(seed >> 32);
+    A.layer = layer;
+    A.tok0 = token_offset;
+    A.draw0 = draw_offset;
+    if (env_flag("DUST_LOG"))
+        std::fprintf(stderr, "[dust] head T=%lld V=%lld d=%lld K=%lld nt=%d q=%d pmode=%d deg=%d lds=%zu\n",
+                     (long long)T, (long long)V, (long long)d, (long long)K, plan.nt, plan.q, plan.pmode, plan.deg,
+                     plan.lds);
+    hipError_t e = dust::launch_head(plan, logits_dtype, A, st);
+    if (e != hipSuccess) return device_fail("dust_estimate_head: estimator launch", e);
+    if ((e = record_stage(0, st)) != hipSuccess) return device_fail("dust_estimate_head: stage event", e);
+    e = dust::launch_outer(g, x, T, V, d, grad_w, ows, outer_ws, st);
+    if (e != hipSuccess) return device_fail("dust_estimate_head: outer-product launch", e);
+    if ((e = record_stage(1, st)) != hipSuccess) return device_fail("dust_estimate_head: stage event", e);
+    return ok();
+}
+
+}  // extern "C"

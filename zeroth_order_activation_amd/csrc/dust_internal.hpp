@@ -1,0 +1,46 @@
+// Host-side launchers of the Dust kernels (internal; the public surface is
+// include/dust.h).  Every launcher assumes its arguments were validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dust {
+
+hipError_t launch_noise_export(uint64_t seed, uint32_t layer, uint32_t draw0, int64_t K, uint32_t tok0,
+                               int64_t T, int64_t n, uint32_t* raw, float* gauss, hipStream_t stream);
+
+// ---- LM head on cached logits -------------------------------------------
+struct HeadArgs {
+    const void* logits;      // [T,V] fp32 or bf16 bits
+    const int32_t* labels;   // [T]
+    float* ghat;             // [T,V] out
+    float* rewards;          // [K,T] out or null
+    int32_t T, V, K;
+    float sigma;
+    float smul;              // factor applied to the per-draw sum before log1p
+    float gscale;            // -1/(K sigma)
+    float coef[8];           // Horner coefficients of expm1(sigma a)/(sigma a), see head.hpp
+    uint32_t k0, k1, layer, tok0, draw0;
+};
+
+struct HeadPlan {
+    int nt;        // threads per workgroup (one workgroup per token)
+    int q;         // channel quads per lane
+    int pmode;     // 0: probabilities in registers, 1: logit row staged in LDS
+    int deg;       // 5: polynomial expm1, 0: library expm1
+    size_t lds;    // dynamic LDS bytes
+    bool ok;
+    const char* why;
+};
+
+HeadPlan plan_head(int64_t V, int logits_dtype, float sigma);
+hipError_t launch_head(const HeadPlan& plan, int logits_dtype, const HeadArgs& args, hipStream_t stream);
+
+// ---- grad_w = ghat^T x (fp32 MFMA) --------------------------------------
+size_t outer_workspace_bytes(int64_t T, int64_t n, int64_t d);
+hipError_t launch_outer(const float* ghat, const float* x, int64_t T, int64_t n, int64_t d, float* grad_w,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+}  // namespace dust

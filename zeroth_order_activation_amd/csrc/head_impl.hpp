@@ -1,0 +1,286 @@
+// LM-head estimator on cached logits: one workgroup per token.
+//
+// Method (TL;DR page "Dust: zeroth-order Transformer pretraining without
+// backprop", section 1, "credit assignment without backprop" and "reducing
+// interference"; news article on tahou.com, mechanism paragraph): the head is
+// jittered on the cached logits z_t, only the loss is recomputed, the reward
+// is the loss reduction at the token and
+//     g_hat_t = -(1/(K sigma)) sum_i r_t^(i) a_t^(i).
+//
+// Per draw the kernel needs CE(z + sigma a) - CE(z).  With p = softmax(z) this
+// is exactly  log1p(S) - sigma a_y,  S = sum_v p_v expm1(sigma a_v),  which
+// avoids subtracting two losses of size ln V in fp32.  |a| <= sqrt(48 ln 2)
+// by construction of the noise, so for small sigma expm1 is a short
+// polynomial: expm1(x) = x (1 + x/2 + x^2/6 + x^3/24 + x^4/120) with x = sigma a,
+// truncation below 2^-25 relative while sigma <= 0.02 (else the library expm1).
+//
+// Layout: lane l owns channel quads q = l + j*NT (j < Q), so each load and
+// store of a quad is one coalesced 16-byte (fp32) or 8-byte (bf16) access.
+// The noise of the current draw and the running sum of r*a live in registers;
+// each draw costs one workgroup reduction (two floats) and one barrier.
+#pragma once
+
+#include "dust_device.hpp"
+#include "dust_internal.hpp"
+
+namespace dust {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int LT>
+__device__ __forceinline__ f32x4 load_quad(const void* row, int q, int V, bool vec) {
+    f32x4 r;
+    const float ninf = -__builtin_inff();
+    if (vec) {
+        if (LT == 0) {
+            const float4 v = reinterpret_cast<const float4*>(row)[q];
+            r.v[0] = v.x; r.v[1] = v.y; r.v[2] = v.z; r.v[3] = v.w;
+        } else {
+            const uint2 v = reinterpret_cast<const uint2*>(row)[q];
+            r.v[0] = __uint_as_float(v.x << 16);
+            r.v[1] = __uint_as_float(v.x & 0xFFFF0000u);
+            r.v[2] = __uint_as_float(v.y << 16);
+            r.v[3] = __uint_as_float(v.y & 0xFFFF0000u);
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int v = 4 * q + c;
+            if (v < V)
+                r.v[c] = LT == 0 ? reinterpret_cast<const float*>(row)[v]
+                                 : bf16_to_f32(reinterpret_cast<const uint16_t*>(row)[v]);
+            else
+                r.v[c] = ninf;
+        }
+    }
+    return r;
+}
+
+// Block-wide reductions for the clean statistics (called a few times per token).
+template <int NT>
+__device__ __forceinline__ float block_max(float v, float* sh) {
+    v = wave_max(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float r = sh[0];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) r = fmaxf(r, sh[w]);
+    return r;
+}
+template <int NT>
+__device__ __forceinline__ float block_sum(float v, float* sh) {
+    v = wave_sum(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float r = 0.f;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) r += sh[w];
+    return r;
+}
+
+// expm1(sigma a) / sigma  (DEG = 5)  or  expm1(sigma a)  (DEG = 0).
+template <int DEG>
+__device__ __forceinline__ float em1(float a, const HeadArgs& A) {
+    if (DEG == 5) {
+        float t = fmaf(a, A.coef[4], A.coef[3]);
+        t = fmaf(a, t, A.coef[2]);
+        t = fmaf(a, t, A.coef[1]);
+        t = fmaf(a, t, 1.0f);
+        return a * t;
+    } else {
+        return expm1f(A.sigma * a);
+    }
+}
+
+// Row of LDS-staged logits (PMODE 1): stored in the logits' own type.
+template <int LT>
+__device__ __forceinline__ f32x4 lds_quad(const unsigned char* zl, int q) {
+    f32x4 r;
+    if (LT == 0) {
+        const float4 v = reinterpret_cast<const float4*>(zl)[q];
+        r.v[0] = v.x; r.v[1] = v.y; r.v[2] = v.z; r.v[3] = v.w;
+    } else {
+        const uint2 v = reinterpret_cast<const uint2*>(zl)[q];
+        r.v[0] = __uint_as_float(v.x << 16);
+        r.v[1] = __uint_as_float(v.x & 0xFFFF0000u);
+        r.v[2] = __uint_as_float(v.y << 16);
+        r.v[3] = __uint_as_float(v.y & 0xFFFF0000u);
+    }
+    return r;
+}
+
+template <int NT, int Q, int LT, int PMODE, int DEG>
+__global__ void __launch_bounds__(NT) head_estimate_kernel(HeadArgs A) {
+    constexpr int NW = NT / 64;
+    __shared__ float sh_stat[NW];
+    __shared__ float sh_red[2][NW][2];
+    extern __shared__ __align__(16) unsigned char zlds[];
+
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int wid = tid >> 6;
+    const int V = A.V;
+    const int nq = (V + 3) >> 2;
+    const bool vec = (V & 3) == 0;
+    const void* row = reinterpret_cast<const unsigned char*>(A.logits) + (size_t)t * V * (LT == 0 ? 4 : 2);
+
+    // ---- clean statistics: max, log-sum-exp, probabilities ---------------
+    float p[PMODE == 0 ? Q : 1][4];
+    float m = -__builtin_inff();
+    if (PMODE == 0) {
+#pragma unroll
+        for (int j = 0; j < Q; ++j) {
+            const int q = tid + j * NT;
+            f32x4 z;
+            if (q < nq) z = load_quad<LT>(row, q, V, vec);
+            else z.v[0] = z.v[1] = z.v[2] = z.v[3] = -__builtin_inff();
+#pragma unroll
+            for (int c = 0; c < 4; ++c) { p[j][c] = z.v[c]; m = fmaxf(m, z.v[c]); }
+        }
+    } else {
+        for (int q = tid; q < nq; q += NT) {
+            const f32x4 z = load_quad<LT>(row, q, V, vec);
+            if (LT == 0) {
+                reinterpret_cast<float4*>(zlds)[q] = make_float4(z.v[0], z.v[1], z.v[2], z.v[3]);
+            } else {
+                uint2 b;
+                b.x = (__float_as_uint(z.v[0]) >> 16) | (__float_as_uint(z.v[1]) & 0xFFFF0000u);
+                b.y = (__float_as_uint(z.v[2]) >> 16) | (__float_as_uint(z.v[3]) & 0xFFFF0000u);
+                reinterpret_cast<uint2*>(zlds)[q] = b;
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) m = fmaxf(m, z.v[c]);
+        }
+    }
+    m = block_max<NT>(m, sh_stat);  // its barriers also publish the LDS row
+    float s = 0.f;
+    if (PMODE == 0) {
+#pragma unroll
+        for (int j = 0; j < Q; ++j)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) s += __expf(p[j][c] - m);
+    } else {
+        for (int q = tid; q < nq; q += NT) {
+            const f32x4 z = lds_quad<LT>(zlds, q);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) s += __expf(z.v[c] - m);
+        }
+    }
+    s = block_sum<NT>(s, sh_stat);
+    const float lse = m + __logf(s);
+    const float lse2 = lse * kLog2e;
+    if (PMODE == 0) {
+#pragma unroll
+        for (int j = 0; j < Q; ++j)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) p[j][c] = __builtin_amdgcn_exp2f(fmaf(p[j][c], kLog2e, -lse2));
+    }
+
+    // ---- label owner --------------------------------------------------------
+    const uint32_t y = (uint32_t)A.labels[t];
+    const uint32_t qy = y >> 2, cy = y & 3u;
+    const uint32_t jy = qy / NT;
+    const bool owner = (qy % NT) == (uint32_t)tid && y < (uint32_t)V;
+
+    const uint32_t tok = A.tok0 + (uint32_t)t;
+    float acc[Q][4];
+#pragma unroll
+    for (int j = 0; j < Q; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[j][c] = 0.f;
+
+    for (int i = 0; i < A.K; ++i) {
+        const uint32_t draw = A.draw0 + (uint32_t)i;
+        float a[Q][4];
+        float sl = 0.f, ly = 0.f;
+#pragma unroll
+        for (int j = 0; j < Q; ++j) {
+            const int q = tid + j * NT;
+            if (q < nq) {
+                const f32x4 g = gauss4(tok, (uint32_t)q, draw, A.layer, A.k0, A.k1);
+                f32x4 pz;
+                if (PMODE == 1) pz = lds_quad<LT>(zlds, q);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    a[j][c] = g.v[c];
+                    const float pc = PMODE == 0 ? p[j][c]
+                                                : __builtin_amdgcn_exp2f(fmaf(pz.v[c], kLog2e, -lse2));
+                    sl = fmaf(pc, em1<DEG>(g.v[c], A), sl);
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) a[j][c] = 0.f;
+            }
+            if ((uint32_t)j == jy) {
+                const float sel = cy == 0 ? a[j][0] : cy == 1 ? a[j][1] : cy == 2 ? a[j][2] : a[j][3];
+                ly = owner ? sel : 0.f;
+            }
+        }
+        sl = wave_sum(sl);
+        ly = wave_sum(ly);
+        const int b = i & 1;
+        if ((tid & 63) == 0) { sh_red[b][wid][0] = sl; sh_red[b][wid][1] = ly; }
+        __syncthreads();
+        float S = 0.f, LY = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) { S += sh_red[b][w][0]; LY += sh_red[b][w][1]; }
+        const float r = A.sigma * LY - log1pf(S * A.smul);
+#pragma unroll
+        for (int j = 0; j < Q; ++j)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[j][c] = fmaf(r, a[j][c], acc[j][c]);
+        if (tid == 0 && A.rewards) A.rewards[(size_t)i * A.T + t] = r;
+    }
+
+    // ---- g_hat_t = -(1/(K sigma)) sum_i r a ------------------------------------
+    float* out = A.ghat + (size_t)t * V;
+#pragma unroll
+    for (int j = 0; j < Q; ++j) {
+        const int q = tid + j * NT;
+        if (q >= nq) continue;
+        if (vec) {
+            reinterpret_cast<float4*>(out)[q] = make_float4(acc[j][0] * A.gscale, acc[j][1] * A.gscale,
+                                                            acc[j][2] * A.gscale, acc[j][3] * A.gscale);
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (4 * q + c < V) out[4 * q + c] = acc[j][c] * A.gscale;
+        }
+    }
+}
+
+template <int NT, int Q, int LT, int PMODE, int DEG>
+hipError_t launch_head_variant(const HeadPlan& plan, const HeadArgs& args, hipStream_t stream) {
+    auto k = head_estimate_kernel<NT, Q, LT, PMODE, DEG>;
+    if (plan.lds > 0) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)plan.lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k, dim3(args.T), dim3(NT), plan.lds, stream, args);
+    return hipGetLastError();
+}
+
+// Dispatch over the compiled variants for one logits type.
+template <int LT>
+hipError_t dispatch_head(const HeadPlan& P, const HeadArgs& A, hipStream_t s) {
+#define DUST_HEAD_CASE(NT_, Q_, PM_)                                                       \
+    if (P.nt == NT_ && P.q == Q_ && P.pmode == PM_) {                                     \
+        return P.deg == 5 ? launch_head_variant<NT_, Q_, LT, PM_, 5>(P, A, s)             \
+                          : launch_head_variant<NT_, Q_, LT, PM_, 0>(P, A, s);            \
+    }
+    DUST_HEAD_CASE(256, 1, 0)
+    DUST_HEAD_CASE(256, 2, 0)
+    DUST_HEAD_CASE(256, 4, 0)
+    DUST_HEAD_CASE(256, 8, 0)
+    DUST_HEAD_CASE(1024, 4, 1)
+    DUST_HEAD_CASE(1024, 8, 1)
+    DUST_HEAD_CASE(768, 17, 1)
+    DUST_HEAD_CASE(1024, 16, 1)
+#undef DUST_HEAD_CASE
+    return hipErrorInvalidConfiguration;
+}
+
+}  // namespace dust
