@@ -117,6 +117,9 @@ def main():
     torch.cuda.synchronize()
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for e3 in ev:  # torch creates the underlying hipEvent at its first record
+        for e in e3:
+            e.record(stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -128,8 +131,8 @@ def main():
     wall = time.perf_counter() - t0
     dust.set_stage_event(0, None)
     dust.set_stage_event(1, None)
-    est_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    outer_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    est_ms = float(np.mean([dust.event_elapsed_ms(e[0], e[1]) for e in ev]))
+    outer_ms = float(np.mean([dust.event_elapsed_ms(e[1], e[2]) for e in ev]))
 
     ms_per_step = wall * 1e3 / args.steps
     td = T * K

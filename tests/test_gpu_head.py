@@ -63,9 +63,16 @@ def test_head_small_cases_elementwise(T, V, d, K, sigma, dt, lab):
 
 
 def test_single_class_vocabulary_gives_zero():
+    # With V = 1 every loss is 0, so the rewards and the estimate vanish in exact
+    # arithmetic (the oracle gives exact zeros).  The kernel evaluates the reward as
+    # sigma a_y - log1p(p_y expm1(sigma a_y)) with p_y = 1, which leaves fp32 rounding
+    # of a few ulp of sigma*a.
     case = synth.head_case(7, 1, 3, seed=3, labels="uniform")
-    gw, ghat, rew = _run(case, 4, 0.2, 9, 1)
-    assert torch.all(rew == 0) and torch.all(ghat == 0) and torch.all(gw == 0)
+    for sigma in (0.2, 1e-2):
+        gw, ghat, rew = _run(case, 4, sigma, 9, 1)
+        assert rew.abs().max().item() <= 8 * 2.0 ** -24 * sigma * 5.77
+        assert ghat.abs().max().item() <= 1e-5
+        assert gw.abs().max().item() <= 1e-4
 
 
 def test_workload1_full_parity():

@@ -105,12 +105,34 @@ def _workspace(nbytes, device, workspace):
 
 def set_stage_event(stage: int, event) -> None:
     """Record ``event`` (a torch.cuda.Event) after ``stage`` of each estimator call
-    from this thread (0: estimator kernel, 1: outer product); None clears it."""
+    from this thread (0: estimator kernel, 1: outer product); None clears it.
+    The event must already exist (torch creates it at its first ``record``)."""
     if event is None:
         ptr = None
     else:
+        if not event.cuda_event:
+            raise ValueError("record the event once before handing it to the library")
         ptr = _vp(event.cuda_event)
     _check(lib().dust_set_stage_event(stage, ptr))
+
+
+_hip = None
+
+
+def event_elapsed_ms(start, end) -> float:
+    """Milliseconds between two recorded torch.cuda.Events, read with
+    hipEventElapsedTime (the library records stage events itself, which torch's
+    own bookkeeping does not see)."""
+    global _hip
+    if _hip is None:
+        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), _vp, _vp]
+        _hip.hipEventElapsedTime.restype = ctypes.c_int
+    ms = ctypes.c_float(0.0)
+    st = _hip.hipEventElapsedTime(ctypes.byref(ms), _vp(start.cuda_event), _vp(end.cuda_event))
+    if st != 0:
+        raise RuntimeError(f"hipEventElapsedTime failed with status {st}")
+    return float(ms.value)
 
 
 def noise(seed: int, layer: int, draw_offset: int, K: int, token_offset: int, T: int, n: int,
