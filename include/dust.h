@@ -76,7 +76,7 @@ const char *dust_last_error(void);
 /*
  * Profiling hook: while set, `event` (a hipEvent_t) is recorded on the call's
  * stream right after the given stage of every estimator call made from this
- * thread.  stage 0 = after the per-token estimator kernel (g_hat ready),
+ * thread.  stage 0 = after g_hat is ready (the per-token estimator kernels),
  * stage 1 = after the weight-gradient outer product.  Pass NULL to clear.
  * The caller owns the events.  Used to time the stages of one call.
  */
@@ -128,6 +128,35 @@ dust_status dust_estimate_head(const void *logits, int logits_dtype, const float
                                uint32_t token_offset, uint32_t draw_offset,
                                float *grad_w, float *ghat, float *rewards,
                                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Interior MLP-linear estimator: W1 of a pre-LN MLP block, with the cached
+ * downstream recomputed per draw (TL;DR page, section 1: noise on the output of
+ * every linear layer, reward = loss reduction at the token; news article on
+ * tahou.com, mechanism paragraph: unperturbed intermediates are cached and
+ * only the part the perturbation changes is recomputed).
+ * For token t and draw i, with a = a_t^(i):
+ *   m   = bf16(GELU_erf(h_t + sigma a))                 (fp32, then round to nearest even)
+ *   f   = bf16(LN(x_t + W2 m))                          (LN without affine, eps = ln_eps)
+ *   CE  = logsumexp(W_head f) - (W_head f)[y_t]         (fp32 accumulation)
+ *   r   = CE(a = 0) - CE(a);  g_hat_t = -(1/(K sigma)) sum_i r a;  G_W1 = sum_t g_hat_t u_t^T.
+ *   u      : float [T, d]   input of W1 (u = LN(x), the x_t of G_W1)
+ *   h      : float [T, n]   cached W1 output (pre-GELU)
+ *   x_res  : float [T, d]   residual stream added after W2
+ *   w2     : bf16 bits [d, n];   w_head : bf16 bits [V, d]
+ *   labels : int32 [T]
+ *   grad_w : OUT float [n, d];  ghat : OUT float [T, n] or NULL;  rewards : OUT float [K, T] or NULL.
+ * Supported: d in {256, 512}, n a multiple of 32, V >= 1.
+ * Workspace: dust_linear_workspace_bytes(T, d, n, V, K) bytes.
+ */
+size_t dust_linear_workspace_bytes(int64_t T, int64_t d, int64_t n, int64_t V, int64_t K);
+dust_status dust_estimate_linear(const float *u, const float *h, const float *x_res,
+                                 const uint16_t *w2, const uint16_t *w_head, const int32_t *labels,
+                                 int64_t T, int64_t d, int64_t n, int64_t V, int64_t K,
+                                 float sigma, float ln_eps, uint64_t seed, uint32_t layer,
+                                 uint32_t token_offset, uint32_t draw_offset,
+                                 float *grad_w, float *ghat, float *rewards,
+                                 void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -33,10 +33,12 @@ Readings where the pages are silent (each also listed in the design notes):
   baseline other than the clean loss; the tokens' losses are summed; noise
   a ~ N(0, I) scaled by sigma; interior block is pre-LN with no biases and no
   LN affine, exact-erf GELU, LN eps given; the interior downstream runs with
-  bf16 GEMM operands: the GELU output and the LN output are each rounded to
-  fp32 and then to bf16 (round to nearest even) -- the same fp32 -> bf16
-  decision the kernels take.  With ``quantize=False`` the downstream is exact
-  fp64 (used for the linearisation pins).
+  bf16 GEMM operands: the perturbed activation h + sigma a is an fp32 tensor
+  (rounded to fp32, like the cached h it perturbs); the GELU output and the LN
+  output are each rounded to fp32 and then to bf16 (round to nearest even) --
+  the bf16 decision is taken from an fp32 value, as in the kernels.  With
+  ``quantize=False`` the downstream is exact fp64 (used for the linearisation
+  pins).
 """
 from __future__ import annotations
 
@@ -240,6 +242,9 @@ def linear_estimate(h, x_res, w2_bits, w_head_bits, labels, K: int, sigma: float
             for i in range(K):
                 a[i, j] = noise(seed, layer, draw_offset + i, token_offset + int(t), n)
         hrows = np.concatenate([h[sel][None], h[sel][None] + sigma * a], axis=0).reshape(-1, n)
+        if quantize:
+            # the perturbed activation is an fp32 tensor, like the cached h it perturbs
+            hrows = hrows.astype(np.float32).astype(np.float64)
         xrows = np.broadcast_to(xr[sel][None], (K + 1, b, xr.shape[1])).reshape(-1, xr.shape[1])
         lrows = np.broadcast_to(lab[sel][None], (K + 1, b)).reshape(-1)
         ce = mlp_downstream_ce(hrows, xrows, lrows, w2, wh, eps, quantize).reshape(K + 1, b)

@@ -61,13 +61,11 @@ def lib():
         L.dust_estimate_head.restype = ctypes.c_int
         L.dust_estimate_head.argtypes = [_vp, ctypes.c_int, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _u64, _u32,
                                          _u32, _u32, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
-        if hasattr(L, "dust_estimate_linear"):
-            L.dust_linear_workspace_bytes.restype = ctypes.c_size_t
-            L.dust_linear_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _i64]
-            L.dust_estimate_linear.restype = ctypes.c_int
-            L.dust_estimate_linear.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32,
-                                               _f32, _u64, _u32, _u32, _u32, _vp, _vp, _vp, _vp, ctypes.c_size_t,
-                                               _vp]
+        L.dust_linear_workspace_bytes.restype = ctypes.c_size_t
+        L.dust_linear_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _i64]
+        L.dust_estimate_linear.restype = ctypes.c_int
+        L.dust_estimate_linear.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32,
+                                           _f32, _u64, _u32, _u32, _u32, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         _lib = L
     return _lib
 
@@ -188,4 +186,44 @@ def estimate_head(logits, x, labels, K: int, sigma: float, seed: int, layer: int
     _check(lib().dust_estimate_head(_p(logits), dt, _p(x), _p(labels), T, V, d, K, sigma, seed, layer,
                                     token_offset, draw_offset, _p(grad_w), _p(ghat), _p(rewards), _p(ws), nb,
                                     _stream(logits)))
+    return grad_w
+
+
+def linear_workspace_bytes(T: int, d: int, n: int, V: int, K: int) -> int:
+    return int(lib().dust_linear_workspace_bytes(T, d, n, V, K))
+
+
+def _bf16_bits(t, name):
+    if t.dtype == torch.bfloat16:
+        return t
+    if t.dtype in (torch.int16,) or str(t.dtype) == "torch.uint16":
+        return t
+    raise TypeError(f"{name} must hold bf16 values (torch.bfloat16 or 16-bit integer bits)")
+
+
+def estimate_linear(u, h, x_res, w2, w_head, labels, K: int, sigma: float, seed: int, layer: int,
+                    token_offset: int = 0, draw_offset: int = 0, *, ln_eps: float = 1e-5, grad_w=None,
+                    ghat=None, rewards=None, workspace=None):
+    """Interior MLP-linear estimator (W1 of a pre-LN block).  Returns grad_w [n,d].
+
+    u [T,d], h [T,n], x_res [T,d] fp32; w2 [d,n], w_head [V,d] bf16; labels [T] int32.
+    """
+    for t, nm in ((u, "u"), (h, "h"), (x_res, "x_res")):
+        _dev_tensor(t, nm, (torch.float32,))
+    _dev_tensor(labels, "labels", (torch.int32,))
+    for t, nm in ((w2, "w2"), (w_head, "w_head")):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+            raise TypeError(f"{nm} must be a contiguous CUDA (HIP) tensor")
+        _bf16_bits(t, nm)
+    T, d = u.shape
+    n = h.shape[1]
+    V = w_head.shape[0]
+    if h.shape[0] != T or x_res.shape != (T, d) or w2.shape != (d, n) or w_head.shape != (V, d) or labels.numel() != T:
+        raise ValueError("inconsistent shapes for the MLP-linear estimator")
+    if grad_w is None:
+        grad_w = torch.empty((n, d), dtype=torch.float32, device=u.device)
+    ws, nb = _workspace(lib().dust_linear_workspace_bytes(T, d, n, V, K), u.device, workspace)
+    _check(lib().dust_estimate_linear(_p(u), _p(h), _p(x_res), _p(w2), _p(w_head), _p(labels), T, d, n, V, K,
+                                      sigma, ln_eps, seed, layer, token_offset, draw_offset, _p(grad_w), _p(ghat),
+                                      _p(rewards), _p(ws), nb, _stream(u)))
     return grad_w

@@ -201,4 +201,69 @@ dust_status dust_estimate_head(const void* logits, int logits_dtype, const float
     return ok();
 }
 
+size_t dust_linear_workspace_bytes(int64_t T, int64_t d, int64_t n, int64_t V, int64_t K) {
+    if (T <= 0 || d <= 0 || n <= 0 || V <= 0 || K <= 0) return 0;
+    return dust::mlp_layout(T, d, n, V, K).total;
+}
+
+dust_status dust_estimate_linear(const float* u, const float* h, const float* x_res, const uint16_t* w2,
+                                 const uint16_t* w_head, const int32_t* labels, int64_t T, int64_t d, int64_t n,
+                                 int64_t V, int64_t K, float sigma, float ln_eps, uint64_t seed, uint32_t layer,
+                                 uint32_t token_offset, uint32_t draw_offset, float* grad_w, float* ghat,
+                                 float* rewards, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!u || !h || !x_res || !w2 || !w_head || !labels || !grad_w)
+        return fail(DUST_E_INVALID, "dust_estimate_linear: u, h, x_res, w2, w_head, labels and grad_w must be non-NULL");
+    if (!aligned16(u) || !aligned16(h) || !aligned16(x_res) || !aligned16(w2) || !aligned16(w_head) ||
+        !aligned16(labels) || !aligned16(grad_w) || (ghat && !aligned16(ghat)) || (rewards && !aligned16(rewards)) ||
+        (workspace && !aligned16(workspace)))
+        return fail(DUST_E_INVALID, "dust_estimate_linear: every pointer must be 16-byte aligned");
+    dust_status s = check_common(T, K, sigma, token_offset, draw_offset);
+    if (s != DUST_OK) return s;
+    if (d <= 0 || n <= 0 || V <= 0) return fail(DUST_E_INVALID, "dust_estimate_linear: d, n, V must be >= 1");
+    if (!std::isfinite(ln_eps) || !(ln_eps > 0.f))
+        return fail(DUST_E_INVALID, "dust_estimate_linear: ln_eps must be finite and > 0: got %g", (double)ln_eps);
+    if (d != 256 && d != 512) return fail(DUST_E_UNSUPPORTED, "dust_estimate_linear: d must be 256 or 512 (got %lld)", (long long)d);
+    if (n % 32 != 0) return fail(DUST_E_UNSUPPORTED, "dust_estimate_linear: n must be a multiple of 32 (got %lld)", (long long)n);
+    if (V > (int64_t)INT32_MAX / 2 || n > (int64_t)INT32_MAX / 4)
+        return fail(DUST_E_UNSUPPORTED, "dust_estimate_linear: V or n too large");
+    if (T * (K + 1) > ((int64_t)1 << 40)) return fail(DUST_E_UNSUPPORTED, "dust_estimate_linear: T*(K+1) too large");
+    const dust::MlpLayout L = dust::mlp_layout(T, d, n, V, K);
+    if (workspace == nullptr || workspace_bytes < L.total)
+        return fail(DUST_E_WORKSPACE, "dust_estimate_linear: workspace of %zu bytes needed, %zu given", L.total,
+                    workspace ? workspace_bytes : (size_t)0);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    s = check_labels(labels, T, V, st);
+    if (s != DUST_OK) return s;
+    dust::MlpArgs A{};
+    A.u = u;
+    A.h = h;
+    A.x_res = x_res;
+    A.w2 = w2;
+    A.w_head = w_head;
+    A.labels = labels;
+    A.rewards = rewards;
+    A.T = (int32_t)T;
+    A.d = (int32_t)d;
+    A.n = (int32_t)n;
+    A.V = (int32_t)V;
+    A.K = (int32_t)K;
+    A.sigma = sigma;
+    A.ln_eps = ln_eps;
+    A.gscale = (float)(-1.0 / ((double)K * (double)sigma));
+    A.k0 = (uint32_t)seed;
+    A.k1 = (uint32_t)(seed >> 32);
+    A.layer = layer;
+    A.tok0 = token_offset;
+    A.draw0 = draw_offset;
+    A.stage_event = g_stage_event[0];
+    if (env_flag("DUST_LOG"))
+        std::fprintf(stderr, "[dust] linear T=%lld d=%lld n=%lld V=%lld K=%lld chunk=%lld vtiles=%d ws=%zu\n",
+                     (long long)T, (long long)d, (long long)n, (long long)V, (long long)K, (long long)L.chunk, L.nvt,
+                     L.total);
+    hipError_t e = dust::launch_mlp(A, L, static_cast<unsigned char*>(workspace), ghat, grad_w, st);
+    if (e != hipSuccess) return device_fail("dust_estimate_linear: launch", e);
+    if ((e = record_stage(1, st)) != hipSuccess) return device_fail("dust_estimate_linear: stage event", e);
+    return ok();
+}
+
 }  // extern "C"

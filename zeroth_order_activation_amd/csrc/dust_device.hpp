@@ -13,6 +13,8 @@
 
 namespace dust {
 
+constexpr float kLog2eF = 1.4426950408889634f;
+
 constexpr uint32_t kPhiloxM0 = 0xD2511F53u;
 constexpr uint32_t kPhiloxM1 = 0xCD9E8D57u;
 constexpr uint32_t kPhiloxW0 = 0x9E3779B9u;

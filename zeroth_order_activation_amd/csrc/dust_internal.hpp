@@ -43,4 +43,29 @@ size_t outer_workspace_bytes(int64_t T, int64_t n, int64_t d);
 hipError_t launch_outer(const float* ghat, const float* x, int64_t T, int64_t n, int64_t d, float* grad_w,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+// ---- interior MLP linear ------------------------------------------------
+struct MlpArgs {
+    const float* u;          // [T,d] input of W1 (the x_t of G_W1)
+    const float* h;          // [T,n] cached W1 output
+    const float* x_res;      // [T,d] residual stream
+    const uint16_t* w2;      // [d,n] bf16
+    const uint16_t* w_head;  // [V,d] bf16
+    const int32_t* labels;   // [T]
+    float* rewards;          // [K,T] out or null
+    int32_t T, d, n, V, K;
+    float sigma, ln_eps, gscale;
+    uint32_t k0, k1, layer, tok0, draw0;
+    hipEvent_t stage_event;  // recorded after g_hat, before the outer product (or null)
+};
+
+struct MlpLayout {
+    int64_t chunk;  // rows of recomputed downstream per pass
+    int nvt;        // vocabulary tiles
+    size_t off_f, off_part, off_zy, off_ce, off_ghat, off_outer, total;
+};
+
+MlpLayout mlp_layout(int64_t T, int64_t d, int64_t n, int64_t V, int64_t K);
+hipError_t launch_mlp(const MlpArgs& args, const MlpLayout& layout, unsigned char* workspace, float* ghat_user,
+                      float* grad_w, hipStream_t stream);
+
 }  // namespace dust

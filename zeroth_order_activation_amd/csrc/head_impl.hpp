@@ -25,7 +25,7 @@
 
 namespace dust {
 
-constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLog2e = kLog2eF;
 
 template <int LT>
 __device__ __forceinline__ f32x4 load_quad(const void* row, int q, int V, bool vec) {

@@ -1,0 +1,501 @@
+// Interior MLP-linear estimator: W1 of a pre-LN MLP block is perturbed and
+// the cached downstream is recomputed per draw.
+//
+// Method: TL;DR page "Dust: zeroth-order Transformer pretraining without
+// backprop", section 1 ("activation-space perturbation", "credit assignment
+// without backprop"): noise sigma*a on the output h_t = W1 u_t of the linear
+// layer, independently per token and draw; reward = reduction of that token's
+// LM loss; g_hat_t = -(1/(K sigma)) sum_i r a; G_W1 = sum_t g_hat_t u_t^T.
+// News article (tahou.com), mechanism paragraph: the unperturbed
+// intermediates are cached and only what the perturbation changes is
+// recomputed -- here GELU -> W2 -> residual -> LayerNorm -> LM head -> CE.
+//
+// Every (token, draw) pair is one row of the recomputed downstream.  Rows are
+// numbered globally: g < T are the clean rows (a = 0, giving CE0), g = T(1+i)+t
+// is draw i of token t.  Rows are processed in chunks; per chunk:
+//   gemm1   F[g] = bf16(LN(x_t + W2 bf16(GELU(h_t + sigma a))))      (MFMA bf16)
+//   gemm2   per (vocab tile, row): max and sum-exp of z = W_head F[g], and the
+//           label logit z[y_t]                                       (MFMA bf16)
+//   combine CE[g] = log-sum-exp over the tiles - z[y_t]
+// then once: reduce (noise regenerated) -> g_hat, and the outer product.
+//
+// Both GEMMs compute the transposed product D[feature][row] = W . X^T: the
+// weight rows are the MFMA A operand and the token-rows the B operand, so each
+// lane ends up holding many features of few rows, and the per-row reductions
+// of the epilogues (LayerNorm over d, log-sum-exp over V) stay mostly in-lane.
+//
+// v_mfma_f32_32x32x16_bf16 operand layout (checked on the device): A[i][k] in
+// lane i + 32*(k/8) element k%8; B[k][j] in lane j + 32*(k/8) element k%8;
+// D[i][j] in lane j + 32*((i/4)%2), register (i%4) + 4*(i/8).
+#include "dust_device.hpp"
+#include "dust_internal.hpp"
+
+namespace dust {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, const f32x16_t& c) {
+    bf16x8_t av, bv;
+    __builtin_memcpy(&av, &a, 16);
+    __builtin_memcpy(&bv, &b, 16);
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, c, 0, 0, 0);
+}
+
+// Row of the D layout held by register r of a lane (within a 32x32 block).
+__device__ __forceinline__ int drow(int r, int lane) { return (r & 3) + 8 * (r >> 2) + 4 * (lane >> 5); }
+
+// GELU(x) = x Phi(x) (exact erf form), rounded to bf16 (nearest even).  The
+// rounding decision only depends on the fp32 value when that value is not
+// within a few ulps of a bf16 tie; in that rare case (~2^-11 of inputs) the
+// GELU is re-evaluated in fp64 and rounded to fp32 once, so the decision is
+// the one the correctly rounded fp32 value takes.
+__device__ __forceinline__ uint16_t gelu_bf16(float x) {
+    float g = 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+    const int low = (int)(__float_as_uint(g) & 0xFFFFu);
+    if (__builtin_expect(abs(low - 0x8000) <= 16, 0)) {
+        const double xd = (double)x;
+        g = (float)(0.5 * xd * (1.0 + erf(xd * 0.70710678118654752440)));
+    }
+    return f32_to_bf16_rne(g);
+}
+
+// ---------------------------------------------------------------------------
+// gemm1: F = bf16(LN(x + W2 . bf16(GELU(h + sigma a))))
+// Workgroup: 64 token-rows x all D features, 8 waves; wave w owns features
+// [w*D/8, (w+1)*D/8).  The B operand (64 rows x 32 channels per step) is
+// generated in the prologue -- one channel quad per thread -- and staged in
+// LDS; W2 fragments are read straight from global memory (W2 is small and
+// stays in L2).  The MFMA accumulator restarts every G1_FLUSH k-steps and is
+// added into a separate fp32 total: the partial sums stay small, which keeps
+// the accumulation error of W2 m (and with it the rate of bf16 rounding
+// decisions of the LayerNorm output that it could flip) low.
+// ---------------------------------------------------------------------------
+constexpr int G1_ROWS = 64;
+constexpr int G1_KS = 32;                   // channels per k-step
+constexpr int G1_LDS_STRIDE = G1_KS + 8;    // bf16 elements per LDS row (80 bytes: conflict-free b128 reads)
+constexpr int G1_FLUSH = 4;                 // k-steps (128 channels) per accumulator restart
+constexpr int G1_WAVES = 8;
+
+__device__ __forceinline__ double red_sum(const double (*red)[G1_ROWS], int lr) {
+    double s = 0.0;
+#pragma unroll
+    for (int w = 0; w < G1_WAVES; ++w) s += red[w][lr];
+    return s;
+}
+
+template <int D>
+__global__ void __launch_bounds__(512) mlp_gemm1_kernel(MlpArgs A, int64_t g0, int64_t nrows, uint16_t* __restrict__ F) {
+    constexpr int DW = D / G1_WAVES;  // features per wave
+    constexpr int NDB = DW / 32;      // 32-feature blocks per wave
+    __shared__ __align__(16) uint16_t Bs[2][G1_ROWS * G1_LDS_STRIDE];
+    __shared__ double red[G1_WAVES][G1_ROWS];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int64_t rbase = (int64_t)blockIdx.x * G1_ROWS;  // chunk-local row of row 0
+    const int n = A.n;
+    const int T = A.T;
+
+    // generation mapping: one channel quad per thread per k-step
+    const int gen_row = tid >> 3, gen_q = tid & 7;
+    const int64_t gen_lr = rbase + gen_row;
+    const bool gen_valid = gen_lr < nrows;
+    const int64_t gen_g = g0 + (gen_valid ? gen_lr : 0);
+    const bool gen_clean = gen_g < T;
+    const int64_t gen_t = gen_g % T;
+    const uint32_t gen_draw = gen_clean ? 0u : A.draw0 + (uint32_t)(gen_g / T - 1);
+    const float* hrow = A.h + gen_t * n;
+
+    auto generate = [&](int ks) -> uint2 {
+        const int c0 = ks * G1_KS + 4 * gen_q;
+        float hv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (gen_valid) {
+            const float4 h4 = *reinterpret_cast<const float4*>(hrow + c0);
+            hv[0] = h4.x; hv[1] = h4.y; hv[2] = h4.z; hv[3] = h4.w;
+            if (!gen_clean) {
+                const f32x4 g = gauss4(A.tok0 + (uint32_t)gen_t, (uint32_t)(c0 >> 2), gen_draw, A.layer, A.k0, A.k1);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) hv[c] = fmaf(A.sigma, g.v[c], hv[c]);
+            }
+        }
+        uint16_t b[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) b[c] = gen_valid ? gelu_bf16(hv[c]) : (uint16_t)0;
+        uint2 out;
+        out.x = (uint32_t)b[0] | ((uint32_t)b[1] << 16);
+        out.y = (uint32_t)b[2] | ((uint32_t)b[3] << 16);
+        return out;
+    };
+    auto store_slab = [&](int buf, uint2 v) {
+        *reinterpret_cast<uint2*>(&Bs[buf][gen_row * G1_LDS_STRIDE + 4 * gen_q]) = v;
+    };
+
+    f32x16_t acc[NDB][2], tot[NDB][2];
+#pragma unroll
+    for (int i = 0; i < NDB; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) { acc[i][j][r] = 0.f; tot[i][j][r] = 0.f; }
+
+    const int nks = n / G1_KS;
+    store_slab(0, generate(0));
+    __syncthreads();
+    const uint16_t* w2 = A.w2;
+    for (int ks = 0; ks < nks; ++ks) {
+        const int buf = ks & 1;
+        // W2 fragments for this k-step: feature f = w*DW + db*32 + lane%32, channels k0 + 16*kk + 8*(lane/32)
+        uint4 af[NDB][2];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const int f = w * DW + db * 32 + (lane & 31);
+                const int k = ks * G1_KS + kk * 16 + 8 * (lane >> 5);
+                af[db][kk] = *reinterpret_cast<const uint4*>(w2 + (int64_t)f * n + k);
+            }
+        uint2 nxt = make_uint2(0, 0);
+        if (ks + 1 < nks) nxt = generate(ks + 1);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            uint4 bf[2];
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+                bf[rb] = *reinterpret_cast<const uint4*>(
+                    &Bs[buf][(rb * 32 + (lane & 31)) * G1_LDS_STRIDE + kk * 16 + 8 * (lane >> 5)]);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb) acc[db][rb] = mfma32(af[db][kk], bf[rb], acc[db][rb]);
+        }
+        if ((ks + 1) % G1_FLUSH == 0 || ks + 1 == nks) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) { tot[db][rb][r] += acc[db][rb][r]; acc[db][rb][r] = 0.f; }
+        }
+        if (ks + 1 < nks) store_slab(buf ^ 1, nxt);
+        __syncthreads();
+    }
+
+    // ---- epilogue: residual add, LayerNorm over D, bf16 ---------------------
+    // lane holds rows j = rb*32 + lane%32 (rb = 0,1); for each, features
+    // w*DW + db*32 + drow(r, lane).  y = x + o is formed in fp32; the LayerNorm
+    // statistics and the normalised value are computed in fp64 and rounded to
+    // fp32 once before the bf16 rounding.
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const int lr = rb * 32 + (lane & 31);
+        const int64_t row = rbase + lr;
+        const bool valid = row < nrows;
+        const int64_t t = (g0 + (valid ? row : 0)) % T;
+        double s = 0.0;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int f = w * DW + db * 32 + 8 * r4 + 4 * (lane >> 5);
+                const float4 xv = *reinterpret_cast<const float4*>(A.x_res + t * D + f);
+                tot[db][rb][4 * r4 + 0] += xv.x;
+                tot[db][rb][4 * r4 + 1] += xv.y;
+                tot[db][rb][4 * r4 + 2] += xv.z;
+                tot[db][rb][4 * r4 + 3] += xv.w;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) s += (double)tot[db][rb][4 * r4 + c];
+            }
+        s += __shfl_xor(s, 32, 64);
+        if (lane < 32) red[w][lr] = s;
+    }
+    __syncthreads();
+    double mean[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const int lr = rb * 32 + (lane & 31);
+        mean[rb] = red_sum(red, lr) * (1.0 / D);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const int lr = rb * 32 + (lane & 31);
+        double s = 0.0;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const double dv = (double)tot[db][rb][r] - mean[rb];
+                s = fma(dv, dv, s);
+            }
+        s += __shfl_xor(s, 32, 64);
+        if (lane < 32) red[w][lr] = s;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const int lr = rb * 32 + (lane & 31);
+        const int64_t row = rbase + lr;
+        const double var = red_sum(red, lr) * (1.0 / D);
+        const double rstd = 1.0 / sqrt(var + (double)A.ln_eps);
+        if (row >= nrows) continue;
+        uint16_t* frow = F + row * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int f = w * DW + db * 32 + 8 * r4 + 4 * (lane >> 5);
+                uint16_t b[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    b[c] = f32_to_bf16_rne((float)(((double)tot[db][rb][4 * r4 + c] - mean[rb]) * rstd));
+                uint2 pk;
+                pk.x = (uint32_t)b[0] | ((uint32_t)b[1] << 16);
+                pk.y = (uint32_t)b[2] | ((uint32_t)b[3] << 16);
+                *reinterpret_cast<uint2*>(frow + f) = pk;
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// gemm2: per (vocab tile of 128, row): partial max / sum-exp of z = W_head F,
+// and the label logit.  Workgroup tile 128 vocab x 128 rows, 4 waves of 64x64,
+// both operands staged through LDS in 32-wide k-steps (double-buffered).
+// ---------------------------------------------------------------------------
+constexpr int G2_TV = 128, G2_TR = 128, G2_KS = 32;
+constexpr int G2_STRIDE = G2_KS + 8;  // bf16 per LDS row (80 bytes)
+
+__global__ void __launch_bounds__(256) mlp_gemm2_kernel(MlpArgs A, int64_t g0, int64_t nrows, int nvt,
+                                                         const uint16_t* __restrict__ F, float2* __restrict__ part,
+                                                         float* __restrict__ zy) {
+    __shared__ __align__(16) uint16_t As[2][G2_TV * G2_STRIDE];
+    __shared__ __align__(16) uint16_t Bs[2][G2_TR * G2_STRIDE];
+    __shared__ float2 red[2][G2_TR];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wv = w & 1, wr = w >> 1;
+    // vocab tile fastest: with a tile count that is a multiple of 8, each XCD
+    // keeps revisiting the same eighth of W_head, which then stays in its L2.
+    const int vt = blockIdx.x % nvt;
+    const int64_t rt = blockIdx.x / nvt;
+    const int v0 = vt * G2_TV;
+    const int64_t r0 = rt * G2_TR;
+    const int D = A.d, V = A.V;
+
+    // load mapping: 128 rows x 32 k = 512 16-byte pieces per operand -> 2 per thread
+    auto load = [&](int ks, uint4 (&ra)[2], uint4 (&rb)[2]) {
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int pi = tid + 256 * jj;
+            const int row = pi >> 2, piece = pi & 3;
+            const int k = ks * G2_KS + 8 * piece;
+            const int v = v0 + row;
+            ra[jj] = v < V ? *reinterpret_cast<const uint4*>(A.w_head + (int64_t)v * D + k) : make_uint4(0, 0, 0, 0);
+            const int64_t rr = r0 + row;
+            rb[jj] = rr < nrows ? *reinterpret_cast<const uint4*>(F + rr * D + k) : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto store = [&](int buf, const uint4 (&ra)[2], const uint4 (&rb)[2]) {
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int pi = tid + 256 * jj;
+            const int row = pi >> 2, piece = pi & 3;
+            *reinterpret_cast<uint4*>(&As[buf][row * G2_STRIDE + 8 * piece]) = ra[jj];
+            *reinterpret_cast<uint4*>(&Bs[buf][row * G2_STRIDE + 8 * piece]) = rb[jj];
+        }
+    };
+
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    const int nks = D / G2_KS;
+    {
+        uint4 ra[2], rb[2];
+        load(0, ra, rb);
+        store(0, ra, rb);
+    }
+    __syncthreads();
+    for (int ks = 0; ks < nks; ++ks) {
+        const int buf = ks & 1;
+        uint4 ra[2], rb[2];
+        if (ks + 1 < nks) load(ks + 1, ra, rb);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            uint4 af[2], bfr[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                af[i] = *reinterpret_cast<const uint4*>(
+                    &As[buf][(wv * 64 + i * 32 + (lane & 31)) * G2_STRIDE + kk * 16 + 8 * (lane >> 5)]);
+                bfr[i] = *reinterpret_cast<const uint4*>(
+                    &Bs[buf][(wr * 64 + i * 32 + (lane & 31)) * G2_STRIDE + kk * 16 + 8 * (lane >> 5)]);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+        }
+        if (ks + 1 < nks) store(buf ^ 1, ra, rb);
+        __syncthreads();
+    }
+
+    // ---- epilogue: per row, max and sum-exp over this tile's vocabulary ------
+    // lane holds rows j = wr*64 + rb*32 + lane%32, vocab v0 + wv*64 + vb*32 + drow(r, lane)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const int lrow = wr * 64 + rb * 32 + (lane & 31);
+        const int64_t row = r0 + lrow;
+        float m = -__builtin_inff();
+#pragma unroll
+        for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int v = v0 + wv * 64 + vb * 32 + drow(r, lane);
+                if (v < V) m = fmaxf(m, acc[vb][rb][r]);
+            }
+        const float m2 = fmaxf(m, __shfl_xor(m, 32, 64));
+        float s = 0.f;
+        const float ml2 = m2 * kLog2eF;
+#pragma unroll
+        for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int v = v0 + wv * 64 + vb * 32 + drow(r, lane);
+                if (v < V) s += __builtin_amdgcn_exp2f(fmaf(acc[vb][rb][r], kLog2eF, -ml2));
+            }
+        s += __shfl_xor(s, 32, 64);
+        if (lane < 32) red[wv][lrow] = make_float2(m2, s);
+        // label logit: exactly one lane of the grid holds z[y] for this row
+        if (row < nrows) {
+            const int64_t t = (g0 + row) % A.T;
+            const int y = A.labels[t];
+#pragma unroll
+            for (int vb = 0; vb < 2; ++vb) {
+                const int ii = y - (v0 + wv * 64 + vb * 32);
+                if (ii >= 0 && ii < 32 && ((ii >> 2) & 1) == (lane >> 5)) {
+                    const int rr = (ii & 3) + 4 * (ii >> 3);
+                    float val = 0.f;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) val = (r == rr) ? acc[vb][rb][r] : val;
+                    zy[row] = val;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    if (tid < G2_TR) {
+        const int64_t row = r0 + tid;
+        if (row < nrows) {
+            const float2 a = red[0][tid], b = red[1][tid];
+            const float m = fmaxf(a.x, b.x);
+            float s = 0.f;
+            if (a.y > 0.f) s += a.y * __builtin_amdgcn_exp2f((a.x - m) * kLog2eF);
+            if (b.y > 0.f) s += b.y * __builtin_amdgcn_exp2f((b.x - m) * kLog2eF);
+            part[(int64_t)vt * nrows + row] = make_float2(m, s);
+        }
+    }
+}
+
+// CE[g0 + row] = max + log(sum) - z_y, combining the vocabulary tiles in order.
+__global__ void __launch_bounds__(256) mlp_combine_kernel(int64_t g0, int64_t nrows, int nvt,
+                                                          const float2* __restrict__ part,
+                                                          const float* __restrict__ zy, float* __restrict__ ce) {
+    const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (row >= nrows) return;
+    float m = -__builtin_inff();
+    for (int vt = 0; vt < nvt; ++vt) m = fmaxf(m, part[(int64_t)vt * nrows + row].x);
+    float s = 0.f;
+    for (int vt = 0; vt < nvt; ++vt) {
+        const float2 p = part[(int64_t)vt * nrows + row];
+        if (p.y > 0.f) s += p.y * __builtin_amdgcn_exp2f((p.x - m) * kLog2eF);
+    }
+    ce[g0 + row] = m + __logf(s) - zy[row];
+}
+
+// g_hat_t = -(1/(K sigma)) sum_i (CE0_t - CE_{t,i}) a_{t,i}, noise regenerated;
+// one thread per (token, channel quad); rewards written by the quad-0 threads.
+__global__ void __launch_bounds__(256) mlp_reduce_kernel(MlpArgs A, const float* __restrict__ ce, float* __restrict__ ghat) {
+    const int nq = A.n >> 2;
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= (int64_t)A.T * nq) return;
+    const int t = (int)(gid / nq);
+    const int q = (int)(gid - (int64_t)t * nq);
+    const float c0 = ce[t];
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    const uint32_t tok = A.tok0 + (uint32_t)t;
+    for (int i = 0; i < A.K; ++i) {
+        const float r = c0 - ce[(int64_t)A.T * (i + 1) + t];
+        const f32x4 g = gauss4(tok, (uint32_t)q, A.draw0 + (uint32_t)i, A.layer, A.k0, A.k1);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] = fmaf(r, g.v[c], acc[c]);
+    }
+    *reinterpret_cast<float4*>(ghat + (int64_t)t * A.n + 4 * q) =
+        make_float4(acc[0] * A.gscale, acc[1] * A.gscale, acc[2] * A.gscale, acc[3] * A.gscale);
+    if (q == 0 && A.rewards)
+        for (int i = 0; i < A.K; ++i) A.rewards[(int64_t)i * A.T + t] = c0 - ce[(int64_t)A.T * (i + 1) + t];
+}
+
+// ---------------------------------------------------------------------------
+size_t mlp_chunk_rows(int64_t T, int64_t K, int64_t d) {
+    // F of one chunk (bf16 rows of d) kept to at most 512 MiB; a whole number of token blocks.
+    const int64_t total = T * (K + 1);
+    int64_t cap = ((int64_t)512 << 20) / (2 * d);
+    cap = cap / T * T;
+    if (cap < T) cap = T;
+    return (size_t)(total < cap ? total : cap);
+}
+
+static size_t al256(size_t v) { return (v + 255) / 256 * 256; }
+
+MlpLayout mlp_layout(int64_t T, int64_t d, int64_t n, int64_t V, int64_t K) {
+    MlpLayout L{};
+    L.chunk = (int64_t)mlp_chunk_rows(T, K, d);
+    L.nvt = (int)((V + G2_TV - 1) / G2_TV);
+    size_t off = 0;
+    L.off_f = off;    off += al256((size_t)L.chunk * d * 2);
+    L.off_part = off; off += al256((size_t)L.chunk * L.nvt * sizeof(float2));
+    L.off_zy = off;   off += al256((size_t)L.chunk * sizeof(float));
+    L.off_ce = off;   off += al256((size_t)T * (K + 1) * sizeof(float));
+    L.off_ghat = off; off += al256((size_t)T * n * sizeof(float));
+    L.off_outer = off;
+    off += outer_workspace_bytes(T, n, d);
+    L.total = off;
+    return L;
+}
+
+hipError_t launch_mlp(const MlpArgs& A, const MlpLayout& L, unsigned char* ws, float* ghat_user, float* grad_w,
+                      hipStream_t stream) {
+    uint16_t* F = reinterpret_cast<uint16_t*>(ws + L.off_f);
+    float2* part = reinterpret_cast<float2*>(ws + L.off_part);
+    float* zy = reinterpret_cast<float*>(ws + L.off_zy);
+    float* ce = reinterpret_cast<float*>(ws + L.off_ce);
+    float* ghat = ghat_user ? ghat_user : reinterpret_cast<float*>(ws + L.off_ghat);
+    const int64_t total = (int64_t)A.T * (A.K + 1);
+    hipError_t e = hipSuccess;
+    for (int64_t g0 = 0; g0 < total; g0 += L.chunk) {
+        const int64_t nrows = (total - g0) < L.chunk ? (total - g0) : L.chunk;
+        const unsigned b1 = (unsigned)((nrows + G1_ROWS - 1) / G1_ROWS);
+        if (A.d == 512)
+            hipLaunchKernelGGL(mlp_gemm1_kernel<512>, dim3(b1), dim3(64 * G1_WAVES), 0, stream, A, g0, nrows, F);
+        else
+            hipLaunchKernelGGL(mlp_gemm1_kernel<256>, dim3(b1), dim3(64 * G1_WAVES), 0, stream, A, g0, nrows, F);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        const int64_t nrt = (nrows + G2_TR - 1) / G2_TR;
+        hipLaunchKernelGGL(mlp_gemm2_kernel, dim3((unsigned)(nrt * L.nvt)), dim3(256), 0, stream, A, g0, nrows, L.nvt,
+                           F, part, zy);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(mlp_combine_kernel, dim3((unsigned)((nrows + 255) / 256)), dim3(256), 0, stream, g0, nrows,
+                           L.nvt, part, zy, ce);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    const int64_t threads = (int64_t)A.T * (A.n / 4);
+    hipLaunchKernelGGL(mlp_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, A, ce, ghat);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (A.stage_event && (e = hipEventRecord(A.stage_event, stream)) != hipSuccess) return e;
+    return launch_outer(ghat, A.u, A.T, A.n, A.d, grad_w, ws + L.off_outer, L.total - L.off_outer, stream);
+}
+
+}  // namespace dust
