@@ -1,23 +1,27 @@
 """Benchmark of the Dust gradient estimator on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--draws K5]
+                    [--no-cpu-baseline]
 
-A step is one full estimate (every stage of the hot path) over one batch of
-synthetic inputs already resident in HBM: for the LM-head workloads, the
-per-token estimator kernel (noise, clean statistics, perturbed losses,
-rewards, reward-weighted noise sum) followed by the weight-gradient outer
-product.  The default workload is the fp32 LM head with T=4096 tokens (2x2048),
-d=512, V=8192, K=256 draws, sigma=1e-2.
+A step is one full estimate -- every stage of the hot path -- over one batch of
+synthetic inputs already resident in HBM:
+  * LM-head workloads (1, 2, 4): the per-token estimator kernel (noise, clean
+    statistics, perturbed losses, rewards, reward-weighted noise sum) and the
+    weight-gradient outer product;
+  * MLP-linear workloads (3, 5): GEMM1 with the noise/GELU prologue and the
+    LayerNorm epilogue, GEMM2 with the log-sum-exp epilogue, the loss combine,
+    the noise-regenerating reduce and the outer product.
+The default workload is the fp32 LM head with T=4096 tokens (2x2048), d=512,
+V=8192, K=256 draws, sigma=1e-2.
 
-Prints one JSON line: token-draws/s (T*K per step), the per-stage times, the
-roofline of the dominant kernel and the oracle timed on the host cores on a
-bounded sample of the same workload.
+Prints one JSON line: token-draws/s (T*K per step), per-stage times from HIP
+events on the call's stream, the roofline of the dominant kernel and the oracle
+timed on the host cores on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
 import sys
 import time
@@ -29,22 +33,27 @@ sys.path.insert(0, ROOT)
 
 # MI355X published peaks and unit counts.
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 N_CU, CLOCK_GHZ, LANES_PER_CU = 256, 2.4, 64
-VALU_PEAK_GSLOT = N_CU * LANES_PER_CU * CLOCK_GHZ  # 39321.6 G lane-slots/s (full-rate, unpacked)
+VALU_PEAK_GSLOT = N_CU * LANES_PER_CU * CLOCK_GHZ  # 39321.6 G lane-slots/s (one full-rate op per lane per clock)
 
 # Algorithmic VALU work of one channel-draw of the head estimator, in full-rate
-# lane-slots (a quarter-rate instruction counts 4): Philox4x32-10 gives four
-# channels for 10 rounds x (2 32x32->64 products at 4 slots + 2 three-way xors)
-# = 100 slots -> 25; Box-Muller gives two channels for 4 transcendentals (log2,
-# sqrt, sin, cos) at 4 slots + 2 int->float conversions + 2 scalings + 2
-# products = 22 -> 11; the perturbed-loss term sum_v p_v expm1(sigma a_v) with
-# a degree-5 polynomial = 5 fma + 1 mul + 1 fma = 7; the running sum r*a = 1.
-SLOTS_PER_CHANNEL_DRAW = 25 + 11 + 7 + 1
+# lane-slots, with the gfx950 issue costs measured by a microbenchmark
+# (v_mad_u64_u32 full rate; log2/exp2/sqrt/sin/cos half rate, 2 slots):
+#   Philox4x32-10: 10 rounds x (2 v_mad_u64_u32 + 2 three-way xors) = 40 slots per 4 channels -> 10
+#   Box-Muller: per 2 channels 2 int->float + 2 scalings + log2 (2) + scale + sqrt (2)
+#               + sin (2) + cos (2) + 2 products = 15 slots -> 7.5
+#   loss term p_v expm1(sigma a_v): 4 fma (Horner) + 1 mul + 1 fma = 6
+#   running sum r*a: 1
+SLOTS_PER_CHANNEL_DRAW = 10 + 7.5 + 6 + 1
 
 WORKLOAD_NAMES = {
     1: "LM-head estimator fp32 logits: T=256, d=64, V=512, K=64, sigma=1e-2, uniform labels",
     2: "LM-head estimator fp32 logits: T=4096 (2x2048), d=512, V=8192, K=256, sigma=1e-2, Zipf(1.1) labels",
+    3: "MLP-linear (W1) estimator, bf16 downstream GELU-W2-residual-LayerNorm-head: T=4096, d=512, n=2048, "
+       "V=8192, K=64, sigma=1e-2, Zipf(1.1) labels",
     4: "243M-shape LM head bf16 logits: T=8192 (4x2048), d=1024, V=50304, K=16, sigma=5e-3, Zipf(1.1) labels",
+    5: "MLP-linear population sweep point: T=2048, d=512, n=2048, V=8192, sigma=1e-2, K={K}",
 }
 
 
@@ -54,12 +63,13 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=2, choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--draws", type=int, default=1024, help="K for workload 5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     return ap.parse_args()
 
 
-def cpu_baseline(case, target_s):
+def cpu_baseline_head(case, target_s):
     """The oracle, as it stands, on a bounded sample of tokens of the same workload."""
     import oracle
 
@@ -74,10 +84,138 @@ def cpu_baseline(case, target_s):
         if el >= target_s / 3 or ntok >= case["T"]:
             break
         ntok = min(case["T"], int(ntok * max(2.0, target_s / max(el, 1e-3))))
-    threads = oracle.num_threads()
-    return {"value": ntok * K / el, "unit": "token-draws/s", "cores": threads, "kind": "oracle",
+    return {"value": ntok * K / el, "unit": "token-draws/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"first {ntok} of {case['T']} tokens x all {K} draws (full vocabulary), "
                       f"fp64 C loops, {el:.1f} s"}
+
+
+def cpu_baseline_linear(case, K, target_s):
+    """The oracle on the first tokens of the workload, all their draws."""
+    import oracle
+
+    ntok = 2
+    while True:
+        t0 = time.perf_counter()
+        oracle.linear_estimate(case["h"], case["x_res"], case["w2_bf16"], case["w_head_bf16"], case["labels"], K,
+                               case["sigma"], case["ln_eps"], case["seed_noise"], case["layer"],
+                               tokens=np.arange(ntok))
+        el = time.perf_counter() - t0
+        if el >= target_s / 3 or ntok >= case["T"]:
+            break
+        ntok = min(case["T"], int(ntok * max(2.0, target_s / max(el, 1e-3))))
+    return {"value": ntok * K / el, "unit": "token-draws/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"first {ntok} of {case['T']} tokens x all {K} draws (clean + perturbed downstream rows), "
+                      f"numpy fp64 with C noise, {el:.1f} s"}
+
+
+def timed(dust, torch, step, nstage, steps):
+    """Run ``steps`` steps with HIP events: [start, stage events 0..nstage-1] per step."""
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(1 + nstage)] for _ in range(steps)]
+    for e_list in ev:  # torch creates the underlying hipEvent at its first record
+        for e in e_list:
+            e.record(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        ev[k][0].record(stream)
+        for s in range(nstage):
+            dust.set_stage_event(s, ev[k][1 + s])
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for s in range(nstage):
+        dust.set_stage_event(s, None)
+    return wall, ev
+
+
+def run_head(args, c, dust, torch):
+    T, V, d, K, sigma = c["T"], c["V"], c["d"], c["K"], c["sigma"]
+    if "logits" in c:
+        z = torch.from_numpy(c["logits"]).cuda()
+        dtype = "f32"
+    else:
+        z = torch.from_numpy(c["logits_bf16"].view(np.int16)).cuda().view(torch.bfloat16)
+        dtype = "f32 (bf16 cached logits)"
+    x = torch.from_numpy(c["x"]).cuda()
+    y = torch.from_numpy(c["labels"]).cuda()
+    gw = torch.empty((V, d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(dust.head_workspace_bytes(T, V, d, K), dtype=torch.uint8, device="cuda")
+
+    def step():
+        dust.estimate_head(z, x, y, K, sigma, c["seed_noise"], c["layer"], grad_w=gw, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    wall, ev = timed(dust, torch, step, 2, args.steps)
+    est_ms = float(np.mean([dust.event_elapsed_ms(e[0], e[1]) for e in ev]))
+    outer_ms = float(np.mean([dust.event_elapsed_ms(e[1], e[2]) for e in ev]))
+    ms_per_step = wall * 1e3 / args.steps
+    achieved = T * K * V * SLOTS_PER_CHANNEL_DRAW / (est_ms / 1e3) / 1e9
+    lb = 4 if "logits" in c else 2
+    # bytes every step must move at least once: logits read, g_hat written and read back,
+    # x read, grad_w written, labels read
+    alg_bytes = T * V * lb + 2 * T * V * 4 + T * d * 4 + V * d * 4 + T * 4
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", f"traffic_head_workload{args.workload}.json")
+    if os.path.exists(tfile):
+        with open(tfile) as f:
+            traffic = json.load(f).get("bytes_per_launch")
+    out = {
+        "dtype": dtype,
+        "stages_ms": {"estimator": est_ms, "outer_product": outer_ms},
+        "roofline": {"bound": "alu", "kernel": "head_estimate_kernel", "achieved": achieved,
+                     "peak": VALU_PEAK_GSLOT, "unit": "G lane-slots/s", "frac": achieved / VALU_PEAK_GSLOT,
+                     "traffic": traffic, "slots_per_channel_draw": SLOTS_PER_CHANNEL_DRAW,
+                     "channel_draws_per_launch": T * K * V},
+        "hbm": {"algorithmic_bytes_per_step": alg_bytes, "GBps": alg_bytes / (ms_per_step / 1e3) / 1e9,
+                "frac": alg_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS},
+    }
+    return ms_per_step, out
+
+
+def run_linear(args, c, K, dust, torch):
+    T, d, n, V, sigma = c["T"], c["d"], c["n"], c["V"], c["sigma"]
+    u, h, xr = (torch.from_numpy(c[k]).cuda() for k in ("u", "h", "x_res"))
+    w2 = torch.from_numpy(c["w2_bf16"].view(np.int16)).cuda().view(torch.bfloat16)
+    wh = torch.from_numpy(c["w_head_bf16"].view(np.int16)).cuda().view(torch.bfloat16)
+    y = torch.from_numpy(c["labels"]).cuda()
+    gw = torch.empty((n, d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(dust.linear_workspace_bytes(T, d, n, V, K), dtype=torch.uint8, device="cuda")
+
+    def step():
+        dust.estimate_linear(u, h, xr, w2, wh, y, K, sigma, c["seed_noise"], c["layer"], ln_eps=c["ln_eps"],
+                             grad_w=gw, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    wall, ev = timed(dust, torch, step, 4, args.steps)
+    # events: 0 start, 1 after g_hat, 2 after outer, 3 after (last) gemm1, 4 after (last) gemm2
+    rows = T * (K + 1)
+    single_chunk = rows * d * 2 <= (512 << 20)
+    ms_per_step = wall * 1e3 / args.steps
+    fl1 = 2.0 * rows * n * d
+    fl2 = 2.0 * rows * d * V
+    out = {"dtype": "bf16 GEMM operands with fp32 accumulate in the downstream; fp32 noise, rewards, g_hat, G_W"}
+    if single_chunk:
+        g1 = float(np.mean([dust.event_elapsed_ms(e[0], e[3]) for e in ev]))
+        g2 = float(np.mean([dust.event_elapsed_ms(e[3], e[4]) for e in ev]))
+        red = float(np.mean([dust.event_elapsed_ms(e[4], e[1]) for e in ev]))
+        outer = float(np.mean([dust.event_elapsed_ms(e[1], e[2]) for e in ev]))
+        out["stages_ms"] = {"gemm1_noise_gelu_w2_ln": g1, "gemm2_head_logsumexp": g2, "combine_and_reduce": red,
+                            "outer_product": outer}
+        out["roofline"] = {"bound": "mfma", "kernel": "mlp_gemm2_kernel", "achieved": fl2 / (g2 / 1e3) / 1e12,
+                           "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": fl2 / (g2 / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                           "flop_per_launch": fl2}
+        out["mfma_downstream"] = {"gemm1_TFLOPs": fl1 / (g1 / 1e3) / 1e12, "gemm2_TFLOPs": fl2 / (g2 / 1e3) / 1e12,
+                                  "both_frac_of_peak": (fl1 + fl2) / ((g1 + g2) / 1e3) / 1e12
+                                  / MFMA_BF16_PEAK_TFLOPS}
+    else:
+        out["mfma_downstream"] = {"both_TFLOPs_whole_step": (fl1 + fl2) / (ms_per_step / 1e3) / 1e12}
+    return ms_per_step, out
 
 
 def main():
@@ -96,84 +234,36 @@ def main():
             return (torch.from_numpy(X).cuda() @ torch.from_numpy(W).cuda().T).cpu().numpy()
 
     c = synth.workload(args.workload, matmul=gpu_matmul)
-    T, V, d, K, sigma = c["T"], c["V"], c["d"], c["K"], c["sigma"]
-    if "logits" in c:
-        z = torch.from_numpy(c["logits"]).cuda()
-        dtype = "f32"
+    name = WORKLOAD_NAMES[args.workload]
+    if c["kind"] == "head":
+        K = c["K"]
+        ms, extra = run_head(args, c, dust, torch)
+        cfg = {"workload": name, "T": c["T"], "V": c["V"], "d": c["d"], "K": K, "sigma": c["sigma"]}
     else:
-        z = torch.from_numpy(c["logits_bf16"].view(np.int16)).cuda().view(torch.bfloat16)
-        dtype = "f32 (bf16 cached logits)"
-    x = torch.from_numpy(c["x"]).cuda()
-    y = torch.from_numpy(c["labels"]).cuda()
-    gw = torch.empty((V, d), dtype=torch.float32, device="cuda")
-    ws = torch.empty(dust.head_workspace_bytes(T, V, d, K), dtype=torch.uint8, device="cuda")
-    stream = torch.cuda.current_stream()
-
-    def step():
-        dust.estimate_head(z, x, y, K, sigma, c["seed_noise"], c["layer"], grad_w=gw, workspace=ws)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for e3 in ev:  # torch creates the underlying hipEvent at its first record
-        for e in e3:
-            e.record(stream)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        ev[k][0].record(stream)
-        dust.set_stage_event(0, ev[k][1])
-        dust.set_stage_event(1, ev[k][2])
-        step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    dust.set_stage_event(0, None)
-    dust.set_stage_event(1, None)
-    est_ms = float(np.mean([dust.event_elapsed_ms(e[0], e[1]) for e in ev]))
-    outer_ms = float(np.mean([dust.event_elapsed_ms(e[1], e[2]) for e in ev]))
-
-    ms_per_step = wall * 1e3 / args.steps
-    td = T * K
-    value = td / (ms_per_step / 1e3)
-    # dominant kernel: the per-token estimator
-    ch_draws = T * K * V
-    achieved = ch_draws * SLOTS_PER_CHANNEL_DRAW / (est_ms / 1e3) / 1e9
-    logit_bytes = 4 if "logits" in c else 2
-    hbm_bytes = T * V * logit_bytes + T * V * 4 + T * 4 + K * 0  # logits read, g_hat written, labels
-    profiles = os.path.join(ROOT, "profiles")
-    traffic = None
-    tfile = os.path.join(profiles, f"traffic_head_workload{args.workload}.json")
-    if os.path.exists(tfile):
-        with open(tfile) as f:
-            traffic = json.load(f).get("bytes_per_launch")
+        K = c["K"] if isinstance(c["K"], int) else args.draws
+        name = name.format(K=K)
+        ms, extra = run_linear(args, c, K, dust, torch)
+        cfg = {"workload": name, "T": c["T"], "d": c["d"], "n": c["n"], "V": c["V"], "K": K, "sigma": c["sigma"]}
+    cfg.update({"noise_seed": c["seed_noise"], "layer": c["layer"], "data_seed": 1000 + args.workload})
     out = {
         "metric": "token-draws/sec per Dust gradient estimate",
-        "value": value,
+        "value": c["T"] * K / (ms / 1e3),
         "unit": "token-draws/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dtype,
+        "dtype": extra.pop("dtype"),
         "data": "synthetic (seeded; stands in for FineWeb)",
-        "config": {"workload": WORKLOAD_NAMES[args.workload], "T": T, "V": V, "d": d, "K": K, "sigma": sigma,
-                   "noise_seed": c["seed_noise"], "layer": c["layer"], "data_seed": 1000 + args.workload},
-        "stages_ms": {"estimator": est_ms, "outer_product": outer_ms},
-        "roofline": {"bound": "alu", "kernel": "head_estimate_kernel",
-                     "achieved": achieved, "peak": VALU_PEAK_GSLOT, "unit": "G lane-slots/s",
-                     "frac": achieved / VALU_PEAK_GSLOT, "traffic": traffic,
-                     "slots_per_channel_draw": SLOTS_PER_CHANNEL_DRAW},
-        "hbm": {"algorithmic_bytes_per_step": hbm_bytes + (V * d + T * d) * 4 + T * V * 4,
-                "GBps_per_step": (hbm_bytes + (V * d + T * d) * 4 + T * V * 4) / (ms_per_step / 1e3) / 1e9,
-                "frac": (hbm_bytes + (V * d + T * d) * 4 + T * V * 4) / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS},
+        "config": cfg,
     }
+    out.update(extra)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(c, args.cpu_seconds)
+        out["cpu_baseline"] = (cpu_baseline_head(c, args.cpu_seconds) if c["kind"] == "head"
+                               else cpu_baseline_linear(c, K, args.cpu_seconds))
     print(json.dumps(out), flush=True)
 
 

@@ -77,8 +77,11 @@ const char *dust_last_error(void);
  * Profiling hook: while set, `event` (a hipEvent_t) is recorded on the call's
  * stream right after the given stage of every estimator call made from this
  * thread.  stage 0 = after g_hat is ready (the per-token estimator kernels),
- * stage 1 = after the weight-gradient outer product.  Pass NULL to clear.
- * The caller owns the events.  Used to time the stages of one call.
+ * stage 1 = after the weight-gradient outer product; for dust_estimate_linear
+ * also stage 2 = after the downstream GEMM1 (F = LN(x + W2 GELU(.))) and
+ * stage 3 = after GEMM2 (logits and their per-tile log-sum-exp) of each row
+ * chunk (the last chunk's record wins).  Pass NULL to clear.  The caller owns
+ * the events.  Used to time the stages of one call.
  */
 dust_status dust_set_stage_event(int stage, void *event);
 

@@ -13,7 +13,7 @@
 namespace {
 
 thread_local std::string g_err;
-thread_local hipEvent_t g_stage_event[2] = {nullptr, nullptr};
+thread_local hipEvent_t g_stage_event[4] = {nullptr, nullptr, nullptr, nullptr};
 
 hipError_t record_stage(int stage, hipStream_t s) {
     return g_stage_event[stage] ? hipEventRecord(g_stage_event[stage], s) : hipSuccess;
@@ -83,7 +83,7 @@ int dust_abi_version(void) { return DUST_ABI_VERSION; }
 const char* dust_last_error(void) { return g_err.c_str(); }
 
 dust_status dust_set_stage_event(int stage, void* event) {
-    if (stage < 0 || stage > 1) return fail(DUST_E_INVALID, "dust_set_stage_event: stage must be 0 or 1");
+    if (stage < 0 || stage > 3) return fail(DUST_E_INVALID, "dust_set_stage_event: stage must be in [0, 3]");
     g_stage_event[stage] = static_cast<hipEvent_t>(event);
     return ok();
 }
@@ -256,6 +256,8 @@ dust_status dust_estimate_linear(const float* u, const float* h, const float* x_
     A.tok0 = token_offset;
     A.draw0 = draw_offset;
     A.stage_event = g_stage_event[0];
+    A.gemm1_event = g_stage_event[2];
+    A.gemm2_event = g_stage_event[3];
     if (env_flag("DUST_LOG"))
         std::fprintf(stderr, "[dust] linear T=%lld d=%lld n=%lld V=%lld K=%lld chunk=%lld vtiles=%d ws=%zu\n",
                      (long long)T, (long long)d, (long long)n, (long long)V, (long long)K, (long long)L.chunk, L.nvt,

@@ -56,6 +56,8 @@ struct MlpArgs {
     float sigma, ln_eps, gscale;
     uint32_t k0, k1, layer, tok0, draw0;
     hipEvent_t stage_event;  // recorded after g_hat, before the outer product (or null)
+    hipEvent_t gemm1_event;  // recorded after each chunk's GEMM1 (or null)
+    hipEvent_t gemm2_event;  // recorded after each chunk's GEMM2 (or null)
 };
 
 struct MlpLayout {

@@ -483,10 +483,12 @@ hipError_t launch_mlp(const MlpArgs& A, const MlpLayout& L, unsigned char* ws, f
         else
             hipLaunchKernelGGL(mlp_gemm1_kernel<256>, dim3(b1), dim3(64 * G1_WAVES), 0, stream, A, g0, nrows, F);
         if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (A.gemm1_event && (e = hipEventRecord(A.gemm1_event, stream)) != hipSuccess) return e;
         const int64_t nrt = (nrows + G2_TR - 1) / G2_TR;
         hipLaunchKernelGGL(mlp_gemm2_kernel, dim3((unsigned)(nrt * L.nvt)), dim3(256), 0, stream, A, g0, nrows, L.nvt,
                            F, part, zy);
         if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (A.gemm2_event && (e = hipEventRecord(A.gemm2_event, stream)) != hipSuccess) return e;
         hipLaunchKernelGGL(mlp_combine_kernel, dim3((unsigned)((nrows + 255) / 256)), dim3(256), 0, stream, g0, nrows,
                            L.nvt, part, zy, ce);
         if ((e = hipGetLastError()) != hipSuccess) return e;
