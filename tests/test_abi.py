@@ -59,7 +59,7 @@ def _head(**kw):
     (dict(tok=2**32 - 2), 1, "token counter"),
     (dict(draw=2**32 - 1), 1, "draw counter"),
     (dict(V=70000), 2, "65536"),
-    (dict(V=50000, dt=0), 2, "LDS"),
+    (dict(V=40000, dt=0), 2, "LDS"),
     (dict(ghat=None), 3, "workspace"),
     (dict(ghat=None, ws=FAKE, wsb=16), 3, "workspace"),
 ])

@@ -45,6 +45,7 @@ SMALL = [
     (4, 50304, 8, 2, 5e-3, "bf16", "zipf"),      # 768 lanes, Q = 17
     (3, 60001, 8, 2, 5e-3, "bf16", "zipf"),      # 1024 lanes, Q = 16
     (9, 500, 8, 3, 0.1, "f32", "uniform"),       # large sigma: library expm1 variant
+    (11, 3000, 8, 3, 0.02, "f32", "zipf"),       # degree-6 polynomial
     (5, 20000, 8, 2, 0.5, "bf16", "zipf"),       # large sigma, LDS row
 ]
 
@@ -114,7 +115,7 @@ def test_named_workload_full_size(wid, ntok):
     ref_rows = ghat[:, rows].cpu().numpy().astype(np.float64).T @ c["x"].astype(np.float64)
     e_w = rel_l2(gw[rows].cpu().numpy(), ref_rows)
     print(f"workload {wid}: sampled ghat {e_g:.2e} rewards {e_r:.2e}; grad_w rows vs G^T X {e_w:.2e}")
-    assert e_g < TOL_GHAT and e_r < TOL_REW and e_w < 1e-5
+    assert e_g < TOL_GHAT and e_r < TOL_REW and e_w < 6e-5  # bf16-pair outer product
 
 
 def test_deterministic_and_split_invariants():

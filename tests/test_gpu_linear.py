@@ -91,7 +91,7 @@ def test_named_workload_full_size(wid, K, ntok):
     ref = ghat[:, rows].cpu().numpy().astype(np.float64).T @ c["u"].astype(np.float64)
     e_w = rel_l2(gw[rows].cpu().numpy(), ref)
     print(f"workload {wid} K={K}: sampled rewards {st}; grad_w rows vs G^T U {e_w:.2e}")
-    assert e_w < 1e-5
+    assert e_w < 6e-5  # bf16-pair outer product
 
 
 def test_linear_deterministic_additive_and_chunked():

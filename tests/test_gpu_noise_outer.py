@@ -41,15 +41,26 @@ def test_noise_gaussians_match_oracle():
     assert np.abs(g).max() <= 5.7684
 
 
-@pytest.mark.parametrize("T,n,d", [(1, 1, 1), (37, 130, 70), (1000, 512, 64), (4096, 2048, 512), (300, 8192, 16)])
+def outer_tol(T, n, d):
+    """Products of >= 4 GFLOP run as bf16 pairs (hi + lo per operand, three MFMA
+    products, fp32 accumulation): each product carries about 3 * 2^-17 relative
+    error, so the result is held to 6e-5; the fp32-MFMA path to 1e-5."""
+    return 6e-5 if 2.0 * T * n * d >= 4e9 else 1e-5
+
+
+@pytest.mark.parametrize("T,n,d", [(1, 1, 1), (37, 130, 70), (1000, 512, 64), (4096, 2048, 512), (300, 8192, 16),
+                                   (1000, 3000, 700), (4097, 1030, 520)])
 def test_outer_product_matches_fp64(T, n, d):
     rng = np.random.default_rng(T * 7 + n)
     G = rng.standard_normal((T, n)).astype(np.float32)
     X = rng.standard_normal((T, d)).astype(np.float32)
     out = dust.outer_product(dev(G), dev(X)).cpu().numpy()
     ref = G.astype(np.float64).T @ X.astype(np.float64)
-    assert rel_l2(out, ref) < 1e-5
+    tol = outer_tol(T, n, d)
+    e = rel_l2(out, ref)
+    print(f"outer T={T} n={n} d={d}: rel L2 {e:.2e} (tol {tol})")
+    assert e < tol
     scale = np.sqrt(T)  # entries are sums of T unit-variance products
-    assert np.abs(out - ref).max() < 1e-4 * scale
+    assert np.abs(out - ref).max() < 10 * tol * scale
     out2 = dust.outer_product(dev(G), dev(X)).cpu().numpy()
     np.testing.assert_array_equal(out, out2)

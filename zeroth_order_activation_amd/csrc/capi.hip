@@ -174,15 +174,20 @@ dust_status dust_estimate_head(const void* logits, int logits_dtype, const float
     A.T = (int32_t)T;
     A.V = (int32_t)V;
     A.K = (int32_t)K;
-    A.sigma = sigma;
-    const double sd = sigma;
-    A.smul = plan.deg == 5 ? sigma : 1.0f;
-    A.gscale = (float)(-1.0 / ((double)K * sd));
-    A.coef[0] = 1.0f;
-    A.coef[1] = (float)(sd / 2.0);
-    A.coef[2] = (float)(sd * sd / 6.0);
-    A.coef[3] = (float)(sd * sd * sd / 24.0);
-    A.coef[4] = (float)(sd * sd * sd * sd / 120.0);
+    // The kernel draws the noise divided by sqrt(2 ln 2); it works with
+    // sigma' = sigma sqrt(2 ln 2), so that sigma' a' = sigma a, and the final
+    // scale takes the factor back: g_hat = -(1/(K sigma)) sqrt(2 ln 2) sum r a'.
+    const double s2 = std::sqrt(2.0 * std::log(2.0));
+    const double sd = (double)sigma * s2;
+    A.sigma = (float)sd;
+    A.smul = plan.deg > 0 ? (float)sd : 1.0f;
+    A.gscale = (float)(-s2 / ((double)K * (double)sigma));
+    double ck = 1.0, fact = 1.0;
+    for (int k = 0; k < 8; ++k) {  // coef[k] = sd^k / (k+1)!
+        fact *= (k + 1);
+        A.coef[k] = (float)(ck / fact);
+        ck *= sd;
+    }
     A.k0 = (uint32_t)seed;
     A.k1 = (uint32_t)(seed >> 32);
     A.layer = layer;

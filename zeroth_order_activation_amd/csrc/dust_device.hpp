@@ -24,17 +24,31 @@ struct u32x4 {
     uint32_t x, y, z, w;
 };
 
-// Ten Philox4x32 rounds.  The counter words that are uniform across a wave
-// (token, draw, layer in the head kernel) sit in c0, c2, c3, so the first
-// products of the chain are scalar; the channel quad sits in c1.
+// Three-way xor in one VALU op (v_bitop3_b32 with the truth table of a^b^c).
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+    return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
+// Ten Philox4x32 rounds (SC'11): per round two 32x32->64 products
+// (v_mad_u64_u32) and two three-way xors.  With UNIFORM3 the caller
+// guarantees that c0, c2, c3 and the key are uniform across the wave (token,
+// draw, layer) and only c1 (the channel quad) varies: the first three rounds
+// then use plain xors so that the uniform halves stay on the scalar unit.
+template <bool UNIFORM3 = false>
 __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
                                                uint32_t k0, uint32_t k1) {
 #pragma unroll
     for (int r = 0; r < 10; ++r) {
         const uint64_t p0 = (uint64_t)kPhiloxM0 * (uint64_t)c0;
         const uint64_t p1 = (uint64_t)kPhiloxM1 * (uint64_t)c2;
-        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        uint32_t n0, n2;
+        if (UNIFORM3 && r < 3) {
+            n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+            n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        } else {
+            n0 = xor3((uint32_t)(p1 >> 32), c1, k0);
+            n2 = xor3((uint32_t)(p0 >> 32), c3, k1);
+        }
         c1 = (uint32_t)p1;
         c3 = (uint32_t)p0;
         c0 = n0;
@@ -47,15 +61,25 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
 
 // Box-Muller on one pair of 32-bit words: the top 24 bits of each give
 // u1 in (0,1] and u2 in [0,1), both exact in fp32.
-//   rho = sqrt(-2 ln u1) = sqrt(-2 ln2 * log2 u1)
+//   rho = sqrt(-2 ln u1) = sqrt(2 ln 2) * sqrt(-log2 u1)
 //   (cos, sin)(2 pi u2): the hardware sine/cosine take their argument in
 //   revolutions, so u2 is used as is.
-__device__ __forceinline__ void box_muller(uint32_t we, uint32_t wo, float& c, float& s) {
-    const float u1 = (float)((we >> 8) + 1u) * 0x1p-24f;
+// box_muller_unscaled returns the pair divided by sqrt(2 ln 2) (one product
+// fewer per pair); callers fold the factor into their own constants.
+constexpr float kSqrt2Ln2 = 1.1774100225154747f;
+
+__device__ __forceinline__ void box_muller_unscaled(uint32_t we, uint32_t wo, float& c, float& s) {
+    const float u1 = fmaf((float)(we >> 8), 0x1p-24f, 0x1p-24f);  // ((we>>8)+1) 2^-24, exact
     const float u2 = (float)(wo >> 8) * 0x1p-24f;
-    const float rho = __builtin_amdgcn_sqrtf(-1.3862943611198906f * __builtin_amdgcn_logf(u1));
+    const float rho = __builtin_amdgcn_sqrtf(-__builtin_amdgcn_logf(u1));
     c = rho * __builtin_amdgcn_cosf(u2);
     s = rho * __builtin_amdgcn_sinf(u2);
+}
+
+__device__ __forceinline__ void box_muller(uint32_t we, uint32_t wo, float& c, float& s) {
+    box_muller_unscaled(we, wo, c, s);
+    c *= kSqrt2Ln2;
+    s *= kSqrt2Ln2;
 }
 
 struct f32x4 {
@@ -69,6 +93,17 @@ __device__ __forceinline__ f32x4 gauss4(uint32_t token, uint32_t quad, uint32_t 
     f32x4 a;
     box_muller(w.x, w.y, a.v[0], a.v[1]);
     box_muller(w.z, w.w, a.v[2], a.v[3]);
+    return a;
+}
+
+// The same Gaussians divided by sqrt(2 ln 2), for a wave whose token, draw and
+// layer are uniform.
+__device__ __forceinline__ f32x4 gauss4_unscaled_uniform(uint32_t token, uint32_t quad, uint32_t draw,
+                                                         uint32_t layer, uint32_t k0, uint32_t k1) {
+    const u32x4 w = philox4x32_10<true>(token, quad, draw, layer, k0, k1);
+    f32x4 a;
+    box_muller_unscaled(w.x, w.y, a.v[0], a.v[1]);
+    box_muller_unscaled(w.z, w.w, a.v[2], a.v[3]);
     return a;
 }
 

@@ -1,4 +1,6 @@
 // Variant planning for the LM-head estimator.
+#include <cmath>
+
 #include "dust_internal.hpp"
 
 namespace dust {
@@ -31,17 +33,24 @@ HeadPlan plan_head(int64_t V, int logits_dtype, float sigma) {
         else { p.nt = 1024; p.q = 16; }
         p.pmode = 1;
         p.lds = (size_t)nq * (logits_dtype == 0 ? 16 : 8);
-        if (p.lds > kMaxDynLds) {
+        if ((size_t)p.nt * p.q * (logits_dtype == 0 ? 16 : 8) > kMaxDynLds) {
             p.ok = false;
-            p.why = "fp32 logits with V > 40896 do not fit one workgroup's LDS; pass bf16 logits";
+            p.why = "fp32 logits with V > 32768 do not fit one workgroup's LDS; pass bf16 logits";
         }
     } else {
         p.ok = false;
         p.why = "vocabulary larger than 65536 is not supported";
     }
-    // expm1(x) = x(1 + x/2 + x^2/6 + x^3/24 + x^4/120) + O(x^6): the dropped part is
-    // below 2^-25 of x for |x| <= 0.117.
-    p.deg = ((double)sigma * kMaxAbsNoise <= 0.117) ? 5 : 0;
+    // Taylor degree of expm1(x), x = sigma a, |x| <= sigma*5.7683: the dropped
+    // terms move S = sum_v p_v expm1(x_v) by at most |x|^(D+1)/(D+1)! e^|x|.
+    const double xm = (double)sigma * kMaxAbsNoise;
+    auto rem = [&](int D) {
+        double f = 1.0;
+        for (int k = 2; k <= D + 1; ++k) f *= k;
+        return std::pow(xm, D + 1) / f * std::exp(xm);
+    };
+    p.deg = rem(4) <= 8e-9 ? 4 : rem(6) <= 8e-9 ? 6 : 0;
+    if (p.pmode == 1) p.lds = (size_t)p.nt * p.q * (logits_dtype == 0 ? 16 : 8);
     return p;
 }
 

@@ -10,9 +10,13 @@
 // Per draw the kernel needs CE(z + sigma a) - CE(z).  With p = softmax(z) this
 // is exactly  log1p(S) - sigma a_y,  S = sum_v p_v expm1(sigma a_v),  which
 // avoids subtracting two losses of size ln V in fp32.  |a| <= sqrt(48 ln 2)
-// by construction of the noise, so for small sigma expm1 is a short
-// polynomial: expm1(x) = x (1 + x/2 + x^2/6 + x^3/24 + x^4/120) with x = sigma a,
-// truncation below 2^-25 relative while sigma <= 0.02 (else the library expm1).
+// by construction of the noise, so for small sigma expm1 is a short Taylor
+// polynomial of degree DEG (4 or 6) in x = sigma a; the host picks the degree
+// so that the dropped terms move S by less than 8e-9 (since sum p = 1, that
+// bound is |x|max^(DEG+1)/(DEG+1)! e^|x|max); larger sigma uses the library
+// expm1 (DEG = 0).  The noise is generated divided by sqrt(2 ln 2) (one
+// product fewer per pair); the host folds that factor into sigma and the
+// final scale.
 //
 // Layout: lane l owns channel quads q = l + j*NT (j < Q), so each load and
 // store of a quad is one coalesced 16-byte (fp32) or 8-byte (bf16) access.
@@ -80,13 +84,13 @@ __device__ __forceinline__ float block_sum(float v, float* sh) {
     return r;
 }
 
-// expm1(sigma a) / sigma  (DEG = 5)  or  expm1(sigma a)  (DEG = 0).
+// expm1(sigma a) / sigma  (DEG = 4, 6)  or  expm1(sigma a)  (DEG = 0).
 template <int DEG>
 __device__ __forceinline__ float em1(float a, const HeadArgs& A) {
-    if (DEG == 5) {
-        float t = fmaf(a, A.coef[4], A.coef[3]);
-        t = fmaf(a, t, A.coef[2]);
-        t = fmaf(a, t, A.coef[1]);
+    if (DEG > 0) {
+        float t = A.coef[DEG - 1];
+#pragma unroll
+        for (int k = DEG - 2; k >= 1; --k) t = fmaf(a, t, A.coef[k]);
         t = fmaf(a, t, 1.0f);
         return a * t;
     } else {
@@ -112,8 +116,9 @@ __device__ __forceinline__ f32x4 lds_quad(const unsigned char* zl, int q) {
 }
 
 template <int NT, int Q, int LT, int PMODE, int DEG>
-__global__ void __launch_bounds__(NT) head_estimate_kernel(HeadArgs A) {
+__global__ void __launch_bounds__(NT, (NT == 256 ? 4 : 1)) head_estimate_kernel(HeadArgs A) {
     constexpr int NW = NT / 64;
+    constexpr bool SCHED_FENCE = Q >= 8;
     __shared__ float sh_stat[NW];
     __shared__ float sh_red[2][NW][2];
     extern __shared__ __align__(16) unsigned char zlds[];
@@ -140,8 +145,12 @@ __global__ void __launch_bounds__(NT) head_estimate_kernel(HeadArgs A) {
             for (int c = 0; c < 4; ++c) { p[j][c] = z.v[c]; m = fmaxf(m, z.v[c]); }
         }
     } else {
-        for (int q = tid; q < nq; q += NT) {
-            const f32x4 z = load_quad<LT>(row, q, V, vec);
+        // the LDS row is padded to NT*Q quads with -inf (probability 0), so the
+        // draw loop needs no bounds test
+        for (int q = tid; q < NT * Q; q += NT) {
+            f32x4 z;
+            if (q < nq) z = load_quad<LT>(row, q, V, vec);
+            else z.v[0] = z.v[1] = z.v[2] = z.v[3] = -__builtin_inff();
             if (LT == 0) {
                 reinterpret_cast<float4*>(zlds)[q] = make_float4(z.v[0], z.v[1], z.v[2], z.v[3]);
             } else {
@@ -197,26 +206,25 @@ __global__ void __launch_bounds__(NT) head_estimate_kernel(HeadArgs A) {
         float sl = 0.f, ly = 0.f;
 #pragma unroll
         for (int j = 0; j < Q; ++j) {
+            // quads past the row have probability 0: they add nothing to S, and
+            // their running sums are never stored
             const int q = tid + j * NT;
-            if (q < nq) {
-                const f32x4 g = gauss4(tok, (uint32_t)q, draw, A.layer, A.k0, A.k1);
-                f32x4 pz;
-                if (PMODE == 1) pz = lds_quad<LT>(zlds, q);
+            const f32x4 g = gauss4_unscaled_uniform(tok, (uint32_t)q, draw, A.layer, A.k0, A.k1);
+            f32x4 pz;
+            if (PMODE == 1) pz = lds_quad<LT>(zlds, q);
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    a[j][c] = g.v[c];
-                    const float pc = PMODE == 0 ? p[j][c]
-                                                : __builtin_amdgcn_exp2f(fmaf(pz.v[c], kLog2e, -lse2));
-                    sl = fmaf(pc, em1<DEG>(g.v[c], A), sl);
-                }
-            } else {
-#pragma unroll
-                for (int c = 0; c < 4; ++c) a[j][c] = 0.f;
+            for (int c = 0; c < 4; ++c) {
+                a[j][c] = g.v[c];
+                const float pc = PMODE == 0 ? p[j][c] : __builtin_amdgcn_exp2f(fmaf(pz.v[c], kLog2e, -lse2));
+                sl = fmaf(pc, em1<DEG>(g.v[c], A), sl);
             }
             if ((uint32_t)j == jy) {
                 const float sel = cy == 0 ? a[j][0] : cy == 1 ? a[j][1] : cy == 2 ? a[j][2] : a[j][3];
                 ly = owner ? sel : 0.f;
             }
+            // keep the scheduler from interleaving many quads (their Philox and
+            // Box-Muller temporaries would not fit next to a[] and acc[])
+            if (SCHED_FENCE) __builtin_amdgcn_sched_barrier(0);
         }
         sl = wave_sum(sl);
         ly = wave_sum(ly);
@@ -268,8 +276,9 @@ template <int LT>
 hipError_t dispatch_head(const HeadPlan& P, const HeadArgs& A, hipStream_t s) {
 #define DUST_HEAD_CASE(NT_, Q_, PM_)                                                       \
     if (P.nt == NT_ && P.q == Q_ && P.pmode == PM_) {                                     \
-        return P.deg == 5 ? launch_head_variant<NT_, Q_, LT, PM_, 5>(P, A, s)             \
-                          : launch_head_variant<NT_, Q_, LT, PM_, 0>(P, A, s);            \
+        return P.deg == 4   ? launch_head_variant<NT_, Q_, LT, PM_, 4>(P, A, s)           \
+               : P.deg == 6 ? launch_head_variant<NT_, Q_, LT, PM_, 6>(P, A, s)           \
+                            : launch_head_variant<NT_, Q_, LT, PM_, 0>(P, A, s);          \
     }
     DUST_HEAD_CASE(256, 1, 0)
     DUST_HEAD_CASE(256, 2, 0)

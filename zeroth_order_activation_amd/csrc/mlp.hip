@@ -415,26 +415,27 @@ __global__ void __launch_bounds__(256) mlp_combine_kernel(int64_t g0, int64_t nr
     ce[g0 + row] = m + __logf(s) - zy[row];
 }
 
-// g_hat_t = -(1/(K sigma)) sum_i (CE0_t - CE_{t,i}) a_{t,i}, noise regenerated;
-// one thread per (token, channel quad); rewards written by the quad-0 threads.
+// g_hat_t = -(1/(K sigma)) sum_i (CE0_t - CE_{t,i}) a_{t,i}, noise regenerated.
+// One workgroup per token (token, draw and layer are then uniform, which keeps
+// the first Philox rounds on the scalar unit); each thread owns channel quads.
 __global__ void __launch_bounds__(256) mlp_reduce_kernel(MlpArgs A, const float* __restrict__ ce, float* __restrict__ ghat) {
+    const int t = blockIdx.x;
     const int nq = A.n >> 2;
-    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (gid >= (int64_t)A.T * nq) return;
-    const int t = (int)(gid / nq);
-    const int q = (int)(gid - (int64_t)t * nq);
     const float c0 = ce[t];
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
     const uint32_t tok = A.tok0 + (uint32_t)t;
-    for (int i = 0; i < A.K; ++i) {
-        const float r = c0 - ce[(int64_t)A.T * (i + 1) + t];
-        const f32x4 g = gauss4(tok, (uint32_t)q, A.draw0 + (uint32_t)i, A.layer, A.k0, A.k1);
+    const float scale = A.gscale * kSqrt2Ln2;  // the noise below is drawn divided by sqrt(2 ln 2)
+    for (int q = threadIdx.x; q < nq; q += 256) {
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < A.K; ++i) {
+            const float r = c0 - ce[(int64_t)A.T * (i + 1) + t];
+            const f32x4 g = gauss4_unscaled_uniform(tok, (uint32_t)q, A.draw0 + (uint32_t)i, A.layer, A.k0, A.k1);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[c] = fmaf(r, g.v[c], acc[c]);
+            for (int c = 0; c < 4; ++c) acc[c] = fmaf(r, g.v[c], acc[c]);
+        }
+        *reinterpret_cast<float4*>(ghat + (int64_t)t * A.n + 4 * q) =
+            make_float4(acc[0] * scale, acc[1] * scale, acc[2] * scale, acc[3] * scale);
     }
-    *reinterpret_cast<float4*>(ghat + (int64_t)t * A.n + 4 * q) =
-        make_float4(acc[0] * A.gscale, acc[1] * A.gscale, acc[2] * A.gscale, acc[3] * A.gscale);
-    if (q == 0 && A.rewards)
+    if (threadIdx.x == 0 && A.rewards)
         for (int i = 0; i < A.K; ++i) A.rewards[(int64_t)i * A.T + t] = c0 - ce[(int64_t)A.T * (i + 1) + t];
 }
 
@@ -493,8 +494,7 @@ hipError_t launch_mlp(const MlpArgs& A, const MlpLayout& L, unsigned char* ws, f
                            L.nvt, part, zy, ce);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    const int64_t threads = (int64_t)A.T * (A.n / 4);
-    hipLaunchKernelGGL(mlp_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, A, ce, ghat);
+    hipLaunchKernelGGL(mlp_reduce_kernel, dim3((unsigned)A.T), dim3(256), 0, stream, A, ce, ghat);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (A.stage_event && (e = hipEventRecord(A.stage_event, stream)) != hipSuccess) return e;
     return launch_outer(ghat, A.u, A.T, A.n, A.d, grad_w, ws + L.off_outer, L.total - L.off_outer, stream);
