@@ -66,6 +66,8 @@ def parse():
     ap.add_argument("--draws", type=int, default=1024, help="K for workload 5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a device-to-device copy of MIB MiB (to scale HBM traffic counters) and exit")
     return ap.parse_args()
 
 
@@ -226,6 +228,14 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "read_bytes": n, "write_bytes": n}), flush=True)
+        return
     import synth
     import zeroth_order_activation_amd as dust
 

@@ -63,7 +63,7 @@ struct MlpArgs {
 struct MlpLayout {
     int64_t chunk;  // rows of recomputed downstream per pass
     int nvt;        // vocabulary tiles
-    size_t off_f, off_part, off_zy, off_ce, off_ghat, off_outer, total;
+    size_t off_f, off_part, off_zy, off_wnorm, off_ce, off_ghat, off_outer, total;
 };
 
 MlpLayout mlp_layout(int64_t T, int64_t d, int64_t n, int64_t V, int64_t K);

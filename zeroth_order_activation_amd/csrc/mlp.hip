@@ -257,139 +257,218 @@ __global__ void __launch_bounds__(512) mlp_gemm1_kernel(MlpArgs A, int64_t g0, i
 }
 
 // ---------------------------------------------------------------------------
-// gemm2: per (vocab tile of 128, row): partial max / sum-exp of z = W_head F,
-// and the label logit.  Workgroup tile 128 vocab x 128 rows, 4 waves of 64x64,
-// both operands staged through LDS in 32-wide k-steps (double-buffered).
+// gemm2: per (vocab tile of 256, row): partial log-sum-exp of z = W_head F
+// and the label logit.  Workgroup tile 256 vocab x 256 rows, 8 waves of
+// 128 vocab x 64 rows (4 x 2 MFMA blocks, 128 accumulators); both operands
+// staged through LDS in 64-wide k-steps (double-buffered, register prefetch).
+// A 128 x 128 wave tile (4 waves) would read less LDS per MFMA but needs
+// 256 accumulators and spills.
 // ---------------------------------------------------------------------------
-constexpr int G2_TV = 128, G2_TR = 128, G2_KS = 32;
-constexpr int G2_STRIDE = G2_KS + 8;  // bf16 per LDS row (80 bytes)
+constexpr int G2_TV = 256, G2_TR = 256, G2_KS = 64;
+constexpr int G2_VB = 4, G2_RB = 2;   // MFMA blocks per wave (vocab, rows): 128 x 64
+constexpr int G2_WAVES = 8;           // 2 vocab halves x 4 row quarters
+constexpr int G2_NT = 64 * G2_WAVES;
+constexpr int G2_WR = G2_RB * 32;     // rows per wave
+// Fixed log-sum-exp offset: |z_v| <= |f| |w_v| (Cauchy-Schwarz) and the bf16
+// LayerNorm output has |f| <= sqrt(d) (1 + 2^-9).  When C = sqrt(d) 1.004
+// max_v |w_v| <= 40, every term exp(z - C) lies in [e^-80, 1]: no overflow,
+// no underflow, so the running maximum (and its second pass) can be skipped.
+constexpr float G2_FIXED_MAX = 40.0f;
 
-__global__ void __launch_bounds__(256) mlp_gemm2_kernel(MlpArgs A, int64_t g0, int64_t nrows, int nvt,
-                                                         const uint16_t* __restrict__ F, float2* __restrict__ part,
-                                                         float* __restrict__ zy) {
-    __shared__ __align__(16) uint16_t As[2][G2_TV * G2_STRIDE];
-    __shared__ __align__(16) uint16_t Bs[2][G2_TR * G2_STRIDE];
+// LDS tile of 128-byte rows (64 bf16 = eight 16-byte pieces; a k-step of 64
+// reads whole cache lines), with piece p of row r stored at piece
+// p ^ ((r >> 1) & 7).  Sixteen lanes reading the same piece of sixteen
+// consecutive rows (an MFMA fragment), and sixteen lanes writing the eight
+// pieces of two consecutive rows (a coalesced global load), then both touch
+// all 64 banks exactly once.
+__device__ __forceinline__ int swz(int row, int piece) { return row * 64 + ((piece ^ ((row >> 1) & 7)) << 3); }
+
+// Largest row norm of W_head, as an fp32 upper bound (one workgroup per 256
+// rows, then a single-block maximum).
+__global__ void __launch_bounds__(256) mlp_wnorm_kernel(const uint16_t* __restrict__ w, int V, int D,
+                                                        float* __restrict__ blockmax) {
+    const int v = blockIdx.x * 256 + threadIdx.x;
+    float s = 0.f;
+    if (v < V) {
+        const uint16_t* row = w + (int64_t)v * D;
+        for (int k = 0; k < D; k += 8) {
+            const uint4 q = *reinterpret_cast<const uint4*>(row + k);
+            const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float a = __uint_as_float(u[e] << 16), b = __uint_as_float(u[e] & 0xFFFF0000u);
+                s = fmaf(a, a, fmaf(b, b, s));
+            }
+        }
+    }
+    __shared__ float sh[4];
+    s = wave_max(s);
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) blockmax[blockIdx.x] = fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
+}
+
+__global__ void __launch_bounds__(256) mlp_wnorm_final_kernel(const float* __restrict__ blockmax, int nb, int D,
+                                                              float* __restrict__ offset) {
+    float m = 0.f;
+    for (int i = threadIdx.x; i < nb; i += 256) m = fmaxf(m, blockmax[i]);
+    __shared__ float sh[4];
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const float mx = fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
+        // sqrt rounded up generously; the 1.004 covers |f| growth by bf16 rounding
+        offset[0] = sqrtf((float)D * mx) * 1.004f * (1.0f + 1e-5f);
+    }
+}
+
+__global__ void __launch_bounds__(G2_NT, 1) mlp_gemm2_kernel(MlpArgs A, int64_t g0, int64_t nrows, int nvt,
+                                                            const uint16_t* __restrict__ F, float2* __restrict__ part,
+                                                            float* __restrict__ zy, const float* __restrict__ offset) {
+    __shared__ __align__(16) uint16_t As[2][G2_TV * G2_KS];
+    __shared__ __align__(16) uint16_t Bs[2][G2_TR * G2_KS];
     __shared__ float2 red[2][G2_TR];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wv = w & 1, wr = w >> 1;
     // vocab tile fastest: with a tile count that is a multiple of 8, each XCD
-    // keeps revisiting the same eighth of W_head, which then stays in its L2.
+    // keeps revisiting the same eighth of W_head, which then stays in its L2,
+    // and the workgroups sharing a row tile on one XCD run back to back.
     const int vt = blockIdx.x % nvt;
     const int64_t rt = blockIdx.x / nvt;
     const int v0 = vt * G2_TV;
     const int64_t r0 = rt * G2_TR;
     const int D = A.d, V = A.V;
 
-    // load mapping: 128 rows x 32 k = 512 16-byte pieces per operand -> 2 per thread
-    auto load = [&](int ks, uint4 (&ra)[2], uint4 (&rb)[2]) {
+    // loads: each operand is 256 rows x 64 k = 2048 pieces of 16 bytes
+    constexpr int NL = 2048 / G2_NT;
+    auto load = [&](int ks, uint4 (&ra)[NL], uint4 (&rb)[NL]) {
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const int pi = tid + 256 * jj;
-            const int row = pi >> 2, piece = pi & 3;
-            const int k = ks * G2_KS + 8 * piece;
+        for (int jj = 0; jj < NL; ++jj) {
+            const int pi = tid + G2_NT * jj;
+            const int row = pi >> 3, piece = pi & 7;
             const int v = v0 + row;
-            ra[jj] = v < V ? *reinterpret_cast<const uint4*>(A.w_head + (int64_t)v * D + k) : make_uint4(0, 0, 0, 0);
+            ra[jj] = v < V ? *reinterpret_cast<const uint4*>(A.w_head + (int64_t)v * D + ks * G2_KS + 8 * piece)
+                           : make_uint4(0, 0, 0, 0);
             const int64_t rr = r0 + row;
-            rb[jj] = rr < nrows ? *reinterpret_cast<const uint4*>(F + rr * D + k) : make_uint4(0, 0, 0, 0);
+            rb[jj] = rr < nrows ? *reinterpret_cast<const uint4*>(F + rr * D + ks * G2_KS + 8 * piece)
+                                : make_uint4(0, 0, 0, 0);
         }
     };
-    auto store = [&](int buf, const uint4 (&ra)[2], const uint4 (&rb)[2]) {
+    auto store = [&](int buf, const uint4 (&ra)[NL], const uint4 (&rb)[NL]) {
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const int pi = tid + 256 * jj;
-            const int row = pi >> 2, piece = pi & 3;
-            *reinterpret_cast<uint4*>(&As[buf][row * G2_STRIDE + 8 * piece]) = ra[jj];
-            *reinterpret_cast<uint4*>(&Bs[buf][row * G2_STRIDE + 8 * piece]) = rb[jj];
+        for (int jj = 0; jj < NL; ++jj) {
+            const int pi = tid + G2_NT * jj;
+            *reinterpret_cast<uint4*>(&As[buf][swz(pi >> 3, pi & 7)]) = ra[jj];
+            *reinterpret_cast<uint4*>(&Bs[buf][swz(pi >> 3, pi & 7)]) = rb[jj];
         }
     };
 
-    f32x16_t acc[2][2];
+    f32x16_t acc[G2_VB][G2_RB];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < G2_VB; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < G2_RB; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     const int nks = D / G2_KS;
     {
-        uint4 ra[2], rb[2];
+        uint4 ra[NL], rb[NL];
         load(0, ra, rb);
         store(0, ra, rb);
     }
     __syncthreads();
     for (int ks = 0; ks < nks; ++ks) {
         const int buf = ks & 1;
-        uint4 ra[2], rb[2];
+        uint4 ra[NL], rb[NL];
         if (ks + 1 < nks) load(ks + 1, ra, rb);
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            uint4 af[2], bfr[2];
+        for (int kk = 0; kk < 4; ++kk) {
+            uint4 af[G2_VB], bfr[G2_RB];
+            const int piece = kk * 2 + (lane >> 5);
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                af[i] = *reinterpret_cast<const uint4*>(
-                    &As[buf][(wv * 64 + i * 32 + (lane & 31)) * G2_STRIDE + kk * 16 + 8 * (lane >> 5)]);
-                bfr[i] = *reinterpret_cast<const uint4*>(
-                    &Bs[buf][(wr * 64 + i * 32 + (lane & 31)) * G2_STRIDE + kk * 16 + 8 * (lane >> 5)]);
-            }
+            for (int i = 0; i < G2_VB; ++i)
+                af[i] = *reinterpret_cast<const uint4*>(&As[buf][swz(wv * 128 + i * 32 + (lane & 31), piece)]);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int j = 0; j < G2_RB; ++j)
+                bfr[j] = *reinterpret_cast<const uint4*>(&Bs[buf][swz(wr * G2_WR + j * 32 + (lane & 31), piece)]);
 #pragma unroll
-                for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+            for (int i = 0; i < G2_VB; ++i)
+#pragma unroll
+                for (int j = 0; j < G2_RB; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
         }
         if (ks + 1 < nks) store(buf ^ 1, ra, rb);
         __syncthreads();
     }
 
-    // ---- epilogue: per row, max and sum-exp over this tile's vocabulary ------
-    // lane holds rows j = wr*64 + rb*32 + lane%32, vocab v0 + wv*64 + vb*32 + drow(r, lane)
+    // ---- epilogue: per row, log-sum-exp over this tile's vocabulary ---------
+    // lane holds rows j = wr*G2_WR + rb*32 + lane%32, vocab v0 + wv*128 + vb*32 + drow(r, lane)
+    const bool full = v0 + G2_TV <= V;  // uniform: no vocabulary bound to test
+    const float C = offset[0];
+    const bool fixed = C <= G2_FIXED_MAX;  // uniform
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        const int lrow = wr * 64 + rb * 32 + (lane & 31);
+    for (int rb = 0; rb < G2_RB; ++rb) {
+        const int lrow = wr * G2_WR + rb * 32 + (lane & 31);
         const int64_t row = r0 + lrow;
-        float m = -__builtin_inff();
+        if (!full) {  // last vocabulary tile: columns past V do not count
 #pragma unroll
-        for (int vb = 0; vb < 2; ++vb)
+            for (int vb = 0; vb < G2_VB; ++vb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int v = v0 + wv * 64 + vb * 32 + drow(r, lane);
-                if (v < V) m = fmaxf(m, acc[vb][rb][r]);
-            }
-        const float m2 = fmaxf(m, __shfl_xor(m, 32, 64));
-        float s = 0.f;
-        const float ml2 = m2 * kLog2eF;
-#pragma unroll
-        for (int vb = 0; vb < 2; ++vb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int v = v0 + wv * 64 + vb * 32 + drow(r, lane);
-                if (v < V) s += __builtin_amdgcn_exp2f(fmaf(acc[vb][rb][r], kLog2eF, -ml2));
-            }
-        s += __shfl_xor(s, 32, 64);
-        if (lane < 32) red[wv][lrow] = make_float2(m2, s);
-        // label logit: exactly one lane of the grid holds z[y] for this row
+                for (int r = 0; r < 16; ++r)
+                    if (v0 + wv * 128 + vb * 32 + drow(r, lane) >= V) acc[vb][rb][r] = -__builtin_inff();
+        }
+        // label logit first (the fixed-offset path below overwrites nothing, but
+        // keep the capture next to the accumulators it reads)
         if (row < nrows) {
             const int64_t t = (g0 + row) % A.T;
-            const int y = A.labels[t];
-#pragma unroll
-            for (int vb = 0; vb < 2; ++vb) {
-                const int ii = y - (v0 + wv * 64 + vb * 32);
-                if (ii >= 0 && ii < 32 && ((ii >> 2) & 1) == (lane >> 5)) {
-                    const int rr = (ii & 3) + 4 * (ii >> 3);
+            const int ii = A.labels[t] - (v0 + wv * 128);
+            const bool mine = ii >= 0 && ii < 128 && (((ii >> 2) & 1) == (lane >> 5));
+            if (__builtin_amdgcn_ballot_w64(mine)) {
+                if (mine) {
+                    const int vb = ii >> 5, i2 = ii & 31;
+                    const int rr = (i2 & 3) + 4 * (i2 >> 3);
                     float val = 0.f;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) val = (r == rr) ? acc[vb][rb][r] : val;
+                    for (int b = 0; b < G2_VB; ++b)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) val = (b == vb && r == rr) ? acc[b][rb][r] : val;
                     zy[row] = val;
                 }
             }
         }
+        float m;
+        if (fixed) {
+            m = C;
+        } else {
+            float m0 = -__builtin_inff(), m1 = -__builtin_inff();
+#pragma unroll
+            for (int vb = 0; vb < G2_VB; ++vb)
+#pragma unroll
+                for (int r = 0; r < 16; r += 4) {
+                    m0 = fmaxf(m0, fmaxf(acc[vb][rb][r], acc[vb][rb][r + 1]));
+                    m1 = fmaxf(m1, fmaxf(acc[vb][rb][r + 2], acc[vb][rb][r + 3]));
+                }
+            m = fmaxf(m0, m1);
+            m = fmaxf(m, __shfl_xor(m, 32, 64));
+        }
+        const float ml2 = m * kLog2eF;
+        float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int vb = 0; vb < G2_VB; ++vb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                s4[r & 3] += __builtin_amdgcn_exp2f(fmaf(acc[vb][rb][r], kLog2eF, -ml2));
+        float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+        s += __shfl_xor(s, 32, 64);
+        if (lane < 32) red[wv][lrow] = make_float2(m, s);
     }
     __syncthreads();
-    if (tid < G2_TR) {
-        const int64_t row = r0 + tid;
+    for (int lr = tid; lr < G2_TR; lr += G2_NT) {
+        const int64_t row = r0 + lr;
         if (row < nrows) {
-            const float2 a = red[0][tid], b = red[1][tid];
+            const float2 a = red[0][lr], b = red[1][lr];
             const float m = fmaxf(a.x, b.x);
             float s = 0.f;
             if (a.y > 0.f) s += a.y * __builtin_amdgcn_exp2f((a.x - m) * kLog2eF);
@@ -459,6 +538,7 @@ MlpLayout mlp_layout(int64_t T, int64_t d, int64_t n, int64_t V, int64_t K) {
     L.off_f = off;    off += al256((size_t)L.chunk * d * 2);
     L.off_part = off; off += al256((size_t)L.chunk * L.nvt * sizeof(float2));
     L.off_zy = off;   off += al256((size_t)L.chunk * sizeof(float));
+    L.off_wnorm = off; off += al256((size_t)((V + 255) / 256 + 1) * sizeof(float));
     L.off_ce = off;   off += al256((size_t)T * (K + 1) * sizeof(float));
     L.off_ghat = off; off += al256((size_t)T * n * sizeof(float));
     L.off_outer = off;
@@ -472,10 +552,17 @@ hipError_t launch_mlp(const MlpArgs& A, const MlpLayout& L, unsigned char* ws, f
     uint16_t* F = reinterpret_cast<uint16_t*>(ws + L.off_f);
     float2* part = reinterpret_cast<float2*>(ws + L.off_part);
     float* zy = reinterpret_cast<float*>(ws + L.off_zy);
+    float* wnorm = reinterpret_cast<float*>(ws + L.off_wnorm);
+    const int nwb = (A.V + 255) / 256;
+    float* offset = wnorm + nwb;
     float* ce = reinterpret_cast<float*>(ws + L.off_ce);
     float* ghat = ghat_user ? ghat_user : reinterpret_cast<float*>(ws + L.off_ghat);
     const int64_t total = (int64_t)A.T * (A.K + 1);
     hipError_t e = hipSuccess;
+    hipLaunchKernelGGL(mlp_wnorm_kernel, dim3((unsigned)nwb), dim3(256), 0, stream, A.w_head, A.V, A.d, wnorm);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(mlp_wnorm_final_kernel, dim3(1), dim3(256), 0, stream, wnorm, nwb, A.d, offset);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     for (int64_t g0 = 0; g0 < total; g0 += L.chunk) {
         const int64_t nrows = (total - g0) < L.chunk ? (total - g0) : L.chunk;
         const unsigned b1 = (unsigned)((nrows + G1_ROWS - 1) / G1_ROWS);
@@ -486,8 +573,8 @@ hipError_t launch_mlp(const MlpArgs& A, const MlpLayout& L, unsigned char* ws, f
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (A.gemm1_event && (e = hipEventRecord(A.gemm1_event, stream)) != hipSuccess) return e;
         const int64_t nrt = (nrows + G2_TR - 1) / G2_TR;
-        hipLaunchKernelGGL(mlp_gemm2_kernel, dim3((unsigned)(nrt * L.nvt)), dim3(256), 0, stream, A, g0, nrows, L.nvt,
-                           F, part, zy);
+        hipLaunchKernelGGL(mlp_gemm2_kernel, dim3((unsigned)(nrt * L.nvt)), dim3(G2_NT), 0, stream, A, g0, nrows,
+                           L.nvt, F, part, zy, offset);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (A.gemm2_event && (e = hipEventRecord(A.gemm2_event, stream)) != hipSuccess) return e;
         hipLaunchKernelGGL(mlp_combine_kernel, dim3((unsigned)((nrows + 255) / 256)), dim3(256), 0, stream, g0, nrows,

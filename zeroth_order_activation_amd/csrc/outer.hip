@@ -28,7 +28,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 namespace {
 constexpr int BM = 128, BN = 128, BK = 16, NTH = 256;
 
-constexpr int XM = 128, XN = 128, XK = 32, XSTRIDE = XK + 8;  // bf16x3 tiles; 80-byte LDS rows
+constexpr int XM = 128, XN = 128, XK = 32;  // bf16x3 tiles; 64-byte LDS rows, xor-swizzled pieces
+
+// piece p (16 bytes) of LDS row r lives at piece p ^ ((r >> 2) & 3): conflict-free
+// for both the coalesced row writes and the MFMA fragment reads.
+__device__ __forceinline__ int xswz(int row, int piece) { return row * XK + ((piece ^ ((row >> 2) & 3)) << 3); }
 constexpr double kSplitMinFlop = 4e9;
 
 struct OuterPlan {
@@ -219,10 +223,18 @@ __global__ void __launch_bounds__(256) outer_bf16x3_kernel(const uint16_t* __res
                                                            const uint16_t* __restrict__ Bh, const uint16_t* __restrict__ Bl,
                                                            int64_t M, int64_t N, int64_t Tp, int64_t tchunk,
                                                            float* __restrict__ out) {
-    __shared__ __align__(16) uint16_t S[4][XM * XSTRIDE];  // Ah, Al, Bh, Bl
+    __shared__ __align__(16) uint16_t S[4][XM * XK];  // Ah, Al, Bh, Bl
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w & 1, wn = w >> 1;
-    const int64_t m0 = (int64_t)blockIdx.x * XM, n0 = (int64_t)blockIdx.y * XN;
+    // XCD-aware tile order: workgroups are dealt round-robin to the 8 XCDs, so
+    // block b runs on XCD b % 8.  All N-tiles of one M-tile go to the same XCD
+    // (consecutive blocks of that XCD), whose L2 then serves the shared ghat
+    // slabs to all of them instead of each refetching from HBM.
+    const int64_t nmt = (M + XM - 1) / XM, nnt = (N + XN - 1) / XN;
+    const int64_t b = blockIdx.x, xcd = b % 8, sq = b / 8;
+    const int64_t mt = (sq / nnt) * 8 + xcd, nt = sq % nnt;
+    if (mt >= nmt) return;
+    const int64_t m0 = mt * XM, n0 = nt * XN;
     const int64_t kb0 = (int64_t)blockIdx.z * tchunk;
     const int64_t ke = (kb0 + tchunk < Tp) ? kb0 + tchunk : Tp;
     const uint16_t* src[4] = {Ah, Al, Bh, Bl};
@@ -259,18 +271,18 @@ __global__ void __launch_bounds__(256) outer_bf16x3_kernel(const uint16_t* __res
             for (int jj = 0; jj < 2; ++jj) {
                 const int pi = tid + 256 * jj;
                 const int row = pi >> 2, piece = pi & 3;
-                *reinterpret_cast<uint4*>(&S[o][row * XSTRIDE + 8 * piece]) = reg[o][jj];
+                *reinterpret_cast<uint4*>(&S[o][xswz(row, piece)]) = reg[o][jj];
             }
         __syncthreads();
         if (kb + XK < ke) load(kb + XK, reg);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             uint4 ah[2], al[2], bh[2], bl[2];
-            const int off = kk * 16 + 8 * (lane >> 5);
+            const int piece = kk * 2 + (lane >> 5);
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                const int ra = (wm * 64 + i * 32 + (lane & 31)) * XSTRIDE + off;
-                const int rb = (wn * 64 + i * 32 + (lane & 31)) * XSTRIDE + off;
+                const int ra = xswz(wm * 64 + i * 32 + (lane & 31), piece);
+                const int rb = xswz(wn * 64 + i * 32 + (lane & 31), piece);
                 ah[i] = *reinterpret_cast<const uint4*>(&S[0][ra]);
                 al[i] = *reinterpret_cast<const uint4*>(&S[1][ra]);
                 bh[i] = *reinterpret_cast<const uint4*>(&S[2][rb]);
@@ -320,7 +332,8 @@ hipError_t launch_outer(const float* ghat, const float* x, int64_t T, int64_t n,
         hipLaunchKernelGGL(split_transpose_kernel, dim3((unsigned)(p.Tp / 64), (unsigned)((d + 63) / 64)), dim3(256), 0,
                            stream, x, T, d, p.Tp, bh, bl);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        const dim3 grid((unsigned)((n + XM - 1) / XM), (unsigned)((d + XN - 1) / XN), (unsigned)p.splits);
+        const int64_t nmt8 = ((n + XM - 1) / XM + 7) / 8 * 8;  // M-tiles rounded up to whole XCD groups
+        const dim3 grid((unsigned)(nmt8 * ((d + XN - 1) / XN)), 1, (unsigned)p.splits);
         hipLaunchKernelGGL(outer_bf16x3_kernel, grid, dim3(256), 0, stream, ah, al, bh, bl, n, d, p.Tp, p.tchunk, part);
     } else {
         const dim3 grid((unsigned)((n + BM - 1) / BM), (unsigned)((d + BN - 1) / BN), (unsigned)p.splits);
