@@ -21,7 +21,9 @@ timed on the host cores on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -35,17 +37,116 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 N_CU, CLOCK_GHZ, LANES_PER_CU = 256, 2.4, 64
-VALU_PEAK_GSLOT = N_CU * LANES_PER_CU * CLOCK_GHZ  # 39321.6 G lane-slots/s (one full-rate op per lane per clock)
+# 32-bit vector ALU: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3 T lane-ops/s.
+# The published fp32 vector figure, 157.3 TFLOP/s, is this times 2 (an FMA is two
+# flops) times 2 (packed fp32 issues two lanes per op); the integer multiplies and
+# xors of Philox and the per-channel float work here cannot use packed issue.
+VALU_PEAK_GOPS = N_CU * LANES_PER_CU * CLOCK_GHZ  # 39321.6 G lane-ops/s
 
-# Algorithmic VALU work of one channel-draw of the head estimator, in full-rate
-# lane-slots, with the gfx950 issue costs measured by a microbenchmark
-# (v_mad_u64_u32 full rate; log2/exp2/sqrt/sin/cos half rate, 2 slots):
-#   Philox4x32-10: 10 rounds x (2 v_mad_u64_u32 + 2 three-way xors) = 40 slots per 4 channels -> 10
-#   Box-Muller: per 2 channels 2 int->float + 2 scalings + log2 (2) + scale + sqrt (2)
-#               + sin (2) + cos (2) + 2 products = 15 slots -> 7.5
-#   loss term p_v expm1(sigma a_v): 4 fma (Horner) + 1 mul + 1 fma = 6
-#   running sum r*a: 1
-SLOTS_PER_CHANNEL_DRAW = 10 + 7.5 + 6 + 1
+
+def head_lane_ops_per_channel_draw(deg):
+    """Vector lane-ops one (token, vocabulary channel, draw) of the head estimator needs.
+
+    Philox4x32-10 per 4 channels: the counter words token, draw and layer are the
+    same across a workgroup, so round 1 costs one xor, round 2 one wide multiply
+    and one xor, round 3 one multiply and two xors, round 4 two multiplies and two
+    three-way xors, rounds 5-10 four ops each: 34 -> 8.5 per channel.
+    Box-Muller per 2 channels: u1 (shift, convert, scale) 3, log2 1, sqrt 1,
+    u2 (shift, convert, scale) 3, sin 1, cos 1, two products 2: 12 -> 6.
+    Loss term p_v expm1(sigma a_v) by a degree-D Taylor polynomial with sigma
+    folded into the coefficients: D-1 fma + 1 mul, then 1 fma into the sum: D + 1.
+    Running sum of r a: 1.
+    """
+    return 8.5 + 6.0 + (deg + 1) + 1.0
+
+
+def head_taylor_degree(sigma):
+    """The library's choice: the lowest of 4, 6 whose dropped terms stay below 8e-9
+    for |sigma a| <= 5.7683 sigma (else the library expm1, counted as degree 6)."""
+    xm = sigma * 5.7683
+    for D in (4, 6):
+        if xm ** (D + 1) / math.factorial(D + 1) * math.exp(xm) <= 8e-9:
+            return D
+    return 6
+
+
+# Sources that define each measured kernel: a traffic file stands only while they
+# are unchanged.
+KERNEL_SOURCES = {
+    "head_estimate_kernel": ["head_impl.hpp", "head_f32.hip", "head_bf16.hip", "head.hip", "dust_device.hpp"],
+    "mlp_gemm2_kernel": ["mlp.hip", "dust_device.hpp", "dust_internal.hpp"],
+}
+
+
+def sources_digest(kernel):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "zeroth_order_activation_amd", "csrc", f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def traffic_path(kernel, workload):
+    return os.path.join(ROOT, "profiles", f"traffic_{kernel}_workload{workload}.json")
+
+
+def load_traffic(kernel, workload):
+    """Measured HBM bytes per launch, or None when absent or taken on other sources."""
+    p = traffic_path(kernel, workload)
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("sources_sha256") != sources_digest(kernel):
+        return None
+    return t["bytes_per_launch"]
+
+
+def _counter_sums(d):
+    """{(dispatch, kernel name): {counter: value}} from a rocprofv3 --pmc output folder."""
+    import csv
+    out = {}
+    for root, _, files in os.walk(d):
+        for fn in files:
+            if fn.endswith("counter_collection.csv"):
+                with open(os.path.join(root, fn)) as fh:
+                    for r in csv.DictReader(fh):
+                        k = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+                        out.setdefault(k, {}).setdefault(r["Counter_Name"], 0.0)
+                        out[k][r["Counter_Name"]] += float(r["Counter_Value"])
+    return out
+
+
+def write_traffic(args):
+    """Turn four rocprofv3 --pmc runs (kernel FETCH_SIZE, kernel WRITE_SIZE, and the
+    same two counters on a plain copy of --copy-calibration MiB) into the traffic
+    file of the workload's dominant kernel."""
+    kernel = "head_estimate_kernel" if args.workload in (1, 2, 4) else "mlp_gemm2_kernel"
+    copy_bytes = args.copy_calibration << 20
+    if copy_bytes <= 0:
+        sys.exit("--traffic-from needs --copy-calibration MIB (the size the copy runs used)")
+    res = {}
+    for ctr, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+        k_runs = [v[ctr] for (_, name), v in _counter_sums(os.path.join(args.traffic_from,
+                                                                       f"{sub}_w{args.workload}")).items()
+                  if kernel in name and ctr in v]
+        c_runs = [v[ctr] for (_, name), v in _counter_sums(os.path.join(args.traffic_from, "copy_" + sub)).items()
+                  if ("copy" in name.lower() or "elementwise" in name) and ctr in v]
+        if not k_runs or not c_runs:
+            sys.exit(f"no {ctr} dispatches of {kernel} / the copy under {args.traffic_from}")
+        kib = float(np.mean(k_runs))
+        copy_kib = max(c_runs)
+        factor = copy_bytes / (copy_kib * 1024.0)
+        res[ctr] = {"kib_per_dispatch": kib, "dispatches": len(k_runs), "copy_kib": copy_kib,
+                    "scale": factor, "bytes": kib * 1024.0 * factor}
+    out = {"kernel": kernel, "workload": args.workload, "copy_bytes": copy_bytes,
+           "fetch": res["FETCH_SIZE"], "write": res["WRITE_SIZE"],
+           "bytes_per_launch": res["FETCH_SIZE"]["bytes"] + res["WRITE_SIZE"]["bytes"],
+           "sources_sha256": sources_digest(kernel)}
+    with open(traffic_path(kernel, args.workload), "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
 
 WORKLOAD_NAMES = {
     1: "LM-head estimator fp32 logits: T=256, d=64, V=512, K=64, sigma=1e-2, uniform labels",
@@ -68,6 +169,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB (to scale HBM traffic counters) and exit")
+    ap.add_argument("--traffic-from", metavar="DIR",
+                    help="with --copy-calibration MIB: read the rocprofv3 --pmc folders DIR/fetch_wN, "
+                         "DIR/write_wN (this workload) and DIR/copy_fetch, DIR/copy_write, and write the "
+                         "workload's traffic file under profiles/")
     return ap.parse_args()
 
 
@@ -154,25 +259,27 @@ def run_head(args, c, dust, torch):
     est_ms = float(np.mean([dust.event_elapsed_ms(e[0], e[1]) for e in ev]))
     outer_ms = float(np.mean([dust.event_elapsed_ms(e[1], e[2]) for e in ev]))
     ms_per_step = wall * 1e3 / args.steps
-    achieved = T * K * V * SLOTS_PER_CHANNEL_DRAW / (est_ms / 1e3) / 1e9
+    deg = head_taylor_degree(sigma)
+    ops = head_lane_ops_per_channel_draw(deg)
+    achieved = T * K * V * ops / (est_ms / 1e3) / 1e9
     lb = 4 if "logits" in c else 2
     # bytes every step must move at least once: logits read, g_hat written and read back,
     # x read, grad_w written, labels read
     alg_bytes = T * V * lb + 2 * T * V * 4 + T * d * 4 + V * d * 4 + T * 4
-    traffic = None
-    tfile = os.path.join(ROOT, "profiles", f"traffic_head_workload{args.workload}.json")
-    if os.path.exists(tfile):
-        with open(tfile) as f:
-            traffic = json.load(f).get("bytes_per_launch")
+    # the estimator kernel alone: logits and labels in, g_hat and rewards out
+    kern_bytes = T * V * lb + T * V * 4 + T * 4 + K * T * 4
     out = {
         "dtype": dtype,
         "stages_ms": {"estimator": est_ms, "outer_product": outer_ms},
         "roofline": {"bound": "alu", "kernel": "head_estimate_kernel", "achieved": achieved,
-                     "peak": VALU_PEAK_GSLOT, "unit": "G lane-slots/s", "frac": achieved / VALU_PEAK_GSLOT,
-                     "traffic": traffic, "slots_per_channel_draw": SLOTS_PER_CHANNEL_DRAW,
-                     "channel_draws_per_launch": T * K * V},
+                     "peak": VALU_PEAK_GOPS, "unit": "G lane-ops/s", "frac": achieved / VALU_PEAK_GOPS,
+                     "traffic": load_traffic("head_estimate_kernel", args.workload),
+                     "lane_ops_per_channel_draw": ops, "taylor_degree": deg,
+                     "channel_draws_per_launch": T * K * V, "kernel_ms": est_ms,
+                     "algorithmic_bytes_per_launch": kern_bytes},
         "hbm": {"algorithmic_bytes_per_step": alg_bytes, "GBps": alg_bytes / (ms_per_step / 1e3) / 1e9,
-                "frac": alg_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS},
+                "frac": alg_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS,
+                "estimator_kernel_GBps": kern_bytes / (est_ms / 1e3) / 1e9},
     }
     return ms_per_step, out
 
@@ -210,8 +317,11 @@ def run_linear(args, c, K, dust, torch):
                             "outer_product": outer}
         out["roofline"] = {"bound": "mfma", "kernel": "mlp_gemm2_kernel", "achieved": fl2 / (g2 / 1e3) / 1e12,
                            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                           "frac": fl2 / (g2 / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
-                           "flop_per_launch": fl2}
+                           "frac": fl2 / (g2 / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                           "traffic": load_traffic("mlp_gemm2_kernel", args.workload),
+                           "flop_per_launch": fl2, "kernel_ms": g2,
+                           "algorithmic_bytes_per_launch": rows * d * 2 + V * d * 2 + rows * 4
+                           + (V + 255) // 256 * rows * 8}
         out["mfma_downstream"] = {"gemm1_TFLOPs": fl1 / (g1 / 1e3) / 1e12, "gemm2_TFLOPs": fl2 / (g2 / 1e3) / 1e12,
                                   "both_frac_of_peak": (fl1 + fl2) / ((g1 + g2) / 1e3) / 1e12
                                   / MFMA_BF16_PEAK_TFLOPS}
@@ -227,6 +337,9 @@ def main():
               "(the estimator shards by tokens or draws with one all-reduce of G_W; not built here)",
               file=sys.stderr)
         sys.exit(2)
+    if args.traffic_from:
+        write_traffic(args)
+        return
     import torch
     if args.copy_calibration:
         n = args.copy_calibration << 20
@@ -256,7 +369,7 @@ def main():
         cfg = {"workload": name, "T": c["T"], "d": c["d"], "n": c["n"], "V": c["V"], "K": K, "sigma": c["sigma"]}
     cfg.update({"noise_seed": c["seed_noise"], "layer": c["layer"], "data_seed": 1000 + args.workload})
     out = {
-        "metric": "token-draws/sec per Dust gradient estimate",
+        "metric": "token-draws/sec per Dust gradient estimate; % of HBM BW / MFMA peak",
         "value": c["T"] * K / (ms / 1e3),
         "unit": "token-draws/s",
         "n_gpus": 1,
