@@ -45,59 +45,78 @@ __device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, const
 // Row of the D layout held by register r of a lane (within a 32x32 block).
 __device__ __forceinline__ int drow(int r, int lane) { return (r & 3) + 8 * (r >> 2) + 4 * (lane >> 5); }
 
-// GELU(x) = x Phi(x) (exact erf form), rounded to bf16 (nearest even).  The
-// rounding decision only depends on the fp32 value when that value is not
-// within a few ulps of a bf16 tie; in that rare case (~2^-11 of inputs) the
-// GELU is re-evaluated in fp64 and rounded to fp32 once, so the decision is
-// the one the correctly rounded fp32 value takes.
-__device__ __forceinline__ uint16_t gelu_bf16(float x) {
+// GELU(x) = x Phi(x) (exact erf form), as the fp32 value whose bf16 rounding
+// (nearest even) is taken next.  That decision only depends on the fp32
+// evaluation when the value is not within a few ulps of a bf16 tie; in that
+// rare case (~2^-11 of inputs) the GELU is re-evaluated in fp64 and rounded to
+// fp32 once, so the decision is the one the correctly rounded value takes.
+__device__ __forceinline__ float gelu_f32(float x) {
     float g = 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
     const int low = (int)(__float_as_uint(g) & 0xFFFFu);
     if (__builtin_expect(abs(low - 0x8000) <= 16, 0)) {
         const double xd = (double)x;
         g = (float)(0.5 * xd * (1.0 + erf(xd * 0.70710678118654752440)));
     }
-    return f32_to_bf16_rne(g);
+    return g;
 }
 
 // ---------------------------------------------------------------------------
 // gemm1: F = bf16(LN(x + W2 . bf16(GELU(h + sigma a))))
-// Workgroup: 64 token-rows x all D features, 8 waves; wave w owns features
-// [w*D/8, (w+1)*D/8).  The B operand (64 rows x 32 channels per step) is
-// generated in the prologue -- one channel quad per thread -- and staged in
-// LDS; W2 fragments are read straight from global memory (W2 is small and
-// stays in L2).  The MFMA accumulator restarts every G1_FLUSH k-steps and is
-// added into a separate fp32 total: the partial sums stay small, which keeps
-// the accumulation error of W2 m (and with it the rate of bf16 rounding
-// decisions of the LayerNorm output that it could flip) low.
+// Workgroup: 64 token-rows x all D features in 16 waves (4 per SIMD); wave w
+// owns 32 features (and, for D = 256, one half of the rows).  The B operand
+// (64 rows x 64 channels per k-step) is generated in the prologue -- one
+// channel quad per thread -- into a double-buffered, XOR-swizzled LDS slab;
+// W2 fragments are read straight from global memory (W2 is small and stays in
+// L2; each k-step's fragments are loaded before the generation that hides
+// their latency, and h a whole k-step ahead).  The MFMA accumulator restarts
+// every G1_FLUSH k-steps (512 channels) and is added into an fp32 running
+// total kept in LDS: summing the 2048 products in groups of about sqrt(n)
+// roughly halves the fp32 accumulation error of W2 m (and with it the rate of
+// bf16 rounding decisions of the LayerNorm output that it could flip), while
+// the registers stay within the 128 that 4 waves per SIMD allow.
 // ---------------------------------------------------------------------------
 constexpr int G1_ROWS = 64;
-constexpr int G1_KS = 32;                   // channels per k-step
-constexpr int G1_LDS_STRIDE = G1_KS + 8;    // bf16 elements per LDS row (80 bytes: conflict-free b128 reads)
-constexpr int G1_FLUSH = 4;                 // k-steps (128 channels) per accumulator restart
-constexpr int G1_WAVES = 8;
+constexpr int G1_KS = 64;     // channels per k-step
+constexpr int G1_FLUSH = 8;   // k-steps (512 channels) per accumulator restart
+constexpr int G1_WAVES = 16;
+constexpr int G1_NT = 64 * G1_WAVES;
 
-__device__ __forceinline__ double red_sum(const double (*red)[G1_ROWS], int lr) {
-    double s = 0.0;
-#pragma unroll
-    for (int w = 0; w < G1_WAVES; ++w) s += red[w][lr];
-    return s;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats to a pair of bf16 (round to nearest even), low half first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const f32x2_t v = {lo, hi};
+    const bf16x2_t b = __builtin_convertvector(v, bf16x2_t);
+    uint32_t u;
+    __builtin_memcpy(&u, &b, 4);
+    return u;
 }
 
+// LDS tile of 128-byte rows (64 bf16 = eight 16-byte pieces), with piece p of
+// row r stored at piece p ^ ((r >> 1) & 7).  Sixteen lanes reading the same
+// piece of sixteen consecutive rows (an MFMA fragment), and sixteen lanes
+// writing the eight pieces of two consecutive rows, then both touch all 64
+// banks exactly once.
+__device__ __forceinline__ int swz(int row, int piece) { return row * 64 + ((piece ^ ((row >> 1) & 7)) << 3); }
+
 template <int D>
-__global__ void __launch_bounds__(512) mlp_gemm1_kernel(MlpArgs A, int64_t g0, int64_t nrows, uint16_t* __restrict__ F) {
-    constexpr int DW = D / G1_WAVES;  // features per wave
-    constexpr int NDB = DW / 32;      // 32-feature blocks per wave
-    __shared__ __align__(16) uint16_t Bs[2][G1_ROWS * G1_LDS_STRIDE];
-    __shared__ double red[G1_WAVES][G1_ROWS];
+__global__ void __launch_bounds__(G1_NT, 1) mlp_gemm1_kernel(MlpArgs A, int64_t g0, int64_t nrows, uint16_t* __restrict__ F) {
+    constexpr int FG = D / 32;                   // 32-feature groups (16 or 8)
+    constexpr int RG = G1_WAVES / FG;            // row groups (1 or 2)
+    constexpr int RB = G1_ROWS / 32 / RG;        // 32-row MFMA blocks per wave (2 or 1)
+    constexpr int NV = RB * 16;                  // accumulator values per lane
+    __shared__ __align__(16) uint16_t Bs[2][G1_ROWS * G1_KS];
+    __shared__ __align__(16) float4 tot[NV / 4][G1_NT];   // running totals, lane-interleaved
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int fg = w % FG, rg = w / FG;
     const int64_t rbase = (int64_t)blockIdx.x * G1_ROWS;  // chunk-local row of row 0
     const int n = A.n;
     const int T = A.T;
 
     // generation mapping: one channel quad per thread per k-step
-    const int gen_row = tid >> 3, gen_q = tid & 7;
+    const int gen_row = tid >> 4, gen_q = tid & 15;
     const int64_t gen_lr = rbase + gen_row;
     const bool gen_valid = gen_lr < nrows;
     const int64_t gen_g = g0 + (gen_valid ? gen_lr : 0);
@@ -106,153 +125,183 @@ __global__ void __launch_bounds__(512) mlp_gemm1_kernel(MlpArgs A, int64_t g0, i
     const uint32_t gen_draw = gen_clean ? 0u : A.draw0 + (uint32_t)(gen_g / T - 1);
     const float* hrow = A.h + gen_t * n;
 
-    auto generate = [&](int ks) -> uint2 {
+    // h of the slab after next is loaded a whole k-step ahead of its use (it
+    // streams from beyond L2, and one quad per thread leaves little to
+    // overlap).  Loads and arithmetic are unconditional -- lanes past the rows
+    // or channels read a clamped, valid address and are zeroed at the end -- so
+    // no branch separates a load from its use.
+    const float sig_eff = gen_clean ? 0.f : A.sigma;
+    const bool gen_any = gen_valid;
+    auto load_h = [&](int ks) -> float4 {
         const int c0 = ks * G1_KS + 4 * gen_q;
-        float hv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (gen_valid) {
-            const float4 h4 = *reinterpret_cast<const float4*>(hrow + c0);
-            hv[0] = h4.x; hv[1] = h4.y; hv[2] = h4.z; hv[3] = h4.w;
-            if (!gen_clean) {
-                const f32x4 g = gauss4(A.tok0 + (uint32_t)gen_t, (uint32_t)(c0 >> 2), gen_draw, A.layer, A.k0, A.k1);
+        return *reinterpret_cast<const float4*>(hrow + (c0 < n ? c0 : n - 4));
+    };
+    auto generate = [&](int ks, const float4& h4) -> uint2 {
+        const int c0 = ks * G1_KS + 4 * gen_q;
+        const f32x4 g = gauss4(A.tok0 + (uint32_t)gen_t, (uint32_t)(c0 >> 2), gen_draw, A.layer, A.k0, A.k1);
+        const float hv[4] = {fmaf(sig_eff, g.v[0], h4.x), fmaf(sig_eff, g.v[1], h4.y), fmaf(sig_eff, g.v[2], h4.z),
+                             fmaf(sig_eff, g.v[3], h4.w)};
+        const bool ok = gen_any && c0 < n;
+        float gv[4];
 #pragma unroll
-                for (int c = 0; c < 4; ++c) hv[c] = fmaf(A.sigma, g.v[c], hv[c]);
-            }
-        }
-        uint16_t b[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) b[c] = gen_valid ? gelu_bf16(hv[c]) : (uint16_t)0;
-        uint2 out;
-        out.x = (uint32_t)b[0] | ((uint32_t)b[1] << 16);
-        out.y = (uint32_t)b[2] | ((uint32_t)b[3] << 16);
-        return out;
+        for (int c = 0; c < 4; ++c) gv[c] = ok ? gelu_f32(hv[c]) : 0.f;
+        return make_uint2(pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3]));
     };
     auto store_slab = [&](int buf, uint2 v) {
-        *reinterpret_cast<uint2*>(&Bs[buf][gen_row * G1_LDS_STRIDE + 4 * gen_q]) = v;
+        *reinterpret_cast<uint2*>(&Bs[buf][swz(gen_row, gen_q >> 1) + 4 * (gen_q & 1)]) = v;
     };
 
-    f32x16_t acc[NDB][2], tot[NDB][2];
+    const f32x16_t zero = {};
+    f32x16_t acc[RB];
+    // each thread owns its column of the total: no atomics needed
+    auto flush = [&]() {
 #pragma unroll
-    for (int i = 0; i < NDB; ++i)
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) { acc[i][j][r] = 0.f; tot[i][j][r] = 0.f; }
-
-    const int nks = n / G1_KS;
-    store_slab(0, generate(0));
-    __syncthreads();
-    const uint16_t* w2 = A.w2;
-    for (int ks = 0; ks < nks; ++ks) {
-        const int buf = ks & 1;
-        // W2 fragments for this k-step: feature f = w*DW + db*32 + lane%32, channels k0 + 16*kk + 8*(lane/32)
-        uint4 af[NDB][2];
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const int f = w * DW + db * 32 + (lane & 31);
-                const int k = ks * G1_KS + kk * 16 + 8 * (lane >> 5);
-                af[db][kk] = *reinterpret_cast<const uint4*>(w2 + (int64_t)f * n + k);
+            for (int r4 = 0; r4 < 4; ++r4) {
+                float4 o = tot[rb * 4 + r4][tid];
+                o.x += acc[rb][4 * r4]; o.y += acc[rb][4 * r4 + 1];
+                o.z += acc[rb][4 * r4 + 2]; o.w += acc[rb][4 * r4 + 3];
+                tot[rb * 4 + r4][tid] = o;
             }
+    };
+    const int f = fg * 32 + (lane & 31);           // W2 row of this lane's A fragments
+    const uint16_t* w2row = A.w2 + (int64_t)f * n;
+    const int row0 = rg * RB * 32;                 // first LDS row of this wave
+    const int nks = (n + G1_KS - 1) / G1_KS;
+
+    // One k-step: fetch this k-step's W2 fragments and the h of the slab after
+    // next, generate slab ks + 1 on the VALU (covering both loads), then -- after
+    // adding the accumulator into the LDS total when a group of G1_FLUSH k-steps
+    // has ended (the MFMAs that produced it are long done) -- read slab ks
+    // (buffer ks & 1) and issue the MFMAs.
+    // KQ: 16-channel sub-steps in this k-step (4, or 2 for a last k-step of 32).
+    // hc holds h of slab ks + 1 (loaded a k-step earlier); hl receives h of slab
+    // ks + 2.  The caller alternates the two, so no register copy waits on a load.
+    auto kstep = [&](int ks, auto kq, const float4& hc, float4& hl) {
+        constexpr int KQ = decltype(kq)::value;
+        const int buf = ks & 1;
+        uint4 af[KQ];
+#pragma unroll
+        for (int kk = 0; kk < KQ; ++kk)
+            af[kk] = *reinterpret_cast<const uint4*>(w2row + ks * G1_KS + kk * 16 + 8 * (lane >> 5));
+        hl = load_h(ks + 2 < nks ? ks + 2 : ks);
         uint2 nxt = make_uint2(0, 0);
-        if (ks + 1 < nks) nxt = generate(ks + 1);
+        if (ks + 1 < nks) nxt = generate(ks + 1, hc);
+        if (ks > 0 && ks % G1_FLUSH == 0) {  // uniform
+            flush();
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            uint4 bf[2];
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-                bf[rb] = *reinterpret_cast<const uint4*>(
-                    &Bs[buf][(rb * 32 + (lane & 31)) * G1_LDS_STRIDE + kk * 16 + 8 * (lane >> 5)]);
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int rb = 0; rb < 2; ++rb) acc[db][rb] = mfma32(af[db][kk], bf[rb], acc[db][rb]);
+            for (int rb = 0; rb < RB; ++rb) acc[rb] = zero;
         }
-        if ((ks + 1) % G1_FLUSH == 0 || ks + 1 == nks) {
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
+        for (int kk = 0; kk < KQ; ++kk) {
+            const int piece = kk * 2 + (lane >> 5);
 #pragma unroll
-                for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) { tot[db][rb][r] += acc[db][rb][r]; acc[db][rb][r] = 0.f; }
+            for (int rb = 0; rb < RB; ++rb) {
+                const uint4 bfr = *reinterpret_cast<const uint4*>(&Bs[buf][swz(row0 + rb * 32 + (lane & 31), piece)]);
+                acc[rb] = mfma32(af[kk], bfr, acc[rb]);
+            }
         }
         if (ks + 1 < nks) store_slab(buf ^ 1, nxt);
         __syncthreads();
+    };
+    using Q4 = std::integral_constant<int, 4>;
+    using Q2 = std::integral_constant<int, 2>;
+
+#pragma unroll
+    for (int r4 = 0; r4 < NV / 4; ++r4) tot[r4][tid] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) acc[rb] = zero;
+    float4 ha = load_h(0), hb;
+    store_slab(0, generate(0, ha));
+    ha = load_h(1 < nks ? 1 : 0);
+    __syncthreads();
+    const int nfull = n / G1_KS;  // k-steps of 64 channels; then one of 32 if n % 64 != 0
+    int ks = 0;
+    for (; ks + 2 <= nfull; ks += 2) {
+        kstep(ks, Q4{}, ha, hb);
+        kstep(ks + 1, Q4{}, hb, ha);
     }
+    if (ks < nfull) {
+        kstep(ks, Q4{}, ha, hb);
+        if (nfull < nks) kstep(ks + 1, Q2{}, hb, ha);
+    } else if (nfull < nks) {
+        kstep(ks, Q2{}, ha, hb);
+    }
+    flush();
 
     // ---- epilogue: residual add, LayerNorm over D, bf16 ---------------------
-    // lane holds rows j = rb*32 + lane%32 (rb = 0,1); for each, features
-    // w*DW + db*32 + drow(r, lane).  y = x + o is formed in fp32; the LayerNorm
+    // lane holds rows j = row0 + rb*32 + lane%32; for each, features
+    // fg*32 + drow(r, lane).  y = x + o is formed in fp32; the LayerNorm
     // statistics and the normalised value are computed in fp64 and rounded to
-    // fp32 once before the bf16 rounding.
+    // fp32 once before the bf16 rounding.  The reduction buffer reuses the slabs.
+    double* red = reinterpret_cast<double*>(&Bs[0][0]);   // [G1_WAVES][G1_ROWS]
+    float y[RB][16];
+    double s[RB];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        const int lr = rb * 32 + (lane & 31);
+    for (int rb = 0; rb < RB; ++rb) {
+        const int lr = row0 + rb * 32 + (lane & 31);
         const int64_t row = rbase + lr;
-        const bool valid = row < nrows;
-        const int64_t t = (g0 + (valid ? row : 0)) % T;
-        double s = 0.0;
+        const int64_t t = (g0 + (row < nrows ? row : 0)) % T;
+        s[rb] = 0.0;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const float4 o = tot[rb * 4 + r4][tid];
+            const int ff = fg * 32 + 8 * r4 + 4 * (lane >> 5);
+            const float4 xv = *reinterpret_cast<const float4*>(A.x_res + t * D + ff);
+            y[rb][4 * r4 + 0] = o.x + xv.x;
+            y[rb][4 * r4 + 1] = o.y + xv.y;
+            y[rb][4 * r4 + 2] = o.z + xv.z;
+            y[rb][4 * r4 + 3] = o.w + xv.w;
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const int f = w * DW + db * 32 + 8 * r4 + 4 * (lane >> 5);
-                const float4 xv = *reinterpret_cast<const float4*>(A.x_res + t * D + f);
-                tot[db][rb][4 * r4 + 0] += xv.x;
-                tot[db][rb][4 * r4 + 1] += xv.y;
-                tot[db][rb][4 * r4 + 2] += xv.z;
-                tot[db][rb][4 * r4 + 3] += xv.w;
-#pragma unroll
-                for (int c = 0; c < 4; ++c) s += (double)tot[db][rb][4 * r4 + c];
-            }
-        s += __shfl_xor(s, 32, 64);
-        if (lane < 32) red[w][lr] = s;
+            for (int c = 0; c < 4; ++c) s[rb] += (double)y[rb][4 * r4 + c];
+        }
+        s[rb] += __shfl_xor(s[rb], 32, 64);
     }
+    // the slabs are free once every wave has passed the loop's last barrier
+    auto row_total = [&](int lr) {
+        const int g = lr / (RB * 32);  // row group of that row
+        double v = 0.0;
+#pragma unroll
+        for (int k = 0; k < FG; ++k) v += red[(g * FG + k) * G1_ROWS + lr];
+        return v;
+    };
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+        if (lane < 32) red[w * G1_ROWS + row0 + rb * 32 + lane] = s[rb];
     __syncthreads();
-    double mean[2];
+    double mean[RB];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        const int lr = rb * 32 + (lane & 31);
-        mean[rb] = red_sum(red, lr) * (1.0 / D);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        const int lr = rb * 32 + (lane & 31);
-        double s = 0.0;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const double dv = (double)tot[db][rb][r] - mean[rb];
-                s = fma(dv, dv, s);
-            }
-        s += __shfl_xor(s, 32, 64);
-        if (lane < 32) red[w][lr] = s;
-    }
+    for (int rb = 0; rb < RB; ++rb) mean[rb] = row_total(row0 + rb * 32 + (lane & 31)) * (1.0 / D);
     __syncthreads();
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        const int lr = rb * 32 + (lane & 31);
+    for (int rb = 0; rb < RB; ++rb) {
+        double v = 0.0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const double dv = (double)y[rb][r] - mean[rb];
+            v = fma(dv, dv, v);
+        }
+        v += __shfl_xor(v, 32, 64);
+        if (lane < 32) red[w * G1_ROWS + row0 + rb * 32 + lane] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const int lr = row0 + rb * 32 + (lane & 31);
         const int64_t row = rbase + lr;
-        const double var = red_sum(red, lr) * (1.0 / D);
+        const double var = row_total(lr) * (1.0 / D);
         const double rstd = 1.0 / sqrt(var + (double)A.ln_eps);
         if (row >= nrows) continue;
         uint16_t* frow = F + row * D;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const int ff = fg * 32 + 8 * r4 + 4 * (lane >> 5);
+            float o[4];
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const int f = w * DW + db * 32 + 8 * r4 + 4 * (lane >> 5);
-                uint16_t b[4];
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    b[c] = f32_to_bf16_rne((float)(((double)tot[db][rb][4 * r4 + c] - mean[rb]) * rstd));
-                uint2 pk;
-                pk.x = (uint32_t)b[0] | ((uint32_t)b[1] << 16);
-                pk.y = (uint32_t)b[2] | ((uint32_t)b[3] << 16);
-                *reinterpret_cast<uint2*>(frow + f) = pk;
-            }
+            for (int c = 0; c < 4; ++c) o[c] = (float)(((double)y[rb][4 * r4 + c] - mean[rb]) * rstd);
+            *reinterpret_cast<uint2*>(frow + ff) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+        }
     }
 }
 
@@ -275,13 +324,6 @@ constexpr int G2_WR = G2_RB * 32;     // rows per wave
 // no underflow, so the running maximum (and its second pass) can be skipped.
 constexpr float G2_FIXED_MAX = 40.0f;
 
-// LDS tile of 128-byte rows (64 bf16 = eight 16-byte pieces; a k-step of 64
-// reads whole cache lines), with piece p of row r stored at piece
-// p ^ ((r >> 1) & 7).  Sixteen lanes reading the same piece of sixteen
-// consecutive rows (an MFMA fragment), and sixteen lanes writing the eight
-// pieces of two consecutive rows (a coalesced global load), then both touch
-// all 64 banks exactly once.
-__device__ __forceinline__ int swz(int row, int piece) { return row * 64 + ((piece ^ ((row >> 1) & 7)) << 3); }
 
 // Largest row norm of W_head, as an fp32 upper bound (one workgroup per 256
 // rows, then a single-block maximum).
@@ -567,9 +609,9 @@ hipError_t launch_mlp(const MlpArgs& A, const MlpLayout& L, unsigned char* ws, f
         const int64_t nrows = (total - g0) < L.chunk ? (total - g0) : L.chunk;
         const unsigned b1 = (unsigned)((nrows + G1_ROWS - 1) / G1_ROWS);
         if (A.d == 512)
-            hipLaunchKernelGGL(mlp_gemm1_kernel<512>, dim3(b1), dim3(64 * G1_WAVES), 0, stream, A, g0, nrows, F);
+            hipLaunchKernelGGL(mlp_gemm1_kernel<512>, dim3(b1), dim3(G1_NT), 0, stream, A, g0, nrows, F);
         else
-            hipLaunchKernelGGL(mlp_gemm1_kernel<256>, dim3(b1), dim3(64 * G1_WAVES), 0, stream, A, g0, nrows, F);
+            hipLaunchKernelGGL(mlp_gemm1_kernel<256>, dim3(b1), dim3(G1_NT), 0, stream, A, g0, nrows, F);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (A.gemm1_event && (e = hipEventRecord(A.gemm1_event, stream)) != hipSuccess) return e;
         const int64_t nrt = (nrows + G2_TR - 1) / G2_TR;
