@@ -309,9 +309,11 @@ __global__ void __launch_bounds__(G1_NT, 1) mlp_gemm1_kernel(MlpArgs A, int64_t 
 // gemm2: per (vocab tile of 256, row): partial log-sum-exp of z = W_head F
 // and the label logit.  Workgroup tile 256 vocab x 256 rows, 8 waves of
 // 128 vocab x 64 rows (4 x 2 MFMA blocks, 128 accumulators); both operands
-// staged through LDS in 64-wide k-steps (double-buffered, register prefetch).
-// A 128 x 128 wave tile (4 waves) would read less LDS per MFMA but needs
-// 256 accumulators and spills.
+// go straight from global memory into double-buffered LDS in 64-wide k-steps,
+// and each wave reads the fragments of the next 16-channel sub-step while the
+// current sub-step's MFMAs issue.  A 128 x 128 wave tile would read a third
+// less LDS per MFMA, but its 256 accumulators leave one wave per SIMD, which
+// measured slower.
 // ---------------------------------------------------------------------------
 constexpr int G2_TV = 256, G2_TR = 256, G2_KS = 64;
 constexpr int G2_VB = 4, G2_RB = 2;   // MFMA blocks per wave (vocab, rows): 128 x 64
@@ -368,8 +370,10 @@ __global__ void __launch_bounds__(256) mlp_wnorm_final_kernel(const float* __res
 __global__ void __launch_bounds__(G2_NT, 1) mlp_gemm2_kernel(MlpArgs A, int64_t g0, int64_t nrows, int nvt,
                                                             const uint16_t* __restrict__ F, float2* __restrict__ part,
                                                             float* __restrict__ zy, const float* __restrict__ offset) {
-    __shared__ __align__(16) uint16_t As[2][G2_TV * G2_KS];
-    __shared__ __align__(16) uint16_t Bs[2][G2_TR * G2_KS];
+    // two buffers per operand as separate LDS objects: reads from one provably
+    // do not alias direct loads in flight into the other
+    __shared__ __align__(16) uint16_t As0[G2_TV * G2_KS], As1[G2_TV * G2_KS];
+    __shared__ __align__(16) uint16_t Bs0[G2_TR * G2_KS], Bs1[G2_TR * G2_KS];
     __shared__ float2 red[2][G2_TR];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -383,27 +387,31 @@ __global__ void __launch_bounds__(G2_NT, 1) mlp_gemm2_kernel(MlpArgs A, int64_t 
     const int64_t r0 = rt * G2_TR;
     const int D = A.d, V = A.V;
 
-    // loads: each operand is 256 rows x 64 k = 2048 pieces of 16 bytes
-    constexpr int NL = 2048 / G2_NT;
-    auto load = [&](int ks, uint4 (&ra)[NL], uint4 (&rb)[NL]) {
+    // Each operand tile is 256 rows x 64 k = 2048 pieces of 16 bytes, loaded
+    // straight from global memory into LDS (no register staging).  A direct
+    // load puts lane l of a wave at LDS slot base + l, so the swizzle is applied
+    // on the global side: the lane whose slot s = 8 row + p' holds logical piece
+    // p' ^ ((row >> 1) & 7) of that row.  Rows past V or past the chunk read a
+    // clamped, valid row (those columns are masked and those rows discarded
+    // below), so every load is unconditional.
+    constexpr int NL = 2048 / G2_NT;   // loads per lane per operand and k-step
+    int offa[NL], offb[NL];            // element offsets of this lane's pieces (k-step 0)
+#pragma unroll
+    for (int jj = 0; jj < NL; ++jj) {
+        const int slot = (jj * G2_WAVES + w) * 64 + lane;
+        const int row = slot >> 3, piece = (slot & 7) ^ ((row >> 1) & 7);
+        const int v = min(v0 + row, V - 1);
+        const int64_t rr = min(r0 + (int64_t)row, nrows - 1);
+        offa[jj] = v * D + 8 * piece;
+        offb[jj] = (int)(rr - r0) * D + 8 * piece;
+    }
+    const uint16_t* Fr = F + r0 * D;
+    auto issue_loads = [&](int ks, uint16_t* as, uint16_t* bs) {
 #pragma unroll
         for (int jj = 0; jj < NL; ++jj) {
-            const int pi = tid + G2_NT * jj;
-            const int row = pi >> 3, piece = pi & 7;
-            const int v = v0 + row;
-            ra[jj] = v < V ? *reinterpret_cast<const uint4*>(A.w_head + (int64_t)v * D + ks * G2_KS + 8 * piece)
-                           : make_uint4(0, 0, 0, 0);
-            const int64_t rr = r0 + row;
-            rb[jj] = rr < nrows ? *reinterpret_cast<const uint4*>(F + rr * D + ks * G2_KS + 8 * piece)
-                                : make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto store = [&](int buf, const uint4 (&ra)[NL], const uint4 (&rb)[NL]) {
-#pragma unroll
-        for (int jj = 0; jj < NL; ++jj) {
-            const int pi = tid + G2_NT * jj;
-            *reinterpret_cast<uint4*>(&As[buf][swz(pi >> 3, pi & 7)]) = ra[jj];
-            *reinterpret_cast<uint4*>(&Bs[buf][swz(pi >> 3, pi & 7)]) = rb[jj];
+            const int base = (jj * G2_WAVES + w) * 64 * 8;  // element offset of this wave's 64 slots
+            __builtin_amdgcn_global_load_lds(A.w_head + offa[jj] + ks * G2_KS, as + base, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(Fr + offb[jj] + ks * G2_KS, bs + base, 16, 0, 0);
         }
     };
 
@@ -415,34 +423,55 @@ __global__ void __launch_bounds__(G2_NT, 1) mlp_gemm2_kernel(MlpArgs A, int64_t 
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    const int nks = D / G2_KS;
-    {
-        uint4 ra[NL], rb[NL];
-        load(0, ra, rb);
-        store(0, ra, rb);
-    }
-    __syncthreads();
-    for (int ks = 0; ks < nks; ++ks) {
-        const int buf = ks & 1;
-        uint4 ra[NL], rb[NL];
-        if (ks + 1 < nks) load(ks + 1, ra, rb);
+    // One k-step on (as, bs) while the next tile lands in (as_n, bs_n).  The
+    // fragments of 16-channel sub-step kk + 1 are read while sub-step kk's
+    // MFMAs issue (one LDS read per MFMA), so LDS latency hides behind MFMA work.
+    auto read_frags = [&](const uint16_t* as, const uint16_t* bs, int kk, uint4 (&a)[G2_VB], uint4 (&b)[G2_RB]) {
+        const int piece = kk * 2 + (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < G2_VB; ++i)
+            a[i] = *reinterpret_cast<const uint4*>(&as[swz(wv * 128 + i * 32 + (lane & 31), piece)]);
+#pragma unroll
+        for (int j = 0; j < G2_RB; ++j)
+            b[j] = *reinterpret_cast<const uint4*>(&bs[swz(wr * G2_WR + j * 32 + (lane & 31), piece)]);
+    };
+    auto kstep = [&](int ks, const uint16_t* as, const uint16_t* bs, uint16_t* as_n, uint16_t* bs_n, bool more) {
+        if (more) issue_loads(ks + 1, as_n, bs_n);
+        uint4 af[2][G2_VB], bfr[2][G2_RB];
+        read_frags(as, bs, 0, af[0], bfr[0]);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            uint4 af[G2_VB], bfr[G2_RB];
-            const int piece = kk * 2 + (lane >> 5);
-#pragma unroll
-            for (int i = 0; i < G2_VB; ++i)
-                af[i] = *reinterpret_cast<const uint4*>(&As[buf][swz(wv * 128 + i * 32 + (lane & 31), piece)]);
-#pragma unroll
-            for (int j = 0; j < G2_RB; ++j)
-                bfr[j] = *reinterpret_cast<const uint4*>(&Bs[buf][swz(wr * G2_WR + j * 32 + (lane & 31), piece)]);
+            if (kk < 3) read_frags(as, bs, kk + 1, af[(kk + 1) & 1], bfr[(kk + 1) & 1]);
 #pragma unroll
             for (int i = 0; i < G2_VB; ++i)
 #pragma unroll
-                for (int j = 0; j < G2_RB; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+                for (int j = 0; j < G2_RB; ++j) acc[i][j] = mfma32(af[kk & 1][i], bfr[kk & 1][j], acc[i][j]);
         }
-        if (ks + 1 < nks) store(buf ^ 1, ra, rb);
+        // order: direct loads, the first sub-step's reads, then per sub-step
+        // its MFMAs interleaved with the next sub-step's reads
+        __builtin_amdgcn_sched_group_barrier(0x020, 2 * NL, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, G2_VB + G2_RB, 0);
+#pragma unroll
+        for (int kk = 0; kk < 3; ++kk) {
+#pragma unroll
+            for (int q = 0; q < G2_VB + G2_RB; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, G2_VB * G2_RB - (G2_VB + G2_RB), 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, G2_VB * G2_RB, 0);
+        __builtin_amdgcn_s_waitcnt(0);  // the next tile's direct loads have landed
         __syncthreads();
+    };
+
+    const int nks = D / G2_KS;  // even: D is 256 or 512
+    issue_loads(0, As0, Bs0);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
+    __syncthreads();
+    for (int ks = 0; ks < nks; ks += 2) {
+        kstep(ks, As0, Bs0, As1, Bs1, true);
+        kstep(ks + 1, As1, Bs1, As0, Bs0, ks + 2 < nks);
     }
 
     // ---- epilogue: per row, log-sum-exp over this tile's vocabulary ---------
