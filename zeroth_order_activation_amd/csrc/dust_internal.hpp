@@ -29,6 +29,7 @@ struct HeadPlan {
     int nt;        // threads per workgroup (one workgroup per token)
     int q;         // channel quads per lane
     int pmode;     // 0: probabilities in registers, 1: logit row staged in LDS
+    int ql;        // quads per lane whose running sums live in LDS (pmode 1 only)
     int deg;       // 5: polynomial expm1, 0: library expm1
     size_t lds;    // dynamic LDS bytes
     bool ok;

@@ -26,14 +26,15 @@ HeadPlan plan_head(int64_t V, int logits_dtype, float sigma) {
     } else if (V <= 65536) {
         // The noise of one draw and the running sum of r*a take 2*4*Q registers per
         // lane: 1024 lanes keep that within the 128 VGPRs of 4 waves/SIMD up to
-        // Q = 8; beyond, 768 lanes (3 waves/SIMD, 170 VGPRs) take Q = 17.
+        // Q = 8.  Up to Q = 13 (V <= 53248, bf16 rows) the running sums of 3
+        // quads per lane move to LDS after the row; beyond, Q = 16 spills.
+        p.ql = 0;
         if (V <= 16384) { p.nt = 1024; p.q = 4; }
         else if (V <= 32768) { p.nt = 1024; p.q = 8; }
-        else if (V <= 768 * 4 * 17) { p.nt = 768; p.q = 17; }
+        else if (V <= 1024 * 4 * 13 && logits_dtype == 1) { p.nt = 1024; p.q = 13; p.ql = 3; }
         else { p.nt = 1024; p.q = 16; }
         p.pmode = 1;
-        p.lds = (size_t)nq * (logits_dtype == 0 ? 16 : 8);
-        if ((size_t)p.nt * p.q * (logits_dtype == 0 ? 16 : 8) > kMaxDynLds) {
+        if ((size_t)p.nt * p.q * (logits_dtype == 0 ? 16 : 8) + (size_t)p.ql * p.nt * 16 > kMaxDynLds) {
             p.ok = false;
             p.why = "fp32 logits with V > 32768 do not fit one workgroup's LDS; pass bf16 logits";
         }
@@ -50,7 +51,7 @@ HeadPlan plan_head(int64_t V, int logits_dtype, float sigma) {
         return std::pow(xm, D + 1) / f * std::exp(xm);
     };
     p.deg = rem(4) <= 8e-9 ? 4 : rem(6) <= 8e-9 ? 6 : 0;
-    if (p.pmode == 1) p.lds = (size_t)p.nt * p.q * (logits_dtype == 0 ? 16 : 8);
+    if (p.pmode == 1) p.lds = (size_t)p.nt * p.q * (logits_dtype == 0 ? 16 : 8) + (size_t)p.ql * p.nt * 16;
     return p;
 }
 

@@ -20,9 +20,14 @@
 //
 // Layout: lane l owns channel quads q = l + j*NT (j < Q), so each load and
 // store of a quad is one coalesced 16-byte (fp32) or 8-byte (bf16) access.
-// The noise of the current draw and the running sum of r*a live in registers;
-// each draw costs one workgroup reduction (two floats) and one barrier.
+// The noise of the current draw and the running sum of r*a live in registers
+// (for the widest rows, the running sums of the last QL quads of each lane
+// live in LDS after the logit row instead, so that 4 waves per SIMD fit without
+// spilling); each draw costs one workgroup reduction (two floats) and one
+// barrier.
 #pragma once
+
+#include <type_traits>
 
 #include "dust_device.hpp"
 #include "dust_internal.hpp"
@@ -84,6 +89,30 @@ __device__ __forceinline__ float block_sum(float v, float* sh) {
     return r;
 }
 
+// Log-sum-exp statistics of a row from per-lane pairs (m, s = sum exp(z - m)):
+// pairs merge as M = max(m, m'), s exp(m - M) + s' exp(m' - M); a pair with
+// m = -inf (no entries) contributes nothing.  One wave butterfly, one LDS
+// exchange between the waves.
+__device__ __forceinline__ void merge_ms(float& m, float& s, float m2, float s2) {
+    const float M = fmaxf(m, m2);
+    const float a = m == -__builtin_inff() ? 0.f : s * __expf(m - M);
+    const float b = m2 == -__builtin_inff() ? 0.f : s2 * __expf(m2 - M);
+    m = M;
+    s = a + b;
+}
+template <int NT>
+__device__ __forceinline__ void block_max_sumexp(float& m, float& s, float2* sh) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) merge_ms(m, s, __shfl_xor(m, o, 64), __shfl_xor(s, o, 64));
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = make_float2(m, s);
+    __syncthreads();
+    float2 r = sh[0];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) merge_ms(r.x, r.y, sh[w].x, sh[w].y);
+    m = r.x;
+    s = r.y;
+}
+
 // expm1(sigma a) / sigma  (DEG = 4, 6)  or  expm1(sigma a)  (DEG = 0).
 template <int DEG>
 __device__ __forceinline__ float em1(float a, const HeadArgs& A) {
@@ -115,11 +144,13 @@ __device__ __forceinline__ f32x4 lds_quad(const unsigned char* zl, int q) {
     return r;
 }
 
-template <int NT, int Q, int LT, int PMODE, int DEG>
+template <int NT, int Q, int LT, int PMODE, int DEG, int QL>
 __global__ void __launch_bounds__(NT, (NT == 256 ? 4 : 1)) head_estimate_kernel(HeadArgs A) {
+    static_assert(QL == 0 || PMODE == 1, "LDS running sums sit after the LDS logit row");
+    constexpr int QR = Q - QL;  // quads whose running sums stay in registers
     constexpr int NW = NT / 64;
     constexpr bool SCHED_FENCE = Q >= 8;
-    __shared__ float sh_stat[NW];
+    __shared__ float2 sh_ms[NW];
     __shared__ float sh_red[2][NW][2];
     extern __shared__ __align__(16) unsigned char zlds[];
 
@@ -132,25 +163,19 @@ __global__ void __launch_bounds__(NT, (NT == 256 ? 4 : 1)) head_estimate_kernel(
     const void* row = reinterpret_cast<const unsigned char*>(A.logits) + (size_t)t * V * (LT == 0 ? 4 : 2);
 
     // ---- clean statistics: max, log-sum-exp, probabilities ---------------
+    // Every quad of the lane is loaded at once (the loads are independent, so
+    // their latencies overlap); PMODE 1 stages the row in LDS, padded to NT*Q
+    // quads with -inf (probability 0) so the draw loop needs no bounds test.
+    // One block reduction merges the per-lane (max, sum of exponentials).
     float p[PMODE == 0 ? Q : 1][4];
-    float m = -__builtin_inff();
-    if (PMODE == 0) {
+    float m = -__builtin_inff(), s = 0.f;
+    // consume quad j of the lane: its four logits (-inf past the row)
+    auto keep = [&](int j, const f32x4& z) {
+        if (PMODE == 0) {
 #pragma unroll
-        for (int j = 0; j < Q; ++j) {
+            for (int c = 0; c < 4; ++c) p[PMODE == 0 ? j : 0][c] = z.v[c];
+        } else {
             const int q = tid + j * NT;
-            f32x4 z;
-            if (q < nq) z = load_quad<LT>(row, q, V, vec);
-            else z.v[0] = z.v[1] = z.v[2] = z.v[3] = -__builtin_inff();
-#pragma unroll
-            for (int c = 0; c < 4; ++c) { p[j][c] = z.v[c]; m = fmaxf(m, z.v[c]); }
-        }
-    } else {
-        // the LDS row is padded to NT*Q quads with -inf (probability 0), so the
-        // draw loop needs no bounds test
-        for (int q = tid; q < NT * Q; q += NT) {
-            f32x4 z;
-            if (q < nq) z = load_quad<LT>(row, q, V, vec);
-            else z.v[0] = z.v[1] = z.v[2] = z.v[3] = -__builtin_inff();
             if (LT == 0) {
                 reinterpret_cast<float4*>(zlds)[q] = make_float4(z.v[0], z.v[1], z.v[2], z.v[3]);
             } else {
@@ -159,25 +184,73 @@ __global__ void __launch_bounds__(NT, (NT == 256 ? 4 : 1)) head_estimate_kernel(
                 b.y = (__float_as_uint(z.v[2]) >> 16) | (__float_as_uint(z.v[3]) & 0xFFFF0000u);
                 reinterpret_cast<uint2*>(zlds)[q] = b;
             }
+        }
+    };
+    if (vec) {
+        // uniform fast path: all quads at once, from clamped (always valid)
+        // addresses, kept packed; padding is applied by select afterwards
+        typedef typename std::conditional<LT == 0, float4, uint2>::type raw_t;
+        raw_t raw[Q];
+#pragma unroll
+        for (int j = 0; j < Q; ++j) {
+            const int q = tid + j * NT;
+            raw[j] = reinterpret_cast<const raw_t*>(row)[q < nq ? q : nq - 1];
+        }
+        auto unpack = [&](int j) {
+            f32x4 z;
+            if (LT == 0) {
+                const float4 v = *reinterpret_cast<const float4*>(&raw[j]);
+                z.v[0] = v.x; z.v[1] = v.y; z.v[2] = v.z; z.v[3] = v.w;
+            } else {
+                const uint2 v = *reinterpret_cast<const uint2*>(&raw[j]);
+                z.v[0] = __uint_as_float(v.x << 16);
+                z.v[1] = __uint_as_float(v.x & 0xFFFF0000u);
+                z.v[2] = __uint_as_float(v.y << 16);
+                z.v[3] = __uint_as_float(v.y & 0xFFFF0000u);
+            }
+            if (tid + j * NT >= nq) z.v[0] = z.v[1] = z.v[2] = z.v[3] = -__builtin_inff();
+            return z;
+        };
+#pragma unroll
+        for (int j = 0; j < Q; ++j) {
+            const f32x4 z = unpack(j);
 #pragma unroll
             for (int c = 0; c < 4; ++c) m = fmaxf(m, z.v[c]);
         }
-    }
-    m = block_max<NT>(m, sh_stat);  // its barriers also publish the LDS row
-    float s = 0.f;
-    if (PMODE == 0) {
+        if (m != -__builtin_inff()) {
 #pragma unroll
-        for (int j = 0; j < Q; ++j)
+            for (int j = 0; j < Q; ++j) {
+                const f32x4 z = unpack(j);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) s += __expf(p[j][c] - m);
+                for (int c = 0; c < 4; ++c) s += __expf(z.v[c] - m);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < Q; ++j) keep(j, unpack(j));
     } else {
-        for (int q = tid; q < nq; q += NT) {
-            const f32x4 z = lds_quad<LT>(zlds, q);
+        // rows whose length is not a multiple of 4: element loads, two passes
 #pragma unroll
-            for (int c = 0; c < 4; ++c) s += __expf(z.v[c] - m);
+        for (int j = 0; j < Q; ++j) {
+            const int q = tid + j * NT;
+            f32x4 z;
+            if (q < nq) z = load_quad<LT>(row, q, V, false);
+            else z.v[0] = z.v[1] = z.v[2] = z.v[3] = -__builtin_inff();
+#pragma unroll
+            for (int c = 0; c < 4; ++c) m = fmaxf(m, z.v[c]);
+            keep(j, z);
+        }
+        if (m != -__builtin_inff()) {
+#pragma unroll
+            for (int j = 0; j < Q; ++j) {
+                const int q = tid + j * NT;
+                if (q >= nq) continue;
+                const f32x4 z = load_quad<LT>(row, q, V, false);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) s += __expf(z.v[c] - m);
+            }
         }
     }
-    s = block_sum<NT>(s, sh_stat);
+    block_max_sumexp<NT>(m, s, sh_ms);  // its barrier also publishes the LDS row
     const float lse = m + __logf(s);
     const float lse2 = lse * kLog2e;
     if (PMODE == 0) {
@@ -194,11 +267,15 @@ __global__ void __launch_bounds__(NT, (NT == 256 ? 4 : 1)) head_estimate_kernel(
     const bool owner = (qy % NT) == (uint32_t)tid && y < (uint32_t)V;
 
     const uint32_t tok = A.tok0 + (uint32_t)t;
-    float acc[Q][4];
+    float acc[QR > 0 ? QR : 1][4];
 #pragma unroll
-    for (int j = 0; j < Q; ++j)
+    for (int j = 0; j < QR; ++j)
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[j][c] = 0.f;
+    // running sums of quads j >= QR: float4 slots [j - QR][lane] after the row
+    float4* accl = reinterpret_cast<float4*>(zlds + (size_t)NT * Q * (LT == 0 ? 16 : 8));
+#pragma unroll
+    for (int j = 0; j < QL; ++j) accl[j * NT + tid] = make_float4(0.f, 0.f, 0.f, 0.f);
 
     for (int i = 0; i < A.K; ++i) {
         const uint32_t draw = A.draw0 + (uint32_t)i;
@@ -236,9 +313,16 @@ __global__ void __launch_bounds__(NT, (NT == 256 ? 4 : 1)) head_estimate_kernel(
         for (int w = 0; w < NW; ++w) { S += sh_red[b][w][0]; LY += sh_red[b][w][1]; }
         const float r = A.sigma * LY - log1pf(S * A.smul);
 #pragma unroll
-        for (int j = 0; j < Q; ++j)
+        for (int j = 0; j < QR; ++j)
 #pragma unroll
             for (int c = 0; c < 4; ++c) acc[j][c] = fmaf(r, a[j][c], acc[j][c]);
+#pragma unroll
+        for (int j = QR; j < Q; ++j) {  // only this lane touches its slots: no barrier needed
+            float4 o = accl[(j - QR) * NT + tid];
+            o.x = fmaf(r, a[j][0], o.x); o.y = fmaf(r, a[j][1], o.y);
+            o.z = fmaf(r, a[j][2], o.z); o.w = fmaf(r, a[j][3], o.w);
+            accl[(j - QR) * NT + tid] = o;
+        }
         if (tid == 0 && A.rewards) A.rewards[(size_t)i * A.T + t] = r;
     }
 
@@ -248,20 +332,28 @@ __global__ void __launch_bounds__(NT, (NT == 256 ? 4 : 1)) head_estimate_kernel(
     for (int j = 0; j < Q; ++j) {
         const int q = tid + j * NT;
         if (q >= nq) continue;
+        float v[4];
+        if (j < QR) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) v[c] = acc[j < QR ? j : 0][c];
+        } else {
+            const float4 o = accl[(j - QR) * NT + tid];
+            v[0] = o.x; v[1] = o.y; v[2] = o.z; v[3] = o.w;
+        }
         if (vec) {
-            reinterpret_cast<float4*>(out)[q] = make_float4(acc[j][0] * A.gscale, acc[j][1] * A.gscale,
-                                                            acc[j][2] * A.gscale, acc[j][3] * A.gscale);
+            reinterpret_cast<float4*>(out)[q] = make_float4(v[0] * A.gscale, v[1] * A.gscale,
+                                                            v[2] * A.gscale, v[3] * A.gscale);
         } else {
 #pragma unroll
             for (int c = 0; c < 4; ++c)
-                if (4 * q + c < V) out[4 * q + c] = acc[j][c] * A.gscale;
+                if (4 * q + c < V) out[4 * q + c] = v[c] * A.gscale;
         }
     }
 }
 
-template <int NT, int Q, int LT, int PMODE, int DEG>
+template <int NT, int Q, int LT, int PMODE, int DEG, int QL>
 hipError_t launch_head_variant(const HeadPlan& plan, const HeadArgs& args, hipStream_t stream) {
-    auto k = head_estimate_kernel<NT, Q, LT, PMODE, DEG>;
+    auto k = head_estimate_kernel<NT, Q, LT, PMODE, DEG, QL>;
     if (plan.lds > 0) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)plan.lds);
@@ -274,20 +366,20 @@ hipError_t launch_head_variant(const HeadPlan& plan, const HeadArgs& args, hipSt
 // Dispatch over the compiled variants for one logits type.
 template <int LT>
 hipError_t dispatch_head(const HeadPlan& P, const HeadArgs& A, hipStream_t s) {
-#define DUST_HEAD_CASE(NT_, Q_, PM_)                                                       \
-    if (P.nt == NT_ && P.q == Q_ && P.pmode == PM_) {                                     \
-        return P.deg == 4   ? launch_head_variant<NT_, Q_, LT, PM_, 4>(P, A, s)           \
-               : P.deg == 6 ? launch_head_variant<NT_, Q_, LT, PM_, 6>(P, A, s)           \
-                            : launch_head_variant<NT_, Q_, LT, PM_, 0>(P, A, s);          \
+#define DUST_HEAD_CASE(NT_, Q_, PM_, QL_)                                                  \
+    if (P.nt == NT_ && P.q == Q_ && P.pmode == PM_ && P.ql == QL_) {                        \
+        return P.deg == 4   ? launch_head_variant<NT_, Q_, LT, PM_, 4, QL_>(P, A, s)         \
+               : P.deg == 6 ? launch_head_variant<NT_, Q_, LT, PM_, 6, QL_>(P, A, s)         \
+                            : launch_head_variant<NT_, Q_, LT, PM_, 0, QL_>(P, A, s);        \
     }
-    DUST_HEAD_CASE(256, 1, 0)
-    DUST_HEAD_CASE(256, 2, 0)
-    DUST_HEAD_CASE(256, 4, 0)
-    DUST_HEAD_CASE(256, 8, 0)
-    DUST_HEAD_CASE(1024, 4, 1)
-    DUST_HEAD_CASE(1024, 8, 1)
-    DUST_HEAD_CASE(768, 17, 1)
-    DUST_HEAD_CASE(1024, 16, 1)
+    DUST_HEAD_CASE(256, 1, 0, 0)
+    DUST_HEAD_CASE(256, 2, 0, 0)
+    DUST_HEAD_CASE(256, 4, 0, 0)
+    DUST_HEAD_CASE(256, 8, 0, 0)
+    DUST_HEAD_CASE(1024, 4, 1, 0)
+    DUST_HEAD_CASE(1024, 8, 1, 0)
+    DUST_HEAD_CASE(1024, 13, 1, 3)
+    DUST_HEAD_CASE(1024, 16, 1, 0)
 #undef DUST_HEAD_CASE
     return hipErrorInvalidConfiguration;
 }
