@@ -83,9 +83,15 @@ def test_outer_and_noise_reject_bad_arguments():
 
 def test_workspace_queries():
     L = dust.lib()
+    # large product (bf16-pair outer product): the estimator writes the g_hat
+    # pairs into the outer product's workspace, which then holds both operands
     T, V, d = 4096, 8192, 512
     need = L.dust_head_workspace_bytes(T, V, d, 256)
-    assert need >= 4 * T * V + L.dust_outer_workspace_bytes(T, V, d)
+    assert need == L.dust_outer_workspace_bytes(T, V, d)
+    assert need >= 2 * 2 * T * V + 2 * 2 * T * d
+    # small product (fp32 outer product): g_hat needs a buffer of its own
+    T, V, d = 256, 512, 64
+    assert L.dust_head_workspace_bytes(T, V, d, 64) >= 4 * T * V + L.dust_outer_workspace_bytes(T, V, d)
     assert L.dust_head_workspace_bytes(0, V, d, 1) == 0
 
 

@@ -126,10 +126,15 @@ dust_status dust_outer_product(const float* ghat, const float* x, int64_t T, int
     return ok();
 }
 
+// g_hat needs a home of its own only when the outer product takes the fp32
+// path; on the bf16-pair path the estimator writes the pairs straight into the
+// outer product's workspace.
+static bool head_pairs_path(int64_t T, int64_t V, int64_t d) { return dust::outer_uses_pairs(T, V, d); }
+
 size_t dust_head_workspace_bytes(int64_t T, int64_t V, int64_t d, int64_t K) {
     (void)K;
     if (T <= 0 || V <= 0 || d <= 0) return 0;
-    return head_ghat_bytes(T, V) + dust::outer_workspace_bytes(T, V, d);
+    return (head_pairs_path(T, V, d) ? 0 : head_ghat_bytes(T, V)) + dust::outer_workspace_bytes(T, V, d);
 }
 
 dust_status dust_estimate_head(const void* logits, int logits_dtype, const float* x, const int32_t* labels,
@@ -152,7 +157,8 @@ dust_status dust_estimate_head(const void* logits, int logits_dtype, const float
     const dust::HeadPlan plan = dust::plan_head(V, logits_dtype, sigma);
     if (!plan.ok) return fail(DUST_E_UNSUPPORTED, "dust_estimate_head: %s", plan.why);
 
-    const size_t ghat_ws = ghat ? 0 : head_ghat_bytes(T, V);
+    const bool pairs = head_pairs_path(T, V, d);
+    const size_t ghat_ws = (ghat || pairs) ? 0 : head_ghat_bytes(T, V);
     const size_t outer_ws = dust::outer_workspace_bytes(T, V, d);
     const size_t need = ghat_ws + outer_ws;
     if (need > 0 && (workspace == nullptr || workspace_bytes < need))
@@ -163,13 +169,17 @@ dust_status dust_estimate_head(const void* logits, int logits_dtype, const float
     if (s != DUST_OK) return s;
 
     unsigned char* ws = static_cast<unsigned char*>(workspace);
-    float* g = ghat ? ghat : reinterpret_cast<float*>(ws);
+    float* g = ghat ? ghat : (pairs ? nullptr : reinterpret_cast<float*>(ws));
     void* ows = outer_ws ? ws + ghat_ws : nullptr;
+    const dust::OuterPairs pr = dust::outer_ghat_pairs(T, V, d, ows);
 
     dust::HeadArgs A{};
     A.logits = logits;
     A.labels = labels;
     A.ghat = g;
+    A.ghi = pr.hi;
+    A.glo = pr.lo;
+    A.ldp = pr.ld;
     A.rewards = rewards;
     A.T = (int32_t)T;
     A.V = (int32_t)V;
@@ -200,7 +210,7 @@ dust_status dust_estimate_head(const void* logits, int logits_dtype, const float
     hipError_t e = dust::launch_head(plan, logits_dtype, A, st);
     if (e != hipSuccess) return device_fail("dust_estimate_head: estimator launch", e);
     if ((e = record_stage(0, st)) != hipSuccess) return device_fail("dust_estimate_head: stage event", e);
-    e = dust::launch_outer(g, x, T, V, d, grad_w, ows, outer_ws, st);
+    e = dust::launch_outer(g, x, T, V, d, grad_w, ows, outer_ws, st, pr.hi != nullptr);
     if (e != hipSuccess) return device_fail("dust_estimate_head: outer-product launch", e);
     if ((e = record_stage(1, st)) != hipSuccess) return device_fail("dust_estimate_head: stage event", e);
     return ok();

@@ -15,7 +15,10 @@ hipError_t launch_noise_export(uint64_t seed, uint32_t layer, uint32_t draw0, in
 struct HeadArgs {
     const void* logits;      // [T,V] fp32 or bf16 bits
     const int32_t* labels;   // [T]
-    float* ghat;             // [T,V] out
+    float* ghat;             // [T,V] out, or null
+    uint16_t* ghi;           // [T, ldp] bf16 hi/lo pairs of g_hat (token-major, zero past V), or null
+    uint16_t* glo;
+    int64_t ldp;
     float* rewards;          // [K,T] out or null
     int32_t T, V, K;
     float sigma;
@@ -41,8 +44,17 @@ hipError_t launch_head(const HeadPlan& plan, int logits_dtype, const HeadArgs& a
 
 // ---- grad_w = ghat^T x (fp32 MFMA) --------------------------------------
 size_t outer_workspace_bytes(int64_t T, int64_t n, int64_t d);
+// Where the bf16 pairs of ghat go in the outer-product workspace when the
+// product takes the bf16-pair path (hi == nullptr otherwise): [T.., ld] rows.
+struct OuterPairs {
+    uint16_t* hi;
+    uint16_t* lo;
+    int64_t ld;
+};
+OuterPairs outer_ghat_pairs(int64_t T, int64_t n, int64_t d, void* workspace);
+bool outer_uses_pairs(int64_t T, int64_t n, int64_t d);
 hipError_t launch_outer(const float* ghat, const float* x, int64_t T, int64_t n, int64_t d, float* grad_w,
-                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+                        void* workspace, size_t workspace_bytes, hipStream_t stream, bool pairs_ready = false);
 
 // ---- interior MLP linear ------------------------------------------------
 struct MlpArgs {

@@ -113,6 +113,17 @@ __device__ __forceinline__ void block_max_sumexp(float& m, float& s, float2* sh)
     s = r.y;
 }
 
+// Two floats to a pair of bf16 (round to nearest even), the first in the low half.
+typedef __bf16 hbf16x2_t __attribute__((ext_vector_type(2)));
+typedef float hf32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16_2(float a, float b) {
+    const hf32x2_t v = {a, b};
+    const hbf16x2_t h = __builtin_convertvector(v, hbf16x2_t);
+    uint32_t u;
+    __builtin_memcpy(&u, &h, 4);
+    return u;
+}
+
 // expm1(sigma a) / sigma  (DEG = 4, 6)  or  expm1(sigma a)  (DEG = 0).
 template <int DEG>
 __device__ __forceinline__ float em1(float a, const HeadArgs& A) {
@@ -327,26 +338,40 @@ __global__ void __launch_bounds__(NT, (NT == 256 ? 4 : 1)) head_estimate_kernel(
     }
 
     // ---- g_hat_t = -(1/(K sigma)) sum_i r a ------------------------------------
-    float* out = A.ghat + (size_t)t * V;
+    // fp32 rows and/or the bf16 pairs (hi = bf16(g), lo = bf16(g - hi)) that the
+    // outer product consumes, token-major with the row zero-padded to ldp
+    float* out = A.ghat ? A.ghat + (size_t)t * V : nullptr;
+    uint16_t* ohi = A.ghi ? A.ghi + (size_t)t * A.ldp : nullptr;
+    uint16_t* olo = A.ghi ? A.glo + (size_t)t * A.ldp : nullptr;
 #pragma unroll
     for (int j = 0; j < Q; ++j) {
         const int q = tid + j * NT;
-        if (q >= nq) continue;
         float v[4];
         if (j < QR) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) v[c] = acc[j < QR ? j : 0][c];
+            for (int c = 0; c < 4; ++c) v[c] = acc[j < QR ? j : 0][c] * A.gscale;
         } else {
             const float4 o = accl[(j - QR) * NT + tid];
-            v[0] = o.x; v[1] = o.y; v[2] = o.z; v[3] = o.w;
+            v[0] = o.x * A.gscale; v[1] = o.y * A.gscale; v[2] = o.z * A.gscale; v[3] = o.w * A.gscale;
         }
+        if (ohi && 4 * (int64_t)q < A.ldp) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) v[c] = 4 * q + c < V ? v[c] : 0.f;
+            uint2 h, l;
+            h.x = pack_bf16_2(v[0], v[1]);
+            h.y = pack_bf16_2(v[2], v[3]);
+            l.x = pack_bf16_2(v[0] - __uint_as_float(h.x << 16), v[1] - __uint_as_float(h.x & 0xFFFF0000u));
+            l.y = pack_bf16_2(v[2] - __uint_as_float(h.y << 16), v[3] - __uint_as_float(h.y & 0xFFFF0000u));
+            *reinterpret_cast<uint2*>(ohi + 4 * q) = h;
+            *reinterpret_cast<uint2*>(olo + 4 * q) = l;
+        }
+        if (!out || q >= nq) continue;
         if (vec) {
-            reinterpret_cast<float4*>(out)[q] = make_float4(v[0] * A.gscale, v[1] * A.gscale,
-                                                            v[2] * A.gscale, v[3] * A.gscale);
+            reinterpret_cast<float4*>(out)[q] = make_float4(v[0], v[1], v[2], v[3]);
         } else {
 #pragma unroll
             for (int c = 0; c < 4; ++c)
-                if (4 * q + c < V) out[4 * q + c] = v[c] * A.gscale;
+                if (4 * q + c < V) out[4 * q + c] = v[c];
         }
     }
 }

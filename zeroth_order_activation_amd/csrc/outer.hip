@@ -4,20 +4,23 @@
 // Two paths.  Small products use the fp32 MFMA directly (below).  Large ones
 // (>= 4 GFLOP) split both fp32 operands into bf16 pairs v = hi + lo (hi =
 // bf16(v), lo = bf16(v - hi), so |v - hi - lo| <= 2^-17 |v|) and accumulate
-// hi*hi + hi*lo + lo*hi on the bf16 MFMA in fp32: each product is then within
-// about 3 * 2^-17 of the fp32 product, at 3/16 of the fp32-MFMA time.  The bf16
-// MFMA wants 8 consecutive tokens per lane, so a transpose pass first writes
-// the pairs token-contiguous ([column][token], token count padded to 64).
+// lo*hi + hi*lo + hi*hi on the bf16 MFMA in fp32: each product is then within
+// about 3 * 2^-17 of the fp32 product, at 3/16 of the fp32-MFMA time.  The
+// pairs keep the operands' own token-major layout ([token][column], row pitch
+// padded to whole 256-column tiles, token count to whole 32-token k-steps,
+// padding zero); the bf16 MFMA wants 8 consecutive tokens per lane, which the
+// transposing LDS read (ds_read_b64_tr_b16) delivers from a token-major tile.
 //
-// The contraction runs over tokens, which is the row index of both operands,
-// so a [BK x BM] slab of ghat and a [BK x BN] slab of x are each contiguous
-// row pieces: both are staged through LDS exactly as they lie in memory and
-// read back as MFMA operands with no transpose.  v_mfma_f32_32x32x2_f32
-// takes A[i][k] from lane i + 32k and B[k][j] from lane j + 32k, i.e. one LDS
-// row segment of 32 floats per half-wave.  Token ranges are split over
-// workgroups when the output has too few tiles to fill the 256 CUs; partial
-// sums then go to the workspace and are added in a fixed order (no atomics,
-// bitwise deterministic).
+// fp32 path: the contraction runs over tokens, which is the row index of both
+// operands, so a [BK x BM] slab of ghat and a [BK x BN] slab of x are each
+// contiguous row pieces: both are staged through LDS exactly as they lie in
+// memory and read back as MFMA operands with no transpose.
+// v_mfma_f32_32x32x2_f32 takes A[i][k] from lane i + 32k and B[k][j] from lane
+// j + 32k, i.e. one LDS row segment of 32 floats per half-wave.
+//
+// Token ranges are split over workgroups when the output has too few tiles to
+// fill the 256 CUs; partial sums then go to the workspace and are added in a
+// fixed order (no atomics, bitwise deterministic).
 #include "dust_device.hpp"
 #include "dust_internal.hpp"
 
@@ -28,26 +31,32 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 namespace {
 constexpr int BM = 128, BN = 128, BK = 16, NTH = 256;
 
-constexpr int XM = 128, XN = 128, XK = 32;  // bf16x3 tiles; 64-byte LDS rows, xor-swizzled pieces
-
-// piece p (16 bytes) of LDS row r lives at piece p ^ ((r >> 2) & 3): conflict-free
-// for both the coalesced row writes and the MFMA fragment reads.
-__device__ __forceinline__ int xswz(int row, int piece) { return row * XK + ((piece ^ ((row >> 2) & 3)) << 3); }
+// bf16x3 tiles: 256 x 256 outputs per workgroup (8 waves of 128 x 64), 32-token
+// k-steps.  LDS rows are 256 columns (32 pieces of 16 bytes, 512 bytes: every
+// row starts on the same bank); piece p of row r is stored at piece
+// p ^ (4 (r & 3)).  Half a wave of transposing reads touches four consecutive
+// rows (r & 3 = 0..3) at the same four pieces, which the swizzle moves into
+// four different quarters of the 64 banks.
+constexpr int YT = 256, YK = 32, YWAVES = 8, YNT = 64 * YWAVES;
+__device__ __forceinline__ int yswz(int row, int piece) { return row * YT + ((piece ^ ((row & 3) << 2)) << 3); }
 constexpr double kSplitMinFlop = 4e9;
 
 struct OuterPlan {
     bool x3;         // bf16x3 path
     int splits;
     int64_t tchunk;  // tokens per split
-    int64_t Tp;      // padded token count of the transposed pairs (x3)
+    int64_t Tp;      // padded token count of the pairs (x3)
+    int64_t Mp, Np;  // padded row pitches of the ghat and x pairs (x3)
     size_t off_ah, off_al, off_bh, off_bl, off_part, total;
 };
 
 OuterPlan plan_outer(int64_t T, int64_t n, int64_t d) {
     OuterPlan p{};
     p.x3 = 2.0 * (double)T * (double)n * (double)d >= kSplitMinFlop;
-    const int64_t bm = p.x3 ? XM : BM, bn = p.x3 ? XN : BN, bk = p.x3 ? 64 : BK;
-    p.Tp = p.x3 ? (T + 63) / 64 * 64 : T;
+    const int64_t bm = p.x3 ? YT : BM, bn = p.x3 ? YT : BN, bk = p.x3 ? YK : BK;
+    p.Tp = p.x3 ? (T + YK - 1) / YK * YK : T;
+    p.Mp = p.x3 ? (n + YT - 1) / YT * YT : n;
+    p.Np = p.x3 ? (d + YT - 1) / YT * YT : d;
     const int64_t tiles = ((n + bm - 1) / bm) * ((d + bn - 1) / bn);
     int64_t s = (512 + tiles - 1) / tiles;
     const int64_t smax = (p.Tp + 255) / 256;  // at least 256 tokens per split
@@ -61,10 +70,10 @@ OuterPlan plan_outer(int64_t T, int64_t n, int64_t d) {
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += (bytes + 255) / 256 * 256; return o; };
     if (p.x3) {
-        p.off_ah = take((size_t)n * p.Tp * 2);
-        p.off_al = take((size_t)n * p.Tp * 2);
-        p.off_bh = take((size_t)d * p.Tp * 2);
-        p.off_bl = take((size_t)d * p.Tp * 2);
+        p.off_ah = take((size_t)p.Mp * p.Tp * 2);
+        p.off_al = take((size_t)p.Mp * p.Tp * 2);
+        p.off_bh = take((size_t)p.Np * p.Tp * 2);
+        p.off_bl = take((size_t)p.Np * p.Tp * 2);
     }
     p.off_part = take(p.splits > 1 ? (size_t)p.splits * n * d * sizeof(float) : 0);
     p.total = off;
@@ -161,52 +170,47 @@ __global__ void __launch_bounds__(256) sum_splits_kernel(const float* __restrict
 // ---------------------------------------------------------------------------
 // bf16x3 path
 // ---------------------------------------------------------------------------
-// src [rows, cols] fp32 -> hi, lo [cols, Tp] bf16 (rows >= nrows read as 0).
-// 64 x 64 tiles through LDS: coalesced 256-byte row reads, 128-byte row writes.
-__global__ void __launch_bounds__(256) split_transpose_kernel(const float* __restrict__ src, int64_t nrows, int64_t ncols,
-                                                              int64_t Tp, uint16_t* __restrict__ hi,
-                                                              uint16_t* __restrict__ lo) {
-    constexpr int TS = 64, LS = TS + 8;
-    __shared__ __align__(16) uint16_t th[TS * LS];
-    __shared__ __align__(16) uint16_t tl[TS * LS];
-    const int tid = threadIdx.x;
-    const int64_t t0 = (int64_t)blockIdx.x * TS, c0 = (int64_t)blockIdx.y * TS;
-    const bool vec = (ncols & 3) == 0;
+typedef __bf16 bf16x2_o __attribute__((ext_vector_type(2)));
+typedef float f32x2_o __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16_pair(float a, float b) {  // round to nearest even, a low
+    const f32x2_o v = {a, b};
+    const bf16x2_o h = __builtin_convertvector(v, bf16x2_o);
+    uint32_t u;
+    __builtin_memcpy(&u, &h, 4);
+    return u;
+}
+
+// src [rows, cols] fp32 -> hi, lo [Tp, ldp] bf16, same (token-major) layout,
+// zero past rows x cols.  One thread per 8 columns: 16-byte stores.
+__global__ void __launch_bounds__(256) split_pairs_kernel(const float* __restrict__ src, int64_t nrows, int64_t ncols,
+                                                          int64_t Tp, int64_t ldp, uint16_t* __restrict__ hi,
+                                                          uint16_t* __restrict__ lo) {
+    const int64_t per_row = ldp / 8;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= Tp * per_row) return;
+    const int64_t t = i / per_row, c = (i % per_row) * 8;
+    float v[8];
+    if (t < nrows && c + 8 <= ncols && (ncols & 3) == 0) {
+        const float4 a = *reinterpret_cast<const float4*>(src + t * ncols + c);
+        const float4 b = *reinterpret_cast<const float4*>(src + t * ncols + c + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int row = tid / 16 + 16 * r;
-        const int col = 4 * (tid % 16);
-        const int64_t t = t0 + row, c = c0 + col;
-        float v[4];
-        if (t < nrows && vec && c + 3 < ncols) {
-            const float4 f = *reinterpret_cast<const float4*>(src + t * ncols + c);
-            v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = (t < nrows && c + e < ncols) ? src[t * ncols + c + e] : 0.f;
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint16_t h = f32_to_bf16_rne(v[e]);
-            th[(col + e) * LS + row] = h;
-            tl[(col + e) * LS + row] = f32_to_bf16_rne(v[e] - bf16_to_f32(h));
-        }
+        for (int e = 0; e < 8; ++e) v[e] = (t < nrows && c + e < ncols) ? src[t * ncols + c + e] : 0.f;
     }
-    __syncthreads();
+    uint32_t h[4], l[4];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int idx = tid + 256 * r;  // 64 columns x 8 pieces of 8 tokens
-        const int col = idx >> 3, piece = idx & 7;
-        const int64_t c = c0 + col;
-        if (c >= ncols) continue;
-        const uint4 vh = *reinterpret_cast<const uint4*>(&th[col * LS + 8 * piece]);
-        const uint4 vl = *reinterpret_cast<const uint4*>(&tl[col * LS + 8 * piece]);
-        *reinterpret_cast<uint4*>(hi + c * Tp + t0 + 8 * piece) = vh;
-        *reinterpret_cast<uint4*>(lo + c * Tp + t0 + 8 * piece) = vl;
+    for (int e = 0; e < 4; ++e) {
+        h[e] = pack_bf16_pair(v[2 * e], v[2 * e + 1]);
+        const float h0 = __uint_as_float(h[e] << 16), h1 = __uint_as_float(h[e] & 0xFFFF0000u);
+        l[e] = pack_bf16_pair(v[2 * e] - h0, v[2 * e + 1] - h1);
     }
+    *reinterpret_cast<uint4*>(hi + t * ldp + c) = make_uint4(h[0], h[1], h[2], h[3]);
+    *reinterpret_cast<uint4*>(lo + t * ldp + c) = make_uint4(l[0], l[1], l[2], l[3]);
 }
 
 typedef __bf16 bf16x8_o __attribute__((ext_vector_type(8)));
+typedef short i16x4_o __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x16 mfma_bf16(const uint4& a, const uint4& b, const f32x16& c) {
     bf16x8_o av, bv;
@@ -215,107 +219,194 @@ __device__ __forceinline__ f32x16 mfma_bf16(const uint4& a, const uint4& b, cons
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, c, 0, 0, 0);
 }
 
-// out[m][n] = sum_k Ah[m][k] Bh[n][k] + Ah Bl + Al Bh over k in this split.
-// 128 x 128 tiles, 4 waves of 64 x 64; 32-token k-steps staged through LDS
-// (register prefetch of the next step).  v_mfma_f32_32x32x16_bf16: A[i][k] in
-// lane i + 32*(k/8), B[k][j] in lane j + 32*(k/8), 8 consecutive k per lane.
-__global__ void __launch_bounds__(256) outer_bf16x3_kernel(const uint16_t* __restrict__ Ah, const uint16_t* __restrict__ Al,
-                                                           const uint16_t* __restrict__ Bh, const uint16_t* __restrict__ Bl,
-                                                           int64_t M, int64_t N, int64_t Tp, int64_t tchunk,
-                                                           float* __restrict__ out) {
-    __shared__ __align__(16) uint16_t S[4][XM * XK];  // Ah, Al, Bh, Bl
+// MFMA fragment of a token-major LDS tile: 32 columns from c0, tokens
+// 16 kk .. 16 kk + 15.  v_mfma_f32_32x32x16_bf16 wants column (lane % 32),
+// tokens 8 (lane / 32) .. + 7 in each lane.  The transposing read gives lane
+// 4a + b of a 16-lane group element b of the 8-byte chunks read by lanes a,
+// 4 + a, 8 + a, 12 + a (checked on the device); so lane 4e + a of group g
+// points at token row 8 (g / 2) + e (+ 16 kk, + 4 for the second read),
+// columns c0 + 16 (g % 2) + 4a.  Every term but c0 is either a per-lane
+// constant or a compile-time offset, so each column block needs one lane
+// offset (tr_lane_off) and the reads use immediate offsets.
+__device__ __forceinline__ int tr_lane_off(int c0, int lane) {
+    const int g = lane >> 4, e = (lane >> 2) & 3, a = lane & 3;
+    const int col = c0 + 16 * (g & 1) + 4 * a;
+    return yswz(8 * (g >> 1) + e, col >> 3) + (col & 7);  // rows 8(g/2)+e: (row & 3) = e
+}
+__device__ __forceinline__ uint4 tr_frag(const uint16_t* p) {  // p = tile + lane offset + 16 kk rows
+    uint32_t u[4];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const i16x4_o v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_o*)(p + 4 * r * YT));
+        __builtin_memcpy(&u[2 * r], &v, 8);
+    }
+    return make_uint4(u[0], u[1], u[2], u[3]);
+}
+
+// out[m][n] = sum_k Ah[k][m] Bh[k][n] + Ah Bl + Al Bh over the tokens k of this
+// split.  256 x 256 tiles, 8 waves of 128 (m) x 64 (n).  Each k-step moves the
+// four [32 x 256] pair tiles straight from global memory into LDS (16-byte
+// direct loads; the swizzle is applied on the global side, since a direct load
+// puts lane l at slot base + l), double-buffered in two separate LDS objects
+// so reads of one never wait on loads in flight into the other.
+__global__ void __launch_bounds__(YNT, 1) outer_x3_kernel(const uint16_t* __restrict__ Ah, const uint16_t* __restrict__ Al,
+                                                         const uint16_t* __restrict__ Bh, const uint16_t* __restrict__ Bl,
+                                                         int64_t M, int64_t N, int64_t Mp, int64_t Np, int64_t Tp,
+                                                         int64_t tchunk, float* __restrict__ out) {
+    __shared__ __align__(16) uint16_t L0[4 * YK * YT], L1[4 * YK * YT];  // [plane][token][column], 64 KB each
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w & 1, wn = w >> 1;
     // XCD-aware tile order: workgroups are dealt round-robin to the 8 XCDs, so
     // block b runs on XCD b % 8.  All N-tiles of one M-tile go to the same XCD
     // (consecutive blocks of that XCD), whose L2 then serves the shared ghat
-    // slabs to all of them instead of each refetching from HBM.
-    const int64_t nmt = (M + XM - 1) / XM, nnt = (N + XN - 1) / XN;
+    // tiles to all of them instead of each refetching from HBM.
+    const int64_t nmt = (M + YT - 1) / YT, nnt = (N + YT - 1) / YT;
     const int64_t b = blockIdx.x, xcd = b % 8, sq = b / 8;
     const int64_t mt = (sq / nnt) * 8 + xcd, nt = sq % nnt;
     if (mt >= nmt) return;
-    const int64_t m0 = mt * XM, n0 = nt * XN;
+    const int64_t m0 = mt * YT, n0 = nt * YT;
     const int64_t kb0 = (int64_t)blockIdx.z * tchunk;
     const int64_t ke = (kb0 + tchunk < Tp) ? kb0 + tchunk : Tp;
-    const uint16_t* src[4] = {Ah, Al, Bh, Bl};
 
-    f32x16 acc[2][2];
+    // direct loads: 4 planes x 32 rows x 32 pieces = 4096 slots, 8 per lane;
+    // load jj of wave w fills slots (8 jj + w) * 64 .. + 63, all of plane
+    // (8 jj + w) / 16, rows 2 ((8 jj + w) % 16) + lane / 32.  The lane's source
+    // offset only depends on jj % 2 and on the plane pitch.
+    constexpr int NL = 4 * YK * (YT / 8) / YNT;
+    int offl[2][2];  // [plane is B][jj % 2]
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int pb = 0; pb < 2; ++pb)
+#pragma unroll
+        for (int odd = 0; odd < 2; ++odd) {
+            const int row = (odd * 8 + w) * 2 + (lane >> 5);
+            const int piece = (lane & 31) ^ ((row & 3) << 2);
+            const int64_t ld = pb ? Np : Mp, c0 = pb ? n0 : m0;
+            offl[pb][odd] = (int)(row * ld + c0 + 8 * piece);
+        }
+    auto issue_loads = [&](int64_t kb, uint16_t* dst) {
+#pragma unroll
+        for (int jj = 0; jj < NL; ++jj) {
+            const int blk = jj * YWAVES + w, plane = blk >> 4;  // plane = jj / 2 (8 waves)
+            const uint16_t* base = plane == 0 ? Ah : plane == 1 ? Al : plane == 2 ? Bh : Bl;
+            const int64_t ld = plane < 2 ? Mp : Np;
+            __builtin_amdgcn_global_load_lds(base + kb * ld + offl[plane >= 2][jj & 1], dst + blk * 64 * 8, 16, 0, 0);
+        }
+    };
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // loads: per operand 128 rows x 32 tokens = 512 pieces of 16 bytes -> 2 per thread
-    auto load = [&](int64_t kb, uint4 (&reg)[4][2]) {
+    constexpr int PL = YK * YT;  // elements per plane tile
+    int oa[4], ob[2];            // lane offsets of the A and B column blocks
 #pragma unroll
-        for (int o = 0; o < 4; ++o)
+    for (int i = 0; i < 4; ++i) oa[i] = tr_lane_off(wm * 128 + 32 * i, lane);
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const int pi = tid + 256 * jj;
-                const int row = pi >> 2, piece = pi & 3;
-                const int64_t grow = (o < 2 ? m0 : n0) + row;
-                const int64_t lim = o < 2 ? M : N;
-                reg[o][jj] = grow < lim ? *reinterpret_cast<const uint4*>(src[o] + grow * Tp + kb + 8 * piece)
-                                        : make_uint4(0, 0, 0, 0);
-            }
-    };
-    uint4 reg[4][2];
-    load(kb0, reg);
-    for (int64_t kb = kb0; kb < ke; kb += XK) {
-        __syncthreads();
+    for (int j = 0; j < 2; ++j) ob[j] = tr_lane_off(wn * 64 + 32 * j, lane);
+    auto read_frags = [&](const uint16_t* t, int kk, uint4 (&ah)[4], uint4 (&al)[4], uint4 (&bh)[2], uint4 (&bl)[2]) {
 #pragma unroll
-        for (int o = 0; o < 4; ++o)
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const int pi = tid + 256 * jj;
-                const int row = pi >> 2, piece = pi & 3;
-                *reinterpret_cast<uint4*>(&S[o][xswz(row, piece)]) = reg[o][jj];
-            }
-        __syncthreads();
-        if (kb + XK < ke) load(kb + XK, reg);
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            uint4 ah[2], al[2], bh[2], bl[2];
-            const int piece = kk * 2 + (lane >> 5);
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int ra = xswz(wm * 64 + i * 32 + (lane & 31), piece);
-                const int rb = xswz(wn * 64 + i * 32 + (lane & 31), piece);
-                ah[i] = *reinterpret_cast<const uint4*>(&S[0][ra]);
-                al[i] = *reinterpret_cast<const uint4*>(&S[1][ra]);
-                bh[i] = *reinterpret_cast<const uint4*>(&S[2][rb]);
-                bl[i] = *reinterpret_cast<const uint4*>(&S[3][rb]);
-            }
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    acc[i][j] = mfma_bf16(al[i], bh[j], acc[i][j]);
-                    acc[i][j] = mfma_bf16(ah[i], bl[j], acc[i][j]);
-                    acc[i][j] = mfma_bf16(ah[i], bh[j], acc[i][j]);
-                }
+        for (int i = 0; i < 4; ++i) {
+            ah[i] = tr_frag(t + oa[i] + 16 * kk * YT);
+            al[i] = tr_frag(t + PL + oa[i] + 16 * kk * YT);
         }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            bh[j] = tr_frag(t + 2 * PL + ob[j] + 16 * kk * YT);
+            bl[j] = tr_frag(t + 3 * PL + ob[j] + 16 * kk * YT);
+        }
+    };
+    auto kstep = [&](int64_t kb, const uint16_t* cur, uint16_t* nxt, bool more) {
+        if (more) issue_loads(kb + YK, nxt);
+        uint4 ah[4], al[4], bh[2], bl[2], nbh[2], nbl[2];
+        read_frags(cur, 0, ah, al, bh, bl);
+        auto pass = [&](const uint4 (&a)[4], const uint4 (&b)[2]) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) acc[i][j] = mfma_bf16(a[i], b[j], acc[i][j]);
+        };
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            nbh[j] = tr_frag(cur + 2 * PL + ob[j] + 16 * YT);
+            nbl[j] = tr_frag(cur + 3 * PL + ob[j] + 16 * YT);
+        }
+        pass(al, bh);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) al[i] = tr_frag(cur + PL + oa[i] + 16 * YT);
+        pass(ah, bl);
+        pass(ah, bh);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ah[i] = tr_frag(cur + oa[i] + 16 * YT);
+        pass(al, nbh);
+        pass(ah, nbl);
+        pass(ah, nbh);
+        // order: direct loads, the first sub-step's 24 reads, the B reads of the
+        // second, then the passes with the A reads in between
+        __builtin_amdgcn_sched_group_barrier(0x020, NL, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 24 + 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 24, 0);
+        __builtin_amdgcn_s_waitcnt(0);  // the next tile's direct loads have landed
+        __syncthreads();
+    };
+
+    issue_loads(kb0, L0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int64_t kb = kb0; kb < ke; kb += 2 * YK) {
+        kstep(kb, L0, L1, kb + YK < ke);
+        if (kb + YK < ke) kstep(kb + YK, L1, L0, kb + 2 * YK < ke);
     }
 
     float* o = out + (int64_t)blockIdx.z * M * N;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int64_t row = m0 + wm * 64 + i * 32 + (r & 3) + 8 * (r >> 2) + 4 * (lane >> 5);
+                const int64_t row = m0 + wm * 128 + i * 32 + (r & 3) + 8 * (r >> 2) + 4 * (lane >> 5);
                 const int64_t col = n0 + wn * 64 + j * 32 + (lane & 31);
                 if (row < M && col < N) o[row * N + col] = acc[i][j][r];
             }
 }
 
+// zero rows [r0, r1) of two [*, ld] bf16 planes (token padding of pairs written elsewhere)
+__global__ void __launch_bounds__(256) zero_rows_kernel(uint16_t* __restrict__ a, uint16_t* __restrict__ b, int64_t r0,
+                                                        int64_t r1, int64_t ld) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 8 elements each
+    const int64_t n8 = (r1 - r0) * ld / 8;
+    if (i >= n8) return;
+    const int64_t off = r0 * ld + 8 * i;
+    *reinterpret_cast<uint4*>(a + off) = make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(b + off) = make_uint4(0, 0, 0, 0);
+}
+
 size_t outer_workspace_bytes(int64_t T, int64_t n, int64_t d) { return plan_outer(T, n, d).total; }
 
+bool outer_uses_pairs(int64_t T, int64_t n, int64_t d) { return plan_outer(T, n, d).x3; }
+
+OuterPairs outer_ghat_pairs(int64_t T, int64_t n, int64_t d, void* workspace) {
+    const OuterPlan p = plan_outer(T, n, d);
+    OuterPairs r{nullptr, nullptr, 0};
+    if (!p.x3 || workspace == nullptr) return r;
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    r.hi = reinterpret_cast<uint16_t*>(ws + p.off_ah);
+    r.lo = reinterpret_cast<uint16_t*>(ws + p.off_al);
+    r.ld = p.Mp;
+    return r;
+}
+
 hipError_t launch_outer(const float* ghat, const float* x, int64_t T, int64_t n, int64_t d, float* grad_w,
-                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                        void* workspace, size_t workspace_bytes, hipStream_t stream, bool pairs_ready) {
     const OuterPlan p = plan_outer(T, n, d);
     if (p.total > 0 && (workspace == nullptr || workspace_bytes < p.total)) return hipErrorInvalidValue;
     unsigned char* ws = static_cast<unsigned char*>(workspace);
@@ -326,15 +417,23 @@ hipError_t launch_outer(const float* ghat, const float* x, int64_t T, int64_t n,
         uint16_t* al = reinterpret_cast<uint16_t*>(ws + p.off_al);
         uint16_t* bh = reinterpret_cast<uint16_t*>(ws + p.off_bh);
         uint16_t* bl = reinterpret_cast<uint16_t*>(ws + p.off_bl);
-        hipLaunchKernelGGL(split_transpose_kernel, dim3((unsigned)(p.Tp / 64), (unsigned)((n + 63) / 64)), dim3(256), 0,
-                           stream, ghat, T, n, p.Tp, ah, al);
+        const int64_t ga = p.Tp * p.Mp / 8, gb = p.Tp * p.Np / 8;
+        if (!pairs_ready) {
+            hipLaunchKernelGGL(split_pairs_kernel, dim3((unsigned)((ga + 255) / 256)), dim3(256), 0, stream, ghat, T, n,
+                               p.Tp, p.Mp, ah, al);
+        } else if (p.Tp > T) {  // rows 0..T-1 (all Mp columns) came from the estimator
+            const int64_t z8 = (p.Tp - T) * p.Mp / 8;
+            hipLaunchKernelGGL(zero_rows_kernel, dim3((unsigned)((z8 + 255) / 256)), dim3(256), 0, stream, ah, al, T, p.Tp,
+                               p.Mp);
+        }
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL(split_transpose_kernel, dim3((unsigned)(p.Tp / 64), (unsigned)((d + 63) / 64)), dim3(256), 0,
-                           stream, x, T, d, p.Tp, bh, bl);
+        hipLaunchKernelGGL(split_pairs_kernel, dim3((unsigned)((gb + 255) / 256)), dim3(256), 0, stream, x, T, d, p.Tp,
+                           p.Np, bh, bl);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        const int64_t nmt8 = ((n + XM - 1) / XM + 7) / 8 * 8;  // M-tiles rounded up to whole XCD groups
-        const dim3 grid((unsigned)(nmt8 * ((d + XN - 1) / XN)), 1, (unsigned)p.splits);
-        hipLaunchKernelGGL(outer_bf16x3_kernel, grid, dim3(256), 0, stream, ah, al, bh, bl, n, d, p.Tp, p.tchunk, part);
+        const int64_t nmt8 = ((n + YT - 1) / YT + 7) / 8 * 8;  // M-tiles rounded up to whole XCD groups
+        const dim3 grid((unsigned)(nmt8 * ((d + YT - 1) / YT)), 1, (unsigned)p.splits);
+        hipLaunchKernelGGL(outer_x3_kernel, grid, dim3(YNT), 0, stream, ah, al, bh, bl, n, d, p.Mp, p.Np, p.Tp, p.tchunk,
+                           part);
     } else {
         const dim3 grid((unsigned)((n + BM - 1) / BM), (unsigned)((d + BN - 1) / BN), (unsigned)p.splits);
         hipLaunchKernelGGL(outer_f32_kernel, grid, dim3(NTH), 0, stream, ghat, x, T, n, d, p.tchunk, part);
