@@ -166,6 +166,8 @@ def parse():
     ap.add_argument("--workload", type=int, default=2, choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--draws", type=int, default=1024, help="K for workload 5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-alignment", action="store_true",
+                    help="MLP-linear workloads: skip the cosine to the backprop gradient")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB (to scale HBM traffic counters) and exit")
@@ -197,21 +199,24 @@ def cpu_baseline_head(case, target_s):
 
 
 def cpu_baseline_linear(case, K, target_s):
-    """The oracle on the first tokens of the workload, all their draws."""
+    """The oracle on the first tokens of the workload, all their draws (beyond 1024 draws:
+    the first 1024, the work being linear in K)."""
     import oracle
 
-    ntok = 2
+    Ku = min(K, 1024)
+    ntok = 1
     while True:
         t0 = time.perf_counter()
-        oracle.linear_estimate(case["h"], case["x_res"], case["w2_bf16"], case["w_head_bf16"], case["labels"], K,
+        oracle.linear_estimate(case["h"], case["x_res"], case["w2_bf16"], case["w_head_bf16"], case["labels"], Ku,
                                case["sigma"], case["ln_eps"], case["seed_noise"], case["layer"],
                                tokens=np.arange(ntok))
         el = time.perf_counter() - t0
         if el >= target_s / 3 or ntok >= case["T"]:
             break
         ntok = min(case["T"], int(ntok * max(2.0, target_s / max(el, 1e-3))))
-    return {"value": ntok * K / el, "unit": "token-draws/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"first {ntok} of {case['T']} tokens x all {K} draws (clean + perturbed downstream rows), "
+    draws = f"all {K} draws" if Ku == K else f"the first {Ku} of {K} draws (rate extrapolated: work is linear in K)"
+    return {"value": ntok * Ku / el, "unit": "token-draws/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"first {ntok} of {case['T']} tokens x {draws} (clean + perturbed downstream rows), "
                       f"numpy fp64 with C noise, {el:.1f} s"}
 
 
@@ -284,6 +289,36 @@ def run_head(args, c, dust, torch):
     return ms_per_step, out
 
 
+def analytic_alignment(c, gw, K, torch):
+    """Cosine of the estimate to the backprop gradient of sum_t CE_t w.r.t. W1 (fp64
+    autograd through the unrounded downstream GELU -> W2 -> +x -> LayerNorm -> head -> CE),
+    and the alignment law 1/sqrt(1 + c/K) of the TL;DR page (section 2, c_max = 1) with
+    c = (n + 1) sum_t |u_t|^2 |g_t|^2 / |G|_F^2 (the estimator's covariance in the linear
+    regime).  Measurement only; outside the timed region."""
+    f64 = torch.float64
+    dev = gw.device
+
+    def bf16v(bits):
+        return torch.from_numpy((bits.astype(np.uint32) << 16).view(np.float32)).to(dev, f64)
+
+    h = torch.from_numpy(c["h"]).to(dev, f64).requires_grad_(True)
+    xr = torch.from_numpy(c["x_res"]).to(dev, f64)
+    u = torch.from_numpy(c["u"]).to(dev, f64)
+    w2, wh = bf16v(c["w2_bf16"]), bf16v(c["w_head_bf16"])
+    y = torch.from_numpy(c["labels"].astype(np.int64)).to(dev)
+    m = 0.5 * h * (1.0 + torch.erf(h / math.sqrt(2.0)))
+    f = torch.nn.functional.layer_norm(xr + m @ w2.T, (xr.shape[1],), eps=c["ln_eps"])
+    loss = torch.nn.functional.cross_entropy(f @ wh.T, y, reduction="sum")
+    (g,) = torch.autograd.grad(loss, h)
+    G = g.T @ u
+    n = g.shape[1]
+    cl = float((n + 1) * ((u * u).sum(1) * (g * g).sum(1)).sum() / (G * G).sum())
+    est = gw.to(f64)
+    cos = float((est * G).sum() / (est.norm() * G.norm()))
+    return {"cosine": cos, "predicted": 1.0 / math.sqrt(1.0 + cl / K), "c": cl, "K": K,
+            "reference": "fp64 autograd gradient of sum_t CE_t w.r.t. W1 (unrounded downstream)"}
+
+
 def run_linear(args, c, K, dust, torch):
     T, d, n, V, sigma = c["T"], c["d"], c["n"], c["V"], c["sigma"]
     u, h, xr = (torch.from_numpy(c[k]).cuda() for k in ("u", "h", "x_res"))
@@ -327,6 +362,13 @@ def run_linear(args, c, K, dust, torch):
                                   / MFMA_BF16_PEAK_TFLOPS}
     else:
         out["mfma_downstream"] = {"both_TFLOPs_whole_step": (fl1 + fl2) / (ms_per_step / 1e3) / 1e12}
+    # bytes the step must move at least once: its inputs and G_W (F stays on chip in
+    # principle; its HBM round trip is not counted)
+    alg_bytes = 4 * T * (d + n + d) + 2 * d * n + 2 * V * d + 4 * T + 4 * n * d
+    out["hbm"] = {"algorithmic_bytes_per_step": alg_bytes, "GBps": alg_bytes / (ms_per_step / 1e3) / 1e9,
+                  "frac": alg_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS}
+    if not args.no_alignment:
+        out["alignment"] = analytic_alignment(c, gw, K, torch)
     return ms_per_step, out
 
 
