@@ -86,6 +86,13 @@ def _lib():
                                         ctypes.c_int64, ctypes.c_double, ctypes.c_uint64,
                                         ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
                                         _f64p, ctypes.c_void_p, ctypes.c_void_p]
+        L.orc_window_offset.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
+                                        ctypes.c_uint32]
+        L.orc_window_offset.restype = ctypes.c_uint32
+        L.orc_head_estimate_subset.argtypes = [_f64p, _i32p, ctypes.c_int64, ctypes.c_int64,
+                                               ctypes.c_int64, ctypes.c_int64, ctypes.c_double, ctypes.c_uint64,
+                                               ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
+                                               _f64p, ctypes.c_void_p, ctypes.c_void_p]
         L.orc_num_threads.restype = ctypes.c_int
         _lib_handle = L
     return _lib_handle
@@ -145,6 +152,33 @@ def head_estimate(logits, labels, K: int, sigma: float, seed: int, layer: int,
     ce0 = np.zeros(T, np.float64)
     _lib().orc_head_estimate(z, y, T, V, K, float(sigma), seed, layer, token_offset,
                              draw_offset, ghat, rew.ctypes.data, ce0.ctypes.data)
+    return ghat, rew, ce0
+
+
+def window_offset(seed: int, layer: int, draw: int, token: int, nq: int) -> int:
+    """Offset of the perturbed window of channel quads for (token, draw) in the
+    vocabulary-subset head estimator (see head_estimate_subset)."""
+    return int(_lib().orc_window_offset(seed, layer, draw, token, nq))
+
+
+def head_estimate_subset(logits, labels, K: int, m: int, sigma: float, seed: int, layer: int,
+                         token_offset: int = 0, draw_offset: int = 0):
+    """Head estimator with a vocabulary subset per draw (TL;DR page, section 1,
+    "reducing interference"; the subset rule is this build's reading): a cyclic
+    window of m/4 channel quads at a per-(token, draw) Philox offset, plus the
+    label, perturbed with the full estimator's noise; the plain cross-entropy of
+    the perturbed row; each channel weighted by the inverse of its inclusion
+    probability.  Returns (ghat [T,V], rewards [K,T], ce0 [T]), fp64."""
+    if m < 4 or m % 4:
+        raise ValueError("m must be a positive multiple of 4")
+    z = np.ascontiguousarray(logits, dtype=np.float64)
+    y = np.ascontiguousarray(labels, dtype=np.int32)
+    T, V = z.shape
+    ghat = np.zeros((T, V), np.float64)
+    rew = np.zeros((K, T), np.float64)
+    ce0 = np.zeros(T, np.float64)
+    _lib().orc_head_estimate_subset(z, y, T, V, K, m, float(sigma), seed, layer, token_offset,
+                                    draw_offset, ghat, rew.ctypes.data, ce0.ctypes.data)
     return ghat, rew, ce0
 
 

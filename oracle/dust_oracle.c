@@ -188,3 +188,72 @@ void orc_head_estimate(const double *logits, const int32_t *labels,
         free(zt);
     }
 }
+
+
+/*
+ * Vocabulary-subset head estimator ([TLDR] section 1, "reducing interference":
+ * only part of the vocabulary is perturbed per head draw; the pages give no
+ * rule).  Reading: per (token, draw) the subset S is a window of mq = m/4
+ * consecutive channel quads, cyclic over the nq = ceil(V/4) quads, at an
+ * offset o drawn from word 0 of Philox4x32-10 on the counter
+ * (token, 0xFFFFFFFF, draw, layer) as o = (w * nq) >> 32, plus the label.
+ * The noise on S is the full estimator's a_v; outside S nothing is perturbed;
+ * the loss is the plain cross-entropy of the perturbed row.  Each channel is
+ * weighted by the inverse of its inclusion probability pi_v (mq/nq for window
+ * channels, 1 for the label), which keeps the estimate unbiased:
+ *   ghat_v = -(1/(K sigma)) sum_i r_i a_v^(i) 1[v in S_i] / pi_v.
+ * With mq >= nq the window is the whole vocabulary and this is
+ * orc_head_estimate.
+ */
+uint32_t orc_window_offset(uint64_t seed, uint32_t layer, uint32_t draw, uint32_t token, uint32_t nq)
+{
+    uint32_t ctr[4] = {token, 0xFFFFFFFFu, draw, layer};
+    uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t out[4];
+    orc_philox4x32_10(ctr, key, out);
+    return (uint32_t)(((uint64_t)out[0] * (uint64_t)nq) >> 32);
+}
+
+void orc_head_estimate_subset(const double *logits, const int32_t *labels,
+                              int64_t T, int64_t V, int64_t K, int64_t m, double sigma,
+                              uint64_t seed, uint32_t layer, uint32_t token_offset,
+                              uint32_t draw_offset, double *ghat, double *rewards, double *ce0)
+{
+    const int64_t nq = (V + 3) / 4;
+    const int64_t mq = m / 4 < nq ? m / 4 : nq;
+    const double pi_win = (double)mq / (double)nq;
+    #pragma omp parallel
+    {
+        double *a = (double *)malloc((size_t)V * sizeof(double));
+        double *zt = (double *)malloc((size_t)V * sizeof(double));
+        unsigned char *in = (unsigned char *)malloc((size_t)V);
+        #pragma omp for schedule(dynamic, 1)
+        for (int64_t t = 0; t < T; ++t) {
+            const double *z = logits + t * V;
+            int32_t y = labels[t];
+            double c0 = row_ce(z, V, y);
+            if (ce0) ce0[t] = c0;
+            double *g = ghat + t * V;
+            for (int64_t v = 0; v < V; ++v) g[v] = 0.0;
+            for (int64_t i = 0; i < K; ++i) {
+                const uint32_t draw = draw_offset + (uint32_t)i, tok = token_offset + (uint32_t)t;
+                const int64_t o = orc_window_offset(seed, layer, draw, tok, (uint32_t)nq);
+                orc_noise(seed, layer, draw, tok, V, a);
+                for (int64_t v = 0; v < V; ++v) {
+                    in[v] = ((v / 4 - o + nq) % nq) < mq || v == y;
+                    zt[v] = in[v] ? z[v] + sigma * a[v] : z[v];
+                }
+                double r = c0 - row_ce(zt, V, y);
+                if (rewards) rewards[i * T + t] = r;
+                for (int64_t v = 0; v < V; ++v)
+                    if (in[v]) g[v] += r * a[v] / (v == y ? 1.0 : pi_win);
+            }
+            double scale = -1.0 / ((double)K * sigma);
+            for (int64_t v = 0; v < V; ++v) g[v] *= scale;
+        }
+        free(a);
+        free(zt);
+        free(in);
+    }
+}
+
