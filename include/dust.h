@@ -133,6 +133,36 @@ dust_status dust_estimate_head(const void *logits, int logits_dtype, const float
                                void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Vocabulary-subset LM-head estimator (TL;DR page, section 1, "reducing
+ * interference": the head is evaluated on part of the vocabulary per draw).
+ * The pages give no subset rule.  Here, per (token, draw), the perturbed set S is
+ * a cyclic window of mq = m/4 consecutive channel quads (channels 4q..4q+3 of
+ * the nq = ceil(V/4) quads) starting at quad o = (w * nq) >> 32, w = word 0 of
+ * Philox4x32-10 on the counter (token_offset + t, 0xFFFFFFFF, draw_offset + i,
+ * layer) with the noise key, plus the label y_t.  S carries the same noise a_v as
+ * dust_estimate_head; nothing else is perturbed, and
+ *   r = CE(z_t) - CE(z_t + sigma a 1_S)
+ *   g_hat_t[v] = -(1/(K sigma)) sum_i r a_v 1[v in S_i] / pi_v
+ * with pi_v = mq/nq the inclusion probability of a window channel (1 for the
+ * label), so the estimate stays unbiased.  Per draw the work is mq quads
+ * instead of nq.
+ *   m : channels per draw, a positive multiple of 4; when m >= 4 nq the window
+ *       is the whole vocabulary and the call is dust_estimate_head's.
+ * Other arguments and outputs as dust_estimate_head.  Supported: V <= 16384
+ * (the probability row and the running sums of a token stay in LDS) unless m
+ * covers the vocabulary.
+ * Workspace: dust_head_subset_workspace_bytes(T, V, d, K) bytes (g_hat is formed
+ * in fp32 first, then the outer product).
+ */
+size_t dust_head_subset_workspace_bytes(int64_t T, int64_t V, int64_t d, int64_t K);
+dust_status dust_estimate_head_subset(const void *logits, int logits_dtype, const float *x,
+                                      const int32_t *labels, int64_t T, int64_t V, int64_t d,
+                                      int64_t K, int64_t m, float sigma, uint64_t seed, uint32_t layer,
+                                      uint32_t token_offset, uint32_t draw_offset,
+                                      float *grad_w, float *ghat, float *rewards,
+                                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Interior MLP-linear estimator: W1 of a pre-LN MLP block, with the cached
  * downstream recomputed per draw (TL;DR page, section 1: noise on the output of
  * every linear layer, reward = loss reduction at the token; news article on

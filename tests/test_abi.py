@@ -69,6 +69,22 @@ def test_head_rejects_bad_arguments_on_host(kw, status, msg):
     assert msg in err
 
 
+def test_head_subset_rejects_bad_arguments_on_host():
+    L = dust.lib()
+
+    def call(m, V=1000, T=4):
+        st = L.dust_estimate_head_subset(FAKE, 0, FAKE, FAKE, T, V, 8, 3, m, ctypes.c_float(0.01), 1, 0, 0, 0,
+                                         FAKE, FAKE, None, None, 0, None)
+        return st, L.dust_last_error().decode()
+
+    for m in (0, -4, 6):
+        st, err = call(m)
+        assert st == 1 and "multiple of 4" in err
+    st, err = call(1024, V=20000)  # window below the vocabulary, V beyond the LDS-resident row
+    assert st == 2 and "16384" in err
+    assert L.dust_head_subset_workspace_bytes(4096, 8192, 512, 256) >= 4 * 4096 * 8192
+
+
 def test_outer_and_noise_reject_bad_arguments():
     L = dust.lib()
     assert L.dust_outer_product(None, FAKE, 4, 4, 4, FAKE, None, 0, None) == 1

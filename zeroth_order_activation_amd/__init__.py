@@ -61,6 +61,11 @@ def lib():
         L.dust_estimate_head.restype = ctypes.c_int
         L.dust_estimate_head.argtypes = [_vp, ctypes.c_int, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _u64, _u32,
                                          _u32, _u32, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.dust_head_subset_workspace_bytes.restype = ctypes.c_size_t
+        L.dust_head_subset_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64]
+        L.dust_estimate_head_subset.restype = ctypes.c_int
+        L.dust_estimate_head_subset.argtypes = [_vp, ctypes.c_int, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32,
+                                                _u64, _u32, _u32, _u32, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.dust_linear_workspace_bytes.restype = ctypes.c_size_t
         L.dust_linear_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _i64]
         L.dust_estimate_linear.restype = ctypes.c_int
@@ -186,6 +191,29 @@ def estimate_head(logits, x, labels, K: int, sigma: float, seed: int, layer: int
     _check(lib().dust_estimate_head(_p(logits), dt, _p(x), _p(labels), T, V, d, K, sigma, seed, layer,
                                     token_offset, draw_offset, _p(grad_w), _p(ghat), _p(rewards), _p(ws), nb,
                                     _stream(logits)))
+    return grad_w
+
+
+def estimate_head_subset(logits, x, labels, K: int, m: int, sigma: float, seed: int, layer: int,
+                         token_offset: int = 0, draw_offset: int = 0, *, grad_w=None, ghat=None,
+                         rewards=None, workspace=None):
+    """Vocabulary-subset LM-head estimator: per draw a window of m channels (a
+    multiple of 4) plus the label is perturbed (see dust_estimate_head_subset in
+    include/dust.h).  Returns grad_w [V,d]."""
+    _dev_tensor(logits, "logits", (torch.float32, torch.bfloat16))
+    _dev_tensor(x, "x", (torch.float32,))
+    _dev_tensor(labels, "labels", (torch.int32,))
+    T, V = logits.shape
+    d = x.shape[1]
+    if x.shape[0] != T or labels.numel() != T:
+        raise ValueError("logits, x and labels disagree on T")
+    dt = F32 if logits.dtype == torch.float32 else BF16
+    if grad_w is None:
+        grad_w = torch.empty((V, d), dtype=torch.float32, device=logits.device)
+    ws, nb = _workspace(lib().dust_head_subset_workspace_bytes(T, V, d, K), logits.device, workspace)
+    _check(lib().dust_estimate_head_subset(_p(logits), dt, _p(x), _p(labels), T, V, d, K, m, sigma, seed, layer,
+                                           token_offset, draw_offset, _p(grad_w), _p(ghat), _p(rewards), _p(ws),
+                                           nb, _stream(logits)))
     return grad_w
 
 

@@ -1,5 +1,6 @@
 // C ABI of the Dust estimator library: argument checks, workspace layout and
 // dispatch.  Every check runs on the host before anything is enqueued.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -131,6 +132,40 @@ dust_status dust_outer_product(const float* ghat, const float* x, int64_t T, int
 // outer product's workspace.
 static bool head_pairs_path(int64_t T, int64_t V, int64_t d) { return dust::outer_uses_pairs(T, V, d); }
 
+// Kernel arguments shared by the head estimators.  The kernels draw the noise
+// divided by sqrt(2 ln 2) and work with sigma' = sigma sqrt(2 ln 2), so that
+// sigma' a' = sigma a; the final scale takes the factor back:
+// g_hat = -(1/(K sigma)) sqrt(2 ln 2) sum r a'.
+static dust::HeadArgs head_args(const void* logits, const int32_t* labels, float* ghat, float* rewards, int64_t T,
+                                int64_t V, int64_t K, float sigma, const dust::HeadPlan& plan, uint64_t seed,
+                                uint32_t layer, uint32_t token_offset, uint32_t draw_offset) {
+    dust::HeadArgs A{};
+    A.logits = logits;
+    A.labels = labels;
+    A.ghat = ghat;
+    A.rewards = rewards;
+    A.T = (int32_t)T;
+    A.V = (int32_t)V;
+    A.K = (int32_t)K;
+    const double s2 = std::sqrt(2.0 * std::log(2.0));
+    const double sd = (double)sigma * s2;
+    A.sigma = (float)sd;
+    A.smul = plan.deg > 0 ? (float)sd : 1.0f;
+    A.gscale = (float)(-s2 / ((double)K * (double)sigma));
+    double ck = 1.0, fact = 1.0;
+    for (int k = 0; k < 8; ++k) {  // coef[k] = sd^k / (k+1)!
+        fact *= (k + 1);
+        A.coef[k] = (float)(ck / fact);
+        ck *= sd;
+    }
+    A.k0 = (uint32_t)seed;
+    A.k1 = (uint32_t)(seed >> 32);
+    A.layer = layer;
+    A.tok0 = token_offset;
+    A.draw0 = draw_offset;
+    return A;
+}
+
 size_t dust_head_workspace_bytes(int64_t T, int64_t V, int64_t d, int64_t K) {
     (void)K;
     if (T <= 0 || V <= 0 || d <= 0) return 0;
@@ -173,36 +208,11 @@ dust_status dust_estimate_head(const void* logits, int logits_dtype, const float
     void* ows = outer_ws ? ws + ghat_ws : nullptr;
     const dust::OuterPairs pr = dust::outer_ghat_pairs(T, V, d, ows);
 
-    dust::HeadArgs A{};
-    A.logits = logits;
-    A.labels = labels;
-    A.ghat = g;
+    dust::HeadArgs A = head_args(logits, labels, g, rewards, T, V, K, sigma, plan, seed, layer, token_offset,
+                                 draw_offset);
     A.ghi = pr.hi;
     A.glo = pr.lo;
     A.ldp = pr.ld;
-    A.rewards = rewards;
-    A.T = (int32_t)T;
-    A.V = (int32_t)V;
-    A.K = (int32_t)K;
-    // The kernel draws the noise divided by sqrt(2 ln 2); it works with
-    // sigma' = sigma sqrt(2 ln 2), so that sigma' a' = sigma a, and the final
-    // scale takes the factor back: g_hat = -(1/(K sigma)) sqrt(2 ln 2) sum r a'.
-    const double s2 = std::sqrt(2.0 * std::log(2.0));
-    const double sd = (double)sigma * s2;
-    A.sigma = (float)sd;
-    A.smul = plan.deg > 0 ? (float)sd : 1.0f;
-    A.gscale = (float)(-s2 / ((double)K * (double)sigma));
-    double ck = 1.0, fact = 1.0;
-    for (int k = 0; k < 8; ++k) {  // coef[k] = sd^k / (k+1)!
-        fact *= (k + 1);
-        A.coef[k] = (float)(ck / fact);
-        ck *= sd;
-    }
-    A.k0 = (uint32_t)seed;
-    A.k1 = (uint32_t)(seed >> 32);
-    A.layer = layer;
-    A.tok0 = token_offset;
-    A.draw0 = draw_offset;
     if (env_flag("DUST_LOG"))
         std::fprintf(stderr, "[dust] head T=%lld V=%lld d=%lld K=%lld nt=%d q=%d pmode=%d deg=%d lds=%zu\n",
                      (long long)T, (long long)V, (long long)d, (long long)K, plan.nt, plan.q, plan.pmode, plan.deg,
@@ -213,6 +223,64 @@ dust_status dust_estimate_head(const void* logits, int logits_dtype, const float
     e = dust::launch_outer(g, x, T, V, d, grad_w, ows, outer_ws, st, pr.hi != nullptr);
     if (e != hipSuccess) return device_fail("dust_estimate_head: outer-product launch", e);
     if ((e = record_stage(1, st)) != hipSuccess) return device_fail("dust_estimate_head: stage event", e);
+    return ok();
+}
+
+size_t dust_head_subset_workspace_bytes(int64_t T, int64_t V, int64_t d, int64_t K) {
+    (void)K;
+    if (T <= 0 || V <= 0 || d <= 0) return 0;
+    // g_hat in fp32 (formed by the estimator, then split for the outer product)
+    return std::max(head_ghat_bytes(T, V) + dust::outer_workspace_bytes(T, V, d),
+                    dust_head_workspace_bytes(T, V, d, K));
+}
+
+dust_status dust_estimate_head_subset(const void* logits, int logits_dtype, const float* x, const int32_t* labels,
+                                      int64_t T, int64_t V, int64_t d, int64_t K, int64_t m, float sigma,
+                                      uint64_t seed, uint32_t layer, uint32_t token_offset, uint32_t draw_offset,
+                                      float* grad_w, float* ghat, float* rewards, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+    if (m < 4 || m % 4 != 0)
+        return fail(DUST_E_INVALID, "dust_estimate_head_subset: m must be a positive multiple of 4 (got %lld)",
+                    (long long)m);
+    if (V > 0 && m / 4 >= (V + 3) / 4)  // the window is the whole vocabulary
+        return dust_estimate_head(logits, logits_dtype, x, labels, T, V, d, K, sigma, seed, layer, token_offset,
+                                  draw_offset, grad_w, ghat, rewards, workspace, workspace_bytes, stream);
+    if (!logits || !x || !labels || !grad_w)
+        return fail(DUST_E_INVALID, "dust_estimate_head_subset: logits, x, labels and grad_w must be non-NULL");
+    if (logits_dtype != DUST_F32 && logits_dtype != DUST_BF16)
+        return fail(DUST_E_UNSUPPORTED, "dust_estimate_head_subset: logits_dtype %d is not DUST_F32 or DUST_BF16",
+                    logits_dtype);
+    if (!aligned16(logits) || !aligned16(x) || !aligned16(labels) || !aligned16(grad_w) ||
+        (ghat && !aligned16(ghat)) || (rewards && !aligned16(rewards)) || (workspace && !aligned16(workspace)))
+        return fail(DUST_E_INVALID, "dust_estimate_head_subset: every pointer must be 16-byte aligned");
+    dust_status s = check_common(T, K, sigma, token_offset, draw_offset);
+    if (s != DUST_OK) return s;
+    if (V <= 0) return fail(DUST_E_INVALID, "dust_estimate_head_subset: V must be >= 1");
+    if (d <= 0) return fail(DUST_E_INVALID, "dust_estimate_head_subset: d must be >= 1");
+    if (V > 16384)
+        return fail(DUST_E_UNSUPPORTED, "dust_estimate_head_subset: V > 16384 is not supported below a full window");
+    if (d > 65535LL * 128) return fail(DUST_E_UNSUPPORTED, "dust_estimate_head_subset: d too large");
+    const dust::HeadPlan plan = dust::plan_head(V, logits_dtype, sigma);  // for the Taylor degree
+    const size_t ghat_ws = ghat ? 0 : head_ghat_bytes(T, V);
+    const size_t outer_ws = dust::outer_workspace_bytes(T, V, d);
+    const size_t need = ghat_ws + outer_ws;
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+        return fail(DUST_E_WORKSPACE, "dust_estimate_head_subset: workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    s = check_labels(labels, T, V, st);
+    if (s != DUST_OK) return s;
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    float* g = ghat ? ghat : reinterpret_cast<float*>(ws);
+    void* ows = outer_ws ? ws + ghat_ws : nullptr;
+    const dust::HeadArgs A = head_args(logits, labels, g, rewards, T, V, K, sigma, plan, seed, layer, token_offset,
+                                       draw_offset);
+    hipError_t e = dust::launch_head_subset(plan, logits_dtype, A, m, st);
+    if (e != hipSuccess) return device_fail("dust_estimate_head_subset: estimator launch", e);
+    if ((e = record_stage(0, st)) != hipSuccess) return device_fail("dust_estimate_head_subset: stage event", e);
+    e = dust::launch_outer(g, x, T, V, d, grad_w, ows, outer_ws, st, false);
+    if (e != hipSuccess) return device_fail("dust_estimate_head_subset: outer-product launch", e);
+    if ((e = record_stage(1, st)) != hipSuccess) return device_fail("dust_estimate_head_subset: stage event", e);
     return ok();
 }
 
