@@ -1,13 +1,15 @@
 """Benchmark of the Dust gradient estimator on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--draws K5]
-                    [--no-cpu-baseline]
+                    [--subset M] [--no-cpu-baseline]
 
 A step is one full estimate -- every stage of the hot path -- over one batch of
 synthetic inputs already resident in HBM:
   * LM-head workloads (1, 2, 4): the per-token estimator kernel (noise, clean
     statistics, perturbed losses, rewards, reward-weighted noise sum) and the
     weight-gradient outer product;
+  * with --subset M on an LM-head workload: the vocabulary-subset estimator
+    (a window of M channels per draw plus the label) and the outer product;
   * MLP-linear workloads (3, 5): GEMM1 with the noise/GELU prologue and the
     LayerNorm epilogue, GEMM2 with the log-sum-exp epilogue, the loss combine,
     the noise-regenerating reduce and the outer product.
@@ -75,6 +77,7 @@ def head_taylor_degree(sigma):
 KERNEL_SOURCES = {
     "head_estimate_kernel": ["head_impl.hpp", "head_f32.hip", "head_bf16.hip", "head.hip", "dust_device.hpp"],
     "mlp_gemm2_kernel": ["mlp.hip", "dust_device.hpp", "dust_internal.hpp"],
+    "head_subset_kernel": ["head_subset.hip", "dust_device.hpp", "dust_internal.hpp"],
 }
 
 
@@ -86,13 +89,14 @@ def sources_digest(kernel):
     return h.hexdigest()
 
 
-def traffic_path(kernel, workload):
-    return os.path.join(ROOT, "profiles", f"traffic_{kernel}_workload{workload}.json")
+def traffic_path(kernel, workload, subset=0):
+    tag = f"_m{subset}" if subset else ""
+    return os.path.join(ROOT, "profiles", f"traffic_{kernel}_workload{workload}{tag}.json")
 
 
-def load_traffic(kernel, workload):
+def load_traffic(kernel, workload, subset=0):
     """Measured HBM bytes per launch, or None when absent or taken on other sources."""
-    p = traffic_path(kernel, workload)
+    p = traffic_path(kernel, workload, subset)
     if not os.path.exists(p):
         return None
     with open(p) as f:
@@ -121,7 +125,8 @@ def write_traffic(args):
     """Turn four rocprofv3 --pmc runs (kernel FETCH_SIZE, kernel WRITE_SIZE, and the
     same two counters on a plain copy of --copy-calibration MiB) into the traffic
     file of the workload's dominant kernel."""
-    kernel = "head_estimate_kernel" if args.workload in (1, 2, 4) else "mlp_gemm2_kernel"
+    kernel = ("head_subset_kernel" if args.subset else "head_estimate_kernel") if args.workload in (1, 2, 4) \
+        else "mlp_gemm2_kernel"
     copy_bytes = args.copy_calibration << 20
     if copy_bytes <= 0:
         sys.exit("--traffic-from needs --copy-calibration MIB (the size the copy runs used)")
@@ -139,11 +144,11 @@ def write_traffic(args):
         factor = copy_bytes / (copy_kib * 1024.0)
         res[ctr] = {"kib_per_dispatch": kib, "dispatches": len(k_runs), "copy_kib": copy_kib,
                     "scale": factor, "bytes": kib * 1024.0 * factor}
-    out = {"kernel": kernel, "workload": args.workload, "copy_bytes": copy_bytes,
+    out = {"kernel": kernel, "workload": args.workload, "subset_m": args.subset, "copy_bytes": copy_bytes,
            "fetch": res["FETCH_SIZE"], "write": res["WRITE_SIZE"],
            "bytes_per_launch": res["FETCH_SIZE"]["bytes"] + res["WRITE_SIZE"]["bytes"],
            "sources_sha256": sources_digest(kernel)}
-    with open(traffic_path(kernel, args.workload), "w") as f:
+    with open(traffic_path(kernel, args.workload, args.subset), "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
 
@@ -165,6 +170,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=2, choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--draws", type=int, default=1024, help="K for workload 5")
+    ap.add_argument("--subset", type=int, default=0, metavar="M",
+                    help="LM-head workloads: perturb a window of M vocabulary channels per draw (plus the "
+                         "label) with the subset estimator; M a multiple of 4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-alignment", action="store_true",
                     help="MLP-linear workloads: skip the cosine to the backprop gradient")
@@ -178,7 +186,7 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline_head(case, target_s):
+def cpu_baseline_head(case, target_s, subset=0):
     """The oracle, as it stands, on a bounded sample of tokens of the same workload."""
     import oracle
 
@@ -188,13 +196,18 @@ def cpu_baseline_head(case, target_s):
     ntok = 8
     while True:
         t0 = time.perf_counter()
-        oracle.head_estimate(z[:ntok], case["labels"][:ntok], K, sigma, case["seed_noise"], case["layer"])
+        if subset:
+            oracle.head_estimate_subset(z[:ntok], case["labels"][:ntok], K, subset, sigma, case["seed_noise"],
+                                        case["layer"])
+        else:
+            oracle.head_estimate(z[:ntok], case["labels"][:ntok], K, sigma, case["seed_noise"], case["layer"])
         el = time.perf_counter() - t0
         if el >= target_s / 3 or ntok >= case["T"]:
             break
         ntok = min(case["T"], int(ntok * max(2.0, target_s / max(el, 1e-3))))
     return {"value": ntok * K / el, "unit": "token-draws/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"first {ntok} of {case['T']} tokens x all {K} draws (full vocabulary), "
+            "sample": f"first {ntok} of {case['T']} tokens x all {K} draws "
+                      f"({f'window of {subset} channels + label' if subset else 'full vocabulary'}), "
                       f"fp64 C loops, {el:.1f} s"}
 
 
@@ -252,10 +265,19 @@ def run_head(args, c, dust, torch):
     x = torch.from_numpy(c["x"]).cuda()
     y = torch.from_numpy(c["labels"]).cuda()
     gw = torch.empty((V, d), dtype=torch.float32, device="cuda")
-    ws = torch.empty(dust.head_workspace_bytes(T, V, d, K), dtype=torch.uint8, device="cuda")
+    m = args.subset
+    if m:
+        if m % 4 or m <= 0:
+            sys.exit("--subset M needs a positive multiple of 4")
+        ws = torch.empty(dust.head_subset_workspace_bytes(T, V, d, K), dtype=torch.uint8, device="cuda")
 
-    def step():
-        dust.estimate_head(z, x, y, K, sigma, c["seed_noise"], c["layer"], grad_w=gw, workspace=ws)
+        def step():
+            dust.estimate_head_subset(z, x, y, K, m, sigma, c["seed_noise"], c["layer"], grad_w=gw, workspace=ws)
+    else:
+        ws = torch.empty(dust.head_workspace_bytes(T, V, d, K), dtype=torch.uint8, device="cuda")
+
+        def step():
+            dust.estimate_head(z, x, y, K, sigma, c["seed_noise"], c["layer"], grad_w=gw, workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -266,7 +288,13 @@ def run_head(args, c, dust, torch):
     ms_per_step = wall * 1e3 / args.steps
     deg = head_taylor_degree(sigma)
     ops = head_lane_ops_per_channel_draw(deg)
-    achieved = T * K * V * ops / (est_ms / 1e3) / 1e9
+    # channels perturbed per (token, draw): the vocabulary, or the window (the label,
+    # perturbed besides when it falls outside, is not counted)
+    nq = (V + 3) // 4
+    covers = not m or m // 4 >= nq
+    per_draw = V if covers else m
+    kernel = "head_estimate_kernel" if covers else "head_subset_kernel"
+    achieved = T * K * per_draw * ops / (est_ms / 1e3) / 1e9
     lb = 4 if "logits" in c else 2
     # bytes every step must move at least once: logits read, g_hat written and read back,
     # x read, grad_w written, labels read
@@ -276,11 +304,11 @@ def run_head(args, c, dust, torch):
     out = {
         "dtype": dtype,
         "stages_ms": {"estimator": est_ms, "outer_product": outer_ms},
-        "roofline": {"bound": "alu", "kernel": "head_estimate_kernel", "achieved": achieved,
+        "roofline": {"bound": "alu", "kernel": kernel, "achieved": achieved,
                      "peak": VALU_PEAK_GOPS, "unit": "G lane-ops/s", "frac": achieved / VALU_PEAK_GOPS,
-                     "traffic": load_traffic("head_estimate_kernel", args.workload),
+                     "traffic": load_traffic(kernel, args.workload, 0 if covers else m),
                      "lane_ops_per_channel_draw": ops, "taylor_degree": deg,
-                     "channel_draws_per_launch": T * K * V, "kernel_ms": est_ms,
+                     "channel_draws_per_launch": T * K * per_draw, "kernel_ms": est_ms,
                      "algorithmic_bytes_per_launch": kern_bytes},
         "hbm": {"algorithmic_bytes_per_step": alg_bytes, "GBps": alg_bytes / (ms_per_step / 1e3) / 1e9,
                 "frac": alg_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS,
@@ -400,10 +428,15 @@ def main():
 
     c = synth.workload(args.workload, matmul=gpu_matmul)
     name = WORKLOAD_NAMES[args.workload]
+    if args.subset and c["kind"] != "head":
+        sys.exit("--subset applies to the LM-head workloads (1, 2, 4)")
     if c["kind"] == "head":
         K = c["K"]
         ms, extra = run_head(args, c, dust, torch)
         cfg = {"workload": name, "T": c["T"], "V": c["V"], "d": c["d"], "K": K, "sigma": c["sigma"]}
+        if args.subset:
+            cfg["workload"] = name + f"; vocabulary subset: window of {args.subset} channels per draw + label"
+            cfg["subset_m"] = args.subset
     else:
         K = c["K"] if isinstance(c["K"], int) else args.draws
         name = name.format(K=K)
@@ -427,7 +460,7 @@ def main():
     }
     out.update(extra)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = (cpu_baseline_head(c, args.cpu_seconds) if c["kind"] == "head"
+        out["cpu_baseline"] = (cpu_baseline_head(c, args.cpu_seconds, args.subset) if c["kind"] == "head"
                                else cpu_baseline_linear(c, K, args.cpu_seconds))
     print(json.dumps(out), flush=True)
 

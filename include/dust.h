@@ -151,8 +151,8 @@ dust_status dust_estimate_head(const void *logits, int logits_dtype, const float
  * Other arguments and outputs as dust_estimate_head.  Supported: V <= 16384
  * (the probability row and the running sums of a token stay in LDS) unless m
  * covers the vocabulary.
- * Workspace: dust_head_subset_workspace_bytes(T, V, d, K) bytes (g_hat is formed
- * in fp32 first, then the outer product).
+ * Workspace: dust_head_subset_workspace_bytes(T, V, d, K) bytes, the same as
+ * dust_head_workspace_bytes (g_hat goes to the outer product in the same form).
  */
 size_t dust_head_subset_workspace_bytes(int64_t T, int64_t V, int64_t d, int64_t K);
 dust_status dust_estimate_head_subset(const void *logits, int logits_dtype, const float *x,

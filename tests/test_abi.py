@@ -82,7 +82,8 @@ def test_head_subset_rejects_bad_arguments_on_host():
         assert st == 1 and "multiple of 4" in err
     st, err = call(1024, V=20000)  # window below the vocabulary, V beyond the LDS-resident row
     assert st == 2 and "16384" in err
-    assert L.dust_head_subset_workspace_bytes(4096, 8192, 512, 256) >= 4 * 4096 * 8192
+    for shape in ((4096, 8192, 512, 256), (7, 1003, 8, 5)):
+        assert L.dust_head_subset_workspace_bytes(*shape) == L.dust_head_workspace_bytes(*shape)
 
 
 def test_outer_and_noise_reject_bad_arguments():

@@ -194,6 +194,10 @@ def estimate_head(logits, x, labels, K: int, sigma: float, seed: int, layer: int
     return grad_w
 
 
+def head_subset_workspace_bytes(T: int, V: int, d: int, K: int) -> int:
+    return int(lib().dust_head_subset_workspace_bytes(T, V, d, K))
+
+
 def estimate_head_subset(logits, x, labels, K: int, m: int, sigma: float, seed: int, layer: int,
                          token_offset: int = 0, draw_offset: int = 0, *, grad_w=None, ghat=None,
                          rewards=None, workspace=None):

@@ -227,11 +227,8 @@ dust_status dust_estimate_head(const void* logits, int logits_dtype, const float
 }
 
 size_t dust_head_subset_workspace_bytes(int64_t T, int64_t V, int64_t d, int64_t K) {
-    (void)K;
-    if (T <= 0 || V <= 0 || d <= 0) return 0;
-    // g_hat in fp32 (formed by the estimator, then split for the outer product)
-    return std::max(head_ghat_bytes(T, V) + dust::outer_workspace_bytes(T, V, d),
-                    dust_head_workspace_bytes(T, V, d, K));
+    // the same layout as the full estimator's (which a covering window runs)
+    return dust_head_workspace_bytes(T, V, d, K);
 }
 
 dust_status dust_estimate_head_subset(const void* logits, int logits_dtype, const float* x, const int32_t* labels,
@@ -261,7 +258,8 @@ dust_status dust_estimate_head_subset(const void* logits, int logits_dtype, cons
         return fail(DUST_E_UNSUPPORTED, "dust_estimate_head_subset: V > 16384 is not supported below a full window");
     if (d > 65535LL * 128) return fail(DUST_E_UNSUPPORTED, "dust_estimate_head_subset: d too large");
     const dust::HeadPlan plan = dust::plan_head(V, logits_dtype, sigma);  // for the Taylor degree
-    const size_t ghat_ws = ghat ? 0 : head_ghat_bytes(T, V);
+    const bool pairs = head_pairs_path(T, V, d);
+    const size_t ghat_ws = (ghat || pairs) ? 0 : head_ghat_bytes(T, V);
     const size_t outer_ws = dust::outer_workspace_bytes(T, V, d);
     const size_t need = ghat_ws + outer_ws;
     if (need > 0 && (workspace == nullptr || workspace_bytes < need))
@@ -271,14 +269,18 @@ dust_status dust_estimate_head_subset(const void* logits, int logits_dtype, cons
     s = check_labels(labels, T, V, st);
     if (s != DUST_OK) return s;
     unsigned char* ws = static_cast<unsigned char*>(workspace);
-    float* g = ghat ? ghat : reinterpret_cast<float*>(ws);
+    float* g = ghat ? ghat : (pairs ? nullptr : reinterpret_cast<float*>(ws));
     void* ows = outer_ws ? ws + ghat_ws : nullptr;
-    const dust::HeadArgs A = head_args(logits, labels, g, rewards, T, V, K, sigma, plan, seed, layer, token_offset,
-                                       draw_offset);
+    const dust::OuterPairs pr = dust::outer_ghat_pairs(T, V, d, ows);
+    dust::HeadArgs A = head_args(logits, labels, g, rewards, T, V, K, sigma, plan, seed, layer, token_offset,
+                                 draw_offset);
+    A.ghi = pr.hi;
+    A.glo = pr.lo;
+    A.ldp = pr.ld;
     hipError_t e = dust::launch_head_subset(plan, logits_dtype, A, m, st);
     if (e != hipSuccess) return device_fail("dust_estimate_head_subset: estimator launch", e);
     if ((e = record_stage(0, st)) != hipSuccess) return device_fail("dust_estimate_head_subset: stage event", e);
-    e = dust::launch_outer(g, x, T, V, d, grad_w, ows, outer_ws, st, false);
+    e = dust::launch_outer(g, x, T, V, d, grad_w, ows, outer_ws, st, pr.hi != nullptr);
     if (e != hipSuccess) return device_fail("dust_estimate_head_subset: outer-product launch", e);
     if ((e = record_stage(1, st)) != hipSuccess) return device_fail("dust_estimate_head_subset: stage event", e);
     return ok();

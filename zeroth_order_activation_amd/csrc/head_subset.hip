@@ -14,18 +14,33 @@
 // unbiased.  The per-draw work is mq quads instead of nq.
 //
 // Layout: the clean probabilities (fp32) and the running sums (fp32) of the
-// row live in LDS; lane l takes window quads l, l + NT, ... of each draw (the
-// window moves, so the sums cannot stay in registers); the label's noise for
-// a chunk of draws is generated up front by all lanes into LDS, so a label
-// outside the window costs no Philox inside the draw loop.
+// row live in LDS, each with one spare quad past the row.  A workgroup holds
+// two draw groups of 256 lanes that work on two draws at once; lane l of a
+// group takes window positions l, l + 256, ... of its draw (the window moves,
+// so the sums cannot stay in registers) and positions past the window take the
+// spare quad, whose probability is 0, so the draw loop has no branches.  The
+// two groups' windows may overlap, so they update the running sums in turn,
+// a barrier apart.  What depends on the draw
+// alone -- the window offset, the label's noise, the label's loss term when the
+// label lies outside the window, and the label channel's weight correction
+// (weight 1 instead of nq/mq inside the window, 1 outside) -- is computed for a
+// chunk of draws up front, one draw per lane, into LDS; the correction is
+// summed in a register and added to the label's running sum at the end.
+//
+// Per draw there is one wave reduction (DPP row operations and two row
+// broadcasts, no LDS round trips), one barrier that publishes the groups' wave
+// sums, and the read-modify-write of the window's running sums.  The noise of
+// the next draw is generated between publishing a draw's wave sum and the
+// barrier, so the reduction's latency hides behind it.
 #include "dust_device.hpp"
 #include "dust_internal.hpp"
 
 namespace dust {
 
 namespace {
-constexpr int SNT = 256;    // lanes per workgroup
-constexpr int SKC = 4096;   // draws per chunk of precomputed label noise
+constexpr int GL = 256;    // lanes per draw group
+constexpr int SKC = 512;   // draws per chunk of precomputed per-draw terms
+constexpr int SH = 2;      // draw groups per workgroup
 constexpr float kL2e = kLog2eF;
 
 __device__ __forceinline__ uint32_t window_offset(uint32_t tok, uint32_t draw, uint32_t layer, uint32_t k0,
@@ -53,142 +68,260 @@ __device__ __forceinline__ float logit_at(const void* row, int64_t v) {
                    : bf16_to_f32(reinterpret_cast<const uint16_t*>(row)[v]);
 }
 
+template <int NT>
 __device__ __forceinline__ float block_reduce_max(float v, float* sh) {
     v = wave_max(v);
     __syncthreads();
     if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
     __syncthreads();
-    return fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
+    float r = sh[0];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) r = fmaxf(r, sh[w]);
+    return r;
 }
+template <int NT>
 __device__ __forceinline__ float block_reduce_sum(float v, float* sh) {
     v = wave_sum(v);
     __syncthreads();
     if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
     __syncthreads();
-    return (sh[0] + sh[1]) + (sh[2] + sh[3]);
+    float r = sh[0];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) r += sh[w];
+    return r;
+}
+
+// Two floats to a pair of bf16 (round to nearest even), the first in the low half.
+typedef __bf16 sbf16x2_t __attribute__((ext_vector_type(2)));
+typedef float sf32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16_pair(float a, float b) {
+    const sf32x2_t v = {a, b};
+    const sbf16x2_t h = __builtin_convertvector(v, sbf16x2_t);
+    uint32_t u;
+    __builtin_memcpy(&u, &h, 4);
+    return u;
+}
+
+// v + (v moved by one DPP pattern); rows outside ROWM add 0.
+template <int CTRL, int ROWM>
+__device__ __forceinline__ float dpp_add(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWM, 0xF, false));
+}
+// Sum over the 64 lanes of a wave, returned wave-uniform (every lane active):
+// lane pairs, quads, half rows and rows by quad permutes and mirrors, then the
+// row sums gathered into the last row by the two row broadcasts.
+__device__ __forceinline__ float wave_total(float v) {
+    v = dpp_add<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+    v = dpp_add<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+    v = dpp_add<0x141, 0xF>(v);  // row_half_mirror
+    v = dpp_add<0x140, 0xF>(v);  // row_mirror
+    v = dpp_add<0x142, 0xA>(v);  // row_bcast15 into rows 1 and 3
+    v = dpp_add<0x143, 0xC>(v);  // row_bcast31 into rows 2 and 3
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// log1p(x) for a wave-uniform x > -1.  For |x| <= 1/8: log1p(x) = 2 atanh(s),
+// s = x / (2 + x), |s| < 0.059, by its series through s^7 (the next term is
+// below 2e-11 relative); otherwise the library function.
+__device__ __forceinline__ float log1p_uniform(float x) {
+    x = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+    if (fabsf(x) <= 0.125f) {
+        const float s = x * __builtin_amdgcn_rcpf(2.0f + x);
+        const float s2 = s * s;
+        const float p = fmaf(s2, fmaf(s2, fmaf(s2, 1.0f / 7.0f, 1.0f / 5.0f), 1.0f / 3.0f), 1.0f);
+        return 2.0f * s * p;
+    }
+    return log1pf(x);
 }
 }  // namespace
 
-// QW: window quads per lane (mq <= SNT * QW).
-template <int LT, int DEG, int QW>
-__global__ void __launch_bounds__(SNT) head_subset_kernel(HeadArgs A, int mq, float winv) {
+// H draw groups of GL lanes each (NT = H GL lanes): group g takes draws
+// g, g + H, ... of every chunk; QW window positions per lane (mq <= GL QW).
+template <int LT, int DEG, int QW, int H>
+__global__ void __launch_bounds__(GL * H) head_subset_kernel(HeadArgs A, int mq, float winv) {
+    constexpr int NT = GL * H;
     extern __shared__ __align__(16) float lds[];
-    __shared__ float sh[4];
-    __shared__ float sh_red[2][4][2];
-    const int t = blockIdx.x, tid = threadIdx.x, wid = tid >> 6;
+    __shared__ float sh[NT / 64];
+    __shared__ float sh_red[2][H][GL / 64];
+    const int t = blockIdx.x, tid = threadIdx.x;
+    const int g = tid / GL, lt = tid % GL, wl = lt >> 6;  // group, lane and wave within the group
     const int V = A.V, nq = (V + 3) >> 2;
-    float* P = lds;               // [4 nq] clean probabilities (0 past V)
-    float* ACC = lds + 4 * nq;    // [4 nq] running sums of r a w
-    float* AY = ACC + 4 * nq;     // [SKC] label noise of the current chunk of draws
+    float* P = lds;                  // [4 (nq + 1)] clean probabilities (0 past V and in the spare quad)
+    float* ACC = P + 4 * (nq + 1);   // [4 (nq + 1)] running sums of r a w
+    // [SKC] per draw of the current chunk: window offset (bits), the label's loss
+    // term when outside the window (else 0), the label's noise, its weight correction
+    float4* DR = reinterpret_cast<float4*>(ACC + 4 * (nq + 1));
+    const float4* P4 = reinterpret_cast<const float4*>(P);
+    float4* ACC4 = reinterpret_cast<float4*>(ACC);
     const void* row = reinterpret_cast<const unsigned char*>(A.logits) + (size_t)t * V * (LT == 0 ? 4 : 2);
 
     // ---- clean statistics ----------------------------------------------------
     float m = -__builtin_inff();
-    for (int v = tid; v < 4 * nq; v += SNT) {
+    for (int v = tid; v < 4 * (nq + 1); v += NT) {
         const float z = v < V ? logit_at<LT>(row, v) : -__builtin_inff();
         P[v] = z;
         ACC[v] = 0.f;
         m = fmaxf(m, z);
     }
-    m = block_reduce_max(m, sh);  // its barriers publish P
+    m = block_reduce_max<NT>(m, sh);  // its barriers publish P
     float s = 0.f;
-    for (int v = tid; v < V; v += SNT) s += __expf(P[v] - m);
-    s = block_reduce_sum(s, sh);
+    for (int v = tid; v < V; v += NT) s += __expf(P[v] - m);
+    s = block_reduce_sum<NT>(s, sh);
     const float lse2 = (m + __logf(s)) * kL2e;
-    for (int v = tid; v < 4 * nq; v += SNT) P[v] = __builtin_amdgcn_exp2f(fmaf(P[v], kL2e, -lse2));
-    // (the next barrier, in the label-noise chunk below, publishes P)
+    for (int v = tid; v < 4 * (nq + 1); v += NT) P[v] = __builtin_amdgcn_exp2f(fmaf(P[v], kL2e, -lse2));
+    __syncthreads();  // publishes P
 
     const uint32_t y = (uint32_t)A.labels[t];
     const int qy = (int)(y >> 2), cy = (int)(y & 3u);
     const uint32_t tok = A.tok0 + (uint32_t)t;
+    const float cw_in = 1.0f - winv;  // label weight correction when the label is in the window
+    float accy = 0.f;                 // this group's sum over its draws of r a_y (weight correction)
+    const float py = P[y];            // clean probability of the label
+
+    // One draw's window: noise a, quads q, and this lane's share of
+    // sum_{v in S} p_v expm1(sigma a_v) (the label's term, when outside the
+    // window, on the group's lane 0); ay, ca: the label's noise and weighted correction.
+    auto gen = [&](int ii, int i0, float (&a)[QW][4], int (&q)[QW], float& ay, float& ca) -> float {
+        const uint32_t draw = A.draw0 + (uint32_t)(i0 + ii);
+        const float4 dr = DR[ii];
+        const int o = __builtin_amdgcn_readfirstlane(__float_as_int(dr.x));
+        ay = dr.z;
+        ca = dr.w;
+        float sl = 0.f;
+#pragma unroll
+        for (int k = 0; k < QW; ++k) {
+            const int j = lt + k * GL;
+            int qq = o + j;
+            qq = qq >= nq ? qq - nq : qq;
+            qq = j < mq ? qq : nq;  // past the window: the spare quad
+            q[k] = qq;
+            const f32x4 gv = gauss4_unscaled_uniform(tok, (uint32_t)qq, draw, A.layer, A.k0, A.k1);
+            const float4 pq = P4[qq];
+            const float pv[4] = {pq.x, pq.y, pq.z, pq.w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                a[k][c] = gv.v[c];
+                sl = fmaf(pv[c], em1s<DEG>(gv.v[c], A), sl);
+            }
+        }
+        return sl + (lt == 0 ? dr.y : 0.f);
+    };
 
     for (int i0 = 0; i0 < A.K; i0 += SKC) {
         const int kc = min(SKC, A.K - i0);
-        __syncthreads();  // AY of the previous chunk fully used
-        for (int i = tid; i < kc; i += SNT) {
-            // the same words and conversion as the window's uniform-counter path
-            const u32x4 w = philox4x32_10<false>(tok, (uint32_t)qy, A.draw0 + (uint32_t)(i0 + i), A.layer, A.k0, A.k1);
-            float g[4];
-            box_muller_unscaled(w.x, w.y, g[0], g[1]);
-            box_muller_unscaled(w.z, w.w, g[2], g[3]);
-            AY[i] = cy == 0 ? g[0] : cy == 1 ? g[1] : cy == 2 ? g[2] : g[3];
-        }
-        __syncthreads();
-        for (int ii = 0; ii < kc; ++ii) {
-            const int i = i0 + ii;
-            const uint32_t draw = A.draw0 + (uint32_t)i;
+        __syncthreads();  // the previous chunk's terms fully used
+        for (int i = tid; i < kc; i += NT) {
+            const uint32_t draw = A.draw0 + (uint32_t)(i0 + i);
             const int o = (int)window_offset(tok, draw, A.layer, A.k0, A.k1, (uint32_t)nq);
             const int jy = qy - o < 0 ? qy - o + nq : qy - o;  // label quad's place in the window
-            const bool inw = jy < mq;                           // uniform
-            float a[QW][4];
-            float sl = 0.f, ly = 0.f;
+            const bool in_w = jy < mq;
+            // the same words and conversion as the window's path
+            const u32x4 w = philox4x32_10<false>(tok, (uint32_t)qy, draw, A.layer, A.k0, A.k1);
+            float gg[4];
+            box_muller_unscaled(w.x, w.y, gg[0], gg[1]);
+            box_muller_unscaled(w.z, w.w, gg[2], gg[3]);
+            const float ay = cy == 0 ? gg[0] : cy == 1 ? gg[1] : cy == 2 ? gg[2] : gg[3];
+            DR[i] = make_float4(__int_as_float(o), in_w ? 0.f : py * em1s<DEG>(ay, A), ay, (in_w ? cw_in : 1.0f) * ay);
+        }
+        __syncthreads();
+
+        const int steps = (kc + H - 1) / H;
+        float a[QW][4], an[QW][4];
+        int q[QW], qn[QW];
+        float ay, ayn, ca, can;
+        float sl = gen(min(g, kc - 1), i0, a, q, ay, ca);
+        float rv = 0.f;  // lane l keeps the reward of this group's step l (mod GL) until it is written
+        for (int st = 0; st < steps; ++st) {
+            const int ii = st * H + g;  // this group's draw
+            const int b = st & 1;
+            sh_red[b][g][wl] = wave_total(sl);  // every lane of the wave writes the same value
+            sl = gen(min(ii + H, kc - 1), i0, an, qn, ayn, can);
+            __syncthreads();  // publishes the wave sums; orders the last group's updates before group 0's
+            const float S = (sh_red[b][g][0] + sh_red[b][g][1]) + (sh_red[b][g][2] + sh_red[b][g][3]);
+            const float r0 = A.sigma * ay - log1p_uniform(S * A.smul);
+            const float r = ii < kc ? r0 : 0.f;  // a group past the chunk's last draw adds nothing
+            const float rw = r * winv;
+            // the groups update the running sums in turn (their windows may overlap)
 #pragma unroll
-            for (int k = 0; k < QW; ++k) {
-                const int j = tid + k * SNT;
-                if (j < mq) {
-                    int q = o + j;
-                    q = q >= nq ? q - nq : q;
-                    const f32x4 g = gauss4_unscaled_uniform(tok, (uint32_t)q, draw, A.layer, A.k0, A.k1);
-                    const float4 pq = reinterpret_cast<const float4*>(P)[q];
-                    const float pv[4] = {pq.x, pq.y, pq.z, pq.w};
+            for (int h = 0; h < H; ++h) {
+                if (g == h) {
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        a[k][c] = g.v[c];
-                        sl = fmaf(pv[c], em1s<DEG>(g.v[c], A), sl);
+                    for (int k = 0; k < QW; ++k) {
+                        float4 acc = ACC4[q[k]];
+                        acc.x = fmaf(rw, a[k][0], acc.x);
+                        acc.y = fmaf(rw, a[k][1], acc.y);
+                        acc.z = fmaf(rw, a[k][2], acc.z);
+                        acc.w = fmaf(rw, a[k][3], acc.w);
+                        ACC4[q[k]] = acc;
                     }
-                    if (j == jy) ly = cy == 0 ? g.v[0] : cy == 1 ? g.v[1] : cy == 2 ? g.v[2] : g.v[3];
-                } else {
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) a[k][c] = 0.f;
                 }
+                if (h + 1 < H) __syncthreads();
             }
-            const float ay = AY[ii];
-            if (!inw && tid == 0) {  // the label alone, outside the window
-                sl = fmaf(P[y], em1s<DEG>(ay, A), sl);
-                ly = ay;
+            accy = fmaf(r, ca, accy);
+            rv = (st & (GL - 1)) == lt ? r : rv;
+            if ((st & (GL - 1)) == GL - 1 || st == steps - 1) {  // uniform
+                const int sb = (st & ~(GL - 1)) + lt;  // the step whose reward this lane holds
+                const int ib = sb * H + g;
+                if (A.rewards && sb <= st && ib < kc) A.rewards[(size_t)(i0 + ib) * A.T + t] = rv;
             }
-            sl = wave_sum(sl);
-            ly = wave_sum(ly);
-            const int b = ii & 1;
-            if ((tid & 63) == 0) { sh_red[b][wid][0] = sl; sh_red[b][wid][1] = ly; }
-            __syncthreads();
-            const float S = (sh_red[b][0][0] + sh_red[b][1][0]) + (sh_red[b][2][0] + sh_red[b][3][0]);
-            const float LY = (sh_red[b][0][1] + sh_red[b][1][1]) + (sh_red[b][2][1] + sh_red[b][3][1]);
-            const float r = A.sigma * LY - log1pf(S * A.smul);
-            // running sums: each window quad belongs to one lane in this draw; the
-            // barrier above separates this draw's updates from the previous one's
 #pragma unroll
             for (int k = 0; k < QW; ++k) {
-                const int j = tid + k * SNT;
-                if (j < mq) {
-                    int q = o + j;
-                    q = q >= nq ? q - nq : q;
-                    float4 acc = reinterpret_cast<float4*>(ACC)[q];
-                    const float rw = r * winv;
-                    const bool lab = j == jy;
-                    acc.x = fmaf(lab && cy == 0 ? r : rw, a[k][0], acc.x);
-                    acc.y = fmaf(lab && cy == 1 ? r : rw, a[k][1], acc.y);
-                    acc.z = fmaf(lab && cy == 2 ? r : rw, a[k][2], acc.z);
-                    acc.w = fmaf(lab && cy == 3 ? r : rw, a[k][3], acc.w);
-                    reinterpret_cast<float4*>(ACC)[q] = acc;
-                }
+                q[k] = qn[k];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) a[k][c] = an[k][c];
             }
-            if (!inw && tid == 0) ACC[y] = fmaf(r, ay, ACC[y]);
-            if (tid == 0 && A.rewards) A.rewards[(size_t)i * A.T + t] = r;
+            ay = ayn;
+            ca = can;
         }
     }
     __syncthreads();
-    float* out = A.ghat + (size_t)t * V;
-    for (int v = tid; v < V; v += SNT) out[v] = ACC[v] * A.gscale;
+    if (lt == 0) sh[g] = accy;
+    __syncthreads();
+    if (tid == 0) {
+        float cy_sum = 0.f;
+#pragma unroll
+        for (int h = 0; h < H; ++h) cy_sum += sh[h];
+        ACC[y] += cy_sum;
+    }
+    __syncthreads();
+
+    // ---- g_hat_t = -(1/(K sigma)) sum_i r a w ---------------------------------
+    // fp32 row and/or the bf16 pairs (hi = bf16(g), lo = bf16(g - hi)) that the
+    // outer product consumes, token-major with the row zero-padded to ldp
+    float* out = A.ghat ? A.ghat + (size_t)t * V : nullptr;
+    uint16_t* ohi = A.ghi ? A.ghi + (size_t)t * A.ldp : nullptr;
+    uint16_t* olo = A.ghi ? A.glo + (size_t)t * A.ldp : nullptr;
+    const int nqo = ohi ? (int)((A.ldp + 3) / 4) : nq;
+    for (int qq = tid; qq < nqo; qq += NT) {
+        float v[4];
+        const float4 o = qq < nq ? ACC4[qq] : make_float4(0.f, 0.f, 0.f, 0.f);
+        v[0] = o.x; v[1] = o.y; v[2] = o.z; v[3] = o.w;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = 4 * qq + c < V ? v[c] * A.gscale : 0.f;
+        if (ohi && 4 * (int64_t)qq < A.ldp) {
+            uint2 h, l;
+            h.x = pack_bf16_pair(v[0], v[1]);
+            h.y = pack_bf16_pair(v[2], v[3]);
+            l.x = pack_bf16_pair(v[0] - __uint_as_float(h.x << 16), v[1] - __uint_as_float(h.x & 0xFFFF0000u));
+            l.y = pack_bf16_pair(v[2] - __uint_as_float(h.y << 16), v[3] - __uint_as_float(h.y & 0xFFFF0000u));
+            *reinterpret_cast<uint2*>(ohi + 4 * qq) = h;
+            *reinterpret_cast<uint2*>(olo + 4 * qq) = l;
+        }
+        if (out && qq < nq) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (4 * qq + c < V) out[4 * qq + c] = v[c];
+        }
+    }
 }
 
-// P and ACC hold 4 nq floats each, AY SKC floats.
-size_t head_subset_lds_bytes(int64_t V) { return (size_t)(8 * ((V + 3) / 4) + SKC) * sizeof(float); }
+// P and ACC hold 4 (nq + 1) floats each, DR SKC float4s.
+size_t head_subset_lds_bytes(int64_t V) { return (size_t)(8 * ((V + 3) / 4 + 1) + 4 * SKC) * sizeof(float); }
 
 int head_subset_qw(int64_t m, int64_t V) {
     const int64_t nq = (V + 3) / 4, mq = m / 4 < nq ? m / 4 : nq;
     for (int qw : {1, 2, 4, 8, 16})
-        if (mq <= (int64_t)SNT * qw) return qw;
+        if (mq <= (int64_t)GL * qw) return qw;
     return 0;
 }
 
@@ -201,11 +334,11 @@ hipError_t launch_head_subset(const HeadPlan& plan, int logits_dtype, const Head
     hipError_t e = hipErrorInvalidConfiguration;
 #define DUST_SUBSET_CASE(LT_, DEG_, QW_)                                                               \
     if (logits_dtype == LT_ && plan.deg == DEG_ && qw == QW_) {                                        \
-        auto k = head_subset_kernel<LT_, DEG_, QW_>;                                                   \
+        auto k = head_subset_kernel<LT_, DEG_, QW_, SH>;                                                   \
         if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),                                 \
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess) \
             return e;                                                                                  \
-        hipLaunchKernelGGL(k, dim3(A.T), dim3(SNT), lds, stream, A, (int)mq, winv);                    \
+        hipLaunchKernelGGL(k, dim3(A.T), dim3(GL * SH), lds, stream, A, (int)mq, winv);                    \
         return hipGetLastError();                                                                      \
     }
 #define DUST_SUBSET_QW(LT_, DEG_)                                                                      \
