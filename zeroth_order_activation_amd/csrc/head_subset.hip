@@ -15,12 +15,12 @@
 //
 // Layout: the clean probabilities (fp32) and the running sums (fp32) of the
 // row live in LDS, each with one spare quad past the row.  A workgroup holds
-// two draw groups of 256 lanes that work on two draws at once; lane l of a
-// group takes window positions l, l + 256, ... of its draw (the window moves,
+// four draw groups of 128 lanes that work on four draws at once; lane l of a
+// group takes window positions l, l + 128, ... of its draw (the window moves,
 // so the sums cannot stay in registers) and positions past the window take the
 // spare quad, whose probability is 0, so the draw loop has no branches.  The
-// two groups' windows may overlap, so they update the running sums in turn,
-// a barrier apart.  What depends on the draw
+// groups' windows may overlap, so they update the running sums in turn, a
+// barrier apart.  What depends on the draw
 // alone -- the window offset, the label's noise, the label's loss term when the
 // label lies outside the window, and the label channel's weight correction
 // (weight 1 instead of nq/mq inside the window, 1 outside) -- is computed for a
@@ -38,9 +38,9 @@
 namespace dust {
 
 namespace {
-constexpr int GL = 256;    // lanes per draw group
+constexpr int GL = 128;    // lanes per draw group
 constexpr int SKC = 512;   // draws per chunk of precomputed per-draw terms
-constexpr int SH = 2;      // draw groups per workgroup
+constexpr int SH = 4;      // draw groups per workgroup
 constexpr float kL2e = kLog2eF;
 
 __device__ __forceinline__ uint32_t window_offset(uint32_t tok, uint32_t draw, uint32_t layer, uint32_t k0,
@@ -237,7 +237,9 @@ __global__ void __launch_bounds__(GL * H) head_subset_kernel(HeadArgs A, int mq,
             sh_red[b][g][wl] = wave_total(sl);  // every lane of the wave writes the same value
             sl = gen(min(ii + H, kc - 1), i0, an, qn, ayn, can);
             __syncthreads();  // publishes the wave sums; orders the last group's updates before group 0's
-            const float S = (sh_red[b][g][0] + sh_red[b][g][1]) + (sh_red[b][g][2] + sh_red[b][g][3]);
+            float S = sh_red[b][g][0];
+#pragma unroll
+            for (int w = 1; w < GL / 64; ++w) S += sh_red[b][g][w];
             const float r0 = A.sigma * ay - log1p_uniform(S * A.smul);
             const float r = ii < kc ? r0 : 0.f;  // a group past the chunk's last draw adds nothing
             const float rw = r * winv;
