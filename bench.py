@@ -144,7 +144,17 @@ def write_traffic(args):
         factor = copy_bytes / (copy_kib * 1024.0)
         res[ctr] = {"kib_per_dispatch": kib, "dispatches": len(k_runs), "copy_kib": copy_kib,
                     "scale": factor, "bytes": kib * 1024.0 * factor}
-    out = {"kernel": kernel, "workload": args.workload, "subset_m": args.subset, "copy_bytes": copy_bytes,
+    wl = f"--workload {args.workload}" + (f" --subset {args.subset}" if args.subset else "")
+    prof = "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 120 rocprofv3 --pmc {c} --output-format csv -d DIR/{n} -o {n} -- python3 $REPO/bench.py {a}"
+    cmds = [prof.format(c="FETCH_SIZE", n="copy_fetch", a=f"--copy-calibration {args.copy_calibration}"),
+            prof.format(c="WRITE_SIZE", n="copy_write", a=f"--copy-calibration {args.copy_calibration}"),
+            prof.format(c="FETCH_SIZE", n=f"fetch_w{args.workload}",
+                        a=f"{wl} --steps 1 --warmup 0 --no-cpu-baseline --no-alignment"),
+            prof.format(c="WRITE_SIZE", n=f"write_w{args.workload}",
+                        a=f"{wl} --steps 1 --warmup 0 --no-cpu-baseline --no-alignment"),
+            f"python bench.py {wl} --traffic-from DIR --copy-calibration {args.copy_calibration}"]
+    out = {"kernel": kernel, "workload": args.workload, "subset_m": args.subset, "commands": cmds,
+           "copy_bytes": copy_bytes,
            "fetch": res["FETCH_SIZE"], "write": res["WRITE_SIZE"],
            "bytes_per_launch": res["FETCH_SIZE"]["bytes"] + res["WRITE_SIZE"]["bytes"],
            "sources_sha256": sources_digest(kernel)}
