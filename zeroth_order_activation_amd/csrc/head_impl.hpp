@@ -314,15 +314,15 @@ __global__ void __launch_bounds__(NT, (NT == 256 ? 4 : 1)) head_estimate_kernel(
             // Box-Muller temporaries would not fit next to a[] and acc[])
             if (SCHED_FENCE) __builtin_amdgcn_sched_barrier(0);
         }
-        sl = wave_sum(sl);
-        ly = wave_sum(ly);
+        sl = wave_total(sl);
+        ly = wave_total(ly);
         const int b = i & 1;
         if ((tid & 63) == 0) { sh_red[b][wid][0] = sl; sh_red[b][wid][1] = ly; }
         __syncthreads();
         float S = 0.f, LY = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) { S += sh_red[b][w][0]; LY += sh_red[b][w][1]; }
-        const float r = A.sigma * LY - log1pf(S * A.smul);
+        const float r = A.sigma * LY - log1p_uniform(S * A.smul);
 #pragma unroll
         for (int j = 0; j < QR; ++j)
 #pragma unroll

@@ -102,37 +102,6 @@ __device__ __forceinline__ uint32_t pack_bf16_pair(float a, float b) {
     return u;
 }
 
-// v + (v moved by one DPP pattern); rows outside ROWM add 0.
-template <int CTRL, int ROWM>
-__device__ __forceinline__ float dpp_add(float v) {
-    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWM, 0xF, false));
-}
-// Sum over the 64 lanes of a wave, returned wave-uniform (every lane active):
-// lane pairs, quads, half rows and rows by quad permutes and mirrors, then the
-// row sums gathered into the last row by the two row broadcasts.
-__device__ __forceinline__ float wave_total(float v) {
-    v = dpp_add<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
-    v = dpp_add<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
-    v = dpp_add<0x141, 0xF>(v);  // row_half_mirror
-    v = dpp_add<0x140, 0xF>(v);  // row_mirror
-    v = dpp_add<0x142, 0xA>(v);  // row_bcast15 into rows 1 and 3
-    v = dpp_add<0x143, 0xC>(v);  // row_bcast31 into rows 2 and 3
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-}
-
-// log1p(x) for a wave-uniform x > -1.  For |x| <= 1/8: log1p(x) = 2 atanh(s),
-// s = x / (2 + x), |s| < 0.059, by its series through s^7 (the next term is
-// below 2e-11 relative); otherwise the library function.
-__device__ __forceinline__ float log1p_uniform(float x) {
-    x = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
-    if (fabsf(x) <= 0.125f) {
-        const float s = x * __builtin_amdgcn_rcpf(2.0f + x);
-        const float s2 = s * s;
-        const float p = fmaf(s2, fmaf(s2, fmaf(s2, 1.0f / 7.0f, 1.0f / 5.0f), 1.0f / 3.0f), 1.0f);
-        return 2.0f * s * p;
-    }
-    return log1pf(x);
-}
 }  // namespace
 
 // H draw groups of GL lanes each (NT = H GL lanes): group g takes draws
