@@ -148,11 +148,14 @@ dust_status dust_estimate_head(const void *logits, int logits_dtype, const float
  * instead of nq.
  *   m : channels per draw, a positive multiple of 4; when m >= 4 nq the window
  *       is the whole vocabulary and the call is dust_estimate_head's.
- * Other arguments and outputs as dust_estimate_head.  Supported: V <= 16384
- * (the probability row and the running sums of a token stay in LDS) unless m
- * covers the vocabulary.
- * Workspace: dust_head_subset_workspace_bytes(T, V, d, K) bytes, the same as
- * dust_head_workspace_bytes (g_hat goes to the outer product in the same form).
+ * Other arguments and outputs as dust_estimate_head, with its limits on V
+ * (fp32 logits V <= 32768, bf16 V <= 65536; DUST_E_UNSUPPORTED beyond).  Rows
+ * of V <= 16384 run in one kernel with the probabilities and running sums of a
+ * token in LDS; wider rows in two (the rewards, then the running sums by
+ * vocabulary segment), regenerating the window's noise in the second.
+ * Workspace: dust_head_subset_workspace_bytes(T, V, d, K) bytes: that of
+ * dust_head_workspace_bytes, plus for V > 16384 room for the rewards and the
+ * window offsets of every (draw, token), 2 * ceil(4KT / 256) * 256 bytes.
  */
 size_t dust_head_subset_workspace_bytes(int64_t T, int64_t V, int64_t d, int64_t K);
 dust_status dust_estimate_head_subset(const void *logits, int logits_dtype, const float *x,

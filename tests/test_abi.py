@@ -72,18 +72,23 @@ def test_head_rejects_bad_arguments_on_host(kw, status, msg):
 def test_head_subset_rejects_bad_arguments_on_host():
     L = dust.lib()
 
-    def call(m, V=1000, T=4):
-        st = L.dust_estimate_head_subset(FAKE, 0, FAKE, FAKE, T, V, 8, 3, m, ctypes.c_float(0.01), 1, 0, 0, 0,
+    def call(m, V=1000, T=4, dtype=0):
+        st = L.dust_estimate_head_subset(FAKE, dtype, FAKE, FAKE, T, V, 8, 3, m, ctypes.c_float(0.01), 1, 0, 0, 0,
                                          FAKE, FAKE, None, None, 0, None)
         return st, L.dust_last_error().decode()
 
     for m in (0, -4, 6):
         st, err = call(m)
         assert st == 1 and "multiple of 4" in err
-    st, err = call(1024, V=20000)  # window below the vocabulary, V beyond the LDS-resident row
-    assert st == 2 and "16384" in err
-    for shape in ((4096, 8192, 512, 256), (7, 1003, 8, 5)):
+    st, err = call(1024, V=70000, dtype=1)  # beyond the widest row
+    assert st == 2 and "65536" in err
+    st, err = call(1024, V=40000, dtype=0)  # fp32 row wider than LDS holds
+    assert st == 2 and "fp32" in err
+    for shape in ((4096, 8192, 512, 256), (7, 1003, 8, 5)):  # rows in LDS: the full estimator's layout
         assert L.dust_head_subset_workspace_bytes(*shape) == L.dust_head_workspace_bytes(*shape)
+    T, K = 8192, 16  # wider rows add K*T rewards and K*T window offsets
+    assert (L.dust_head_subset_workspace_bytes(T, 50304, 1024, K)
+            == L.dust_head_workspace_bytes(T, 50304, 1024, K) + 2 * 4 * K * T)
 
 
 def test_outer_and_noise_reject_bad_arguments():

@@ -1,9 +1,11 @@
 """GPU parity of the vocabulary-subset LM-head estimator against its oracle.
 
 Small cases element by element (fp32 and bf16 logits, ragged V, a one-quad window,
-windows spanning several quads per lane, the degree-6 polynomial, the largest
-supported V), a window covering the vocabulary (bitwise the full estimator), the
-full-size workload-2 shape with m = 1024 on sampled tokens, and determinism.
+windows spanning several quads per lane, the degree-6 polynomial, the widest row of
+the one-pass kernel), rows wider than LDS (the rewards + accumulation passes), a
+window covering the vocabulary (bitwise the full estimator), the full-size
+4096 x 8192 shape with m = 1024 and the 243M-shape head with m = 4096 on sampled
+tokens, and determinism.
 """
 import numpy as np
 import pytest
@@ -37,6 +39,12 @@ SMALL = [
     (5, 16384, 8, 3, 8192, 1e-2, "f32"),    # largest V, 8 quads per lane
     (6, 9000, 8, 4, 16000, 1e-2, "bf16"),   # 4000 >= 2250 quads: the window covers, full estimator path
     (8, 300, 8, 9, 120, 0.1, "f32"),        # library expm1 (large sigma)
+    # rows wider than the one-pass kernel's LDS: rewards pass + accumulation pass
+    (5, 20000, 8, 7, 2048, 1e-2, "f32"),
+    (4, 50304, 8, 5, 4096, 5e-3, "bf16"),   # the 243M-shape vocabulary
+    (3, 40001, 8, 3, 4, 1e-2, "bf16"),      # ragged, one-quad window
+    (6, 30000, 8, 9, 1000, 0.1, "f32"),     # library expm1, window not a multiple of 64 quads
+    (5, 65536, 8, 4, 60000, 5e-3, "bf16"),  # widest bf16 row, window almost everything
 ]
 
 
@@ -89,4 +97,31 @@ def test_workload2_shape_with_a_1024_channel_window():
     ref = ghat[:, rows].cpu().numpy().astype(np.float64).T @ c["x"].astype(np.float64)
     e_w = rel_l2(gw[rows].cpu().numpy(), ref)
     print(f"workload-2 shape, m={m}: sampled ghat {e_g:.2e} rewards {e_r:.2e}; grad_w rows vs G^T X {e_w:.2e}")
+    assert e_g < TOL and e_r < TOL and e_w < 6e-5
+
+
+def test_243m_shape_with_a_4096_channel_window():
+    c = synth.workload(4, matmul=gpu_matmul)
+    T, V, K, sigma, m = c["T"], c["V"], c["K"], c["sigma"], 4096
+    ghat = torch.empty((T, V), dtype=torch.float32, device="cuda")
+    rew = torch.empty((K, T), dtype=torch.float32, device="cuda")
+    z, x, y = logits_to_device(c), dev(c["x"]), dev(c["labels"])
+    gw = dust.estimate_head_subset(z, x, y, K, m, sigma, c["seed_noise"], c["layer"], ghat=ghat, rewards=rew)
+    gw2 = dust.estimate_head_subset(z, x, y, K, m, sigma, c["seed_noise"], c["layer"])
+    torch.cuda.synchronize()
+    assert torch.equal(gw, gw2)  # deterministic, with or without the g_hat and reward outputs
+    toks = np.random.default_rng(24).choice(T, 6, replace=False)
+    zv = logits_values({k: (v[toks] if k == "logits_bf16" else v) for k, v in c.items()})
+    rows_g, rows_r = [], []
+    for j, t in enumerate(toks):
+        g1, r1, _ = oracle.head_estimate_subset(zv[j][None], c["labels"][[t]], K, m, sigma, c["seed_noise"],
+                                                c["layer"], token_offset=int(t))
+        rows_g.append(g1[0])
+        rows_r.append(r1[:, 0])
+    e_g = rel_l2(ghat[toks].cpu().numpy(), np.stack(rows_g))
+    e_r = rel_l2(rew[:, toks].cpu().numpy(), np.stack(rows_r, axis=1))
+    rows = np.random.default_rng(25).choice(V, 64, replace=False)
+    ref = ghat[:, rows].cpu().numpy().astype(np.float64).T @ c["x"].astype(np.float64)
+    e_w = rel_l2(gw[rows].cpu().numpy(), ref)
+    print(f"243M shape, m={m}: sampled ghat {e_g:.2e} rewards {e_r:.2e}; grad_w rows vs G^T X {e_w:.2e}")
     assert e_g < TOL and e_r < TOL and e_w < 6e-5

@@ -226,9 +226,18 @@ dust_status dust_estimate_head(const void* logits, int logits_dtype, const float
     return ok();
 }
 
+// bytes of K*T floats or ints, padded to 256
+static size_t kt_bytes(int64_t T, int64_t K) { return ((size_t)T * (size_t)K * 4 + 255) & ~(size_t)255; }
+
+// dynamic LDS a workgroup of the wide-row subset rewards pass may take
+static constexpr size_t kMaxWideLds = 160 * 1024 - 1024;
+
 size_t dust_head_subset_workspace_bytes(int64_t T, int64_t V, int64_t d, int64_t K) {
-    // the same layout as the full estimator's (which a covering window runs)
-    return dust_head_workspace_bytes(T, V, d, K);
+    // the full estimator's layout (which a covering window runs); rows wider
+    // than LDS add the rewards and window offsets of every (draw, token)
+    const size_t base = dust_head_workspace_bytes(T, V, d, K);
+    if (base == 0 || K <= 0 || V <= dust::kSubsetLdsMaxV) return base;
+    return base + 2 * kt_bytes(T, K);
 }
 
 dust_status dust_estimate_head_subset(const void* logits, int logits_dtype, const float* x, const int32_t* labels,
@@ -254,14 +263,18 @@ dust_status dust_estimate_head_subset(const void* logits, int logits_dtype, cons
     if (s != DUST_OK) return s;
     if (V <= 0) return fail(DUST_E_INVALID, "dust_estimate_head_subset: V must be >= 1");
     if (d <= 0) return fail(DUST_E_INVALID, "dust_estimate_head_subset: d must be >= 1");
-    if (V > 16384)
-        return fail(DUST_E_UNSUPPORTED, "dust_estimate_head_subset: V > 16384 is not supported below a full window");
-    if (d > 65535LL * 128) return fail(DUST_E_UNSUPPORTED, "dust_estimate_head_subset: d too large");
-    const dust::HeadPlan plan = dust::plan_head(V, logits_dtype, sigma);  // for the Taylor degree
+    if (V > 65535LL * 128 || d > 65535LL * 128)
+        return fail(DUST_E_UNSUPPORTED, "dust_estimate_head_subset: V or d too large");
+    const dust::HeadPlan plan = dust::plan_head(V, logits_dtype, sigma);  // the Taylor degree and the row limits
+    if (!plan.ok) return fail(DUST_E_UNSUPPORTED, "dust_estimate_head_subset: %s", plan.why);
+    const bool wide = V > dust::kSubsetLdsMaxV;
+    if (wide && dust::head_subset_wide_lds_bytes(V, logits_dtype) > kMaxWideLds)
+        return fail(DUST_E_UNSUPPORTED, "dust_estimate_head_subset: the logit row does not fit in LDS");
     const bool pairs = head_pairs_path(T, V, d);
     const size_t ghat_ws = (ghat || pairs) ? 0 : head_ghat_bytes(T, V);
     const size_t outer_ws = dust::outer_workspace_bytes(T, V, d);
-    const size_t need = ghat_ws + outer_ws;
+    const size_t kt_ws = wide ? kt_bytes(T, K) : 0;  // rewards, then window offsets
+    const size_t need = ghat_ws + outer_ws + 2 * kt_ws;
     if (need > 0 && (workspace == nullptr || workspace_bytes < need))
         return fail(DUST_E_WORKSPACE, "dust_estimate_head_subset: workspace of %zu bytes needed, %zu given", need,
                     workspace ? workspace_bytes : (size_t)0);
@@ -277,7 +290,9 @@ dust_status dust_estimate_head_subset(const void* logits, int logits_dtype, cons
     A.ghi = pr.hi;
     A.glo = pr.lo;
     A.ldp = pr.ld;
-    hipError_t e = dust::launch_head_subset(plan, logits_dtype, A, m, st);
+    float* rew_ws = wide ? reinterpret_cast<float*>(ws + ghat_ws + outer_ws) : nullptr;
+    int* off_ws = wide ? reinterpret_cast<int*>(ws + ghat_ws + outer_ws + kt_ws) : nullptr;
+    hipError_t e = dust::launch_head_subset(plan, logits_dtype, A, m, rew_ws, off_ws, st);
     if (e != hipSuccess) return device_fail("dust_estimate_head_subset: estimator launch", e);
     if ((e = record_stage(0, st)) != hipSuccess) return device_fail("dust_estimate_head_subset: stage event", e);
     e = dust::launch_outer(g, x, T, V, d, grad_w, ows, outer_ws, st, pr.hi != nullptr);

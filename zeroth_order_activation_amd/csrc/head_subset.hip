@@ -32,6 +32,8 @@
 // sums, and the read-modify-write of the window's running sums.  The noise of
 // the next draw is generated between publishing a draw's wave sum and the
 // barrier, so the reduction's latency hides behind it.
+#include <algorithm>
+
 #include "dust_device.hpp"
 #include "dust_internal.hpp"
 
@@ -286,8 +288,208 @@ __global__ void __launch_bounds__(GL * H) head_subset_kernel(HeadArgs A, int mq,
     }
 }
 
+// ---- rows beyond LDS (V > 16384): a rewards pass, then an accumulation pass ----
+//
+// The probabilities and the running sums of a wide row do not fit in LDS
+// together.  The rewards pass keeps only the logit row (in its own type) in
+// LDS and recomputes p per window channel; every wave works on whole draws
+// (wave w: draws w, w + 16, ... of a chunk), so the wave's own reduction gives
+// S and the draw loop has no barrier.  It writes r and the window offset o of
+// every (draw, token).  The accumulation pass gives each workgroup one
+// vocabulary segment of one token with the running sums in registers (lane l
+// owns quads l, l + 256, ... of the segment); per draw it regenerates the
+// noise of the segment's quads that lie in the window (and of the label quad),
+// skipping 64-quad blocks the window misses, and adds r a / pi.  The noise is
+// generated twice, once per pass.
+constexpr int RNT = 1024;  // rewards pass: lanes per workgroup
+constexpr int BNT = 256;   // accumulation pass: lanes per workgroup
+constexpr int BQS = 8;     // accumulation pass: quads per lane (segments of BNT * BQS quads)
+
+template <int LT>
+__device__ __forceinline__ f32x4 row_quad(const unsigned char* zl, int q) {  // quad q of the LDS row, as fp32
+    f32x4 r;
+    if (LT == 0) {
+        const float4 v = reinterpret_cast<const float4*>(zl)[q];
+        r.v[0] = v.x; r.v[1] = v.y; r.v[2] = v.z; r.v[3] = v.w;
+    } else {
+        const uint2 v = reinterpret_cast<const uint2*>(zl)[q];
+        r.v[0] = __uint_as_float(v.x << 16);
+        r.v[1] = __uint_as_float(v.x & 0xFFFF0000u);
+        r.v[2] = __uint_as_float(v.y << 16);
+        r.v[3] = __uint_as_float(v.y & 0xFFFF0000u);
+    }
+    return r;
+}
+
+__host__ __device__ constexpr size_t wide_row_bytes(int nq, int lt) {  // LDS row, padded to 16 bytes
+    return (((size_t)(nq + 1) * (lt == 0 ? 16 : 8)) + 15) & ~(size_t)15;
+}
+
+template <int LT, int DEG>
+__global__ void __launch_bounds__(RNT) head_subset_rewards_kernel(HeadArgs A, int mq, float* __restrict__ rew,
+                                                                   int* __restrict__ woff) {
+    extern __shared__ __align__(16) unsigned char zl[];
+    __shared__ float sh[RNT / 64];
+    const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int V = A.V, nq = (V + 3) >> 2;
+    float4* DR = reinterpret_cast<float4*>(zl + wide_row_bytes(nq, LT));
+    const void* row = reinterpret_cast<const unsigned char*>(A.logits) + (size_t)t * V * (LT == 0 ? 4 : 2);
+
+    // ---- clean statistics; the row (plus a spare quad of -inf) goes to LDS ----
+    float m = -__builtin_inff();
+    for (int q = tid; q <= nq; q += RNT) {
+        f32x4 z;
+        if ((V & 3) == 0 && q < nq) {
+            if (LT == 0) {
+                const float4 v = reinterpret_cast<const float4*>(row)[q];
+                z.v[0] = v.x; z.v[1] = v.y; z.v[2] = v.z; z.v[3] = v.w;
+            } else {
+                const uint2 v = reinterpret_cast<const uint2*>(row)[q];
+                z.v[0] = __uint_as_float(v.x << 16);
+                z.v[1] = __uint_as_float(v.x & 0xFFFF0000u);
+                z.v[2] = __uint_as_float(v.y << 16);
+                z.v[3] = __uint_as_float(v.y & 0xFFFF0000u);
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) z.v[c] = 4 * q + c < V ? logit_at<LT>(row, 4 * q + c) : -__builtin_inff();
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) m = fmaxf(m, z.v[c]);
+        if (LT == 0) {
+            reinterpret_cast<float4*>(zl)[q] = make_float4(z.v[0], z.v[1], z.v[2], z.v[3]);
+        } else {  // back to bf16 bits: exact (-inf included)
+            uint2 b;
+            b.x = (__float_as_uint(z.v[0]) >> 16) | (__float_as_uint(z.v[1]) & 0xFFFF0000u);
+            b.y = (__float_as_uint(z.v[2]) >> 16) | (__float_as_uint(z.v[3]) & 0xFFFF0000u);
+            reinterpret_cast<uint2*>(zl)[q] = b;
+        }
+    }
+    m = block_reduce_max<RNT>(m, sh);  // its barriers publish the row
+    float s = 0.f;
+    for (int q = tid; q < nq; q += RNT) {
+        const f32x4 z = row_quad<LT>(zl, q);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) s += __expf(z.v[c] - m);
+    }
+    s = block_reduce_sum<RNT>(s, sh);
+    const float lse2 = (m + __logf(s)) * kL2e;
+
+    const uint32_t y = (uint32_t)A.labels[t];
+    const int qy = (int)(y >> 2), cy = (int)(y & 3u);
+    const uint32_t tok = A.tok0 + (uint32_t)t;
+    const float py = __builtin_amdgcn_exp2f(fmaf(row_quad<LT>(zl, qy).v[cy], kL2e, -lse2));
+
+    for (int i0 = 0; i0 < A.K; i0 += SKC) {
+        const int kc = min(SKC, A.K - i0);
+        __syncthreads();  // the previous chunk's terms fully used
+        for (int i = tid; i < kc; i += RNT) {
+            const uint32_t draw = A.draw0 + (uint32_t)(i0 + i);
+            const int o = (int)window_offset(tok, draw, A.layer, A.k0, A.k1, (uint32_t)nq);
+            const int jy = qy - o < 0 ? qy - o + nq : qy - o;
+            const bool in_w = jy < mq;
+            const u32x4 w = philox4x32_10<false>(tok, (uint32_t)qy, draw, A.layer, A.k0, A.k1);
+            float gg[4];
+            box_muller_unscaled(w.x, w.y, gg[0], gg[1]);
+            box_muller_unscaled(w.z, w.w, gg[2], gg[3]);
+            const float ay = cy == 0 ? gg[0] : cy == 1 ? gg[1] : cy == 2 ? gg[2] : gg[3];
+            DR[i] = make_float4(__int_as_float(o), in_w ? 0.f : py * em1s<DEG>(ay, A), ay, 0.f);
+        }
+        __syncthreads();
+        for (int ii = wv; ii < kc; ii += RNT / 64) {  // wave-uniform
+            const uint32_t draw = A.draw0 + (uint32_t)(i0 + ii);
+            const float4 dr = DR[ii];
+            const int o = __builtin_amdgcn_readfirstlane(__float_as_int(dr.x));
+            float sl = 0.f;
+            for (int j0 = 0; j0 < mq; j0 += 64) {
+                const int j = j0 + lane;
+                int q = o + j;
+                q = q >= nq ? q - nq : q;
+                q = j < mq ? q : nq;  // past the window: the spare quad
+                const f32x4 g = gauss4_unscaled_uniform(tok, (uint32_t)q, draw, A.layer, A.k0, A.k1);
+                const f32x4 z = row_quad<LT>(zl, q);
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    sl = fmaf(__builtin_amdgcn_exp2f(fmaf(z.v[c], kL2e, -lse2)), em1s<DEG>(g.v[c], A), sl);
+            }
+            const float S = wave_total(sl) + dr.y;
+            const float r = A.sigma * dr.z - log1p_uniform(S * A.smul);
+            if (lane == 0) {
+                rew[(size_t)(i0 + ii) * A.T + t] = r;
+                woff[(size_t)(i0 + ii) * A.T + t] = o;
+            }
+        }
+    }
+}
+
+__global__ void __launch_bounds__(BNT) head_subset_accum_kernel(HeadArgs A, int mq, float winv, int nseg,
+                                                                const float* __restrict__ rew,
+                                                                const int* __restrict__ woff) {
+    const int t = blockIdx.x / nseg, sg = blockIdx.x % nseg, tid = threadIdx.x;
+    const int V = A.V, nq = (V + 3) >> 2;
+    const int qbase = sg * BNT * BQS + tid;
+    const uint32_t y = (uint32_t)A.labels[t];
+    const int qy = (int)(y >> 2), cy = (int)(y & 3u);
+    const uint32_t tok = A.tok0 + (uint32_t)t;
+    float acc[BQS][4];
+#pragma unroll
+    for (int k = 0; k < BQS; ++k)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[k][c] = 0.f;
+    for (int i = 0; i < A.K; ++i) {
+        const int o = woff[(size_t)i * A.T + t];  // wave-uniform
+        const float r = rew[(size_t)i * A.T + t];
+        const float rw = r * winv;
+        const uint32_t draw = A.draw0 + (uint32_t)i;
+#pragma unroll
+        for (int k = 0; k < BQS; ++k) {
+            const int q = qbase + k * BNT;
+            int dq = q - o;
+            dq = dq < 0 ? dq + nq : dq;
+            const bool in = q < nq && dq < mq;
+            const bool lab = q == qy;
+            if (__builtin_amdgcn_ballot_w64(in || lab)) {  // wave-uniform: skip blocks the window misses
+                const f32x4 g = gauss4_unscaled_uniform(tok, (uint32_t)q, draw, A.layer, A.k0, A.k1);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const float w = (lab && c == cy) ? r : (in ? rw : 0.f);  // label weight 1, window nq/mq
+                    acc[k][c] = fmaf(w, g.v[c], acc[k][c]);
+                }
+            }
+        }
+    }
+    float* out = A.ghat ? A.ghat + (size_t)t * V : nullptr;
+    uint16_t* ohi = A.ghi ? A.ghi + (size_t)t * A.ldp : nullptr;
+    uint16_t* olo = A.ghi ? A.glo + (size_t)t * A.ldp : nullptr;
+#pragma unroll
+    for (int k = 0; k < BQS; ++k) {
+        const int q = qbase + k * BNT;
+        float v[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = 4 * q + c < V ? acc[k][c] * A.gscale : 0.f;
+        if (ohi && 4 * (int64_t)q < A.ldp) {
+            uint2 h, l;
+            h.x = pack_bf16_pair(v[0], v[1]);
+            h.y = pack_bf16_pair(v[2], v[3]);
+            l.x = pack_bf16_pair(v[0] - __uint_as_float(h.x << 16), v[1] - __uint_as_float(h.x & 0xFFFF0000u));
+            l.y = pack_bf16_pair(v[2] - __uint_as_float(h.y << 16), v[3] - __uint_as_float(h.y & 0xFFFF0000u));
+            *reinterpret_cast<uint2*>(ohi + 4 * q) = h;
+            *reinterpret_cast<uint2*>(olo + 4 * q) = l;
+        }
+        if (out && q < nq) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (4 * q + c < V) out[4 * q + c] = v[c];
+        }
+    }
+}
+
 // P and ACC hold 4 (nq + 1) floats each, DR SKC float4s.
 size_t head_subset_lds_bytes(int64_t V) { return (size_t)(8 * ((V + 3) / 4 + 1) + 4 * SKC) * sizeof(float); }
+
+size_t head_subset_wide_lds_bytes(int64_t V, int logits_dtype) {
+    return wide_row_bytes((int)((V + 3) / 4), logits_dtype) + (size_t)SKC * 16;
+}
 
 int head_subset_qw(int64_t m, int64_t V) {
     const int64_t nq = (V + 3) / 4, mq = m / 4 < nq ? m / 4 : nq;
@@ -296,9 +498,33 @@ int head_subset_qw(int64_t m, int64_t V) {
     return 0;
 }
 
-hipError_t launch_head_subset(const HeadPlan& plan, int logits_dtype, const HeadArgs& A, int64_t m,
-                              hipStream_t stream) {
+hipError_t launch_head_subset(const HeadPlan& plan, int logits_dtype, const HeadArgs& A, int64_t m, float* rew_ws,
+                              int* off_ws, hipStream_t stream) {
     const int64_t nq = (A.V + 3) / 4, mq = m / 4 < nq ? m / 4 : nq;
+    if (A.V > kSubsetLdsMaxV) {  // two passes
+        const float winv = (float)((double)nq / (double)mq);
+        float* rew = A.rewards ? A.rewards : rew_ws;
+        const size_t lds = head_subset_wide_lds_bytes(A.V, logits_dtype);
+        hipError_t e = hipErrorInvalidConfiguration;
+#define DUST_WIDE_CASE(LT_, DEG_)                                                                      \
+        if (logits_dtype == LT_ && plan.deg == DEG_) {                                                \
+            auto k = head_subset_rewards_kernel<LT_, DEG_>;                                            \
+            if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),                             \
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess) \
+                return e;                                                                              \
+            hipLaunchKernelGGL(k, dim3(A.T), dim3(RNT), lds, stream, A, (int)mq, rew, off_ws);         \
+            e = hipGetLastError();                                                                     \
+        }
+        DUST_WIDE_CASE(0, 4) DUST_WIDE_CASE(0, 6) DUST_WIDE_CASE(0, 0)
+        DUST_WIDE_CASE(1, 4) DUST_WIDE_CASE(1, 6) DUST_WIDE_CASE(1, 0)
+#undef DUST_WIDE_CASE
+        if (e != hipSuccess) return e;
+        const int64_t nqo = A.ghi ? std::max<int64_t>(nq, (A.ldp + 3) / 4) : nq;
+        const int nseg = (int)((nqo + BNT * BQS - 1) / (BNT * BQS));
+        hipLaunchKernelGGL(head_subset_accum_kernel, dim3((unsigned)(A.T * nseg)), dim3(BNT), 0, stream, A, (int)mq,
+                           winv, nseg, rew, off_ws);
+        return hipGetLastError();
+    }
     const int qw = head_subset_qw(m, A.V);
     const size_t lds = head_subset_lds_bytes(A.V);
     const float winv = (float)((double)nq / (double)mq);
