@@ -436,19 +436,23 @@ __global__ void __launch_bounds__(BNT) head_subset_accum_kernel(HeadArgs A, int 
     for (int k = 0; k < BQS; ++k)
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[k][c] = 0.f;
+    // this wave's 64-quad blocks start at wq0 + k BNT
+    const int wq0 = sg * BNT * BQS + __builtin_amdgcn_readfirstlane(tid & ~63);
     for (int i = 0; i < A.K; ++i) {
         const int o = woff[(size_t)i * A.T + t];  // wave-uniform
         const float r = rew[(size_t)i * A.T + t];
         const float rw = r * winv;
         const uint32_t draw = A.draw0 + (uint32_t)i;
+        // the window as [o, e1) and, when it wraps, [0, e2)
+        const int e1 = min(o + mq, nq), e2 = o + mq - nq;
 #pragma unroll
         for (int k = 0; k < BQS; ++k) {
-            const int q = qbase + k * BNT;
-            int dq = q - o;
-            dq = dq < 0 ? dq + nq : dq;
-            const bool in = q < nq && dq < mq;
-            const bool lab = q == qy;
-            if (__builtin_amdgcn_ballot_w64(in || lab)) {  // wave-uniform: skip blocks the window misses
+            const int b0 = wq0 + k * BNT;  // wave-uniform: the block [b0, b0 + 64)
+            const bool hit = (b0 < e1 && b0 + 64 > o) || b0 < e2 || (qy >= b0 && qy < b0 + 64);
+            if (hit) {  // scalar test: blocks the window misses cost no vector work
+                const int q = qbase + k * BNT;
+                const bool in = q < nq && ((q >= o && q < e1) || q < e2);
+                const bool lab = q == qy;
                 const f32x4 g = gauss4_unscaled_uniform(tok, (uint32_t)q, draw, A.layer, A.k0, A.k1);
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
