@@ -329,3 +329,132 @@ def cosine_law_c(g, x) -> float:
     n = g.shape[1]
     num = (n + 1) * np.sum((x * x).sum(1) * (g * g).sum(1))
     return float(num / np.sum(G * G))
+
+
+# --------------------------------------------------------------------------
+# Attention internals: the value projection
+# --------------------------------------------------------------------------
+# TL;DR page, section 1, "credit assignment without backprop": attention
+# internals are handled like the other linear layers, but their reward is the
+# change of the attention output rather than the token's loss; the news
+# article's mechanism paragraph judges that change against the error signal;
+# the iitog.ru mechanics paragraph takes the error at the attention output over
+# the current and future tokens.  Reading: with e_s the error (gradient of the
+# loss) at the attention output of token s, the reward of token t's noise is
+# the first-order loss reduction over the outputs it can move,
+#     r_t = -sum_{s >= t, same sequence} <e_s, o'_s - o_s>,
+# every token of the sequence being perturbed in the same draw.  For the value
+# projection (y_t = v_t = W_V u_t) only the values move, so the probabilities
+# stay those of the clean pass.
+
+def causal_attention(q, k, v, S: int, H: int) -> np.ndarray:
+    """Causal multi-head self-attention within sequences of S tokens (tokens
+    t = b S + s): o_s = concat_h sum_{t <= s} softmax_t(q_s . k_t / sqrt(dh)) v_t,
+    dh = d / H, in fp64."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    T, d = q.shape
+    dh = d // H
+    o = np.zeros((T, d))
+    future = np.triu(np.ones((S, S), bool), 1)
+    for b in range(T // S):
+        rows = slice(b * S, (b + 1) * S)
+        for h in range(H):
+            ch = slice(h * dh, (h + 1) * dh)
+            L = q[rows, ch] @ k[rows, ch].T / np.sqrt(dh)
+            L[future] = -np.inf
+            L -= L.max(axis=1, keepdims=True)
+            P = np.exp(L)
+            P /= P.sum(axis=1, keepdims=True)
+            o[rows, ch] = P @ v[rows, ch]
+    return o
+
+
+def attn_v_estimate(q, k, v, e, S: int, H: int, K: int, sigma: float, seed: int, layer: int,
+                    token_offset: int = 0, draw_offset: int = 0):
+    """Value-projection estimator: per draw i, v' = v + sigma a^(i) on every
+    token, o' the recomputed attention output, c_s = <e_s, o'_s - o_s>,
+    r_t = -sum_{s >= t in t's sequence} c_s, and
+    g_hat_t = -(1/(K sigma)) sum_i r_t^(i) a_t^(i).  Returns (g_hat [T,d],
+    rewards [K,T])."""
+    q = np.asarray(q, np.float64)
+    T, d = q.shape
+    e = np.asarray(e, np.float64)
+    v = np.asarray(v, np.float64)
+    o = causal_attention(q, k, v, S, H)
+    ghat = np.zeros((T, d))
+    rew = np.zeros((K, T))
+    for i in range(K):
+        a = noise_block(seed, layer, draw_offset + i, 1, token_offset, T, d)[0]
+        c = np.sum(e * (causal_attention(q, k, v + sigma * a, S, H) - o), axis=1)
+        for b in range(T // S):
+            cs = c[b * S:(b + 1) * S]
+            rew[i, b * S:(b + 1) * S] = -np.cumsum(cs[::-1])[::-1]
+        ghat -= rew[i][:, None] * a
+    return ghat / (K * sigma), rew
+
+
+def attn_v_estimate_tokens(q, k, v, e, S: int, H: int, K: int, sigma: float, seed: int, layer: int,
+                           tokens, token_offset: int = 0, draw_offset: int = 0):
+    """The same estimator on the tokens ``tokens`` only: the attention outputs of
+    the queries s >= t of their sequences are recomputed row by row (for
+    sampled checks of large inputs).  Returns (g_hat [len(tokens), d],
+    rewards [K, len(tokens)])."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    e = np.asarray(e, np.float64)
+    T, d = q.shape
+    dh = d // H
+    tokens = [int(t) for t in tokens]
+    need = sorted({s for t in tokens for s in range(t, (t // S + 1) * S)})
+    probs = {}  # query s -> [H, s - b S + 1] clean probabilities over its keys
+    for s in need:
+        b0 = (s // S) * S
+        Ph = []
+        for h in range(H):
+            ch = slice(h * dh, (h + 1) * dh)
+            L = k[b0:s + 1, ch] @ q[s, ch] / np.sqrt(dh)
+            P = np.exp(L - L.max())
+            Ph.append(P / P.sum())
+        probs[s] = Ph
+    ghat = np.zeros((len(tokens), d))
+    rew = np.zeros((K, len(tokens)))
+    for i in range(K):
+        a = noise_block(seed, layer, draw_offset + i, 1, token_offset, T, d)[0]
+        c = {}
+        for s in need:
+            b0 = (s // S) * S
+            do = np.zeros(d)
+            for h in range(H):
+                ch = slice(h * dh, (h + 1) * dh)
+                vv = v[b0:s + 1, ch]
+                do[ch] = probs[s][h] @ (vv + sigma * a[b0:s + 1, ch]) - probs[s][h] @ vv
+            c[s] = float(e[s] @ do)
+        for j, t in enumerate(tokens):
+            rew[i, j] = -sum(c[s] for s in range(t, (t // S + 1) * S))
+            ghat[j] -= rew[i, j] * a[t]
+    return ghat / (K * sigma), rew
+
+
+def attn_v_analytic(q, k, e, S: int, H: int) -> np.ndarray:
+    """Gradient of sum_s <e_s, o_s> w.r.t. the values: per head, P^T e (fp64)."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    e = np.asarray(e, np.float64)
+    T, d = q.shape
+    dh = d // H
+    g = np.zeros((T, d))
+    future = np.triu(np.ones((S, S), bool), 1)
+    for b in range(T // S):
+        rows = slice(b * S, (b + 1) * S)
+        for h in range(H):
+            ch = slice(h * dh, (h + 1) * dh)
+            L = q[rows, ch] @ k[rows, ch].T / np.sqrt(dh)
+            L[future] = -np.inf
+            L -= L.max(axis=1, keepdims=True)
+            P = np.exp(L)
+            P /= P.sum(axis=1, keepdims=True)
+            g[rows, ch] = P.T @ e[rows, ch]
+    return g

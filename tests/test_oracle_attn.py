@@ -1,0 +1,98 @@
+"""Pins of the oracle's attention value-projection estimator (TL;DR page, section 1,
+"credit assignment without backprop": attention internals rewarded by the change of the
+attention output; news article, mechanism paragraph: that change judged against the error
+signal; iitog.ru, mechanics paragraph: the error at the attention output over the current
+and future tokens).  Reading: r_t = -sum_{s >= t in t's sequence} <e_s, o'_s - o_s>.
+
+- the oracle's causal attention equals torch's scaled_dot_product_attention (fp64);
+- every reward equals the definition evaluated with torch's attention on v + sigma a;
+- the closed-form target P^T e equals torch autograd of sum_s <e_s, o_s> w.r.t. v;
+- one-token sequences reduce to r = -sigma <e_t, a_t> (no mixing across tokens);
+- unbiased: as K grows the estimate regresses on the analytic gradient with slope 1;
+- draw additivity: two draw ranges combine to the estimate over their union.
+"""
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+import oracle
+
+SEED = 0x4455535400000031
+
+
+def _inputs(B, S, H, dh, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    T, d = B * S, H * dh
+    return [rng.standard_normal((T, d)) for _ in range(4)]  # q, k, v, e
+
+
+def _torch_attn(x_q, x_k, x_v, B, S, H):
+    def heads(x):
+        return torch.as_tensor(x, dtype=torch.float64).reshape(B, S, H, -1).permute(0, 2, 1, 3)
+    o = F.scaled_dot_product_attention(heads(x_q), heads(x_k), heads(x_v), is_causal=True)
+    return o.permute(0, 2, 1, 3).reshape(B * S, -1)
+
+
+def test_causal_attention_is_torch_sdpa():
+    B, S, H, dh = 2, 7, 3, 4
+    q, k, v, _ = _inputs(B, S, H, dh, 1)
+    np.testing.assert_allclose(oracle.causal_attention(q, k, v, S, H), _torch_attn(q, k, v, B, S, H).numpy(),
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_rewards_are_the_output_change_against_the_error():
+    B, S, H, dh = 2, 5, 2, 4
+    q, k, v, e = _inputs(B, S, H, dh, 2)
+    K, sigma, t0, d0 = 4, 3e-2, 11, 5
+    g, rew = oracle.attn_v_estimate(q, k, v, e, S, H, K, sigma, SEED, 2, token_offset=t0, draw_offset=d0)
+    a = oracle.noise_block(SEED, 2, d0, K, t0, B * S, H * dh)
+    o = _torch_attn(q, k, v, B, S, H).numpy()
+    expect = np.zeros_like(rew)
+    for i in range(K):
+        c = np.sum(e * (_torch_attn(q, k, v + sigma * a[i], B, S, H).numpy() - o), axis=1)
+        for t in range(B * S):
+            b = t // S
+            expect[i, t] = -c[t:(b + 1) * S].sum()
+    np.testing.assert_allclose(rew, expect, rtol=1e-9, atol=1e-13)
+    np.testing.assert_allclose(g, -np.einsum("it,itd->td", rew, a) / (K * sigma), rtol=1e-12, atol=1e-14)
+
+
+def test_analytic_target_is_autograd():
+    B, S, H, dh = 2, 6, 2, 3
+    q, k, v, e = _inputs(B, S, H, dh, 3)
+    vt = torch.tensor(v, requires_grad=True)
+    loss = (torch.as_tensor(e) * _torch_attn(q, k, vt, B, S, H)).sum()
+    loss.backward()
+    np.testing.assert_allclose(oracle.attn_v_analytic(q, k, e, S, H), vt.grad.numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_one_token_sequences_have_no_mixing():
+    B, S, H, dh = 9, 1, 2, 4
+    q, k, v, e = _inputs(B, S, H, dh, 4)
+    K, sigma = 6, 0.1
+    g, rew = oracle.attn_v_estimate(q, k, v, e, S, H, K, sigma, SEED, 2)
+    a = oracle.noise_block(SEED, 2, 0, K, 0, B, H * dh)
+    np.testing.assert_allclose(rew, -sigma * np.einsum("td,itd->it", e, a), rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(g, np.einsum("itd,it->td", a, np.einsum("td,itd->it", e, a)) / K, rtol=1e-10)
+
+
+def test_estimate_is_unbiased_for_the_analytic_gradient():
+    B, S, H, dh = 2, 4, 2, 2
+    q, k, v, e = _inputs(B, S, H, dh, 5)
+    K, sigma = 20000, 1e-2
+    g, _ = oracle.attn_v_estimate(q, k, v, e, S, H, K, sigma, SEED, 2)
+    ga = oracle.attn_v_analytic(q, k, e, S, H)
+    slope = float((g * ga).sum() / (ga * ga).sum())
+    print(f"slope of the value-projection estimate on P^T e: {slope:.3f}, cosine {oracle.cosine(g, ga):.3f}")
+    assert abs(slope - 1.0) < 0.06
+
+
+def test_draw_ranges_combine():
+    B, S, H, dh = 2, 5, 2, 4
+    q, k, v, e = _inputs(B, S, H, dh, 6)
+    sigma = 2e-2
+    g_all, r_all = oracle.attn_v_estimate(q, k, v, e, S, H, 7, sigma, SEED, 2, draw_offset=3)
+    g1, r1 = oracle.attn_v_estimate(q, k, v, e, S, H, 4, sigma, SEED, 2, draw_offset=3)
+    g2, r2 = oracle.attn_v_estimate(q, k, v, e, S, H, 3, sigma, SEED, 2, draw_offset=7)
+    np.testing.assert_allclose(r_all, np.concatenate([r1, r2]), rtol=0, atol=0)
+    np.testing.assert_allclose(g_all, (4 * g1 + 3 * g2) / 7, rtol=1e-12, atol=1e-15)
