@@ -194,6 +194,37 @@ dust_status dust_estimate_linear(const float *u, const float *h, const float *x_
                                  float *grad_w, float *ghat, float *rewards,
                                  void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Attention value projection (W_V): the attention-internal estimator.
+ * Method: TL;DR page "Dust: zeroth-order Transformer pretraining without backprop",
+ * section 1, "credit assignment without backprop" (attention internals are rewarded by
+ * the change of the attention output, not the token's loss) and "reducing interference"
+ * (only the attention output is recomputed); the tahou.com news article, mechanism
+ * paragraph (that change is judged against the error signal); the iitog.ru page,
+ * mechanics paragraph (the error at the attention output over current and future
+ * tokens).  Reading: causal multi-head attention within sequences of S tokens (token
+ * t = b S + s), every token's value v_t perturbed by sigma a_t^(i) in the same draw, e_s
+ * the error (loss gradient) at the attention output o_s:
+ *   r_t   = -sum_{s >= t, same sequence} <e_s, o'_s - o_s>
+ *         = -sigma sum_{s >= t} sum_{t' <= s} P_{s t'} <e_s, a_t'>     (per head; exact:
+ *           only the values move, so the probabilities P stay those of the clean pass)
+ *   g_hat_t = -(1/(K sigma)) sum_i r_t a_t;   G_WV = sum_t g_hat_t u_t^T.
+ *   q, k   : float [T, d]  clean query and key projections (heads of 64 channels: d = 64 H)
+ *   e      : float [T, d]  error at the attention output (per head, before W_O)
+ *   u      : float [T, d]  input of W_V (the u_t of G_WV)
+ *   grad_w : OUT float [d, d];  ghat : OUT float [T, d] or NULL;  rewards : OUT float [K, T] or NULL.
+ * The values themselves are not needed.  Noise counter: (token, channel/4, draw, layer).
+ * Supported: S a multiple of 64 up to 4096, T a multiple of S, d = 64 H.
+ * Stages (dust_set_stage_event): 2 = after the rewards, 0 = after g_hat, 1 = after G_WV.
+ * Workspace: dust_attn_v_workspace_bytes(T, S, d, H, K) bytes.
+ */
+size_t dust_attn_v_workspace_bytes(int64_t T, int64_t S, int64_t d, int64_t H, int64_t K);
+dust_status dust_estimate_attn_v(const float *q, const float *k, const float *e, const float *u,
+                                 int64_t T, int64_t S, int64_t d, int64_t H, int64_t K, float sigma,
+                                 uint64_t seed, uint32_t layer, uint32_t token_offset,
+                                 uint32_t draw_offset, float *grad_w, float *ghat, float *rewards,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

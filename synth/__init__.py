@@ -17,6 +17,7 @@ import numpy as np
 NOISE_SEED_BASE = 0x4455535400000000  # noise seed of workload i is this + i
 HEAD_LAYER = 1
 W1_LAYER = 0
+WV_LAYER = 2
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -88,13 +89,30 @@ def linear_case(T: int, d: int, n: int, V: int, *, seed: int, ln_eps: float = 1e
             "ln_eps": ln_eps}
 
 
-# The five named workloads (token counts are batch x sequence, flattened t = b*S + s).
+def attn_case(B: int, S: int, H: int, seed: int, dh: int = 64, matmul=None) -> dict:
+    """Inputs of the attention value-projection estimator: the attention input
+    u ~ N(0,1) [T,d] (T = B S, d = H dh), projections W_Q, W_K, W_V ~ N(0, 1/d)
+    and their clean outputs q, k, v = u W^T, and the error at the attention
+    output e ~ N(0,1) [T,d] (it stands in for the back-projected output error
+    of W_O).  ``matmul(X, W)`` computes X W^T (numpy by default)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    T, d = B * S, H * dh
+    U = rng.standard_normal((T, d), dtype=np.float32)
+    Ws = [(rng.standard_normal((d, d), dtype=np.float32) / np.float32(np.sqrt(d))) for _ in range(3)]
+    E = rng.standard_normal((T, d), dtype=np.float32)
+    mm = matmul or (lambda X, W: (X.astype(np.float64) @ W.astype(np.float64).T).astype(np.float32))
+    q, k, v = (np.ascontiguousarray(mm(U, W), dtype=np.float32) for W in Ws)
+    return {"u": U, "q": q, "k": k, "v": v, "e": E, "T": T, "S": S, "H": H, "d": d}
+
+
+# The named workloads (token counts are batch x sequence, flattened t = b*S + s).
 WORKLOADS = {
     1: dict(kind="head", T=256, V=512, d=64, K=64, sigma=1e-2, labels="uniform", logits_dtype="f32"),
     2: dict(kind="head", T=4096, V=8192, d=512, K=256, sigma=1e-2, labels="zipf", logits_dtype="f32"),
     3: dict(kind="linear", T=4096, d=512, n=2048, V=8192, K=64, sigma=1e-2),
     4: dict(kind="head", T=8192, V=50304, d=1024, K=16, sigma=5e-3, labels="zipf", logits_dtype="bf16"),
     5: dict(kind="linear", T=2048, d=512, n=2048, V=8192, K=(64, 256, 1024, 4096, 16384), sigma=1e-2),
+    6: dict(kind="attn_v", B=2, S=2048, H=8, K=64, sigma=1e-2),
 }
 
 
@@ -105,6 +123,9 @@ def workload(i: int, matmul=None) -> dict:
         case = head_case(w["T"], w["V"], w["d"], seed=1000 + i, labels=w["labels"],
                          logits_dtype=w["logits_dtype"], matmul=matmul)
         case["layer"] = HEAD_LAYER
+    elif w["kind"] == "attn_v":
+        case = attn_case(w["B"], w["S"], w["H"], seed=1000 + i, matmul=matmul)
+        case["layer"] = WV_LAYER
     else:
         case = linear_case(w["T"], w["d"], w["n"], w["V"], seed=1000 + i)
         case["layer"] = W1_LAYER

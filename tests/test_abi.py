@@ -91,6 +91,23 @@ def test_head_subset_rejects_bad_arguments_on_host():
             == L.dust_head_workspace_bytes(T, 50304, 1024, K) + 2 * 4 * K * T)
 
 
+def test_attn_v_rejects_bad_arguments_on_host():
+    L = dust.lib()
+
+    def call(T=128, S=64, d=128, H=2, K=3, sigma=0.01):
+        st = L.dust_estimate_attn_v(FAKE, FAKE, FAKE, FAKE, T, S, d, H, K, ctypes.c_float(sigma), 1, 2, 0, 0,
+                                    FAKE, None, None, FAKE, 1 << 30, None)
+        return st, L.dust_last_error().decode()
+
+    assert call(d=96, H=2)[0] == 2       # heads of 64 channels only
+    assert call(S=96, T=192)[0] == 2     # sequences of whole 64-token tiles
+    assert call(S=8192, T=8192)[0] == 2  # longest sequence 4096
+    assert call(T=100)[0] == 1           # T a multiple of S
+    assert call(sigma=0.0)[0] == 1
+    assert call(K=0)[0] == 1
+    assert L.dust_attn_v_workspace_bytes(4096, 2048, 512, 8, 64) > 4096 * 512 * 4
+
+
 def test_outer_and_noise_reject_bad_arguments():
     L = dust.lib()
     assert L.dust_outer_product(None, FAKE, 4, 4, 4, FAKE, None, 0, None) == 1

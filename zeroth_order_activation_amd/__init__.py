@@ -66,6 +66,12 @@ def lib():
         L.dust_estimate_head_subset.restype = ctypes.c_int
         L.dust_estimate_head_subset.argtypes = [_vp, ctypes.c_int, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32,
                                                 _u64, _u32, _u32, _u32, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.dust_attn_v_workspace_bytes.restype = ctypes.c_size_t
+        L.dust_attn_v_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _i64]
+        L.dust_estimate_attn_v.restype = ctypes.c_int
+        L.dust_estimate_attn_v.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32,
+                                           ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
+                                           _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.dust_linear_workspace_bytes.restype = ctypes.c_size_t
         L.dust_linear_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _i64]
         L.dust_estimate_linear.restype = ctypes.c_int
@@ -258,4 +264,26 @@ def estimate_linear(u, h, x_res, w2, w_head, labels, K: int, sigma: float, seed:
     _check(lib().dust_estimate_linear(_p(u), _p(h), _p(x_res), _p(w2), _p(w_head), _p(labels), T, d, n, V, K,
                                       sigma, ln_eps, seed, layer, token_offset, draw_offset, _p(grad_w), _p(ghat),
                                       _p(rewards), _p(ws), nb, _stream(u)))
+    return grad_w
+
+
+def attn_v_workspace_bytes(T: int, S: int, d: int, H: int, K: int) -> int:
+    return int(lib().dust_attn_v_workspace_bytes(T, S, d, H, K))
+
+
+def estimate_attn_v(q, k, e, u, S: int, H: int, K: int, sigma: float, seed: int, layer: int,
+                    token_offset: int = 0, draw_offset: int = 0, *, grad_w=None, ghat=None, rewards=None,
+                    workspace=None):
+    """Attention value-projection estimator (see dust_estimate_attn_v in dust.h).  Returns
+    grad_w [d,d].  q, k, e, u [T,d] fp32; sequences of S tokens; H heads of 64 channels."""
+    for t, nm in ((q, "q"), (k, "k"), (e, "e"), (u, "u")):
+        _dev_tensor(t, nm, (torch.float32,))
+    T, d = q.shape
+    if k.shape != (T, d) or e.shape != (T, d) or u.shape != (T, d):
+        raise ValueError("q, k, e and u must share the shape [T, d]")
+    if grad_w is None:
+        grad_w = torch.empty((d, d), dtype=torch.float32, device=q.device)
+    ws, nb = _workspace(lib().dust_attn_v_workspace_bytes(T, S, d, H, K), q.device, workspace)
+    _check(lib().dust_estimate_attn_v(_p(q), _p(k), _p(e), _p(u), T, S, d, H, K, sigma, seed, layer, token_offset,
+                                      draw_offset, _p(grad_w), _p(ghat), _p(rewards), _p(ws), nb, _stream(q)))
     return grad_w

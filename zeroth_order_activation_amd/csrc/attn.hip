@@ -1,0 +1,378 @@
+// Attention internals: the value-projection estimator.
+//
+// Method (TL;DR page "Dust: zeroth-order Transformer pretraining without
+// backprop", section 1, "credit assignment without backprop": attention
+// internals are rewarded by the change of the attention output instead of the
+// token's loss; news article, mechanism paragraph: that change is judged
+// against the error signal; iitog.ru page, mechanics paragraph: the error at
+// the attention output over the current and future tokens).  Reading: with
+// e_s the error at the attention output of token s and every token's value
+// v_t perturbed by sigma a_t in the same draw,
+//     r_t = -sum_{s >= t, same sequence} <e_s, o'_s - o_s>,
+//     g_hat_t = -(1/(K sigma)) sum_i r_t^(i) a_t^(i),   G_WV = sum_t g_hat_t u_t^T.
+// Only the values move, so o'_s - o_s = sigma sum_{t <= s} P_st a_t exactly,
+// P the clean causal attention probabilities, and per head
+//     c_s = <e_s, o'_s - o_s> = sigma sum_{t <= s} P_st <e_s, a_t>,
+// no difference of two outputs is formed (no cancellation).
+//
+// Kernels (heads of 64 channels, sequences of whole 64-token tiles):
+//   attn_lse_kernel   per (sequence, head, query tile): log-sum-exp of the
+//                     clean scaled logits of each query;
+//   attn_v_kernel     per (sequence, head, key tile): the key tile's noise for
+//                     a chunk of draws is generated once into LDS; for every
+//                     query tile at or after it the transposed logits
+//                     K Q^T / sqrt(64) are recomputed, P = exp(L - lse), and
+//                     per draw G^T = A E^T on MFMA, then per query the column
+//                     sum of P (.) G^T: the partial c of this key tile;
+//   attn_suffix_kernel per (draw, sequence): c_s = sum of the partials,
+//                     r_t = -sigma sum_{s >= t} c_s by a reverse block scan;
+//   attn_reduce_kernel per token: g_hat from the rewards, noise regenerated.
+// Products of two fp32 operands run on bf16 MFMA with both operands split into
+// pairs v = hi + lo and the three products lo.hi + hi.lo + hi.hi accumulated in
+// fp32 (each within about 3 2^-17 of fp32).
+#include "dust_device.hpp"
+#include "dust_internal.hpp"
+
+namespace dust {
+
+namespace {
+typedef __bf16 abf16x2_t __attribute__((ext_vector_type(2)));
+typedef float af32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 abf16x8_t __attribute__((ext_vector_type(8)));
+typedef float af32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int AT = 64;    // tokens per query / key tile
+constexpr int ADH = 64;   // channels per head
+constexpr int ANT = 256;  // lanes per workgroup: 4 waves of 32 keys x 32 queries
+constexpr int ADC = 8;    // draws whose key-tile noise sits in LDS at once
+constexpr float kAL2e = kLog2eF;
+
+__device__ __forceinline__ uint32_t pack2(float a, float b) {  // two floats -> bf16 pair (RNE), a low
+    const af32x2_t v = {a, b};
+    const abf16x2_t h = __builtin_convertvector(v, abf16x2_t);
+    uint32_t u;
+    __builtin_memcpy(&u, &h, 4);
+    return u;
+}
+
+// 8 consecutive fp32 values as bf16 hi and lo parts (x = hi + lo + O(2^-17 |x|)).
+__device__ __forceinline__ void split8(const float4& x0, const float4& x1, uint4& hi, uint4& lo) {
+    const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        h[p] = pack2(x[2 * p], x[2 * p + 1]);
+        l[p] = pack2(x[2 * p] - __uint_as_float(h[p] << 16), x[2 * p + 1] - __uint_as_float(h[p] & 0xFFFF0000u));
+    }
+    hi = make_uint4(h[0], h[1], h[2], h[3]);
+    lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+__device__ __forceinline__ af32x16_t mfma(const uint4& a, const uint4& b, const af32x16_t& c) {
+    abf16x8_t av, bv;
+    __builtin_memcpy(&av, &a, 16);
+    __builtin_memcpy(&bv, &b, 16);
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, c, 0, 0, 0);
+}
+
+// Fragments of one 32-row x 64-channel block of a row-major fp32 matrix: lane l
+// holds row (l & 31), channels 16 ks + 8 (l >> 5) + [0, 8) for ks = 0..3.
+__device__ __forceinline__ void load_frags(const float* __restrict__ M, int64_t ld, int64_t row, int ch0,
+                                           uint4 (&hi)[4], uint4 (&lo)[4]) {
+    const int lane = threadIdx.x & 63;
+    const float* p = M + row * ld + ch0 + 8 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const float4 a = *reinterpret_cast<const float4*>(p + 16 * ks);
+        const float4 b = *reinterpret_cast<const float4*>(p + 16 * ks + 4);
+        split8(a, b, hi[ks], lo[ks]);
+    }
+}
+
+// 32 x 32 block of A B^T over 64 channels from split fragments (three products).
+__device__ __forceinline__ af32x16_t prod_x3(const uint4 (&ahi)[4], const uint4 (&alo)[4], const uint4 (&bhi)[4],
+                                             const uint4 (&blo)[4]) {
+    af32x16_t acc = {};
+    af32x16_t acc2 = {};  // two chains, so no MFMA waits on the one just issued
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        acc = mfma(alo[ks], bhi[ks], acc);
+        acc2 = mfma(ahi[ks], blo[ks], acc2);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) acc = mfma(ahi[ks], bhi[ks], acc);
+    return acc + acc2;
+}
+
+// Row of the D layout (the A operand's row) held by register r of a lane.
+__device__ __forceinline__ int drow(int r, int lane) { return (r & 3) + 8 * (r >> 2) + 4 * (lane >> 5); }
+
+// LDS layout of a 64-key x 64-channel bf16 tile: row = key, 8 pieces of 8
+// channels, piece p of row r at p ^ ((r >> 1) & 7) (fragment reads of 16
+// consecutive rows touch all banks once).
+__device__ __forceinline__ int aswz(int row, int piece) { return row * 64 + ((piece ^ ((row >> 1) & 7)) << 3); }
+}  // namespace
+
+struct AttnKArgs {
+    const float* q;  // [T,d]
+    const float* k;  // [T,d]
+    const float* e;  // [T,d] error at the attention output
+    float* lse2;     // [T,H] log2-sum-exp2 of the clean scaled logits (log2 e / sqrt(dh) q.k)
+    float* cpart;    // [KC][nkt][H][2][T] partial c per (draw, key tile, head, key half, query)
+    int T, S, d, H;
+    uint32_t k0, k1, layer, tok0, draw0;
+};
+
+// ---- clean statistics -------------------------------------------------------
+__global__ void __launch_bounds__(ANT) attn_lse_kernel(AttnKArgs A) {
+    __shared__ float2 sh[2][AT];
+    const int nqt = A.S / AT;
+    const int qt = blockIdx.x % nqt, bh = blockIdx.x / nqt, b = bh / A.H, h = bh % A.H;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, kh = w >> 1, qh = w & 1;
+    const int64_t s0 = (int64_t)b * A.S;  // first token of the sequence
+    const float sl2 = kAL2e * 0.125f;     // log2 e / sqrt(64)
+    uint4 qhi[4], qlo[4];
+    load_frags(A.q, A.d, s0 + qt * AT + qh * 32 + (lane & 31), h * ADH, qhi, qlo);
+    const int query = qt * AT + qh * 32 + (lane & 31);
+    float m = -__builtin_inff(), s = 0.f;
+    for (int kt = 0; kt <= qt; ++kt) {
+        uint4 khi[4], klo[4];
+        load_frags(A.k, A.d, s0 + kt * AT + kh * 32 + (lane & 31), h * ADH, khi, klo);
+        const af32x16_t L = prod_x3(khi, klo, qhi, qlo);  // [key][query]
+        float x[16];
+        float mt = -__builtin_inff();
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = kt * AT + kh * 32 + drow(r, lane);
+            x[r] = key <= query ? L[r] * sl2 : -__builtin_inff();
+            mt = fmaxf(mt, x[r]);
+        }
+        const float mn = fmaxf(m, mt);
+        if (mn == -__builtin_inff()) continue;  // every key of this lane so far lies after its query
+        float st = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st += __builtin_amdgcn_exp2f(x[r] - mn);
+        s = (m == -__builtin_inff() ? 0.f : s * __builtin_amdgcn_exp2f(m - mn)) + st;
+        m = mn;
+    }
+    // merge the two lanes of a query (lane, lane ^ 32), then the two key halves
+    const float mo = __shfl_xor(m, 32, 64), so = __shfl_xor(s, 32, 64);
+    const float mm = fmaxf(m, mo);
+    const float ss = (m == -__builtin_inff() ? 0.f : s * __builtin_amdgcn_exp2f(m - mm)) +
+                     (mo == -__builtin_inff() ? 0.f : so * __builtin_amdgcn_exp2f(mo - mm));
+    if (lane < 32) sh[kh][qh * 32 + lane] = make_float2(mm, ss);
+    __syncthreads();
+    if (tid < AT) {
+        const float2 p0 = sh[0][tid], p1 = sh[1][tid];
+        const float M = fmaxf(p0.x, p1.x);
+        float S2 = 0.f;
+        if (p0.y > 0.f) S2 += p0.y * __builtin_amdgcn_exp2f(p0.x - M);
+        if (p1.y > 0.f) S2 += p1.y * __builtin_amdgcn_exp2f(p1.x - M);
+        A.lse2[(s0 + qt * AT + tid) * A.H + h] = M + __builtin_amdgcn_logf(S2);  // log2 of sum exp2
+    }
+}
+
+// ---- per-draw partial output changes ------------------------------------------
+__global__ void __launch_bounds__(ANT, 1) attn_v_kernel(AttnKArgs A, int i0, int kc) {
+    __shared__ __align__(16) uint16_t NH[ADC][AT * ADH];  // noise tile, bf16 hi parts
+    __shared__ __align__(16) uint16_t NL[ADC][AT * ADH];  // and lo parts
+    const int nqt = A.S / AT, nbh = (A.T / A.S) * A.H;
+    // key tiles with the most query tiles after them first
+    const int kt = blockIdx.x / nbh, bh = blockIdx.x % nbh, b = bh / A.H, h = bh % A.H;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, kh = w >> 1, qh = w & 1;
+    const int64_t s0 = (int64_t)b * A.S;
+    const int nkt = nqt;
+    const float sl2 = kAL2e * 0.125f;
+    uint4 khi[4], klo[4];  // this wave's 32 keys
+    load_frags(A.k, A.d, s0 + kt * AT + kh * 32 + (lane & 31), h * ADH, khi, klo);
+
+    for (int d0 = 0; d0 < kc; d0 += ADC) {
+        const int dn = min(ADC, kc - d0);
+        __syncthreads();  // the previous chunk's noise fully used
+        // noise of the 64 keys x 64 channels for dn draws: 1024 quads per draw
+        for (int dd = 0; dd < dn; ++dd) {
+            const uint32_t draw = A.draw0 + (uint32_t)(i0 + d0 + dd);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int qi = tid + j * ANT;
+                const int key = qi >> 4, cq = qi & 15;  // channel quad within the head
+                const uint32_t tok = A.tok0 + (uint32_t)(s0 + kt * AT + key);
+                const f32x4 g = gauss4(tok, (uint32_t)(h * (ADH / 4) + cq), draw, A.layer, A.k0, A.k1);
+                const uint32_t h0 = pack2(g.v[0], g.v[1]), h1 = pack2(g.v[2], g.v[3]);
+                const uint32_t l0 = pack2(g.v[0] - __uint_as_float(h0 << 16), g.v[1] - __uint_as_float(h0 & 0xFFFF0000u));
+                const uint32_t l1 = pack2(g.v[2] - __uint_as_float(h1 << 16), g.v[3] - __uint_as_float(h1 & 0xFFFF0000u));
+                const int off = aswz(key, cq >> 1) + 4 * (cq & 1);
+                *reinterpret_cast<uint2*>(&NH[dd][off]) = make_uint2(h0, h1);
+                *reinterpret_cast<uint2*>(&NL[dd][off]) = make_uint2(l0, l1);
+            }
+        }
+        __syncthreads();
+        for (int qt = kt; qt < nqt; ++qt) {
+            const int64_t qrow = s0 + qt * AT + qh * 32 + (lane & 31);
+            const int query = qt * AT + qh * 32 + (lane & 31);
+            uint4 qhi[4], qlo[4], ehi[4], elo[4];
+            load_frags(A.q, A.d, qrow, h * ADH, qhi, qlo);
+            load_frags(A.e, A.d, qrow, h * ADH, ehi, elo);
+            const float l2q = A.lse2[qrow * A.H + h];
+            const af32x16_t L = prod_x3(khi, klo, qhi, qlo);  // [key][query]
+            float P[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = kt * AT + kh * 32 + drow(r, lane);
+                P[r] = key <= query ? __builtin_amdgcn_exp2f(fmaf(L[r], sl2, -l2q)) : 0.f;
+            }
+            for (int dd = 0; dd < dn; ++dd) {
+                uint4 ahi[4], alo[4];
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    const int off = aswz(kh * 32 + (lane & 31), 2 * ks + (lane >> 5));
+                    ahi[ks] = *reinterpret_cast<const uint4*>(&NH[dd][off]);
+                    alo[ks] = *reinterpret_cast<const uint4*>(&NL[dd][off]);
+                }
+                const af32x16_t G = prod_x3(ahi, alo, ehi, elo);  // [key][query]: <a_key, e_query>
+                float c = 0.f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) c = fmaf(P[r], G[r], c);
+                c += __shfl_xor(c, 32, 64);
+                if (lane < 32)
+                    A.cpart[((((int64_t)(d0 + dd) * nkt + kt) * A.H + h) * 2 + kh) * A.T + s0 + qt * AT + qh * 32 +
+                            lane] = c;
+            }
+        }
+    }
+}
+
+// ---- rewards: c_s from the partials, r_t = -sigma sum_{s >= t} c_s -----------
+constexpr int ASMAX = 4096;  // longest sequence
+__global__ void __launch_bounds__(256) attn_suffix_kernel(const float* __restrict__ cpart, int T, int S, int H,
+                                                          int i0, float sigma, float* __restrict__ rew) {
+    __shared__ float cs[ASMAX];
+    __shared__ float sh[256];
+    const int nkt = S / AT, nb = T / S;
+    const int dd = blockIdx.x / nb, b = blockIdx.x % nb, tid = threadIdx.x;
+    const int per = (S + 255) / 256;  // consecutive tokens per lane
+    const int64_t s0 = (int64_t)b * S;
+    for (int s = tid; s < S; s += 256) {
+        float c = 0.f;
+        for (int kt = 0; kt <= s / AT; ++kt)
+            for (int h = 0; h < H; ++h) {
+                const float* pp = cpart + (((int64_t)dd * nkt + kt) * H + h) * 2 * T + s0 + s;
+                c += pp[0] + pp[T];
+            }
+        cs[s] = c;
+    }
+    __syncthreads();
+    float tot = 0.f;  // suffix sums within this lane's tokens, in place
+    for (int j = per - 1; j >= 0; --j) {
+        const int s = tid * per + j;
+        if (s < S) {
+            tot += cs[s];
+            cs[s] = tot;
+        }
+    }
+    sh[tid] = tot;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {  // inclusive suffix scan of the lane totals
+        const float v = tid + off < 256 ? sh[tid + off] : 0.f;
+        __syncthreads();
+        sh[tid] += v;
+        __syncthreads();
+    }
+    const float after = tid + 1 < 256 ? sh[tid + 1] : 0.f;
+    for (int j = 0; j < per; ++j) {
+        const int s = tid * per + j;
+        if (s < S) rew[(int64_t)(i0 + dd) * T + s0 + s] = -sigma * (cs[s] + after);
+    }
+}
+
+// ---- g_hat_t = -(1/(K sigma)) sum_i r_t^(i) a_t^(i) ------------------------------
+__global__ void __launch_bounds__(128) attn_reduce_kernel(AttnKArgs A, int K, const float* __restrict__ rew,
+                                                          float gscale, float* __restrict__ ghat) {
+    const int t = blockIdx.x;
+    const int nqd = A.d / 4;
+    const uint32_t tok = A.tok0 + (uint32_t)t;
+    for (int qd = threadIdx.x; qd < nqd; qd += 128) {
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < K; ++i) {
+            const float r = rew[(int64_t)i * A.T + t];
+            const f32x4 g = gauss4(tok, (uint32_t)qd, A.draw0 + (uint32_t)i, A.layer, A.k0, A.k1);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[c] = fmaf(r, g.v[c], acc[c]);
+        }
+        *reinterpret_cast<float4*>(ghat + (int64_t)t * A.d + 4 * qd) =
+            make_float4(acc[0] * gscale, acc[1] * gscale, acc[2] * gscale, acc[3] * gscale);
+    }
+}
+
+// Draws per pass of the partial buffer (kept to about 256 MB).
+static int attn_kc(int64_t T, int64_t S, int64_t H, int64_t K) {
+    const int64_t per_draw = (S / AT) * H * 2 * T * 4;
+    int64_t kc = ((int64_t)256 << 20) / (per_draw > 0 ? per_draw : 1);
+    kc = kc < 1 ? 1 : kc > 64 ? 64 : kc;
+    return (int)(K < kc ? K : kc);
+}
+
+static size_t al256(size_t x) { return (x + 255) / 256 * 256; }
+
+AttnVLayout attn_v_layout(int64_t T, int64_t S, int64_t d, int64_t H, int64_t K) {
+    AttnVLayout L{};
+    const int64_t nkt = S / AT;
+    size_t off = 0;
+    L.off_lse = off;   off += al256((size_t)T * H * 4);
+    L.off_cpart = off; off += al256((size_t)attn_kc(T, S, H, K) * nkt * H * 2 * T * 4);
+    L.off_rew = off;   off += al256((size_t)K * T * 4);
+    L.off_ghat = off;  off += al256((size_t)T * d * 4);
+    L.off_outer = off; off += outer_workspace_bytes(T, d, d);
+    L.total = off;
+    return L;
+}
+
+static AttnKArgs attn_args(const float* q, const float* k, const float* e, int64_t T, int64_t S, int64_t d,
+                           int64_t H, uint64_t seed, uint32_t layer, uint32_t token_offset, uint32_t draw_offset,
+                           unsigned char* ws, const AttnVLayout& L) {
+    AttnKArgs A{};
+    A.q = q; A.k = k; A.e = e;
+    A.lse2 = reinterpret_cast<float*>(ws + L.off_lse);
+    A.cpart = reinterpret_cast<float*>(ws + L.off_cpart);
+    A.T = (int)T; A.S = (int)S; A.d = (int)d; A.H = (int)H;
+    A.k0 = (uint32_t)seed; A.k1 = (uint32_t)(seed >> 32);
+    A.layer = layer; A.tok0 = token_offset; A.draw0 = draw_offset;
+    return A;
+}
+
+hipError_t launch_attn_v_rewards(const float* q, const float* k, const float* e, int64_t T, int64_t S, int64_t d,
+                                 int64_t H, int64_t K, float sigma, uint64_t seed, uint32_t layer,
+                                 uint32_t token_offset, uint32_t draw_offset, float* rew, unsigned char* ws,
+                                 const AttnVLayout& L, hipStream_t stream) {
+    const int64_t nkt = S / AT, nb = T / S;
+    const int kcmax = attn_kc(T, S, H, K);
+    const AttnKArgs A = attn_args(q, k, e, T, S, d, H, seed, layer, token_offset, draw_offset, ws, L);
+    hipLaunchKernelGGL(attn_lse_kernel, dim3((unsigned)(nb * H * nkt)), dim3(ANT), 0, stream, A);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    for (int64_t i0 = 0; i0 < K; i0 += kcmax) {
+        const int kc = (int)(K - i0 < kcmax ? K - i0 : kcmax);
+        AttnKArgs Ai = A;
+        Ai.draw0 = draw_offset + (uint32_t)i0;
+        hipLaunchKernelGGL(attn_v_kernel, dim3((unsigned)(nb * H * nkt)), dim3(ANT), 0, stream, Ai, 0, kc);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        hipLaunchKernelGGL(attn_suffix_kernel, dim3((unsigned)(kc * nb)), dim3(256), 0, stream, A.cpart, (int)T,
+                           (int)S, (int)H, (int)i0, sigma, rew);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_attn_v_ghat(int64_t T, int64_t d, int64_t K, float sigma, uint64_t seed, uint32_t layer,
+                              uint32_t token_offset, uint32_t draw_offset, const float* rew, float* ghat,
+                              hipStream_t stream) {
+    AttnKArgs A{};
+    A.T = (int)T; A.d = (int)d;
+    A.k0 = (uint32_t)seed; A.k1 = (uint32_t)(seed >> 32);
+    A.layer = layer; A.tok0 = token_offset; A.draw0 = draw_offset;
+    hipLaunchKernelGGL(attn_reduce_kernel, dim3((unsigned)T), dim3(128), 0, stream, A, (int)K, rew,
+                       -1.0f / ((float)K * sigma), ghat);
+    return hipGetLastError();
+}
+
+}  // namespace dust
