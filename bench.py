@@ -78,6 +78,7 @@ KERNEL_SOURCES = {
     "head_estimate_kernel": ["head_impl.hpp", "head_f32.hip", "head_bf16.hip", "head.hip", "dust_device.hpp"],
     "mlp_gemm2_kernel": ["mlp.hip", "dust_device.hpp", "dust_internal.hpp"],
     "head_subset_kernel": ["head_subset.hip", "dust_device.hpp", "dust_internal.hpp"],
+    "attn_v_kernel": ["attn.hip", "dust_device.hpp", "dust_internal.hpp"],
 }
 
 
@@ -126,7 +127,7 @@ def write_traffic(args):
     same two counters on a plain copy of --copy-calibration MiB) into the traffic
     file of the workload's dominant kernel."""
     kernel = ("head_subset_kernel" if args.subset else "head_estimate_kernel") if args.workload in (1, 2, 4) \
-        else "mlp_gemm2_kernel"
+        else "attn_v_kernel" if args.workload == 6 else "mlp_gemm2_kernel"
     copy_bytes = args.copy_calibration << 20
     if copy_bytes <= 0:
         sys.exit("--traffic-from needs --copy-calibration MIB (the size the copy runs used)")
@@ -170,6 +171,8 @@ WORKLOAD_NAMES = {
        "V=8192, K=64, sigma=1e-2, Zipf(1.1) labels",
     4: "243M-shape LM head bf16 logits: T=8192 (4x2048), d=1024, V=50304, K=16, sigma=5e-3, Zipf(1.1) labels",
     5: "MLP-linear population sweep point: T=2048, d=512, n=2048, V=8192, sigma=1e-2, K={K}",
+    6: "attention value-projection (W_V) estimator, causal: T=4096 (2x2048), d=512, 8 heads of 64, K=64, "
+       "sigma=1e-2",
 }
 
 
@@ -357,6 +360,82 @@ def analytic_alignment(c, gw, K, torch):
             "reference": "fp64 autograd gradient of sum_t CE_t w.r.t. W1 (unrounded downstream)"}
 
 
+def cpu_baseline_attn(case, target_s):
+    """The oracle on all tokens of the workload and its first draws (the work is linear in K)."""
+    import oracle
+
+    K = case["K"]
+    kd = 1
+    while True:
+        t0 = time.perf_counter()
+        oracle.attn_v_estimate(case["q"], case["k"], case["v"], case["e"], case["S"], case["H"], kd, case["sigma"],
+                               case["seed_noise"], case["layer"])
+        el = time.perf_counter() - t0
+        if el >= target_s / 3 or kd >= K:
+            break
+        kd = min(K, int(kd * max(2.0, target_s / max(el, 1e-3))))
+    return {"value": case["T"] * kd / el, "unit": "token-draws/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"all {case['T']} tokens x the first {kd} of {K} draws (two causal attentions per draw, "
+                      f"numpy fp64; rate extrapolated: work is linear in K), {el:.1f} s"}
+
+
+def run_attn(args, c, dust, torch):
+    """Attention value-projection estimator: rewards (attention passes), g_hat, outer product."""
+    T, S, d, H, K, sigma = c["T"], c["S"], c["d"], c["H"], c["K"], c["sigma"]
+    q, k, e, u = (torch.from_numpy(c[n]).cuda() for n in ("q", "k", "e", "u"))
+    gw = torch.empty((d, d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(dust.attn_v_workspace_bytes(T, S, d, H, K), dtype=torch.uint8, device="cuda")
+
+    def step():
+        dust.estimate_attn_v(q, k, e, u, S, H, K, sigma, c["seed_noise"], c["layer"], grad_w=gw, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # stages: 2 after the rewards, 0 after g_hat, 1 after G_WV
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for el in ev:
+        for x in el:
+            x.record(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for kk in range(args.steps):
+        ev[kk][0].record(stream)
+        dust.set_stage_event(2, ev[kk][1])
+        dust.set_stage_event(0, ev[kk][2])
+        dust.set_stage_event(1, ev[kk][3])
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for st in (0, 1, 2):
+        dust.set_stage_event(st, None)
+    att_ms = float(np.mean([dust.event_elapsed_ms(x[0], x[1]) for x in ev]))
+    red_ms = float(np.mean([dust.event_elapsed_ms(x[1], x[2]) for x in ev]))
+    out_ms = float(np.mean([dust.event_elapsed_ms(x[2], x[3]) for x in ev]))
+    ms_per_step = wall * 1e3 / args.steps
+    # bf16 MFMA work of the attention passes: per (key tile <= query tile) pair of 64-token
+    # tiles and head, 2 * 64^3 flops per product, three products (hi/lo pairs) for the logits
+    # once per chunk of 8 draws and for <e_s, a_t> once per draw, plus the clean statistics pass
+    nkt = S // 64
+    pairs = (T // S) * H * nkt * (nkt + 1) // 2
+    per_pair = 2 * 64 ** 3 * 3
+    kc = max(1, min(64, (256 << 20) // (nkt * H * 2 * T * 4)))
+    chunks = sum(-(-min(kc, K - i0) // 8) for i0 in range(0, K, kc))
+    flops = pairs * per_pair * (K + chunks + 1)
+    achieved = flops / (att_ms / 1e3) / 1e12
+    out = {
+        "dtype": "f32 (bf16x3 MFMA products)",
+        "stages_ms": {"attention_rewards": att_ms, "ghat_reduce": red_ms, "outer_product": out_ms},
+        "roofline": {"bound": "mfma", "kernel": "attn_v_kernel", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": load_traffic("attn_v_kernel", args.workload),
+                     "flops_per_launch": flops, "kernel_ms": att_ms,
+                     "note": "issued bf16 MFMA flops of the attention passes (three products per fp32 product)"},
+    }
+    return ms_per_step, out
+
+
 def run_linear(args, c, K, dust, torch):
     T, d, n, V, sigma = c["T"], c["d"], c["n"], c["V"], c["sigma"]
     u, h, xr = (torch.from_numpy(c[k]).cuda() for k in ("u", "h", "x_res"))
@@ -447,6 +526,10 @@ def main():
         if args.subset:
             cfg["workload"] = name + f"; vocabulary subset: window of {args.subset} channels per draw + label"
             cfg["subset_m"] = args.subset
+    elif c["kind"] == "attn_v":
+        K = c["K"]
+        ms, extra = run_attn(args, c, dust, torch)
+        cfg = {"workload": name, "T": c["T"], "S": c["S"], "d": c["d"], "H": c["H"], "K": K, "sigma": c["sigma"]}
     else:
         K = c["K"] if isinstance(c["K"], int) else args.draws
         name = name.format(K=K)
@@ -471,6 +554,7 @@ def main():
     out.update(extra)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = (cpu_baseline_head(c, args.cpu_seconds, args.subset) if c["kind"] == "head"
+                               else cpu_baseline_attn(c, args.cpu_seconds) if c["kind"] == "attn_v"
                                else cpu_baseline_linear(c, K, args.cpu_seconds))
     print(json.dumps(out), flush=True)
 

@@ -43,7 +43,8 @@ typedef float af32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int AT = 64;    // tokens per query / key tile
 constexpr int ADH = 64;   // channels per head
-constexpr int ANT = 256;  // lanes per workgroup: 4 waves of 32 keys x 32 queries
+constexpr int ANT = 256;  // lanes of the statistics pass: 4 waves of 32 keys x 32 queries
+constexpr int VNT = 512;  // lanes of the main pass: two groups of 4 waves on alternate query tiles
 constexpr int ADC = 8;    // draws whose key-tile noise sits in LDS at once
 constexpr float kAL2e = kLog2eF;
 
@@ -173,13 +174,13 @@ __global__ void __launch_bounds__(ANT) attn_lse_kernel(AttnKArgs A) {
 }
 
 // ---- per-draw partial output changes ------------------------------------------
-__global__ void __launch_bounds__(ANT, 1) attn_v_kernel(AttnKArgs A, int i0, int kc) {
+__global__ void __launch_bounds__(VNT, 1) attn_v_kernel(AttnKArgs A, int i0, int kc) {
     __shared__ __align__(16) uint16_t NH[ADC][AT * ADH];  // noise tile, bf16 hi parts
     __shared__ __align__(16) uint16_t NL[ADC][AT * ADH];  // and lo parts
     const int nqt = A.S / AT, nbh = (A.T / A.S) * A.H;
     // key tiles with the most query tiles after them first
     const int kt = blockIdx.x / nbh, bh = blockIdx.x % nbh, b = bh / A.H, h = bh % A.H;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, kh = w >> 1, qh = w & 1;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, kh = (w >> 1) & 1, qh = w & 1, grp = w >> 2;
     const int64_t s0 = (int64_t)b * A.S;
     const int nkt = nqt;
     const float sl2 = kAL2e * 0.125f;
@@ -193,8 +194,8 @@ __global__ void __launch_bounds__(ANT, 1) attn_v_kernel(AttnKArgs A, int i0, int
         for (int dd = 0; dd < dn; ++dd) {
             const uint32_t draw = A.draw0 + (uint32_t)(i0 + d0 + dd);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int qi = tid + j * ANT;
+            for (int j = 0; j < 2; ++j) {
+                const int qi = tid + j * VNT;
                 const int key = qi >> 4, cq = qi & 15;  // channel quad within the head
                 const uint32_t tok = A.tok0 + (uint32_t)(s0 + kt * AT + key);
                 const f32x4 g = gauss4(tok, (uint32_t)(h * (ADH / 4) + cq), draw, A.layer, A.k0, A.k1);
@@ -207,7 +208,9 @@ __global__ void __launch_bounds__(ANT, 1) attn_v_kernel(AttnKArgs A, int i0, int
             }
         }
         __syncthreads();
-        for (int qt = kt; qt < nqt; ++qt) {
+        // query tiles kt + grp, kt + grp + 2, ...: the two wave groups share the
+        // noise tile and run without barriers
+        for (int qt = kt + grp; qt < nqt; qt += 2) {
             const int64_t qrow = s0 + qt * AT + qh * 32 + (lane & 31);
             const int query = qt * AT + qh * 32 + (lane & 31);
             uint4 qhi[4], qlo[4], ehi[4], elo[4];
@@ -221,22 +224,40 @@ __global__ void __launch_bounds__(ANT, 1) attn_v_kernel(AttnKArgs A, int i0, int
                 const int key = kt * AT + kh * 32 + drow(r, lane);
                 P[r] = key <= query ? __builtin_amdgcn_exp2f(fmaf(L[r], sl2, -l2q)) : 0.f;
             }
-            for (int dd = 0; dd < dn; ++dd) {
-                uint4 ahi[4], alo[4];
+            float cacc[ADC];
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const int off = aswz(kh * 32 + (lane & 31), 2 * ks + (lane >> 5));
-                    ahi[ks] = *reinterpret_cast<const uint4*>(&NH[dd][off]);
-                    alo[ks] = *reinterpret_cast<const uint4*>(&NL[dd][off]);
+            for (int dd = 0; dd < ADC; ++dd) {
+                if (dd < dn) {
+                    uint4 ahi[4], alo[4];
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) {
+                        const int off = aswz(kh * 32 + (lane & 31), 2 * ks + (lane >> 5));
+                        ahi[ks] = *reinterpret_cast<const uint4*>(&NH[dd][off]);
+                        alo[ks] = *reinterpret_cast<const uint4*>(&NL[dd][off]);
+                    }
+                    af32x16_t g = {};  // [key][query]: <a_key, e_query>, one accumulator chain
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) g = mfma(alo[ks], ehi[ks], g);
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) g = mfma(ahi[ks], elo[ks], g);
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) g = mfma(ahi[ks], ehi[ks], g);
+                    float c = 0.f;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) c = fmaf(P[r], g[r], c);
+                    cacc[dd] = c;
                 }
-                const af32x16_t G = prod_x3(ahi, alo, ehi, elo);  // [key][query]: <a_key, e_query>
-                float c = 0.f;
+            }
+            // the two lanes of a query (lane, lane ^ 32) hold the two halves of its 32 keys
 #pragma unroll
-                for (int r = 0; r < 16; ++r) c = fmaf(P[r], G[r], c);
-                c += __shfl_xor(c, 32, 64);
-                if (lane < 32)
-                    A.cpart[((((int64_t)(d0 + dd) * nkt + kt) * A.H + h) * 2 + kh) * A.T + s0 + qt * AT + qh * 32 +
-                            lane] = c;
+            for (int dd = 0; dd < ADC; ++dd)
+                if (dd < dn) cacc[dd] += __shfl_xor(cacc[dd], 32, 64);
+            if (lane < 32) {
+#pragma unroll
+                for (int dd = 0; dd < ADC; ++dd)
+                    if (dd < dn)
+                        A.cpart[((((int64_t)(d0 + dd) * nkt + kt) * A.H + h) * 2 + kh) * A.T + s0 + qt * AT +
+                                qh * 32 + lane] = cacc[dd];
             }
         }
     }
@@ -354,7 +375,7 @@ hipError_t launch_attn_v_rewards(const float* q, const float* k, const float* e,
         const int kc = (int)(K - i0 < kcmax ? K - i0 : kcmax);
         AttnKArgs Ai = A;
         Ai.draw0 = draw_offset + (uint32_t)i0;
-        hipLaunchKernelGGL(attn_v_kernel, dim3((unsigned)(nb * H * nkt)), dim3(ANT), 0, stream, Ai, 0, kc);
+        hipLaunchKernelGGL(attn_v_kernel, dim3((unsigned)(nb * H * nkt)), dim3(VNT), 0, stream, Ai, 0, kc);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         hipLaunchKernelGGL(attn_suffix_kernel, dim3((unsigned)(kc * nb)), dim3(256), 0, stream, A.cpart, (int)T,
                            (int)S, (int)H, (int)i0, sigma, rew);
