@@ -371,36 +371,58 @@ def causal_attention(q, k, v, S: int, H: int) -> np.ndarray:
     return o
 
 
-def attn_v_estimate(q, k, v, e, S: int, H: int, K: int, sigma: float, seed: int, layer: int,
-                    token_offset: int = 0, draw_offset: int = 0):
-    """Value-projection estimator: per draw i, v' = v + sigma a^(i) on every
-    token, o' the recomputed attention output, c_s = <e_s, o'_s - o_s>,
-    r_t = -sum_{s >= t in t's sequence} c_s, and
-    g_hat_t = -(1/(K sigma)) sum_i r_t^(i) a_t^(i).  Returns (g_hat [T,d],
-    rewards [K,T])."""
+def _perturbed(proj: str, q, k, v, pert):
+    return (q + pert, k, v) if proj == "q" else (q, k + pert, v) if proj == "k" else (q, k, v + pert)
+
+
+def _check_proj(proj: str):
+    if proj not in ("q", "k", "v"):
+        raise ValueError("proj must be 'q', 'k' or 'v'")
+
+
+def attn_estimate(proj: str, q, k, v, e, S: int, H: int, K: int, sigma: float, seed: int, layer: int,
+                  token_offset: int = 0, draw_offset: int = 0):
+    """Estimator of the attention projection ``proj`` ('q', 'k' or 'v'): per draw i
+    its output y' = y + sigma a^(i) on every token, o' the recomputed attention
+    output, c_s = <e_s, o'_s - o_s>, and the reward of token t the change over the
+    outputs its perturbation can move: r_t = -sum_{s >= t in t's sequence} c_s for
+    keys and values, r_t = -c_t for queries (o_s depends on q_t only for s = t).
+    g_hat_t = -(1/(K sigma)) sum_i r_t^(i) a_t^(i).  Returns (g_hat [T,d], rewards [K,T])."""
+    _check_proj(proj)
     q = np.asarray(q, np.float64)
-    T, d = q.shape
-    e = np.asarray(e, np.float64)
+    k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
+    e = np.asarray(e, np.float64)
+    T, d = q.shape
     o = causal_attention(q, k, v, S, H)
     ghat = np.zeros((T, d))
     rew = np.zeros((K, T))
     for i in range(K):
         a = noise_block(seed, layer, draw_offset + i, 1, token_offset, T, d)[0]
-        c = np.sum(e * (causal_attention(q, k, v + sigma * a, S, H) - o), axis=1)
-        for b in range(T // S):
-            cs = c[b * S:(b + 1) * S]
-            rew[i, b * S:(b + 1) * S] = -np.cumsum(cs[::-1])[::-1]
+        c = np.sum(e * (causal_attention(*_perturbed(proj, q, k, v, sigma * a), S, H) - o), axis=1)
+        if proj == "q":
+            rew[i] = -c
+        else:
+            for b in range(T // S):
+                cs = c[b * S:(b + 1) * S]
+                rew[i, b * S:(b + 1) * S] = -np.cumsum(cs[::-1])[::-1]
         ghat -= rew[i][:, None] * a
     return ghat / (K * sigma), rew
 
 
-def attn_v_estimate_tokens(q, k, v, e, S: int, H: int, K: int, sigma: float, seed: int, layer: int,
-                           tokens, token_offset: int = 0, draw_offset: int = 0):
-    """The same estimator on the tokens ``tokens`` only: the attention outputs of
-    the queries s >= t of their sequences are recomputed row by row (for
-    sampled checks of large inputs).  Returns (g_hat [len(tokens), d],
-    rewards [K, len(tokens)])."""
+def attn_v_estimate(q, k, v, e, S: int, H: int, K: int, sigma: float, seed: int, layer: int,
+                    token_offset: int = 0, draw_offset: int = 0):
+    """The value-projection estimator (attn_estimate with proj = 'v')."""
+    return attn_estimate("v", q, k, v, e, S, H, K, sigma, seed, layer, token_offset, draw_offset)
+
+
+def attn_estimate_tokens(proj: str, q, k, v, e, S: int, H: int, K: int, sigma: float, seed: int, layer: int,
+                         tokens, token_offset: int = 0, draw_offset: int = 0):
+    """attn_estimate on the tokens ``tokens`` only: the attention outputs the rewards
+    of those tokens need (query s = t for queries, s >= t in the sequence otherwise)
+    are recomputed row by row (for sampled checks of large inputs).  Returns
+    (g_hat [len(tokens), d], rewards [K, len(tokens)])."""
+    _check_proj(proj)
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -408,34 +430,36 @@ def attn_v_estimate_tokens(q, k, v, e, S: int, H: int, K: int, sigma: float, see
     T, d = q.shape
     dh = d // H
     tokens = [int(t) for t in tokens]
-    need = sorted({s for t in tokens for s in range(t, (t // S + 1) * S)})
-    probs = {}  # query s -> [H, s - b S + 1] clean probabilities over its keys
-    for s in need:
+    span = (lambda t: [t]) if proj == "q" else (lambda t: list(range(t, (t // S + 1) * S)))
+    need = sorted({s for t in tokens for s in span(t)})
+
+    def row(s, qq, kk, vv):  # attention output of query s
         b0 = (s // S) * S
-        Ph = []
+        out = np.zeros(d)
         for h in range(H):
             ch = slice(h * dh, (h + 1) * dh)
-            L = k[b0:s + 1, ch] @ q[s, ch] / np.sqrt(dh)
+            L = kk[b0:s + 1, ch] @ qq[s, ch] / np.sqrt(dh)
             P = np.exp(L - L.max())
-            Ph.append(P / P.sum())
-        probs[s] = Ph
+            out[ch] = (P / P.sum()) @ vv[b0:s + 1, ch]
+        return out
+
+    o = {s: row(s, q, k, v) for s in need}
     ghat = np.zeros((len(tokens), d))
     rew = np.zeros((K, len(tokens)))
     for i in range(K):
         a = noise_block(seed, layer, draw_offset + i, 1, token_offset, T, d)[0]
-        c = {}
-        for s in need:
-            b0 = (s // S) * S
-            do = np.zeros(d)
-            for h in range(H):
-                ch = slice(h * dh, (h + 1) * dh)
-                vv = v[b0:s + 1, ch]
-                do[ch] = probs[s][h] @ (vv + sigma * a[b0:s + 1, ch]) - probs[s][h] @ vv
-            c[s] = float(e[s] @ do)
+        qq, kk, vv = _perturbed(proj, q, k, v, sigma * a)
+        c = {s: float(e[s] @ (row(s, qq, kk, vv) - o[s])) for s in need}
         for j, t in enumerate(tokens):
-            rew[i, j] = -sum(c[s] for s in range(t, (t // S + 1) * S))
+            rew[i, j] = -sum(c[s] for s in span(t))
             ghat[j] -= rew[i, j] * a[t]
     return ghat / (K * sigma), rew
+
+
+def attn_v_estimate_tokens(q, k, v, e, S: int, H: int, K: int, sigma: float, seed: int, layer: int,
+                           tokens, token_offset: int = 0, draw_offset: int = 0):
+    """The value-projection estimator on a token subset (attn_estimate_tokens, 'v')."""
+    return attn_estimate_tokens("v", q, k, v, e, S, H, K, sigma, seed, layer, tokens, token_offset, draw_offset)
 
 
 def attn_v_analytic(q, k, e, S: int, H: int) -> np.ndarray:

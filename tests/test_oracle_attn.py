@@ -1,14 +1,18 @@
-"""Pins of the oracle's attention value-projection estimator (TL;DR page, section 1,
+"""Pins of the oracle's attention projection estimators (TL;DR page, section 1,
 "credit assignment without backprop": attention internals rewarded by the change of the
 attention output; news article, mechanism paragraph: that change judged against the error
 signal; iitog.ru, mechanics paragraph: the error at the attention output over the current
-and future tokens).  Reading: r_t = -sum_{s >= t in t's sequence} <e_s, o'_s - o_s>.
+and future tokens).  Reading: r_t = -sum_{s >= t in t's sequence} <e_s, o'_s - o_s> for the
+key and value projections, r_t = -<e_t, o'_t - o_t> for the query projection.
 
 - the oracle's causal attention equals torch's scaled_dot_product_attention (fp64);
-- every reward equals the definition evaluated with torch's attention on v + sigma a;
+- every reward equals the definition evaluated with torch's attention on the perturbed
+  q, k or v;
 - the closed-form target P^T e equals torch autograd of sum_s <e_s, o_s> w.r.t. v;
-- one-token sequences reduce to r = -sigma <e_t, a_t> (no mixing across tokens);
-- unbiased: as K grows the estimate regresses on the analytic gradient with slope 1;
+- one-token sequences reduce to r = -sigma <e_t, a_t> for values and to r = 0 for queries
+  and keys (a lone key's softmax weight is 1 whatever it is);
+- unbiased: as K grows the estimate regresses on the analytic (autograd) gradient with
+  slope 1, for each projection;
 - draw additivity: two draw ranges combine to the estimate over their union.
 """
 import numpy as np
@@ -96,3 +100,46 @@ def test_draw_ranges_combine():
     g2, r2 = oracle.attn_v_estimate(q, k, v, e, S, H, 3, sigma, SEED, 2, draw_offset=7)
     np.testing.assert_allclose(r_all, np.concatenate([r1, r2]), rtol=0, atol=0)
     np.testing.assert_allclose(g_all, (4 * g1 + 3 * g2) / 7, rtol=1e-12, atol=1e-15)
+
+
+def test_query_and_key_rewards_are_the_output_change_against_the_error():
+    B, S, H, dh = 2, 5, 2, 4
+    q, k, v, e = _inputs(B, S, H, dh, 7)
+    K, sigma, t0, d0 = 3, 5e-2, 2, 9
+    a = oracle.noise_block(SEED, 4, d0, K, t0, B * S, H * dh)
+    o = _torch_attn(q, k, v, B, S, H).numpy()
+    for proj in ("q", "k"):
+        g, rew = oracle.attn_estimate(proj, q, k, v, e, S, H, K, sigma, SEED, 4, token_offset=t0, draw_offset=d0)
+        expect = np.zeros_like(rew)
+        for i in range(K):
+            qq, kk = (q + sigma * a[i], k) if proj == "q" else (q, k + sigma * a[i])
+            c = np.sum(e * (_torch_attn(qq, kk, v, B, S, H).numpy() - o), axis=1)
+            for t in range(B * S):
+                b = t // S
+                expect[i, t] = -c[t] if proj == "q" else -c[t:(b + 1) * S].sum()
+        np.testing.assert_allclose(rew, expect, rtol=1e-9, atol=1e-13)
+        np.testing.assert_allclose(g, -np.einsum("it,itd->td", rew, a) / (K * sigma), rtol=1e-12, atol=1e-14)
+
+
+def test_lone_queries_and_keys_move_nothing():
+    B, S, H, dh = 5, 1, 2, 4
+    q, k, v, e = _inputs(B, S, H, dh, 8)
+    for proj in ("q", "k"):
+        g, rew = oracle.attn_estimate(proj, q, k, v, e, S, H, 4, 0.1, SEED, 4)
+        assert np.all(rew == 0.0) and np.all(g == 0.0)
+
+
+def test_query_and_key_estimates_are_unbiased():
+    B, S, H, dh = 2, 4, 2, 2
+    q, k, v, e = _inputs(B, S, H, dh, 9)
+    K, sigma = 20000, 1e-3
+    for proj in ("q", "k"):
+        x = torch.tensor(q if proj == "q" else k, requires_grad=True)
+        loss = (torch.as_tensor(e) * (_torch_attn(x, k, v, B, S, H) if proj == "q"
+                                      else _torch_attn(q, x, v, B, S, H))).sum()
+        loss.backward()
+        ga = x.grad.numpy()
+        g, _ = oracle.attn_estimate(proj, q, k, v, e, S, H, K, sigma, SEED, 4)
+        slope = float((g * ga).sum() / (ga * ga).sum())
+        print(f"{proj}: slope on the autograd gradient {slope:.3f}, cosine {oracle.cosine(g, ga):.3f}")
+        assert abs(slope - 1.0) < 0.08
