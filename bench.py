@@ -79,6 +79,8 @@ KERNEL_SOURCES = {
     "mlp_gemm2_kernel": ["mlp.hip", "dust_device.hpp", "dust_internal.hpp"],
     "head_subset_kernel": ["head_subset.hip", "dust_device.hpp", "dust_internal.hpp"],
     "attn_v_kernel": ["attn.hip", "dust_device.hpp", "dust_internal.hpp"],
+    "attn_k_kernel": ["attn.hip", "dust_device.hpp", "dust_internal.hpp"],
+    "attn_q_kernel": ["attn.hip", "dust_device.hpp", "dust_internal.hpp"],
 }
 
 
@@ -127,7 +129,7 @@ def write_traffic(args):
     same two counters on a plain copy of --copy-calibration MiB) into the traffic
     file of the workload's dominant kernel."""
     kernel = ("head_subset_kernel" if args.subset else "head_estimate_kernel") if args.workload in (1, 2, 4) \
-        else "attn_v_kernel" if args.workload == 6 else "mlp_gemm2_kernel"
+        else f"attn_{args.attn_proj}_kernel" if args.workload == 6 else "mlp_gemm2_kernel"
     copy_bytes = args.copy_calibration << 20
     if copy_bytes <= 0:
         sys.exit("--traffic-from needs --copy-calibration MIB (the size the copy runs used)")
@@ -171,8 +173,7 @@ WORKLOAD_NAMES = {
        "V=8192, K=64, sigma=1e-2, Zipf(1.1) labels",
     4: "243M-shape LM head bf16 logits: T=8192 (4x2048), d=1024, V=50304, K=16, sigma=5e-3, Zipf(1.1) labels",
     5: "MLP-linear population sweep point: T=2048, d=512, n=2048, V=8192, sigma=1e-2, K={K}",
-    6: "attention value-projection (W_V) estimator, causal: T=4096 (2x2048), d=512, 8 heads of 64, K=64, "
-       "sigma=1e-2",
+    6: "attention {P} estimator, causal: T=4096 (2x2048), d=512, 8 heads of 64, K=64, sigma=1e-2",
 }
 
 
@@ -186,6 +187,8 @@ def parse():
     ap.add_argument("--subset", type=int, default=0, metavar="M",
                     help="LM-head workloads: perturb a window of M vocabulary channels per draw (plus the "
                          "label) with the subset estimator; M a multiple of 4")
+    ap.add_argument("--attn-proj", default="v", choices=("q", "k", "v"),
+                    help="workload 6: the attention projection whose output is perturbed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-alignment", action="store_true",
                     help="MLP-linear workloads: skip the cosine to the backprop gradient")
@@ -360,7 +363,7 @@ def analytic_alignment(c, gw, K, torch):
             "reference": "fp64 autograd gradient of sum_t CE_t w.r.t. W1 (unrounded downstream)"}
 
 
-def cpu_baseline_attn(case, target_s):
+def cpu_baseline_attn(case, target_s, proj):
     """The oracle on all tokens of the workload and its first draws (the work is linear in K)."""
     import oracle
 
@@ -368,8 +371,8 @@ def cpu_baseline_attn(case, target_s):
     kd = 1
     while True:
         t0 = time.perf_counter()
-        oracle.attn_v_estimate(case["q"], case["k"], case["v"], case["e"], case["S"], case["H"], kd, case["sigma"],
-                               case["seed_noise"], case["layer"])
+        oracle.attn_estimate(proj, case["q"], case["k"], case["v"], case["e"], case["S"], case["H"], kd,
+                             case["sigma"], case["seed_noise"], case["layer"])
         el = time.perf_counter() - t0
         if el >= target_s / 3 or kd >= K:
             break
@@ -380,14 +383,16 @@ def cpu_baseline_attn(case, target_s):
 
 
 def run_attn(args, c, dust, torch):
-    """Attention value-projection estimator: rewards (attention passes), g_hat, outer product."""
+    """Attention projection estimator: rewards (attention passes), g_hat, outer product."""
     T, S, d, H, K, sigma = c["T"], c["S"], c["d"], c["H"], c["K"], c["sigma"]
-    q, k, e, u = (torch.from_numpy(c[n]).cuda() for n in ("q", "k", "e", "u"))
+    proj = args.attn_proj
+    q, k, v, e, u = (torch.from_numpy(c[n]).cuda() for n in ("q", "k", "v", "e", "u"))
     gw = torch.empty((d, d), dtype=torch.float32, device="cuda")
-    ws = torch.empty(dust.attn_v_workspace_bytes(T, S, d, H, K), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(dust.attn_workspace_bytes(proj, T, S, d, H, K), dtype=torch.uint8, device="cuda")
 
     def step():
-        dust.estimate_attn_v(q, k, e, u, S, H, K, sigma, c["seed_noise"], c["layer"], grad_w=gw, workspace=ws)
+        dust.estimate_attn(proj, q, k, v, e, u, S, H, K, sigma, c["seed_noise"], c["layer"], grad_w=gw,
+                           workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -415,21 +420,25 @@ def run_attn(args, c, dust, torch):
     out_ms = float(np.mean([dust.event_elapsed_ms(x[2], x[3]) for x in ev]))
     ms_per_step = wall * 1e3 / args.steps
     # bf16 MFMA work of the attention passes: per (key tile <= query tile) pair of 64-token
-    # tiles and head, 2 * 64^3 flops per product, three products (hi/lo pairs) for the logits
-    # once per chunk of 8 draws and for <e_s, a_t> once per draw, plus the clean statistics pass
+    # tiles and head, 2 * 64^3 flops per product, three products (hi/lo pairs) each: per draw
+    # one product (<a, e> for values, <a, q> or <k, a> for keys and queries); per chunk of 8
+    # draws the logits (and for keys and queries <v, e>); the clean statistics pass once
+    # (and <v, e> there for keys and queries)
     nkt = S // 64
     pairs = (T // S) * H * nkt * (nkt + 1) // 2
     per_pair = 2 * 64 ** 3 * 3
-    kc = max(1, min(64, (256 << 20) // (nkt * H * 2 * T * 4)))
+    part = {"v": nkt * H * 2 * T, "k": nkt * H * 4 * T, "q": H * T}[proj] * 4
+    kc = max(1, min(64, (256 << 20) // part))
     chunks = sum(-(-min(kc, K - i0) // 8) for i0 in range(0, K, kc))
-    flops = pairs * per_pair * (K + chunks + 1)
+    per_chunk, stats = (1, 1) if proj == "v" else (2, 2)
+    flops = pairs * per_pair * (K + per_chunk * chunks + stats)
     achieved = flops / (att_ms / 1e3) / 1e12
     out = {
         "dtype": "f32 (bf16x3 MFMA products)",
         "stages_ms": {"attention_rewards": att_ms, "ghat_reduce": red_ms, "outer_product": out_ms},
-        "roofline": {"bound": "mfma", "kernel": "attn_v_kernel", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+        "roofline": {"bound": "mfma", "kernel": f"attn_{proj}_kernel", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": load_traffic("attn_v_kernel", args.workload),
+                     "traffic": load_traffic(f"attn_{proj}_kernel", args.workload),
                      "flops_per_launch": flops, "kernel_ms": att_ms,
                      "note": "issued bf16 MFMA flops of the attention passes (three products per fp32 product)"},
     }
@@ -528,8 +537,11 @@ def main():
             cfg["subset_m"] = args.subset
     elif c["kind"] == "attn_v":
         K = c["K"]
+        name = name.format(P={"q": "query-projection (W_Q)", "k": "key-projection (W_K)",
+                              "v": "value-projection (W_V)"}[args.attn_proj])
         ms, extra = run_attn(args, c, dust, torch)
-        cfg = {"workload": name, "T": c["T"], "S": c["S"], "d": c["d"], "H": c["H"], "K": K, "sigma": c["sigma"]}
+        cfg = {"workload": name, "T": c["T"], "S": c["S"], "d": c["d"], "H": c["H"], "K": K, "sigma": c["sigma"],
+               "projection": args.attn_proj}
     else:
         K = c["K"] if isinstance(c["K"], int) else args.draws
         name = name.format(K=K)
@@ -554,7 +566,7 @@ def main():
     out.update(extra)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = (cpu_baseline_head(c, args.cpu_seconds, args.subset) if c["kind"] == "head"
-                               else cpu_baseline_attn(c, args.cpu_seconds) if c["kind"] == "attn_v"
+                               else cpu_baseline_attn(c, args.cpu_seconds, args.attn_proj) if c["kind"] == "attn_v"
                                else cpu_baseline_linear(c, K, args.cpu_seconds))
     print(json.dumps(out), flush=True)
 

@@ -195,7 +195,7 @@ dust_status dust_estimate_linear(const float *u, const float *h, const float *x_
                                  void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Attention value projection (W_V): the attention-internal estimator.
+ * Attention internals: the estimators of the query, key and value projections.
  * Method: TL;DR page "Dust: zeroth-order Transformer pretraining without backprop",
  * section 1, "credit assignment without backprop" (attention internals are rewarded by
  * the change of the attention output, not the token's loss) and "reducing interference"
@@ -203,21 +203,37 @@ dust_status dust_estimate_linear(const float *u, const float *h, const float *x_
  * paragraph (that change is judged against the error signal); the iitog.ru page,
  * mechanics paragraph (the error at the attention output over current and future
  * tokens).  Reading: causal multi-head attention within sequences of S tokens (token
- * t = b S + s), every token's value v_t perturbed by sigma a_t^(i) in the same draw, e_s
- * the error (loss gradient) at the attention output o_s:
- *   r_t   = -sum_{s >= t, same sequence} <e_s, o'_s - o_s>
- *         = -sigma sum_{s >= t} sum_{t' <= s} P_{s t'} <e_s, a_t'>     (per head; exact:
- *           only the values move, so the probabilities P stay those of the clean pass)
- *   g_hat_t = -(1/(K sigma)) sum_i r_t a_t;   G_WV = sum_t g_hat_t u_t^T.
+ * t = b S + s); the chosen projection's output y_t (q_t, k_t or v_t) of every token
+ * perturbed by sigma a_t^(i) in the same draw; e_s the error (loss gradient) at the
+ * attention output o_s, before W_O:
+ *   c_s   = <e_s, o'_s - o_s>
+ *   r_t   = -sum_{s >= t, same sequence} c_s     (keys and values: the outputs they move)
+ *   r_t   = -c_t                                (queries: only o_t depends on q_t)
+ *   g_hat_t = -(1/(K sigma)) sum_i r_t a_t;   G_W = sum_t g_hat_t u_t^T.
+ * The output change is formed without subtracting two outputs: for values
+ * o'_s - o_s = sigma sum_t P_st a_t (P unchanged); for queries and keys, with delta_st
+ * the logit change (sigma <a_s, k_t> / sqrt(dh) or sigma <q_s, a_t> / sqrt(dh)),
+ * rho_s = sum_t P_st expm1(delta_st) and mu_s = sum_t P_st expm1(delta_st) <v_t, e_s>:
+ * c_s = (mu_s - rho_s <e_s, o_s>) / (1 + rho_s), per head.
+ *   proj   : DUST_ATTN_Q, DUST_ATTN_K or DUST_ATTN_V
  *   q, k   : float [T, d]  clean query and key projections (heads of 64 channels: d = 64 H)
+ *   v      : float [T, d]  clean value projection (queries and keys only; may be NULL for values)
  *   e      : float [T, d]  error at the attention output (per head, before W_O)
- *   u      : float [T, d]  input of W_V (the u_t of G_WV)
+ *   u      : float [T, d]  input of the projection (the u_t of G_W)
  *   grad_w : OUT float [d, d];  ghat : OUT float [T, d] or NULL;  rewards : OUT float [K, T] or NULL.
- * The values themselves are not needed.  Noise counter: (token, channel/4, draw, layer).
- * Supported: S a multiple of 64 up to 4096, T a multiple of S, d = 64 H.
- * Stages (dust_set_stage_event): 2 = after the rewards, 0 = after g_hat, 1 = after G_WV.
- * Workspace: dust_attn_v_workspace_bytes(T, S, d, H, K) bytes.
+ * Noise counter: (token, channel/4, draw, layer).  Supported: S a multiple of 64 up to
+ * 4096, T a multiple of S, d = 64 H.  Stages (dust_set_stage_event): 2 = after the
+ * rewards, 0 = after g_hat, 1 = after G_W.
+ * Workspace: dust_attn_workspace_bytes(proj, T, S, d, H, K) bytes.
+ * dust_estimate_attn_v is dust_estimate_attn with DUST_ATTN_V (no v argument).
  */
+typedef enum { DUST_ATTN_Q = 0, DUST_ATTN_K = 1, DUST_ATTN_V = 2 } dust_attn_proj;
+size_t dust_attn_workspace_bytes(int proj, int64_t T, int64_t S, int64_t d, int64_t H, int64_t K);
+dust_status dust_estimate_attn(int proj, const float *q, const float *k, const float *v, const float *e,
+                               const float *u, int64_t T, int64_t S, int64_t d, int64_t H, int64_t K,
+                               float sigma, uint64_t seed, uint32_t layer, uint32_t token_offset,
+                               uint32_t draw_offset, float *grad_w, float *ghat, float *rewards,
+                               void *workspace, size_t workspace_bytes, void *stream);
 size_t dust_attn_v_workspace_bytes(int64_t T, int64_t S, int64_t d, int64_t H, int64_t K);
 dust_status dust_estimate_attn_v(const float *q, const float *k, const float *e, const float *u,
                                  int64_t T, int64_t S, int64_t d, int64_t H, int64_t K, float sigma,

@@ -106,6 +106,19 @@ def test_attn_v_rejects_bad_arguments_on_host():
     assert call(sigma=0.0)[0] == 1
     assert call(K=0)[0] == 1
     assert L.dust_attn_v_workspace_bytes(4096, 2048, 512, 8, 64) > 4096 * 512 * 4
+    assert L.dust_attn_v_workspace_bytes(4096, 2048, 512, 8, 64) == L.dust_attn_workspace_bytes(2, 4096, 2048, 512,
+                                                                                                8, 64)
+
+    def gen(proj, v=FAKE):
+        st = L.dust_estimate_attn(proj, FAKE, FAKE, v, FAKE, FAKE, 128, 64, 128, 2, 3, ctypes.c_float(0.01), 1, 2, 0,
+                                  0, FAKE, None, None, FAKE, 1 << 30, None)
+        return st, L.dust_last_error().decode()
+
+    assert gen(3)[0] == 1 and gen(-1)[0] == 1       # no such projection
+    assert gen(0, None)[0] == 1 and gen(1, None)[0] == 1  # queries and keys need v
+    assert L.dust_attn_workspace_bytes(3, 128, 64, 128, 2, 3) == 0
+    assert L.dust_attn_workspace_bytes(1, 4096, 2048, 512, 8, 64) > L.dust_attn_workspace_bytes(2, 4096, 2048, 512,
+                                                                                                 8, 64)
 
 
 def test_outer_and_noise_reject_bad_arguments():

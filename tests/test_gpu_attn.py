@@ -1,4 +1,4 @@
-"""GPU parity of the attention value-projection estimator against its oracle.
+"""GPU parity of the attention projection estimators (values, keys, queries) against their oracle.
 
 Small cases element by element (one and several query tiles per sequence, several
 sequences and heads, more draws than one pass of the partial buffer holds), and the
@@ -68,4 +68,57 @@ def test_attn_v_full_workload_on_sampled_tokens():
     ref = ghat[:, rows].cpu().numpy().astype(np.float64).T @ c["u"].astype(np.float64)
     e_w = rel_l2(gw[rows].cpu().numpy(), ref)
     print(f"2x2048 tokens, 8 heads, K={K}: sampled rewards {e_r:.2e} ghat {e_g:.2e}; grad_w rows vs G^T U {e_w:.2e}")
+    assert e_r < TOL and e_g < TOL and e_w < 6e-5
+
+
+QK_CASES = [
+    # proj, B, S, H, K, sigma
+    ("k", 2, 64, 2, 5, 1e-2),
+    ("k", 1, 192, 1, 9, 3e-2),   # causal tiles below the diagonal; larger logit changes
+    ("k", 3, 128, 4, 3, 1e-2),
+    ("q", 2, 64, 2, 5, 1e-2),
+    ("q", 1, 192, 1, 9, 3e-2),
+    ("q", 3, 128, 4, 70, 1e-2),  # more draws than one pass of partials
+    ("k", 1, 64, 1, 70, 0.2),    # |delta| past the polynomial's range: exp - 1
+]
+
+
+@pytest.mark.parametrize("proj,B,S,H,K,sigma", QK_CASES)
+def test_attn_query_key_small_cases_elementwise(proj, B, S, H, K, sigma):
+    c = synth.attn_case(B, S, H, seed=43 + S + H)
+    seed, layer, tok0, draw0 = 0x4455535400000050 + S, 3, 7, 2
+    T, d = c["T"], c["d"]
+    ghat = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    rew = torch.empty((K, T), dtype=torch.float32, device="cuda")
+    gw = dust.estimate_attn(proj, dev(c["q"]), dev(c["k"]), dev(c["v"]), dev(c["e"]), dev(c["u"]), S, H, K, sigma,
+                            seed, layer, tok0, draw0, ghat=ghat, rewards=rew)
+    torch.cuda.synchronize()
+    og, orew = oracle.attn_estimate(proj, c["q"], c["k"], c["v"], c["e"], S, H, K, sigma, seed, layer, tok0, draw0)
+    e_g, e_r = rel_l2(ghat.cpu().numpy(), og), rel_l2(rew.cpu().numpy(), orew)
+    e_w = rel_l2(gw.cpu().numpy(), oracle.grad_w(og, c["u"]))
+    print(f"{proj}: B={B} S={S} H={H} K={K} sigma={sigma}: rewards {e_r:.2e} ghat {e_g:.2e} grad_w {e_w:.2e}")
+    assert e_r < TOL and e_g < TOL and e_w < 1e-3
+
+
+@pytest.mark.parametrize("proj", ["q", "k"])
+def test_attn_query_key_full_workload_on_sampled_tokens(proj):
+    c = synth.workload(6, matmul=gpu_matmul)
+    K, sigma, S, H = c["K"], c["sigma"], c["S"], c["H"]
+    T, d = c["T"], c["d"]
+    ghat = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    rew = torch.empty((K, T), dtype=torch.float32, device="cuda")
+    args = (dev(c["q"]), dev(c["k"]), dev(c["v"]), dev(c["e"]), dev(c["u"]), S, H, K, sigma, c["seed_noise"], 5)
+    gw = dust.estimate_attn(proj, *args, ghat=ghat, rewards=rew)
+    gw2 = dust.estimate_attn(proj, *args)
+    torch.cuda.synchronize()
+    assert torch.equal(gw, gw2)
+    toks = [3, 1000, S - 2, 2 * S - 1] if proj == "q" else [S - 4, 2 * S - 2]
+    og, orew = oracle.attn_estimate_tokens(proj, c["q"], c["k"], c["v"], c["e"], S, H, K, sigma, c["seed_noise"], 5,
+                                           toks)
+    e_g = rel_l2(ghat[toks].cpu().numpy(), og)
+    e_r = rel_l2(rew[:, toks].cpu().numpy(), orew)
+    rows = np.random.default_rng(27).choice(d, 64, replace=False)
+    ref = ghat[:, rows].cpu().numpy().astype(np.float64).T @ c["u"].astype(np.float64)
+    e_w = rel_l2(gw[rows].cpu().numpy(), ref)
+    print(f"{proj}, 2x2048 tokens, 8 heads, K={K}: sampled rewards {e_r:.2e} ghat {e_g:.2e}; grad_w rows {e_w:.2e}")
     assert e_r < TOL and e_g < TOL and e_w < 6e-5

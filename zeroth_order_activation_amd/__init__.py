@@ -66,6 +66,12 @@ def lib():
         L.dust_estimate_head_subset.restype = ctypes.c_int
         L.dust_estimate_head_subset.argtypes = [_vp, ctypes.c_int, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32,
                                                 _u64, _u32, _u32, _u32, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.dust_attn_workspace_bytes.restype = ctypes.c_size_t
+        L.dust_attn_workspace_bytes.argtypes = [ctypes.c_int, _i64, _i64, _i64, _i64, _i64]
+        L.dust_estimate_attn.restype = ctypes.c_int
+        L.dust_estimate_attn.argtypes = [ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32,
+                                         ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
+                                         _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.dust_attn_v_workspace_bytes.restype = ctypes.c_size_t
         L.dust_attn_v_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _i64]
         L.dust_estimate_attn_v.restype = ctypes.c_int
@@ -286,4 +292,32 @@ def estimate_attn_v(q, k, e, u, S: int, H: int, K: int, sigma: float, seed: int,
     ws, nb = _workspace(lib().dust_attn_v_workspace_bytes(T, S, d, H, K), q.device, workspace)
     _check(lib().dust_estimate_attn_v(_p(q), _p(k), _p(e), _p(u), T, S, d, H, K, sigma, seed, layer, token_offset,
                                       draw_offset, _p(grad_w), _p(ghat), _p(rewards), _p(ws), nb, _stream(q)))
+    return grad_w
+
+
+ATTN_PROJ = {"q": 0, "k": 1, "v": 2}
+
+
+def attn_workspace_bytes(proj: str, T: int, S: int, d: int, H: int, K: int) -> int:
+    return int(lib().dust_attn_workspace_bytes(ATTN_PROJ[proj], T, S, d, H, K))
+
+
+def estimate_attn(proj: str, q, k, v, e, u, S: int, H: int, K: int, sigma: float, seed: int, layer: int,
+                  token_offset: int = 0, draw_offset: int = 0, *, grad_w=None, ghat=None, rewards=None,
+                  workspace=None):
+    """Attention projection estimator ('q', 'k' or 'v'; see dust_estimate_attn in dust.h).
+    Returns grad_w [d,d].  q, k, v, e, u [T,d] fp32 (v may be None for 'v')."""
+    if proj not in ATTN_PROJ:
+        raise ValueError("proj must be 'q', 'k' or 'v'")
+    for t, nm in ((q, "q"), (k, "k"), (e, "e"), (u, "u")) + (((v, "v"),) if v is not None else ()):
+        _dev_tensor(t, nm, (torch.float32,))
+    T, d = q.shape
+    if any(x is not None and x.shape != (T, d) for x in (k, v, e, u)):
+        raise ValueError("q, k, v, e and u must share the shape [T, d]")
+    if grad_w is None:
+        grad_w = torch.empty((d, d), dtype=torch.float32, device=q.device)
+    ws, nb = _workspace(attn_workspace_bytes(proj, T, S, d, H, K), q.device, workspace)
+    _check(lib().dust_estimate_attn(ATTN_PROJ[proj], _p(q), _p(k), _p(v), _p(e), _p(u), T, S, d, H, K, sigma, seed,
+                                    layer, token_offset, draw_offset, _p(grad_w), _p(ghat), _p(rewards), _p(ws), nb,
+                                    _stream(q)))
     return grad_w

@@ -46,6 +46,7 @@ constexpr int ADH = 64;   // channels per head
 constexpr int ANT = 256;  // lanes of the statistics pass: 4 waves of 32 keys x 32 queries
 constexpr int VNT = 512;  // lanes of the main pass: two groups of 4 waves on alternate query tiles
 constexpr int ADC = 8;    // draws whose key-tile noise sits in LDS at once
+constexpr int ASMAX = 4096;  // longest sequence
 constexpr float kAL2e = kLog2eF;
 
 __device__ __forceinline__ uint32_t pack2(float a, float b) {  // two floats -> bf16 pair (RNE), a low
@@ -117,29 +118,50 @@ __device__ __forceinline__ int aswz(int row, int piece) { return row * 64 + ((pi
 struct AttnKArgs {
     const float* q;  // [T,d]
     const float* k;  // [T,d]
+    const float* v;  // [T,d] (query and key projections only)
     const float* e;  // [T,d] error at the attention output
+    float* ob;       // [T,H] <e_s, o_s> per head (query and key projections only)
+    float sdelta;    // sigma / sqrt(dh): the logit change per unit of <a, q> or <k, a>
     float* lse2;     // [T,H] log2-sum-exp2 of the clean scaled logits (log2 e / sqrt(dh) q.k)
     float* cpart;    // [KC][nkt][H][2][T] partial c per (draw, key tile, head, key half, query)
     int T, S, d, H;
     uint32_t k0, k1, layer, tok0, draw0;
 };
 
+// expm1(x): degree-6 Taylor polynomial for |x| < 1/4 (truncation below 5e-8
+// relative), exp(x) - 1 beyond (no cancellation there).
+__device__ __forceinline__ float expm1_small(float x) {
+    const float p = x * fmaf(x, fmaf(x, fmaf(x, fmaf(x, fmaf(x, 1.0f / 720.0f, 1.0f / 120.0f), 1.0f / 24.0f),
+                                              1.0f / 6.0f), 0.5f), 1.0f);
+    return fabsf(x) < 0.25f ? p : __expf(x) - 1.0f;
+}
+
 // ---- clean statistics -------------------------------------------------------
-__global__ void __launch_bounds__(ANT) attn_lse_kernel(AttnKArgs A) {
-    __shared__ float2 sh[2][AT];
+// Per (sequence, head, query tile): log2-sum-exp2 of the scaled logits and, with
+// OB, <e_s, o_s> = sum_t P_st <v_t, e_s> (needed by the query and key projections).
+template <bool OB>
+__global__ void __launch_bounds__(ANT) attn_stats_kernel(AttnKArgs A) {
+    __shared__ float4 sh[2][AT];
     const int nqt = A.S / AT;
     const int qt = blockIdx.x % nqt, bh = blockIdx.x / nqt, b = bh / A.H, h = bh % A.H;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, kh = w >> 1, qh = w & 1;
     const int64_t s0 = (int64_t)b * A.S;  // first token of the sequence
     const float sl2 = kAL2e * 0.125f;     // log2 e / sqrt(64)
-    uint4 qhi[4], qlo[4];
+    uint4 qhi[4], qlo[4], ehi[4], elo[4];
     load_frags(A.q, A.d, s0 + qt * AT + qh * 32 + (lane & 31), h * ADH, qhi, qlo);
+    if (OB) load_frags(A.e, A.d, s0 + qt * AT + qh * 32 + (lane & 31), h * ADH, ehi, elo);
     const int query = qt * AT + qh * 32 + (lane & 31);
-    float m = -__builtin_inff(), s = 0.f;
+    float m = -__builtin_inff(), s = 0.f, o = 0.f;
     for (int kt = 0; kt <= qt; ++kt) {
         uint4 khi[4], klo[4];
         load_frags(A.k, A.d, s0 + kt * AT + kh * 32 + (lane & 31), h * ADH, khi, klo);
         const af32x16_t L = prod_x3(khi, klo, qhi, qlo);  // [key][query]
+        af32x16_t W = {};
+        if (OB) {
+            uint4 vhi[4], vlo[4];
+            load_frags(A.v, A.d, s0 + kt * AT + kh * 32 + (lane & 31), h * ADH, vhi, vlo);
+            W = prod_x3(vhi, vlo, ehi, elo);  // [key][query]: <v_key, e_query>
+        }
         float x[16];
         float mt = -__builtin_inff();
 #pragma unroll
@@ -150,27 +172,78 @@ __global__ void __launch_bounds__(ANT) attn_lse_kernel(AttnKArgs A) {
         }
         const float mn = fmaxf(m, mt);
         if (mn == -__builtin_inff()) continue;  // every key of this lane so far lies after its query
-        float st = 0.f;
+        float st = 0.f, ot = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) st += __builtin_amdgcn_exp2f(x[r] - mn);
-        s = (m == -__builtin_inff() ? 0.f : s * __builtin_amdgcn_exp2f(m - mn)) + st;
+        for (int r = 0; r < 16; ++r) {
+            const float pr = __builtin_amdgcn_exp2f(x[r] - mn);
+            st += pr;
+            if (OB) ot = fmaf(pr, W[r], ot);
+        }
+        const float f = m == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+        s = s * f + st;
+        o = o * f + ot;
         m = mn;
     }
     // merge the two lanes of a query (lane, lane ^ 32), then the two key halves
-    const float mo = __shfl_xor(m, 32, 64), so = __shfl_xor(s, 32, 64);
+    const float mo = __shfl_xor(m, 32, 64), so = __shfl_xor(s, 32, 64), oo = __shfl_xor(o, 32, 64);
     const float mm = fmaxf(m, mo);
-    const float ss = (m == -__builtin_inff() ? 0.f : s * __builtin_amdgcn_exp2f(m - mm)) +
-                     (mo == -__builtin_inff() ? 0.f : so * __builtin_amdgcn_exp2f(mo - mm));
-    if (lane < 32) sh[kh][qh * 32 + lane] = make_float2(mm, ss);
+    const float f0 = m == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m - mm);
+    const float f1 = mo == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mo - mm);
+    if (lane < 32) sh[kh][qh * 32 + lane] = make_float4(mm, s * f0 + so * f1, o * f0 + oo * f1, 0.f);
     __syncthreads();
     if (tid < AT) {
-        const float2 p0 = sh[0][tid], p1 = sh[1][tid];
+        const float4 p0 = sh[0][tid], p1 = sh[1][tid];
         const float M = fmaxf(p0.x, p1.x);
-        float S2 = 0.f;
-        if (p0.y > 0.f) S2 += p0.y * __builtin_amdgcn_exp2f(p0.x - M);
-        if (p1.y > 0.f) S2 += p1.y * __builtin_amdgcn_exp2f(p1.x - M);
-        A.lse2[(s0 + qt * AT + tid) * A.H + h] = M + __builtin_amdgcn_logf(S2);  // log2 of sum exp2
+        const float g0 = p0.y > 0.f ? __builtin_amdgcn_exp2f(p0.x - M) : 0.f;
+        const float g1 = p1.y > 0.f ? __builtin_amdgcn_exp2f(p1.x - M) : 0.f;
+        const float S2 = p0.y * g0 + p1.y * g1;
+        const int64_t tok = s0 + qt * AT + tid;
+        A.lse2[tok * A.H + h] = M + __builtin_amdgcn_logf(S2);  // log2 of sum exp2
+        if (OB) A.ob[tok * A.H + h] = (p0.z * g0 + p1.z * g1) / S2;
     }
+}
+
+// Noise of 64 tokens (rows) x the 64 channels of head h for one draw, as bf16
+// hi/lo parts in the swizzled LDS layout; NTH lanes, 1024 / NTH quads each.
+template <int NTH>
+__device__ __forceinline__ void gen_tile(uint16_t* nh, uint16_t* nl, uint32_t tok_row0, int h, uint32_t draw,
+                                         const AttnKArgs& A) {
+#pragma unroll
+    for (int j = 0; j < 1024 / NTH; ++j) {
+        const int qi = (int)threadIdx.x + j * NTH;
+        const int row = qi >> 4, cq = qi & 15;  // channel quad within the head
+        const f32x4 g = gauss4(tok_row0 + (uint32_t)row, (uint32_t)(h * (ADH / 4) + cq), draw, A.layer, A.k0, A.k1);
+        const uint32_t h0 = pack2(g.v[0], g.v[1]), h1 = pack2(g.v[2], g.v[3]);
+        const uint32_t l0 = pack2(g.v[0] - __uint_as_float(h0 << 16), g.v[1] - __uint_as_float(h0 & 0xFFFF0000u));
+        const uint32_t l1 = pack2(g.v[2] - __uint_as_float(h1 << 16), g.v[3] - __uint_as_float(h1 & 0xFFFF0000u));
+        const int off = aswz(row, cq >> 1) + 4 * (cq & 1);
+        *reinterpret_cast<uint2*>(nh + off) = make_uint2(h0, h1);
+        *reinterpret_cast<uint2*>(nl + off) = make_uint2(l0, l1);
+    }
+}
+
+__device__ __forceinline__ void read_tile_frags(const uint16_t* nh, const uint16_t* nl, int row, uint4 (&hi)[4],
+                                                uint4 (&lo)[4]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const int off = aswz(row, 2 * ks + (lane >> 5));
+        hi[ks] = *reinterpret_cast<const uint4*>(nh + off);
+        lo[ks] = *reinterpret_cast<const uint4*>(nl + off);
+    }
+}
+
+// One accumulator chain of the three products A B^T (hi/lo pairs).
+__device__ __forceinline__ af32x16_t prod_x3c(const uint4 (&ahi)[4], const uint4 (&alo)[4], const uint4 (&bhi)[4],
+                                              const uint4 (&blo)[4]) {
+    af32x16_t g = {};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) g = mfma(alo[ks], bhi[ks], g);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) g = mfma(ahi[ks], blo[ks], g);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) g = mfma(ahi[ks], bhi[ks], g);
+    return g;
 }
 
 // ---- per-draw partial output changes ------------------------------------------
@@ -263,8 +336,238 @@ __global__ void __launch_bounds__(VNT, 1) attn_v_kernel(AttnKArgs A, int i0, int
     }
 }
 
+// ---- key projection: per-draw partial sums of the softmax change ---------------
+// With k'_t = k_t + sigma a_t, the logit of (s, t) moves by delta_st = sigma
+// <q_s, a_t> / 8 (times log2 e for exp2) and, per head,
+//     o'_s - o_s = sum_t (P'_st - P_st) v_t,  P'_st = P_st e^delta_st / (1 + rho_s),
+//     rho_s = sum_t P_st expm1(delta_st),
+// so c_s = <e_s, o'_s - o_s> = (mu_s - rho_s <e_s, o_s>) / (1 + rho_s) with
+// mu_s = sum_t P_st expm1(delta_st) <v_t, e_s>: two sums over the keys, formed
+// per key tile (partials rho, mu) like the value projection's c.
+__global__ void __launch_bounds__(VNT, 1) attn_k_kernel(AttnKArgs A, int kc) {
+    __shared__ __align__(16) uint16_t NH[ADC][AT * ADH];
+    __shared__ __align__(16) uint16_t NL[ADC][AT * ADH];
+    const int nqt = A.S / AT, nbh = (A.T / A.S) * A.H;
+    const int kt = blockIdx.x / nbh, bh = blockIdx.x % nbh, b = bh / A.H, h = bh % A.H;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, kh = (w >> 1) & 1, qh = w & 1, grp = w >> 2;
+    const int64_t s0 = (int64_t)b * A.S;
+    const int nkt = nqt;
+    const float sl2 = kAL2e * 0.125f;
+    uint4 khi[4], klo[4], vhi[4], vlo[4];  // this wave's 32 keys
+    load_frags(A.k, A.d, s0 + kt * AT + kh * 32 + (lane & 31), h * ADH, khi, klo);
+    load_frags(A.v, A.d, s0 + kt * AT + kh * 32 + (lane & 31), h * ADH, vhi, vlo);
+    for (int d0 = 0; d0 < kc; d0 += ADC) {
+        const int dn = min(ADC, kc - d0);
+        __syncthreads();  // the previous chunk's noise fully used
+        for (int dd = 0; dd < dn; ++dd)
+            gen_tile<VNT>(NH[dd], NL[dd], A.tok0 + (uint32_t)(s0 + kt * AT), h, A.draw0 + (uint32_t)(d0 + dd), A);
+        __syncthreads();
+        for (int qt = kt + grp; qt < nqt; qt += 2) {
+            const int64_t qrow = s0 + qt * AT + qh * 32 + (lane & 31);
+            const int query = qt * AT + qh * 32 + (lane & 31);
+            uint4 qhi[4], qlo[4];
+            load_frags(A.q, A.d, qrow, h * ADH, qhi, qlo);
+            float P[16], PW[16];
+            {
+                uint4 ehi[4], elo[4];
+                load_frags(A.e, A.d, qrow, h * ADH, ehi, elo);
+                const float l2q = A.lse2[qrow * A.H + h];
+                const af32x16_t L = prod_x3c(khi, klo, qhi, qlo);  // [key][query]
+                const af32x16_t W = prod_x3c(vhi, vlo, ehi, elo);  // [key][query]: <v_key, e_query>
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kt * AT + kh * 32 + drow(r, lane);
+                    P[r] = key <= query ? __builtin_amdgcn_exp2f(fmaf(L[r], sl2, -l2q)) : 0.f;
+                    PW[r] = P[r] * W[r];
+                }
+            }
+            float rho[ADC], mu[ADC];
+#pragma unroll
+            for (int dd = 0; dd < ADC; ++dd) {
+                if (dd < dn) {
+                    uint4 ahi[4], alo[4];
+                    read_tile_frags(NH[dd], NL[dd], kh * 32 + (lane & 31), ahi, alo);
+                    const af32x16_t D = prod_x3c(ahi, alo, qhi, qlo);  // [key][query]: <a_key, q_query>
+                    float rr = 0.f, mm = 0.f;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float x = expm1_small(D[r] * A.sdelta);
+                        rr = fmaf(P[r], x, rr);
+                        mm = fmaf(PW[r], x, mm);
+                    }
+                    rho[dd] = rr;
+                    mu[dd] = mm;
+                }
+            }
+#pragma unroll
+            for (int dd = 0; dd < ADC; ++dd)
+                if (dd < dn) {
+                    rho[dd] += __shfl_xor(rho[dd], 32, 64);
+                    mu[dd] += __shfl_xor(mu[dd], 32, 64);
+                }
+            if (lane < 32) {
+#pragma unroll
+                for (int dd = 0; dd < ADC; ++dd)
+                    if (dd < dn) {
+                        float* pp = A.cpart + (((((int64_t)(d0 + dd) * nkt + kt) * A.H + h) * 2 + kh) * 2) * A.T +
+                                    s0 + qt * AT + qh * 32 + lane;
+                        pp[0] = rho[dd];
+                        pp[A.T] = mu[dd];
+                    }
+            }
+        }
+    }
+}
+
+// ---- query projection: every sum stays in one workgroup ----------------------------
+// With q'_s = q_s + sigma a_s only the row of query s moves: delta_st = sigma
+// <a_s, k_t> / 8, and c_s = (mu_s - rho_s <e_s, o_s>) / (1 + rho_s) as for the keys,
+// the sums over the keys of query s, all in the query tile's workgroup: two wave
+// groups on alternate key tiles, merged through LDS at the end.  The reward is the
+// current token's own, r_s = -c_s, summed over the heads (per-head values go to
+// the partial buffer [draw][head][token]).
+__global__ void __launch_bounds__(VNT, 1) attn_q_kernel(AttnKArgs A, int kc) {
+    __shared__ __align__(16) uint16_t NH[ADC][AT * ADH];
+    __shared__ __align__(16) uint16_t NL[ADC][AT * ADH];
+    __shared__ float2 red[4][ADC][32 * 2];  // [group, key half][draw][query of the half * 2 + half]
+    const int nqt = A.S / AT, nbh = (A.T / A.S) * A.H;
+    // query tiles with the most key tiles first
+    const int qt = nqt - 1 - blockIdx.x / nbh, bh = blockIdx.x % nbh, b = bh / A.H, h = bh % A.H;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, kh = (w >> 1) & 1, qh = w & 1, grp = w >> 2;
+    const int64_t s0 = (int64_t)b * A.S;
+    const float sl2 = kAL2e * 0.125f;
+    const int64_t qrow = s0 + qt * AT + qh * 32 + (lane & 31);
+    const int query = qt * AT + qh * 32 + (lane & 31);
+    uint4 qhi[4], qlo[4], ehi[4], elo[4];  // this wave's 32 queries
+    load_frags(A.q, A.d, qrow, h * ADH, qhi, qlo);
+    load_frags(A.e, A.d, qrow, h * ADH, ehi, elo);
+    const float l2q = A.lse2[qrow * A.H + h];
+    for (int d0 = 0; d0 < kc; d0 += ADC) {
+        const int dn = min(ADC, kc - d0);
+        __syncthreads();  // the previous chunk's noise and sums fully used
+        for (int dd = 0; dd < dn; ++dd)
+            gen_tile<VNT>(NH[dd], NL[dd], A.tok0 + (uint32_t)(s0 + qt * AT), h, A.draw0 + (uint32_t)(d0 + dd), A);
+        __syncthreads();
+        float rho[ADC], mu[ADC];
+#pragma unroll
+        for (int dd = 0; dd < ADC; ++dd) rho[dd] = mu[dd] = 0.f;
+        for (int kt = grp; kt <= qt; kt += 2) {
+            uint4 khi[4], klo[4], vhi[4], vlo[4];
+            load_frags(A.k, A.d, s0 + kt * AT + kh * 32 + (lane & 31), h * ADH, khi, klo);
+            load_frags(A.v, A.d, s0 + kt * AT + kh * 32 + (lane & 31), h * ADH, vhi, vlo);
+            const af32x16_t L = prod_x3c(khi, klo, qhi, qlo);  // [key][query]
+            const af32x16_t W = prod_x3c(vhi, vlo, ehi, elo);  // [key][query]: <v_key, e_query>
+            float P[16], PW[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = kt * AT + kh * 32 + drow(r, lane);
+                P[r] = key <= query ? __builtin_amdgcn_exp2f(fmaf(L[r], sl2, -l2q)) : 0.f;
+                PW[r] = P[r] * W[r];
+            }
+#pragma unroll
+            for (int dd = 0; dd < ADC; ++dd) {
+                if (dd < dn) {
+                    uint4 ahi[4], alo[4];  // this wave's queries' noise
+                    read_tile_frags(NH[dd], NL[dd], qh * 32 + (lane & 31), ahi, alo);
+                    const af32x16_t D = prod_x3c(khi, klo, ahi, alo);  // [key][query]: <k_key, a_query>
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float x = expm1_small(D[r] * A.sdelta);
+                        rho[dd] = fmaf(P[r], x, rho[dd]);
+                        mu[dd] = fmaf(PW[r], x, mu[dd]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int dd = 0; dd < ADC; ++dd)
+            if (dd < dn) {
+                rho[dd] += __shfl_xor(rho[dd], 32, 64);
+                mu[dd] += __shfl_xor(mu[dd], 32, 64);
+            }
+        if (lane < 32) {
+#pragma unroll
+            for (int dd = 0; dd < ADC; ++dd)
+                if (dd < dn) red[grp * 2 + kh][dd][lane * 2 + qh] = make_float2(rho[dd], mu[dd]);
+        }
+        __syncthreads();
+        for (int x = tid; x < dn * AT; x += VNT) {
+            const int dd = x / AT, qq = x % AT;  // query qq of the tile
+            const int slot = (qq & 31) * 2 + (qq >> 5);
+            float rr = 0.f, mm = 0.f;
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                rr += red[g4][dd][slot].x;
+                mm += red[g4][dd][slot].y;
+            }
+            const int64_t tok = s0 + qt * AT + qq;
+            const float c = (mm - rr * A.ob[tok * A.H + h]) / (1.0f + rr);
+            A.cpart[((int64_t)(d0 + dd) * A.H + h) * A.T + tok] = -c;
+        }
+    }
+}
+
+// ---- key projection: c_s from the partial sums, r_t = -sum_{s >= t} c_s ---------
+__global__ void __launch_bounds__(256) attn_suffix_k_kernel(const float* __restrict__ cpart,
+                                                            const float* __restrict__ ob, int T, int S, int H,
+                                                            int i0, float* __restrict__ rew) {
+    __shared__ float cs[ASMAX];
+    __shared__ float sh[256];
+    const int nkt = S / AT, nb = T / S;
+    const int dd = blockIdx.x / nb, b = blockIdx.x % nb, tid = threadIdx.x;
+    const int per = (S + 255) / 256;
+    const int64_t s0 = (int64_t)b * S;
+    for (int s = tid; s < S; s += 256) {
+        float c = 0.f;
+        for (int h = 0; h < H; ++h) {
+            float rr = 0.f, mm = 0.f;
+            for (int kt = 0; kt <= s / AT; ++kt)
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh) {
+                    const float* pp = cpart + (((((int64_t)dd * nkt + kt) * H + h) * 2 + kh) * 2) * T + s0 + s;
+                    rr += pp[0];
+                    mm += pp[T];
+                }
+            c += (mm - rr * ob[(s0 + s) * H + h]) / (1.0f + rr);
+        }
+        cs[s] = c;
+    }
+    __syncthreads();
+    float tot = 0.f;
+    for (int j = per - 1; j >= 0; --j) {
+        const int s = tid * per + j;
+        if (s < S) {
+            tot += cs[s];
+            cs[s] = tot;
+        }
+    }
+    sh[tid] = tot;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+        const float v = tid + off < 256 ? sh[tid + off] : 0.f;
+        __syncthreads();
+        sh[tid] += v;
+        __syncthreads();
+    }
+    const float after = tid + 1 < 256 ? sh[tid + 1] : 0.f;
+    for (int j = 0; j < per; ++j) {
+        const int s = tid * per + j;
+        if (s < S) rew[(int64_t)(i0 + dd) * T + s0 + s] = -(cs[s] + after);
+    }
+}
+
+// ---- query projection: r_t = -sum over the heads of c_t --------------------------
+__global__ void __launch_bounds__(256) attn_heads_q_kernel(const float* __restrict__ cpart, int T, int H, int i0,
+                                                           int kc, float* __restrict__ rew) {
+    const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (x >= (int64_t)kc * T) return;
+    const int64_t dd = x / T, t = x % T;
+    float r = 0.f;
+    for (int h = 0; h < H; ++h) r += cpart[(dd * H + h) * T + t];
+    rew[(i0 + dd) * T + t] = r;
+}
+
 // ---- rewards: c_s from the partials, r_t = -sigma sum_{s >= t} c_s -----------
-constexpr int ASMAX = 4096;  // longest sequence
 __global__ void __launch_bounds__(256) attn_suffix_kernel(const float* __restrict__ cpart, int T, int S, int H,
                                                           int i0, float sigma, float* __restrict__ rew) {
     __shared__ float cs[ASMAX];
@@ -325,9 +628,16 @@ __global__ void __launch_bounds__(128) attn_reduce_kernel(AttnKArgs A, int K, co
     }
 }
 
+// Partial-buffer floats per draw: per (key tile, head, key half) one c (values)
+// or the two sums rho, mu (keys); per head one c (queries).
+static int64_t attn_part_per_draw(int proj, int64_t T, int64_t S, int64_t H) {
+    const int64_t nkt = S / AT;
+    return proj == 2 ? nkt * H * 2 * T : proj == 1 ? nkt * H * 4 * T : H * T;
+}
+
 // Draws per pass of the partial buffer (kept to about 256 MB).
-static int attn_kc(int64_t T, int64_t S, int64_t H, int64_t K) {
-    const int64_t per_draw = (S / AT) * H * 2 * T * 4;
+static int attn_kc(int proj, int64_t T, int64_t S, int64_t H, int64_t K) {
+    const int64_t per_draw = attn_part_per_draw(proj, T, S, H) * 4;
     int64_t kc = ((int64_t)256 << 20) / (per_draw > 0 ? per_draw : 1);
     kc = kc < 1 ? 1 : kc > 64 ? 64 : kc;
     return (int)(K < kc ? K : kc);
@@ -335,12 +645,12 @@ static int attn_kc(int64_t T, int64_t S, int64_t H, int64_t K) {
 
 static size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 
-AttnVLayout attn_v_layout(int64_t T, int64_t S, int64_t d, int64_t H, int64_t K) {
+AttnVLayout attn_layout(int proj, int64_t T, int64_t S, int64_t d, int64_t H, int64_t K) {
     AttnVLayout L{};
-    const int64_t nkt = S / AT;
     size_t off = 0;
     L.off_lse = off;   off += al256((size_t)T * H * 4);
-    L.off_cpart = off; off += al256((size_t)attn_kc(T, S, H, K) * nkt * H * 2 * T * 4);
+    L.off_ob = off;    off += proj == 2 ? 0 : al256((size_t)T * H * 4);
+    L.off_cpart = off; off += al256((size_t)attn_kc(proj, T, S, H, K) * attn_part_per_draw(proj, T, S, H) * 4);
     L.off_rew = off;   off += al256((size_t)K * T * 4);
     L.off_ghat = off;  off += al256((size_t)T * d * 4);
     L.off_outer = off; off += outer_workspace_bytes(T, d, d);
@@ -348,37 +658,46 @@ AttnVLayout attn_v_layout(int64_t T, int64_t S, int64_t d, int64_t H, int64_t K)
     return L;
 }
 
-static AttnKArgs attn_args(const float* q, const float* k, const float* e, int64_t T, int64_t S, int64_t d,
-                           int64_t H, uint64_t seed, uint32_t layer, uint32_t token_offset, uint32_t draw_offset,
-                           unsigned char* ws, const AttnVLayout& L) {
+hipError_t launch_attn_rewards(int proj, const float* q, const float* k, const float* v, const float* e, int64_t T,
+                               int64_t S, int64_t d, int64_t H, int64_t K, float sigma, uint64_t seed, uint32_t layer,
+                               uint32_t token_offset, uint32_t draw_offset, float* rew, unsigned char* ws,
+                               const AttnVLayout& L, hipStream_t stream) {
+    const int64_t nkt = S / AT, nb = T / S;
+    const int kcmax = attn_kc(proj, T, S, H, K);
     AttnKArgs A{};
-    A.q = q; A.k = k; A.e = e;
+    A.q = q; A.k = k; A.v = v; A.e = e;
     A.lse2 = reinterpret_cast<float*>(ws + L.off_lse);
+    A.ob = proj == 2 ? nullptr : reinterpret_cast<float*>(ws + L.off_ob);
     A.cpart = reinterpret_cast<float*>(ws + L.off_cpart);
     A.T = (int)T; A.S = (int)S; A.d = (int)d; A.H = (int)H;
     A.k0 = (uint32_t)seed; A.k1 = (uint32_t)(seed >> 32);
     A.layer = layer; A.tok0 = token_offset; A.draw0 = draw_offset;
-    return A;
-}
-
-hipError_t launch_attn_v_rewards(const float* q, const float* k, const float* e, int64_t T, int64_t S, int64_t d,
-                                 int64_t H, int64_t K, float sigma, uint64_t seed, uint32_t layer,
-                                 uint32_t token_offset, uint32_t draw_offset, float* rew, unsigned char* ws,
-                                 const AttnVLayout& L, hipStream_t stream) {
-    const int64_t nkt = S / AT, nb = T / S;
-    const int kcmax = attn_kc(T, S, H, K);
-    const AttnKArgs A = attn_args(q, k, e, T, S, d, H, seed, layer, token_offset, draw_offset, ws, L);
-    hipLaunchKernelGGL(attn_lse_kernel, dim3((unsigned)(nb * H * nkt)), dim3(ANT), 0, stream, A);
+    A.sdelta = sigma * 0.125f;
+    const unsigned grid = (unsigned)(nb * H * nkt);
+    if (proj == 2) hipLaunchKernelGGL(attn_stats_kernel<false>, dim3(grid), dim3(ANT), 0, stream, A);
+    else hipLaunchKernelGGL(attn_stats_kernel<true>, dim3(grid), dim3(ANT), 0, stream, A);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     for (int64_t i0 = 0; i0 < K; i0 += kcmax) {
         const int kc = (int)(K - i0 < kcmax ? K - i0 : kcmax);
         AttnKArgs Ai = A;
         Ai.draw0 = draw_offset + (uint32_t)i0;
-        hipLaunchKernelGGL(attn_v_kernel, dim3((unsigned)(nb * H * nkt)), dim3(VNT), 0, stream, Ai, 0, kc);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
-        hipLaunchKernelGGL(attn_suffix_kernel, dim3((unsigned)(kc * nb)), dim3(256), 0, stream, A.cpart, (int)T,
-                           (int)S, (int)H, (int)i0, sigma, rew);
+        if (proj == 2) {
+            hipLaunchKernelGGL(attn_v_kernel, dim3(grid), dim3(VNT), 0, stream, Ai, 0, kc);
+            if ((err = hipGetLastError()) != hipSuccess) return err;
+            hipLaunchKernelGGL(attn_suffix_kernel, dim3((unsigned)(kc * nb)), dim3(256), 0, stream, A.cpart, (int)T,
+                               (int)S, (int)H, (int)i0, sigma, rew);
+        } else if (proj == 1) {
+            hipLaunchKernelGGL(attn_k_kernel, dim3(grid), dim3(VNT), 0, stream, Ai, kc);
+            if ((err = hipGetLastError()) != hipSuccess) return err;
+            hipLaunchKernelGGL(attn_suffix_k_kernel, dim3((unsigned)(kc * nb)), dim3(256), 0, stream, A.cpart, A.ob,
+                               (int)T, (int)S, (int)H, (int)i0, rew);
+        } else {
+            hipLaunchKernelGGL(attn_q_kernel, dim3(grid), dim3(VNT), 0, stream, Ai, kc);
+            if ((err = hipGetLastError()) != hipSuccess) return err;
+            hipLaunchKernelGGL(attn_heads_q_kernel, dim3((unsigned)((kc * T + 255) / 256)), dim3(256), 0, stream,
+                               A.cpart, (int)T, (int)H, (int)i0, kc, rew);
+        }
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     return hipSuccess;

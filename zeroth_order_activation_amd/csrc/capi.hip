@@ -370,9 +370,60 @@ dust_status dust_estimate_linear(const float* u, const float* h, const float* x_
 
 }  // extern "C"
 
+size_t dust_attn_workspace_bytes(int proj, int64_t T, int64_t S, int64_t d, int64_t H, int64_t K) {
+    if (proj < 0 || proj > 2 || T <= 0 || S <= 0 || d <= 0 || H <= 0 || K <= 0) return 0;
+    return dust::attn_layout(proj, T, S, d, H, K).total;
+}
+
 size_t dust_attn_v_workspace_bytes(int64_t T, int64_t S, int64_t d, int64_t H, int64_t K) {
-    if (T <= 0 || S <= 0 || d <= 0 || H <= 0 || K <= 0) return 0;
-    return dust::attn_v_layout(T, S, d, H, K).total;
+    return dust_attn_workspace_bytes(DUST_ATTN_V, T, S, d, H, K);
+}
+
+dust_status dust_estimate_attn(int proj, const float* q, const float* k, const float* v, const float* e,
+                               const float* u, int64_t T, int64_t S, int64_t d, int64_t H, int64_t K, float sigma,
+                               uint64_t seed, uint32_t layer, uint32_t token_offset, uint32_t draw_offset,
+                               float* grad_w, float* ghat, float* rewards, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+    if (proj != DUST_ATTN_Q && proj != DUST_ATTN_K && proj != DUST_ATTN_V)
+        return fail(DUST_E_INVALID, "dust_estimate_attn: proj %d is not DUST_ATTN_Q, _K or _V", proj);
+    if (!q || !k || !e || !u || !grad_w || (proj != DUST_ATTN_V && !v))
+        return fail(DUST_E_INVALID, "dust_estimate_attn: q, k, e, u, grad_w (and v for queries and keys) must be "
+                                    "non-NULL");
+    if (!aligned16(q) || !aligned16(k) || (v && !aligned16(v)) || !aligned16(e) || !aligned16(u) ||
+        !aligned16(grad_w) || (ghat && !aligned16(ghat)) || (rewards && !aligned16(rewards)) ||
+        (workspace && !aligned16(workspace)))
+        return fail(DUST_E_INVALID, "dust_estimate_attn: every pointer must be 16-byte aligned");
+    dust_status s = check_common(T, K, sigma, token_offset, draw_offset);
+    if (s != DUST_OK) return s;
+    if (S <= 0 || d <= 0 || H <= 0) return fail(DUST_E_INVALID, "dust_estimate_attn: S, d and H must be >= 1");
+    if (T % S != 0)
+        return fail(DUST_E_INVALID, "dust_estimate_attn: T (%lld) must be a multiple of S (%lld)", (long long)T,
+                    (long long)S);
+    if (d != 64 * H) return fail(DUST_E_UNSUPPORTED, "dust_estimate_attn: heads of 64 channels only (d = 64 H)");
+    if (S % 64 != 0 || S > 4096)
+        return fail(DUST_E_UNSUPPORTED, "dust_estimate_attn: S must be a multiple of 64 up to 4096 (got %lld)",
+                    (long long)S);
+    if (T > (1LL << 31) / 64 || K * T > (1LL << 31))
+        return fail(DUST_E_UNSUPPORTED, "dust_estimate_attn: T or K*T too large");
+    const dust::AttnVLayout L = dust::attn_layout(proj, T, S, d, H, K);
+    if (workspace == nullptr || workspace_bytes < L.total)
+        return fail(DUST_E_WORKSPACE, "dust_estimate_attn: workspace of %zu bytes needed, %zu given", L.total,
+                    workspace ? workspace_bytes : (size_t)0);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    float* rew = rewards ? rewards : reinterpret_cast<float*>(ws + L.off_rew);
+    float* g = ghat ? ghat : reinterpret_cast<float*>(ws + L.off_ghat);
+    hipError_t err = dust::launch_attn_rewards(proj, q, k, v, e, T, S, d, H, K, sigma, seed, layer, token_offset,
+                                               draw_offset, rew, ws, L, st);
+    if (err != hipSuccess) return device_fail("dust_estimate_attn: attention passes", err);
+    if ((err = record_stage(2, st)) != hipSuccess) return device_fail("dust_estimate_attn: stage event", err);
+    err = dust::launch_attn_v_ghat(T, d, K, sigma, seed, layer, token_offset, draw_offset, rew, g, st);
+    if (err != hipSuccess) return device_fail("dust_estimate_attn: reduction launch", err);
+    if ((err = record_stage(0, st)) != hipSuccess) return device_fail("dust_estimate_attn: stage event", err);
+    err = dust::launch_outer(g, u, T, d, d, grad_w, ws + L.off_outer, L.total - L.off_outer, st, false);
+    if (err != hipSuccess) return device_fail("dust_estimate_attn: outer-product launch", err);
+    if ((err = record_stage(1, st)) != hipSuccess) return device_fail("dust_estimate_attn: stage event", err);
+    return ok();
 }
 
 dust_status dust_estimate_attn_v(const float* q, const float* k, const float* e, const float* u, int64_t T,
@@ -380,41 +431,6 @@ dust_status dust_estimate_attn_v(const float* q, const float* k, const float* e,
                                  uint32_t layer, uint32_t token_offset, uint32_t draw_offset, float* grad_w,
                                  float* ghat, float* rewards, void* workspace, size_t workspace_bytes,
                                  void* stream) {
-    if (!q || !k || !e || !u || !grad_w)
-        return fail(DUST_E_INVALID, "dust_estimate_attn_v: q, k, e, u and grad_w must be non-NULL");
-    if (!aligned16(q) || !aligned16(k) || !aligned16(e) || !aligned16(u) || !aligned16(grad_w) ||
-        (ghat && !aligned16(ghat)) || (rewards && !aligned16(rewards)) || (workspace && !aligned16(workspace)))
-        return fail(DUST_E_INVALID, "dust_estimate_attn_v: every pointer must be 16-byte aligned");
-    dust_status s = check_common(T, K, sigma, token_offset, draw_offset);
-    if (s != DUST_OK) return s;
-    if (S <= 0 || d <= 0 || H <= 0)
-        return fail(DUST_E_INVALID, "dust_estimate_attn_v: S, d and H must be >= 1");
-    if (T % S != 0) return fail(DUST_E_INVALID, "dust_estimate_attn_v: T (%lld) must be a multiple of S (%lld)",
-                                (long long)T, (long long)S);
-    if (d != 64 * H)
-        return fail(DUST_E_UNSUPPORTED, "dust_estimate_attn_v: heads of 64 channels only (d = 64 H)");
-    if (S % 64 != 0 || S > 4096)
-        return fail(DUST_E_UNSUPPORTED, "dust_estimate_attn_v: S must be a multiple of 64 up to 4096 (got %lld)",
-                    (long long)S);
-    if (T > (1LL << 31) / 64 || K * T > (1LL << 31))
-        return fail(DUST_E_UNSUPPORTED, "dust_estimate_attn_v: T or K*T too large");
-    const dust::AttnVLayout L = dust::attn_v_layout(T, S, d, H, K);
-    if (workspace == nullptr || workspace_bytes < L.total)
-        return fail(DUST_E_WORKSPACE, "dust_estimate_attn_v: workspace of %zu bytes needed, %zu given", L.total,
-                    workspace ? workspace_bytes : (size_t)0);
-    const hipStream_t st = static_cast<hipStream_t>(stream);
-    unsigned char* ws = static_cast<unsigned char*>(workspace);
-    float* rew = rewards ? rewards : reinterpret_cast<float*>(ws + L.off_rew);
-    float* g = ghat ? ghat : reinterpret_cast<float*>(ws + L.off_ghat);
-    hipError_t err = dust::launch_attn_v_rewards(q, k, e, T, S, d, H, K, sigma, seed, layer, token_offset,
-                                                 draw_offset, rew, ws, L, st);
-    if (err != hipSuccess) return device_fail("dust_estimate_attn_v: attention passes", err);
-    if ((err = record_stage(2, st)) != hipSuccess) return device_fail("dust_estimate_attn_v: stage event", err);
-    err = dust::launch_attn_v_ghat(T, d, K, sigma, seed, layer, token_offset, draw_offset, rew, g, st);
-    if (err != hipSuccess) return device_fail("dust_estimate_attn_v: reduction launch", err);
-    if ((err = record_stage(0, st)) != hipSuccess) return device_fail("dust_estimate_attn_v: stage event", err);
-    err = dust::launch_outer(g, u, T, d, d, grad_w, ws + L.off_outer, L.total - L.off_outer, st, false);
-    if (err != hipSuccess) return device_fail("dust_estimate_attn_v: outer-product launch", err);
-    if ((err = record_stage(1, st)) != hipSuccess) return device_fail("dust_estimate_attn_v: stage event", err);
-    return ok();
+    return dust_estimate_attn(DUST_ATTN_V, q, k, nullptr, e, u, T, S, d, H, K, sigma, seed, layer, token_offset,
+                              draw_offset, grad_w, ghat, rewards, workspace, workspace_bytes, stream);
 }

@@ -93,15 +93,15 @@ MlpLayout mlp_layout(int64_t T, int64_t d, int64_t n, int64_t V, int64_t K);
 hipError_t launch_mlp(const MlpArgs& args, const MlpLayout& layout, unsigned char* workspace, float* ghat_user,
                       float* grad_w, hipStream_t stream);
 
-// attention value-projection estimator (attn.hip)
+// attention projection estimators (attn.hip); proj 0 = query, 1 = key, 2 = value
 struct AttnVLayout {
-    size_t off_lse, off_cpart, off_rew, off_ghat, off_outer, total;
+    size_t off_lse, off_ob, off_cpart, off_rew, off_ghat, off_outer, total;
 };
-AttnVLayout attn_v_layout(int64_t T, int64_t S, int64_t d, int64_t H, int64_t K);
-hipError_t launch_attn_v_rewards(const float* q, const float* k, const float* e, int64_t T, int64_t S, int64_t d,
-                                 int64_t H, int64_t K, float sigma, uint64_t seed, uint32_t layer,
-                                 uint32_t token_offset, uint32_t draw_offset, float* rew, unsigned char* ws,
-                                 const AttnVLayout& L, hipStream_t stream);
+AttnVLayout attn_layout(int proj, int64_t T, int64_t S, int64_t d, int64_t H, int64_t K);
+hipError_t launch_attn_rewards(int proj, const float* q, const float* k, const float* v, const float* e, int64_t T,
+                               int64_t S, int64_t d, int64_t H, int64_t K, float sigma, uint64_t seed, uint32_t layer,
+                               uint32_t token_offset, uint32_t draw_offset, float* rew, unsigned char* ws,
+                               const AttnVLayout& L, hipStream_t stream);
 hipError_t launch_attn_v_ghat(int64_t T, int64_t d, int64_t K, float sigma, uint64_t seed, uint32_t layer,
                               uint32_t token_offset, uint32_t draw_offset, const float* rew, float* ghat,
                               hipStream_t stream);
