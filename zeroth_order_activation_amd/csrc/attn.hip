@@ -128,12 +128,24 @@ struct AttnKArgs {
     uint32_t k0, k1, layer, tok0, draw0;
 };
 
-// expm1(x): degree-6 Taylor polynomial for |x| < 1/4 (truncation below 5e-8
-// relative), exp(x) - 1 beyond (no cancellation there).
-__device__ __forceinline__ float expm1_small(float x) {
-    const float p = x * fmaf(x, fmaf(x, fmaf(x, fmaf(x, fmaf(x, 1.0f / 720.0f, 1.0f / 120.0f), 1.0f / 24.0f),
-                                              1.0f / 6.0f), 0.5f), 1.0f);
-    return fabsf(x) < 0.25f ? p : __expf(x) - 1.0f;
+// expm1 of the 16 logit changes of a lane: the degree-6 Taylor polynomial
+// (truncation below 5e-8 relative for |x| < 1/4); where some lane of the wave
+// holds a larger |x|, those values take exp(x) - 1 (no cancellation there).
+__device__ __forceinline__ void expm1_16(float (&x)[16]) {
+    bool big = false;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) big |= fabsf(x[r]) >= 0.25f;
+    float p[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        p[r] = x[r] * fmaf(x[r], fmaf(x[r], fmaf(x[r], fmaf(x[r], fmaf(x[r], 1.0f / 720.0f, 1.0f / 120.0f),
+                                                             1.0f / 24.0f), 1.0f / 6.0f), 0.5f), 1.0f);
+    if (__builtin_amdgcn_ballot_w64(big)) {  // wave-uniform, rare at small sigma
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p[r] = fabsf(x[r]) < 0.25f ? p[r] : __expf(x[r]) - 1.0f;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = p[r];
 }
 
 // ---- clean statistics -------------------------------------------------------
@@ -388,12 +400,15 @@ __global__ void __launch_bounds__(VNT, 1) attn_k_kernel(AttnKArgs A, int kc) {
                     uint4 ahi[4], alo[4];
                     read_tile_frags(NH[dd], NL[dd], kh * 32 + (lane & 31), ahi, alo);
                     const af32x16_t D = prod_x3c(ahi, alo, qhi, qlo);  // [key][query]: <a_key, q_query>
+                    float x[16];
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) x[r] = D[r] * A.sdelta;
+                    expm1_16(x);
                     float rr = 0.f, mm = 0.f;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const float x = expm1_small(D[r] * A.sdelta);
-                        rr = fmaf(P[r], x, rr);
-                        mm = fmaf(PW[r], x, mm);
+                        rr = fmaf(P[r], x[r], rr);
+                        mm = fmaf(PW[r], x[r], mm);
                     }
                     rho[dd] = rr;
                     mu[dd] = mm;
@@ -470,11 +485,14 @@ __global__ void __launch_bounds__(VNT, 1) attn_q_kernel(AttnKArgs A, int kc) {
                     uint4 ahi[4], alo[4];  // this wave's queries' noise
                     read_tile_frags(NH[dd], NL[dd], qh * 32 + (lane & 31), ahi, alo);
                     const af32x16_t D = prod_x3c(khi, klo, ahi, alo);  // [key][query]: <k_key, a_query>
+                    float x[16];
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) x[r] = D[r] * A.sdelta;
+                    expm1_16(x);
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const float x = expm1_small(D[r] * A.sdelta);
-                        rho[dd] = fmaf(P[r], x, rho[dd]);
-                        mu[dd] = fmaf(PW[r], x, mu[dd]);
+                        rho[dd] = fmaf(P[r], x[r], rho[dd]);
+                        mu[dd] = fmaf(PW[r], x[r], mu[dd]);
                     }
                 }
             }
