@@ -80,6 +80,7 @@ QK_CASES = [
     ("q", 1, 192, 1, 9, 3e-2),
     ("q", 3, 128, 4, 70, 1e-2),  # more draws than one pass of partials
     ("k", 1, 64, 1, 70, 0.2),    # |delta| past the polynomial's range: exp - 1
+    ("q", 2, 128, 2, 9, 0.2),    # the same for queries, over two key tiles
 ]
 
 
