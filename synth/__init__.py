@@ -105,6 +105,40 @@ def attn_case(B: int, S: int, H: int, seed: int, dh: int = 64, matmul=None) -> d
     return {"u": U, "q": q, "k": k, "v": v, "e": E, "T": T, "S": S, "H": H, "d": d}
 
 
+LM_NOISE_SEED = NOISE_SEED_BASE + 7
+
+
+def lm_param_layout(V: int, d: int, L: int, n: int, S: int):
+    """Named tensors of a small LM's packed fp32 parameter vector, in storage
+    order (weights [out, in]; scal = alpha_0, beta_0, alpha_1, beta_1, ...)."""
+    out = [("emb", (V, d)), ("pos", (S, d))]
+    for l in range(L):
+        out += [(f"wq{l}", (d, d)), (f"wk{l}", (d, d)), (f"wv{l}", (d, d)), (f"wo{l}", (d, d)),
+                (f"w1{l}", (n, d)), (f"w2{l}", (d, n))]
+    return out + [("head", (V, d)), ("scal", (2 * L,))]
+
+
+def lm_case(V: int, d: int, H: int, L: int, n: int, S: int, B: int, *, seed: int, scal: float = 1.0) -> dict:
+    """A small causal LM at random initialisation and a batch of B sequences:
+    embeddings N(0,1), weights N(0, 1/fan_in), residual scalars ``scal``; token
+    sequences of S + 1 Zipf(1.1) ids over [0, V), inputs the first S, labels the
+    next token.  Parameters are packed fp32 (see lm_param_layout)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    parts = []
+    for name, shp in lm_param_layout(V, d, L, n, S):
+        if name == "scal":
+            parts.append(np.full(shp, scal, np.float32))
+        elif name in ("emb", "pos"):
+            parts.append(rng.standard_normal(shp, dtype=np.float32))
+        else:
+            parts.append(rng.standard_normal(shp, dtype=np.float32) / np.float32(np.sqrt(shp[1])))
+    seq = zipf_labels(rng, B * (S + 1), V).reshape(B, S + 1)
+    return {"params": np.concatenate([p_.reshape(-1) for p_ in parts]).astype(np.float32),
+            "tokens": np.ascontiguousarray(seq[:, :S].reshape(-1), dtype=np.int32),
+            "labels": np.ascontiguousarray(seq[:, 1:].reshape(-1), dtype=np.int32),
+            "V": V, "d": d, "H": H, "L": L, "n": n, "S": S, "B": B, "T": B * S}
+
+
 # The named workloads (token counts are batch x sequence, flattened t = b*S + s).
 WORKLOADS = {
     1: dict(kind="head", T=256, V=512, d=64, K=64, sigma=1e-2, labels="uniform", logits_dtype="f32"),

@@ -1,0 +1,235 @@
+"""Pins of the oracle's full Dust step on a small causal LM (TL;DR page, section 1,
+"reducing interference": per-type passes with their own noise scales, attention
+internals through the attention output, the head on cached logits; section 2: SGD with
+momentum; iitog.ru mechanics paragraph: the 2L residual scalars by weight-space ES).
+
+An independent torch fp64 model (library layer_norm, causal scaled-dot-product attention,
+erf GELU, cross-entropy) fixes:
+- the forward pass, and every pass's rewards as torch loss differences on the same noise;
+- G = g_hat^T (layer input) for every linear and the embedding scatter, as autograd of
+  sum_t <g_hat_t, y_t(W)>;
+- unbiasedness: at small sigma and large K each estimate regresses with slope 1 on the
+  autograd target (the token's own-loss gradient at the perturbed output; for attention
+  internals the gradient of sum <e, o> with e the own-loss gradient at the attention
+  output; for the scalars the gradient of the summed loss);
+- the optimiser against torch.optim.SGD with momentum.
+"""
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+import oracle
+import synth
+from oracle import lm
+
+SEED = 0x4455535400000031
+CFG = lm.LMConfig(V=11, d=8, H=2, L=2, n=16, S=8)
+B = 2
+
+
+def _case(seed=1, scal=1.0):
+    c = synth.lm_case(CFG.V, CFG.d, CFG.H, CFG.L, CFG.n, CFG.S, B, seed=seed, scal=scal)
+    return c["params"], c["tokens"], c["labels"]
+
+
+def _split(flat):
+    out, o = {}, 0
+    for name, shp in synth.lm_param_layout(CFG.V, CFG.d, CFG.L, CFG.n, CFG.S):
+        m = int(np.prod(shp))
+        out[name] = flat[o:o + m].reshape(shp)
+        o += m
+    return out
+
+
+def _attn(q, k, v):
+    T, d = q.shape
+    dh = d // CFG.H
+
+    def heads(x):
+        return x.reshape(T // CFG.S, CFG.S, CFG.H, dh).transpose(1, 2)
+
+    o = F.scaled_dot_product_attention(heads(q), heads(k), heads(v), is_causal=True)
+    return o.transpose(1, 2).reshape(T, d)
+
+
+def torch_forward(flat, tokens, labels, deltas=None, scal=None, hold=None):
+    """Per-token CE of the model in torch fp64.  ``deltas`` adds tensors at the
+    linear outputs ("emb",), (l, "o"|"up"|"down"); ``hold`` collects outputs."""
+    p = _split(flat)
+    deltas = deltas or {}
+    s = p["scal"] if scal is None else scal
+    tok = torch.as_tensor(tokens, dtype=torch.long)
+    T = tok.shape[0]
+    x = p["emb"][tok] + p["pos"][torch.arange(T) % CFG.S]
+    if ("emb",) in deltas:
+        x = x + deltas[("emb",)]
+    for l in range(CFG.L):
+        u1 = F.layer_norm(x, (CFG.d,), eps=CFG.eps)
+        q, k, v = u1 @ p[f"wq{l}"].T, u1 @ p[f"wk{l}"].T, u1 @ p[f"wv{l}"].T
+        o = _attn(q, k, v)
+        if hold is not None:
+            hold[l] = dict(u1=u1, o=o)
+        ba = o @ p[f"wo{l}"].T + deltas.get((l, "o"), 0.0)
+        x = x + s[2 * l] * ba
+        h = F.layer_norm(x, (CFG.d,), eps=CFG.eps) @ p[f"w1{l}"].T + deltas.get((l, "up"), 0.0)
+        x = x + s[2 * l + 1] * (F.gelu(h) @ p[f"w2{l}"].T + deltas.get((l, "down"), 0.0))
+    z = F.layer_norm(x, (CFG.d,), eps=CFG.eps) @ p["head"].T
+    if hold is not None:
+        hold["z"] = z
+    return F.cross_entropy(z, torch.as_tensor(labels, dtype=torch.long), reduction="none")
+
+
+def _t(x, grad=False):
+    return torch.tensor(np.asarray(x, np.float64), requires_grad=grad)
+
+
+def _points(kind):
+    if kind == "emb":
+        return [(("emb",), lm.LID_EMB, CFG.d)]
+    return [((l, kind), lm.lid(l, kind), CFG.n if kind == "up" else CFG.d) for l in range(CFG.L)]
+
+
+def _own_token_grads(flat, tokens, labels, kind):
+    """d CE_t / d y_t at every point of ``kind`` (the token's own loss only)."""
+    T = len(tokens)
+    dl = {pt: torch.zeros((T, w), dtype=torch.float64, requires_grad=True) for pt, _, w in _points(kind)}
+    ce = torch_forward(_t(flat), tokens, labels, deltas=dl)
+    out = {pt: np.zeros((T, x.shape[1])) for pt, x in dl.items()}
+    for t in range(T):
+        gs = torch.autograd.grad(ce[t], list(dl.values()), retain_graph=True)
+        for pt, g in zip(dl, gs):
+            out[pt][t] = g[t].numpy()
+    return out
+
+
+def _slope(g, t):
+    g, t = np.ravel(g), np.ravel(t)
+    return float(g @ t / (t @ t))
+
+
+def test_forward_is_torch():
+    flat, tok, lab = _case()
+    ce, _ = lm.forward(CFG, flat, tok, lab)
+    np.testing.assert_allclose(ce, torch_forward(_t(flat), tok, lab).numpy(), rtol=1e-12, atol=1e-13)
+    assert lm.param_count(CFG) == flat.size
+    assert [s for _, s in lm.param_shapes(CFG)] == [s for _, s in synth.lm_param_layout(CFG.V, CFG.d, CFG.L,
+                                                                                          CFG.n, CFG.S)]
+
+
+def test_pass_rewards_are_torch_loss_differences():
+    flat, tok, lab = _case(2)
+    T, K, sigma = len(tok), 3, 0.05
+    ce0 = torch_forward(_t(flat), tok, lab).numpy()
+    for kind in lm.ACT_TYPES:
+        rew, _, _ = lm.activation_pass(CFG, flat, tok, lab, kind, K, sigma, SEED, draw_offset=5)
+        for i in range(K):
+            dl = {pt: _t(sigma * oracle.noise_block(SEED, li, 5 + i, 1, 0, T, w)[0]) for pt, li, w in _points(kind)}
+            np.testing.assert_allclose(rew[i], ce0 - torch_forward(_t(flat), tok, lab, deltas=dl).numpy(),
+                                       rtol=1e-9, atol=1e-12)
+    # the head pass perturbs the model's own logits
+    hold = {}
+    torch_forward(_t(flat), tok, lab, hold=hold)
+    sig = dict.fromkeys(lm.ALL_TYPES, sigma)
+    _, info = lm.estimate(CFG, flat, tok, lab, 2, 1, sig, 1e-2, SEED)
+    z = hold["z"].detach().numpy()
+    a = oracle.noise_block(SEED, lm.LID_HEAD, 0, 2, 0, T, CFG.V)
+    yl = torch.as_tensor(lab, dtype=torch.long)
+    for i in range(2):
+        ce1 = F.cross_entropy(torch.from_numpy(z + sigma * a[i]), yl, reduction="none").numpy()
+        np.testing.assert_allclose(info["rew_head"][i], ce0 - ce1, rtol=1e-9, atol=1e-12)
+    # ES: each member's summed-loss change
+    for j in range(1):
+        eps = oracle.noise(SEED, lm.LID_ES, j, 0, 2 * CFG.L)
+        base = _split(_t(flat))["scal"]
+        for sgn, got in ((1, info["es_plus"][j]), (-1, info["es_minus"][j])):
+            want = (torch_forward(_t(flat), tok, lab, scal=base + sgn * 1e-2 * _t(eps)).sum() - ce0.sum()).item()
+            assert abs(got - want) <= 1e-9 * max(1.0, abs(want))
+
+
+def test_weight_gradients_are_the_outer_products():
+    """G_W = autograd of sum_t <g_hat_t, y_t(W)> for every linear (the embedding rows
+    gathered by token id and position)."""
+    flat, tok, lab = _case(3)
+    sig = dict.fromkeys(lm.ALL_TYPES, 0.02)
+    G, info = lm.estimate(CFG, flat, tok, lab, 3, 2, sig, 1e-2, SEED)
+    gh = info["ghat"]
+    W = _t(flat, grad=True)
+    p = _split(W)
+    hold = {}
+    torch_forward(W, tok, lab, hold=hold)
+    T = len(tok)
+    tok_t = torch.as_tensor(tok, dtype=torch.long)
+    tgt = (_t(gh[("emb",)]) * (p["emb"][tok_t] + p["pos"][torch.arange(T) % CFG.S])).sum()
+    _, c = lm.forward(CFG, flat, tok, lab)
+    for l in range(CFG.L):
+        u1, o = _t(c[f"u1_{l}"]), _t(c[f"o{l}"])
+        for kind in ("q", "k", "v"):
+            tgt = tgt + (_t(gh[(l, kind)]) * (u1 @ p[f"w{kind}{l}"].T)).sum()
+        tgt = tgt + (_t(gh[(l, "o")]) * (o @ p[f"wo{l}"].T)).sum()
+        tgt = tgt + (_t(gh[(l, "up")]) * (_t(c[f"u2_{l}"]) @ p[f"w1{l}"].T)).sum()
+        tgt = tgt + (_t(gh[(l, "down")]) * (_t(c[f"m{l}"]) @ p[f"w2{l}"].T)).sum()
+    tgt = tgt + (_t(gh[("head",)]) * (_t(c["uf"]) @ p["head"].T)).sum()
+    (gref,) = torch.autograd.grad(tgt, W)
+    gref = gref.numpy()
+    ns = 2 * CFG.L
+    np.testing.assert_allclose(G[:-ns], gref[:-ns], rtol=1e-10, atol=1e-12)
+
+
+def test_estimates_are_unbiased():
+    """Slope 1 of every estimate on its autograd target (sigma -> 0, K large)."""
+    flat, tok, lab = _case(4, scal=0.7)
+    K, M = 4000, 3000
+    sig = dict.fromkeys(lm.ALL_TYPES, 1e-4)
+    G, info = lm.estimate(CFG, flat, tok, lab, K, M, sig, 1e-3, SEED)
+    gh = info["ghat"]
+    p = _split(_t(flat))
+    for kind in lm.ACT_TYPES:
+        own = _own_token_grads(flat, tok, lab, kind)
+        for pt in own:
+            s = _slope(gh[pt], own[pt])
+            print(f"{pt}: slope {s:.3f}")
+            assert abs(s - 1.0) < 0.1
+    # error at the attention output: the own-loss gradient at o (slope 1)
+    T = len(tok)
+    own_o = _own_token_grads(flat, tok, lab, "o")
+    _, c = lm.forward(CFG, flat, tok, lab)
+    for l in range(CFG.L):
+        e_true = own_o[(l, "o")] @ p[f"wo{l}"].numpy()
+        s = _slope(info[f"e{l}"], e_true)
+        print(f"e{l}: slope {s:.3f}")
+        assert abs(s - 1.0) < 0.1
+        # attention internals: gradient of sum <e_true, o(W)> at the clean input
+        u1 = _t(c[f"u1_{l}"])
+        Wq, Wk, Wv = (_t(flat_w, grad=True) for flat_w in (p[f"wq{l}"].numpy(), p[f"wk{l}"].numpy(),
+                                                            p[f"wv{l}"].numpy()))
+        obj = (_t(e_true) * _attn(u1 @ Wq.T, u1 @ Wk.T, u1 @ Wv.T)).sum()
+        targets = torch.autograd.grad(obj, [Wq, Wk, Wv])
+        Gd = lm.unpack(CFG, G)
+        for kind, tg in zip(("q", "k", "v"), targets):
+            s = _slope(Gd[f"w{kind}{l}"], tg.numpy())
+            print(f"w{kind}{l}: slope {s:.3f}")
+            assert abs(s - 1.0) < 0.15
+    # residual scalars: gradient of the summed loss
+    sc = _t(p["scal"].numpy(), grad=True)
+    (gs,) = torch.autograd.grad(torch_forward(_t(flat), tok, lab, scal=sc).sum(), sc)
+    s = _slope(lm.unpack(CFG, G)["scal"], gs.numpy())
+    print(f"scalars: slope {s:.3f}")
+    assert abs(s - 1.0) < 0.1
+    assert T == 16
+
+
+def test_sgd_momentum_is_torch():
+    rng = np.random.default_rng(5)
+    n = lm.param_count(CFG)
+    theta = rng.standard_normal(n)
+    mom = np.zeros(n)
+    w = torch.tensor(theta[:-2 * CFG.L].copy(), requires_grad=True)
+    s = torch.tensor(theta[-2 * CFG.L:].copy(), requires_grad=True)
+    opt = torch.optim.SGD([{"params": [w]}, {"params": [s], "lr": 0.3}], lr=0.05, momentum=0.9)
+    for _ in range(3):
+        G = rng.standard_normal(n)
+        theta, mom = lm.sgd_momentum(CFG, theta, mom, G, 0.05, 0.3, 0.9)
+        w.grad, s.grad = torch.tensor(G[:-2 * CFG.L]), torch.tensor(G[-2 * CFG.L:])
+        opt.step()
+    np.testing.assert_allclose(theta, np.concatenate([w.detach().numpy(), s.detach().numpy()]), rtol=1e-12,
+                               atol=1e-14)
