@@ -241,6 +241,89 @@ dust_status dust_estimate_attn_v(const float *q, const float *k, const float *e,
                                  uint32_t draw_offset, float *grad_w, float *ghat, float *rewards,
                                  void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * One full Dust update step on a small causal language model.
+ * Method: TL;DR page "Dust: zeroth-order Transformer pretraining without backprop",
+ * section 1, "reducing interference" (each layer type jittered in a forward pass of
+ * its own with its own noise scale; attention internals with only the attention output
+ * recomputed; the head on cached logits) and "credit assignment without backprop"
+ * (g_hat, G_W); section 2, "pretraining results" (SGD with momentum); iitog.ru page,
+ * mechanics paragraph (every weight by the per-token estimator except the 2L residual
+ * mixing scalars, which weight-space ES trains).
+ *
+ * Model (a reading; the pages give no architecture): tokens t = b S + s of B sequences
+ * of S tokens; x_0 = E[token] + P[s]; L pre-LN blocks
+ *     x <- x + alpha_l W_O attn(LN(x) W_Q^T, LN(x) W_K^T, LN(x) W_V^T)
+ *     x <- x + beta_l  W_2 GELU(W_1 LN(x))
+ * then LN, logits z = W_head LN(x), cross-entropy against the next-token label.  Causal
+ * attention within each sequence, heads of 64 channels (d = 64 H), scale 1/8;
+ * exact-erf GELU; LayerNorm without affine, eps = ln_eps; no biases.
+ *
+ * Parameters: one packed fp32 vector, in this order, weights [out, in] row-major:
+ *     E [V, d], P [S, d], then per block l: W_Q [d, d], W_K [d, d], W_V [d, d],
+ *     W_O [d, d], W_1 [n, d], W_2 [d, n]; then W_head [V, d]; then the scalars
+ *     alpha_0, beta_0, alpha_1, beta_1, ... (2L).
+ * dust_lm_param_count gives its length (0 for an invalid config).
+ *
+ * One step, all estimates at the same parameters:
+ *   head   dust_estimate_head on the cached logits (sigma_head, noise layer 2);
+ *   emb, o, up, down   one pass per linear type: every point of that type (the embedding
+ *          sum x_0; each block's W_O, W_1 or W_2 output) perturbed by sigma a in the same
+ *          draw, the rest of the network recomputed, r_t = CE_t - CE'_t (the token's own
+ *          loss); noise layer 1 for the embedding, 16 (l + 1) + {3, 4, 5} for o, up, down;
+ *          G_E[v] = sum of g_hat over tokens equal to v, G_P[s] = sum over sequences;
+ *   q, k, v   dust_estimate_attn per block with the error at the attention output
+ *          e_l = g_hat_O,l W_O,l (noise layer 16 (l + 1) + {0, 1, 2});
+ *   scalars   antithetic ES with M pairs on the summed loss: member 2j is s + sigma_es eps_j,
+ *          member 2j + 1 is s - sigma_es eps_j, eps_j[c] = the noise of (token 0, channel c,
+ *          draw j, layer 3); g = (1/(2 M sigma_es)) sum_j (L_2j - L_2j+1) eps_j.
+ * Each perturbed forward is evaluated as the change of every activation against the
+ * cached clean pass (no difference of two losses is taken), over chunks of draws.
+ * Then SGD with momentum: m <- momentum m + G; theta <- theta - lr m (lr_scalar for the
+ * 2L scalars).
+ *
+ * Arguments (device pointers unless stated):
+ *   cfg, hp : host structs.   tokens, labels : int32 [B S] ids in [0, V) (trusted: an
+ *   out-of-range id is clamped, never read out of bounds).   seed : noise key.
+ *   grads   : OUT float [param_count] the estimates G, packed like the parameters.
+ *   rewards : OUT float [dust_lm_rewards_count] or NULL: each pass's rewards [K, T] in
+ *             the order head, emb, o, up, down, then per block q, k, v; then the 2M
+ *             members' summed-loss changes L(member) - L(clean), member 2j then 2j + 1.
+ *   ce      : OUT float [T] the clean per-token cross-entropy (dust_lm_forward).
+ * Supported: 1 <= H <= 16, S a multiple of 64 up to 4096, n a multiple of 64 up to 65536,
+ * 1 <= V <= 32768, 1 <= L <= 32, K >= 1, M >= 1; every sigma > 0.
+ * Workspace: dust_lm_workspace_bytes(cfg, hp) bytes (the clean cache, the change tensors
+ * of one chunk of draws (at most 1 GiB, at least one draw), the rewards and the
+ * estimators' own scratch); dust_lm_forward needs the same query's size.
+ */
+typedef struct {
+    int32_t V, d, H, L, n, S, B;
+    float ln_eps;
+} dust_lm_config;
+
+typedef struct {
+    int32_t K, M;
+    float sigma_emb, sigma_q, sigma_k, sigma_v, sigma_o, sigma_up, sigma_down, sigma_head, sigma_es;
+    float lr, lr_scalar, momentum;
+} dust_lm_hparams;
+
+size_t dust_lm_param_count(const dust_lm_config *cfg);
+size_t dust_lm_rewards_count(const dust_lm_config *cfg, const dust_lm_hparams *hp);
+size_t dust_lm_workspace_bytes(const dust_lm_config *cfg, const dust_lm_hparams *hp);
+dust_status dust_lm_forward(const dust_lm_config *cfg, const float *params, const int32_t *tokens,
+                            const int32_t *labels, float *ce, void *workspace, size_t workspace_bytes,
+                            void *stream);
+dust_status dust_lm_estimate(const dust_lm_config *cfg, const dust_lm_hparams *hp, const float *params,
+                             const int32_t *tokens, const int32_t *labels, uint64_t seed, float *grads,
+                             float *rewards, void *workspace, size_t workspace_bytes, void *stream);
+/* m <- momentum m + grads; params <- params - lr m (lr_scalar on the last 2L entries). */
+dust_status dust_lm_sgd(const dust_lm_config *cfg, const dust_lm_hparams *hp, float *params, float *momentum,
+                        const float *grads, void *stream);
+/* dust_lm_estimate followed by dust_lm_sgd. */
+dust_status dust_lm_step(const dust_lm_config *cfg, const dust_lm_hparams *hp, float *params, float *momentum,
+                         const int32_t *tokens, const int32_t *labels, uint64_t seed, float *grads,
+                         float *rewards, void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

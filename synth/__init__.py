@@ -147,6 +147,8 @@ WORKLOADS = {
     4: dict(kind="head", T=8192, V=50304, d=1024, K=16, sigma=5e-3, labels="zipf", logits_dtype="bf16"),
     5: dict(kind="linear", T=2048, d=512, n=2048, V=8192, K=(64, 256, 1024, 4096, 16384), sigma=1e-2),
     6: dict(kind="attn_v", B=2, S=2048, H=8, K=64, sigma=1e-2),
+    # one full Dust step of a 2M-class causal LM (2.5M parameters): every pass K draws
+    7: dict(kind="lm", V=8192, d=128, H=2, L=2, n=512, S=256, B=4, K=64, M=32, sigma=1e-2, sigma_es=1e-2),
 }
 
 
@@ -157,6 +159,11 @@ def workload(i: int, matmul=None) -> dict:
         case = head_case(w["T"], w["V"], w["d"], seed=1000 + i, labels=w["labels"],
                          logits_dtype=w["logits_dtype"], matmul=matmul)
         case["layer"] = HEAD_LAYER
+    elif w["kind"] == "lm":
+        case = lm_case(w["V"], w["d"], w["H"], w["L"], w["n"], w["S"], w["B"], seed=1000 + i)
+        case.update(K=w["K"], M=w["M"], sigma=w["sigma"], sigma_es=w["sigma_es"], seed_noise=LM_NOISE_SEED,
+                    kind="lm")
+        return case
     elif w["kind"] == "attn_v":
         case = attn_case(w["B"], w["S"], w["H"], seed=1000 + i, matmul=matmul)
         case["layer"] = WV_LAYER

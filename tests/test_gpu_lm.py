@@ -1,0 +1,147 @@
+"""GPU parity of the full Dust step on a small causal LM against its oracle.
+
+Small models element by element: the clean per-token loss; every pass's rewards (head,
+embedding, W_O, W_1, W_2 outputs, q/k/v per block) and the ES members' loss changes; every
+packed gradient estimate; the parameters and momentum after SGD.  Cases: one and two heads,
+one and two blocks, one and two query tiles per sequence, a vocabulary that is not a multiple
+of 64, and a large noise scale (changes past the small-argument branches).  The 2M-class
+shape the benchmark times (V 8192, d 128, 2 blocks, 4 x 256 tokens, K 64 over three chunks of
+draws, 32 ES pairs): rewards of sampled draws and members against the oracle draw by draw.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import zeroth_order_activation_amd as dust
+from gpu_cases import dev, rel_l2
+from oracle import lm
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3  # relative L2, fp32 path
+
+SEED = 0x4455535400000040
+
+
+def _setup(V, d, H, L, n, S, B, seed, scal=1.0):
+    c = synth.lm_case(V, d, H, L, n, S, B, seed=seed, scal=scal)
+    cfg = dust.lm_config(V, d, H, L, n, S, B)
+    ocfg = lm.LMConfig(V, d, H, L, n, S)
+    return c, cfg, ocfg, dev(c["params"]), dev(c["tokens"]), dev(c["labels"])
+
+
+CASES = [
+    # V, d, H, L, n, S, B, K, M, sigma
+    (100, 64, 1, 2, 128, 128, 2, 5, 3, 2e-2),   # two query tiles, two blocks, ragged V
+    (64, 128, 2, 1, 256, 64, 3, 4, 2, 1e-2),    # two heads, one block
+    (70, 64, 1, 1, 64, 64, 2, 3, 2, 0.3),       # large changes: exp - 1 and erfc branches
+]
+
+
+def test_clean_forward_loss():
+    for (V, d, H, L, n, S, B, *_), seed in zip(CASES, (1, 2, 3)):
+        c, cfg, ocfg, p, tok, lab = _setup(V, d, H, L, n, S, B, seed)
+        ce = dust.lm_forward(cfg, p, tok, lab)
+        torch.cuda.synchronize()
+        ref, _ = lm.forward(ocfg, c["params"], c["tokens"], c["labels"])
+        e = rel_l2(ce.cpu().numpy(), ref)
+        print(f"V={V} d={d} L={L} S={S}: clean CE rel {e:.2e}")
+        assert e < 1e-5
+
+
+def _slices(ocfg):
+    out, o = {}, 0
+    for name, shp in lm.param_shapes(ocfg):
+        m = int(np.prod(shp))
+        out[name] = slice(o, o + m)
+        o += m
+    return out
+
+
+@pytest.mark.parametrize("V,d,H,L,n,S,B,K,M,sigma", CASES)
+def test_estimate_elementwise(V, d, H, L, n, S, B, K, M, sigma):
+    c, cfg, ocfg, p, tok, lab = _setup(V, d, H, L, n, S, B, seed=11 + V, scal=0.8)
+    hp = dust.lm_hparams(K, M, sigma, 2e-2)
+    rew = torch.empty(dust.lm_rewards_count(cfg, hp), dtype=torch.float32, device="cuda")
+    G = dust.lm_estimate(cfg, hp, p, tok, lab, SEED, rewards=rew)
+    G2 = dust.lm_estimate(cfg, hp, p, tok, lab, SEED)
+    torch.cuda.synchronize()
+    assert torch.equal(G, G2)  # deterministic
+    sig = dict.fromkeys(lm.ALL_TYPES, sigma)
+    og, info = lm.estimate(ocfg, c["params"], c["tokens"], c["labels"], K, M, sig, 2e-2, SEED)
+    T = B * S
+    KT = K * T
+    r = rew.cpu().numpy()
+    names = ["head", "emb", "o", "up", "down"] + [f"{k}{l}" for l in range(L) for k in ("q", "k", "v")]
+    worst = 0.0
+    for j, nm in enumerate(names):
+        e = rel_l2(r[j * KT:(j + 1) * KT].reshape(K, T), info["rew_" + nm])
+        worst = max(worst, e)
+        assert e < TOL, (nm, e)
+    dl = r[len(names) * KT:]
+    e_es = rel_l2(dl, np.stack([info["es_plus"], info["es_minus"]], axis=1).reshape(-1))
+    assert e_es < TOL, e_es
+    g = G.cpu().numpy()
+    gw = 0.0
+    for name, sl in _slices(ocfg).items():
+        e = rel_l2(g[sl], og[sl])
+        gw = max(gw, e)
+        assert e < TOL, (name, e)
+    print(f"V={V} d={d} L={L} S={S} K={K} sigma={sigma}: rewards {worst:.2e}, ES {e_es:.2e}, gradients {gw:.2e}")
+
+
+def test_step_updates_parameters_and_momentum():
+    V, d, H, L, n, S, B, K, M = 100, 64, 1, 2, 128, 128, 2, 4, 2
+    c, cfg, ocfg, p, tok, lab = _setup(V, d, H, L, n, S, B, seed=7, scal=0.9)
+    hp = dust.lm_hparams(K, M, 2e-2, 2e-2, lr=0.05, lr_scalar=0.01, momentum=0.9)
+    rng = np.random.default_rng(8)
+    mom0 = rng.standard_normal(c["params"].size).astype(np.float32) * 0.1
+    mom = dev(mom0)
+    p0 = p.clone()
+    G = dust.lm_step(cfg, hp, p, mom, tok, lab, SEED)
+    torch.cuda.synchronize()
+    sig = dict.fromkeys(lm.ALL_TYPES, 2e-2)
+    th, m2, og, _ = lm.step(ocfg, c["params"], mom0, c["tokens"], c["labels"], K, M, sig, 2e-2, SEED, 0.05, 0.01,
+                            0.9)
+    e_g = rel_l2(G.cpu().numpy(), og)
+    e_m = rel_l2(mom.cpu().numpy(), m2)
+    e_u = rel_l2((p - p0).cpu().numpy(), th - c["params"].astype(np.float64))
+    print(f"step: grads {e_g:.2e} momentum {e_m:.2e} update {e_u:.2e}")
+    assert e_g < TOL and e_m < TOL and e_u < TOL
+
+
+def test_bench_shape_on_sampled_draws():
+    """The 2M-class shape: V 8192, d 128 (2 heads), 2 blocks, n 512, 4 x 256 tokens,
+    K = 64 (three chunks of draws), 32 ES pairs: rewards of sampled draws of every
+    layer-type pass and of sampled ES members against the oracle, draw by draw."""
+    w = synth.WORKLOADS[7]
+    c, cfg, ocfg, p, tok, lab = _setup(w["V"], w["d"], w["H"], w["L"], w["n"], w["S"], w["B"], seed=1007)
+    K, M, sigma, ses = w["K"], w["M"], w["sigma"], w["sigma_es"]
+    hp = dust.lm_hparams(K, M, sigma, ses)
+    rew = torch.empty(dust.lm_rewards_count(cfg, hp), dtype=torch.float32, device="cuda")
+    dust.lm_estimate(cfg, hp, p, tok, lab, synth.LM_NOISE_SEED, rewards=rew)
+    torch.cuda.synchronize()
+    r = rew.cpu().numpy()
+    T = w["B"] * w["S"]
+    KT = K * T
+    errs = []
+    for j, kind in enumerate(lm.ACT_TYPES):
+        for i in (0, 27, K - 1):  # first, middle and last chunk of draws
+            orw, _, _ = lm.activation_pass(ocfg, c["params"], c["tokens"], c["labels"], kind, 1, sigma,
+                                           synth.LM_NOISE_SEED, draw_offset=i)
+            e = rel_l2(r[(1 + j) * KT + i * T:(1 + j) * KT + (i + 1) * T], orw[0])
+            errs.append(e)
+            assert e < TOL, (kind, i, e)
+    ce0 = lm.forward(ocfg, c["params"], c["tokens"], c["labels"])[0].sum()
+    base = lm.unpack(ocfg, c["params"])["scal"].astype(np.float64)
+    dl = r[(5 + 3 * w["L"]) * KT:]
+    for jm in (0, 1, 2 * M - 1):
+        eps = oracle.noise(synth.LM_NOISE_SEED, lm.LID_ES, jm // 2, 0, 2 * w["L"])
+        sc = base + (ses if jm % 2 == 0 else -ses) * eps
+        want = lm.forward(ocfg, c["params"], c["tokens"], c["labels"], scal=sc)[0].sum() - ce0
+        e = abs(dl[jm] - want) / abs(want)
+        errs.append(e)
+        assert e < TOL, (jm, e)
+    print(f"2M-class shape: sampled rewards worst rel {max(errs):.2e}")

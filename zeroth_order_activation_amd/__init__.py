@@ -83,6 +83,19 @@ def lib():
         L.dust_estimate_linear.restype = ctypes.c_int
         L.dust_estimate_linear.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32,
                                            _f32, _u64, _u32, _u32, _u32, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        for nm in ("dust_lm_param_count", "dust_lm_rewards_count", "dust_lm_workspace_bytes"):
+            getattr(L, nm).restype = ctypes.c_size_t
+        L.dust_lm_param_count.argtypes = [_vp]
+        L.dust_lm_rewards_count.argtypes = [_vp, _vp]
+        L.dust_lm_workspace_bytes.argtypes = [_vp, _vp]
+        L.dust_lm_forward.restype = ctypes.c_int
+        L.dust_lm_forward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.dust_lm_estimate.restype = ctypes.c_int
+        L.dust_lm_estimate.argtypes = [_vp, _vp, _vp, _vp, _vp, _u64, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.dust_lm_sgd.restype = ctypes.c_int
+        L.dust_lm_sgd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp]
+        L.dust_lm_step.restype = ctypes.c_int
+        L.dust_lm_step.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _u64, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         _lib = L
     return _lib
 
@@ -321,3 +334,97 @@ def estimate_attn(proj: str, q, k, v, e, u, S: int, H: int, K: int, sigma: float
                                     layer, token_offset, draw_offset, _p(grad_w), _p(ghat), _p(rewards), _p(ws), nb,
                                     _stream(q)))
     return grad_w
+
+
+# ---- one full Dust step on a small causal LM (see dust_lm_* in dust.h) ----------------
+class LMConfig(ctypes.Structure):
+    """dust_lm_config: V, d = 64 H, H, L blocks, MLP width n, sequence length S, batch B."""
+    _fields_ = [("V", ctypes.c_int32), ("d", ctypes.c_int32), ("H", ctypes.c_int32), ("L", ctypes.c_int32),
+                ("n", ctypes.c_int32), ("S", ctypes.c_int32), ("B", ctypes.c_int32), ("ln_eps", ctypes.c_float)]
+
+
+class LMHparams(ctypes.Structure):
+    """dust_lm_hparams: draws per pass K, ES pairs M, the noise scale of every pass,
+    the SGD-momentum settings."""
+    _fields_ = [("K", ctypes.c_int32), ("M", ctypes.c_int32)] + [
+        (nm, ctypes.c_float) for nm in ("sigma_emb", "sigma_q", "sigma_k", "sigma_v", "sigma_o", "sigma_up",
+                                        "sigma_down", "sigma_head", "sigma_es", "lr", "lr_scalar", "momentum")]
+
+
+LM_TYPES = ("emb", "q", "k", "v", "o", "up", "down", "head")
+
+
+def lm_config(V: int, d: int, H: int, L: int, n: int, S: int, B: int, ln_eps: float = 1e-5) -> LMConfig:
+    return LMConfig(V, d, H, L, n, S, B, ln_eps)
+
+
+def lm_hparams(K: int, M: int, sigma, sigma_es: float, lr: float = 0.0, lr_scalar: float = 0.0,
+               momentum: float = 0.0) -> LMHparams:
+    """``sigma``: one noise scale for every pass, or a dict over LM_TYPES."""
+    sg = sigma if isinstance(sigma, dict) else dict.fromkeys(LM_TYPES, float(sigma))
+    return LMHparams(K, M, *(sg[t] for t in LM_TYPES), sigma_es, lr, lr_scalar, momentum)
+
+
+def lm_param_count(cfg: LMConfig) -> int:
+    return int(lib().dust_lm_param_count(ctypes.byref(cfg)))
+
+
+def lm_rewards_count(cfg: LMConfig, hp: LMHparams) -> int:
+    return int(lib().dust_lm_rewards_count(ctypes.byref(cfg), ctypes.byref(hp)))
+
+
+def lm_workspace_bytes(cfg: LMConfig, hp: LMHparams | None = None) -> int:
+    return int(lib().dust_lm_workspace_bytes(ctypes.byref(cfg), None if hp is None else ctypes.byref(hp)))
+
+
+def _lm_inputs(cfg, params, tokens, labels):
+    _dev_tensor(params, "params", (torch.float32,))
+    _dev_tensor(tokens, "tokens", (torch.int32,))
+    _dev_tensor(labels, "labels", (torch.int32,))
+    T = cfg.B * cfg.S
+    if params.numel() != lm_param_count(cfg) or tokens.numel() != T or labels.numel() != T:
+        raise ValueError("params must hold dust_lm_param_count floats, tokens and labels B*S ids")
+
+
+def lm_forward(cfg: LMConfig, params, tokens, labels, *, ce=None, workspace=None):
+    """Clean per-token cross-entropy [B*S] of the model."""
+    _lm_inputs(cfg, params, tokens, labels)
+    if ce is None:
+        ce = torch.empty(cfg.B * cfg.S, dtype=torch.float32, device=params.device)
+    ws, nb = _workspace(lm_workspace_bytes(cfg), params.device, workspace)
+    _check(lib().dust_lm_forward(ctypes.byref(cfg), _p(params), _p(tokens), _p(labels), _p(ce), _p(ws), nb,
+                                 _stream(params)))
+    return ce
+
+
+def lm_estimate(cfg: LMConfig, hp: LMHparams, params, tokens, labels, seed: int, *, grads=None, rewards=None,
+                workspace=None):
+    """Every gradient estimate of one Dust step, packed like the parameters."""
+    _lm_inputs(cfg, params, tokens, labels)
+    if grads is None:
+        grads = torch.empty_like(params)
+    ws, nb = _workspace(lm_workspace_bytes(cfg, hp), params.device, workspace)
+    _check(lib().dust_lm_estimate(ctypes.byref(cfg), ctypes.byref(hp), _p(params), _p(tokens), _p(labels), seed,
+                                  _p(grads), _p(rewards), _p(ws), nb, _stream(params)))
+    return grads
+
+
+def lm_sgd(cfg: LMConfig, hp: LMHparams, params, momentum, grads) -> None:
+    """m <- momentum m + grads; params <- params - lr m (lr_scalar on the 2L scalars)."""
+    for t, nm in ((params, "params"), (momentum, "momentum"), (grads, "grads")):
+        _dev_tensor(t, nm, (torch.float32,))
+    _check(lib().dust_lm_sgd(ctypes.byref(cfg), ctypes.byref(hp), _p(params), _p(momentum), _p(grads),
+                             _stream(params)))
+
+
+def lm_step(cfg: LMConfig, hp: LMHparams, params, momentum, tokens, labels, seed: int, *, grads=None, rewards=None,
+            workspace=None):
+    """One Dust update in place on params and momentum; returns the estimates."""
+    _lm_inputs(cfg, params, tokens, labels)
+    _dev_tensor(momentum, "momentum", (torch.float32,))
+    if grads is None:
+        grads = torch.empty_like(params)
+    ws, nb = _workspace(lm_workspace_bytes(cfg, hp), params.device, workspace)
+    _check(lib().dust_lm_step(ctypes.byref(cfg), ctypes.byref(hp), _p(params), _p(momentum), _p(tokens), _p(labels),
+                              seed, _p(grads), _p(rewards), _p(ws), nb, _stream(params)))
+    return grads

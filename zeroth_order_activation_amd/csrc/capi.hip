@@ -434,3 +434,447 @@ dust_status dust_estimate_attn_v(const float* q, const float* k, const float* e,
     return dust_estimate_attn(DUST_ATTN_V, q, k, nullptr, e, u, T, S, d, H, K, sigma, seed, layer, token_offset,
                               draw_offset, grad_w, ghat, rewards, workspace, workspace_bytes, stream);
 }
+
+// ---- one full Dust step on a small causal LM -----------------------------------------
+namespace {
+
+constexpr uint32_t kLmLidEmb = 1, kLmLidHead = 2, kLmLidEs = 3;
+constexpr int kLmMaxL = 32;
+constexpr size_t kLmChunkBytes = size_t(1) << 30;  // change tensors of one chunk of draws
+
+// noise layer word of block l's linear: 0 q, 1 k, 2 v, 3 o, 4 up, 5 down
+uint32_t lm_lid(int64_t l, int kind) { return 16u * (uint32_t)(l + 1) + (uint32_t)kind; }
+
+struct LmDims {
+    int64_t V, d, H, L, n, S, B, T;
+    float eps;
+};
+
+dust_status lm_check_cfg(const dust_lm_config* c, LmDims& D, const char* who) {
+    if (!c) return fail(DUST_E_INVALID, "%s: cfg is NULL", who);
+    if (c->H < 1 || c->H > 16 || c->d != 64 * c->H)
+        return fail(DUST_E_UNSUPPORTED, "%s: heads of 64 channels, 1 <= H <= 16 and d = 64 H (got d=%d H=%d)", who,
+                    c->d, c->H);
+    if (c->S < 64 || c->S % 64 != 0 || c->S > 4096)
+        return fail(DUST_E_UNSUPPORTED, "%s: S must be a multiple of 64 in [64, 4096] (got %d)", who, c->S);
+    if (c->n < 64 || c->n % 64 != 0 || c->n > 65536)
+        return fail(DUST_E_UNSUPPORTED, "%s: n must be a multiple of 64 in [64, 65536] (got %d)", who, c->n);
+    if (c->V < 1 || c->V > 32768) return fail(DUST_E_UNSUPPORTED, "%s: V must be in [1, 32768] (got %d)", who, c->V);
+    if (c->L < 1 || c->L > kLmMaxL) return fail(DUST_E_UNSUPPORTED, "%s: L must be in [1, 32] (got %d)", who, c->L);
+    if (c->B < 1 || (int64_t)c->B * c->S > (int64_t(1) << 24))
+        return fail(DUST_E_INVALID, "%s: B must be >= 1 with B S <= 2^24 (got B=%d)", who, c->B);
+    if (!std::isfinite(c->ln_eps) || !(c->ln_eps > 0.f))
+        return fail(DUST_E_INVALID, "%s: ln_eps must be finite and > 0", who);
+    D = {c->V, c->d, c->H, c->L, c->n, c->S, c->B, (int64_t)c->B * c->S, c->ln_eps};
+    return ok();
+}
+
+dust_status lm_check_hp(const dust_lm_hparams* h, const char* who, bool step) {
+    if (!h) return fail(DUST_E_INVALID, "%s: hp is NULL", who);
+    if (h->K < 1 || h->K > (1 << 24) || h->M < 1 || h->M > (1 << 24))
+        return fail(DUST_E_INVALID, "%s: K and M must be in [1, 2^24] (got K=%d M=%d)", who, h->K, h->M);
+    const float s[9] = {h->sigma_emb, h->sigma_q,    h->sigma_k,    h->sigma_v, h->sigma_o,
+                        h->sigma_up,  h->sigma_down, h->sigma_head, h->sigma_es};
+    for (float v : s)
+        if (!std::isfinite(v) || !(v > 0.f)) return fail(DUST_E_INVALID, "%s: every sigma must be finite and > 0", who);
+    if (step && !(std::isfinite(h->lr) && std::isfinite(h->lr_scalar) && std::isfinite(h->momentum)))
+        return fail(DUST_E_INVALID, "%s: lr, lr_scalar and momentum must be finite", who);
+    return ok();
+}
+
+struct LmParams {
+    int64_t d, n, emb, pos, layer0, per_layer, head, scal, count;
+    int64_t wq(int64_t l) const { return layer0 + l * per_layer; }
+    int64_t wo(int64_t l) const { return wq(l) + 3 * d * d; }
+    int64_t w1(int64_t l) const { return wq(l) + 4 * d * d; }
+    int64_t w2(int64_t l) const { return w1(l) + n * d; }
+};
+
+LmParams lm_params(const LmDims& D) {
+    LmParams P;
+    P.d = D.d;
+    P.n = D.n;
+    P.emb = 0;
+    P.pos = D.V * D.d;
+    P.layer0 = P.pos + D.S * D.d;
+    P.per_layer = 4 * D.d * D.d + 2 * D.n * D.d;
+    P.head = P.layer0 + D.L * P.per_layer;
+    P.scal = P.head + D.V * D.d;
+    P.count = P.scal + 2 * D.L;
+    return P;
+}
+
+struct LmLayout {
+    int64_t kc;
+    size_t X[kLmMaxL + 1], U1[kLmMaxL], Q[kLmMaxL], Kk[kLmMaxL], Vv[kLmMaxL], O[kLmMaxL], BA[kLmMaxL], XM[kLmMaxL],
+        U2[kLmMaxL], BM[kLmMaxL], Hh[kLmMaxL], Mm[kLmMaxL], MU1[kLmMaxL], RS1[kLmMaxL], MU2[kLmMaxL], RS2[kLmMaxL],
+        LSE[kLmMaxL], GO[kLmMaxL], GUP[kLmMaxL], GDN[kLmMaxL];
+    size_t UF, MUF, RSF, Z, LSEZ, CE;
+    size_t DX, DU, DQ, DK, DV, DO, DB, DH, DM, DZ;
+    size_t REWS, REWES, DL, GE, E, WOT, SUB, sub_bytes, total;
+};
+
+size_t lm_rewards_count(const LmDims& D, int64_t K, int64_t M) {
+    return (size_t)((5 + 3 * D.L) * K * D.T + 2 * M);
+}
+
+LmLayout lm_layout(const LmDims& D, int64_t K, int64_t M) {
+    LmLayout L{};
+    size_t off = 0;
+    auto take = [&](int64_t floats) {
+        const size_t o = off;
+        off += round_up((size_t)floats * sizeof(float));
+        return o;
+    };
+    const int64_t T = D.T, d = D.d, n = D.n;
+    for (int64_t l = 0; l < D.L; ++l) {
+        L.X[l] = take(T * d);
+        L.U1[l] = take(T * d);
+        L.Q[l] = take(T * d);
+        L.Kk[l] = take(T * d);
+        L.Vv[l] = take(T * d);
+        L.O[l] = take(T * d);
+        L.BA[l] = take(T * d);
+        L.XM[l] = take(T * d);
+        L.U2[l] = take(T * d);
+        L.BM[l] = take(T * d);
+        L.Hh[l] = take(T * n);
+        L.Mm[l] = take(T * n);
+        L.MU1[l] = take(T);
+        L.RS1[l] = take(T);
+        L.MU2[l] = take(T);
+        L.RS2[l] = take(T);
+        L.LSE[l] = take(T * D.H);
+        L.GO[l] = take(T * d);
+        L.GUP[l] = take(T * n);
+        L.GDN[l] = take(T * d);
+    }
+    L.X[D.L] = take(T * d);
+    L.UF = take(T * d);
+    L.MUF = take(T);
+    L.RSF = take(T);
+    L.Z = take(T * D.V);
+    L.LSEZ = take(T);
+    L.CE = take(T);
+    const int64_t per_draw = T * (7 * d + 2 * n + D.V) * (int64_t)sizeof(float);
+    L.kc = std::max<int64_t>(1, std::min<int64_t>(std::max(K, 2 * M), (int64_t)kLmChunkBytes / per_draw));
+    const int64_t R = L.kc * T;
+    L.DX = take(R * d);
+    L.DU = take(R * d);
+    L.DQ = take(R * d);
+    L.DK = take(R * d);
+    L.DV = take(R * d);
+    L.DO = take(R * d);
+    L.DB = take(R * d);
+    L.DH = take(R * n);
+    L.DM = take(R * n);
+    L.DZ = take(R * D.V);
+    L.REWS = take((int64_t)lm_rewards_count(D, K, M));
+    L.REWES = take(2 * M * T);
+    L.DL = take(2 * M);
+    L.GE = take(T * d);
+    L.E = take(T * d);
+    L.WOT = take(d * d);
+    size_t sub = dust_head_workspace_bytes(T, D.V, d, K);
+    for (int p = 0; p < 3; ++p) sub = std::max(sub, dust_attn_workspace_bytes(p, T, D.S, d, D.H, K));
+    sub = std::max({sub, dust::outer_workspace_bytes(T, d, d), dust::outer_workspace_bytes(T, n, d),
+                    dust::outer_workspace_bytes(T, d, n)});
+    L.sub_bytes = round_up(sub);
+    L.SUB = off;
+    off += L.sub_bytes;
+    L.total = off;
+    return L;
+}
+
+struct LmRun {
+    LmDims D;
+    LmParams P;
+    const LmLayout* L;
+    unsigned char* ws;
+    hipStream_t st;
+    const float* prm;
+    const int32_t* tok;
+    const int32_t* lab;
+    float* f(size_t off) const { return reinterpret_cast<float*>(ws + off); }
+};
+
+#define LM_TRY(x)                           \
+    do {                                    \
+        const hipError_t e_ = (x);          \
+        if (e_ != hipSuccess) return e_;    \
+    } while (0)
+
+hipError_t lm_clean_forward(const LmRun& R) {
+    const LmDims& D = R.D;
+    const LmLayout& L = *R.L;
+    const int T = (int)D.T, d = (int)D.d, n = (int)D.n;
+    const hipStream_t st = R.st;
+    const float* p = R.prm;
+    LM_TRY(dust::lm_embed(p + R.P.emb, p + R.P.pos, R.tok, T, (int)D.S, d, (int)D.V, R.f(L.X[0]), st));
+    for (int64_t l = 0; l < D.L; ++l) {
+        const int64_t wq = R.P.wq(l);
+        LM_TRY(dust::lm_layernorm(R.f(L.X[l]), T, d, D.eps, R.f(L.U1[l]), R.f(L.MU1[l]), R.f(L.RS1[l]), st));
+        LM_TRY(dust::lm_gemm_nt(R.f(L.U1[l]), p + wq, R.f(L.Q[l]), T, d, d, nullptr, false, st));
+        LM_TRY(dust::lm_gemm_nt(R.f(L.U1[l]), p + wq + D.d * D.d, R.f(L.Kk[l]), T, d, d, nullptr, false, st));
+        LM_TRY(dust::lm_gemm_nt(R.f(L.U1[l]), p + wq + 2 * D.d * D.d, R.f(L.Vv[l]), T, d, d, nullptr, false, st));
+        LM_TRY(dust::lm_attn_fwd(R.f(L.Q[l]), R.f(L.Kk[l]), R.f(L.Vv[l]), T, (int)D.S, (int)D.H, R.f(L.O[l]),
+                                 R.f(L.LSE[l]), st));
+        LM_TRY(dust::lm_gemm_nt(R.f(L.O[l]), p + R.P.wo(l), R.f(L.BA[l]), T, d, d, nullptr, false, st));
+        LM_TRY(dust::lm_residual(R.f(L.X[l]), R.f(L.BA[l]), p + R.P.scal + 2 * l, D.T * D.d, R.f(L.XM[l]), st));
+        LM_TRY(dust::lm_layernorm(R.f(L.XM[l]), T, d, D.eps, R.f(L.U2[l]), R.f(L.MU2[l]), R.f(L.RS2[l]), st));
+        LM_TRY(dust::lm_gemm_nt(R.f(L.U2[l]), p + R.P.w1(l), R.f(L.Hh[l]), T, n, d, nullptr, false, st));
+        LM_TRY(dust::lm_gelu(R.f(L.Hh[l]), D.T * D.n, R.f(L.Mm[l]), st));
+        LM_TRY(dust::lm_gemm_nt(R.f(L.Mm[l]), p + R.P.w2(l), R.f(L.BM[l]), T, d, n, nullptr, false, st));
+        LM_TRY(dust::lm_residual(R.f(L.XM[l]), R.f(L.BM[l]), p + R.P.scal + 2 * l + 1, D.T * D.d, R.f(L.X[l + 1]),
+                                 st));
+    }
+    LM_TRY(dust::lm_layernorm(R.f(L.X[D.L]), T, d, D.eps, R.f(L.UF), R.f(L.MUF), R.f(L.RSF), st));
+    LM_TRY(dust::lm_gemm_nt(R.f(L.UF), p + R.P.head, R.f(L.Z), T, D.V, d, nullptr, false, st));
+    return dust::lm_ce(R.f(L.Z), R.lab, T, (int)D.V, R.f(L.LSEZ), R.f(L.CE), st);
+}
+
+// One chunk of kn draws (or ES members from draw0) of a pass: kind 0 emb, 1 o, 2 up,
+// 3 down, 4 residual-scalar ES.  Writes the rewards -D_CE of rows i T + t to rew.
+hipError_t lm_delta_chunk(const LmRun& R, int kind, int kn, uint32_t draw0, float sigma, uint32_t k0, uint32_t k1,
+                          float* rew) {
+    const LmDims& D = R.D;
+    const LmLayout& L = *R.L;
+    const hipStream_t st = R.st;
+    const float* p = R.prm;
+    const int T = (int)D.T, d = (int)D.d, n = (int)D.n;
+    const int64_t rows = (int64_t)kn * D.T;
+    const bool es = kind == 4;
+    const float es_sigma = es ? sigma : 0.f;
+    float *DX = R.f(L.DX), *DU = R.f(L.DU), *DQ = R.f(L.DQ), *DK = R.f(L.DK), *DV = R.f(L.DV), *DO = R.f(L.DO),
+          *DB = R.f(L.DB), *DH = R.f(L.DH), *DM = R.f(L.DM), *DZ = R.f(L.DZ);
+    auto zero = [&](float* ptr, int64_t count) { return hipMemsetAsync(ptr, 0, (size_t)count * sizeof(float), st); };
+    bool live = false;  // whether DX holds a change yet
+    if (kind == 0) {
+        LM_TRY(zero(DX, rows * d));
+        LM_TRY(dust::lm_noise_add(DX, kn, T, d, sigma, k0, k1, kLmLidEmb, draw0, st));
+        live = true;
+    }
+    for (int64_t l = 0; l < D.L; ++l) {
+        const int64_t wq = R.P.wq(l);
+        if (live) {
+            LM_TRY(dust::lm_layernorm_delta(R.f(L.X[l]), R.f(L.MU1[l]), R.f(L.RS1[l]), DX, rows, T, d, DU, st));
+            LM_TRY(dust::lm_gemm_nt(DU, p + wq, DQ, rows, d, d, nullptr, false, st));
+            LM_TRY(dust::lm_gemm_nt(DU, p + wq + D.d * D.d, DK, rows, d, d, nullptr, false, st));
+            LM_TRY(dust::lm_gemm_nt(DU, p + wq + 2 * D.d * D.d, DV, rows, d, d, nullptr, false, st));
+            LM_TRY(dust::lm_attn_delta(R.f(L.Q[l]), R.f(L.Kk[l]), R.f(L.Vv[l]), R.f(L.O[l]), R.f(L.LSE[l]), DQ, DK,
+                                       DV, kn, T, (int)D.S, (int)D.H, DO, st));
+            LM_TRY(dust::lm_gemm_nt(DO, p + R.P.wo(l), DB, rows, d, d, nullptr, false, st));
+        } else if (kind == 1 || es) {
+            LM_TRY(zero(DB, rows * d));
+        }
+        if (kind == 1) LM_TRY(dust::lm_noise_add(DB, kn, T, d, sigma, k0, k1, lm_lid(l, 3), draw0, st));
+        if (live || kind == 1 || es) {
+            if (!live) LM_TRY(zero(DX, rows * d));
+            LM_TRY(dust::lm_residual_delta(DX, DB, R.f(L.BA[l]), p + R.P.scal, (int)(2 * l), kn, D.T * D.d, es_sigma,
+                                           draw0, k0, k1, kLmLidEs, st));
+            live = true;
+        }
+        if (live) {
+            LM_TRY(dust::lm_layernorm_delta(R.f(L.XM[l]), R.f(L.MU2[l]), R.f(L.RS2[l]), DX, rows, T, d, DU, st));
+            LM_TRY(dust::lm_gemm_nt(DU, p + R.P.w1(l), DH, rows, n, d, nullptr, false, st));
+        } else if (kind == 2) {
+            LM_TRY(zero(DH, rows * n));
+        }
+        if (kind == 2) LM_TRY(dust::lm_noise_add(DH, kn, T, n, sigma, k0, k1, lm_lid(l, 4), draw0, st));
+        const bool mlp = live || kind == 2;
+        if (mlp) {
+            LM_TRY(dust::lm_gelu_delta(R.f(L.Hh[l]), DH, D.T * D.n, rows * n, DM, st));
+            LM_TRY(dust::lm_gemm_nt(DM, p + R.P.w2(l), DB, rows, d, n, nullptr, false, st));
+        } else if (kind == 3) {
+            LM_TRY(zero(DB, rows * d));
+        }
+        if (kind == 3) LM_TRY(dust::lm_noise_add(DB, kn, T, d, sigma, k0, k1, lm_lid(l, 5), draw0, st));
+        if (mlp || kind == 3 || es) {
+            if (!live) LM_TRY(zero(DX, rows * d));
+            LM_TRY(dust::lm_residual_delta(DX, DB, R.f(L.BM[l]), p + R.P.scal, (int)(2 * l + 1), kn, D.T * D.d,
+                                           es_sigma, draw0, k0, k1, kLmLidEs, st));
+            live = true;
+        }
+    }
+    LM_TRY(dust::lm_layernorm_delta(R.f(L.X[D.L]), R.f(L.MUF), R.f(L.RSF), DX, rows, T, d, DU, st));
+    LM_TRY(dust::lm_gemm_nt(DU, p + R.P.head, DZ, rows, D.V, d, nullptr, false, st));
+    return dust::lm_ce_delta(R.f(L.Z), R.f(L.LSEZ), DZ, R.lab, kn, T, (int)D.V, rew, st);
+}
+
+dust_status lm_prepare(const dust_lm_config* cfg, const dust_lm_hparams* hp, const float* params,
+                       const int32_t* tokens, const int32_t* labels, void* workspace, size_t workspace_bytes,
+                       void* stream, const char* who, bool step, LmRun& R, LmLayout& L) {
+    dust_status s = lm_check_cfg(cfg, R.D, who);
+    if (s != DUST_OK) return s;
+    if (hp && (s = lm_check_hp(hp, who, step)) != DUST_OK) return s;
+    if (!params || !tokens || !labels) return fail(DUST_E_INVALID, "%s: params, tokens and labels must be non-NULL", who);
+    if (!aligned16(params)) return fail(DUST_E_INVALID, "%s: params must be 16-byte aligned", who);
+    L = lm_layout(R.D, hp ? hp->K : 1, hp ? hp->M : 1);
+    if (!workspace || workspace_bytes < L.total)
+        return fail(DUST_E_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", who, L.total,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(DUST_E_INVALID, "%s: workspace must be 16-byte aligned", who);
+    R.P = lm_params(R.D);
+    R.L = &L;
+    R.ws = static_cast<unsigned char*>(workspace);
+    R.st = static_cast<hipStream_t>(stream);
+    R.prm = params;
+    R.tok = tokens;
+    R.lab = labels;
+    return ok();
+}
+
+}  // namespace
+
+size_t dust_lm_param_count(const dust_lm_config* cfg) {
+    LmDims D;
+    if (lm_check_cfg(cfg, D, "dust_lm_param_count") != DUST_OK) return 0;
+    return (size_t)lm_params(D).count;
+}
+
+size_t dust_lm_rewards_count(const dust_lm_config* cfg, const dust_lm_hparams* hp) {
+    LmDims D;
+    if (lm_check_cfg(cfg, D, "dust_lm_rewards_count") != DUST_OK) return 0;
+    if (lm_check_hp(hp, "dust_lm_rewards_count", false) != DUST_OK) return 0;
+    return lm_rewards_count(D, hp->K, hp->M);
+}
+
+size_t dust_lm_workspace_bytes(const dust_lm_config* cfg, const dust_lm_hparams* hp) {
+    LmDims D;
+    if (lm_check_cfg(cfg, D, "dust_lm_workspace_bytes") != DUST_OK) return 0;
+    if (hp && lm_check_hp(hp, "dust_lm_workspace_bytes", false) != DUST_OK) return 0;
+    return lm_layout(D, hp ? hp->K : 1, hp ? hp->M : 1).total;
+}
+
+dust_status dust_lm_forward(const dust_lm_config* cfg, const float* params, const int32_t* tokens,
+                            const int32_t* labels, float* ce, void* workspace, size_t workspace_bytes, void* stream) {
+    LmRun R;
+    LmLayout L;
+    dust_status s = lm_prepare(cfg, nullptr, params, tokens, labels, workspace, workspace_bytes, stream,
+                               "dust_lm_forward", false, R, L);
+    if (s != DUST_OK) return s;
+    if (!ce) return fail(DUST_E_INVALID, "dust_lm_forward: ce must be non-NULL");
+    hipError_t e = lm_clean_forward(R);
+    if (e != hipSuccess) return device_fail("dust_lm_forward: forward", e);
+    e = hipMemcpyAsync(ce, R.f(L.CE), (size_t)R.D.T * sizeof(float), hipMemcpyDeviceToDevice, R.st);
+    if (e != hipSuccess) return device_fail("dust_lm_forward: copy", e);
+    return ok();
+}
+
+dust_status dust_lm_estimate(const dust_lm_config* cfg, const dust_lm_hparams* hp, const float* params,
+                             const int32_t* tokens, const int32_t* labels, uint64_t seed, float* grads,
+                             float* rewards, void* workspace, size_t workspace_bytes, void* stream) {
+    const char* who = "dust_lm_estimate";
+    if (!hp) return fail(DUST_E_INVALID, "%s: hp is NULL", who);
+    LmRun R;
+    LmLayout L;
+    dust_status s = lm_prepare(cfg, hp, params, tokens, labels, workspace, workspace_bytes, stream, who, false, R, L);
+    if (s != DUST_OK) return s;
+    if (!grads || !aligned16(grads)) return fail(DUST_E_INVALID, "%s: grads must be non-NULL and 16-byte aligned", who);
+    if (rewards && !aligned16(rewards)) return fail(DUST_E_INVALID, "%s: rewards must be 16-byte aligned", who);
+    if (env_flag("DUST_DEBUG_CHECKS")) {
+        if ((s = check_labels(tokens, R.D.T, R.D.V, R.st)) != DUST_OK) return s;
+        if ((s = check_labels(labels, R.D.T, R.D.V, R.st)) != DUST_OK) return s;
+    }
+    const LmDims& D = R.D;
+    const LmParams& P = R.P;
+    const hipStream_t st = R.st;
+    const int64_t K = hp->K, M = hp->M, T = D.T, KT = K * T;
+    const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+    unsigned char* sub = R.ws + L.SUB;
+    float* rw = rewards ? rewards : R.f(L.REWS);
+    hipError_t e = lm_clean_forward(R);
+    if (e != hipSuccess) return device_fail("dust_lm_estimate: clean forward", e);
+    // head on the cached logits
+    s = dust_estimate_head(R.f(L.Z), DUST_F32, R.f(L.UF), labels, T, D.V, D.d, K, hp->sigma_head, seed, kLmLidHead,
+                           0, 0, grads + P.head, nullptr, rw, sub, L.sub_bytes, stream);
+    if (s != DUST_OK) return s;
+    // one pass per linear type, the network recomputed as changes
+    const float sig[4] = {hp->sigma_emb, hp->sigma_o, hp->sigma_up, hp->sigma_down};
+    for (int kind = 0; kind < 4; ++kind) {
+        float* r = rw + (1 + kind) * KT;
+        for (int64_t i0 = 0; i0 < K; i0 += L.kc) {
+            const int kn = (int)std::min<int64_t>(L.kc, K - i0);
+            if ((e = lm_delta_chunk(R, kind, kn, (uint32_t)i0, sig[kind], k0, k1, r + i0 * T)) != hipSuccess)
+                return device_fail("dust_lm_estimate: perturbed pass", e);
+        }
+        const float scale = -1.0f / ((float)K * sig[kind]);
+        for (int64_t l = 0; l < (kind == 0 ? 1 : D.L); ++l) {
+            if (kind == 0) {
+                e = dust::lm_ghat(r, (int)K, (int)T, (int)D.d, scale, k0, k1, kLmLidEmb, R.f(L.GE), st);
+                if (e == hipSuccess)
+                    e = dust::lm_embed_grads(R.f(L.GE), tokens, (int)T, (int)D.S, (int)D.V, (int)D.d, grads + P.emb,
+                                             grads + P.pos, st);
+            } else if (kind == 1) {
+                e = dust::lm_ghat(r, (int)K, (int)T, (int)D.d, scale, k0, k1, lm_lid(l, 3), R.f(L.GO[l]), st);
+                if (e == hipSuccess)
+                    e = dust::launch_outer(R.f(L.GO[l]), R.f(L.O[l]), T, D.d, D.d, grads + P.wo(l), sub, L.sub_bytes,
+                                           st, false);
+            } else if (kind == 2) {
+                e = dust::lm_ghat(r, (int)K, (int)T, (int)D.n, scale, k0, k1, lm_lid(l, 4), R.f(L.GUP[l]), st);
+                if (e == hipSuccess)
+                    e = dust::launch_outer(R.f(L.GUP[l]), R.f(L.U2[l]), T, D.n, D.d, grads + P.w1(l), sub,
+                                           L.sub_bytes, st, false);
+            } else {
+                e = dust::lm_ghat(r, (int)K, (int)T, (int)D.d, scale, k0, k1, lm_lid(l, 5), R.f(L.GDN[l]), st);
+                if (e == hipSuccess)
+                    e = dust::launch_outer(R.f(L.GDN[l]), R.f(L.Mm[l]), T, D.d, D.n, grads + P.w2(l), sub,
+                                           L.sub_bytes, st, false);
+            }
+            if (e != hipSuccess) return device_fail("dust_lm_estimate: g_hat / outer product", e);
+        }
+    }
+    // attention internals, with the error at the attention output e = g_hat_O W_O
+    const float sqkv[3] = {hp->sigma_q, hp->sigma_k, hp->sigma_v};
+    for (int64_t l = 0; l < D.L; ++l) {
+        e = dust::lm_transpose(params + P.wo(l), (int)D.d, (int)D.d, R.f(L.WOT), st);
+        if (e == hipSuccess) e = dust::lm_gemm_nt(R.f(L.GO[l]), R.f(L.WOT), R.f(L.E), T, D.d, D.d, nullptr, false, st);
+        if (e != hipSuccess) return device_fail("dust_lm_estimate: attention-output error", e);
+        for (int proj = 0; proj < 3; ++proj) {
+            s = dust_estimate_attn(proj, R.f(L.Q[l]), R.f(L.Kk[l]), R.f(L.Vv[l]), R.f(L.E), R.f(L.U1[l]), T, D.S, D.d,
+                                   D.H, K, sqkv[proj], seed, lm_lid(l, proj), 0, 0, grads + P.wq(l) + proj * D.d * D.d,
+                                   nullptr, rw + (5 + 3 * l + proj) * KT, sub, L.sub_bytes, stream);
+            if (s != DUST_OK) return s;
+        }
+    }
+    // residual scalars: antithetic weight-space ES
+    float* res = R.f(L.REWES);
+    for (int64_t m0 = 0; m0 < 2 * M; m0 += L.kc) {
+        const int kn = (int)std::min<int64_t>(L.kc, 2 * M - m0);
+        if ((e = lm_delta_chunk(R, 4, kn, (uint32_t)m0, hp->sigma_es, k0, k1, res + m0 * T)) != hipSuccess)
+            return device_fail("dust_lm_estimate: ES pass", e);
+    }
+    float* dL = rewards ? rewards + (5 + 3 * D.L) * KT : R.f(L.DL);
+    e = dust::lm_member_losses(res, (int)(2 * M), (int)T, dL, st);
+    if (e == hipSuccess)
+        e = dust::lm_es_grad(dL, (int)M, (int)(2 * D.L), 1.0f / (2.0f * (float)M * hp->sigma_es), k0, k1, kLmLidEs,
+                             grads + P.scal, st);
+    if (e != hipSuccess) return device_fail("dust_lm_estimate: ES gradient", e);
+    return ok();
+}
+
+dust_status dust_lm_sgd(const dust_lm_config* cfg, const dust_lm_hparams* hp, float* params, float* momentum,
+                        const float* grads, void* stream) {
+    LmDims D;
+    dust_status s = lm_check_cfg(cfg, D, "dust_lm_sgd");
+    if (s != DUST_OK) return s;
+    if ((s = lm_check_hp(hp, "dust_lm_sgd", true)) != DUST_OK) return s;
+    if (!params || !momentum || !grads) return fail(DUST_E_INVALID, "dust_lm_sgd: params, momentum and grads must be non-NULL");
+    const LmParams P = lm_params(D);
+    const hipError_t e = dust::lm_sgd(params, momentum, grads, P.count, P.scal, hp->lr, hp->lr_scalar, hp->momentum,
+                                      static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_fail("dust_lm_sgd", e);
+    return ok();
+}
+
+dust_status dust_lm_step(const dust_lm_config* cfg, const dust_lm_hparams* hp, float* params, float* momentum,
+                         const int32_t* tokens, const int32_t* labels, uint64_t seed, float* grads, float* rewards,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    if (!hp) return fail(DUST_E_INVALID, "dust_lm_step: hp is NULL");
+    dust_status s = lm_check_hp(hp, "dust_lm_step", true);
+    if (s != DUST_OK) return s;
+    if (!momentum) return fail(DUST_E_INVALID, "dust_lm_step: momentum must be non-NULL");
+    s = dust_lm_estimate(cfg, hp, params, tokens, labels, seed, grads, rewards, workspace, workspace_bytes, stream);
+    if (s != DUST_OK) return s;
+    return dust_lm_sgd(cfg, hp, params, momentum, grads, stream);
+}

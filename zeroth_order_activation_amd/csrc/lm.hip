@@ -1,0 +1,657 @@
+// Kernels of the full Dust step on a small causal LM: the clean forward with
+// its cached intermediates, and the change-propagating forward that every
+// layer-type pass and the residual-scalar ES pass run over a chunk of draws.
+//
+// Method: TL;DR page "Dust: zeroth-order Transformer pretraining without
+// backprop", section 1, "reducing interference" (each layer type jittered in a
+// forward pass of its own, with its own noise scale; the rest cached) and
+// "credit assignment without backprop" (reward = the token's loss reduction);
+// iitog.ru page, mechanics paragraph (the 2L residual mixing scalars by
+// weight-space ES).  The model (pre-LN blocks x <- x + alpha W_O attn(...),
+// x <- x + beta W_2 GELU(W_1 LN(x)), final LN, head) is this library's reading.
+//
+// A perturbed forward is carried as the change D = x' - x of every activation
+// relative to the cached clean pass, never as a second forward whose loss is
+// subtracted from the clean one:
+//   linear      D_y = D_x W^T                                  (exact)
+//   LayerNorm   D_u = c rs (1 + f) + (x - mu) rs f,  c = D - mean(D),
+//               f = (1 + dv rs^2)^(-1/2) - 1 = expm1(-log1p(dv rs^2) / 2),
+//               dv = 2 mean((x - mu) c) + mean(c^2)
+//   GELU        D_m = D_h Phi(h + D_h) + h (Phi(h + D_h) - Phi(h)), the
+//               difference of Phi by Simpson's rule for |D_h| < 1/4, else by
+//               complementary error functions of one sign
+//   attention   P' = P e^delta / (1 + rho), rho = sum_t P expm1(delta),
+//               D_o = (sum_t P expm1(delta) v_t + sum_t P e^delta D_v_t - rho o) / (1 + rho)
+//   CE          D_CE = log1p(sum_v p_v expm1(D_z_v)) - D_z_y
+// so every reward keeps fp32 relative accuracy however small it is.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "dust_device.hpp"
+#include "dust_internal.hpp"
+
+namespace dust {
+namespace {
+
+typedef float lf32x16 __attribute__((ext_vector_type(16)));
+
+// ---- GEMM  C (=|+=) alpha A B^T,  A [M, K], B [N, K] row-major, fp32 MFMA ------------
+constexpr int GB = 64, GK = 16;
+
+__global__ void __launch_bounds__(256) lm_gemm_nt_kernel(const float* __restrict__ A, const float* __restrict__ B,
+                                                         float* __restrict__ C, int M, int N, int K,
+                                                         const float* __restrict__ alpha, int accumulate) {
+    __shared__ float As[GK][GB + 4];
+    __shared__ float Bs[GK][GB + 4];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w & 1, wn = w >> 1;
+    const int64_t m0 = (int64_t)blockIdx.x * GB, n0 = (int64_t)blockIdx.y * GB;
+    const int lr = tid >> 2, lk = (tid & 3) * 4;  // loader: row of the tile, 4 consecutive k
+    const float* ap = A + (m0 + lr) * (int64_t)K + lk;
+    const bool bok = n0 + lr < N;
+    const float* bp = B + (bok ? (n0 + lr) : 0) * (int64_t)K + lk;
+    lf32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    float4 ra = *reinterpret_cast<const float4*>(ap);
+    float4 rb = bok ? *reinterpret_cast<const float4*>(bp) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k0 = 0; k0 < K; k0 += GK) {
+        __syncthreads();
+        As[lk + 0][lr] = ra.x;
+        As[lk + 1][lr] = ra.y;
+        As[lk + 2][lr] = ra.z;
+        As[lk + 3][lr] = ra.w;
+        Bs[lk + 0][lr] = rb.x;
+        Bs[lk + 1][lr] = rb.y;
+        Bs[lk + 2][lr] = rb.z;
+        Bs[lk + 3][lr] = rb.w;
+        __syncthreads();
+        if (k0 + GK < K) {  // next k-step's operands, in flight during the MFMAs
+            ra = *reinterpret_cast<const float4*>(ap + k0 + GK);
+            if (bok) rb = *reinterpret_cast<const float4*>(bp + k0 + GK);
+        }
+#pragma unroll
+        for (int kk = 0; kk < GK; kk += 2) {
+            const int k = kk + (lane >> 5);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[k][wm * 32 + (lane & 31)], Bs[k][wn * 32 + (lane & 31)],
+                                                       acc, 0, 0, 0);
+        }
+    }
+    // D[i][j] of the 32x32 block: lane j + 32 ((i / 4) % 2), register (i % 4) + 4 (i / 8)
+    const float al = alpha ? *alpha : 1.0f;
+    const int64_t col = n0 + wn * 32 + (lane & 31);
+    if (col < N) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int64_t row = m0 + wm * 32 + (r & 3) + 8 * (r >> 2) + 4 * (lane >> 5);
+            float* c = C + row * N + col;
+            *c = accumulate ? fmaf(al, acc[r], *c) : al * acc[r];
+        }
+    }
+}
+
+// ---- clean forward ------------------------------------------------------------
+__global__ void __launch_bounds__(256) lm_embed_kernel(const float* __restrict__ emb, const float* __restrict__ pos,
+                                                       const int32_t* __restrict__ tok, int T, int S, int d, int V,
+                                                       float* __restrict__ x) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // float index
+    if (i >= (int64_t)T * d) return;
+    const int t = (int)(i / d), c = (int)(i % d);
+    const int id = min(max(tok[t], 0), V - 1);  // an out-of-range id reads row 0 or V - 1, never outside
+    x[i] = emb[(int64_t)id * d + c] + pos[(int64_t)(t % S) * d + c];
+}
+
+// One wave per row of d = 64 E channels (E <= 16): lane holds channels lane + 64 e.
+constexpr int LNE = 16;
+
+__global__ void __launch_bounds__(256) lm_layernorm_kernel(const float* __restrict__ x, int R, int d, float eps,
+                                                           float* __restrict__ u, float* __restrict__ mu,
+                                                           float* __restrict__ rs) {
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63, E = d >> 6;
+    if (row >= R) return;
+    const float* xr = x + (int64_t)row * d;
+    float v[LNE], s = 0.f;
+#pragma unroll
+    for (int e = 0; e < LNE; ++e)
+        if (e < E) {
+            v[e] = xr[lane + 64 * e];
+            s += v[e];
+        }
+    const float m = wave_total(s) / (float)d;
+    float q = 0.f;
+#pragma unroll
+    for (int e = 0; e < LNE; ++e)
+        if (e < E) q = fmaf(v[e] - m, v[e] - m, q);
+    const float r = 1.0f / sqrtf(wave_total(q) / (float)d + eps);
+#pragma unroll
+    for (int e = 0; e < LNE; ++e)
+        if (e < E) u[(int64_t)row * d + lane + 64 * e] = (v[e] - m) * r;
+    if (lane == 0) {
+        mu[row] = m;
+        rs[row] = r;
+    }
+}
+
+// Causal attention of 64 queries x one head, 4 threads per query (16 channels
+// each); two passes over the keys: the row maximum, then p, sum p, sum p v.
+__device__ __forceinline__ float quad_total(float v) {
+    v += __shfl_xor(v, 1, 64);
+    return v + __shfl_xor(v, 2, 64);
+}
+
+__device__ __forceinline__ void load16(const float* p, float (&r)[16]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float4 f = *reinterpret_cast<const float4*>(p + 4 * j);
+        r[4 * j] = f.x;
+        r[4 * j + 1] = f.y;
+        r[4 * j + 2] = f.z;
+        r[4 * j + 3] = f.w;
+    }
+}
+
+__device__ __forceinline__ void stage_tile(float (*dst)[64], const float* src, int64_t row0, int d, int h) {
+    // 64 rows x 64 channels of head h: 1024 float4, 4 per thread
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int f = threadIdx.x + 256 * j, row = f >> 4, c4 = (f & 15) * 4;
+        *reinterpret_cast<float4*>(&dst[row][c4]) =
+            *reinterpret_cast<const float4*>(src + (row0 + row) * d + h * 64 + c4);
+    }
+}
+
+__global__ void __launch_bounds__(256) lm_attn_fwd_kernel(const float* __restrict__ q, const float* __restrict__ k,
+                                                          const float* __restrict__ v, int T, int S, int H,
+                                                          float* __restrict__ o, float* __restrict__ lse) {
+    __shared__ __align__(16) float Ks[64][64];
+    __shared__ __align__(16) float Vs[64][64];
+    const int nqt = S / 64, qt = blockIdx.x % nqt, bh = blockIdx.x / nqt, b = bh / H, h = bh % H;
+    const int d = 64 * H, ql = threadIdx.x >> 2, qr = threadIdx.x & 3;
+    const int64_t s0 = (int64_t)b * S, row = s0 + qt * 64 + ql;
+    float qv[16];
+    load16(q + row * d + h * 64 + qr * 16, qv);
+    float mx = -INFINITY;
+    for (int kt = 0; kt <= qt; ++kt) {
+        __syncthreads();
+        stage_tile(Ks, k, s0 + kt * 64, d, h);
+        __syncthreads();
+        for (int j = 0; j < 64; ++j) {
+            float dot = 0.f;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) dot = fmaf(qv[c], Ks[j][qr * 16 + c], dot);
+            dot = quad_total(dot) * 0.125f;
+            if (kt < qt || j <= ql) mx = fmaxf(mx, dot);
+        }
+    }
+    float s = 0.f, acc[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) acc[c] = 0.f;
+    for (int kt = 0; kt <= qt; ++kt) {
+        __syncthreads();
+        stage_tile(Ks, k, s0 + kt * 64, d, h);
+        stage_tile(Vs, v, s0 + kt * 64, d, h);
+        __syncthreads();
+        for (int j = 0; j < 64; ++j) {
+            float dot = 0.f;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) dot = fmaf(qv[c], Ks[j][qr * 16 + c], dot);
+            dot = quad_total(dot) * 0.125f;
+            const float p = (kt < qt || j <= ql) ? __expf(dot - mx) : 0.f;
+            s += p;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) acc[c] = fmaf(p, Vs[j][qr * 16 + c], acc[c]);
+        }
+    }
+    const float inv = 1.0f / s;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) o[row * d + h * 64 + qr * 16 + c] = acc[c] * inv;
+    if (qr == 0) lse[row * H + h] = mx + logf(s);
+}
+
+__device__ __forceinline__ float phi_cdf(float x) { return 0.5f * erfcf(-x * 0.70710678118654752f); }
+__device__ __forceinline__ float phi_pdf(float x) { return 0.39894228040143268f * __expf(-0.5f * x * x); }
+
+__global__ void __launch_bounds__(256) lm_gelu_kernel(const float* __restrict__ h, int64_t count,
+                                                      float* __restrict__ m) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < count) m[i] = h[i] * phi_cdf(h[i]);
+}
+
+// out = x + alpha b
+__global__ void __launch_bounds__(256) lm_residual_kernel(const float* __restrict__ x, const float* __restrict__ b,
+                                                          const float* __restrict__ alpha, int64_t count,
+                                                          float* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < count) out[i] = fmaf(*alpha, b[i], x[i]);
+}
+
+// Per row: lse = log sum exp z, ce = lse - z_label.  One workgroup per row.
+__device__ __forceinline__ float block_total(float v, float* red) {
+    v = wave_total(v);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+    v = wave_max(v);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+__global__ void __launch_bounds__(256) lm_ce_kernel(const float* __restrict__ z, const int32_t* __restrict__ labels,
+                                                    int V, float* __restrict__ lse, float* __restrict__ ce) {
+    __shared__ float red[4];
+    const int64_t t = blockIdx.x;
+    const float* zr = z + t * V;
+    float m = -INFINITY;
+    for (int j = threadIdx.x; j < V; j += 256) m = fmaxf(m, zr[j]);
+    m = block_max(m, red);
+    float s = 0.f;
+    for (int j = threadIdx.x; j < V; j += 256) s += __expf(zr[j] - m);
+    s = block_total(s, red);
+    if (threadIdx.x == 0) {
+        const float l = m + logf(s);
+        lse[t] = l;
+        ce[t] = l - zr[min(max(labels[t], 0), V - 1)];
+    }
+}
+
+// ---- change-propagating forward (rows r = i T + t for draw i of the chunk) --------
+// D[r][c] += sigma a(t, c, draw0 + i, layer)
+__global__ void __launch_bounds__(256) lm_noise_add_kernel(float* __restrict__ D, int kc, int T, int w, float sigma,
+                                                           uint32_t k0, uint32_t k1, uint32_t layer, uint32_t draw0) {
+    const int64_t qi = (int64_t)blockIdx.x * 256 + threadIdx.x;  // quad index
+    const int nq = w >> 2;
+    if (qi >= (int64_t)kc * T * nq) return;
+    const int64_t r = qi / nq;
+    const int cq = (int)(qi % nq), i = (int)(r / T), t = (int)(r % T);
+    const f32x4 a = gauss4((uint32_t)t, (uint32_t)cq, draw0 + (uint32_t)i, layer, k0, k1);
+    float4* p = reinterpret_cast<float4*>(D + r * w + 4 * cq);
+    float4 v = *p;
+    v.x = fmaf(sigma, a.v[0], v.x);
+    v.y = fmaf(sigma, a.v[1], v.y);
+    v.z = fmaf(sigma, a.v[2], v.z);
+    v.w = fmaf(sigma, a.v[3], v.w);
+    *p = v;
+}
+
+__global__ void __launch_bounds__(256) lm_layernorm_delta_kernel(const float* __restrict__ x,
+                                                                 const float* __restrict__ mu,
+                                                                 const float* __restrict__ rs,
+                                                                 const float* __restrict__ dx, int R, int T, int d,
+                                                                 float* __restrict__ du) {
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63, E = d >> 6;
+    if (row >= R) return;
+    const int t = row % T;
+    const float m = mu[t], r = rs[t];
+    float xc[LNE], c[LNE], s = 0.f;
+#pragma unroll
+    for (int e = 0; e < LNE; ++e)
+        if (e < E) {
+            xc[e] = x[(int64_t)t * d + lane + 64 * e] - m;
+            c[e] = dx[(int64_t)row * d + lane + 64 * e];
+            s += c[e];
+        }
+    const float dm = wave_total(s) / (float)d;
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < LNE; ++e)
+        if (e < E) {
+            c[e] -= dm;
+            s1 = fmaf(xc[e], c[e], s1);
+            s2 = fmaf(c[e], c[e], s2);
+        }
+    const float dv = (2.0f * wave_total(s1) + wave_total(s2)) / (float)d;
+    const float f = expm1f(-0.5f * log1pf(dv * r * r));  // rs' / rs - 1
+    const float a = r * (1.0f + f), bb = r * f;
+#pragma unroll
+    for (int e = 0; e < LNE; ++e)
+        if (e < E) du[(int64_t)row * d + lane + 64 * e] = fmaf(c[e], a, xc[e] * bb);
+}
+
+__device__ __forceinline__ float expm1_s(float x) {
+    if (fabsf(x) < 0.25f)
+        return x * fmaf(x, fmaf(x, fmaf(x, fmaf(x, fmaf(x, 1.0f / 720.0f, 1.0f / 120.0f), 1.0f / 24.0f),
+                                          1.0f / 6.0f), 0.5f), 1.0f);
+    return __expf(x) - 1.0f;
+}
+
+// Change of the attention output of 64 queries x one head for one draw:
+// D_o = (sum_t P expm1(delta) v_t + sum_t P e^delta D_v_t - rho o) / (1 + rho),
+// delta = (<D_q, k_t> + <q + D_q, D_k_t>) / 8.
+__global__ void __launch_bounds__(256) lm_attn_delta_kernel(const float* __restrict__ q, const float* __restrict__ k,
+                                                            const float* __restrict__ v, const float* __restrict__ o,
+                                                            const float* __restrict__ lse,
+                                                            const float* __restrict__ dq,
+                                                            const float* __restrict__ dk,
+                                                            const float* __restrict__ dv, int T, int S, int H,
+                                                            float* __restrict__ dout) {
+    __shared__ __align__(16) float Ks[64][64];
+    __shared__ __align__(16) float Vs[64][64];
+    __shared__ __align__(16) float DKs[64][64];
+    __shared__ __align__(16) float DVs[64][64];
+    const int nqt = S / 64, nbh = (T / S) * H;
+    const int qt = blockIdx.x % nqt, bh = (blockIdx.x / nqt) % nbh, i = blockIdx.x / (nqt * nbh);
+    const int b = bh / H, h = bh % H, d = 64 * H, ql = threadIdx.x >> 2, qr = threadIdx.x & 3;
+    const int64_t s0 = (int64_t)b * S, row = s0 + qt * 64 + ql, drow0 = (int64_t)i * T;
+    float qv[16], dqv[16], qq[16], acc[16];
+    load16(q + row * d + h * 64 + qr * 16, qv);
+    load16(dq + (drow0 + row) * d + h * 64 + qr * 16, dqv);
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        qq[c] = qv[c] + dqv[c];
+        acc[c] = 0.f;
+    }
+    const float l = lse[row * H + h];
+    float rho = 0.f;
+    for (int kt = 0; kt <= qt; ++kt) {
+        __syncthreads();
+        stage_tile(Ks, k, s0 + kt * 64, d, h);
+        stage_tile(Vs, v, s0 + kt * 64, d, h);
+        stage_tile(DKs, dk, drow0 + s0 + kt * 64, d, h);
+        stage_tile(DVs, dv, drow0 + s0 + kt * 64, d, h);
+        __syncthreads();
+        for (int j = 0; j < 64; ++j) {
+            float lg = 0.f, dl = 0.f;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) {
+                const float kc = Ks[j][qr * 16 + c];
+                lg = fmaf(qv[c], kc, lg);
+                dl = fmaf(dqv[c], kc, dl);
+                dl = fmaf(qq[c], DKs[j][qr * 16 + c], dl);
+            }
+            lg = quad_total(lg) * 0.125f;
+            dl = quad_total(dl) * 0.125f;
+            const bool on = kt < qt || j <= ql;  // keys after the query do not enter
+            const float p = on ? __expf(lg - l) : 0.f;
+            const float w1 = on ? p * expm1_s(dl) : 0.f, w2 = p + w1;
+            rho += w1;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) acc[c] = fmaf(w1, Vs[j][qr * 16 + c], fmaf(w2, DVs[j][qr * 16 + c], acc[c]));
+        }
+    }
+    float ov[16];
+    load16(o + row * d + h * 64 + qr * 16, ov);
+    const float inv = 1.0f / (1.0f + rho);
+#pragma unroll
+    for (int c = 0; c < 16; ++c) dout[(drow0 + row) * d + h * 64 + qr * 16 + c] = (acc[c] - rho * ov[c]) * inv;
+}
+
+// D_m = GELU(h + D_h) - GELU(h) = D_h Phi(h + D_h) + h (Phi(h + D_h) - Phi(h))
+__global__ void __launch_bounds__(256) lm_gelu_delta_kernel(const float* __restrict__ hc,
+                                                            const float* __restrict__ dh, int64_t per_draw,
+                                                            int64_t count, float* __restrict__ dm) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= count) return;
+    const float h = hc[i % per_draw], e = dh[i], h1 = h + e;
+    float dphi;
+    if (fabsf(e) < 0.25f) {
+        // Simpson's rule on the density: error below |e|^5 max|phi''''| / 2880
+        dphi = e * (1.0f / 6.0f) * (phi_pdf(h) + 4.0f * phi_pdf(h + 0.5f * e) + phi_pdf(h1));
+    } else if (h + 0.5f * e > 0.f) {  // upper tail: 1 - Phi by erfc
+        dphi = 0.5f * (erfcf(h * 0.70710678118654752f) - erfcf(h1 * 0.70710678118654752f));
+    } else {
+        dphi = 0.5f * (erfcf(-h1 * 0.70710678118654752f) - erfcf(-h * 0.70710678118654752f));
+    }
+    dm[i] = fmaf(e, phi_cdf(h1), h * dphi);
+}
+
+// dx += alpha db, plus for an ES member (es_sigma > 0) the change of the scalar:
+// + s sigma_es eps_{j, slot} (b + db), member m = member0 + i, j = m / 2, s = +1 / -1
+// for even / odd m, eps from the noise stream (token 0, channel slot, draw j).
+__global__ void __launch_bounds__(256) lm_residual_delta_kernel(float* __restrict__ dx, const float* __restrict__ db,
+                                                                const float* __restrict__ b,
+                                                                const float* __restrict__ scal, int slot, int kc,
+                                                                int64_t per_draw, float es_sigma, uint32_t member0,
+                                                                uint32_t k0, uint32_t k1, uint32_t es_layer) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (int64_t)kc * per_draw) return;
+    const float al = scal[slot];
+    float v = fmaf(al, db[idx], dx[idx]);
+    if (es_sigma > 0.f) {
+        const uint32_t m = member0 + (uint32_t)(idx / per_draw);
+        const f32x4 g = gauss4(0u, (uint32_t)(slot >> 2), m >> 1, es_layer, k0, k1);
+        const float coef = ((m & 1u) ? -es_sigma : es_sigma) * g.v[slot & 3];
+        v = fmaf(coef, b[idx % per_draw] + db[idx], v);
+    }
+    dx[idx] = v;
+}
+
+// rew[r] = -(log1p(sum_v p_v expm1(D_z_v)) - D_z_y),  p = exp(z - lse)
+__global__ void __launch_bounds__(256) lm_ce_delta_kernel(const float* __restrict__ z, const float* __restrict__ lse,
+                                                          const float* __restrict__ dz,
+                                                          const int32_t* __restrict__ labels, int T, int V,
+                                                          float* __restrict__ rew) {
+    __shared__ float red[4];
+    const int64_t r = blockIdx.x;
+    const int t = (int)(r % T);
+    const float* zr = z + (int64_t)t * V;
+    const float* dr = dz + r * V;
+    const float l = lse[t];
+    float s = 0.f;
+    for (int j = threadIdx.x; j < V; j += 256) s = fmaf(__expf(zr[j] - l), expm1f(dr[j]), s);
+    s = block_total(s, red);
+    if (threadIdx.x == 0) rew[r] = dr[min(max(labels[t], 0), V - 1)] - log1pf(s);
+}
+
+// g_hat[t][c] = scale sum_i rew[i][t] a(t, c, draw0 + i, layer)
+__global__ void __launch_bounds__(256) lm_ghat_kernel(const float* __restrict__ rew, int K, int T, int w, float scale,
+                                                      uint32_t k0, uint32_t k1, uint32_t layer,
+                                                      float* __restrict__ ghat) {
+    const int64_t qi = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int nq = w >> 2;
+    if (qi >= (int64_t)T * nq) return;
+    const int t = (int)(qi / nq), cq = (int)(qi % nq);
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+    for (int i = 0; i < K; ++i) {
+        const float r = rew[(int64_t)i * T + t];
+        const f32x4 a = gauss4((uint32_t)t, (uint32_t)cq, (uint32_t)i, layer, k0, k1);
+        s0 = fmaf(r, a.v[0], s0);
+        s1 = fmaf(r, a.v[1], s1);
+        s2 = fmaf(r, a.v[2], s2);
+        s3 = fmaf(r, a.v[3], s3);
+    }
+    *reinterpret_cast<float4*>(ghat + (int64_t)t * w + 4 * cq) = make_float4(s0 * scale, s1 * scale, s2 * scale,
+                                                                             s3 * scale);
+}
+
+// G_E[v] = sum over tokens equal to v of g_hat (one wave per vocabulary row and
+// 64-channel block, tokens in order); G_P[s] = sum over sequences of g_hat at s.
+__global__ void __launch_bounds__(64) lm_embed_grad_kernel(const float* __restrict__ ghat,
+                                                           const int32_t* __restrict__ tok, int T, int d,
+                                                           float* __restrict__ gemb) {
+    const int vrow = blockIdx.x, c = blockIdx.y * 64 + threadIdx.x;
+    float s = 0.f;
+    for (int t = 0; t < T; ++t)
+        if (tok[t] == vrow) s += ghat[(int64_t)t * d + c];
+    gemb[(int64_t)vrow * d + c] = s;
+}
+
+__global__ void __launch_bounds__(256) lm_pos_grad_kernel(const float* __restrict__ ghat, int T, int S, int d,
+                                                          float* __restrict__ gpos) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)S * d) return;
+    float s = 0.f;
+    for (int b = 0; b < T / S; ++b) s += ghat[(int64_t)b * S * d + i];
+    gpos[i] = s;
+}
+
+__global__ void __launch_bounds__(256) lm_transpose_kernel(const float* __restrict__ W, int R, int Cn,
+                                                           float* __restrict__ WT) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)R * Cn) return;
+    const int r = (int)(i / Cn), c = (int)(i % Cn);
+    WT[(int64_t)c * R + r] = W[i];
+}
+
+// dL[m] = -sum_t rew[m][t] (the member's summed-loss change), fixed order.
+__global__ void __launch_bounds__(256) lm_rowsum_neg_kernel(const float* __restrict__ rew, int T,
+                                                            float* __restrict__ out) {
+    __shared__ float red[4];
+    const int64_t m = blockIdx.x;
+    float s = 0.f;
+    for (int t = threadIdx.x; t < T; t += 256) s += rew[m * T + t];
+    s = block_total(s, red);
+    if (threadIdx.x == 0) out[m] = -s;
+}
+
+// g[c] = scale sum_j (dL[2j] - dL[2j+1]) eps_{j,c}
+__global__ void __launch_bounds__(64) lm_es_grad_kernel(const float* __restrict__ dL, int M, int nsc, float scale,
+                                                        uint32_t k0, uint32_t k1, uint32_t es_layer,
+                                                        float* __restrict__ g) {
+    const int c = threadIdx.x;
+    if (c >= nsc) return;
+    float s = 0.f;
+    for (int j = 0; j < M; ++j) {
+        const f32x4 e = gauss4(0u, (uint32_t)(c >> 2), (uint32_t)j, es_layer, k0, k1);
+        s = fmaf(dL[2 * j] - dL[2 * j + 1], e.v[c & 3], s);
+    }
+    g[c] = s * scale;
+}
+
+__global__ void __launch_bounds__(256) lm_sgd_kernel(float* __restrict__ theta, float* __restrict__ mom,
+                                                     const float* __restrict__ G, int64_t count, int64_t scal0,
+                                                     float lr, float lr_scalar, float mu) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= count) return;
+    const float m = fmaf(mu, mom[i], G[i]);
+    mom[i] = m;
+    theta[i] = fmaf(-(i >= scal0 ? lr_scalar : lr), m, theta[i]);
+}
+
+unsigned blocks(int64_t n, int per = 256) { return (unsigned)((n + per - 1) / per); }
+
+}  // namespace
+
+// ---- launchers (arguments validated by the caller) ------------------------------
+hipError_t lm_gemm_nt(const float* A, const float* B, float* C, int64_t M, int64_t N, int64_t K, const float* alpha,
+                      bool accumulate, hipStream_t s) {
+    hipLaunchKernelGGL(lm_gemm_nt_kernel, dim3((unsigned)(M / GB), (unsigned)((N + GB - 1) / GB)), dim3(256), 0, s,
+                       A, B, C, (int)M, (int)N, (int)K, alpha, accumulate ? 1 : 0);
+    return hipGetLastError();
+}
+
+hipError_t lm_embed(const float* emb, const float* pos, const int32_t* tok, int T, int S, int d, int V, float* x,
+                    hipStream_t s) {
+    hipLaunchKernelGGL(lm_embed_kernel, dim3(blocks((int64_t)T * d)), dim3(256), 0, s, emb, pos, tok, T, S, d, V, x);
+    return hipGetLastError();
+}
+
+hipError_t lm_layernorm(const float* x, int64_t R, int d, float eps, float* u, float* mu, float* rs, hipStream_t s) {
+    hipLaunchKernelGGL(lm_layernorm_kernel, dim3(blocks(R, 4)), dim3(256), 0, s, x, (int)R, d, eps, u, mu, rs);
+    return hipGetLastError();
+}
+
+hipError_t lm_attn_fwd(const float* q, const float* k, const float* v, int T, int S, int H, float* o, float* lse,
+                       hipStream_t s) {
+    hipLaunchKernelGGL(lm_attn_fwd_kernel, dim3((unsigned)((T / S) * H * (S / 64))), dim3(256), 0, s, q, k, v, T, S,
+                       H, o, lse);
+    return hipGetLastError();
+}
+
+hipError_t lm_gelu(const float* h, int64_t count, float* m, hipStream_t s) {
+    hipLaunchKernelGGL(lm_gelu_kernel, dim3(blocks(count)), dim3(256), 0, s, h, count, m);
+    return hipGetLastError();
+}
+
+hipError_t lm_residual(const float* x, const float* b, const float* alpha, int64_t count, float* out,
+                       hipStream_t s) {
+    hipLaunchKernelGGL(lm_residual_kernel, dim3(blocks(count)), dim3(256), 0, s, x, b, alpha, count, out);
+    return hipGetLastError();
+}
+
+hipError_t lm_ce(const float* z, const int32_t* labels, int T, int V, float* lse, float* ce, hipStream_t s) {
+    hipLaunchKernelGGL(lm_ce_kernel, dim3((unsigned)T), dim3(256), 0, s, z, labels, V, lse, ce);
+    return hipGetLastError();
+}
+
+hipError_t lm_noise_add(float* D, int kc, int T, int w, float sigma, uint32_t k0, uint32_t k1, uint32_t layer,
+                        uint32_t draw0, hipStream_t s) {
+    hipLaunchKernelGGL(lm_noise_add_kernel, dim3(blocks((int64_t)kc * T * (w / 4))), dim3(256), 0, s, D, kc, T, w,
+                       sigma, k0, k1, layer, draw0);
+    return hipGetLastError();
+}
+
+hipError_t lm_layernorm_delta(const float* x, const float* mu, const float* rs, const float* dx, int64_t R, int T,
+                              int d, float* du, hipStream_t s) {
+    hipLaunchKernelGGL(lm_layernorm_delta_kernel, dim3(blocks(R, 4)), dim3(256), 0, s, x, mu, rs, dx, (int)R, T, d,
+                       du);
+    return hipGetLastError();
+}
+
+hipError_t lm_attn_delta(const float* q, const float* k, const float* v, const float* o, const float* lse,
+                         const float* dq, const float* dk, const float* dv, int kc, int T, int S, int H, float* dout,
+                         hipStream_t s) {
+    hipLaunchKernelGGL(lm_attn_delta_kernel, dim3((unsigned)(kc * (T / S) * H * (S / 64))), dim3(256), 0, s, q, k, v,
+                       o, lse, dq, dk, dv, T, S, H, dout);
+    return hipGetLastError();
+}
+
+hipError_t lm_gelu_delta(const float* h, const float* dh, int64_t per_draw, int64_t count, float* dm,
+                         hipStream_t s) {
+    hipLaunchKernelGGL(lm_gelu_delta_kernel, dim3(blocks(count)), dim3(256), 0, s, h, dh, per_draw, count, dm);
+    return hipGetLastError();
+}
+
+hipError_t lm_residual_delta(float* dx, const float* db, const float* b, const float* scal, int slot, int kc,
+                             int64_t per_draw, float es_sigma, uint32_t member0, uint32_t k0, uint32_t k1,
+                             uint32_t es_layer, hipStream_t s) {
+    hipLaunchKernelGGL(lm_residual_delta_kernel, dim3(blocks((int64_t)kc * per_draw)), dim3(256), 0, s, dx, db, b,
+                       scal, slot, kc, per_draw, es_sigma, member0, k0, k1, es_layer);
+    return hipGetLastError();
+}
+
+hipError_t lm_ce_delta(const float* z, const float* lse, const float* dz, const int32_t* labels, int kc, int T, int V,
+                       float* rew, hipStream_t s) {
+    hipLaunchKernelGGL(lm_ce_delta_kernel, dim3((unsigned)((int64_t)kc * T)), dim3(256), 0, s, z, lse, dz, labels, T,
+                       V, rew);
+    return hipGetLastError();
+}
+
+hipError_t lm_ghat(const float* rew, int K, int T, int w, float scale, uint32_t k0, uint32_t k1, uint32_t layer,
+                   float* ghat, hipStream_t s) {
+    hipLaunchKernelGGL(lm_ghat_kernel, dim3(blocks((int64_t)T * (w / 4))), dim3(256), 0, s, rew, K, T, w, scale, k0,
+                       k1, layer, ghat);
+    return hipGetLastError();
+}
+
+hipError_t lm_embed_grads(const float* ghat, const int32_t* tok, int T, int S, int V, int d, float* gemb, float* gpos,
+                          hipStream_t s) {
+    hipLaunchKernelGGL(lm_embed_grad_kernel, dim3((unsigned)V, (unsigned)(d / 64)), dim3(64), 0, s, ghat, tok, T, d,
+                       gemb);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(lm_pos_grad_kernel, dim3(blocks((int64_t)S * d)), dim3(256), 0, s, ghat, T, S, d, gpos);
+    return hipGetLastError();
+}
+
+hipError_t lm_transpose(const float* W, int R, int C, float* WT, hipStream_t s) {
+    hipLaunchKernelGGL(lm_transpose_kernel, dim3(blocks((int64_t)R * C)), dim3(256), 0, s, W, R, C, WT);
+    return hipGetLastError();
+}
+
+hipError_t lm_member_losses(const float* rew, int members, int T, float* dL, hipStream_t s) {
+    hipLaunchKernelGGL(lm_rowsum_neg_kernel, dim3((unsigned)members), dim3(256), 0, s, rew, T, dL);
+    return hipGetLastError();
+}
+
+hipError_t lm_es_grad(const float* dL, int M, int nsc, float scale, uint32_t k0, uint32_t k1, uint32_t es_layer,
+                      float* g, hipStream_t s) {
+    hipLaunchKernelGGL(lm_es_grad_kernel, dim3(1), dim3(64), 0, s, dL, M, nsc, scale, k0, k1, es_layer, g);
+    return hipGetLastError();
+}
+
+hipError_t lm_sgd(float* theta, float* mom, const float* G, int64_t count, int64_t scal0, float lr, float lr_scalar,
+                  float mu, hipStream_t s) {
+    hipLaunchKernelGGL(lm_sgd_kernel, dim3(blocks(count)), dim3(256), 0, s, theta, mom, G, count, scal0, lr,
+                       lr_scalar, mu);
+    return hipGetLastError();
+}
+
+}  // namespace dust
