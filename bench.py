@@ -38,6 +38,7 @@ sys.path.insert(0, ROOT)
 # MI355X published peaks and unit counts.
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_F32_PEAK_TFLOPS = 157.3
 N_CU, CLOCK_GHZ, LANES_PER_CU = 256, 2.4, 64
 # 32-bit vector ALU: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3 T lane-ops/s.
 # The published fp32 vector figure, 157.3 TFLOP/s, is this times 2 (an FMA is two
@@ -81,6 +82,7 @@ KERNEL_SOURCES = {
     "attn_v_kernel": ["attn.hip", "dust_device.hpp", "dust_internal.hpp"],
     "attn_k_kernel": ["attn.hip", "dust_device.hpp", "dust_internal.hpp"],
     "attn_q_kernel": ["attn.hip", "dust_device.hpp", "dust_internal.hpp"],
+    "lm_gemm_nt_kernel": ["lm.hip", "dust_internal.hpp"],
 }
 
 
@@ -174,6 +176,9 @@ WORKLOAD_NAMES = {
     4: "243M-shape LM head bf16 logits: T=8192 (4x2048), d=1024, V=50304, K=16, sigma=5e-3, Zipf(1.1) labels",
     5: "MLP-linear population sweep point: T=2048, d=512, n=2048, V=8192, sigma=1e-2, K={K}",
     6: "attention {P} estimator, causal: T=4096 (2x2048), d=512, 8 heads of 64, K=64, sigma=1e-2",
+    7: "full Dust step of a 2M-class causal LM (2.5M parameters: V=8192, d=128, 2 heads, 2 blocks, n=512): "
+       "T=1024 (4x256), head + 4 layer-type passes + q/k/v per block, K=64 draws each, ES on the 4 residual "
+       "scalars with 32 antithetic pairs, sigma=1e-2, SGD with momentum",
 }
 
 
@@ -382,6 +387,115 @@ def cpu_baseline_attn(case, target_s, proj):
                       f"numpy fp64; rate extrapolated: work is linear in K), {el:.1f} s"}
 
 
+def cpu_baseline_lm(case, target_s):
+    """The oracle's full step on the workload with the first draws of every pass (and as
+    many ES pairs); the work is linear in K and M, so the rate is per token-draw."""
+    import oracle
+    from oracle import lm
+
+    ocfg = lm.LMConfig(case["V"], case["d"], case["H"], case["L"], case["n"], case["S"])
+    T, L = case["T"], case["L"]
+    sig = dict.fromkeys(lm.ALL_TYPES, case["sigma"])
+    kd = 1
+    while True:
+        t0 = time.perf_counter()
+        lm.estimate(ocfg, case["params"], case["tokens"], case["labels"], kd, kd, sig, case["sigma_es"],
+                    case["seed_noise"])
+        el = time.perf_counter() - t0
+        if el >= target_s / 3 or kd >= case["K"]:
+            break
+        kd = min(case["K"], int(kd * max(2.0, target_s / max(el, 1e-3))))
+    td = ((5 + 3 * L) * kd + 2 * kd) * T
+    return {"value": td / el, "unit": "token-draws/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"the full step on all {T} tokens with {kd} draws per pass and {kd} ES pairs "
+                      f"({td} token-draws: per draw a full fp64 forward in numpy for the layer-type and ES "
+                      f"passes, one causal attention for q/k/v, the C head estimator), {el:.1f} s"}
+
+
+def lm_gemm_flops(c):
+    """Flops of the GEMM launches of one step (2 x rows x out x in each): the clean
+    forward; per draw of each layer-type pass the blocks after its first perturbed
+    point (block 0 keeps only what follows the point) and the head; the ES members
+    likewise (block 0's attention branch has no change yet); e = g_hat_O W_O."""
+    T, d, n, V, L, K, M = c["T"], c["d"], c["n"], c["V"], c["L"], c["K"], c["M"]
+    attn, mlp, head = 2 * 4 * d * d, 2 * 2 * n * d, 2 * V * d
+    full = attn + mlp
+    first = {"emb": full, "o": mlp, "up": mlp // 2, "down": 0, "es": mlp}
+    per_draw = {k: v + (L - 1) * full + head for k, v in first.items()}
+    passes = K * T * (per_draw["emb"] + per_draw["o"] + per_draw["up"] + per_draw["down"])
+    return T * (L * full + head) + passes + 2 * M * T * per_draw["es"] + L * T * 2 * d * d
+
+
+def run_lm(args, c, dust, torch):
+    """Full Dust step: clean forward, head, the four layer-type passes, attention
+    internals, residual-scalar ES, SGD with momentum."""
+    cfg = dust.lm_config(c["V"], c["d"], c["H"], c["L"], c["n"], c["S"], c["B"])
+    # the estimates are gradients of the summed (not mean) loss over T tokens: small rates
+    hp = dust.lm_hparams(c["K"], c["M"], c["sigma"], c["sigma_es"], lr=1e-5, lr_scalar=1e-7, momentum=0.9)
+    params = torch.from_numpy(c["params"]).cuda()
+    tok = torch.from_numpy(c["tokens"]).cuda()
+    lab = torch.from_numpy(c["labels"]).cuda()
+    mom = torch.zeros_like(params)
+    grads = torch.empty_like(params)
+    ws = torch.empty(dust.lm_workspace_bytes(cfg, hp), dtype=torch.uint8, device="cuda")
+
+    def step():
+        dust.lm_step(cfg, hp, params, mom, tok, lab, c["seed_noise"], grads=grads, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    for el in ev:
+        for x in el:
+            x.record(stream)
+    gs = [torch.cuda.Event(enable_timing=True) for _ in range(2048)]
+    ge = [torch.cuda.Event(enable_timing=True) for _ in range(2048)]
+    for x in gs + ge:
+        x.record(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for kk in range(args.steps):
+        ev[kk][0].record(stream)
+        for j, st in enumerate((4, 5, 6, 7)):
+            dust.set_stage_event(st, ev[kk][1 + j])
+        if kk == args.steps - 1:  # the last timed step also times each GEMM launch
+            dust.set_gemm_events(gs, ge)
+        step()
+        ev[kk][5].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ngemm = dust.gemm_event_count()
+    dust.set_gemm_events(None, None)
+    for st in (4, 5, 6, 7):
+        dust.set_stage_event(st, None)
+    gemm_ms = float(sum(dust.event_elapsed_ms(gs[i], ge[i]) for i in range(ngemm)))
+    names = ("clean_forward", "head_pass", "layer_type_passes", "attention_internals", "es_and_sgd")
+    stages = {nm: float(np.mean([dust.event_elapsed_ms(x[j], x[j + 1]) for x in ev])) for j, nm in enumerate(names)}
+    ms_per_step = wall * 1e3 / args.steps
+    T, L = c["T"], c["L"]
+    td = ((5 + 3 * L) * c["K"] + 2 * c["M"]) * T
+    ce = dust.lm_forward(cfg, params, tok, lab)
+    torch.cuda.synchronize()
+    flops = lm_gemm_flops(c)
+    achieved = flops / (gemm_ms / 1e3) / 1e12
+    out = {
+        "dtype": "f32 (fp32 MFMA GEMMs)",
+        "token_draws_per_step": td,
+        "stages_ms": stages,
+        "loss_after": float(ce.mean()),
+        "roofline": {"bound": "mfma", "kernel": "lm_gemm_nt_kernel", "achieved": achieved,
+                     "peak": MFMA_F32_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / MFMA_F32_PEAK_TFLOPS,
+                     "traffic": load_traffic("lm_gemm_nt_kernel", args.workload),
+                     "flops_per_launch": flops / max(ngemm, 1), "launches_per_step": ngemm,
+                     "kernel_ms": gemm_ms / max(ngemm, 1), "kernel_ms_per_step": gemm_ms,
+                     "note": "fp32 MFMA flops of every GEMM launch of one step over the summed durations of "
+                             "those launches (HIP events around each launch of the last timed step)"},
+    }
+    return ms_per_step, td, out
+
+
 def run_attn(args, c, dust, torch):
     """Attention projection estimator: rewards (attention passes), g_hat, outer product."""
     T, S, d, H, K, sigma = c["T"], c["S"], c["d"], c["H"], c["K"], c["sigma"]
@@ -535,6 +649,11 @@ def main():
         if args.subset:
             cfg["workload"] = name + f"; vocabulary subset: window of {args.subset} channels per draw + label"
             cfg["subset_m"] = args.subset
+    elif c["kind"] == "lm":
+        ms, td, extra = run_lm(args, c, dust, torch)
+        cfg = {"workload": name, "T": c["T"], "V": c["V"], "d": c["d"], "H": c["H"], "L": c["L"], "n": c["n"],
+               "S": c["S"], "K": c["K"], "M": c["M"], "sigma": c["sigma"], "sigma_es": c["sigma_es"]}
+        c["layer"] = "per pass (1 embedding, 2 head, 3 ES, 16 (l + 1) + type)"
     elif c["kind"] == "attn_v":
         K = c["K"]
         name = name.format(P={"q": "query-projection (W_Q)", "k": "key-projection (W_K)",
@@ -550,7 +669,7 @@ def main():
     cfg.update({"noise_seed": c["seed_noise"], "layer": c["layer"], "data_seed": 1000 + args.workload})
     out = {
         "metric": "token-draws/sec per Dust gradient estimate; % of HBM BW / MFMA peak",
-        "value": c["T"] * K / (ms / 1e3),
+        "value": (td if c["kind"] == "lm" else c["T"] * K) / (ms / 1e3),
         "unit": "token-draws/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -565,7 +684,8 @@ def main():
     }
     out.update(extra)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = (cpu_baseline_head(c, args.cpu_seconds, args.subset) if c["kind"] == "head"
+        out["cpu_baseline"] = (cpu_baseline_lm(c, args.cpu_seconds) if c["kind"] == "lm"
+                               else cpu_baseline_head(c, args.cpu_seconds, args.subset) if c["kind"] == "head"
                                else cpu_baseline_attn(c, args.cpu_seconds, args.attn_proj) if c["kind"] == "attn_v"
                                else cpu_baseline_linear(c, K, args.cpu_seconds))
     print(json.dumps(out), flush=True)

@@ -80,10 +80,24 @@ const char *dust_last_error(void);
  * stage 1 = after the weight-gradient outer product; for dust_estimate_linear
  * also stage 2 = after the downstream GEMM1 (F = LN(x + W2 GELU(.))) and
  * stage 3 = after GEMM2 (logits and their per-tile log-sum-exp) of each row
- * chunk (the last chunk's record wins).  Pass NULL to clear.  The caller owns
- * the events.  Used to time the stages of one call.
+ * chunk (the last chunk's record wins); for dust_lm_estimate (and dust_lm_step)
+ * stage 4 = after the clean forward, 5 = after the head pass, 6 = after the
+ * layer-type passes, 7 = after the attention internals (the residual-scalar ES
+ * follows).  Pass NULL to clear.  The caller owns the events.  Used to time the
+ * stages of one call.
  */
 dust_status dust_set_stage_event(int stage, void *event);
+
+/*
+ * Profiling hook of the small-LM step (dust_lm_*): while set, each launch of its
+ * GEMM kernel (C = A B^T, fp32) from this thread records starts[i] before and
+ * ends[i] after it on the call's stream, i = 0, 1, ... for the first `capacity`
+ * launches (hipEvent_t handles owned by the caller; the arrays are copied).
+ * dust_gemm_event_count() returns how many launches were recorded since the hook
+ * was set.  NULL arrays or capacity <= 0 clear it.
+ */
+dust_status dust_set_gemm_events(void *const *starts, void *const *ends, int capacity);
+int dust_gemm_event_count(void);
 
 /*
  * Noise export: the exact Gaussian values (and optionally the raw Philox words)

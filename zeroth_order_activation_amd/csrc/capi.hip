@@ -14,7 +14,7 @@
 namespace {
 
 thread_local std::string g_err;
-thread_local hipEvent_t g_stage_event[4] = {nullptr, nullptr, nullptr, nullptr};
+thread_local hipEvent_t g_stage_event[8] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
 
 hipError_t record_stage(int stage, hipStream_t s) {
     return g_stage_event[stage] ? hipEventRecord(g_stage_event[stage], s) : hipSuccess;
@@ -84,10 +84,28 @@ int dust_abi_version(void) { return DUST_ABI_VERSION; }
 const char* dust_last_error(void) { return g_err.c_str(); }
 
 dust_status dust_set_stage_event(int stage, void* event) {
-    if (stage < 0 || stage > 3) return fail(DUST_E_INVALID, "dust_set_stage_event: stage must be in [0, 3]");
+    if (stage < 0 || stage > 7) return fail(DUST_E_INVALID, "dust_set_stage_event: stage must be in [0, 7]");
     g_stage_event[stage] = static_cast<hipEvent_t>(event);
     return ok();
 }
+
+dust_status dust_set_gemm_events(void* const* starts, void* const* ends, int capacity) {
+    static thread_local std::vector<hipEvent_t> s_starts, s_ends;
+    dust::LaunchEvents& le = dust::g_gemm_events;
+    if (!starts || !ends || capacity <= 0) {
+        le = dust::LaunchEvents{};
+        return ok();
+    }
+    s_starts.assign(reinterpret_cast<hipEvent_t const*>(starts), reinterpret_cast<hipEvent_t const*>(starts) + capacity);
+    s_ends.assign(reinterpret_cast<hipEvent_t const*>(ends), reinterpret_cast<hipEvent_t const*>(ends) + capacity);
+    le.starts = s_starts.data();
+    le.ends = s_ends.data();
+    le.capacity = capacity;
+    le.count = 0;
+    return ok();
+}
+
+int dust_gemm_event_count(void) { return dust::g_gemm_events.count; }
 
 dust_status dust_noise(uint64_t seed, uint32_t layer, uint32_t draw_offset, int64_t K, uint32_t token_offset,
                        int64_t T, int64_t n, uint32_t* raw, float* gauss, void* stream) {
@@ -784,11 +802,13 @@ dust_status dust_lm_estimate(const dust_lm_config* cfg, const dust_lm_hparams* h
     unsigned char* sub = R.ws + L.SUB;
     float* rw = rewards ? rewards : R.f(L.REWS);
     hipError_t e = lm_clean_forward(R);
+    if (e == hipSuccess) e = record_stage(4, st);
     if (e != hipSuccess) return device_fail("dust_lm_estimate: clean forward", e);
     // head on the cached logits
     s = dust_estimate_head(R.f(L.Z), DUST_F32, R.f(L.UF), labels, T, D.V, D.d, K, hp->sigma_head, seed, kLmLidHead,
                            0, 0, grads + P.head, nullptr, rw, sub, L.sub_bytes, stream);
     if (s != DUST_OK) return s;
+    if ((e = record_stage(5, st)) != hipSuccess) return device_fail("dust_lm_estimate: stage event", e);
     // one pass per linear type, the network recomputed as changes
     const float sig[4] = {hp->sigma_emb, hp->sigma_o, hp->sigma_up, hp->sigma_down};
     for (int kind = 0; kind < 4; ++kind) {
@@ -824,6 +844,7 @@ dust_status dust_lm_estimate(const dust_lm_config* cfg, const dust_lm_hparams* h
             if (e != hipSuccess) return device_fail("dust_lm_estimate: g_hat / outer product", e);
         }
     }
+    if ((e = record_stage(6, st)) != hipSuccess) return device_fail("dust_lm_estimate: stage event", e);
     // attention internals, with the error at the attention output e = g_hat_O W_O
     const float sqkv[3] = {hp->sigma_q, hp->sigma_k, hp->sigma_v};
     for (int64_t l = 0; l < D.L; ++l) {
@@ -837,6 +858,7 @@ dust_status dust_lm_estimate(const dust_lm_config* cfg, const dust_lm_hparams* h
             if (s != DUST_OK) return s;
         }
     }
+    if ((e = record_stage(7, st)) != hipSuccess) return device_fail("dust_lm_estimate: stage event", e);
     // residual scalars: antithetic weight-space ES
     float* res = R.f(L.REWES);
     for (int64_t m0 = 0; m0 < 2 * M; m0 += L.kc) {

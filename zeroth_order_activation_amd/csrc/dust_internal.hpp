@@ -107,6 +107,16 @@ hipError_t launch_attn_v_ghat(int64_t T, int64_t d, int64_t K, float sigma, uint
                               hipStream_t stream);
 
 // ---- small causal LM: clean forward and change-propagating forward (lm.hip) ----
+// Profiling: while starts is set, each launch of the LM's GEMM kernel records
+// starts[count] before and ends[count] after it, for the first `capacity` launches.
+struct LaunchEvents {
+    hipEvent_t* starts = nullptr;
+    hipEvent_t* ends = nullptr;
+    int capacity = 0;
+    int count = 0;
+};
+extern thread_local LaunchEvents g_gemm_events;
+
 // Rows of a change tensor are r = i T + t for draw i of the chunk; every size
 // assumption (M % 64, K % 16, d = 64 H, S % 64, widths % 4) is checked by the caller.
 hipError_t lm_gemm_nt(const float* A, const float* B, float* C, int64_t M, int64_t N, int64_t K, const float* alpha,

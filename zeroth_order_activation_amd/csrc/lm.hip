@@ -530,11 +530,24 @@ unsigned blocks(int64_t n, int per = 256) { return (unsigned)((n + per - 1) / pe
 }  // namespace
 
 // ---- launchers (arguments validated by the caller) ------------------------------
+thread_local LaunchEvents g_gemm_events;
+
 hipError_t lm_gemm_nt(const float* A, const float* B, float* C, int64_t M, int64_t N, int64_t K, const float* alpha,
                       bool accumulate, hipStream_t s) {
+    LaunchEvents& le = g_gemm_events;
+    const bool timed = le.starts && le.count < le.capacity;
+    if (timed) {
+        const hipError_t e = hipEventRecord(le.starts[le.count], s);
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(lm_gemm_nt_kernel, dim3((unsigned)(M / GB), (unsigned)((N + GB - 1) / GB)), dim3(256), 0, s,
                        A, B, C, (int)M, (int)N, (int)K, alpha, accumulate ? 1 : 0);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess && timed) {
+        e = hipEventRecord(le.ends[le.count], s);
+        ++le.count;
+    }
+    return e;
 }
 
 hipError_t lm_embed(const float* emb, const float* pos, const int32_t* tok, int T, int S, int d, int V, float* x,
