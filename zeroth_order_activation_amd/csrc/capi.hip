@@ -524,6 +524,9 @@ LmParams lm_params(const LmDims& D) {
 
 struct LmLayout {
     int64_t kc;
+    bool fused;                  // head change fused with its loss change (d = 64 or 128)
+    int64_t vp, nseg, vseg;      // padded vocabulary, its segments for the fused kernel
+    size_t HBHI, HBLO, PP, PART;
     size_t X[kLmMaxL + 1], U1[kLmMaxL], Q[kLmMaxL], Kk[kLmMaxL], Vv[kLmMaxL], O[kLmMaxL], BA[kLmMaxL], XM[kLmMaxL],
         U2[kLmMaxL], BM[kLmMaxL], Hh[kLmMaxL], Mm[kLmMaxL], MU1[kLmMaxL], RS1[kLmMaxL], MU2[kLmMaxL], RS2[kLmMaxL],
         LSE[kLmMaxL], GO[kLmMaxL], GUP[kLmMaxL], GDN[kLmMaxL];
@@ -574,9 +577,21 @@ LmLayout lm_layout(const LmDims& D, int64_t K, int64_t M) {
     L.Z = take(T * D.V);
     L.LSEZ = take(T);
     L.CE = take(T);
-    const int64_t per_draw = T * (7 * d + 2 * n + D.V) * (int64_t)sizeof(float);
+    L.fused = d == 64 || d == 128;
+    L.vp = (D.V + 127) / 128 * 128;
+    if (L.fused) {
+        L.HBHI = take(L.vp * d / 2);
+        L.HBLO = take(L.vp * d / 2);
+        L.PP = take(T * L.vp);
+    }
+    const int64_t per_draw = T * (7 * d + 2 * n + (L.fused ? L.vp / 128 : D.V)) * (int64_t)sizeof(float);
     L.kc = std::max<int64_t>(1, std::min<int64_t>(std::max(K, 2 * M), (int64_t)kLmChunkBytes / per_draw));
     const int64_t R = L.kc * T;
+    // segments: enough workgroups (64 rows x one segment each) to fill the chip
+    const int64_t tiles = L.vp / 128, rb = R / 64;
+    L.nseg = std::max<int64_t>(1, std::min<int64_t>(tiles, (2048 + rb - 1) / rb));
+    L.vseg = (tiles + L.nseg - 1) / L.nseg * 128;
+    L.nseg = (L.vp + L.vseg - 1) / L.vseg;
     L.DX = take(R * d);
     L.DU = take(R * d);
     L.DQ = take(R * d);
@@ -586,7 +601,10 @@ LmLayout lm_layout(const LmDims& D, int64_t K, int64_t M) {
     L.DB = take(R * d);
     L.DH = take(R * n);
     L.DM = take(R * n);
-    L.DZ = take(R * D.V);
+    if (L.fused)
+        L.PART = take(R * L.nseg);
+    else
+        L.DZ = take(R * D.V);
     L.REWS = take((int64_t)lm_rewards_count(D, K, M));
     L.REWES = take(2 * M * T);
     L.DL = take(2 * M);
@@ -648,7 +666,11 @@ hipError_t lm_clean_forward(const LmRun& R) {
     }
     LM_TRY(dust::lm_layernorm(R.f(L.X[D.L]), T, d, D.eps, R.f(L.UF), R.f(L.MUF), R.f(L.RSF), st));
     LM_TRY(dust::lm_gemm_nt(R.f(L.UF), p + R.P.head, R.f(L.Z), T, D.V, d, nullptr, false, st));
-    return dust::lm_ce(R.f(L.Z), R.lab, T, (int)D.V, R.f(L.LSEZ), R.f(L.CE), st);
+    if (L.fused)
+        LM_TRY(dust::lm_split(p + R.P.head, D.V, L.vp, d, reinterpret_cast<uint16_t*>(R.ws + L.HBHI),
+                              reinterpret_cast<uint16_t*>(R.ws + L.HBLO), st));
+    return dust::lm_ce(R.f(L.Z), R.lab, T, (int)D.V, R.f(L.LSEZ), R.f(L.CE), L.fused ? R.f(L.PP) : nullptr,
+                       (int)L.vp, st);
 }
 
 // One chunk of kn draws (or ES members from draw0) of a pass: kind 0 emb, 1 o, 2 up,
@@ -664,7 +686,7 @@ hipError_t lm_delta_chunk(const LmRun& R, int kind, int kn, uint32_t draw0, floa
     const bool es = kind == 4;
     const float es_sigma = es ? sigma : 0.f;
     float *DX = R.f(L.DX), *DU = R.f(L.DU), *DQ = R.f(L.DQ), *DK = R.f(L.DK), *DV = R.f(L.DV), *DO = R.f(L.DO),
-          *DB = R.f(L.DB), *DH = R.f(L.DH), *DM = R.f(L.DM), *DZ = R.f(L.DZ);
+          *DB = R.f(L.DB), *DH = R.f(L.DH), *DM = R.f(L.DM), *DZ = L.fused ? nullptr : R.f(L.DZ);
     auto zero = [&](float* ptr, int64_t count) { return hipMemsetAsync(ptr, 0, (size_t)count * sizeof(float), st); };
     bool live = false;  // whether DX holds a change yet
     if (kind == 0) {
@@ -715,6 +737,12 @@ hipError_t lm_delta_chunk(const LmRun& R, int kind, int kn, uint32_t draw0, floa
         }
     }
     LM_TRY(dust::lm_layernorm_delta(R.f(L.X[D.L]), R.f(L.MUF), R.f(L.RSF), DX, rows, T, d, DU, st));
+    if (L.fused) {
+        LM_TRY(dust::lm_head_delta(DU, reinterpret_cast<const uint16_t*>(R.ws + L.HBHI),
+                                   reinterpret_cast<const uint16_t*>(R.ws + L.HBLO), R.f(L.PP), d, kn, T, (int)L.vp,
+                                   (int)L.vseg, (int)L.nseg, R.f(L.PART), st));
+        return dust::lm_head_reward(DU, p + R.P.head, R.lab, R.f(L.PART), T, (int)D.V, d, (int)L.nseg, rows, rew, st);
+    }
     LM_TRY(dust::lm_gemm_nt(DU, p + R.P.head, DZ, rows, D.V, d, nullptr, false, st));
     return dust::lm_ce_delta(R.f(L.Z), R.f(L.LSEZ), DZ, R.lab, kn, T, (int)D.V, rew, st);
 }

@@ -128,7 +128,16 @@ hipError_t lm_attn_fwd(const float* q, const float* k, const float* v, int T, in
                        hipStream_t s);
 hipError_t lm_gelu(const float* h, int64_t count, float* m, hipStream_t s);
 hipError_t lm_residual(const float* x, const float* b, const float* alpha, int64_t count, float* out, hipStream_t s);
-hipError_t lm_ce(const float* z, const int32_t* labels, int T, int V, float* lse, float* ce, hipStream_t s);
+hipError_t lm_ce(const float* z, const int32_t* labels, int T, int V, float* lse, float* ce, float* prob, int Vp,
+                 hipStream_t s);
+// the head's change fused with its loss change (d = 64 or 128): bf16 parts of W_head
+// [Vp, d] (Vp = V rounded up to 128, zero rows past V), probabilities [T, Vp];
+// part [kc T, nseg] the per-segment sums, then rew = D_z_y - log1p(sum part)
+hipError_t lm_split(const float* W, int64_t rows, int64_t rows_p, int K, uint16_t* hi, uint16_t* lo, hipStream_t s);
+hipError_t lm_head_delta(const float* du, const uint16_t* whi, const uint16_t* wlo, const float* prob, int d, int kc,
+                         int T, int Vp, int vseg, int nseg, float* part, hipStream_t s);
+hipError_t lm_head_reward(const float* du, const float* whead, const int32_t* labels, const float* part, int T, int V,
+                          int d, int nseg, int64_t rows, float* rew, hipStream_t s);
 hipError_t lm_noise_add(float* D, int kc, int T, int w, float sigma, uint32_t k0, uint32_t k1, uint32_t layer,
                         uint32_t draw0, hipStream_t s);
 hipError_t lm_layernorm_delta(const float* x, const float* mu, const float* rs, const float* dx, int64_t R, int T,

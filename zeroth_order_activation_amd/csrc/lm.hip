@@ -245,7 +245,8 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 }
 
 __global__ void __launch_bounds__(256) lm_ce_kernel(const float* __restrict__ z, const int32_t* __restrict__ labels,
-                                                    int V, float* __restrict__ lse, float* __restrict__ ce) {
+                                                    int V, float* __restrict__ lse, float* __restrict__ ce,
+                                                    float* __restrict__ prob, int Vp) {
     __shared__ float red[4];
     const int64_t t = blockIdx.x;
     const float* zr = z + t * V;
@@ -255,11 +256,13 @@ __global__ void __launch_bounds__(256) lm_ce_kernel(const float* __restrict__ z,
     float s = 0.f;
     for (int j = threadIdx.x; j < V; j += 256) s += __expf(zr[j] - m);
     s = block_total(s, red);
+    const float l = m + logf(s);
     if (threadIdx.x == 0) {
-        const float l = m + logf(s);
         lse[t] = l;
         ce[t] = l - zr[min(max(labels[t], 0), V - 1)];
     }
+    if (prob)  // softmax row, zero past V up to the padded width Vp
+        for (int j = threadIdx.x; j < Vp; j += 256) prob[t * Vp + j] = j < V ? __expf(zr[j] - l) : 0.f;
 }
 
 // ---- change-propagating forward (rows r = i T + t for draw i of the chunk) --------
@@ -525,6 +528,204 @@ __global__ void __launch_bounds__(256) lm_sgd_kernel(float* __restrict__ theta, 
     theta[i] = fmaf(-(i >= scal0 ? lr_scalar : lr), m, theta[i]);
 }
 
+// ---- head change fused with its loss change (bf16x3 MFMA) -----------------------
+typedef float hf32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 hbf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 hbf16x8 __attribute__((ext_vector_type(8)));
+typedef float hf32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b) {  // round to nearest even, a in the low half
+    const hf32x2 v = {a, b};
+    const hbf16x2 h = __builtin_convertvector(v, hbf16x2);
+    uint32_t u;
+    __builtin_memcpy(&u, &h, 4);
+    return u;
+}
+
+// 8 fp32 values as bf16 hi and lo parts: x = hi + lo within 2^-17 |x|
+__device__ __forceinline__ void split8(const float4& x0, const float4& x1, uint4& hi, uint4& lo) {
+    const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        h[q] = bf16_pair(x[2 * q], x[2 * q + 1]);
+        l[q] = bf16_pair(x[2 * q] - __uint_as_float(h[q] << 16), x[2 * q + 1] - __uint_as_float(h[q] & 0xFFFF0000u));
+    }
+    hi = make_uint4(h[0], h[1], h[2], h[3]);
+    lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+__device__ __forceinline__ hf32x16 mfma_bf16(const uint4& a, const uint4& b, const hf32x16& c) {
+    hbf16x8 av, bv;
+    __builtin_memcpy(&av, &a, 16);
+    __builtin_memcpy(&bv, &b, 16);
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, c, 0, 0, 0);
+}
+
+// hi/lo bf16 parts of a [rows, K] fp32 matrix into [rows_p, K] arrays (rows past `rows` zero)
+__global__ void __launch_bounds__(256) lm_split_kernel(const float* __restrict__ W, int64_t rows, int64_t rows_p,
+                                                       int K, uint32_t* __restrict__ hi, uint32_t* __restrict__ lo) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // pair index
+    if (i >= rows_p * K / 2) return;
+    const int64_t row = (2 * i) / K;
+    const float a = row < rows ? W[2 * i] : 0.f, b = row < rows ? W[2 * i + 1] : 0.f;
+    const uint32_t h = bf16_pair(a, b);
+    hi[i] = h;
+    lo[i] = bf16_pair(a - __uint_as_float(h << 16), b - __uint_as_float(h & 0xFFFF0000u));
+}
+
+// expm1 of 16 values: the degree-6 Taylor polynomial (relative truncation below 5e-8
+// for |x| < 1/4); waves holding a larger |x| take exp(x) - 1 for those values.
+__device__ __forceinline__ void expm1_x16(float (&x)[16]) {
+    bool big = false;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) big |= fabsf(x[r]) >= 0.25f;
+    float q[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        q[r] = x[r] * fmaf(x[r], fmaf(x[r], fmaf(x[r], fmaf(x[r], fmaf(x[r], 1.0f / 720.0f, 1.0f / 120.0f),
+                                                             1.0f / 24.0f), 1.0f / 6.0f), 0.5f), 1.0f);
+    if (__builtin_amdgcn_ballot_w64(big)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) q[r] = fabsf(x[r]) < 0.25f ? q[r] : __expf(x[r]) - 1.0f;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = q[r];
+}
+
+// Per row r (draw i, token t) and vocabulary segment: sum_v p_t[v] expm1(D_z[r][v]) with
+// D_z = D_u W_head^T formed on bf16x3 MFMA (products within ~3 2^-17 of fp32), as the
+// transposed product D_z^T[v][r] so that a lane holds one row (token) and 16 of its
+// vocabulary entries: the row's sum accumulates in one register.  One workgroup: a
+// block of 64 tokens x one vocabulary segment x a group of HDG draws; the group's D_u
+// rows are split into bf16 parts once, into LDS; each wave takes every fourth 32-entry
+// vocabulary block of the segment, holds its W_head fragments and the 64 tokens'
+// probabilities in registers and runs all the group's rows against them.  Workgroups
+// of one (token block, segment) run on one XCD (workgroup id mod 8), sharing its L2.
+constexpr int HDG = 4;  // draws per workgroup
+
+template <int KS>  // d = 16 KS
+__global__ void __launch_bounds__(256) lm_head_delta_kernel(const float* __restrict__ du,
+                                                            const uint16_t* __restrict__ whi,
+                                                            const uint16_t* __restrict__ wlo,
+                                                            const float* __restrict__ prob, int T, int Vp, int vseg,
+                                                            int nseg, int kc, float* __restrict__ part) {
+    constexpr int D = 16 * KS, UNITS = HDG * 64 * KS * 2;  // 16-byte units of one group's parts
+    __shared__ uint4 UH[UNITS];
+    __shared__ uint4 UL[UNITS];
+    __shared__ float red[4][HDG][64];
+    const int ngr = (kc + HDG - 1) / HDG;
+    const int id = blockIdx.x, xcd = id & 7, loc = id >> 3;
+    const int pair = xcd + 8 * (loc / ngr), g = loc % ngr;
+    if (pair >= (T / 64) * nseg) return;
+    const int tb = pair / nseg, sg = pair % nseg, dn = min(HDG, kc - g * HDG);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hf = lane >> 5;
+    // unit (j, row, ks, h) = 8 channels 16 ks + 8 h of row `row` of draw j; stored at
+    // ((j 64 + row) KS + (ks ^ (row & (KS - 1)))) 2 + h so that a wave's 32 rows spread over the banks
+    for (int u = threadIdx.x; u < dn * 64 * KS * 2; u += 256) {
+        const int h = u & 1, ks = (u >> 1) % KS, row = (u / (2 * KS)) % 64, j = u / (2 * KS * 64);
+        const float* a = du + ((int64_t)(g * HDG + j) * T + (int64_t)tb * 64 + row) * D + 16 * ks + 8 * h;
+        uint4 hi, lo;
+        split8(*reinterpret_cast<const float4*>(a), *reinterpret_cast<const float4*>(a + 4), hi, lo);
+        const int at = ((j * 64 + row) * KS + (ks ^ (row & (KS - 1)))) * 2 + h;
+        UH[at] = hi;
+        UL[at] = lo;
+    }
+    __syncthreads();
+    float s[HDG][2];
+#pragma unroll
+    for (int j = 0; j < HDG; ++j) s[j][0] = s[j][1] = 0.f;
+    const int vb = sg * vseg, ve = min(Vp, vb + vseg);
+    for (int v0 = vb + 32 * w; v0 < ve; v0 += 128) {
+        uint4 ahi[KS], alo[KS];  // W_head rows v0 + (lane & 31), channels 16 ks + 8 hf + [0, 8)
+        const uint16_t* bh = whi + (int64_t)(v0 + (lane & 31)) * D + 8 * hf;
+        const uint16_t* bl = wlo + (int64_t)(v0 + (lane & 31)) * D + 8 * hf;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            ahi[ks] = *reinterpret_cast<const uint4*>(bh + 16 * ks);
+            alo[ks] = *reinterpret_cast<const uint4*>(bl + 16 * ks);
+        }
+        float pv[2][16];  // p of this lane's token (column) at the 16 vocabulary rows it holds
+#pragma unroll
+        for (int th = 0; th < 2; ++th) {
+            const float* pp = prob + ((int64_t)tb * 64 + 32 * th + (lane & 31)) * Vp + v0 + 4 * hf;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const float4 q = *reinterpret_cast<const float4*>(pp + 8 * m);
+                pv[th][4 * m] = q.x;
+                pv[th][4 * m + 1] = q.y;
+                pv[th][4 * m + 2] = q.z;
+                pv[th][4 * m + 3] = q.w;
+            }
+        }
+        for (int j = 0; j < dn; ++j) {
+            hf32x16 c0 = {}, c1 = {};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int r0 = lane & 31, r1 = 32 + (lane & 31);
+                const int a0 = ((j * 64 + r0) * KS + (ks ^ (r0 & (KS - 1)))) * 2 + hf;
+                const int a1 = ((j * 64 + r1) * KS + (ks ^ (r1 & (KS - 1)))) * 2 + hf;
+                const uint4 h0 = UH[a0], l0 = UL[a0], h1 = UH[a1], l1 = UL[a1];
+                c0 = mfma_bf16(alo[ks], h0, c0);
+                c1 = mfma_bf16(alo[ks], h1, c1);
+                c0 = mfma_bf16(ahi[ks], l0, c0);
+                c1 = mfma_bf16(ahi[ks], l1, c1);
+                c0 = mfma_bf16(ahi[ks], h0, c0);
+                c1 = mfma_bf16(ahi[ks], h1, c1);
+            }
+#pragma unroll
+            for (int th = 0; th < 2; ++th) {
+                float x[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) x[r] = th ? c1[r] : c0[r];
+                expm1_x16(x);
+                float acc = 0.f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc = fmaf(pv[th][r], x[r], acc);
+#pragma unroll
+                for (int jj = 0; jj < HDG; ++jj)
+                    if (jj == j) s[jj][th] += acc;
+            }
+        }
+    }
+    // the two halves of a wave hold the same tokens (different vocabulary rows); then the waves
+#pragma unroll
+    for (int j = 0; j < HDG; ++j)
+#pragma unroll
+        for (int th = 0; th < 2; ++th) s[j][th] += __shfl_xor(s[j][th], 32, 64);
+    if (hf == 0) {
+#pragma unroll
+        for (int j = 0; j < HDG; ++j) {
+            red[w][j][lane] = s[j][0];
+            red[w][j][32 + lane] = s[j][1];
+        }
+    }
+    __syncthreads();
+    for (int x = threadIdx.x; x < dn * 64; x += 256) {
+        const int j = x >> 6, q = x & 63;
+        part[((int64_t)(g * HDG + j) * T + (int64_t)tb * 64 + q) * nseg + sg] =
+            (red[0][j][q] + red[1][j][q]) + (red[2][j][q] + red[3][j][q]);
+    }
+}
+
+// rew[r] = D_z_y - log1p(sum over segments), D_z_y = <D_u[r], W_head[y_t]> in fp32.
+// One wave per row.
+__global__ void __launch_bounds__(256) lm_head_reward_kernel(const float* __restrict__ du,
+                                                             const float* __restrict__ whead,
+                                                             const int32_t* __restrict__ labels,
+                                                             const float* __restrict__ part, int T, int V, int d,
+                                                             int nseg, int64_t rows, float* __restrict__ rew) {
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= rows) return;
+    const int lane = threadIdx.x & 63, t = (int)(r % T), y = min(max(labels[t], 0), V - 1);
+    float zy = 0.f, ps = 0.f;
+    for (int c = lane; c < d; c += 64) zy = fmaf(du[r * d + c], whead[(int64_t)y * d + c], zy);
+    for (int j = lane; j < nseg; j += 64) ps += part[r * nseg + j];
+    zy = wave_total(zy);
+    ps = wave_total(ps);
+    if (lane == 0) rew[r] = zy - log1pf(ps);
+}
+
 unsigned blocks(int64_t n, int per = 256) { return (unsigned)((n + per - 1) / per); }
 
 }  // namespace
@@ -579,8 +780,9 @@ hipError_t lm_residual(const float* x, const float* b, const float* alpha, int64
     return hipGetLastError();
 }
 
-hipError_t lm_ce(const float* z, const int32_t* labels, int T, int V, float* lse, float* ce, hipStream_t s) {
-    hipLaunchKernelGGL(lm_ce_kernel, dim3((unsigned)T), dim3(256), 0, s, z, labels, V, lse, ce);
+hipError_t lm_ce(const float* z, const int32_t* labels, int T, int V, float* lse, float* ce, float* prob, int Vp,
+                 hipStream_t s) {
+    hipLaunchKernelGGL(lm_ce_kernel, dim3((unsigned)T), dim3(256), 0, s, z, labels, V, lse, ce, prob, Vp);
     return hipGetLastError();
 }
 
@@ -641,6 +843,32 @@ hipError_t lm_embed_grads(const float* ghat, const int32_t* tok, int T, int S, i
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(lm_pos_grad_kernel, dim3(blocks((int64_t)S * d)), dim3(256), 0, s, ghat, T, S, d, gpos);
+    return hipGetLastError();
+}
+
+hipError_t lm_split(const float* W, int64_t rows, int64_t rows_p, int K, uint16_t* hi, uint16_t* lo, hipStream_t s) {
+    hipLaunchKernelGGL(lm_split_kernel, dim3(blocks(rows_p * K / 2)), dim3(256), 0, s, W, rows, rows_p, K,
+                       reinterpret_cast<uint32_t*>(hi), reinterpret_cast<uint32_t*>(lo));
+    return hipGetLastError();
+}
+
+hipError_t lm_head_delta(const float* du, const uint16_t* whi, const uint16_t* wlo, const float* prob, int d, int kc,
+                         int T, int Vp, int vseg, int nseg, float* part, hipStream_t s) {
+    const int64_t npairs = (int64_t)(T / 64) * nseg, ngr = (kc + HDG - 1) / HDG;
+    const dim3 grid((unsigned)(8 * ngr * ((npairs + 7) / 8)));
+    if (d == 64)
+        hipLaunchKernelGGL(lm_head_delta_kernel<4>, grid, dim3(256), 0, s, du, whi, wlo, prob, T, Vp, vseg, nseg, kc,
+                           part);
+    else
+        hipLaunchKernelGGL(lm_head_delta_kernel<8>, grid, dim3(256), 0, s, du, whi, wlo, prob, T, Vp, vseg, nseg, kc,
+                           part);
+    return hipGetLastError();
+}
+
+hipError_t lm_head_reward(const float* du, const float* whead, const int32_t* labels, const float* part, int T, int V,
+                          int d, int nseg, int64_t rows, float* rew, hipStream_t s) {
+    hipLaunchKernelGGL(lm_head_reward_kernel, dim3(blocks(rows, 4)), dim3(256), 0, s, du, whead, labels, part, T, V, d,
+                       nseg, rows, rew);
     return hipGetLastError();
 }
 
