@@ -151,3 +151,61 @@ def test_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(TypeError):
         dust.estimate_head(torch.zeros(2, 4), torch.zeros(2, 3), torch.zeros(2, dtype=torch.int32), 1, 0.1, 0, 0)
+
+
+def _lm(cfg_kw=None, hp_kw=None, **kw):
+    c = dict(V=100, d=64, H=1, L=2, n=128, S=128, B=2, ln_eps=1e-5)
+    c.update(cfg_kw or {})
+    h = dict(K=4, M=2, sigma=0.01, sigma_es=0.01)
+    h.update(hp_kw or {})
+    cfg = dust.LMConfig(**c)
+    hp = dust.lm_hparams(h["K"], h["M"], h["sigma"], h["sigma_es"])
+    a = dict(params=FAKE, tok=FAKE, lab=FAKE, grads=FAKE, rew=None, ws=None, wsb=0, hp=ctypes.byref(hp))
+    a.update(kw)
+    L = dust.lib()
+    st = L.dust_lm_estimate(ctypes.byref(cfg), a["hp"], a["params"], a["tok"], a["lab"], 1, a["grads"], a["rew"],
+                            a["ws"], a["wsb"], None)
+    return st, L.dust_last_error().decode()
+
+
+@pytest.mark.parametrize("cfg_kw,hp_kw,kw,status,msg", [
+    (dict(d=96), None, {}, 2, "d = 64 H"),
+    (dict(H=17, d=64 * 17), None, {}, 2, "d = 64 H"),
+    (dict(S=100), None, {}, 2, "S must be"),
+    (dict(S=8192), None, {}, 2, "S must be"),
+    (dict(n=100), None, {}, 2, "n must be"),
+    (dict(V=40000), None, {}, 2, "V must be"),
+    (dict(L=0), None, {}, 2, "L must be"),
+    (dict(L=33), None, {}, 2, "L must be"),
+    (dict(B=0), None, {}, 1, "B must be"),
+    (dict(ln_eps=0.0), None, {}, 1, "ln_eps"),
+    (None, dict(K=0), {}, 1, "K and M"),
+    (None, dict(M=0), {}, 1, "K and M"),
+    (None, dict(sigma=0.0), {}, 1, "sigma"),
+    (None, dict(sigma_es=float("nan")), {}, 1, "sigma"),
+    (None, None, dict(hp=None), 1, "hp is NULL"),
+    (None, None, dict(params=None), 1, "non-NULL"),
+    (None, None, dict(params=FAKE_MIS), 1, "aligned"),
+    (None, None, dict(ws=None), 3, "workspace"),
+])
+def test_lm_step_rejects_bad_arguments_on_host(cfg_kw, hp_kw, kw, status, msg):
+    st, err = _lm(cfg_kw, hp_kw, **kw)
+    assert st == status and msg in err, (st, err)
+
+
+def test_lm_sizes():
+    import synth
+
+    for V, d, H, L, n, S in ((100, 64, 1, 2, 128, 128), (8192, 128, 2, 2, 512, 256), (7, 192, 3, 1, 64, 64)):
+        cfg = dust.lm_config(V, d, H, L, n, S, 2)
+        want = sum(int(ctypes.c_int64(1).value * __import__("math").prod(s)) for _, s in
+                   synth.lm_param_layout(V, d, L, n, S))
+        assert dust.lm_param_count(cfg) == want
+        hp = dust.lm_hparams(5, 3, 0.01, 0.01)
+        assert dust.lm_rewards_count(cfg, hp) == (5 + 3 * L) * 5 * 2 * S + 2 * 3
+        assert dust.lm_workspace_bytes(cfg, hp) > 4 * want
+    assert dust.lm_param_count(dust.lm_config(100, 96, 1, 2, 128, 128, 2)) == 0
+    L = dust.lib()
+    st = L.dust_lm_sgd(ctypes.byref(dust.lm_config(100, 64, 1, 2, 128, 128, 2)),
+                       ctypes.byref(dust.lm_hparams(4, 2, 0.01, 0.01, lr=float("nan"))), FAKE, FAKE, FAKE, None)
+    assert st == 1 and "finite" in L.dust_last_error().decode()

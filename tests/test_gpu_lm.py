@@ -4,7 +4,8 @@ Small models element by element: the clean per-token loss; every pass's rewards 
 embedding, W_O, W_1, W_2 outputs, q/k/v per block) and the ES members' loss changes; every
 packed gradient estimate; the parameters and momentum after SGD.  Cases: one and two heads,
 one and two blocks, one and two query tiles per sequence, a vocabulary that is not a multiple
-of 64, and a large noise scale (changes past the small-argument branches).  The 2M-class
+of 64, a large noise scale (changes past the small-argument branches), and a width whose
+head change takes the unfused path.  The 2M-class
 shape the benchmark times (V 8192, d 128, 2 blocks, 4 x 256 tokens, K 64 over three chunks of
 draws, 32 ES pairs): rewards of sampled draws and members against the oracle draw by draw.
 """
@@ -37,6 +38,7 @@ CASES = [
     (100, 64, 1, 2, 128, 128, 2, 5, 3, 2e-2),   # two query tiles, two blocks, ragged V
     (64, 128, 2, 1, 256, 64, 3, 4, 2, 1e-2),    # two heads, one block
     (70, 64, 1, 1, 64, 64, 2, 3, 2, 0.3),       # large changes: exp - 1 and erfc branches
+    (50, 192, 3, 1, 64, 64, 2, 3, 2, 1e-2),     # d = 192: the head change by GEMM + loss-change kernel
 ]
 
 
