@@ -305,7 +305,7 @@ dust_status dust_estimate_attn_v(const float *q, const float *k, const float *e,
  *             members' summed-loss changes L(member) - L(clean), member 2j then 2j + 1.
  *   ce      : OUT float [T] the clean per-token cross-entropy (dust_lm_forward).
  * Supported: 1 <= H <= 16, S a multiple of 64 up to 4096, n a multiple of 64 up to 65536,
- * 1 <= V <= 32768, 1 <= L <= 32, K >= 1, M >= 1; every sigma > 0.
+ * 1 <= V <= 32768, 1 <= L <= 32, K >= 1, M >= 1, chunk >= 0; every sigma > 0.
  * Workspace: dust_lm_workspace_bytes(cfg, hp) bytes (the clean cache, the change tensors
  * of one chunk of draws (at most 1 GiB, at least one draw), the rewards and the
  * estimators' own scratch); dust_lm_forward needs the same query's size.
@@ -319,6 +319,7 @@ typedef struct {
     int32_t K, M;
     float sigma_emb, sigma_q, sigma_k, sigma_v, sigma_o, sigma_up, sigma_down, sigma_head, sigma_es;
     float lr, lr_scalar, momentum;
+    int32_t chunk; /* most draws (or ES members) per chunk of change tensors; 0: as many as fit in 1 GiB */
 } dust_lm_hparams;
 
 size_t dust_lm_param_count(const dust_lm_config *cfg);

@@ -6,8 +6,9 @@ packed gradient estimate; the parameters and momentum after SGD.  Cases: one and
 one and two blocks, one and two query tiles per sequence, a vocabulary that is not a multiple
 of 64, a large noise scale (changes past the small-argument branches), and a width whose
 head change takes the unfused path.  The 2M-class
-shape the benchmark times (V 8192, d 128, 2 blocks, 4 x 256 tokens, K 64 over three chunks of
-draws, 32 ES pairs): rewards of sampled draws and members against the oracle draw by draw.
+shape the benchmark times (V 8192, d 128, 2 blocks, 4 x 256 tokens, K 64, 32 ES pairs):
+rewards of sampled draws and members against the oracle draw by draw.  Chunks of a few draws
+(and ES members) are forced in one case.
 """
 import numpy as np
 import pytest
@@ -34,11 +35,12 @@ def _setup(V, d, H, L, n, S, B, seed, scal=1.0):
 
 
 CASES = [
-    # V, d, H, L, n, S, B, K, M, sigma
-    (100, 64, 1, 2, 128, 128, 2, 5, 3, 2e-2),   # two query tiles, two blocks, ragged V
-    (64, 128, 2, 1, 256, 64, 3, 4, 2, 1e-2),    # two heads, one block
-    (70, 64, 1, 1, 64, 64, 2, 3, 2, 0.3),       # large changes: exp - 1 and erfc branches
-    (50, 192, 3, 1, 64, 64, 2, 3, 2, 1e-2),     # d = 192: the head change by GEMM + loss-change kernel
+    # V, d, H, L, n, S, B, K, M, sigma, chunk
+    (100, 64, 1, 2, 128, 128, 2, 5, 3, 2e-2, 0),   # two query tiles, two blocks, ragged V
+    (64, 128, 2, 1, 256, 64, 3, 4, 2, 1e-2, 0),    # two heads, one block
+    (70, 64, 1, 1, 64, 64, 2, 3, 2, 0.3, 0),       # large changes: exp - 1 and erfc branches
+    (50, 192, 3, 1, 64, 64, 2, 3, 2, 1e-2, 0),     # d = 192: the head change by GEMM + loss-change kernel
+    (100, 128, 2, 2, 128, 64, 2, 11, 5, 1e-2, 3),  # chunks of 3 draws (11 = 3+3+3+2, 10 members = 3+3+3+1)
 ]
 
 
@@ -62,10 +64,10 @@ def _slices(ocfg):
     return out
 
 
-@pytest.mark.parametrize("V,d,H,L,n,S,B,K,M,sigma", CASES)
-def test_estimate_elementwise(V, d, H, L, n, S, B, K, M, sigma):
+@pytest.mark.parametrize("V,d,H,L,n,S,B,K,M,sigma,chunk", CASES)
+def test_estimate_elementwise(V, d, H, L, n, S, B, K, M, sigma, chunk):
     c, cfg, ocfg, p, tok, lab = _setup(V, d, H, L, n, S, B, seed=11 + V, scal=0.8)
-    hp = dust.lm_hparams(K, M, sigma, 2e-2)
+    hp = dust.lm_hparams(K, M, sigma, 2e-2, chunk=chunk)
     rew = torch.empty(dust.lm_rewards_count(cfg, hp), dtype=torch.float32, device="cuda")
     G = dust.lm_estimate(cfg, hp, p, tok, lab, SEED, rewards=rew)
     G2 = dust.lm_estimate(cfg, hp, p, tok, lab, SEED)
@@ -116,8 +118,9 @@ def test_step_updates_parameters_and_momentum():
 
 def test_bench_shape_on_sampled_draws():
     """The 2M-class shape: V 8192, d 128 (2 heads), 2 blocks, n 512, 4 x 256 tokens,
-    K = 64 (three chunks of draws), 32 ES pairs: rewards of sampled draws of every
-    layer-type pass and of sampled ES members against the oracle, draw by draw."""
+    K = 64 (one chunk, 16 groups of four draws in the fused head), 32 ES pairs: rewards of
+    sampled draws of every layer-type pass and of sampled ES members against the oracle,
+    draw by draw."""
     w = synth.WORKLOADS[7]
     c, cfg, ocfg, p, tok, lab = _setup(w["V"], w["d"], w["H"], w["L"], w["n"], w["S"], w["B"], seed=1007)
     K, M, sigma, ses = w["K"], w["M"], w["sigma"], w["sigma_es"]
@@ -130,7 +133,7 @@ def test_bench_shape_on_sampled_draws():
     KT = K * T
     errs = []
     for j, kind in enumerate(lm.ACT_TYPES):
-        for i in (0, 27, K - 1):  # first, middle and last chunk of draws
+        for i in (0, 27, K - 1):  # first, a middle and the last draw
             orw, _, _ = lm.activation_pass(ocfg, c["params"], c["tokens"], c["labels"], kind, 1, sigma,
                                            synth.LM_NOISE_SEED, draw_offset=i)
             e = rel_l2(r[(1 + j) * KT + i * T:(1 + j) * KT + (i + 1) * T], orw[0])

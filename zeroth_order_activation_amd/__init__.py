@@ -367,7 +367,8 @@ class LMHparams(ctypes.Structure):
     the SGD-momentum settings."""
     _fields_ = [("K", ctypes.c_int32), ("M", ctypes.c_int32)] + [
         (nm, ctypes.c_float) for nm in ("sigma_emb", "sigma_q", "sigma_k", "sigma_v", "sigma_o", "sigma_up",
-                                        "sigma_down", "sigma_head", "sigma_es", "lr", "lr_scalar", "momentum")]
+                                        "sigma_down", "sigma_head", "sigma_es", "lr", "lr_scalar", "momentum")] + [
+        ("chunk", ctypes.c_int32)]
 
 
 LM_TYPES = ("emb", "q", "k", "v", "o", "up", "down", "head")
@@ -378,10 +379,11 @@ def lm_config(V: int, d: int, H: int, L: int, n: int, S: int, B: int, ln_eps: fl
 
 
 def lm_hparams(K: int, M: int, sigma, sigma_es: float, lr: float = 0.0, lr_scalar: float = 0.0,
-               momentum: float = 0.0) -> LMHparams:
-    """``sigma``: one noise scale for every pass, or a dict over LM_TYPES."""
+               momentum: float = 0.0, chunk: int = 0) -> LMHparams:
+    """``sigma``: one noise scale for every pass, or a dict over LM_TYPES; ``chunk``: most
+    draws per chunk of change tensors (0: as many as fit in 1 GiB)."""
     sg = sigma if isinstance(sigma, dict) else dict.fromkeys(LM_TYPES, float(sigma))
-    return LMHparams(K, M, *(sg[t] for t in LM_TYPES), sigma_es, lr, lr_scalar, momentum)
+    return LMHparams(K, M, *(sg[t] for t in LM_TYPES), sigma_es, lr, lr_scalar, momentum, chunk)
 
 
 def lm_param_count(cfg: LMConfig) -> int:

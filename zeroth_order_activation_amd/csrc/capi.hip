@@ -491,6 +491,7 @@ dust_status lm_check_hp(const dust_lm_hparams* h, const char* who, bool step) {
     if (!h) return fail(DUST_E_INVALID, "%s: hp is NULL", who);
     if (h->K < 1 || h->K > (1 << 24) || h->M < 1 || h->M > (1 << 24))
         return fail(DUST_E_INVALID, "%s: K and M must be in [1, 2^24] (got K=%d M=%d)", who, h->K, h->M);
+    if (h->chunk < 0) return fail(DUST_E_INVALID, "%s: chunk must be >= 0 (got %d)", who, h->chunk);
     const float s[9] = {h->sigma_emb, h->sigma_q,    h->sigma_k,    h->sigma_v, h->sigma_o,
                         h->sigma_up,  h->sigma_down, h->sigma_head, h->sigma_es};
     for (float v : s)
@@ -529,7 +530,7 @@ struct LmLayout {
     size_t HBHI, HBLO, PP, PART;
     size_t X[kLmMaxL + 1], U1[kLmMaxL], Q[kLmMaxL], Kk[kLmMaxL], Vv[kLmMaxL], O[kLmMaxL], BA[kLmMaxL], XM[kLmMaxL],
         U2[kLmMaxL], BM[kLmMaxL], Hh[kLmMaxL], Mm[kLmMaxL], MU1[kLmMaxL], RS1[kLmMaxL], MU2[kLmMaxL], RS2[kLmMaxL],
-        LSE[kLmMaxL], GO[kLmMaxL], GUP[kLmMaxL], GDN[kLmMaxL];
+        LSE[kLmMaxL], PC[kLmMaxL], GO[kLmMaxL], GUP[kLmMaxL], GDN[kLmMaxL];
     size_t UF, MUF, RSF, Z, LSEZ, CE;
     size_t DX, DU, DQ, DK, DV, DO, DB, DH, DM, DZ;
     size_t REWS, REWES, DL, GE, E, WOT, SUB, sub_bytes, total;
@@ -539,7 +540,7 @@ size_t lm_rewards_count(const LmDims& D, int64_t K, int64_t M) {
     return (size_t)((5 + 3 * D.L) * K * D.T + 2 * M);
 }
 
-LmLayout lm_layout(const LmDims& D, int64_t K, int64_t M) {
+LmLayout lm_layout(const LmDims& D, int64_t K, int64_t M, int64_t chunk) {
     LmLayout L{};
     size_t off = 0;
     auto take = [&](int64_t floats) {
@@ -566,6 +567,7 @@ LmLayout lm_layout(const LmDims& D, int64_t K, int64_t M) {
         L.MU2[l] = take(T);
         L.RS2[l] = take(T);
         L.LSE[l] = take(T * D.H);
+        L.PC[l] = take(T * D.S * D.H);  // clean attention probabilities, [b, h, query, key]
         L.GO[l] = take(T * d);
         L.GUP[l] = take(T * n);
         L.GDN[l] = take(T * d);
@@ -586,6 +588,7 @@ LmLayout lm_layout(const LmDims& D, int64_t K, int64_t M) {
     }
     const int64_t per_draw = T * (7 * d + 2 * n + (L.fused ? L.vp / 128 : D.V)) * (int64_t)sizeof(float);
     L.kc = std::max<int64_t>(1, std::min<int64_t>(std::max(K, 2 * M), (int64_t)kLmChunkBytes / per_draw));
+    if (chunk > 0) L.kc = std::min(L.kc, chunk);
     const int64_t R = L.kc * T;
     // segments: enough workgroups (64 rows x one segment each) to fill the chip
     const int64_t tiles = L.vp / 128, rb = R / 64;
@@ -654,7 +657,7 @@ hipError_t lm_clean_forward(const LmRun& R) {
         LM_TRY(dust::lm_gemm_nt(R.f(L.U1[l]), p + wq + D.d * D.d, R.f(L.Kk[l]), T, d, d, nullptr, false, st));
         LM_TRY(dust::lm_gemm_nt(R.f(L.U1[l]), p + wq + 2 * D.d * D.d, R.f(L.Vv[l]), T, d, d, nullptr, false, st));
         LM_TRY(dust::lm_attn_fwd(R.f(L.Q[l]), R.f(L.Kk[l]), R.f(L.Vv[l]), T, (int)D.S, (int)D.H, R.f(L.O[l]),
-                                 R.f(L.LSE[l]), st));
+                                 R.f(L.LSE[l]), R.f(L.PC[l]), st));
         LM_TRY(dust::lm_gemm_nt(R.f(L.O[l]), p + R.P.wo(l), R.f(L.BA[l]), T, d, d, nullptr, false, st));
         LM_TRY(dust::lm_residual(R.f(L.X[l]), R.f(L.BA[l]), p + R.P.scal + 2 * l, D.T * D.d, R.f(L.XM[l]), st));
         LM_TRY(dust::lm_layernorm(R.f(L.XM[l]), T, d, D.eps, R.f(L.U2[l]), R.f(L.MU2[l]), R.f(L.RS2[l]), st));
@@ -701,7 +704,7 @@ hipError_t lm_delta_chunk(const LmRun& R, int kind, int kn, uint32_t draw0, floa
             LM_TRY(dust::lm_gemm_nt(DU, p + wq, DQ, rows, d, d, nullptr, false, st));
             LM_TRY(dust::lm_gemm_nt(DU, p + wq + D.d * D.d, DK, rows, d, d, nullptr, false, st));
             LM_TRY(dust::lm_gemm_nt(DU, p + wq + 2 * D.d * D.d, DV, rows, d, d, nullptr, false, st));
-            LM_TRY(dust::lm_attn_delta(R.f(L.Q[l]), R.f(L.Kk[l]), R.f(L.Vv[l]), R.f(L.O[l]), R.f(L.LSE[l]), DQ, DK,
+            LM_TRY(dust::lm_attn_delta(R.f(L.Q[l]), R.f(L.Kk[l]), R.f(L.Vv[l]), R.f(L.O[l]), R.f(L.PC[l]), DQ, DK,
                                        DV, kn, T, (int)D.S, (int)D.H, DO, st));
             LM_TRY(dust::lm_gemm_nt(DO, p + R.P.wo(l), DB, rows, d, d, nullptr, false, st));
         } else if (kind == 1 || es) {
@@ -755,7 +758,7 @@ dust_status lm_prepare(const dust_lm_config* cfg, const dust_lm_hparams* hp, con
     if (hp && (s = lm_check_hp(hp, who, step)) != DUST_OK) return s;
     if (!params || !tokens || !labels) return fail(DUST_E_INVALID, "%s: params, tokens and labels must be non-NULL", who);
     if (!aligned16(params)) return fail(DUST_E_INVALID, "%s: params must be 16-byte aligned", who);
-    L = lm_layout(R.D, hp ? hp->K : 1, hp ? hp->M : 1);
+    L = lm_layout(R.D, hp ? hp->K : 1, hp ? hp->M : 1, hp ? hp->chunk : 0);
     if (!workspace || workspace_bytes < L.total)
         return fail(DUST_E_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", who, L.total,
                     workspace ? workspace_bytes : (size_t)0);
@@ -789,7 +792,7 @@ size_t dust_lm_workspace_bytes(const dust_lm_config* cfg, const dust_lm_hparams*
     LmDims D;
     if (lm_check_cfg(cfg, D, "dust_lm_workspace_bytes") != DUST_OK) return 0;
     if (hp && lm_check_hp(hp, "dust_lm_workspace_bytes", false) != DUST_OK) return 0;
-    return lm_layout(D, hp ? hp->K : 1, hp ? hp->M : 1).total;
+    return lm_layout(D, hp ? hp->K : 1, hp ? hp->M : 1, hp ? hp->chunk : 0).total;
 }
 
 dust_status dust_lm_forward(const dust_lm_config* cfg, const float* params, const int32_t* tokens,

@@ -124,8 +124,10 @@ hipError_t lm_gemm_nt(const float* A, const float* B, float* C, int64_t M, int64
 hipError_t lm_embed(const float* emb, const float* pos, const int32_t* tok, int T, int S, int d, int V, float* x,
                     hipStream_t s);
 hipError_t lm_layernorm(const float* x, int64_t R, int d, float eps, float* u, float* mu, float* rs, hipStream_t s);
+// also writes the clean probabilities pc[((b H + h) S + query) S + key] for the key tiles up
+// to the query's own (zero after the query)
 hipError_t lm_attn_fwd(const float* q, const float* k, const float* v, int T, int S, int H, float* o, float* lse,
-                       hipStream_t s);
+                       float* pc, hipStream_t s);
 hipError_t lm_gelu(const float* h, int64_t count, float* m, hipStream_t s);
 hipError_t lm_residual(const float* x, const float* b, const float* alpha, int64_t count, float* out, hipStream_t s);
 hipError_t lm_ce(const float* z, const int32_t* labels, int T, int V, float* lse, float* ce, float* prob, int Vp,
@@ -142,7 +144,7 @@ hipError_t lm_noise_add(float* D, int kc, int T, int w, float sigma, uint32_t k0
                         uint32_t draw0, hipStream_t s);
 hipError_t lm_layernorm_delta(const float* x, const float* mu, const float* rs, const float* dx, int64_t R, int T,
                               int d, float* du, hipStream_t s);
-hipError_t lm_attn_delta(const float* q, const float* k, const float* v, const float* o, const float* lse,
+hipError_t lm_attn_delta(const float* q, const float* k, const float* v, const float* o, const float* pc,
                          const float* dq, const float* dk, const float* dv, int kc, int T, int S, int H, float* dout,
                          hipStream_t s);
 hipError_t lm_gelu_delta(const float* h, const float* dh, int64_t per_draw, int64_t count, float* dm, hipStream_t s);

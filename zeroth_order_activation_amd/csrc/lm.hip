@@ -162,7 +162,8 @@ __device__ __forceinline__ void stage_tile(float (*dst)[64], const float* src, i
 
 __global__ void __launch_bounds__(256) lm_attn_fwd_kernel(const float* __restrict__ q, const float* __restrict__ k,
                                                           const float* __restrict__ v, int T, int S, int H,
-                                                          float* __restrict__ o, float* __restrict__ lse) {
+                                                          float* __restrict__ o, float* __restrict__ lse,
+                                                          float* __restrict__ pc) {
     __shared__ __align__(16) float Ks[64][64];
     __shared__ __align__(16) float Vs[64][64];
     const int nqt = S / 64, qt = blockIdx.x % nqt, bh = blockIdx.x / nqt, b = bh / H, h = bh % H;
@@ -202,10 +203,25 @@ __global__ void __launch_bounds__(256) lm_attn_fwd_kernel(const float* __restric
             for (int c = 0; c < 16; ++c) acc[c] = fmaf(p, Vs[j][qr * 16 + c], acc[c]);
         }
     }
-    const float inv = 1.0f / s;
+    const float inv = 1.0f / s, l = mx + logf(s);
 #pragma unroll
     for (int c = 0; c < 16; ++c) o[row * d + h * 64 + qr * 16 + c] = acc[c] * inv;
-    if (qr == 0) lse[row * H + h] = mx + logf(s);
+    if (qr == 0) lse[row * H + h] = l;
+    // the probabilities of this query over the key tiles up to its own (zero after it):
+    // pc[((b H + h) S + query) S + key]; lane qr of the query writes keys j = qr mod 4
+    float* prow = pc + ((int64_t)bh * S + qt * 64 + ql) * S;
+    for (int kt = 0; kt <= qt; ++kt) {
+        __syncthreads();
+        stage_tile(Ks, k, s0 + kt * 64, d, h);
+        __syncthreads();
+        for (int j = 0; j < 64; ++j) {
+            float dot = 0.f;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) dot = fmaf(qv[c], Ks[j][qr * 16 + c], dot);
+            dot = quad_total(dot) * 0.125f;
+            if ((j & 3) == qr) prow[kt * 64 + j] = (kt < qt || j <= ql) ? __expf(dot - l) : 0.f;
+        }
+    }
 }
 
 __device__ __forceinline__ float phi_cdf(float x) { return 0.5f * erfcf(-x * 0.70710678118654752f); }
@@ -323,67 +339,6 @@ __device__ __forceinline__ float expm1_s(float x) {
         return x * fmaf(x, fmaf(x, fmaf(x, fmaf(x, fmaf(x, 1.0f / 720.0f, 1.0f / 120.0f), 1.0f / 24.0f),
                                           1.0f / 6.0f), 0.5f), 1.0f);
     return __expf(x) - 1.0f;
-}
-
-// Change of the attention output of 64 queries x one head for one draw:
-// D_o = (sum_t P expm1(delta) v_t + sum_t P e^delta D_v_t - rho o) / (1 + rho),
-// delta = (<D_q, k_t> + <q + D_q, D_k_t>) / 8.
-__global__ void __launch_bounds__(256) lm_attn_delta_kernel(const float* __restrict__ q, const float* __restrict__ k,
-                                                            const float* __restrict__ v, const float* __restrict__ o,
-                                                            const float* __restrict__ lse,
-                                                            const float* __restrict__ dq,
-                                                            const float* __restrict__ dk,
-                                                            const float* __restrict__ dv, int T, int S, int H,
-                                                            float* __restrict__ dout) {
-    __shared__ __align__(16) float Ks[64][64];
-    __shared__ __align__(16) float Vs[64][64];
-    __shared__ __align__(16) float DKs[64][64];
-    __shared__ __align__(16) float DVs[64][64];
-    const int nqt = S / 64, nbh = (T / S) * H;
-    const int qt = blockIdx.x % nqt, bh = (blockIdx.x / nqt) % nbh, i = blockIdx.x / (nqt * nbh);
-    const int b = bh / H, h = bh % H, d = 64 * H, ql = threadIdx.x >> 2, qr = threadIdx.x & 3;
-    const int64_t s0 = (int64_t)b * S, row = s0 + qt * 64 + ql, drow0 = (int64_t)i * T;
-    float qv[16], dqv[16], qq[16], acc[16];
-    load16(q + row * d + h * 64 + qr * 16, qv);
-    load16(dq + (drow0 + row) * d + h * 64 + qr * 16, dqv);
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-        qq[c] = qv[c] + dqv[c];
-        acc[c] = 0.f;
-    }
-    const float l = lse[row * H + h];
-    float rho = 0.f;
-    for (int kt = 0; kt <= qt; ++kt) {
-        __syncthreads();
-        stage_tile(Ks, k, s0 + kt * 64, d, h);
-        stage_tile(Vs, v, s0 + kt * 64, d, h);
-        stage_tile(DKs, dk, drow0 + s0 + kt * 64, d, h);
-        stage_tile(DVs, dv, drow0 + s0 + kt * 64, d, h);
-        __syncthreads();
-        for (int j = 0; j < 64; ++j) {
-            float lg = 0.f, dl = 0.f;
-#pragma unroll
-            for (int c = 0; c < 16; ++c) {
-                const float kc = Ks[j][qr * 16 + c];
-                lg = fmaf(qv[c], kc, lg);
-                dl = fmaf(dqv[c], kc, dl);
-                dl = fmaf(qq[c], DKs[j][qr * 16 + c], dl);
-            }
-            lg = quad_total(lg) * 0.125f;
-            dl = quad_total(dl) * 0.125f;
-            const bool on = kt < qt || j <= ql;  // keys after the query do not enter
-            const float p = on ? __expf(lg - l) : 0.f;
-            const float w1 = on ? p * expm1_s(dl) : 0.f, w2 = p + w1;
-            rho += w1;
-#pragma unroll
-            for (int c = 0; c < 16; ++c) acc[c] = fmaf(w1, Vs[j][qr * 16 + c], fmaf(w2, DVs[j][qr * 16 + c], acc[c]));
-        }
-    }
-    float ov[16];
-    load16(o + row * d + h * 64 + qr * 16, ov);
-    const float inv = 1.0f / (1.0f + rho);
-#pragma unroll
-    for (int c = 0; c < 16; ++c) dout[(drow0 + row) * d + h * 64 + qr * 16 + c] = (acc[c] - rho * ov[c]) * inv;
 }
 
 // D_m = GELU(h + D_h) - GELU(h) = D_h Phi(h + D_h) + h (Phi(h + D_h) - Phi(h))
@@ -726,6 +681,193 @@ __global__ void __launch_bounds__(256) lm_head_reward_kernel(const float* __rest
     if (lane == 0) rew[r] = zy - log1pf(ps);
 }
 
+// ---- change of the attention output (bf16x3 MFMA) ---------------------------------
+// One workgroup: draw i, sequence b, head h, 64 queries; wave w takes queries 32 (w >> 1)
+// and, of every 64-key tile, keys 32 (w & 1).  Per key tile:
+//   delta^T[key][query] = (<k, D_q> + <D_k, q + D_q>) / 8  (one accumulator, 24 MFMAs),
+//   w1 = P expm1(delta), w2 = P + w1 with P the cached clean probabilities,
+//   acc^T[c][query] += sum_key v[key][c] w1 + D_v[key][c] w2  (24 MFMAs),
+// the weights going from the accumulator registers straight into the second product's
+// B operand: register r of a lane holds key (r & 3) + 8 (r >> 2) + 4 (lane >> 5), so
+// k-step s takes registers 8 s .. 8 s + 7 and v, D_v are read from LDS, transposed to
+// [channel][key] bf16 parts, in that key order.  Then
+//   D_o = (acc - rho o) / (1 + rho),  rho = sum_key w1,
+// the two key halves added through LDS.
+constexpr int AVP = 72;  // padded row of the transposed tiles (bf16)
+
+__device__ __forceinline__ uint4 vt_frag(const uint16_t (*t)[AVP], int c, int k0) {
+    const uint2 a = *reinterpret_cast<const uint2*>(&t[c][k0]);
+    const uint2 b = *reinterpret_cast<const uint2*>(&t[c][k0 + 8]);
+    return make_uint4(a.x, a.y, b.x, b.y);
+}
+
+__global__ void __launch_bounds__(256) lm_attn_delta_kernel(const float* __restrict__ q, const float* __restrict__ k,
+                                                            const float* __restrict__ v, const float* __restrict__ o,
+                                                            const float* __restrict__ pc,
+                                                            const float* __restrict__ dq,
+                                                            const float* __restrict__ dk,
+                                                            const float* __restrict__ dv, int T, int S, int H,
+                                                            float* __restrict__ dout) {
+    __shared__ __align__(16) uint16_t VTH[64][AVP];
+    __shared__ __align__(16) uint16_t VTL[64][AVP];
+    __shared__ __align__(16) uint16_t DVTH[64][AVP];
+    __shared__ __align__(16) uint16_t DVTL[64][AVP];
+    __shared__ float accx[2][64][33];  // the odd key half's partial sums: [query block][channel][query]
+    __shared__ float rhox[2][32];
+    const int nqt = S / 64, nbh = (T / S) * H;
+    const int qt = blockIdx.x % nqt, bh = (blockIdx.x / nqt) % nbh, i = blockIdx.x / (nqt * nbh);
+    const int b = bh / H, h = bh % H, d = 64 * H;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, qb = w >> 1, kb = w & 1, hf = lane >> 5, l31 = lane & 31;
+    const int64_t s0 = (int64_t)b * S, drow0 = (int64_t)i * T;
+    const int query = qt * 64 + 32 * qb + l31;  // this lane's query (column of both products)
+    // B operands over the channels: D_q and q + D_q of this wave's 32 queries
+    uint4 dqh[4], dql[4], qqh[4], qql[4];
+    {
+        const float* pq = q + (s0 + query) * d + h * 64 + 8 * hf;
+        const float* pd = dq + (drow0 + s0 + query) * d + h * 64 + 8 * hf;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            float4 a0 = *reinterpret_cast<const float4*>(pd + 16 * ks);
+            float4 a1 = *reinterpret_cast<const float4*>(pd + 16 * ks + 4);
+            const float4 b0 = *reinterpret_cast<const float4*>(pq + 16 * ks);
+            const float4 b1 = *reinterpret_cast<const float4*>(pq + 16 * ks + 4);
+            split8(a0, a1, dqh[ks], dql[ks]);
+            a0 = make_float4(a0.x + b0.x, a0.y + b0.y, a0.z + b0.z, a0.w + b0.w);
+            a1 = make_float4(a1.x + b1.x, a1.y + b1.y, a1.z + b1.z, a1.w + b1.w);
+            split8(a0, a1, qqh[ks], qql[ks]);
+        }
+    }
+    hf32x16 acc0 = {}, acc1 = {};  // channels 0..31 and 32..63 (rows) x this wave's queries
+    float rho = 0.f;
+    const float* prow = pc + ((int64_t)bh * S + query) * S;
+    for (int kt = 0; kt <= qt; ++kt) {
+        __syncthreads();  // the previous tile's transposed values are used up
+        // v and D_v of the 64 keys, transposed into bf16 parts: unit = 2 keys x 4 channels
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int f = threadIdx.x + 256 * u, kp = f >> 4, c4 = (f & 15) * 4;
+            const int64_t r0 = s0 + kt * 64 + 2 * kp;
+            const float4 va = *reinterpret_cast<const float4*>(v + r0 * d + h * 64 + c4);
+            const float4 vb = *reinterpret_cast<const float4*>(v + (r0 + 1) * d + h * 64 + c4);
+            const float4 da = *reinterpret_cast<const float4*>(dv + (drow0 + r0) * d + h * 64 + c4);
+            const float4 db = *reinterpret_cast<const float4*>(dv + (drow0 + r0 + 1) * d + h * 64 + c4);
+            const float xa[4] = {va.x, va.y, va.z, va.w}, xb[4] = {vb.x, vb.y, vb.z, vb.w};
+            const float ya[4] = {da.x, da.y, da.z, da.w}, yb[4] = {db.x, db.y, db.z, db.w};
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const uint32_t hv = bf16_pair(xa[m], xb[m]);
+                const uint32_t lv = bf16_pair(xa[m] - __uint_as_float(hv << 16), xb[m] - __uint_as_float(hv & 0xFFFF0000u));
+                const uint32_t hd = bf16_pair(ya[m], yb[m]);
+                const uint32_t ld = bf16_pair(ya[m] - __uint_as_float(hd << 16), yb[m] - __uint_as_float(hd & 0xFFFF0000u));
+                *reinterpret_cast<uint32_t*>(&VTH[c4 + m][2 * kp]) = hv;
+                *reinterpret_cast<uint32_t*>(&VTL[c4 + m][2 * kp]) = lv;
+                *reinterpret_cast<uint32_t*>(&DVTH[c4 + m][2 * kp]) = hd;
+                *reinterpret_cast<uint32_t*>(&DVTL[c4 + m][2 * kp]) = ld;
+            }
+        }
+        // logit change of this wave's 32 keys x 32 queries
+        const int64_t krow = s0 + kt * 64 + 32 * kb + l31;
+        hf32x16 dl = {};
+        {
+            const float* pk = k + krow * d + h * 64 + 8 * hf;
+            const float* pdk = dk + (drow0 + krow) * d + h * 64 + 8 * hf;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                uint4 kh, kl, dh, dlo;
+                split8(*reinterpret_cast<const float4*>(pk + 16 * ks), *reinterpret_cast<const float4*>(pk + 16 * ks + 4),
+                       kh, kl);
+                split8(*reinterpret_cast<const float4*>(pdk + 16 * ks),
+                       *reinterpret_cast<const float4*>(pdk + 16 * ks + 4), dh, dlo);
+                dl = mfma_bf16(kl, dqh[ks], dl);
+                dl = mfma_bf16(kh, dql[ks], dl);
+                dl = mfma_bf16(kh, dqh[ks], dl);
+                dl = mfma_bf16(dlo, qqh[ks], dl);
+                dl = mfma_bf16(dh, qql[ks], dl);
+                dl = mfma_bf16(dh, qqh[ks], dl);
+            }
+        }
+        float x[16], pv[16];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {  // P of keys 8 m + 4 hf + [0, 4) of this key half
+            const float4 pp = *reinterpret_cast<const float4*>(prow + kt * 64 + 32 * kb + 8 * m + 4 * hf);
+            pv[4 * m] = pp.x;
+            pv[4 * m + 1] = pp.y;
+            pv[4 * m + 2] = pp.z;
+            pv[4 * m + 3] = pp.w;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = dl[r] * 0.125f;
+        expm1_x16(x);
+        uint4 w1h[2], w1l[2], w2h[2], w2l[2];
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            uint32_t a[4], al[4], c[4], cl[4];
+#pragma unroll
+            for (int pr = 0; pr < 4; ++pr) {
+                const int r = 8 * st + 2 * pr;
+                const float u0 = pv[r] * x[r], u1 = pv[r + 1] * x[r + 1];  // w1
+                const float z0 = pv[r] + u0, z1 = pv[r + 1] + u1;          // w2
+                rho += u0 + u1;
+                a[pr] = bf16_pair(u0, u1);
+                al[pr] = bf16_pair(u0 - __uint_as_float(a[pr] << 16), u1 - __uint_as_float(a[pr] & 0xFFFF0000u));
+                c[pr] = bf16_pair(z0, z1);
+                cl[pr] = bf16_pair(z0 - __uint_as_float(c[pr] << 16), z1 - __uint_as_float(c[pr] & 0xFFFF0000u));
+            }
+            w1h[st] = make_uint4(a[0], a[1], a[2], a[3]);
+            w1l[st] = make_uint4(al[0], al[1], al[2], al[3]);
+            w2h[st] = make_uint4(c[0], c[1], c[2], c[3]);
+            w2l[st] = make_uint4(cl[0], cl[1], cl[2], cl[3]);
+        }
+        __syncthreads();  // transposed tiles written
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            const int k0 = 32 * kb + 16 * st + 4 * hf;
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+                const int c = 32 * cb + l31;
+                const uint4 vh = vt_frag(VTH, c, k0), vl = vt_frag(VTL, c, k0);
+                const uint4 eh = vt_frag(DVTH, c, k0), el = vt_frag(DVTL, c, k0);
+                hf32x16& a = cb ? acc1 : acc0;
+                a = mfma_bf16(vl, w1h[st], a);
+                a = mfma_bf16(vh, w1l[st], a);
+                a = mfma_bf16(vh, w1h[st], a);
+                a = mfma_bf16(el, w2h[st], a);
+                a = mfma_bf16(eh, w2l[st], a);
+                a = mfma_bf16(eh, w2h[st], a);
+            }
+        }
+    }
+    rho += __shfl_xor(rho, 32, 64);  // the lane pair of a query holds its two key quarters
+    if (kb == 1) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int cr = (r & 3) + 8 * (r >> 2) + 4 * hf;
+            accx[qb][cr][l31] = acc0[r];
+            accx[qb][32 + cr][l31] = acc1[r];
+        }
+        if (hf == 0) rhox[qb][l31] = rho;
+    }
+    __syncthreads();
+    if (kb == 0) {
+        const float rt = rho + rhox[qb][l31], inv = 1.0f / (1.0f + rt);
+        const int64_t orow = s0 + query;
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {  // channels 32 cb + 8 m + 4 hf + [0, 4)
+                const int c0 = 32 * cb + 8 * m + 4 * hf;
+                const float4 ov = *reinterpret_cast<const float4*>(o + orow * d + h * 64 + c0);
+                const hf32x16& a = cb ? acc1 : acc0;
+                float4 r4;
+                r4.x = (a[4 * m] + accx[qb][c0][l31] - rt * ov.x) * inv;
+                r4.y = (a[4 * m + 1] + accx[qb][c0 + 1][l31] - rt * ov.y) * inv;
+                r4.z = (a[4 * m + 2] + accx[qb][c0 + 2][l31] - rt * ov.z) * inv;
+                r4.w = (a[4 * m + 3] + accx[qb][c0 + 3][l31] - rt * ov.w) * inv;
+                *reinterpret_cast<float4*>(dout + (drow0 + orow) * d + h * 64 + c0) = r4;
+            }
+    }
+}
+
 unsigned blocks(int64_t n, int per = 256) { return (unsigned)((n + per - 1) / per); }
 
 }  // namespace
@@ -763,9 +905,9 @@ hipError_t lm_layernorm(const float* x, int64_t R, int d, float eps, float* u, f
 }
 
 hipError_t lm_attn_fwd(const float* q, const float* k, const float* v, int T, int S, int H, float* o, float* lse,
-                       hipStream_t s) {
+                       float* pc, hipStream_t s) {
     hipLaunchKernelGGL(lm_attn_fwd_kernel, dim3((unsigned)((T / S) * H * (S / 64))), dim3(256), 0, s, q, k, v, T, S,
-                       H, o, lse);
+                       H, o, lse, pc);
     return hipGetLastError();
 }
 
@@ -800,11 +942,11 @@ hipError_t lm_layernorm_delta(const float* x, const float* mu, const float* rs, 
     return hipGetLastError();
 }
 
-hipError_t lm_attn_delta(const float* q, const float* k, const float* v, const float* o, const float* lse,
+hipError_t lm_attn_delta(const float* q, const float* k, const float* v, const float* o, const float* pc,
                          const float* dq, const float* dk, const float* dv, int kc, int T, int S, int H, float* dout,
                          hipStream_t s) {
     hipLaunchKernelGGL(lm_attn_delta_kernel, dim3((unsigned)(kc * (T / S) * H * (S / 64))), dim3(256), 0, s, q, k, v,
-                       o, lse, dq, dk, dv, T, S, H, dout);
+                       o, pc, dq, dk, dv, T, S, H, dout);
     return hipGetLastError();
 }
 
