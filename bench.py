@@ -79,10 +79,11 @@ KERNEL_SOURCES = {
     "head_estimate_kernel": ["head_impl.hpp", "head_f32.hip", "head_bf16.hip", "head.hip", "dust_device.hpp"],
     "mlp_gemm2_kernel": ["mlp.hip", "dust_device.hpp", "dust_internal.hpp"],
     "head_subset_kernel": ["head_subset.hip", "dust_device.hpp", "dust_internal.hpp"],
-    "attn_v_kernel": ["attn.hip", "dust_device.hpp", "dust_internal.hpp"],
-    "attn_k_kernel": ["attn.hip", "dust_device.hpp", "dust_internal.hpp"],
-    "attn_q_kernel": ["attn.hip", "dust_device.hpp", "dust_internal.hpp"],
-    "lm_gemm_nt_kernel": ["lm.hip", "dust_internal.hpp"],
+    "attn_v_kernel": ["attn.hip", "dust_device.hpp", "dust_internal.hpp", "launch_events.hpp"],
+    "attn_k_kernel": ["attn.hip", "dust_device.hpp", "dust_internal.hpp", "launch_events.hpp"],
+    "attn_q_kernel": ["attn.hip", "dust_device.hpp", "dust_internal.hpp", "launch_events.hpp"],
+    "lm_gemm_nt_kernel": ["lm.hip", "lm_internal.hpp", "launch_events.hpp"],
+    "lm_head_delta_kernel": ["lm.hip", "lm_internal.hpp", "launch_events.hpp"],
 }
 
 
@@ -412,18 +413,20 @@ def cpu_baseline_lm(case, target_s):
                       f"passes, one causal attention for q/k/v, the C head estimator), {el:.1f} s"}
 
 
-def lm_gemm_flops(c):
+def lm_gemm_flops(c, head=True):
     """Flops of the GEMM launches of one step (2 x rows x out x in each): the clean
     forward; per draw of each layer-type pass the blocks after its first perturbed
-    point (block 0 keeps only what follows the point) and the head; the ES members
-    likewise (block 0's attention branch has no change yet); e = g_hat_O W_O."""
+    point (block 0 keeps only what follows the point) and, unless the fused head kernel
+    takes it (head=False), the head; the ES members likewise (block 0's attention branch
+    has no change yet); e = g_hat_O W_O."""
     T, d, n, V, L, K, M = c["T"], c["d"], c["n"], c["V"], c["L"], c["K"], c["M"]
-    attn, mlp, head = 2 * 4 * d * d, 2 * 2 * n * d, 2 * V * d
+    attn, mlp = 2 * 4 * d * d, 2 * 2 * n * d
+    head = 2 * V * d if head else 0
     full = attn + mlp
     first = {"emb": full, "o": mlp, "up": mlp // 2, "down": 0, "es": mlp}
     per_draw = {k: v + (L - 1) * full + head for k, v in first.items()}
     passes = K * T * (per_draw["emb"] + per_draw["o"] + per_draw["up"] + per_draw["down"])
-    return T * (L * full + head) + passes + 2 * M * T * per_draw["es"] + L * T * 2 * d * d
+    return T * (L * full + 2 * V * d) + passes + 2 * M * T * per_draw["es"] + L * T * 2 * d * d
 
 
 def run_lm(args, c, dust, torch):
@@ -450,27 +453,31 @@ def run_lm(args, c, dust, torch):
     for el in ev:
         for x in el:
             x.record(stream)
-    gs = [torch.cuda.Event(enable_timing=True) for _ in range(2048)]
-    ge = [torch.cuda.Event(enable_timing=True) for _ in range(2048)]
-    for x in gs + ge:
-        x.record(stream)
+    timed = {"lm_gemm": [[torch.cuda.Event(enable_timing=True) for _ in range(1024)] for _ in range(2)],
+             "lm_head": [[torch.cuda.Event(enable_timing=True) for _ in range(64)] for _ in range(2)]}
+    for pair in timed.values():
+        for x in pair[0] + pair[1]:
+            x.record(stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for kk in range(args.steps):
         ev[kk][0].record(stream)
         for j, st in enumerate((4, 5, 6, 7)):
             dust.set_stage_event(st, ev[kk][1 + j])
-        if kk == args.steps - 1:  # the last timed step also times each GEMM launch
-            dust.set_gemm_events(gs, ge)
+        if kk == args.steps - 1:  # the last timed step also times each launch of two kernels
+            for name, (a, b) in timed.items():
+                dust.set_kernel_events(name, a, b)
         step()
         ev[kk][5].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ngemm = dust.gemm_event_count()
-    dust.set_gemm_events(None, None)
+    per = {}
+    for name, (a, b) in timed.items():
+        n_l = dust.kernel_event_count(name)
+        dust.set_kernel_events(name, None, None)
+        per[name] = (n_l, float(sum(dust.event_elapsed_ms(a[j], b[j]) for j in range(n_l))))
     for st in (4, 5, 6, 7):
         dust.set_stage_event(st, None)
-    gemm_ms = float(sum(dust.event_elapsed_ms(gs[i], ge[i]) for i in range(ngemm)))
     names = ("clean_forward", "head_pass", "layer_type_passes", "attention_internals", "es_and_sgd")
     stages = {nm: float(np.mean([dust.event_elapsed_ms(x[j], x[j + 1]) for x in ev])) for j, nm in enumerate(names)}
     ms_per_step = wall * 1e3 / args.steps
@@ -478,20 +485,37 @@ def run_lm(args, c, dust, torch):
     td = ((5 + 3 * L) * c["K"] + 2 * c["M"]) * T
     ce = dust.lm_forward(cfg, params, tok, lab)
     torch.cuda.synchronize()
-    flops = lm_gemm_flops(c)
-    achieved = flops / (gemm_ms / 1e3) / 1e12
+    # fused head change: per draw and token, d x Vp products on bf16 MFMA, three each (hi/lo)
+    vp = -(-c["V"] // 128) * 128
+    head_flops = (4 * c["K"] + 2 * c["M"]) * T * vp * c["d"] * 2 * 3
+    gemm_flops = lm_gemm_flops(c, head=False)
+    lines = {
+        "lm_head_delta_kernel": {"bound": "mfma", "flops": head_flops, "peak": MFMA_BF16_PEAK_TFLOPS,
+                                 "launches": per["lm_head"][0], "ms": per["lm_head"][1],
+                                 "note": "issued bf16 MFMA flops (three products per fp32 product) of the fused "
+                                         "head change over its launches' durations (HIP events around each "
+                                         "launch of the last timed step)"},
+        "lm_gemm_nt_kernel": {"bound": "mfma", "flops": gemm_flops, "peak": MFMA_F32_PEAK_TFLOPS,
+                              "launches": per["lm_gemm"][0], "ms": per["lm_gemm"][1],
+                              "note": "fp32 MFMA flops of every launch of the GEMM kernel in one step over the "
+                                      "summed durations of those launches (HIP events around each launch)"},
+    }
+    roof = {}
+    for name, x in lines.items():
+        ach = x["flops"] / (x["ms"] / 1e3) / 1e12
+        roof[name] = {"bound": x["bound"], "kernel": name, "achieved": ach, "peak": x["peak"], "unit": "TFLOP/s",
+                      "frac": ach / x["peak"], "traffic": load_traffic(name, args.workload),
+                      "flops_per_launch": x["flops"] / max(x["launches"], 1), "launches_per_step": x["launches"],
+                      "kernel_ms": x["ms"] / max(x["launches"], 1), "kernel_ms_per_step": x["ms"],
+                      "note": x["note"]}
+    dom = max(roof, key=lambda k_: roof[k_]["kernel_ms_per_step"])
     out = {
-        "dtype": "f32 (fp32 MFMA GEMMs)",
+        "dtype": "f32 (fp32 MFMA GEMMs, bf16x3 MFMA head change and attention change)",
         "token_draws_per_step": td,
         "stages_ms": stages,
         "loss_after": float(ce.mean()),
-        "roofline": {"bound": "mfma", "kernel": "lm_gemm_nt_kernel", "achieved": achieved,
-                     "peak": MFMA_F32_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / MFMA_F32_PEAK_TFLOPS,
-                     "traffic": load_traffic("lm_gemm_nt_kernel", args.workload),
-                     "flops_per_launch": flops / max(ngemm, 1), "launches_per_step": ngemm,
-                     "kernel_ms": gemm_ms / max(ngemm, 1), "kernel_ms_per_step": gemm_ms,
-                     "note": "fp32 MFMA flops of every GEMM launch of one step over the summed durations of "
-                             "those launches (HIP events around each launch of the last timed step)"},
+        "roofline": roof[dom],
+        "roofline_other": [v_ for k_, v_ in roof.items() if k_ != dom],
     }
     return ms_per_step, td, out
 
@@ -514,9 +538,9 @@ def run_attn(args, c, dust, torch):
     # stages: 2 after the rewards, 0 after g_hat, 1 after G_WV
     stream = torch.cuda.current_stream()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    for el in ev:
-        for x in el:
-            x.record(stream)
+    ks, ke = ([torch.cuda.Event(enable_timing=True) for _ in range(64)] for _ in range(2))
+    for x in [y for el in ev for y in el] + ks + ke:
+        x.record(stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for kk in range(args.steps):
@@ -524,37 +548,43 @@ def run_attn(args, c, dust, torch):
         dust.set_stage_event(2, ev[kk][1])
         dust.set_stage_event(0, ev[kk][2])
         dust.set_stage_event(1, ev[kk][3])
+        if kk == args.steps - 1:  # the last timed step also times each launch of the main kernel
+            dust.set_kernel_events("attn_main", ks, ke)
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    nl = dust.kernel_event_count("attn_main")
+    dust.set_kernel_events("attn_main", None, None)
     for st in (0, 1, 2):
         dust.set_stage_event(st, None)
+    main_ms = float(sum(dust.event_elapsed_ms(ks[j], ke[j]) for j in range(nl)))
     att_ms = float(np.mean([dust.event_elapsed_ms(x[0], x[1]) for x in ev]))
     red_ms = float(np.mean([dust.event_elapsed_ms(x[1], x[2]) for x in ev]))
     out_ms = float(np.mean([dust.event_elapsed_ms(x[2], x[3]) for x in ev]))
     ms_per_step = wall * 1e3 / args.steps
-    # bf16 MFMA work of the attention passes: per (key tile <= query tile) pair of 64-token
-    # tiles and head, 2 * 64^3 flops per product, three products (hi/lo pairs) each: per draw
-    # one product (<a, e> for values, <a, q> or <k, a> for keys and queries); per chunk of 8
-    # draws the logits (and for keys and queries <v, e>); the clean statistics pass once
-    # (and <v, e> there for keys and queries)
+    # bf16 MFMA work of the main kernel's launches: per (key tile <= query tile) pair of
+    # 64-token tiles and head, 2 * 64^3 flops per product, three products (hi/lo pairs)
+    # each: per draw one product (<a, e> for values, <a, q> or <k, a> for keys and queries);
+    # per chunk of 8 draws the logits (and for keys and queries <v, e>)
     nkt = S // 64
     pairs = (T // S) * H * nkt * (nkt + 1) // 2
     per_pair = 2 * 64 ** 3 * 3
     part = {"v": nkt * H * 2 * T, "k": nkt * H * 4 * T, "q": H * T}[proj] * 4
     kc = max(1, min(64, (256 << 20) // part))
     chunks = sum(-(-min(kc, K - i0) // 8) for i0 in range(0, K, kc))
-    per_chunk, stats = (1, 1) if proj == "v" else (2, 2)
-    flops = pairs * per_pair * (K + per_chunk * chunks + stats)
-    achieved = flops / (att_ms / 1e3) / 1e12
+    per_chunk = 1 if proj == "v" else 2
+    flops = pairs * per_pair * (K + per_chunk * chunks)
+    achieved = flops / (main_ms / 1e3) / 1e12
     out = {
         "dtype": "f32 (bf16x3 MFMA products)",
         "stages_ms": {"attention_rewards": att_ms, "ghat_reduce": red_ms, "outer_product": out_ms},
         "roofline": {"bound": "mfma", "kernel": f"attn_{proj}_kernel", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
                      "traffic": load_traffic(f"attn_{proj}_kernel", args.workload),
-                     "flops_per_launch": flops, "kernel_ms": att_ms,
-                     "note": "issued bf16 MFMA flops of the attention passes (three products per fp32 product)"},
+                     "flops_per_launch": flops / max(nl, 1), "launches_per_step": nl,
+                     "kernel_ms": main_ms / max(nl, 1),
+                     "note": "issued bf16 MFMA flops of the main kernel (three products per fp32 product) over "
+                             "its launches' durations (HIP events around each launch of the last timed step)"},
     }
     return ms_per_step, out
 

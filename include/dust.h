@@ -89,15 +89,16 @@ const char *dust_last_error(void);
 dust_status dust_set_stage_event(int stage, void *event);
 
 /*
- * Profiling hook of the small-LM step (dust_lm_*): while set, each launch of its
- * GEMM kernel (C = A B^T, fp32) from this thread records starts[i] before and
- * ends[i] after it on the call's stream, i = 0, 1, ... for the first `capacity`
- * launches (hipEvent_t handles owned by the caller; the arrays are copied).
- * dust_gemm_event_count() returns how many launches were recorded since the hook
- * was set.  NULL arrays or capacity <= 0 clear it.
+ * Profiling hook: while set, each launch of the chosen kernel from this thread records
+ * starts[i] before and ends[i] after it on the call's stream, i = 0, 1, ... for the
+ * first `capacity` launches (hipEvent_t handles owned by the caller; the arrays are
+ * copied).  kernel 0 = the small-LM step's GEMM (C = A B^T, fp32), 1 = its fused head
+ * change, 2 = the main pass of dust_estimate_attn (query, key or value kernel).
+ * dust_kernel_event_count(kernel) returns how many launches were recorded since the
+ * hook was set (-1 for an unknown kernel).  NULL arrays or capacity <= 0 clear it.
  */
-dust_status dust_set_gemm_events(void *const *starts, void *const *ends, int capacity);
-int dust_gemm_event_count(void);
+dust_status dust_set_kernel_events(int kernel, void *const *starts, void *const *ends, int capacity);
+int dust_kernel_event_count(int kernel);
 
 /*
  * Noise export: the exact Gaussian values (and optionally the raw Philox words)

@@ -83,9 +83,10 @@ def lib():
         L.dust_estimate_linear.restype = ctypes.c_int
         L.dust_estimate_linear.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32,
                                            _f32, _u64, _u32, _u32, _u32, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
-        L.dust_set_gemm_events.restype = ctypes.c_int
-        L.dust_set_gemm_events.argtypes = [_vp, _vp, ctypes.c_int]
-        L.dust_gemm_event_count.restype = ctypes.c_int
+        L.dust_set_kernel_events.restype = ctypes.c_int
+        L.dust_set_kernel_events.argtypes = [ctypes.c_int, _vp, _vp, ctypes.c_int]
+        L.dust_kernel_event_count.restype = ctypes.c_int
+        L.dust_kernel_event_count.argtypes = [ctypes.c_int]
         for nm in ("dust_lm_param_count", "dust_lm_rewards_count", "dust_lm_workspace_bytes"):
             getattr(L, nm).restype = ctypes.c_size_t
         L.dust_lm_param_count.argtypes = [_vp]
@@ -150,20 +151,24 @@ def set_stage_event(stage: int, event) -> None:
 _hip = None
 
 
-def set_gemm_events(starts, ends) -> None:
-    """Record starts[i] / ends[i] (torch.cuda.Events that already exist) around the
-    i-th launch of the small-LM GEMM kernel from this thread; None clears."""
+TIMED_KERNELS = {"lm_gemm": 0, "lm_head": 1, "attn_main": 2}
+
+
+def set_kernel_events(kernel: str, starts, ends) -> None:
+    """Record starts[i] / ends[i] (torch.cuda.Events that already exist) around the i-th
+    launch of ``kernel`` (a key of TIMED_KERNELS) from this thread; None clears."""
+    kid = TIMED_KERNELS[kernel]
     if starts is None:
-        _check(lib().dust_set_gemm_events(None, None, 0))
+        _check(lib().dust_set_kernel_events(kid, None, None, 0))
         return
     n = min(len(starts), len(ends))
     arr_s = (_vp * n)(*[e.cuda_event for e in starts[:n]])
     arr_e = (_vp * n)(*[e.cuda_event for e in ends[:n]])
-    _check(lib().dust_set_gemm_events(arr_s, arr_e, n))
+    _check(lib().dust_set_kernel_events(kid, arr_s, arr_e, n))
 
 
-def gemm_event_count() -> int:
-    return int(lib().dust_gemm_event_count())
+def kernel_event_count(kernel: str) -> int:
+    return int(lib().dust_kernel_event_count(TIMED_KERNELS[kernel]))
 
 
 def event_elapsed_ms(start, end) -> float:

@@ -16,22 +16,25 @@
 // no difference of two outputs is formed (no cancellation).
 //
 // Kernels (heads of 64 channels, sequences of whole 64-token tiles):
-//   attn_lse_kernel   per (sequence, head, query tile): log-sum-exp of the
-//                     clean scaled logits of each query;
+//   attn_stats_kernel per (sequence, head, query tile): log-sum-exp of the
+//                     clean scaled logits of each query (and <e, o>);
 //   attn_v_kernel     per (sequence, head, key tile): the key tile's noise for
 //                     a chunk of draws is generated once into LDS; for every
 //                     query tile at or after it the transposed logits
 //                     K Q^T / sqrt(64) are recomputed, P = exp(L - lse), and
 //                     per draw G^T = A E^T on MFMA, then per query the column
 //                     sum of P (.) G^T: the partial c of this key tile;
-//   attn_suffix_kernel per (draw, sequence): c_s = sum of the partials,
-//                     r_t = -sigma sum_{s >= t} c_s by a reverse block scan;
+//   attn_k_kernel, attn_q_kernel: the same for keys and queries (two sums);
+//   attn_csum(_k)_kernel per (draw, token): c_s from the partials;
+//   attn_suffix_scan_kernel per (draw, sequence): r_t = -sigma sum_{s >= t} c_s
+//                     by a reverse block scan;
 //   attn_reduce_kernel per token: g_hat from the rewards, noise regenerated.
 // Products of two fp32 operands run on bf16 MFMA with both operands split into
 // pairs v = hi + lo and the three products lo.hi + hi.lo + hi.hi accumulated in
 // fp32 (each within about 3 2^-17 of fp32).
 #include "dust_device.hpp"
 #include "dust_internal.hpp"
+#include "launch_events.hpp"
 
 namespace dust {
 
@@ -525,84 +528,43 @@ __global__ void __launch_bounds__(VNT, 1) attn_q_kernel(AttnKArgs A, int kc) {
     }
 }
 
-// ---- key projection: c_s from the partial sums, r_t = -sum_{s >= t} c_s ---------
-__global__ void __launch_bounds__(256) attn_suffix_k_kernel(const float* __restrict__ cpart,
-                                                            const float* __restrict__ ob, int T, int S, int H,
-                                                            int i0, float* __restrict__ rew) {
-    __shared__ float cs[ASMAX];
-    __shared__ float sh[256];
-    const int nkt = S / AT, nb = T / S;
-    const int dd = blockIdx.x / nb, b = blockIdx.x % nb, tid = threadIdx.x;
-    const int per = (S + 255) / 256;
-    const int64_t s0 = (int64_t)b * S;
-    for (int s = tid; s < S; s += 256) {
-        float c = 0.f;
-        for (int h = 0; h < H; ++h) {
-            float rr = 0.f, mm = 0.f;
-            for (int kt = 0; kt <= s / AT; ++kt)
-#pragma unroll
-                for (int kh = 0; kh < 2; ++kh) {
-                    const float* pp = cpart + (((((int64_t)dd * nkt + kt) * H + h) * 2 + kh) * 2) * T + s0 + s;
-                    rr += pp[0];
-                    mm += pp[T];
-                }
-            c += (mm - rr * ob[(s0 + s) * H + h]) / (1.0f + rr);
-        }
-        cs[s] = c;
-    }
-    __syncthreads();
-    float tot = 0.f;
-    for (int j = per - 1; j >= 0; --j) {
-        const int s = tid * per + j;
-        if (s < S) {
-            tot += cs[s];
-            cs[s] = tot;
-        }
-    }
-    sh[tid] = tot;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-        const float v = tid + off < 256 ? sh[tid + off] : 0.f;
-        __syncthreads();
-        sh[tid] += v;
-        __syncthreads();
-    }
-    const float after = tid + 1 < 256 ? sh[tid + 1] : 0.f;
-    for (int j = 0; j < per; ++j) {
-        const int s = tid * per + j;
-        if (s < S) rew[(int64_t)(i0 + dd) * T + s0 + s] = -(cs[s] + after);
-    }
-}
-
-// ---- query projection: r_t = -sum over the heads of c_t --------------------------
-__global__ void __launch_bounds__(256) attn_heads_q_kernel(const float* __restrict__ cpart, int T, int H, int i0,
-                                                           int kc, float* __restrict__ rew) {
+// ---- key projection: c_t from the partial sums (one thread per draw and token) -----
+// c = sum over heads of (mu - rho <e, o>) / (1 + rho), rho and mu summed over the key
+// tiles up to the token's own and the key halves; written to rew[(i0 + dd) T + t] for
+// the suffix scan.
+__global__ void __launch_bounds__(256) attn_csum_k_kernel(const float* __restrict__ cpart,
+                                                          const float* __restrict__ ob, int T, int S, int H, int i0,
+                                                          int kc, float* __restrict__ rew) {
     const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (x >= (int64_t)kc * T) return;
     const int64_t dd = x / T, t = x % T;
-    float r = 0.f;
-    for (int h = 0; h < H; ++h) r += cpart[(dd * H + h) * T + t];
-    rew[(i0 + dd) * T + t] = r;
+    const int s = (int)(t % S), nkt = S / AT;
+    float c = 0.f;
+    for (int h = 0; h < H; ++h) {
+        float rr = 0.f, mm = 0.f;
+        for (int kt = 0; kt <= s / AT; ++kt)
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) {
+                const float* pp = cpart + ((((dd * nkt + kt) * H + h) * 2 + kh) * 2) * T + t;
+                rr += pp[0];
+                mm += pp[T];
+            }
+        c += (mm - rr * ob[t * H + h]) / (1.0f + rr);
+    }
+    rew[(i0 + dd) * T + t] = c;
 }
 
-// ---- rewards: c_s from the partials, r_t = -sigma sum_{s >= t} c_s -----------
-__global__ void __launch_bounds__(256) attn_suffix_kernel(const float* __restrict__ cpart, int T, int S, int H,
-                                                          int i0, float sigma, float* __restrict__ rew) {
+// ---- in place: rew_t = -scale sum_{s >= t, same sequence} c_s (one workgroup per
+// draw and sequence) ----------------------------------------------------------------
+__global__ void __launch_bounds__(256) attn_suffix_scan_kernel(float* __restrict__ rew, int T, int S, int i0,
+                                                               float scale) {
     __shared__ float cs[ASMAX];
     __shared__ float sh[256];
-    const int nkt = S / AT, nb = T / S;
+    const int nb = T / S;
     const int dd = blockIdx.x / nb, b = blockIdx.x % nb, tid = threadIdx.x;
     const int per = (S + 255) / 256;  // consecutive tokens per lane
-    const int64_t s0 = (int64_t)b * S;
-    for (int s = tid; s < S; s += 256) {
-        float c = 0.f;
-        for (int kt = 0; kt <= s / AT; ++kt)
-            for (int h = 0; h < H; ++h) {
-                const float* pp = cpart + (((int64_t)dd * nkt + kt) * H + h) * 2 * T + s0 + s;
-                c += pp[0] + pp[T];
-            }
-        cs[s] = c;
-    }
+    float* row = rew + (int64_t)(i0 + dd) * T + (int64_t)b * S;
+    for (int s = tid; s < S; s += 256) cs[s] = row[s];
     __syncthreads();
     float tot = 0.f;  // suffix sums within this lane's tokens, in place
     for (int j = per - 1; j >= 0; --j) {
@@ -623,8 +585,36 @@ __global__ void __launch_bounds__(256) attn_suffix_kernel(const float* __restric
     const float after = tid + 1 < 256 ? sh[tid + 1] : 0.f;
     for (int j = 0; j < per; ++j) {
         const int s = tid * per + j;
-        if (s < S) rew[(int64_t)(i0 + dd) * T + s0 + s] = -sigma * (cs[s] + after);
+        if (s < S) row[s] = -scale * (cs[s] + after);
     }
+}
+
+// ---- query projection: r_t = -sum over the heads of c_t --------------------------
+__global__ void __launch_bounds__(256) attn_heads_q_kernel(const float* __restrict__ cpart, int T, int H, int i0,
+                                                           int kc, float* __restrict__ rew) {
+    const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (x >= (int64_t)kc * T) return;
+    const int64_t dd = x / T, t = x % T;
+    float r = 0.f;
+    for (int h = 0; h < H; ++h) r += cpart[(dd * H + h) * T + t];
+    rew[(i0 + dd) * T + t] = r;
+}
+
+// ---- value projection: c_t = sum over key tiles, heads and key halves of the partials
+// (one thread per draw and token), written to rew[(i0 + dd) T + t] for the suffix scan
+__global__ void __launch_bounds__(256) attn_csum_kernel(const float* __restrict__ cpart, int T, int S, int H, int i0,
+                                                        int kc, float* __restrict__ rew) {
+    const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (x >= (int64_t)kc * T) return;
+    const int64_t dd = x / T, t = x % T;
+    const int s = (int)(t % S), nkt = S / AT;
+    float c = 0.f;
+    for (int kt = 0; kt <= s / AT; ++kt)
+        for (int h = 0; h < H; ++h) {
+            const float* pp = cpart + (((dd * nkt + kt) * H + h) * 2) * T + t;
+            c += pp[0] + pp[T];
+        }
+    rew[(i0 + dd) * T + t] = c;
 }
 
 // ---- g_hat_t = -(1/(K sigma)) sum_i r_t^(i) a_t^(i) ------------------------------
@@ -700,19 +690,30 @@ hipError_t launch_attn_rewards(int proj, const float* q, const float* k, const f
         const int kc = (int)(K - i0 < kcmax ? K - i0 : kcmax);
         AttnKArgs Ai = A;
         Ai.draw0 = draw_offset + (uint32_t)i0;
-        if (proj == 2) {
+        bool timed;
+        if ((err = launch_timer_begin(kTimedAttnMain, stream, timed)) != hipSuccess) return err;
+        if (proj == 2)
             hipLaunchKernelGGL(attn_v_kernel, dim3(grid), dim3(VNT), 0, stream, Ai, 0, kc);
-            if ((err = hipGetLastError()) != hipSuccess) return err;
-            hipLaunchKernelGGL(attn_suffix_kernel, dim3((unsigned)(kc * nb)), dim3(256), 0, stream, A.cpart, (int)T,
-                               (int)S, (int)H, (int)i0, sigma, rew);
-        } else if (proj == 1) {
+        else if (proj == 1)
             hipLaunchKernelGGL(attn_k_kernel, dim3(grid), dim3(VNT), 0, stream, Ai, kc);
-            if ((err = hipGetLastError()) != hipSuccess) return err;
-            hipLaunchKernelGGL(attn_suffix_k_kernel, dim3((unsigned)(kc * nb)), dim3(256), 0, stream, A.cpart, A.ob,
-                               (int)T, (int)S, (int)H, (int)i0, rew);
-        } else {
+        else
             hipLaunchKernelGGL(attn_q_kernel, dim3(grid), dim3(VNT), 0, stream, Ai, kc);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        if ((err = launch_timer_end(kTimedAttnMain, stream, timed)) != hipSuccess) return err;
+        const unsigned nthr = (unsigned)((kc * T + 255) / 256);
+        if (proj == 2) {
+            hipLaunchKernelGGL(attn_csum_kernel, dim3(nthr), dim3(256), 0, stream, A.cpart, (int)T, (int)S, (int)H,
+                               (int)i0, kc, rew);
             if ((err = hipGetLastError()) != hipSuccess) return err;
+            hipLaunchKernelGGL(attn_suffix_scan_kernel, dim3((unsigned)(kc * nb)), dim3(256), 0, stream, rew, (int)T,
+                               (int)S, (int)i0, sigma);
+        } else if (proj == 1) {
+            hipLaunchKernelGGL(attn_csum_k_kernel, dim3(nthr), dim3(256), 0, stream, A.cpart, A.ob, (int)T, (int)S,
+                               (int)H, (int)i0, kc, rew);
+            if ((err = hipGetLastError()) != hipSuccess) return err;
+            hipLaunchKernelGGL(attn_suffix_scan_kernel, dim3((unsigned)(kc * nb)), dim3(256), 0, stream, rew, (int)T,
+                               (int)S, (int)i0, 1.0f);
+        } else {
             hipLaunchKernelGGL(attn_heads_q_kernel, dim3((unsigned)((kc * T + 255) / 256)), dim3(256), 0, stream,
                                A.cpart, (int)T, (int)H, (int)i0, kc, rew);
         }

@@ -10,6 +10,12 @@
 
 #include "dust.h"
 #include "dust_internal.hpp"
+#include "launch_events.hpp"
+#include "lm_internal.hpp"
+
+namespace dust {
+thread_local LaunchEvents g_kernel_events[kTimedKernels];
+}
 
 namespace {
 
@@ -89,23 +95,28 @@ dust_status dust_set_stage_event(int stage, void* event) {
     return ok();
 }
 
-dust_status dust_set_gemm_events(void* const* starts, void* const* ends, int capacity) {
-    static thread_local std::vector<hipEvent_t> s_starts, s_ends;
-    dust::LaunchEvents& le = dust::g_gemm_events;
+dust_status dust_set_kernel_events(int kernel, void* const* starts, void* const* ends, int capacity) {
+    static thread_local std::vector<hipEvent_t> s_starts[dust::kTimedKernels], s_ends[dust::kTimedKernels];
+    if (kernel < 0 || kernel >= dust::kTimedKernels)
+        return fail(DUST_E_INVALID, "dust_set_kernel_events: kernel must be in [0, %d)", (int)dust::kTimedKernels);
+    dust::LaunchEvents& le = dust::g_kernel_events[kernel];
     if (!starts || !ends || capacity <= 0) {
         le = dust::LaunchEvents{};
         return ok();
     }
-    s_starts.assign(reinterpret_cast<hipEvent_t const*>(starts), reinterpret_cast<hipEvent_t const*>(starts) + capacity);
-    s_ends.assign(reinterpret_cast<hipEvent_t const*>(ends), reinterpret_cast<hipEvent_t const*>(ends) + capacity);
-    le.starts = s_starts.data();
-    le.ends = s_ends.data();
+    s_starts[kernel].assign(reinterpret_cast<hipEvent_t const*>(starts),
+                            reinterpret_cast<hipEvent_t const*>(starts) + capacity);
+    s_ends[kernel].assign(reinterpret_cast<hipEvent_t const*>(ends), reinterpret_cast<hipEvent_t const*>(ends) + capacity);
+    le.starts = s_starts[kernel].data();
+    le.ends = s_ends[kernel].data();
     le.capacity = capacity;
     le.count = 0;
     return ok();
 }
 
-int dust_gemm_event_count(void) { return dust::g_gemm_events.count; }
+int dust_kernel_event_count(int kernel) {
+    return kernel >= 0 && kernel < dust::kTimedKernels ? dust::g_kernel_events[kernel].count : -1;
+}
 
 dust_status dust_noise(uint64_t seed, uint32_t layer, uint32_t draw_offset, int64_t K, uint32_t token_offset,
                        int64_t T, int64_t n, uint32_t* raw, float* gauss, void* stream) {

@@ -30,6 +30,8 @@
 
 #include "dust_device.hpp"
 #include "dust_internal.hpp"
+#include "launch_events.hpp"
+#include "lm_internal.hpp"
 
 namespace dust {
 namespace {
@@ -873,24 +875,15 @@ unsigned blocks(int64_t n, int per = 256) { return (unsigned)((n + per - 1) / pe
 }  // namespace
 
 // ---- launchers (arguments validated by the caller) ------------------------------
-thread_local LaunchEvents g_gemm_events;
-
 hipError_t lm_gemm_nt(const float* A, const float* B, float* C, int64_t M, int64_t N, int64_t K, const float* alpha,
                       bool accumulate, hipStream_t s) {
-    LaunchEvents& le = g_gemm_events;
-    const bool timed = le.starts && le.count < le.capacity;
-    if (timed) {
-        const hipError_t e = hipEventRecord(le.starts[le.count], s);
-        if (e != hipSuccess) return e;
-    }
+    bool timed;
+    hipError_t e = launch_timer_begin(kTimedLmGemm, s, timed);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(lm_gemm_nt_kernel, dim3((unsigned)(M / GB), (unsigned)((N + GB - 1) / GB)), dim3(256), 0, s,
                        A, B, C, (int)M, (int)N, (int)K, alpha, accumulate ? 1 : 0);
-    hipError_t e = hipGetLastError();
-    if (e == hipSuccess && timed) {
-        e = hipEventRecord(le.ends[le.count], s);
-        ++le.count;
-    }
-    return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return launch_timer_end(kTimedLmGemm, s, timed);
 }
 
 hipError_t lm_embed(const float* emb, const float* pos, const int32_t* tok, int T, int S, int d, int V, float* x,
@@ -998,13 +991,17 @@ hipError_t lm_head_delta(const float* du, const uint16_t* whi, const uint16_t* w
                          int T, int Vp, int vseg, int nseg, float* part, hipStream_t s) {
     const int64_t npairs = (int64_t)(T / 64) * nseg, ngr = (kc + HDG - 1) / HDG;
     const dim3 grid((unsigned)(8 * ngr * ((npairs + 7) / 8)));
+    bool timed;
+    hipError_t e = launch_timer_begin(kTimedLmHead, s, timed);
+    if (e != hipSuccess) return e;
     if (d == 64)
         hipLaunchKernelGGL(lm_head_delta_kernel<4>, grid, dim3(256), 0, s, du, whi, wlo, prob, T, Vp, vseg, nseg, kc,
                            part);
     else
         hipLaunchKernelGGL(lm_head_delta_kernel<8>, grid, dim3(256), 0, s, du, whi, wlo, prob, T, Vp, vseg, nseg, kc,
                            part);
-    return hipGetLastError();
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return launch_timer_end(kTimedLmHead, s, timed);
 }
 
 hipError_t lm_head_reward(const float* du, const float* whead, const int32_t* labels, const float* part, int T, int V,
