@@ -82,7 +82,7 @@ KERNEL_SOURCES = {
     "attn_v_kernel": ["attn.hip", "dust_device.hpp", "dust_internal.hpp", "launch_events.hpp"],
     "attn_k_kernel": ["attn.hip", "dust_device.hpp", "dust_internal.hpp", "launch_events.hpp"],
     "attn_q_kernel": ["attn.hip", "dust_device.hpp", "dust_internal.hpp", "launch_events.hpp"],
-    "lm_gemm_nt_kernel": ["lm.hip", "lm_internal.hpp", "launch_events.hpp"],
+    "lm_gemm_x3_kernel": ["lm.hip", "lm_internal.hpp", "launch_events.hpp"],
     "lm_head_delta_kernel": ["lm.hip", "lm_internal.hpp", "launch_events.hpp"],
 }
 
@@ -413,20 +413,19 @@ def cpu_baseline_lm(case, target_s):
                       f"passes, one causal attention for q/k/v, the C head estimator), {el:.1f} s"}
 
 
-def lm_gemm_flops(c, head=True):
-    """Flops of the GEMM launches of one step (2 x rows x out x in each): the clean
-    forward; per draw of each layer-type pass the blocks after its first perturbed
-    point (block 0 keeps only what follows the point) and, unless the fused head kernel
-    takes it (head=False), the head; the ES members likewise (block 0's attention branch
-    has no change yet); e = g_hat_O W_O."""
-    T, d, n, V, L, K, M = c["T"], c["d"], c["n"], c["V"], c["L"], c["K"], c["M"]
+def lm_change_gemm_flops(c):
+    """Flops of the change-row GEMMs of one step (2 x rows x out x in each): per draw of
+    each layer-type pass the blocks after its first perturbed point (block 0 keeps only
+    what follows the point), the ES members likewise (block 0's attention branch has no
+    change yet).  The head's change is the fused head kernel's."""
+    T, d, n, L, K, M = c["T"], c["d"], c["n"], c["L"], c["K"], c["M"]
     attn, mlp = 2 * 4 * d * d, 2 * 2 * n * d
-    head = 2 * V * d if head else 0
+    head = 0
     full = attn + mlp
     first = {"emb": full, "o": mlp, "up": mlp // 2, "down": 0, "es": mlp}
     per_draw = {k: v + (L - 1) * full + head for k, v in first.items()}
     passes = K * T * (per_draw["emb"] + per_draw["o"] + per_draw["up"] + per_draw["down"])
-    return T * (L * full + 2 * V * d) + passes + 2 * M * T * per_draw["es"] + L * T * 2 * d * d
+    return passes + 2 * M * T * per_draw["es"]
 
 
 def run_lm(args, c, dust, torch):
@@ -488,17 +487,18 @@ def run_lm(args, c, dust, torch):
     # fused head change: per draw and token, d x Vp products on bf16 MFMA, three each (hi/lo)
     vp = -(-c["V"] // 128) * 128
     head_flops = (4 * c["K"] + 2 * c["M"]) * T * vp * c["d"] * 2 * 3
-    gemm_flops = lm_gemm_flops(c, head=False)
+    gemm_flops = 3 * lm_change_gemm_flops(c)
     lines = {
         "lm_head_delta_kernel": {"bound": "mfma", "flops": head_flops, "peak": MFMA_BF16_PEAK_TFLOPS,
                                  "launches": per["lm_head"][0], "ms": per["lm_head"][1],
                                  "note": "issued bf16 MFMA flops (three products per fp32 product) of the fused "
                                          "head change over its launches' durations (HIP events around each "
                                          "launch of the last timed step)"},
-        "lm_gemm_nt_kernel": {"bound": "mfma", "flops": gemm_flops, "peak": MFMA_F32_PEAK_TFLOPS,
+        "lm_gemm_x3_kernel": {"bound": "mfma", "flops": gemm_flops, "peak": MFMA_BF16_PEAK_TFLOPS,
                               "launches": per["lm_gemm"][0], "ms": per["lm_gemm"][1],
-                              "note": "fp32 MFMA flops of every launch of the GEMM kernel in one step over the "
-                                      "summed durations of those launches (HIP events around each launch)"},
+                              "note": "issued bf16 MFMA flops (three products per fp32 product) of every launch of "
+                                      "the change-row GEMM in one step over the summed durations of those "
+                                      "launches (HIP events around each launch)"},
     }
     roof = {}
     for name, x in lines.items():
@@ -510,7 +510,7 @@ def run_lm(args, c, dust, torch):
                       "note": x["note"]}
     dom = max(roof, key=lambda k_: roof[k_]["kernel_ms_per_step"])
     out = {
-        "dtype": "f32 (fp32 MFMA GEMMs, bf16x3 MFMA head change and attention change)",
+        "dtype": "f32 (clean forward on fp32 MFMA; change rows on bf16x3 MFMA)",
         "token_draws_per_step": td,
         "stages_ms": stages,
         "loss_after": float(ce.mean()),

@@ -92,8 +92,9 @@ dust_status dust_set_stage_event(int stage, void *event);
  * Profiling hook: while set, each launch of the chosen kernel from this thread records
  * starts[i] before and ends[i] after it on the call's stream, i = 0, 1, ... for the
  * first `capacity` launches (hipEvent_t handles owned by the caller; the arrays are
- * copied).  kernel 0 = the small-LM step's GEMM (C = A B^T, fp32), 1 = its fused head
- * change, 2 = the main pass of dust_estimate_attn (query, key or value kernel).
+ * copied).  kernel 0 = the small-LM step's GEMM of change rows (C = A B^T on bf16x3
+ * MFMA), 1 = its fused head change, 2 = the main pass of dust_estimate_attn (query, key
+ * or value kernel).
  * dust_kernel_event_count(kernel) returns how many launches were recorded since the
  * hook was set (-1 for an unknown kernel).  NULL arrays or capacity <= 0 clear it.
  */

@@ -541,7 +541,7 @@ struct LmLayout {
     size_t HBHI, HBLO, PP, PART;
     size_t X[kLmMaxL + 1], U1[kLmMaxL], Q[kLmMaxL], Kk[kLmMaxL], Vv[kLmMaxL], O[kLmMaxL], BA[kLmMaxL], XM[kLmMaxL],
         U2[kLmMaxL], BM[kLmMaxL], Hh[kLmMaxL], Mm[kLmMaxL], MU1[kLmMaxL], RS1[kLmMaxL], MU2[kLmMaxL], RS2[kLmMaxL],
-        LSE[kLmMaxL], PC[kLmMaxL], GO[kLmMaxL], GUP[kLmMaxL], GDN[kLmMaxL];
+        LSE[kLmMaxL], PC[kLmMaxL], GO[kLmMaxL], GUP[kLmMaxL], GDN[kLmMaxL], WSH[kLmMaxL], WSL[kLmMaxL];
     size_t UF, MUF, RSF, Z, LSEZ, CE;
     size_t DX, DU, DQ, DK, DV, DO, DB, DH, DM, DZ;
     size_t REWS, REWES, DL, GE, E, WOT, SUB, sub_bytes, total;
@@ -582,6 +582,9 @@ LmLayout lm_layout(const LmDims& D, int64_t K, int64_t M, int64_t chunk) {
         L.GO[l] = take(T * d);
         L.GUP[l] = take(T * n);
         L.GDN[l] = take(T * d);
+        // bf16 parts of the block's weights (W_Q, W_K, W_V, W_O, W_1, W_2 as in the parameters)
+        L.WSH[l] = take((4 * d * d + 2 * n * d) / 2);
+        L.WSL[l] = take((4 * d * d + 2 * n * d) / 2);
     }
     L.X[D.L] = take(T * d);
     L.UF = take(T * d);
@@ -678,6 +681,9 @@ hipError_t lm_clean_forward(const LmRun& R) {
         LM_TRY(dust::lm_residual(R.f(L.XM[l]), R.f(L.BM[l]), p + R.P.scal + 2 * l + 1, D.T * D.d, R.f(L.X[l + 1]),
                                  st));
     }
+    for (int64_t l = 0; l < D.L; ++l)  // bf16 parts of the block's weights, for the change GEMMs
+        LM_TRY(dust::lm_split(p + R.P.wq(l), 1, 1, (int)R.P.per_layer, reinterpret_cast<uint16_t*>(R.ws + L.WSH[l]),
+                              reinterpret_cast<uint16_t*>(R.ws + L.WSL[l]), st));
     LM_TRY(dust::lm_layernorm(R.f(L.X[D.L]), T, d, D.eps, R.f(L.UF), R.f(L.MUF), R.f(L.RSF), st));
     LM_TRY(dust::lm_gemm_nt(R.f(L.UF), p + R.P.head, R.f(L.Z), T, D.V, d, nullptr, false, st));
     if (L.fused)
@@ -702,6 +708,13 @@ hipError_t lm_delta_chunk(const LmRun& R, int kind, int kn, uint32_t draw0, floa
     float *DX = R.f(L.DX), *DU = R.f(L.DU), *DQ = R.f(L.DQ), *DK = R.f(L.DK), *DV = R.f(L.DV), *DO = R.f(L.DO),
           *DB = R.f(L.DB), *DH = R.f(L.DH), *DM = R.f(L.DM), *DZ = L.fused ? nullptr : R.f(L.DZ);
     auto zero = [&](float* ptr, int64_t count) { return hipMemsetAsync(ptr, 0, (size_t)count * sizeof(float), st); };
+    // bf16 parts of block l's weight at parameter offset `off`
+    auto wh = [&](int64_t l, int64_t off) {
+        return reinterpret_cast<const uint16_t*>(R.ws + L.WSH[l]) + (off - R.P.wq(l));
+    };
+    auto wl = [&](int64_t l, int64_t off) {
+        return reinterpret_cast<const uint16_t*>(R.ws + L.WSL[l]) + (off - R.P.wq(l));
+    };
     bool live = false;  // whether DX holds a change yet
     if (kind == 0) {
         LM_TRY(zero(DX, rows * d));
@@ -712,12 +725,12 @@ hipError_t lm_delta_chunk(const LmRun& R, int kind, int kn, uint32_t draw0, floa
         const int64_t wq = R.P.wq(l);
         if (live) {
             LM_TRY(dust::lm_layernorm_delta(R.f(L.X[l]), R.f(L.MU1[l]), R.f(L.RS1[l]), DX, rows, T, d, DU, st));
-            LM_TRY(dust::lm_gemm_nt(DU, p + wq, DQ, rows, d, d, nullptr, false, st));
-            LM_TRY(dust::lm_gemm_nt(DU, p + wq + D.d * D.d, DK, rows, d, d, nullptr, false, st));
-            LM_TRY(dust::lm_gemm_nt(DU, p + wq + 2 * D.d * D.d, DV, rows, d, d, nullptr, false, st));
+            LM_TRY(dust::lm_gemm_x3(DU, wh(l, wq), wl(l, wq), DQ, rows, d, d, st));
+            LM_TRY(dust::lm_gemm_x3(DU, wh(l, wq + D.d * D.d), wl(l, wq + D.d * D.d), DK, rows, d, d, st));
+            LM_TRY(dust::lm_gemm_x3(DU, wh(l, wq + 2 * D.d * D.d), wl(l, wq + 2 * D.d * D.d), DV, rows, d, d, st));
             LM_TRY(dust::lm_attn_delta(R.f(L.Q[l]), R.f(L.Kk[l]), R.f(L.Vv[l]), R.f(L.O[l]), R.f(L.PC[l]), DQ, DK,
                                        DV, kn, T, (int)D.S, (int)D.H, DO, st));
-            LM_TRY(dust::lm_gemm_nt(DO, p + R.P.wo(l), DB, rows, d, d, nullptr, false, st));
+            LM_TRY(dust::lm_gemm_x3(DO, wh(l, R.P.wo(l)), wl(l, R.P.wo(l)), DB, rows, d, d, st));
         } else if (kind == 1 || es) {
             LM_TRY(zero(DB, rows * d));
         }
@@ -730,7 +743,7 @@ hipError_t lm_delta_chunk(const LmRun& R, int kind, int kn, uint32_t draw0, floa
         }
         if (live) {
             LM_TRY(dust::lm_layernorm_delta(R.f(L.XM[l]), R.f(L.MU2[l]), R.f(L.RS2[l]), DX, rows, T, d, DU, st));
-            LM_TRY(dust::lm_gemm_nt(DU, p + R.P.w1(l), DH, rows, n, d, nullptr, false, st));
+            LM_TRY(dust::lm_gemm_x3(DU, wh(l, R.P.w1(l)), wl(l, R.P.w1(l)), DH, rows, n, d, st));
         } else if (kind == 2) {
             LM_TRY(zero(DH, rows * n));
         }
@@ -738,7 +751,7 @@ hipError_t lm_delta_chunk(const LmRun& R, int kind, int kn, uint32_t draw0, floa
         const bool mlp = live || kind == 2;
         if (mlp) {
             LM_TRY(dust::lm_gelu_delta(R.f(L.Hh[l]), DH, D.T * D.n, rows * n, DM, st));
-            LM_TRY(dust::lm_gemm_nt(DM, p + R.P.w2(l), DB, rows, d, n, nullptr, false, st));
+            LM_TRY(dust::lm_gemm_x3(DM, wh(l, R.P.w2(l)), wl(l, R.P.w2(l)), DB, rows, d, n, st));
         } else if (kind == 3) {
             LM_TRY(zero(DB, rows * d));
         }

@@ -870,6 +870,94 @@ __global__ void __launch_bounds__(256) lm_attn_delta_kernel(const float* __restr
     }
 }
 
+// ---- change rows times a weight on bf16x3 MFMA: C = A B^T ----------------------------
+// A [M, K] fp32 (change rows, split into bf16 parts as they are read), B [N, K] given as
+// bf16 parts Bh, Bl (the weight split once per step).  Workgroup tile 128 rows x 128
+// columns, 4 waves of 64 x 64 (2 x 2 MFMA blocks); B's parts go through LDS in chunks
+// of 64 channels, A's fragments come from global memory.  M % 128 == 0 or the rows past
+// M are not stored; columns past N read zero weights and are not stored; K % 64 == 0.
+constexpr int XT = 128, XK = 64;
+
+__global__ void __launch_bounds__(256) lm_gemm_x3_kernel(const float* __restrict__ A, const uint16_t* __restrict__ Bh,
+                                                         const uint16_t* __restrict__ Bl, float* __restrict__ C,
+                                                         int M, int N, int K) {
+    __shared__ __align__(16) uint4 SH[XT][XK / 8 + 1];  // [column][8-channel piece], padded
+    __shared__ __align__(16) uint4 SL[XT][XK / 8 + 1];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w & 1, wn = w >> 1, hf = lane >> 5;
+    const int64_t m0 = (int64_t)blockIdx.x * XT, n0 = (int64_t)blockIdx.y * XT;
+    hf32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = hf32x16{};
+    // this lane's A rows (clamped to M - 1: rows past M are computed but never stored)
+    const float* arow[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int64_t r = min(m0 + 64 * wm + 32 * i + (lane & 31), (int64_t)M - 1);
+        arow[i] = A + r * K + 8 * hf;
+    }
+    for (int k0 = 0; k0 < K; k0 += XK) {
+        // this chunk's A values, in flight while the weight parts are staged
+        float4 av[2][XK / 16][2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int ks = 0; ks < XK / 16; ++ks) {
+                av[i][ks][0] = *reinterpret_cast<const float4*>(arow[i] + k0 + 16 * ks);
+                av[i][ks][1] = *reinterpret_cast<const float4*>(arow[i] + k0 + 16 * ks + 4);
+            }
+        __syncthreads();  // the previous chunk's weight parts are used up
+        // 128 columns x 8 pieces of 8 channels, hi and lo: 1024 uint4 each, 4 per thread
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int f = threadIdx.x + 256 * u, col = f >> 3, pc = f & 7;
+            const int64_t n = n0 + col;
+            uint4 h = make_uint4(0u, 0u, 0u, 0u), l = h;
+            if (n < N) {
+                h = *reinterpret_cast<const uint4*>(Bh + n * K + k0 + 8 * pc);
+                l = *reinterpret_cast<const uint4*>(Bl + n * K + k0 + 8 * pc);
+            }
+            SH[col][pc] = h;
+            SL[col][pc] = l;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < XK / 16; ++ks) {
+            uint4 ah[2], al[2], bh[2], bl[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) split8(av[i][ks][0], av[i][ks][1], ah[i], al[i]);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int col = 64 * wn + 32 * j + (lane & 31);
+                bh[j] = SH[col][2 * ks + hf];
+                bl[j] = SL[col][2 * ks + hf];
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    acc[i][j] = mfma_bf16(al[i], bh[j], acc[i][j]);
+                    acc[i][j] = mfma_bf16(ah[i], bl[j], acc[i][j]);
+                    acc[i][j] = mfma_bf16(ah[i], bh[j], acc[i][j]);
+                }
+        }
+    }
+    // D[row][col]: lane holds column lane & 31 and rows (r & 3) + 8 (r >> 2) + 4 hf
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int64_t col = n0 + 64 * wn + 32 * j + (lane & 31);
+        if (col >= N) continue;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t row = m0 + 64 * wm + 32 * i + (r & 3) + 8 * (r >> 2) + 4 * hf;
+                if (row < M) C[row * N + col] = acc[i][j][r];
+            }
+    }
+}
+
 unsigned blocks(int64_t n, int per = 256) { return (unsigned)((n + per - 1) / per); }
 
 }  // namespace
@@ -877,13 +965,9 @@ unsigned blocks(int64_t n, int per = 256) { return (unsigned)((n + per - 1) / pe
 // ---- launchers (arguments validated by the caller) ------------------------------
 hipError_t lm_gemm_nt(const float* A, const float* B, float* C, int64_t M, int64_t N, int64_t K, const float* alpha,
                       bool accumulate, hipStream_t s) {
-    bool timed;
-    hipError_t e = launch_timer_begin(kTimedLmGemm, s, timed);
-    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(lm_gemm_nt_kernel, dim3((unsigned)(M / GB), (unsigned)((N + GB - 1) / GB)), dim3(256), 0, s,
                        A, B, C, (int)M, (int)N, (int)K, alpha, accumulate ? 1 : 0);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    return launch_timer_end(kTimedLmGemm, s, timed);
+    return hipGetLastError();
 }
 
 hipError_t lm_embed(const float* emb, const float* pos, const int32_t* tok, int T, int S, int d, int V, float* x,
@@ -1009,6 +1093,17 @@ hipError_t lm_head_reward(const float* du, const float* whead, const int32_t* la
     hipLaunchKernelGGL(lm_head_reward_kernel, dim3(blocks(rows, 4)), dim3(256), 0, s, du, whead, labels, part, T, V, d,
                        nseg, rows, rew);
     return hipGetLastError();
+}
+
+hipError_t lm_gemm_x3(const float* A, const uint16_t* Bh, const uint16_t* Bl, float* C, int64_t M, int64_t N,
+                      int64_t K, hipStream_t s) {
+    bool timed;
+    hipError_t e = launch_timer_begin(kTimedLmGemm, s, timed);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(lm_gemm_x3_kernel, dim3((unsigned)((M + XT - 1) / XT), (unsigned)((N + XT - 1) / XT)),
+                       dim3(256), 0, s, A, Bh, Bl, C, (int)M, (int)N, (int)K);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return launch_timer_end(kTimedLmGemm, s, timed);
 }
 
 hipError_t lm_transpose(const float* W, int R, int C, float* WT, hipStream_t s) {
