@@ -132,7 +132,8 @@ def write_traffic(args):
     same two counters on a plain copy of --copy-calibration MiB) into the traffic
     file of the workload's dominant kernel."""
     kernel = ("head_subset_kernel" if args.subset else "head_estimate_kernel") if args.workload in (1, 2, 4) \
-        else f"attn_{args.attn_proj}_kernel" if args.workload == 6 else "mlp_gemm2_kernel"
+        else f"attn_{args.attn_proj}_kernel" if args.workload == 6 \
+        else "lm_head_delta_kernel" if args.workload == 7 else "mlp_gemm2_kernel"
     copy_bytes = args.copy_calibration << 20
     if copy_bytes <= 0:
         sys.exit("--traffic-from needs --copy-calibration MIB (the size the copy runs used)")
