@@ -559,10 +559,11 @@ __device__ __forceinline__ void expm1_x16(float (&x)[16]) {
 // vocabulary block of the segment, holds its W_head fragments and the 64 tokens'
 // probabilities in registers and runs all the group's rows against them.  Workgroups
 // of one (token block, segment) run on one XCD (workgroup id mod 8), sharing its L2.
-constexpr int HDG = 4;  // draws per workgroup
+constexpr int HDG = 4;   // draws per workgroup
+constexpr int HW = 8;    // waves per workgroup (two per SIMD)
 
 template <int KS>  // d = 16 KS
-__global__ void __launch_bounds__(256) lm_head_delta_kernel(const float* __restrict__ du,
+__global__ void __launch_bounds__(64 * HW) lm_head_delta_kernel(const float* __restrict__ du,
                                                             const uint16_t* __restrict__ whi,
                                                             const uint16_t* __restrict__ wlo,
                                                             const float* __restrict__ prob, int T, int Vp, int vseg,
@@ -570,7 +571,7 @@ __global__ void __launch_bounds__(256) lm_head_delta_kernel(const float* __restr
     constexpr int D = 16 * KS, UNITS = HDG * 64 * KS * 2;  // 16-byte units of one group's parts
     __shared__ uint4 UH[UNITS];
     __shared__ uint4 UL[UNITS];
-    __shared__ float red[4][HDG][64];
+    __shared__ float red[HW][HDG][64];
     const int ngr = (kc + HDG - 1) / HDG;
     const int id = blockIdx.x, xcd = id & 7, loc = id >> 3;
     const int pair = xcd + 8 * (loc / ngr), g = loc % ngr;
@@ -579,7 +580,7 @@ __global__ void __launch_bounds__(256) lm_head_delta_kernel(const float* __restr
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hf = lane >> 5;
     // unit (j, row, ks, h) = 8 channels 16 ks + 8 h of row `row` of draw j; stored at
     // ((j 64 + row) KS + (ks ^ (row & (KS - 1)))) 2 + h so that a wave's 32 rows spread over the banks
-    for (int u = threadIdx.x; u < dn * 64 * KS * 2; u += 256) {
+    for (int u = threadIdx.x; u < dn * 64 * KS * 2; u += 64 * HW) {
         const int h = u & 1, ks = (u >> 1) % KS, row = (u / (2 * KS)) % 64, j = u / (2 * KS * 64);
         const float* a = du + ((int64_t)(g * HDG + j) * T + (int64_t)tb * 64 + row) * D + 16 * ks + 8 * h;
         uint4 hi, lo;
@@ -593,7 +594,7 @@ __global__ void __launch_bounds__(256) lm_head_delta_kernel(const float* __restr
 #pragma unroll
     for (int j = 0; j < HDG; ++j) s[j][0] = s[j][1] = 0.f;
     const int vb = sg * vseg, ve = min(Vp, vb + vseg);
-    for (int v0 = vb + 32 * w; v0 < ve; v0 += 128) {
+    for (int v0 = vb + 32 * w; v0 < ve; v0 += 32 * HW) {
         uint4 ahi[KS], alo[KS];  // W_head rows v0 + (lane & 31), channels 16 ks + 8 hf + [0, 8)
         const uint16_t* bh = whi + (int64_t)(v0 + (lane & 31)) * D + 8 * hf;
         const uint16_t* bl = wlo + (int64_t)(v0 + (lane & 31)) * D + 8 * hf;
@@ -602,43 +603,36 @@ __global__ void __launch_bounds__(256) lm_head_delta_kernel(const float* __restr
             ahi[ks] = *reinterpret_cast<const uint4*>(bh + 16 * ks);
             alo[ks] = *reinterpret_cast<const uint4*>(bl + 16 * ks);
         }
-        float pv[2][16];  // p of this lane's token (column) at the 16 vocabulary rows it holds
 #pragma unroll
-        for (int th = 0; th < 2; ++th) {
+        for (int th = 0; th < 2; ++th) {  // token half: 32 tokens as the MFMA columns
+            float pv[16];  // p of this lane's token (column) at the 16 vocabulary rows it holds
             const float* pp = prob + ((int64_t)tb * 64 + 32 * th + (lane & 31)) * Vp + v0 + 4 * hf;
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const float4 q = *reinterpret_cast<const float4*>(pp + 8 * m);
-                pv[th][4 * m] = q.x;
-                pv[th][4 * m + 1] = q.y;
-                pv[th][4 * m + 2] = q.z;
-                pv[th][4 * m + 3] = q.w;
+                pv[4 * m] = q.x;
+                pv[4 * m + 1] = q.y;
+                pv[4 * m + 2] = q.z;
+                pv[4 * m + 3] = q.w;
             }
-        }
-        for (int j = 0; j < dn; ++j) {
-            hf32x16 c0 = {}, c1 = {};
+            const int row = 32 * th + (lane & 31);
+            for (int j = 0; j < dn; ++j) {
+                hf32x16 c = {};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int r0 = lane & 31, r1 = 32 + (lane & 31);
-                const int a0 = ((j * 64 + r0) * KS + (ks ^ (r0 & (KS - 1)))) * 2 + hf;
-                const int a1 = ((j * 64 + r1) * KS + (ks ^ (r1 & (KS - 1)))) * 2 + hf;
-                const uint4 h0 = UH[a0], l0 = UL[a0], h1 = UH[a1], l1 = UL[a1];
-                c0 = mfma_bf16(alo[ks], h0, c0);
-                c1 = mfma_bf16(alo[ks], h1, c1);
-                c0 = mfma_bf16(ahi[ks], l0, c0);
-                c1 = mfma_bf16(ahi[ks], l1, c1);
-                c0 = mfma_bf16(ahi[ks], h0, c0);
-                c1 = mfma_bf16(ahi[ks], h1, c1);
-            }
-#pragma unroll
-            for (int th = 0; th < 2; ++th) {
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int at = ((j * 64 + row) * KS + (ks ^ (row & (KS - 1)))) * 2 + hf;
+                    const uint4 h = UH[at], l = UL[at];
+                    c = mfma_bf16(alo[ks], h, c);
+                    c = mfma_bf16(ahi[ks], l, c);
+                    c = mfma_bf16(ahi[ks], h, c);
+                }
                 float x[16];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) x[r] = th ? c1[r] : c0[r];
+                for (int r = 0; r < 16; ++r) x[r] = c[r];
                 expm1_x16(x);
                 float acc = 0.f;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc = fmaf(pv[th][r], x[r], acc);
+                for (int r = 0; r < 16; ++r) acc = fmaf(pv[r], x[r], acc);
 #pragma unroll
                 for (int jj = 0; jj < HDG; ++jj)
                     if (jj == j) s[jj][th] += acc;
@@ -658,10 +652,12 @@ __global__ void __launch_bounds__(256) lm_head_delta_kernel(const float* __restr
         }
     }
     __syncthreads();
-    for (int x = threadIdx.x; x < dn * 64; x += 256) {
+    for (int x = threadIdx.x; x < dn * 64; x += 64 * HW) {
         const int j = x >> 6, q = x & 63;
-        part[((int64_t)(g * HDG + j) * T + (int64_t)tb * 64 + q) * nseg + sg] =
-            (red[0][j][q] + red[1][j][q]) + (red[2][j][q] + red[3][j][q]);
+        float t = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < HW; ++ww) t += red[ww][j][q];
+        part[((int64_t)(g * HDG + j) * T + (int64_t)tb * 64 + q) * nseg + sg] = t;
     }
 }
 
@@ -1079,11 +1075,11 @@ hipError_t lm_head_delta(const float* du, const uint16_t* whi, const uint16_t* w
     hipError_t e = launch_timer_begin(kTimedLmHead, s, timed);
     if (e != hipSuccess) return e;
     if (d == 64)
-        hipLaunchKernelGGL(lm_head_delta_kernel<4>, grid, dim3(256), 0, s, du, whi, wlo, prob, T, Vp, vseg, nseg, kc,
-                           part);
+        hipLaunchKernelGGL(lm_head_delta_kernel<4>, grid, dim3(64 * HW), 0, s, du, whi, wlo, prob, T, Vp, vseg, nseg,
+                           kc, part);
     else
-        hipLaunchKernelGGL(lm_head_delta_kernel<8>, grid, dim3(256), 0, s, du, whi, wlo, prob, T, Vp, vseg, nseg, kc,
-                           part);
+        hipLaunchKernelGGL(lm_head_delta_kernel<8>, grid, dim3(64 * HW), 0, s, du, whi, wlo, prob, T, Vp, vseg, nseg,
+                           kc, part);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return launch_timer_end(kTimedLmHead, s, timed);
 }
