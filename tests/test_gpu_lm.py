@@ -41,6 +41,7 @@ CASES = [
     (70, 64, 1, 1, 64, 64, 2, 3, 2, 0.3, 0),       # large changes: exp - 1 and erfc branches
     (50, 192, 3, 1, 64, 64, 2, 3, 2, 1e-2, 0),     # d = 192: the head change by GEMM + loss-change kernel
     (100, 128, 2, 2, 128, 64, 2, 11, 5, 1e-2, 3),  # chunks of 3 draws (11 = 3+3+3+2, 10 members = 3+3+3+1)
+    (130, 64, 1, 3, 64, 192, 1, 3, 2, 1e-2, 0),    # three blocks, three query tiles per sequence
 ]
 
 

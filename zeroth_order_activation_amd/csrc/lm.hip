@@ -421,16 +421,25 @@ __global__ void __launch_bounds__(256) lm_ghat_kernel(const float* __restrict__ 
                                                                              s3 * scale);
 }
 
-// G_E[v] = sum over tokens equal to v of g_hat (one wave per vocabulary row and
-// 64-channel block, tokens in order); G_P[s] = sum over sequences of g_hat at s.
-__global__ void __launch_bounds__(64) lm_embed_grad_kernel(const float* __restrict__ ghat,
-                                                           const int32_t* __restrict__ tok, int T, int d,
-                                                           float* __restrict__ gemb) {
-    const int vrow = blockIdx.x, c = blockIdx.y * 64 + threadIdx.x;
-    float s = 0.f;
-    for (int t = 0; t < T; ++t)
-        if (tok[t] == vrow) s += ghat[(int64_t)t * d + c];
-    gemb[(int64_t)vrow * d + c] = s;
+// G_E[v] = sum over tokens equal to v of g_hat: one workgroup per EVB vocabulary rows
+// and 256 channels scans the tokens once, in order, adding the matching rows into
+// LDS (so each sum runs in token order: deterministic); G_P[s] = sum over sequences
+// of g_hat at position s.
+constexpr int EVB = 16;
+
+__global__ void __launch_bounds__(256) lm_embed_grad_kernel(const float* __restrict__ ghat,
+                                                            const int32_t* __restrict__ tok, int T, int V, int d,
+                                                            float* __restrict__ gemb) {
+    __shared__ float acc[EVB][256];
+    const int v0 = blockIdx.x * EVB, c = blockIdx.y * 256 + threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < EVB; ++j) acc[j][threadIdx.x] = 0.f;
+    for (int t = 0; t < T; ++t) {
+        const int id = tok[t] - v0;  // uniform across the workgroup
+        if (id >= 0 && id < EVB && c < d) acc[id][threadIdx.x] += ghat[(int64_t)t * d + c];
+    }
+    if (c < d)
+        for (int j = 0; j < EVB && v0 + j < V; ++j) gemb[(int64_t)(v0 + j) * d + c] = acc[j][threadIdx.x];
 }
 
 __global__ void __launch_bounds__(256) lm_pos_grad_kernel(const float* __restrict__ ghat, int T, int S, int d,
@@ -1053,8 +1062,8 @@ hipError_t lm_ghat(const float* rew, int K, int T, int w, float scale, uint32_t 
 
 hipError_t lm_embed_grads(const float* ghat, const int32_t* tok, int T, int S, int V, int d, float* gemb, float* gpos,
                           hipStream_t s) {
-    hipLaunchKernelGGL(lm_embed_grad_kernel, dim3((unsigned)V, (unsigned)(d / 64)), dim3(64), 0, s, ghat, tok, T, d,
-                       gemb);
+    hipLaunchKernelGGL(lm_embed_grad_kernel, dim3((unsigned)((V + EVB - 1) / EVB), (unsigned)((d + 255) / 256)),
+                       dim3(256), 0, s, ghat, tok, T, V, d, gemb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(lm_pos_grad_kernel, dim3(blocks((int64_t)S * d)), dim3(256), 0, s, ghat, T, S, d, gpos);
