@@ -646,8 +646,8 @@ def run_linear(args, c, K, dust, torch):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
-              "(the estimator shards by tokens or draws with one all-reduce of G_W; not built here)",
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the estimator would shard by tokens or draws with one all-reduce of G_W)",
               file=sys.stderr)
         sys.exit(2)
     if args.traffic_from:

@@ -164,7 +164,7 @@ def window_offset(seed: int, layer: int, draw: int, token: int, nq: int) -> int:
 def head_estimate_subset(logits, labels, K: int, m: int, sigma: float, seed: int, layer: int,
                          token_offset: int = 0, draw_offset: int = 0):
     """Head estimator with a vocabulary subset per draw (TL;DR page, section 1,
-    "reducing interference"; the subset rule is this build's reading): a cyclic
+    "reducing interference"; the pages give no subset rule, this is a reading): a cyclic
     window of m/4 channel quads at a per-(token, draw) Philox offset, plus the
     label, perturbed with the full estimator's noise; the plain cross-entropy of
     the perturbed row; each channel weighted by the inverse of its inclusion

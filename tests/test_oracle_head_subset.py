@@ -1,7 +1,7 @@
 """Pins of the oracle's vocabulary-subset head estimator (TL;DR page, section 1,
 "reducing interference": only part of the vocabulary is perturbed per head draw; the
 subset rule -- a cyclic window of m/4 channel quads at a per-(token, draw) offset, plus the
-label -- and the inverse-inclusion-probability weights are this build's reading).
+label -- and the inverse-inclusion-probability weights are a reading of that passage).
 
 - a window covering the vocabulary reproduces the (separately pinned) full estimator exactly;
 - the window offset is uniform over the quads (chi-square) and the label is always perturbed;
