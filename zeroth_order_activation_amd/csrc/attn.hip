@@ -18,8 +18,8 @@
 // Kernels (heads of 64 channels, sequences of whole 64-token tiles):
 //   attn_stats_kernel per (sequence, head, query tile): log-sum-exp of the
 //                     clean scaled logits of each query (and <e, o>);
-//   attn_v_kernel     per (sequence, head, key tile): the key tile's noise for
-//                     a chunk of draws is generated once into LDS; for every
+//   attn_v_kernel     per (sequence, head, key tile) and chunk of 8 draws: the
+//                     key tile's noise for the chunk is generated once into LDS; for every
 //                     query tile at or after it the transposed logits
 //                     K Q^T / sqrt(64) are recomputed, P = exp(L - lse), and
 //                     per draw G^T = A E^T on MFMA, then per query the column
@@ -32,6 +32,8 @@
 // Products of two fp32 operands run on bf16 MFMA with both operands split into
 // pairs v = hi + lo and the three products lo.hi + hi.lo + hi.hi accumulated in
 // fp32 (each within about 3 2^-17 of fp32).
+#include <algorithm>
+
 #include "dust_device.hpp"
 #include "dust_internal.hpp"
 #include "launch_events.hpp"
@@ -127,6 +129,7 @@ struct AttnKArgs {
     float sdelta;    // sigma / sqrt(dh): the logit change per unit of <a, q> or <k, a>
     float* lse2;     // [T,H] log2-sum-exp2 of the clean scaled logits (log2 e / sqrt(dh) q.k)
     float* cpart;    // [KC][nkt][H][2][T] partial c per (draw, key tile, head, key half, query)
+    int dper;        // draws per workgroup along y (a multiple of ADC): workgroup y takes [y dper, (y+1) dper)
     int T, S, d, H;
     uint32_t k0, k1, layer, tok0, draw0;
 };
@@ -275,7 +278,7 @@ __global__ void __launch_bounds__(VNT, 1) attn_v_kernel(AttnKArgs A, int i0, int
     uint4 khi[4], klo[4];  // this wave's 32 keys
     load_frags(A.k, A.d, s0 + kt * AT + kh * 32 + (lane & 31), h * ADH, khi, klo);
 
-    for (int d0 = 0; d0 < kc; d0 += ADC) {
+    for (int d0 = (int)blockIdx.y * A.dper; d0 < kc && d0 < ((int)blockIdx.y + 1) * A.dper; d0 += ADC) {
         const int dn = min(ADC, kc - d0);
         __syncthreads();  // the previous chunk's noise fully used
         // noise of the 64 keys x 64 channels for dn draws: 1024 quads per draw
@@ -371,7 +374,7 @@ __global__ void __launch_bounds__(VNT, 1) attn_k_kernel(AttnKArgs A, int kc) {
     uint4 khi[4], klo[4], vhi[4], vlo[4];  // this wave's 32 keys
     load_frags(A.k, A.d, s0 + kt * AT + kh * 32 + (lane & 31), h * ADH, khi, klo);
     load_frags(A.v, A.d, s0 + kt * AT + kh * 32 + (lane & 31), h * ADH, vhi, vlo);
-    for (int d0 = 0; d0 < kc; d0 += ADC) {
+    for (int d0 = (int)blockIdx.y * A.dper; d0 < kc && d0 < ((int)blockIdx.y + 1) * A.dper; d0 += ADC) {
         const int dn = min(ADC, kc - d0);
         __syncthreads();  // the previous chunk's noise fully used
         for (int dd = 0; dd < dn; ++dd)
@@ -460,7 +463,7 @@ __global__ void __launch_bounds__(VNT, 1) attn_q_kernel(AttnKArgs A, int kc) {
     load_frags(A.q, A.d, qrow, h * ADH, qhi, qlo);
     load_frags(A.e, A.d, qrow, h * ADH, ehi, elo);
     const float l2q = A.lse2[qrow * A.H + h];
-    for (int d0 = 0; d0 < kc; d0 += ADC) {
+    for (int d0 = (int)blockIdx.y * A.dper; d0 < kc && d0 < ((int)blockIdx.y + 1) * A.dper; d0 += ADC) {
         const int dn = min(ADC, kc - d0);
         __syncthreads();  // the previous chunk's noise and sums fully used
         for (int dd = 0; dd < dn; ++dd)
@@ -692,12 +695,19 @@ hipError_t launch_attn_rewards(int proj, const float* q, const float* k, const f
         Ai.draw0 = draw_offset + (uint32_t)i0;
         bool timed;
         if ((err = launch_timer_begin(kTimedAttnMain, stream, timed)) != hipSuccess) return err;
+        // one workgroup per (sequence, head, tile) and range of draws: the draws are split
+        // across workgroups only as far as needed for about two workgroups per CU (each
+        // workgroup recomputes its tiles' clean products per chunk of ADC draws anyway)
+        const int nch = (kc + ADC - 1) / ADC;
+        const int ny = (int)std::min<int64_t>(nch, std::max<int64_t>(1, (512 + grid - 1) / grid));
+        Ai.dper = ((nch + ny - 1) / ny) * ADC;
+        const dim3 g2(grid, (unsigned)((kc + Ai.dper - 1) / Ai.dper));
         if (proj == 2)
-            hipLaunchKernelGGL(attn_v_kernel, dim3(grid), dim3(VNT), 0, stream, Ai, 0, kc);
+            hipLaunchKernelGGL(attn_v_kernel, g2, dim3(VNT), 0, stream, Ai, 0, kc);
         else if (proj == 1)
-            hipLaunchKernelGGL(attn_k_kernel, dim3(grid), dim3(VNT), 0, stream, Ai, kc);
+            hipLaunchKernelGGL(attn_k_kernel, g2, dim3(VNT), 0, stream, Ai, kc);
         else
-            hipLaunchKernelGGL(attn_q_kernel, dim3(grid), dim3(VNT), 0, stream, Ai, kc);
+            hipLaunchKernelGGL(attn_q_kernel, g2, dim3(VNT), 0, stream, Ai, kc);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         if ((err = launch_timer_end(kTimedAttnMain, stream, timed)) != hipSuccess) return err;
         const unsigned nthr = (unsigned)((kc * T + 255) / 256);
