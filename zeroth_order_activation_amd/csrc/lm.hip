@@ -152,54 +152,62 @@ __device__ __forceinline__ void load16(const float* p, float (&r)[16]) {
     }
 }
 
+template <int NT = 256>
 __device__ __forceinline__ void stage_tile(float (*dst)[64], const float* src, int64_t row0, int d, int h) {
-    // 64 rows x 64 channels of head h: 1024 float4, 4 per thread
+    // 64 rows x 64 channels of head h: 1024 float4 over NT lanes
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int f = threadIdx.x + 256 * j, row = f >> 4, c4 = (f & 15) * 4;
+    for (int j = 0; j < 1024 / NT; ++j) {
+        const int f = threadIdx.x + NT * j, row = f >> 4, c4 = (f & 15) * 4;
         *reinterpret_cast<float4*>(&dst[row][c4]) =
             *reinterpret_cast<const float4*>(src + (row0 + row) * d + h * 64 + c4);
     }
 }
 
-__global__ void __launch_bounds__(256) lm_attn_fwd_kernel(const float* __restrict__ q, const float* __restrict__ k,
-                                                          const float* __restrict__ v, int T, int S, int H,
-                                                          float* __restrict__ o, float* __restrict__ lse,
-                                                          float* __restrict__ pc) {
+// Causal attention of FQ = 16 queries x one head per workgroup (one wave, 4 lanes per
+// query, 16 channels each), so that short inputs still give many workgroups; the key
+// tiles up to the queries' own 64-key tile are staged in LDS; three passes over the
+// keys: the row maximum; p, sum p and sum p v; the probabilities for the cache.
+constexpr int FQ = 16;
+
+__global__ void __launch_bounds__(4 * FQ) lm_attn_fwd_kernel(const float* __restrict__ q, const float* __restrict__ k,
+                                                             const float* __restrict__ v, int T, int S, int H,
+                                                             float* __restrict__ o, float* __restrict__ lse,
+                                                             float* __restrict__ pc) {
     __shared__ __align__(16) float Ks[64][64];
     __shared__ __align__(16) float Vs[64][64];
-    const int nqt = S / 64, qt = blockIdx.x % nqt, bh = blockIdx.x / nqt, b = bh / H, h = bh % H;
+    const int nqt = S / FQ, qt = blockIdx.x % nqt, bh = blockIdx.x / nqt, b = bh / H, h = bh % H;
     const int d = 64 * H, ql = threadIdx.x >> 2, qr = threadIdx.x & 3;
-    const int64_t s0 = (int64_t)b * S, row = s0 + qt * 64 + ql;
+    const int query = qt * FQ + ql, q64 = (qt * FQ) / 64;  // the queries' 64-key tile
+    const int64_t s0 = (int64_t)b * S, row = s0 + query;
     float qv[16];
     load16(q + row * d + h * 64 + qr * 16, qv);
     float mx = -INFINITY;
-    for (int kt = 0; kt <= qt; ++kt) {
+    for (int kt = 0; kt <= q64; ++kt) {
         __syncthreads();
-        stage_tile(Ks, k, s0 + kt * 64, d, h);
+        stage_tile<4 * FQ>(Ks, k, s0 + kt * 64, d, h);
         __syncthreads();
         for (int j = 0; j < 64; ++j) {
             float dot = 0.f;
 #pragma unroll
             for (int c = 0; c < 16; ++c) dot = fmaf(qv[c], Ks[j][qr * 16 + c], dot);
             dot = quad_total(dot) * 0.125f;
-            if (kt < qt || j <= ql) mx = fmaxf(mx, dot);
+            if (kt * 64 + j <= query) mx = fmaxf(mx, dot);
         }
     }
     float s = 0.f, acc[16];
 #pragma unroll
     for (int c = 0; c < 16; ++c) acc[c] = 0.f;
-    for (int kt = 0; kt <= qt; ++kt) {
+    for (int kt = 0; kt <= q64; ++kt) {
         __syncthreads();
-        stage_tile(Ks, k, s0 + kt * 64, d, h);
-        stage_tile(Vs, v, s0 + kt * 64, d, h);
+        stage_tile<4 * FQ>(Ks, k, s0 + kt * 64, d, h);
+        stage_tile<4 * FQ>(Vs, v, s0 + kt * 64, d, h);
         __syncthreads();
         for (int j = 0; j < 64; ++j) {
             float dot = 0.f;
 #pragma unroll
             for (int c = 0; c < 16; ++c) dot = fmaf(qv[c], Ks[j][qr * 16 + c], dot);
             dot = quad_total(dot) * 0.125f;
-            const float p = (kt < qt || j <= ql) ? __expf(dot - mx) : 0.f;
+            const float p = kt * 64 + j <= query ? __expf(dot - mx) : 0.f;
             s += p;
 #pragma unroll
             for (int c = 0; c < 16; ++c) acc[c] = fmaf(p, Vs[j][qr * 16 + c], acc[c]);
@@ -211,17 +219,17 @@ __global__ void __launch_bounds__(256) lm_attn_fwd_kernel(const float* __restric
     if (qr == 0) lse[row * H + h] = l;
     // the probabilities of this query over the key tiles up to its own (zero after it):
     // pc[((b H + h) S + query) S + key]; lane qr of the query writes keys j = qr mod 4
-    float* prow = pc + ((int64_t)bh * S + qt * 64 + ql) * S;
-    for (int kt = 0; kt <= qt; ++kt) {
+    float* prow = pc + ((int64_t)bh * S + query) * S;
+    for (int kt = 0; kt <= q64; ++kt) {
         __syncthreads();
-        stage_tile(Ks, k, s0 + kt * 64, d, h);
+        stage_tile<4 * FQ>(Ks, k, s0 + kt * 64, d, h);
         __syncthreads();
         for (int j = 0; j < 64; ++j) {
             float dot = 0.f;
 #pragma unroll
             for (int c = 0; c < 16; ++c) dot = fmaf(qv[c], Ks[j][qr * 16 + c], dot);
             dot = quad_total(dot) * 0.125f;
-            if ((j & 3) == qr) prow[kt * 64 + j] = (kt < qt || j <= ql) ? __expf(dot - l) : 0.f;
+            if ((j & 3) == qr) prow[kt * 64 + j] = kt * 64 + j <= query ? __expf(dot - l) : 0.f;
         }
     }
 }
@@ -988,8 +996,8 @@ hipError_t lm_layernorm(const float* x, int64_t R, int d, float eps, float* u, f
 
 hipError_t lm_attn_fwd(const float* q, const float* k, const float* v, int T, int S, int H, float* o, float* lse,
                        float* pc, hipStream_t s) {
-    hipLaunchKernelGGL(lm_attn_fwd_kernel, dim3((unsigned)((T / S) * H * (S / 64))), dim3(256), 0, s, q, k, v, T, S,
-                       H, o, lse, pc);
+    hipLaunchKernelGGL(lm_attn_fwd_kernel, dim3((unsigned)((T / S) * H * (S / FQ))), dim3(4 * FQ), 0, s, q, k, v, T,
+                       S, H, o, lse, pc);
     return hipGetLastError();
 }
 
