@@ -541,7 +541,7 @@ struct LmLayout {
     size_t HBHI, HBLO, PP, PART;
     size_t X[kLmMaxL + 1], U1[kLmMaxL], Q[kLmMaxL], Kk[kLmMaxL], Vv[kLmMaxL], O[kLmMaxL], BA[kLmMaxL], XM[kLmMaxL],
         U2[kLmMaxL], BM[kLmMaxL], Hh[kLmMaxL], Mm[kLmMaxL], MU1[kLmMaxL], RS1[kLmMaxL], MU2[kLmMaxL], RS2[kLmMaxL],
-        LSE[kLmMaxL], PC[kLmMaxL], GO[kLmMaxL], GUP[kLmMaxL], GDN[kLmMaxL], WSH[kLmMaxL], WSL[kLmMaxL];
+        LSE[kLmMaxL], PC[kLmMaxL], CDF[kLmMaxL], PDF[kLmMaxL], GO[kLmMaxL], GUP[kLmMaxL], GDN[kLmMaxL], WSH[kLmMaxL], WSL[kLmMaxL];
     size_t UF, MUF, RSF, Z, LSEZ, CE;
     size_t DX, DU, DQ, DK, DV, DO, DB, DH, DM, DZ;
     size_t REWS, REWES, DL, GE, E, WOT, SUB, sub_bytes, total;
@@ -573,6 +573,8 @@ LmLayout lm_layout(const LmDims& D, int64_t K, int64_t M, int64_t chunk) {
         L.BM[l] = take(T * d);
         L.Hh[l] = take(T * n);
         L.Mm[l] = take(T * n);
+        L.CDF[l] = take(T * n);  // Phi(h) and phi(h) of the clean W_1 output
+        L.PDF[l] = take(T * n);
         L.MU1[l] = take(T);
         L.RS1[l] = take(T);
         L.MU2[l] = take(T);
@@ -676,7 +678,7 @@ hipError_t lm_clean_forward(const LmRun& R) {
         LM_TRY(dust::lm_residual(R.f(L.X[l]), R.f(L.BA[l]), p + R.P.scal + 2 * l, D.T * D.d, R.f(L.XM[l]), st));
         LM_TRY(dust::lm_layernorm(R.f(L.XM[l]), T, d, D.eps, R.f(L.U2[l]), R.f(L.MU2[l]), R.f(L.RS2[l]), st));
         LM_TRY(dust::lm_gemm_nt(R.f(L.U2[l]), p + R.P.w1(l), R.f(L.Hh[l]), T, n, d, nullptr, false, st));
-        LM_TRY(dust::lm_gelu(R.f(L.Hh[l]), D.T * D.n, R.f(L.Mm[l]), st));
+        LM_TRY(dust::lm_gelu(R.f(L.Hh[l]), D.T * D.n, R.f(L.Mm[l]), R.f(L.CDF[l]), R.f(L.PDF[l]), st));
         LM_TRY(dust::lm_gemm_nt(R.f(L.Mm[l]), p + R.P.w2(l), R.f(L.BM[l]), T, d, n, nullptr, false, st));
         LM_TRY(dust::lm_residual(R.f(L.XM[l]), R.f(L.BM[l]), p + R.P.scal + 2 * l + 1, D.T * D.d, R.f(L.X[l + 1]),
                                  st));
@@ -750,7 +752,7 @@ hipError_t lm_delta_chunk(const LmRun& R, int kind, int kn, uint32_t draw0, floa
         if (kind == 2) LM_TRY(dust::lm_noise_add(DH, kn, T, n, sigma, k0, k1, lm_lid(l, 4), draw0, st));
         const bool mlp = live || kind == 2;
         if (mlp) {
-            LM_TRY(dust::lm_gelu_delta(R.f(L.Hh[l]), DH, D.T * D.n, rows * n, DM, st));
+            LM_TRY(dust::lm_gelu_delta(R.f(L.Hh[l]), R.f(L.CDF[l]), R.f(L.PDF[l]), DH, D.T * D.n, rows * n, DM, st));
             LM_TRY(dust::lm_gemm_x3(DM, wh(l, R.P.w2(l)), wl(l, R.P.w2(l)), DB, rows, d, n, st));
         } else if (kind == 3) {
             LM_TRY(zero(DB, rows * d));

@@ -237,10 +237,16 @@ __global__ void __launch_bounds__(4 * FQ) lm_attn_fwd_kernel(const float* __rest
 __device__ __forceinline__ float phi_cdf(float x) { return 0.5f * erfcf(-x * 0.70710678118654752f); }
 __device__ __forceinline__ float phi_pdf(float x) { return 0.39894228040143268f * __expf(-0.5f * x * x); }
 
+// m = GELU(h) = h Phi(h); also Phi(h) and phi(h), which the change passes reuse
 __global__ void __launch_bounds__(256) lm_gelu_kernel(const float* __restrict__ h, int64_t count,
-                                                      float* __restrict__ m) {
+                                                      float* __restrict__ m, float* __restrict__ cdf,
+                                                      float* __restrict__ pdf) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < count) m[i] = h[i] * phi_cdf(h[i]);
+    if (i >= count) return;
+    const float x = h[i], c = phi_cdf(x);
+    m[i] = x * c;
+    cdf[i] = c;
+    pdf[i] = phi_pdf(x);
 }
 
 // out = x + alpha b
@@ -344,6 +350,54 @@ __global__ void __launch_bounds__(256) lm_layernorm_delta_kernel(const float* __
         if (e < E) du[(int64_t)row * d + lane + 64 * e] = fmaf(c[e], a, xc[e] * bb);
 }
 
+// The same with 8 channels per lane and LPR = d / 8 lanes per row (d <= 512): several
+// rows per wave, float4 accesses, sums over the row's lanes.
+template <int LPR>
+__device__ __forceinline__ float group_total(float v) {
+#pragma unroll
+    for (int o = LPR / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+template <int LPR>
+__global__ void __launch_bounds__(256) lm_layernorm_delta8_kernel(const float* __restrict__ x,
+                                                                  const float* __restrict__ mu,
+                                                                  const float* __restrict__ rs,
+                                                                  const float* __restrict__ dx, int64_t R, int T,
+                                                                  float* __restrict__ du) {
+    constexpr int D = 8 * LPR;
+    const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LPR;
+    if (row >= R) return;  // whole lane groups: the sums below stay within live groups
+    const int li = threadIdx.x % LPR, t = (int)(row % T);
+    const float m = mu[t], r = rs[t];
+    const float* xp = x + (int64_t)t * D + 8 * li;
+    const float* dp = dx + row * D + 8 * li;
+    const float4 x0 = *reinterpret_cast<const float4*>(xp), x1 = *reinterpret_cast<const float4*>(xp + 4);
+    const float4 d0 = *reinterpret_cast<const float4*>(dp), d1 = *reinterpret_cast<const float4*>(dp + 4);
+    float xc[8] = {x0.x - m, x0.y - m, x0.z - m, x0.w - m, x1.x - m, x1.y - m, x1.z - m, x1.w - m};
+    float c[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += c[e];
+    const float dm = group_total<LPR>(s) / (float)D;
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        c[e] -= dm;
+        s1 = fmaf(xc[e], c[e], s1);
+        s2 = fmaf(c[e], c[e], s2);
+    }
+    const float dv = (2.0f * group_total<LPR>(s1) + group_total<LPR>(s2)) / (float)D;
+    const float f = expm1f(-0.5f * log1pf(dv * r * r));  // rs' / rs - 1
+    const float a = r * (1.0f + f), bb = r * f;
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = fmaf(c[e], a, xc[e] * bb);
+    float* op = du + row * D + 8 * li;
+    *reinterpret_cast<float4*>(op) = make_float4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<float4*>(op + 4) = make_float4(o[4], o[5], o[6], o[7]);
+}
+
 __device__ __forceinline__ float expm1_s(float x) {
     if (fabsf(x) < 0.25f)
         return x * fmaf(x, fmaf(x, fmaf(x, fmaf(x, fmaf(x, 1.0f / 720.0f, 1.0f / 120.0f), 1.0f / 24.0f),
@@ -351,23 +405,28 @@ __device__ __forceinline__ float expm1_s(float x) {
     return __expf(x) - 1.0f;
 }
 
-// D_m = GELU(h + D_h) - GELU(h) = D_h Phi(h + D_h) + h (Phi(h + D_h) - Phi(h))
+// D_m = GELU(h + D_h) - GELU(h) = D_h Phi(h) + (D_h + h) (Phi(h + D_h) - Phi(h)), with the
+// cached Phi(h), phi(h) of the clean pass; the difference of Phi by Simpson's rule on the
+// density for |D_h| < 1/4 (error below |D_h|^5 max|phi''''| / 2880), else by complementary
+// error functions of one sign (no cancellation in either).
 __global__ void __launch_bounds__(256) lm_gelu_delta_kernel(const float* __restrict__ hc,
+                                                            const float* __restrict__ cdf,
+                                                            const float* __restrict__ pdf,
                                                             const float* __restrict__ dh, int64_t per_draw,
                                                             int64_t count, float* __restrict__ dm) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= count) return;
-    const float h = hc[i % per_draw], e = dh[i], h1 = h + e;
+    const int64_t j = i % per_draw;
+    const float h = hc[j], e = dh[i], h1 = h + e;
     float dphi;
     if (fabsf(e) < 0.25f) {
-        // Simpson's rule on the density: error below |e|^5 max|phi''''| / 2880
-        dphi = e * (1.0f / 6.0f) * (phi_pdf(h) + 4.0f * phi_pdf(h + 0.5f * e) + phi_pdf(h1));
+        dphi = e * (1.0f / 6.0f) * (pdf[j] + 4.0f * phi_pdf(h + 0.5f * e) + phi_pdf(h1));
     } else if (h + 0.5f * e > 0.f) {  // upper tail: 1 - Phi by erfc
         dphi = 0.5f * (erfcf(h * 0.70710678118654752f) - erfcf(h1 * 0.70710678118654752f));
     } else {
         dphi = 0.5f * (erfcf(-h1 * 0.70710678118654752f) - erfcf(-h * 0.70710678118654752f));
     }
-    dm[i] = fmaf(e, phi_cdf(h1), h * dphi);
+    dm[i] = fmaf(e, cdf[j], (e + h) * dphi);
 }
 
 // dx += alpha db, plus for an ES member (es_sigma > 0) the change of the scalar:
@@ -439,12 +498,19 @@ __global__ void __launch_bounds__(256) lm_embed_grad_kernel(const float* __restr
                                                             const int32_t* __restrict__ tok, int T, int V, int d,
                                                             float* __restrict__ gemb) {
     __shared__ float acc[EVB][256];
+    __shared__ int ids[1024];
     const int v0 = blockIdx.x * EVB, c = blockIdx.y * 256 + threadIdx.x;
 #pragma unroll
     for (int j = 0; j < EVB; ++j) acc[j][threadIdx.x] = 0.f;
-    for (int t = 0; t < T; ++t) {
-        const int id = tok[t] - v0;  // uniform across the workgroup
-        if (id >= 0 && id < EVB && c < d) acc[id][threadIdx.x] += ghat[(int64_t)t * d + c];
+    for (int t0 = 0; t0 < T; t0 += 1024) {  // token ids staged through LDS, 1024 at a time
+        const int nt = min(1024, T - t0);
+        __syncthreads();
+        for (int u = threadIdx.x; u < nt; u += 256) ids[u] = tok[t0 + u] - v0;
+        __syncthreads();
+        for (int u = 0; u < nt; ++u) {
+            const int id = ids[u];  // uniform across the workgroup
+            if (id >= 0 && id < EVB && c < d) acc[id][threadIdx.x] += ghat[(int64_t)(t0 + u) * d + c];
+        }
     }
     if (c < d)
         for (int j = 0; j < EVB && v0 + j < V; ++j) gemb[(int64_t)(v0 + j) * d + c] = acc[j][threadIdx.x];
@@ -1001,8 +1067,8 @@ hipError_t lm_attn_fwd(const float* q, const float* k, const float* v, int T, in
     return hipGetLastError();
 }
 
-hipError_t lm_gelu(const float* h, int64_t count, float* m, hipStream_t s) {
-    hipLaunchKernelGGL(lm_gelu_kernel, dim3(blocks(count)), dim3(256), 0, s, h, count, m);
+hipError_t lm_gelu(const float* h, int64_t count, float* m, float* cdf, float* pdf, hipStream_t s) {
+    hipLaunchKernelGGL(lm_gelu_kernel, dim3(blocks(count)), dim3(256), 0, s, h, count, m, cdf, pdf);
     return hipGetLastError();
 }
 
@@ -1027,8 +1093,28 @@ hipError_t lm_noise_add(float* D, int kc, int T, int w, float sigma, uint32_t k0
 
 hipError_t lm_layernorm_delta(const float* x, const float* mu, const float* rs, const float* dx, int64_t R, int T,
                               int d, float* du, hipStream_t s) {
-    hipLaunchKernelGGL(lm_layernorm_delta_kernel, dim3(blocks(R, 4)), dim3(256), 0, s, x, mu, rs, dx, (int)R, T, d,
-                       du);
+    const int64_t lanes = R * (d / 8);
+    switch (d) {
+        case 64:
+            hipLaunchKernelGGL(lm_layernorm_delta8_kernel<8>, dim3(blocks(lanes)), dim3(256), 0, s, x, mu, rs, dx, R, T,
+                               du);
+            break;
+        case 128:
+            hipLaunchKernelGGL(lm_layernorm_delta8_kernel<16>, dim3(blocks(lanes)), dim3(256), 0, s, x, mu, rs, dx, R,
+                               T, du);
+            break;
+        case 256:
+            hipLaunchKernelGGL(lm_layernorm_delta8_kernel<32>, dim3(blocks(lanes)), dim3(256), 0, s, x, mu, rs, dx, R,
+                               T, du);
+            break;
+        case 512:
+            hipLaunchKernelGGL(lm_layernorm_delta8_kernel<64>, dim3(blocks(lanes)), dim3(256), 0, s, x, mu, rs, dx, R,
+                               T, du);
+            break;
+        default:  // other widths: one wave per row
+            hipLaunchKernelGGL(lm_layernorm_delta_kernel, dim3(blocks(R, 4)), dim3(256), 0, s, x, mu, rs, dx, (int)R,
+                               T, d, du);
+    }
     return hipGetLastError();
 }
 
@@ -1040,9 +1126,10 @@ hipError_t lm_attn_delta(const float* q, const float* k, const float* v, const f
     return hipGetLastError();
 }
 
-hipError_t lm_gelu_delta(const float* h, const float* dh, int64_t per_draw, int64_t count, float* dm,
-                         hipStream_t s) {
-    hipLaunchKernelGGL(lm_gelu_delta_kernel, dim3(blocks(count)), dim3(256), 0, s, h, dh, per_draw, count, dm);
+hipError_t lm_gelu_delta(const float* h, const float* cdf, const float* pdf, const float* dh, int64_t per_draw,
+                         int64_t count, float* dm, hipStream_t s) {
+    hipLaunchKernelGGL(lm_gelu_delta_kernel, dim3(blocks(count)), dim3(256), 0, s, h, cdf, pdf, dh, per_draw, count,
+                       dm);
     return hipGetLastError();
 }
 

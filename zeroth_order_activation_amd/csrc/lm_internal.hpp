@@ -20,7 +20,8 @@ hipError_t lm_layernorm(const float* x, int64_t R, int d, float eps, float* u, f
 // to the query's own (zero after the query)
 hipError_t lm_attn_fwd(const float* q, const float* k, const float* v, int T, int S, int H, float* o, float* lse,
                        float* pc, hipStream_t s);
-hipError_t lm_gelu(const float* h, int64_t count, float* m, hipStream_t s);
+// also writes Phi(h) and phi(h) (the normal distribution and density), reused by lm_gelu_delta
+hipError_t lm_gelu(const float* h, int64_t count, float* m, float* cdf, float* pdf, hipStream_t s);
 hipError_t lm_residual(const float* x, const float* b, const float* alpha, int64_t count, float* out, hipStream_t s);
 hipError_t lm_ce(const float* z, const int32_t* labels, int T, int V, float* lse, float* ce, float* prob, int Vp,
                  hipStream_t s);
@@ -42,7 +43,8 @@ hipError_t lm_layernorm_delta(const float* x, const float* mu, const float* rs, 
 hipError_t lm_attn_delta(const float* q, const float* k, const float* v, const float* o, const float* pc,
                          const float* dq, const float* dk, const float* dv, int kc, int T, int S, int H, float* dout,
                          hipStream_t s);
-hipError_t lm_gelu_delta(const float* h, const float* dh, int64_t per_draw, int64_t count, float* dm, hipStream_t s);
+hipError_t lm_gelu_delta(const float* h, const float* cdf, const float* pdf, const float* dh, int64_t per_draw,
+                         int64_t count, float* dm, hipStream_t s);
 hipError_t lm_residual_delta(float* dx, const float* db, const float* b, const float* scal, int slot, int kc,
                              int64_t per_draw, float es_sigma, uint32_t member0, uint32_t k0, uint32_t k1,
                              uint32_t es_layer, hipStream_t s);

@@ -59,7 +59,9 @@ OuterPlan plan_outer(int64_t T, int64_t n, int64_t d) {
     p.Np = p.x3 ? (d + YT - 1) / YT * YT : d;
     const int64_t tiles = ((n + bm - 1) / bm) * ((d + bn - 1) / bn);
     int64_t s = (512 + tiles - 1) / tiles;
-    const int64_t smax = (p.Tp + 255) / 256;  // at least 256 tokens per split
+    // at least 256 tokens per split; 64 when the output has few tiles (short inputs)
+    const int64_t minsplit = tiles < 64 ? 64 : 256;
+    const int64_t smax = (p.Tp + minsplit - 1) / minsplit;
     if (s > smax) s = smax;
     if (s < 1) s = 1;
     int64_t chunk = (p.Tp + s - 1) / s;
