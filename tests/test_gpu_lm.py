@@ -151,3 +151,31 @@ def test_bench_shape_on_sampled_draws():
         errs.append(e)
         assert e < TOL, (jm, e)
     print(f"2M-class shape: sampled rewards worst rel {max(errs):.2e}")
+
+
+def test_three_steps_follow_the_oracle_trajectory():
+    """Three consecutive updates (noise seed advanced per step, momentum carried): the
+    parameters after each step against the oracle's trajectory."""
+    V, d, H, L, n, S, B, K, M = 70, 64, 1, 2, 64, 64, 2, 3, 2
+    c, cfg, ocfg, p, tok, lab = _setup(V, d, H, L, n, S, B, seed=17, scal=0.9)
+    lr, lrs, mu = 2e-3, 2e-4, 0.9  # estimates of the summed loss over 128 tokens: small rates
+    hp = dust.lm_hparams(K, M, 2e-2, 2e-2, lr=lr, lr_scalar=lrs, momentum=mu)
+    mom = torch.zeros_like(p)
+    th = c["params"].astype(np.float64)
+    m = np.zeros_like(th)
+    sig = dict.fromkeys(lm.ALL_TYPES, 2e-2)
+    for step in range(3):
+        p_before = th.copy()
+        dust.lm_step(cfg, hp, p, mom, tok, lab, SEED + step)
+        torch.cuda.synchronize()
+        # the oracle steps from the GPU's own parameters, so the comparison is per step
+        th, m, _, _ = lm.step(ocfg, p_before, m, c["tokens"], c["labels"], K, M, sig, 2e-2, SEED + step, lr, lrs,
+                              mu)
+        e_u = rel_l2(p.cpu().numpy() - p_before, th - p_before)
+        e_m = rel_l2(mom.cpu().numpy(), m)
+        print(f"step {step}: update {e_u:.2e} momentum {e_m:.2e}, max |param| {np.abs(th).max():.2f}")
+        assert e_u < TOL and e_m < TOL
+        th = p.cpu().numpy().astype(np.float64)
+    ce0 = lm.forward(ocfg, c["params"], c["tokens"], c["labels"])[0].mean()
+    ce3 = lm.forward(ocfg, th, c["tokens"], c["labels"])[0].mean()
+    print(f"mean loss {ce0:.4f} -> {ce3:.4f}")
