@@ -429,6 +429,19 @@ def lm_change_gemm_flops(c):
     return passes + 2 * M * T * per_draw["es"]
 
 
+def lm_change_gemm_bytes(c):
+    """HBM bytes of the change-row GEMMs of one step: each reads its change rows (K_in
+    floats) and writes its output rows (N_out floats); the weights' bf16 parts are small and
+    stay in cache.  Blocks as in lm_change_gemm_flops."""
+    T, d, n, L, K, M = c["T"], c["d"], c["n"], c["L"], c["K"], c["M"]
+    attn, mlp = 4 * (d + d), 2 * (d + n)
+    full = attn + mlp
+    first = {"emb": full, "o": mlp, "up": n + d, "down": 0, "es": mlp}
+    per_draw = {k: v + (L - 1) * full for k, v in first.items()}
+    rows = K * T * (per_draw["emb"] + per_draw["o"] + per_draw["up"] + per_draw["down"]) + 2 * M * T * per_draw["es"]
+    return 4 * rows
+
+
 def run_lm(args, c, dust, torch):
     """Full Dust step: clean forward, head, the four layer-type passes, attention
     internals, residual-scalar ES, SGD with momentum."""
@@ -488,26 +501,30 @@ def run_lm(args, c, dust, torch):
     # fused head change: per draw and token, d x Vp products on bf16 MFMA, three each (hi/lo)
     vp = -(-c["V"] // 128) * 128
     head_flops = (4 * c["K"] + 2 * c["M"]) * T * vp * c["d"] * 2 * 3
-    gemm_flops = 3 * lm_change_gemm_flops(c)
     lines = {
         "lm_head_delta_kernel": {"bound": "mfma", "flops": head_flops, "peak": MFMA_BF16_PEAK_TFLOPS,
                                  "launches": per["lm_head"][0], "ms": per["lm_head"][1],
                                  "note": "issued bf16 MFMA flops (three products per fp32 product) of the fused "
                                          "head change over its launches' durations (HIP events around each "
                                          "launch of the last timed step)"},
-        "lm_gemm_x3_kernel": {"bound": "mfma", "flops": gemm_flops, "peak": MFMA_BF16_PEAK_TFLOPS,
+        "lm_gemm_x3_kernel": {"bound": "hbm", "bytes": lm_change_gemm_bytes(c), "peak": HBM_PEAK_GBS,
                               "launches": per["lm_gemm"][0], "ms": per["lm_gemm"][1],
-                              "note": "issued bf16 MFMA flops (three products per fp32 product) of every launch of "
-                                      "the change-row GEMM in one step over the summed durations of those "
-                                      "launches (HIP events around each launch)"},
+                              "note": "change rows read and written by every launch of the change-row GEMM in one "
+                                      "step (about 95 issued bf16 flops per byte: HBM-bound) over the summed "
+                                      "durations of those launches (HIP events around each launch)"},
     }
     roof = {}
     for name, x in lines.items():
-        ach = x["flops"] / (x["ms"] / 1e3) / 1e12
-        roof[name] = {"bound": x["bound"], "kernel": name, "achieved": ach, "peak": x["peak"], "unit": "TFLOP/s",
-                      "frac": ach / x["peak"], "traffic": load_traffic(name, args.workload),
-                      "flops_per_launch": x["flops"] / max(x["launches"], 1), "launches_per_step": x["launches"],
-                      "kernel_ms": x["ms"] / max(x["launches"], 1), "kernel_ms_per_step": x["ms"],
+        nl = max(x["launches"], 1)
+        if x["bound"] == "hbm":
+            ach = x["bytes"] / (x["ms"] / 1e3) / 1e9
+            unit, per_launch = "GB/s", {"bytes_per_launch": x["bytes"] / nl}
+        else:
+            ach = x["flops"] / (x["ms"] / 1e3) / 1e12
+            unit, per_launch = "TFLOP/s", {"flops_per_launch": x["flops"] / nl}
+        roof[name] = {"bound": x["bound"], "kernel": name, "achieved": ach, "peak": x["peak"], "unit": unit,
+                      "frac": ach / x["peak"], "traffic": load_traffic(name, args.workload), **per_launch,
+                      "launches_per_step": x["launches"], "kernel_ms": x["ms"] / nl, "kernel_ms_per_step": x["ms"],
                       "note": x["note"]}
     dom = max(roof, key=lambda k_: roof[k_]["kernel_ms_per_step"])
     out = {

@@ -954,8 +954,8 @@ __global__ void __launch_bounds__(256) lm_attn_delta_kernel(const float* __restr
 // bf16 parts Bh, Bl (the weight split once per step).  Workgroup tile 128 rows x 128
 // columns, 4 waves of 64 x 64 (2 x 2 MFMA blocks); B's parts go through LDS in chunks
 // of 64 channels, A's fragments come from global memory.  M % 128 == 0 or the rows past
-// M are not stored; columns past N read zero weights and are not stored; K % 64 == 0.
-constexpr int XT = 128, XK = 64;
+// M are not stored; columns past N read zero weights and are not stored; K % XK == 0.
+constexpr int XT = 128, XK = 32;
 
 __global__ void __launch_bounds__(256) lm_gemm_x3_kernel(const float* __restrict__ A, const uint16_t* __restrict__ Bh,
                                                          const uint16_t* __restrict__ Bl, float* __restrict__ C,
@@ -963,7 +963,8 @@ __global__ void __launch_bounds__(256) lm_gemm_x3_kernel(const float* __restrict
     __shared__ __align__(16) uint4 SH[XT][XK / 8 + 1];  // [column][8-channel piece], padded
     __shared__ __align__(16) uint4 SL[XT][XK / 8 + 1];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w & 1, wn = w >> 1, hf = lane >> 5;
-    const int64_t m0 = (int64_t)blockIdx.x * XT, n0 = (int64_t)blockIdx.y * XT;
+    // column tile fastest: the workgroups of one row tile run together and share its rows in L2
+    const int64_t m0 = (int64_t)blockIdx.y * XT, n0 = (int64_t)blockIdx.x * XT;
     hf32x16 acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -987,10 +988,10 @@ __global__ void __launch_bounds__(256) lm_gemm_x3_kernel(const float* __restrict
                 av[i][ks][1] = *reinterpret_cast<const float4*>(arow[i] + k0 + 16 * ks + 4);
             }
         __syncthreads();  // the previous chunk's weight parts are used up
-        // 128 columns x 8 pieces of 8 channels, hi and lo: 1024 uint4 each, 4 per thread
+        // 128 columns x XK / 8 pieces of 8 channels, hi and lo
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int f = threadIdx.x + 256 * u, col = f >> 3, pc = f & 7;
+        for (int u = 0; u < XT * (XK / 8) / 256; ++u) {
+            const int f = threadIdx.x + 256 * u, col = f / (XK / 8), pc = f % (XK / 8);
             const int64_t n = n0 + col;
             uint4 h = make_uint4(0u, 0u, 0u, 0u), l = h;
             if (n < N) {
@@ -1200,7 +1201,7 @@ hipError_t lm_gemm_x3(const float* A, const uint16_t* Bh, const uint16_t* Bl, fl
     bool timed;
     hipError_t e = launch_timer_begin(kTimedLmGemm, s, timed);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(lm_gemm_x3_kernel, dim3((unsigned)((M + XT - 1) / XT), (unsigned)((N + XT - 1) / XT)),
+    hipLaunchKernelGGL(lm_gemm_x3_kernel, dim3((unsigned)((N + XT - 1) / XT), (unsigned)((M + XT - 1) / XT)),
                        dim3(256), 0, s, A, Bh, Bl, C, (int)M, (int)N, (int)K);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return launch_timer_end(kTimedLmGemm, s, timed);
