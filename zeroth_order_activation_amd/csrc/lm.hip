@@ -25,6 +25,7 @@
 //   CE          D_CE = log1p(sum_v p_v expm1(D_z_v)) - D_z_y
 // so every reward keeps fp32 relative accuracy however small it is.
 #include <hip/hip_runtime.h>
+#include <algorithm>
 #include <math.h>
 #include <stdint.h>
 
@@ -633,17 +634,47 @@ __device__ __forceinline__ void expm1_x16(float (&x)[16]) {
     for (int r = 0; r < 16; ++r) x[r] = q[r];
 }
 
+// the degree-6 Taylor polynomial of exp(x) - 1 (relative truncation below 5e-8 for |x| < 1/4)
+__device__ __forceinline__ float expm1_poly(float x) {
+    return x * fmaf(x, fmaf(x, fmaf(x, fmaf(x, fmaf(x, 1.0f / 720.0f, 1.0f / 120.0f), 1.0f / 24.0f), 1.0f / 6.0f),
+                        0.5f), 1.0f);
+}
+
 // Per row r (draw i, token t) and vocabulary segment: sum_v p_t[v] expm1(D_z[r][v]) with
 // D_z = D_u W_head^T formed on bf16x3 MFMA (products within ~3 2^-17 of fp32), as the
 // transposed product D_z^T[v][r] so that a lane holds one row (token) and 16 of its
 // vocabulary entries: the row's sum accumulates in one register.  One workgroup: a
 // block of 64 tokens x one vocabulary segment x a group of HDG draws; the group's D_u
-// rows are split into bf16 parts once, into LDS; each wave takes every fourth 32-entry
+// rows are split into bf16 parts once, into LDS; each wave takes every eighth 32-entry
 // vocabulary block of the segment, holds its W_head fragments and the 64 tokens'
 // probabilities in registers and runs all the group's rows against them.  Workgroups
 // of one (token block, segment) run on one XCD (workgroup id mod 8), sharing its L2.
 constexpr int HDG = 4;   // draws per workgroup
 constexpr int HW = 8;    // waves per workgroup (two per SIMD)
+
+// slot swizzle of the split D_u rows in LDS (2 KS 16-byte slots per row)
+template <int KS>
+__device__ __forceinline__ int head_swz(int row) {
+    static_assert(KS == 4 || KS == 8, "d = 64 or 128");
+    return KS == 8 ? (row & 15) : ((row & 7) ^ ((row >> 3) & 1));
+}
+
+// D_z^T block of 32 vocabulary rows (the W_head fragments a lane holds) x the 32 tokens
+// of `row`'s half, for draw j of the workgroup's group: hi*lo + lo*hi + hi*hi per 16 channels
+template <int KS>
+__device__ __forceinline__ hf32x16 head_block(const uint4 (&ahi)[KS], const uint4 (&alo)[KS], const uint4* UH,
+                                              const uint4* UL, int j, int row, int hf) {
+    hf32x16 c = {};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const int at = (j * 64 + row) * 2 * KS + ((2 * ks + hf) ^ head_swz<KS>(row));
+        const uint4 h = UH[at], l = UL[at];
+        c = mfma_bf16(alo[ks], h, c);
+        c = mfma_bf16(ahi[ks], l, c);
+        c = mfma_bf16(ahi[ks], h, c);
+    }
+    return c;
+}
 
 template <int KS>  // d = 16 KS
 __global__ void __launch_bounds__(64 * HW) lm_head_delta_kernel(const float* __restrict__ du,
@@ -661,14 +692,18 @@ __global__ void __launch_bounds__(64 * HW) lm_head_delta_kernel(const float* __r
     if (pair >= (T / 64) * nseg) return;
     const int tb = pair / nseg, sg = pair % nseg, dn = min(HDG, kc - g * HDG);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hf = lane >> 5;
-    // unit (j, row, ks, h) = 8 channels 16 ks + 8 h of row `row` of draw j; stored at
-    // ((j 64 + row) KS + (ks ^ (row & (KS - 1)))) 2 + h so that a wave's 32 rows spread over the banks
-    for (int u = threadIdx.x; u < dn * 64 * KS * 2; u += 64 * HW) {
+    // unit (j, row, ks, h) = 8 channels 16 ks + 8 h of row `row` of draw j, stored at slot
+    // (2 ks + h) ^ head_swz(row) of the row's 2 KS slots: any 8 (and any 16) consecutive rows
+    // reading one (ks, h) hit distinct 16-byte bank groups
+    // draws past the last one of a short group are zero rows: their changes are 0 and unused
+    for (int u = threadIdx.x; u < UNITS; u += 64 * HW) {
         const int h = u & 1, ks = (u >> 1) % KS, row = (u / (2 * KS)) % 64, j = u / (2 * KS * 64);
-        const float* a = du + ((int64_t)(g * HDG + j) * T + (int64_t)tb * 64 + row) * D + 16 * ks + 8 * h;
-        uint4 hi, lo;
-        split8(*reinterpret_cast<const float4*>(a), *reinterpret_cast<const float4*>(a + 4), hi, lo);
-        const int at = ((j * 64 + row) * KS + (ks ^ (row & (KS - 1)))) * 2 + h;
+        uint4 hi = make_uint4(0, 0, 0, 0), lo = hi;
+        if (j < dn) {
+            const float* a = du + ((int64_t)(g * HDG + j) * T + (int64_t)tb * 64 + row) * D + 16 * ks + 8 * h;
+            split8(*reinterpret_cast<const float4*>(a), *reinterpret_cast<const float4*>(a + 4), hi, lo);
+        }
+        const int at = (j * 64 + row) * 2 * KS + ((2 * ks + h) ^ head_swz<KS>(row));
         UH[at] = hi;
         UL[at] = lo;
     }
@@ -686,41 +721,64 @@ __global__ void __launch_bounds__(64 * HW) lm_head_delta_kernel(const float* __r
             ahi[ks] = *reinterpret_cast<const uint4*>(bh + 16 * ks);
             alo[ks] = *reinterpret_cast<const uint4*>(bl + 16 * ks);
         }
+        float pv[2][16];  // p of this lane's token (column) at the 16 vocabulary rows it holds, per token half
 #pragma unroll
-        for (int th = 0; th < 2; ++th) {  // token half: 32 tokens as the MFMA columns
-            float pv[16];  // p of this lane's token (column) at the 16 vocabulary rows it holds
+        for (int th = 0; th < 2; ++th) {
             const float* pp = prob + ((int64_t)tb * 64 + 32 * th + (lane & 31)) * Vp + v0 + 4 * hf;
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const float4 q = *reinterpret_cast<const float4*>(pp + 8 * m);
-                pv[4 * m] = q.x;
-                pv[4 * m + 1] = q.y;
-                pv[4 * m + 2] = q.z;
-                pv[4 * m + 3] = q.w;
-            }
-            const int row = 32 * th + (lane & 31);
-            for (int j = 0; j < dn; ++j) {
-                hf32x16 c = {};
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const int at = ((j * 64 + row) * KS + (ks ^ (row & (KS - 1)))) * 2 + hf;
-                    const uint4 h = UH[at], l = UL[at];
-                    c = mfma_bf16(alo[ks], h, c);
-                    c = mfma_bf16(ahi[ks], l, c);
-                    c = mfma_bf16(ahi[ks], h, c);
-                }
-                float x[16];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) x[r] = c[r];
-                expm1_x16(x);
-                float acc = 0.f;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc = fmaf(pv[r], x[r], acc);
-#pragma unroll
-                for (int jj = 0; jj < HDG; ++jj)
-                    if (jj == j) s[jj][th] += acc;
+                pv[th][4 * m] = q.x;
+                pv[th][4 * m + 1] = q.y;
+                pv[th][4 * m + 2] = q.z;
+                pv[th][4 * m + 3] = q.w;
             }
         }
+        // Fast pass over the (token half, draw) blocks with the polynomial alone, branch-free and
+        // software-pipelined: stage b runs block b's MFMA chain beside block b - 1's exp - 1 and
+        // sum (scheduling barriers keep two blocks live at most).  A block in which some |D_z|
+        // reaches 1/4 is flagged (wave-uniform) and recomputed below.
+        float acc[2][HDG];
+        uint32_t bad = 0;
+        hf32x16 cp = head_block<KS>(ahi, alo, UH, UL, 0, lane & 31, hf);
+#pragma unroll
+        for (int b = 1; b <= 2 * HDG; ++b) {
+            hf32x16 cn;
+            if (b < 2 * HDG) cn = head_block<KS>(ahi, alo, UH, UL, b % HDG, 32 * (b / HDG) + (lane & 31), hf);
+            const int th = (b - 1) / HDG, j = (b - 1) % HDG;
+            float mx = 0.f, a = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                mx = fmaxf(mx, fabsf(cp[r]));
+                a = fmaf(pv[th][r], expm1_poly(cp[r]), a);
+            }
+            acc[th][j] = a;
+            bad |= __builtin_amdgcn_ballot_w64(mx >= 0.25f) ? 1u << (b - 1) : 0u;
+            __builtin_amdgcn_sched_barrier(0);
+            if (b < 2 * HDG) cp = cn;
+        }
+        if (bad) {  // exact pass for the flagged blocks: exp(x) - 1 where |x| >= 1/4
+            for (int b = 0; b < 2 * HDG; ++b) {
+                if (!((bad >> b) & 1)) continue;
+                const int th = b / HDG, j = b % HDG, row = 32 * th + (lane & 31);
+                const hf32x16 c = head_block<KS>(ahi, alo, UH, UL, j, row, hf);
+                float a = 0.f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float x = c[r];
+                    a = fmaf(th ? pv[1][r] : pv[0][r], fabsf(x) < 0.25f ? expm1_poly(x) : __expf(x) - 1.0f, a);
+                }
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int jj = 0; jj < HDG; ++jj)
+                        if (tt * HDG + jj == b) acc[tt][jj] = a;
+            }
+        }
+#pragma unroll
+        for (int th = 0; th < 2; ++th)
+#pragma unroll
+            for (int j = 0; j < HDG; ++j) s[j][th] += acc[th][j];
     }
     // the two halves of a wave hold the same tokens (different vocabulary rows); then the waves
 #pragma unroll
@@ -774,7 +832,16 @@ __global__ void __launch_bounds__(256) lm_head_reward_kernel(const float* __rest
 // [channel][key] bf16 parts, in that key order.  Then
 //   D_o = (acc - rho o) / (1 + rho),  rho = sum_key w1,
 // the two key halves added through LDS.
-constexpr int AVP = 72;  // padded row of the transposed tiles (bf16)
+constexpr int AVP = 68;  // padded row of the transposed tiles (bf16): 136 bytes, so that the 8-byte
+                         // reads of 32 consecutive channels at one key fall in distinct bank pairs
+
+// the transposed tiles, and after the last tile the odd key half's partial sums in the same bytes
+union AttnDeltaLds {
+    struct {
+        uint16_t vth[64][AVP], vtl[64][AVP], dvth[64][AVP], dvtl[64][AVP];
+    } t;
+    float accx[2][64][33];  // [query block][channel][query]
+};
 
 __device__ __forceinline__ uint4 vt_frag(const uint16_t (*t)[AVP], int c, int k0) {
     const uint2 a = *reinterpret_cast<const uint2*>(&t[c][k0]);
@@ -789,12 +856,13 @@ __global__ void __launch_bounds__(256) lm_attn_delta_kernel(const float* __restr
                                                             const float* __restrict__ dk,
                                                             const float* __restrict__ dv, int T, int S, int H,
                                                             float* __restrict__ dout) {
-    __shared__ __align__(16) uint16_t VTH[64][AVP];
-    __shared__ __align__(16) uint16_t VTL[64][AVP];
-    __shared__ __align__(16) uint16_t DVTH[64][AVP];
-    __shared__ __align__(16) uint16_t DVTL[64][AVP];
-    __shared__ float accx[2][64][33];  // the odd key half's partial sums: [query block][channel][query]
+    __shared__ __align__(16) AttnDeltaLds lds;
     __shared__ float rhox[2][32];
+    uint16_t(*VTH)[AVP] = lds.t.vth;
+    uint16_t(*VTL)[AVP] = lds.t.vtl;
+    uint16_t(*DVTH)[AVP] = lds.t.dvth;
+    uint16_t(*DVTL)[AVP] = lds.t.dvtl;
+    float(*accx)[64][33] = lds.accx;
     const int nqt = S / 64, nbh = (T / S) * H;
     const int qt = blockIdx.x % nqt, bh = (blockIdx.x / nqt) % nbh, i = blockIdx.x / (nqt * nbh);
     const int b = bh / H, h = bh % H, d = 64 * H;
@@ -919,6 +987,7 @@ __global__ void __launch_bounds__(256) lm_attn_delta_kernel(const float* __restr
         }
     }
     rho += __shfl_xor(rho, 32, 64);  // the lane pair of a query holds its two key quarters
+    __syncthreads();  // the last tile's transposed values are used up: accx takes their bytes
     if (kb == 1) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -963,8 +1032,9 @@ __global__ void __launch_bounds__(256) lm_gemm_x3_kernel(const float* __restrict
     __shared__ __align__(16) uint4 SH[XT][XK / 8 + 1];  // [column][8-channel piece], padded
     __shared__ __align__(16) uint4 SL[XT][XK / 8 + 1];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w & 1, wn = w >> 1, hf = lane >> 5;
-    // column tile fastest: the workgroups of one row tile run together and share its rows in L2
-    const int64_t m0 = (int64_t)blockIdx.y * XT, n0 = (int64_t)blockIdx.x * XT;
+    const int nx = (N + XT - 1) / XT, loc = blockIdx.x >> 3, rt = (blockIdx.x & 7) + 8 * (loc / nx);
+    if ((int64_t)rt * XT >= M) return;
+    const int64_t m0 = (int64_t)rt * XT, n0 = (int64_t)(loc % nx) * XT;
     hf32x16 acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -1201,7 +1271,8 @@ hipError_t lm_gemm_x3(const float* A, const uint16_t* Bh, const uint16_t* Bl, fl
     bool timed;
     hipError_t e = launch_timer_begin(kTimedLmGemm, s, timed);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(lm_gemm_x3_kernel, dim3((unsigned)((N + XT - 1) / XT), (unsigned)((M + XT - 1) / XT)),
+    const int64_t nx = (N + XT - 1) / XT, ny = (M + XT - 1) / XT;
+    hipLaunchKernelGGL(lm_gemm_x3_kernel, dim3((unsigned)(8 * nx * ((ny + 7) / 8))),
                        dim3(256), 0, s, A, Bh, Bl, C, (int)M, (int)N, (int)K);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return launch_timer_end(kTimedLmGemm, s, timed);
