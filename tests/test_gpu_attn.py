@@ -1,7 +1,8 @@
 """GPU parity of the attention projection estimators (values, keys, queries) against their oracle.
 
 Small cases element by element (one and several query tiles per sequence, several
-sequences and heads, more draws than one pass of the partial buffer holds), and the
+sequences and heads, more draws than one pass of the partial buffer holds, the longest
+sequence accepted (4096) and sixteen heads), and the
 full-size 2 x 2048-token, 8-head workload on tokens sampled near the ends of the
 sequences (their rewards need the outputs of few later queries), the weight gradient
 against the fp64 identity G = g_hat^T U, and determinism.
@@ -36,6 +37,8 @@ CASES = [
     (1, 192, 1, 9, 3e-2),   # three query tiles: causal tiles below the diagonal
     (3, 128, 4, 3, 1e-2),   # several sequences and heads
     (1, 64, 1, 70, 1e-2),   # more draws than one pass of partials (64)
+    (1, 4096, 1, 2, 1e-2),  # the longest sequence accepted: 64 query tiles
+    (1, 64, 16, 3, 1e-2),   # sixteen heads
 ]
 
 
@@ -81,6 +84,10 @@ QK_CASES = [
     ("q", 3, 128, 4, 70, 1e-2),  # more draws than one pass of partials
     ("k", 1, 64, 1, 70, 0.2),    # |delta| past the polynomial's range: exp - 1
     ("q", 2, 128, 2, 9, 0.2),    # the same for queries, over two key tiles
+    ("k", 1, 4096, 1, 2, 1e-2),  # the longest sequence accepted
+    ("q", 1, 4096, 1, 2, 1e-2),
+    ("k", 1, 64, 16, 3, 1e-2),   # sixteen heads
+    ("q", 1, 64, 16, 3, 1e-2),
 ]
 
 
