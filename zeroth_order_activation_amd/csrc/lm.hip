@@ -135,104 +135,120 @@ __global__ void __launch_bounds__(256) lm_layernorm_kernel(const float* __restri
     }
 }
 
-// Causal attention of 64 queries x one head, 4 threads per query (16 channels
-// each); two passes over the keys: the row maximum, then p, sum p, sum p v.
-__device__ __forceinline__ float quad_total(float v) {
-    v += __shfl_xor(v, 1, 64);
-    return v + __shfl_xor(v, 2, 64);
+// Causal attention of FQ = 8 queries x one head per workgroup (one wave): the 8 lanes of
+// a query split its keys (lane r takes keys r mod 8) and hold all 64 channels, so a dot
+// product needs no other lane.  Each lane keeps an online softmax over its keys (running
+// maximum, sum and output) and the 8 lanes merge once at the end.  The key and value tiles
+// up to the queries' own 64-key tile are staged in LDS, rows padded to 68 floats so that
+// the 8 lanes of a query read 8 consecutive rows at one column in distinct banks.  The raw
+// logits go to the probability cache during the pass and become probabilities once the
+// log-sum-exp is known: each lane rewrites the keys it wrote.
+constexpr int FQ = 8;
+constexpr int FKP = 68;
+
+// over the 8 lanes of an aligned octet: row half-mirror (lane i with 7 - i), then quad xor 1 and 2
+__device__ __forceinline__ float oct_total(float v) {
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+    return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float oct_max(float v) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true)));
+    return fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true)));
 }
 
-__device__ __forceinline__ void load16(const float* p, float (&r)[16]) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const float4 f = *reinterpret_cast<const float4*>(p + 4 * j);
-        r[4 * j] = f.x;
-        r[4 * j + 1] = f.y;
-        r[4 * j + 2] = f.z;
-        r[4 * j + 3] = f.w;
-    }
-}
-
-template <int NT = 256>
-__device__ __forceinline__ void stage_tile(float (*dst)[64], const float* src, int64_t row0, int d, int h) {
-    // 64 rows x 64 channels of head h: 1024 float4 over NT lanes
-#pragma unroll
-    for (int j = 0; j < 1024 / NT; ++j) {
-        const int f = threadIdx.x + NT * j, row = f >> 4, c4 = (f & 15) * 4;
-        *reinterpret_cast<float4*>(&dst[row][c4]) =
-            *reinterpret_cast<const float4*>(src + (row0 + row) * d + h * 64 + c4);
-    }
-}
-
-// Causal attention of FQ = 16 queries x one head per workgroup (one wave, 4 lanes per
-// query, 16 channels each), so that short inputs still give many workgroups; the key
-// tiles up to the queries' own 64-key tile are staged in LDS; three passes over the
-// keys: the row maximum; p, sum p and sum p v; the probabilities for the cache.
-constexpr int FQ = 16;
-
-__global__ void __launch_bounds__(4 * FQ) lm_attn_fwd_kernel(const float* __restrict__ q, const float* __restrict__ k,
+__global__ void __launch_bounds__(8 * FQ) lm_attn_fwd_kernel(const float* __restrict__ q, const float* __restrict__ k,
                                                              const float* __restrict__ v, int T, int S, int H,
                                                              float* __restrict__ o, float* __restrict__ lse,
                                                              float* __restrict__ pc) {
-    __shared__ __align__(16) float Ks[64][64];
-    __shared__ __align__(16) float Vs[64][64];
+    __shared__ __align__(16) float Ks[64][FKP];
+    __shared__ __align__(16) float Vs[64][FKP];
     const int nqt = S / FQ, qt = blockIdx.x % nqt, bh = blockIdx.x / nqt, b = bh / H, h = bh % H;
-    const int d = 64 * H, ql = threadIdx.x >> 2, qr = threadIdx.x & 3;
+    const int d = 64 * H, ql = threadIdx.x >> 3, r = threadIdx.x & 7;
     const int query = qt * FQ + ql, q64 = (qt * FQ) / 64;  // the queries' 64-key tile
     const int64_t s0 = (int64_t)b * S, row = s0 + query;
-    float qv[16];
-    load16(q + row * d + h * 64 + qr * 16, qv);
-    float mx = -INFINITY;
-    for (int kt = 0; kt <= q64; ++kt) {
-        __syncthreads();
-        stage_tile<4 * FQ>(Ks, k, s0 + kt * 64, d, h);
-        __syncthreads();
-        for (int j = 0; j < 64; ++j) {
-            float dot = 0.f;
+    float qv[64];  // the query scaled by 1/8 (exact)
 #pragma unroll
-            for (int c = 0; c < 16; ++c) dot = fmaf(qv[c], Ks[j][qr * 16 + c], dot);
-            dot = quad_total(dot) * 0.125f;
-            if (kt * 64 + j <= query) mx = fmaxf(mx, dot);
-        }
+    for (int c4 = 0; c4 < 16; ++c4) {
+        const float4 f = *reinterpret_cast<const float4*>(q + row * d + h * 64 + 4 * c4);
+        qv[4 * c4] = 0.125f * f.x;
+        qv[4 * c4 + 1] = 0.125f * f.y;
+        qv[4 * c4 + 2] = 0.125f * f.z;
+        qv[4 * c4 + 3] = 0.125f * f.w;
     }
-    float s = 0.f, acc[16];
+    float m = -INFINITY, s = 0.f, acc[64];
 #pragma unroll
-    for (int c = 0; c < 16; ++c) acc[c] = 0.f;
-    for (int kt = 0; kt <= q64; ++kt) {
-        __syncthreads();
-        stage_tile<4 * FQ>(Ks, k, s0 + kt * 64, d, h);
-        stage_tile<4 * FQ>(Vs, v, s0 + kt * 64, d, h);
-        __syncthreads();
-        for (int j = 0; j < 64; ++j) {
-            float dot = 0.f;
-#pragma unroll
-            for (int c = 0; c < 16; ++c) dot = fmaf(qv[c], Ks[j][qr * 16 + c], dot);
-            dot = quad_total(dot) * 0.125f;
-            const float p = kt * 64 + j <= query ? __expf(dot - mx) : 0.f;
-            s += p;
-#pragma unroll
-            for (int c = 0; c < 16; ++c) acc[c] = fmaf(p, Vs[j][qr * 16 + c], acc[c]);
-        }
-    }
-    const float inv = 1.0f / s, l = mx + logf(s);
-#pragma unroll
-    for (int c = 0; c < 16; ++c) o[row * d + h * 64 + qr * 16 + c] = acc[c] * inv;
-    if (qr == 0) lse[row * H + h] = l;
-    // the probabilities of this query over the key tiles up to its own (zero after it):
-    // pc[((b H + h) S + query) S + key]; lane qr of the query writes keys j = qr mod 4
+    for (int c = 0; c < 64; ++c) acc[c] = 0.f;
     float* prow = pc + ((int64_t)bh * S + query) * S;
     for (int kt = 0; kt <= q64; ++kt) {
+        __syncthreads();  // the previous tiles are used up
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {  // 64 rows x 16 float4 of each tile over the 64 lanes
+            const int f = threadIdx.x + 64 * jj, rr = f >> 4, c4 = (f & 15) * 4;
+            const int64_t src = (s0 + kt * 64 + rr) * d + h * 64 + c4;
+            *reinterpret_cast<float4*>(&Ks[rr][c4]) = *reinterpret_cast<const float4*>(k + src);
+            *reinterpret_cast<float4*>(&Vs[rr][c4]) = *reinterpret_cast<const float4*>(v + src);
+        }
         __syncthreads();
-        stage_tile<4 * FQ>(Ks, k, s0 + kt * 64, d, h);
-        __syncthreads();
-        for (int j = 0; j < 64; ++j) {
+        float dl[8], tm = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int j = 8 * i + r, key = kt * 64 + j;
             float dot = 0.f;
 #pragma unroll
-            for (int c = 0; c < 16; ++c) dot = fmaf(qv[c], Ks[j][qr * 16 + c], dot);
-            dot = quad_total(dot) * 0.125f;
-            if ((j & 3) == qr) prow[kt * 64 + j] = kt * 64 + j <= query ? __expf(dot - l) : 0.f;
+            for (int c4 = 0; c4 < 16; ++c4) {
+                const float4 kk = *reinterpret_cast<const float4*>(&Ks[j][4 * c4]);
+                dot = fmaf(qv[4 * c4], kk.x, dot);
+                dot = fmaf(qv[4 * c4 + 1], kk.y, dot);
+                dot = fmaf(qv[4 * c4 + 2], kk.z, dot);
+                dot = fmaf(qv[4 * c4 + 3], kk.w, dot);
+            }
+            dl[i] = key <= query ? dot : -INFINITY;
+            tm = fmaxf(tm, dl[i]);
+            prow[key] = dl[i];  // the raw logit, rewritten as a probability below
+        }
+        const float mn = fmaxf(m, tm), sc = mn == m ? 1.f : __expf(m - mn);
+        s *= sc;
+#pragma unroll
+        for (int c = 0; c < 64; ++c) acc[c] *= sc;
+        m = mn;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int j = 8 * i + r;
+            const float p = dl[i] > -INFINITY ? __expf(dl[i] - m) : 0.f;
+            s += p;
+#pragma unroll
+            for (int c4 = 0; c4 < 16; ++c4) {
+                const float4 vv = *reinterpret_cast<const float4*>(&Vs[j][4 * c4]);
+                acc[4 * c4] = fmaf(p, vv.x, acc[4 * c4]);
+                acc[4 * c4 + 1] = fmaf(p, vv.y, acc[4 * c4 + 1]);
+                acc[4 * c4 + 2] = fmaf(p, vv.z, acc[4 * c4 + 2]);
+                acc[4 * c4 + 3] = fmaf(p, vv.w, acc[4 * c4 + 3]);
+            }
         }
     }
+    // merge the 8 lanes: lane 0 holds key 0, so the maximum is finite
+    const float M = oct_max(m), sc = __expf(m - M);  // 0 for a lane whose keys were all masked
+    s = oct_total(s * sc);
+#pragma unroll
+    for (int c = 0; c < 64; ++c) acc[c] = oct_total(acc[c] * sc);
+    const float inv = 1.0f / s, l = M + logf(s);
+    if (r == 0) {
+#pragma unroll
+        for (int c4 = 0; c4 < 16; ++c4)
+            *reinterpret_cast<float4*>(o + row * d + h * 64 + 4 * c4) =
+                make_float4(acc[4 * c4] * inv, acc[4 * c4 + 1] * inv, acc[4 * c4 + 2] * inv, acc[4 * c4 + 3] * inv);
+        lse[row * H + h] = l;
+    }
+    // the probabilities over the key tiles up to the query's own (zero after the query):
+    // pc[((b H + h) S + query) S + key]
+    for (int kt = 0; kt <= q64; ++kt)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int key = kt * 64 + 8 * i + r;
+            prow[key] = key <= query ? __expf(prow[key] - l) : 0.f;
+        }
 }
 
 __device__ __forceinline__ float phi_cdf(float x) { return 0.5f * erfcf(-x * 0.70710678118654752f); }
@@ -1133,7 +1149,7 @@ hipError_t lm_layernorm(const float* x, int64_t R, int d, float eps, float* u, f
 
 hipError_t lm_attn_fwd(const float* q, const float* k, const float* v, int T, int S, int H, float* o, float* lse,
                        float* pc, hipStream_t s) {
-    hipLaunchKernelGGL(lm_attn_fwd_kernel, dim3((unsigned)((T / S) * H * (S / FQ))), dim3(4 * FQ), 0, s, q, k, v, T,
+    hipLaunchKernelGGL(lm_attn_fwd_kernel, dim3((unsigned)((T / S) * H * (S / FQ))), dim3(8 * FQ), 0, s, q, k, v, T,
                        S, H, o, lse, pc);
     return hipGetLastError();
 }
