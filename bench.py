@@ -432,9 +432,10 @@ def lm_change_gemm_flops(c):
 def lm_change_gemm_bytes(c):
     """HBM bytes of the change-row GEMMs of one step: each reads its change rows (K_in
     floats) and writes its output rows (N_out floats); the weights' bf16 parts are small and
-    stay in cache.  Blocks as in lm_change_gemm_flops."""
+    stay in cache.  The query, key and value changes are one product (d in, 3d out), then W_O
+    (d in, d out).  Blocks as in lm_change_gemm_flops."""
     T, d, n, L, K, M = c["T"], c["d"], c["n"], c["L"], c["K"], c["M"]
-    attn, mlp = 4 * (d + d), 2 * (d + n)
+    attn, mlp = (d + 3 * d) + (d + d), 2 * (d + n)
     full = attn + mlp
     first = {"emb": full, "o": mlp, "up": n + d, "down": 0, "es": mlp}
     per_draw = {k: v + (L - 1) * full for k, v in first.items()}

@@ -613,9 +613,9 @@ LmLayout lm_layout(const LmDims& D, int64_t K, int64_t M, int64_t chunk) {
     L.nseg = (L.vp + L.vseg - 1) / L.vseg;
     L.DX = take(R * d);
     L.DU = take(R * d);
-    L.DQ = take(R * d);
-    L.DK = take(R * d);
-    L.DV = take(R * d);
+    L.DQ = take(3 * R * d);  // D_q, D_k, D_v: three consecutive [R, d] planes (one product writes them)
+    L.DK = L.DQ + (size_t)(R * d) * sizeof(float);
+    L.DV = L.DK + (size_t)(R * d) * sizeof(float);
     L.DO = take(R * d);
     L.DB = take(R * d);
     L.DH = take(R * n);
@@ -717,6 +717,7 @@ hipError_t lm_delta_chunk(const LmRun& R, int kind, int kn, uint32_t draw0, floa
     auto wl = [&](int64_t l, int64_t off) {
         return reinterpret_cast<const uint16_t*>(R.ws + L.WSL[l]) + (off - R.P.wq(l));
     };
+    const int64_t qkv_plane = L.kc * D.T * D.d;  // floats from D_q to D_k and from D_k to D_v
     bool live = false;  // whether DX holds a change yet
     if (kind == 0) {
         LM_TRY(zero(DX, rows * d));
@@ -727,9 +728,9 @@ hipError_t lm_delta_chunk(const LmRun& R, int kind, int kn, uint32_t draw0, floa
         const int64_t wq = R.P.wq(l);
         if (live) {
             LM_TRY(dust::lm_layernorm_delta(R.f(L.X[l]), R.f(L.MU1[l]), R.f(L.RS1[l]), DX, rows, T, d, DU, st));
-            LM_TRY(dust::lm_gemm_x3(DU, wh(l, wq), wl(l, wq), DQ, rows, d, d, st));
-            LM_TRY(dust::lm_gemm_x3(DU, wh(l, wq + D.d * D.d), wl(l, wq + D.d * D.d), DK, rows, d, d, st));
-            LM_TRY(dust::lm_gemm_x3(DU, wh(l, wq + 2 * D.d * D.d), wl(l, wq + 2 * D.d * D.d), DV, rows, d, d, st));
+            // W_Q, W_K, W_V are consecutive rows of one [3d, d] weight and D_q, D_k, D_v
+            // consecutive planes of the workspace: one product reads the change rows once
+            LM_TRY(dust::lm_gemm_x3(DU, wh(l, wq), wl(l, wq), DQ, rows, 3 * d, d, st, d, qkv_plane));
             LM_TRY(dust::lm_attn_delta(R.f(L.Q[l]), R.f(L.Kk[l]), R.f(L.Vv[l]), R.f(L.O[l]), R.f(L.PC[l]), DQ, DK,
                                        DV, kn, T, (int)D.S, (int)D.H, DO, st));
             LM_TRY(dust::lm_gemm_x3(DO, wh(l, R.P.wo(l)), wl(l, R.P.wo(l)), DB, rows, d, d, st));

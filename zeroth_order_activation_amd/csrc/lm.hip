@@ -1044,7 +1044,7 @@ constexpr int XT = 128, XK = 32;
 
 __global__ void __launch_bounds__(256) lm_gemm_x3_kernel(const float* __restrict__ A, const uint16_t* __restrict__ Bh,
                                                          const uint16_t* __restrict__ Bl, float* __restrict__ C,
-                                                         int M, int N, int K) {
+                                                         int M, int N, int K, int pw, int64_t ps) {
     __shared__ __align__(16) uint4 SH[XT][XK / 8 + 1];  // [column][8-channel piece], padded
     __shared__ __align__(16) uint4 SL[XT][XK / 8 + 1];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w & 1, wn = w >> 1, hf = lane >> 5;
@@ -1109,17 +1109,19 @@ __global__ void __launch_bounds__(256) lm_gemm_x3_kernel(const float* __restrict
                 }
         }
     }
-    // D[row][col]: lane holds column lane & 31 and rows (r & 3) + 8 (r >> 2) + 4 hf
+    // D[row][col]: lane holds column lane & 31 and rows (r & 3) + 8 (r >> 2) + 4 hf; column
+    // col goes to plane col / pw (planes of [M, pw], ps floats apart), column col % pw
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        const int64_t col = n0 + 64 * wn + 32 * j + (lane & 31);
+        const int col = (int)n0 + 64 * wn + 32 * j + (lane & 31);
         if (col >= N) continue;
+        float* cp = C + (col / pw) * ps + col % pw;
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t row = m0 + 64 * wm + 32 * i + (r & 3) + 8 * (r >> 2) + 4 * hf;
-                if (row < M) C[row * N + col] = acc[i][j][r];
+                if (row < M) cp[row * pw] = acc[i][j][r];
             }
     }
 }
@@ -1283,13 +1285,15 @@ hipError_t lm_head_reward(const float* du, const float* whead, const int32_t* la
 }
 
 hipError_t lm_gemm_x3(const float* A, const uint16_t* Bh, const uint16_t* Bl, float* C, int64_t M, int64_t N,
-                      int64_t K, hipStream_t s) {
+                      int64_t K, hipStream_t s, int64_t pw, int64_t ps) {
+    if (pw <= 0) pw = N;
+    if (N % pw != 0) return hipErrorInvalidValue;
     bool timed;
     hipError_t e = launch_timer_begin(kTimedLmGemm, s, timed);
     if (e != hipSuccess) return e;
     const int64_t nx = (N + XT - 1) / XT, ny = (M + XT - 1) / XT;
     hipLaunchKernelGGL(lm_gemm_x3_kernel, dim3((unsigned)(8 * nx * ((ny + 7) / 8))),
-                       dim3(256), 0, s, A, Bh, Bl, C, (int)M, (int)N, (int)K);
+                       dim3(256), 0, s, A, Bh, Bl, C, (int)M, (int)N, (int)K, (int)pw, ps);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return launch_timer_end(kTimedLmGemm, s, timed);
 }

@@ -28,9 +28,10 @@ hipError_t lm_ce(const float* z, const int32_t* labels, int T, int V, float* lse
 // the head's change fused with its loss change (d = 64 or 128): bf16 parts of W_head
 // [Vp, d] (Vp = V rounded up to 128, zero rows past V), probabilities [T, Vp];
 // part [kc T, nseg] the per-segment sums, then rew = D_z_y - log1p(sum part)
-// C = A B^T on bf16x3 MFMA for change rows: B given as bf16 parts [N, K]; K % 64 == 0
+// C = A B^T on bf16x3 MFMA for change rows: B given as bf16 parts [N, K]; K % 32 == 0.
+// C is [M, N], or with a plane width pw (N % pw == 0) N / pw planes [M, pw] ps floats apart
 hipError_t lm_gemm_x3(const float* A, const uint16_t* Bh, const uint16_t* Bl, float* C, int64_t M, int64_t N,
-                      int64_t K, hipStream_t s);
+                      int64_t K, hipStream_t s, int64_t pw = 0, int64_t ps = 0);
 hipError_t lm_split(const float* W, int64_t rows, int64_t rows_p, int K, uint16_t* hi, uint16_t* lo, hipStream_t s);
 hipError_t lm_head_delta(const float* du, const uint16_t* whi, const uint16_t* wlo, const float* prob, int d, int kc,
                          int T, int Vp, int vseg, int nseg, float* part, hipStream_t s);
