@@ -719,6 +719,10 @@ hipError_t lm_delta_chunk(const LmRun& R, int kind, int kn, uint32_t draw0, floa
     };
     const int64_t qkv_plane = L.kc * D.T * D.d;  // floats from D_q to D_k and from D_k to D_v
     bool live = false;  // whether DX holds a change yet
+    // the residual updates also form the following LayerNorm change in the same pass when
+    // the width allows; du_ready then says that DU already holds it
+    const bool fuse = dust::lm_residual_ln_fusable(d);
+    bool du_ready = false;
     if (kind == 0) {
         LM_TRY(zero(DX, rows * d));
         LM_TRY(dust::lm_noise_add(DX, kn, T, d, sigma, k0, k1, kLmLidEmb, draw0, st));
@@ -727,7 +731,9 @@ hipError_t lm_delta_chunk(const LmRun& R, int kind, int kn, uint32_t draw0, floa
     for (int64_t l = 0; l < D.L; ++l) {
         const int64_t wq = R.P.wq(l);
         if (live) {
-            LM_TRY(dust::lm_layernorm_delta(R.f(L.X[l]), R.f(L.MU1[l]), R.f(L.RS1[l]), DX, rows, T, d, DU, st));
+            if (!du_ready)
+                LM_TRY(dust::lm_layernorm_delta(R.f(L.X[l]), R.f(L.MU1[l]), R.f(L.RS1[l]), DX, rows, T, d, DU, st));
+            du_ready = false;
             // W_Q, W_K, W_V are consecutive rows of one [3d, d] weight and D_q, D_k, D_v
             // consecutive planes of the workspace: one product reads the change rows once
             LM_TRY(dust::lm_gemm_x3(DU, wh(l, wq), wl(l, wq), DQ, rows, 3 * d, d, st, d, qkv_plane));
@@ -740,12 +746,20 @@ hipError_t lm_delta_chunk(const LmRun& R, int kind, int kn, uint32_t draw0, floa
         if (kind == 1) LM_TRY(dust::lm_noise_add(DB, kn, T, d, sigma, k0, k1, lm_lid(l, 3), draw0, st));
         if (live || kind == 1 || es) {
             if (!live) LM_TRY(zero(DX, rows * d));
-            LM_TRY(dust::lm_residual_delta(DX, DB, R.f(L.BA[l]), p + R.P.scal, (int)(2 * l), kn, D.T * D.d, es_sigma,
-                                           draw0, k0, k1, kLmLidEs, st));
+            if (fuse)
+                LM_TRY(dust::lm_residual_ln_delta(DX, DB, R.f(L.BA[l]), p + R.P.scal, (int)(2 * l), kn, T, d, es_sigma,
+                                                  draw0, k0, k1, kLmLidEs, R.f(L.XM[l]), R.f(L.MU2[l]),
+                                                  R.f(L.RS2[l]), DU, st));
+            else
+                LM_TRY(dust::lm_residual_delta(DX, DB, R.f(L.BA[l]), p + R.P.scal, (int)(2 * l), kn, D.T * D.d,
+                                               es_sigma, draw0, k0, k1, kLmLidEs, st));
             live = true;
+            du_ready = fuse;
         }
         if (live) {
-            LM_TRY(dust::lm_layernorm_delta(R.f(L.XM[l]), R.f(L.MU2[l]), R.f(L.RS2[l]), DX, rows, T, d, DU, st));
+            if (!du_ready)
+                LM_TRY(dust::lm_layernorm_delta(R.f(L.XM[l]), R.f(L.MU2[l]), R.f(L.RS2[l]), DX, rows, T, d, DU, st));
+            du_ready = false;
             LM_TRY(dust::lm_gemm_x3(DU, wh(l, R.P.w1(l)), wl(l, R.P.w1(l)), DH, rows, n, d, st));
         } else if (kind == 2) {
             LM_TRY(zero(DH, rows * n));
@@ -761,12 +775,22 @@ hipError_t lm_delta_chunk(const LmRun& R, int kind, int kn, uint32_t draw0, floa
         if (kind == 3) LM_TRY(dust::lm_noise_add(DB, kn, T, d, sigma, k0, k1, lm_lid(l, 5), draw0, st));
         if (mlp || kind == 3 || es) {
             if (!live) LM_TRY(zero(DX, rows * d));
-            LM_TRY(dust::lm_residual_delta(DX, DB, R.f(L.BM[l]), p + R.P.scal, (int)(2 * l + 1), kn, D.T * D.d,
-                                           es_sigma, draw0, k0, k1, kLmLidEs, st));
+            // the next LayerNorm: the next block's first, or the final one
+            const bool last = l + 1 == D.L;
+            const float* nx = R.f(L.X[l + 1]);
+            const float* nmu = R.f(last ? L.MUF : L.MU1[l + 1]);
+            const float* nrs = R.f(last ? L.RSF : L.RS1[l + 1]);
+            if (fuse)
+                LM_TRY(dust::lm_residual_ln_delta(DX, DB, R.f(L.BM[l]), p + R.P.scal, (int)(2 * l + 1), kn, T, d,
+                                                  es_sigma, draw0, k0, k1, kLmLidEs, nx, nmu, nrs, DU, st));
+            else
+                LM_TRY(dust::lm_residual_delta(DX, DB, R.f(L.BM[l]), p + R.P.scal, (int)(2 * l + 1), kn, D.T * D.d,
+                                               es_sigma, draw0, k0, k1, kLmLidEs, st));
             live = true;
+            du_ready = fuse;
         }
     }
-    LM_TRY(dust::lm_layernorm_delta(R.f(L.X[D.L]), R.f(L.MUF), R.f(L.RSF), DX, rows, T, d, DU, st));
+    if (!du_ready) LM_TRY(dust::lm_layernorm_delta(R.f(L.X[D.L]), R.f(L.MUF), R.f(L.RSF), DX, rows, T, d, DU, st));
     if (L.fused) {
         LM_TRY(dust::lm_head_delta(DU, reinterpret_cast<const uint16_t*>(R.ws + L.HBHI),
                                    reinterpret_cast<const uint16_t*>(R.ws + L.HBLO), R.f(L.PP), d, kn, T, (int)L.vp,

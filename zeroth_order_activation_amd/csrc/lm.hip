@@ -415,6 +415,74 @@ __global__ void __launch_bounds__(256) lm_layernorm_delta8_kernel(const float* _
     *reinterpret_cast<float4*>(op + 4) = make_float4(o[4], o[5], o[6], o[7]);
 }
 
+// The residual change (as lm_residual_delta_kernel) of a row, then the LayerNorm change
+// of the updated row (as lm_layernorm_delta8_kernel): D_x is read once.
+template <int LPR>
+__global__ void __launch_bounds__(256) lm_residual_ln_delta8_kernel(float* __restrict__ dx,
+                                                                    const float* __restrict__ db,
+                                                                    const float* __restrict__ b,
+                                                                    const float* __restrict__ scal, int slot,
+                                                                    int64_t R, int T, float es_sigma,
+                                                                    uint32_t member0, uint32_t k0, uint32_t k1,
+                                                                    uint32_t es_layer, const float* __restrict__ x,
+                                                                    const float* __restrict__ mu,
+                                                                    const float* __restrict__ rs,
+                                                                    float* __restrict__ du) {
+    constexpr int D = 8 * LPR;
+    const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LPR;
+    if (row >= R) return;  // whole lane groups: the sums below stay within live groups
+    const int li = threadIdx.x % LPR;
+    const int64_t dr = row / T;
+    const int t = (int)(row - dr * T);
+    const float al = scal[slot];
+    float* dp = dx + row * D + 8 * li;
+    const float* bp = db + row * D + 8 * li;
+    const float4 d0 = *reinterpret_cast<const float4*>(dp), d1 = *reinterpret_cast<const float4*>(dp + 4);
+    const float4 y0 = *reinterpret_cast<const float4*>(bp), y1 = *reinterpret_cast<const float4*>(bp + 4);
+    const float y[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+    float c[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c[e] = fmaf(al, y[e], c[e]);
+    if (es_sigma > 0.f) {
+        const uint32_t m = member0 + (uint32_t)dr;
+        const f32x4 g = gauss4(0u, (uint32_t)(slot >> 2), m >> 1, es_layer, k0, k1);
+        const float coef = ((m & 1u) ? -es_sigma : es_sigma) * g.v[slot & 3];
+        const float* bb = b + (int64_t)t * D + 8 * li;
+        const float4 b0 = *reinterpret_cast<const float4*>(bb), b1 = *reinterpret_cast<const float4*>(bb + 4);
+        const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) c[e] = fmaf(coef, bv[e] + y[e], c[e]);
+    }
+    *reinterpret_cast<float4*>(dp) = make_float4(c[0], c[1], c[2], c[3]);
+    *reinterpret_cast<float4*>(dp + 4) = make_float4(c[4], c[5], c[6], c[7]);
+    // the LayerNorm change of the updated row
+    const float mm = mu[t], r = rs[t];
+    const float* xp = x + (int64_t)t * D + 8 * li;
+    const float4 x0 = *reinterpret_cast<const float4*>(xp), x1 = *reinterpret_cast<const float4*>(xp + 4);
+    const float xc[8] = {x0.x - mm, x0.y - mm, x0.z - mm, x0.w - mm, x1.x - mm, x1.y - mm, x1.z - mm, x1.w - mm};
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += c[e];
+    const float dm = group_total<LPR>(s) / (float)D;
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        c[e] -= dm;
+        s1 = fmaf(xc[e], c[e], s1);
+        s2 = fmaf(c[e], c[e], s2);
+    }
+    const float dv = (2.0f * group_total<LPR>(s1) + group_total<LPR>(s2)) / (float)D;
+    const float f = expm1f(-0.5f * log1pf(dv * r * r));  // rs' / rs - 1
+    const float a = r * (1.0f + f), bf = r * f;
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = fmaf(c[e], a, xc[e] * bf);
+    float* op = du + row * D + 8 * li;
+    *reinterpret_cast<float4*>(op) = make_float4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<float4*>(op + 4) = make_float4(o[4], o[5], o[6], o[7]);
+}
+
+
 __device__ __forceinline__ float expm1_s(float x) {
     if (fabsf(x) < 0.25f)
         return x * fmaf(x, fmaf(x, fmaf(x, fmaf(x, fmaf(x, 1.0f / 720.0f, 1.0f / 120.0f), 1.0f / 24.0f),
@@ -1227,6 +1295,32 @@ hipError_t lm_residual_delta(float* dx, const float* db, const float* b, const f
                              uint32_t es_layer, hipStream_t s) {
     hipLaunchKernelGGL(lm_residual_delta_kernel, dim3(blocks((int64_t)kc * per_draw)), dim3(256), 0, s, dx, db, b,
                        scal, slot, kc, per_draw, es_sigma, member0, k0, k1, es_layer);
+    return hipGetLastError();
+}
+
+bool lm_residual_ln_fusable(int d) { return d == 64 || d == 128 || d == 256 || d == 512; }
+
+template <int LPR>
+static void launch_residual_ln(float* dx, const float* db, const float* b, const float* scal, int slot, int64_t R,
+                               int T, float es_sigma, uint32_t member0, uint32_t k0, uint32_t k1, uint32_t es_layer,
+                               const float* x, const float* mu, const float* rs, float* du, hipStream_t s) {
+    hipLaunchKernelGGL(lm_residual_ln_delta8_kernel<LPR>, dim3(blocks(R * LPR)), dim3(256), 0, s, dx, db, b, scal,
+                       slot, R, T, es_sigma, member0, k0, k1, es_layer, x, mu, rs, du);
+}
+
+hipError_t lm_residual_ln_delta(float* dx, const float* db, const float* b, const float* scal, int slot, int kc,
+                                int T, int d, float es_sigma, uint32_t member0, uint32_t k0, uint32_t k1,
+                                uint32_t es_layer, const float* x, const float* mu, const float* rs, float* du,
+                                hipStream_t s) {
+    const int64_t R = (int64_t)kc * T;
+    if (R == 0) return hipSuccess;
+    switch (d) {
+        case 64: launch_residual_ln<8>(dx, db, b, scal, slot, R, T, es_sigma, member0, k0, k1, es_layer, x, mu, rs, du, s); break;
+        case 128: launch_residual_ln<16>(dx, db, b, scal, slot, R, T, es_sigma, member0, k0, k1, es_layer, x, mu, rs, du, s); break;
+        case 256: launch_residual_ln<32>(dx, db, b, scal, slot, R, T, es_sigma, member0, k0, k1, es_layer, x, mu, rs, du, s); break;
+        case 512: launch_residual_ln<64>(dx, db, b, scal, slot, R, T, es_sigma, member0, k0, k1, es_layer, x, mu, rs, du, s); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

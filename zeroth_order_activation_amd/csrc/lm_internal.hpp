@@ -49,6 +49,13 @@ hipError_t lm_gelu_delta(const float* h, const float* cdf, const float* pdf, con
 hipError_t lm_residual_delta(float* dx, const float* db, const float* b, const float* scal, int slot, int kc,
                              int64_t per_draw, float es_sigma, uint32_t member0, uint32_t k0, uint32_t k1,
                              uint32_t es_layer, hipStream_t s);
+// the residual change, then the LayerNorm change (x, mu, rs of that LayerNorm) of the updated
+// rows into du, in one pass; for d = 64, 128, 256 or 512 (lm_residual_ln_fusable)
+bool lm_residual_ln_fusable(int d);
+hipError_t lm_residual_ln_delta(float* dx, const float* db, const float* b, const float* scal, int slot, int kc,
+                                int T, int d, float es_sigma, uint32_t member0, uint32_t k0, uint32_t k1,
+                                uint32_t es_layer, const float* x, const float* mu, const float* rs, float* du,
+                                hipStream_t s);
 hipError_t lm_ce_delta(const float* z, const float* lse, const float* dz, const int32_t* labels, int kc, int T, int V,
                        float* rew, hipStream_t s);
 hipError_t lm_ghat(const float* rew, int K, int T, int w, float scale, uint32_t k0, uint32_t k1, uint32_t layer,
