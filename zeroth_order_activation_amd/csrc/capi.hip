@@ -724,8 +724,7 @@ hipError_t lm_delta_chunk(const LmRun& R, int kind, int kn, uint32_t draw0, floa
     const bool fuse = dust::lm_residual_ln_fusable(d);
     bool du_ready = false;
     if (kind == 0) {
-        LM_TRY(zero(DX, rows * d));
-        LM_TRY(dust::lm_noise_add(DX, kn, T, d, sigma, k0, k1, kLmLidEmb, draw0, st));
+        LM_TRY(dust::lm_noise_add(DX, kn, T, d, sigma, k0, k1, kLmLidEmb, draw0, st, /*set=*/true));
         live = true;
     }
     for (int64_t l = 0; l < D.L; ++l) {
@@ -740,10 +739,11 @@ hipError_t lm_delta_chunk(const LmRun& R, int kind, int kn, uint32_t draw0, floa
             LM_TRY(dust::lm_attn_delta(R.f(L.Q[l]), R.f(L.Kk[l]), R.f(L.Vv[l]), R.f(L.O[l]), R.f(L.PC[l]), DQ, DK,
                                        DV, kn, T, (int)D.S, (int)D.H, DO, st));
             LM_TRY(dust::lm_gemm_x3(DO, wh(l, R.P.wo(l)), wl(l, R.P.wo(l)), DB, rows, d, d, st));
-        } else if (kind == 1 || es) {
+        } else if (es) {
             LM_TRY(zero(DB, rows * d));
         }
-        if (kind == 1) LM_TRY(dust::lm_noise_add(DB, kn, T, d, sigma, k0, k1, lm_lid(l, 3), draw0, st));
+        // with no change yet the noise is written, not added
+        if (kind == 1) LM_TRY(dust::lm_noise_add(DB, kn, T, d, sigma, k0, k1, lm_lid(l, 3), draw0, st, !live));
         if (live || kind == 1 || es) {
             if (!live) LM_TRY(zero(DX, rows * d));
             if (fuse)
@@ -761,18 +761,14 @@ hipError_t lm_delta_chunk(const LmRun& R, int kind, int kn, uint32_t draw0, floa
                 LM_TRY(dust::lm_layernorm_delta(R.f(L.XM[l]), R.f(L.MU2[l]), R.f(L.RS2[l]), DX, rows, T, d, DU, st));
             du_ready = false;
             LM_TRY(dust::lm_gemm_x3(DU, wh(l, R.P.w1(l)), wl(l, R.P.w1(l)), DH, rows, n, d, st));
-        } else if (kind == 2) {
-            LM_TRY(zero(DH, rows * n));
         }
-        if (kind == 2) LM_TRY(dust::lm_noise_add(DH, kn, T, n, sigma, k0, k1, lm_lid(l, 4), draw0, st));
+        if (kind == 2) LM_TRY(dust::lm_noise_add(DH, kn, T, n, sigma, k0, k1, lm_lid(l, 4), draw0, st, !live));
         const bool mlp = live || kind == 2;
         if (mlp) {
             LM_TRY(dust::lm_gelu_delta(R.f(L.Hh[l]), R.f(L.CDF[l]), R.f(L.PDF[l]), DH, D.T * D.n, rows * n, DM, st));
             LM_TRY(dust::lm_gemm_x3(DM, wh(l, R.P.w2(l)), wl(l, R.P.w2(l)), DB, rows, d, n, st));
-        } else if (kind == 3) {
-            LM_TRY(zero(DB, rows * d));
         }
-        if (kind == 3) LM_TRY(dust::lm_noise_add(DB, kn, T, d, sigma, k0, k1, lm_lid(l, 5), draw0, st));
+        if (kind == 3) LM_TRY(dust::lm_noise_add(DB, kn, T, d, sigma, k0, k1, lm_lid(l, 5), draw0, st, !mlp));
         if (mlp || kind == 3 || es) {
             if (!live) LM_TRY(zero(DX, rows * d));
             // the next LayerNorm: the next block's first, or the final one

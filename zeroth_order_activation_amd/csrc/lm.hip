@@ -317,7 +317,8 @@ __global__ void __launch_bounds__(256) lm_ce_kernel(const float* __restrict__ z,
 // ---- change-propagating forward (rows r = i T + t for draw i of the chunk) --------
 // D[r][c] += sigma a(t, c, draw0 + i, layer)
 __global__ void __launch_bounds__(256) lm_noise_add_kernel(float* __restrict__ D, int kc, int T, int w, float sigma,
-                                                           uint32_t k0, uint32_t k1, uint32_t layer, uint32_t draw0) {
+                                                           uint32_t k0, uint32_t k1, uint32_t layer, uint32_t draw0,
+                                                           int set) {
     const int64_t qi = (int64_t)blockIdx.x * 256 + threadIdx.x;  // quad index
     const int nq = w >> 2;
     if (qi >= (int64_t)kc * T * nq) return;
@@ -325,7 +326,8 @@ __global__ void __launch_bounds__(256) lm_noise_add_kernel(float* __restrict__ D
     const int cq = (int)(qi % nq), i = (int)(r / T), t = (int)(r % T);
     const f32x4 a = gauss4((uint32_t)t, (uint32_t)cq, draw0 + (uint32_t)i, layer, k0, k1);
     float4* p = reinterpret_cast<float4*>(D + r * w + 4 * cq);
-    float4 v = *p;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);  // set: D holds no change yet (not read)
+    if (!set) v = *p;
     v.x = fmaf(sigma, a.v[0], v.x);
     v.y = fmaf(sigma, a.v[1], v.y);
     v.z = fmaf(sigma, a.v[2], v.z);
@@ -1242,9 +1244,9 @@ hipError_t lm_ce(const float* z, const int32_t* labels, int T, int V, float* lse
 }
 
 hipError_t lm_noise_add(float* D, int kc, int T, int w, float sigma, uint32_t k0, uint32_t k1, uint32_t layer,
-                        uint32_t draw0, hipStream_t s) {
+                        uint32_t draw0, hipStream_t s, bool set) {
     hipLaunchKernelGGL(lm_noise_add_kernel, dim3(blocks((int64_t)kc * T * (w / 4))), dim3(256), 0, s, D, kc, T, w,
-                       sigma, k0, k1, layer, draw0);
+                       sigma, k0, k1, layer, draw0, set ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -38,7 +38,7 @@ hipError_t lm_head_delta(const float* du, const uint16_t* whi, const uint16_t* w
 hipError_t lm_head_reward(const float* du, const float* whead, const int32_t* labels, const float* part, int T, int V,
                           int d, int nseg, int64_t rows, float* rew, hipStream_t s);
 hipError_t lm_noise_add(float* D, int kc, int T, int w, float sigma, uint32_t k0, uint32_t k1, uint32_t layer,
-                        uint32_t draw0, hipStream_t s);
+                        uint32_t draw0, hipStream_t s, bool set = false);  // set: D holds no change yet
 hipError_t lm_layernorm_delta(const float* x, const float* mu, const float* rs, const float* dx, int64_t R, int T,
                               int d, float* du, hipStream_t s);
 hipError_t lm_attn_delta(const float* q, const float* k, const float* v, const float* o, const float* pc,
