@@ -47,6 +47,8 @@ SMALL = [
     (9, 500, 8, 3, 0.1, "f32", "uniform"),       # large sigma: library expm1 variant
     (11, 3000, 8, 3, 0.02, "f32", "zipf"),       # degree-6 polynomial
     (5, 20000, 8, 2, 0.5, "bf16", "zipf"),       # large sigma, LDS row
+    (3, 32768, 8, 2, 5e-3, "f32", "zipf"),       # the widest fp32 row accepted
+    (3, 65536, 8, 2, 5e-3, "bf16", "zipf"),      # the widest bf16 row accepted
 ]
 
 
