@@ -60,6 +60,8 @@ SMALL = [
     (37, 512, 128, 1000, 4, 1e-2),     # ragged vocabulary tile, ragged row tiles
     (70, 256, 96, 300, 5, 2e-2),
     (130, 512, 256, 2048, 2, 1e-2),
+    (8, 256, 32, 777, 3, 1e-2),        # the narrowest layer accepted (n = 32), ragged vocabulary
+    (4, 512, 64, 50304, 2, 1e-2),      # a 50304-entry vocabulary (197 tiles of 256)
 ]
 
 
