@@ -49,7 +49,10 @@ def outer_tol(T, n, d):
 
 
 @pytest.mark.parametrize("T,n,d", [(1, 1, 1), (37, 130, 70), (1000, 512, 64), (4096, 2048, 512), (300, 8192, 16),
-                                   (1000, 3000, 700), (4097, 1030, 520)])
+                                   (1000, 3000, 700), (4097, 1030, 520),
+                                   # more 256 x 256 tiles than one round of workgroups: the last
+                                   # round's M-tiles run again with their token range split
+                                   (512, 16640, 1024), (768, 24832, 768)])
 def test_outer_product_matches_fp64(T, n, d):
     rng = np.random.default_rng(T * 7 + n)
     G = rng.standard_normal((T, n)).astype(np.float32)

@@ -21,6 +21,8 @@
 // Token ranges are split over workgroups when the output has too few tiles to
 // fill the 256 CUs; partial sums then go to the workspace and are added in a
 // fixed order (no atomics, bitwise deterministic).
+#include <algorithm>
+
 #include "dust_device.hpp"
 #include "dust_internal.hpp"
 
@@ -45,10 +47,18 @@ struct OuterPlan {
     bool x3;         // bf16x3 path
     int splits;
     int64_t tchunk;  // tokens per split
+    // bf16x3, one split: when the tiles leave a last round of workgroups mostly idle, the
+    // main launch takes the M-tiles [0, mA) (whole rounds) and the rest run as a second
+    // launch with their token range split tsplits ways (partial sums, then summed)
+    int64_t mA;
+    int tsplits;
+    int64_t tchunk_t;
     int64_t Tp;      // padded token count of the pairs (x3)
     int64_t Mp, Np;  // padded row pitches of the ghat and x pairs (x3)
-    size_t off_ah, off_al, off_bh, off_bl, off_part, total;
+    size_t off_ah, off_al, off_bh, off_bl, off_part, off_tail, total;
 };
+
+constexpr int64_t kOuterCUs = 256;  // workgroups of the bf16x3 kernel resident at once (one per CU)
 
 OuterPlan plan_outer(int64_t T, int64_t n, int64_t d) {
     OuterPlan p{};
@@ -69,6 +79,23 @@ OuterPlan plan_outer(int64_t T, int64_t n, int64_t d) {
     s = (p.Tp + chunk - 1) / chunk;
     p.splits = (int)s;
     p.tchunk = chunk;
+    const int64_t nmt = (n + bm - 1) / bm, nnt = (d + bn - 1) / bn;
+    p.mA = nmt;
+    p.tsplits = 1;
+    p.tchunk_t = p.Tp;
+    if (p.x3 && p.splits == 1 && tiles > kOuterCUs && tiles % kOuterCUs != 0 &&
+        tiles % kOuterCUs <= kOuterCUs / 2) {
+        const int64_t mA = (tiles / kOuterCUs) * kOuterCUs / nnt / 8 * 8;  // whole rounds, whole XCD groups
+        const int64_t tail = (nmt - mA) * nnt;
+        int64_t ts = std::min<int64_t>((kOuterCUs + tail - 1) / tail, (p.Tp + 255) / 256);
+        if (mA > 0 && ts > 1) {
+            int64_t tc = ((p.Tp + ts - 1) / ts + YK - 1) / YK * YK;
+            ts = (p.Tp + tc - 1) / tc;
+            p.mA = mA;
+            p.tsplits = (int)ts;
+            p.tchunk_t = tc;
+        }
+    }
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += (bytes + 255) / 256 * 256; return o; };
     if (p.x3) {
@@ -78,6 +105,7 @@ OuterPlan plan_outer(int64_t T, int64_t n, int64_t d) {
         p.off_bl = take((size_t)p.Np * p.Tp * 2);
     }
     p.off_part = take(p.splits > 1 ? (size_t)p.splits * n * d * sizeof(float) : 0);
+    p.off_tail = take(p.tsplits > 1 ? (size_t)p.tsplits * (n - p.mA * bm) * d * sizeof(float) : 0);
     p.total = off;
     return p;
 }
@@ -255,7 +283,8 @@ __device__ __forceinline__ uint4 tr_frag(const uint16_t* p) {  // p = tile + lan
 __global__ void __launch_bounds__(YNT, 1) outer_x3_kernel(const uint16_t* __restrict__ Ah, const uint16_t* __restrict__ Al,
                                                          const uint16_t* __restrict__ Bh, const uint16_t* __restrict__ Bl,
                                                          int64_t M, int64_t N, int64_t Mp, int64_t Np, int64_t Tp,
-                                                         int64_t tchunk, float* __restrict__ out) {
+                                                         int64_t tchunk, float* __restrict__ out, int64_t mt0,
+                                                         int64_t zs, int64_t orow0) {
     __shared__ __align__(16) uint16_t L0[4 * YK * YT], L1[4 * YK * YT];  // [plane][token][column], 64 KB each
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w & 1, wn = w >> 1;
@@ -265,7 +294,7 @@ __global__ void __launch_bounds__(YNT, 1) outer_x3_kernel(const uint16_t* __rest
     // tiles to all of them instead of each refetching from HBM.
     const int64_t nmt = (M + YT - 1) / YT, nnt = (N + YT - 1) / YT;
     const int64_t b = blockIdx.x, xcd = b % 8, sq = b / 8;
-    const int64_t mt = (sq / nnt) * 8 + xcd, nt = sq % nnt;
+    const int64_t mt = mt0 + (sq / nnt) * 8 + xcd, nt = sq % nnt;  // M-tiles from mt0 on
     if (mt >= nmt) return;
     const int64_t m0 = mt * YT, n0 = nt * YT;
     const int64_t kb0 = (int64_t)blockIdx.z * tchunk;
@@ -368,7 +397,8 @@ __global__ void __launch_bounds__(YNT, 1) outer_x3_kernel(const uint16_t* __rest
         if (kb + YK < ke) kstep(kb + YK, L1, L0, kb + 2 * YK < ke);
     }
 
-    float* o = out + (int64_t)blockIdx.z * M * N;
+    // split z writes plane z (zs floats apart) of rows orow0 on
+    float* o = out + (int64_t)blockIdx.z * zs - orow0 * N;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -432,10 +462,22 @@ hipError_t launch_outer(const float* ghat, const float* x, int64_t T, int64_t n,
         hipLaunchKernelGGL(split_pairs_kernel, dim3((unsigned)((gb + 255) / 256)), dim3(256), 0, stream, x, T, d, p.Tp,
                            p.Np, bh, bl);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        const int64_t nmt8 = ((n + YT - 1) / YT + 7) / 8 * 8;  // M-tiles rounded up to whole XCD groups
-        const dim3 grid((unsigned)(nmt8 * ((d + YT - 1) / YT)), 1, (unsigned)p.splits);
-        hipLaunchKernelGGL(outer_x3_kernel, grid, dim3(YNT), 0, stream, ah, al, bh, bl, n, d, p.Mp, p.Np, p.Tp, p.tchunk,
-                           part);
+        const int64_t nnt = (d + YT - 1) / YT, nmt = (n + YT - 1) / YT;
+        const int64_t nmt8 = (p.mA + 7) / 8 * 8;  // M-tiles rounded up to whole XCD groups
+        const dim3 grid((unsigned)(nmt8 * nnt), 1, (unsigned)p.splits);
+        hipLaunchKernelGGL(outer_x3_kernel, grid, dim3(YNT), 0, stream, ah, al, bh, bl, std::min(n, p.mA * YT), d, p.Mp,
+                           p.Np, p.Tp, p.tchunk, part, (int64_t)0, n * d, (int64_t)0);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (p.mA < nmt) {  // the last round's M-tiles, their tokens split
+            float* tpart = reinterpret_cast<float*>(ws + p.off_tail);
+            const int64_t rows = n - p.mA * YT, tcount = rows * d;
+            const dim3 gt((unsigned)((nmt - p.mA + 7) / 8 * 8 * nnt), 1, (unsigned)p.tsplits);
+            hipLaunchKernelGGL(outer_x3_kernel, gt, dim3(YNT), 0, stream, ah, al, bh, bl, n, d, p.Mp, p.Np, p.Tp,
+                               p.tchunk_t, tpart, p.mA, tcount, p.mA * YT);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((tcount + 255) / 256)), dim3(256), 0, stream, tpart,
+                               p.tsplits, tcount, grad_w + p.mA * YT * d);
+        }
     } else {
         const dim3 grid((unsigned)((n + BM - 1) / BM), (unsigned)((d + BN - 1) / BN), (unsigned)p.splits);
         hipLaunchKernelGGL(outer_f32_kernel, grid, dim3(NTH), 0, stream, ghat, x, T, n, d, p.tchunk, part);
