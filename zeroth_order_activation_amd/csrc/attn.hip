@@ -621,11 +621,41 @@ __global__ void __launch_bounds__(256) attn_csum_kernel(const float* __restrict_
 }
 
 // ---- g_hat_t = -(1/(K sigma)) sum_i r_t^(i) a_t^(i) ------------------------------
+// One workgroup per token.  With fewer than 128 channel quads, the draws are spread over
+// G = 128 / (d / 4) thread groups (group g takes draws g, g + G, ...) and the groups'
+// sums are added in a fixed order through LDS.
 __global__ void __launch_bounds__(128) attn_reduce_kernel(AttnKArgs A, int K, const float* __restrict__ rew,
                                                           float gscale, float* __restrict__ ghat) {
+    __shared__ float4 part[128];
     const int t = blockIdx.x;
     const int nqd = A.d / 4;
     const uint32_t tok = A.tok0 + (uint32_t)t;
+    if (nqd < 128) {
+        const int G = 128 / nqd, g = threadIdx.x / nqd, qd = threadIdx.x % nqd;
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        if (g < G)
+            for (int i = g; i < K; i += G) {
+                const float r = rew[(int64_t)i * A.T + t];
+                const f32x4 gg = gauss4(tok, (uint32_t)qd, A.draw0 + (uint32_t)i, A.layer, A.k0, A.k1);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc[c] = fmaf(r, gg.v[c], acc[c]);
+            }
+        part[threadIdx.x] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        __syncthreads();
+        if (threadIdx.x < nqd) {
+            float4 s4 = part[threadIdx.x];
+            for (int gg = 1; gg < G; ++gg) {
+                const float4 o = part[gg * nqd + threadIdx.x];
+                s4.x += o.x;
+                s4.y += o.y;
+                s4.z += o.z;
+                s4.w += o.w;
+            }
+            *reinterpret_cast<float4*>(ghat + (int64_t)t * A.d + 4 * threadIdx.x) =
+                make_float4(s4.x * gscale, s4.y * gscale, s4.z * gscale, s4.w * gscale);
+        }
+        return;
+    }
     for (int qd = threadIdx.x; qd < nqd; qd += 128) {
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
         for (int i = 0; i < K; ++i) {

@@ -555,24 +555,39 @@ __global__ void __launch_bounds__(256) lm_ce_delta_kernel(const float* __restric
 }
 
 // g_hat[t][c] = scale sum_i rew[i][t] a(t, c, draw0 + i, layer)
+// ghat[t][c] = scale sum_i rew[i][t] a(t, c, i): one workgroup per (token, 32 channel quads);
+// its 8 thread groups take draws g, g + 8, ... and their sums are added in a fixed order
+// through LDS (noise regenerated)
 __global__ void __launch_bounds__(256) lm_ghat_kernel(const float* __restrict__ rew, int K, int T, int w, float scale,
                                                       uint32_t k0, uint32_t k1, uint32_t layer,
                                                       float* __restrict__ ghat) {
-    const int64_t qi = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int nq = w >> 2;
-    if (qi >= (int64_t)T * nq) return;
-    const int t = (int)(qi / nq), cq = (int)(qi % nq);
+    __shared__ float4 part[8][32];
+    const int nq = w >> 2, nch = (nq + 31) / 32;
+    const int t = blockIdx.x / nch, cq = (blockIdx.x % nch) * 32 + (threadIdx.x & 31), g = threadIdx.x >> 5;
     float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-    for (int i = 0; i < K; ++i) {
-        const float r = rew[(int64_t)i * T + t];
-        const f32x4 a = gauss4((uint32_t)t, (uint32_t)cq, (uint32_t)i, layer, k0, k1);
-        s0 = fmaf(r, a.v[0], s0);
-        s1 = fmaf(r, a.v[1], s1);
-        s2 = fmaf(r, a.v[2], s2);
-        s3 = fmaf(r, a.v[3], s3);
+    if (cq < nq)
+        for (int i = g; i < K; i += 8) {
+            const float r = rew[(int64_t)i * T + t];
+            const f32x4 a = gauss4((uint32_t)t, (uint32_t)cq, (uint32_t)i, layer, k0, k1);
+            s0 = fmaf(r, a.v[0], s0);
+            s1 = fmaf(r, a.v[1], s1);
+            s2 = fmaf(r, a.v[2], s2);
+            s3 = fmaf(r, a.v[3], s3);
+        }
+    part[g][threadIdx.x & 31] = make_float4(s0, s1, s2, s3);
+    __syncthreads();
+    if (threadIdx.x < 32 && cq < nq) {
+        float4 v = part[0][threadIdx.x];
+        for (int gg = 1; gg < 8; ++gg) {
+            const float4 o = part[gg][threadIdx.x];
+            v.x += o.x;
+            v.y += o.y;
+            v.z += o.z;
+            v.w += o.w;
+        }
+        *reinterpret_cast<float4*>(ghat + (int64_t)t * w + 4 * cq) =
+            make_float4(v.x * scale, v.y * scale, v.z * scale, v.w * scale);
     }
-    *reinterpret_cast<float4*>(ghat + (int64_t)t * w + 4 * cq) = make_float4(s0 * scale, s1 * scale, s2 * scale,
-                                                                             s3 * scale);
 }
 
 // G_E[v] = sum over tokens equal to v of g_hat: one workgroup per EVB vocabulary rows
@@ -1335,8 +1350,8 @@ hipError_t lm_ce_delta(const float* z, const float* lse, const float* dz, const 
 
 hipError_t lm_ghat(const float* rew, int K, int T, int w, float scale, uint32_t k0, uint32_t k1, uint32_t layer,
                    float* ghat, hipStream_t s) {
-    hipLaunchKernelGGL(lm_ghat_kernel, dim3(blocks((int64_t)T * (w / 4))), dim3(256), 0, s, rew, K, T, w, scale, k0,
-                       k1, layer, ghat);
+    hipLaunchKernelGGL(lm_ghat_kernel, dim3((unsigned)((int64_t)T * ((w / 4 + 31) / 32))), dim3(256), 0, s, rew, K, T, w,
+                       scale, k0, k1, layer, ghat);
     return hipGetLastError();
 }
 
