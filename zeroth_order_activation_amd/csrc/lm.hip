@@ -590,32 +590,44 @@ __global__ void __launch_bounds__(256) lm_ghat_kernel(const float* __restrict__ 
     }
 }
 
-// G_E[v] = sum over tokens equal to v of g_hat: one workgroup per EVB vocabulary rows
-// and 256 channels scans the tokens once, in order, adding the matching rows into
-// LDS (so each sum runs in token order: deterministic); G_P[s] = sum over sequences
-// of g_hat at position s.
-constexpr int EVB = 16;
+// G_E[v] = sum over the tokens t with id v of g_hat[t], in token order (deterministic);
+// G_P[s] = sum over sequences of g_hat at position s.  The embedding gradient takes one
+// workgroup per token t: unless an earlier token has t's id (each wave checks 64 ids per
+// ballot), it walks the ids from t on, 64 per ballot, and adds the matching rows in token
+// order.  Rows no token names keep the zero written before.  Ids outside [0, V) add nothing.
+constexpr int ECH = 4;  // channels per thread: d <= 1024
 
 __global__ void __launch_bounds__(256) lm_embed_grad_kernel(const float* __restrict__ ghat,
                                                             const int32_t* __restrict__ tok, int T, int V, int d,
                                                             float* __restrict__ gemb) {
-    __shared__ float acc[EVB][256];
-    __shared__ int ids[1024];
-    const int v0 = blockIdx.x * EVB, c = blockIdx.y * 256 + threadIdx.x;
+    const int t = blockIdx.x, lane = threadIdx.x & 63;
+    const int id = tok[t];
+    if (id < 0 || id >= V) return;
+    for (int u0 = 0; u0 < t; u0 += 64) {  // the same answer in every wave: the workgroup leaves together
+        const int u = u0 + lane;
+        if (__builtin_amdgcn_ballot_w64(u < t && tok[u] == id)) return;
+    }
+    float acc[ECH];
 #pragma unroll
-    for (int j = 0; j < EVB; ++j) acc[j][threadIdx.x] = 0.f;
-    for (int t0 = 0; t0 < T; t0 += 1024) {  // token ids staged through LDS, 1024 at a time
-        const int nt = min(1024, T - t0);
-        __syncthreads();
-        for (int u = threadIdx.x; u < nt; u += 256) ids[u] = tok[t0 + u] - v0;
-        __syncthreads();
-        for (int u = 0; u < nt; ++u) {
-            const int id = ids[u];  // uniform across the workgroup
-            if (id >= 0 && id < EVB && c < d) acc[id][threadIdx.x] += ghat[(int64_t)(t0 + u) * d + c];
+    for (int k = 0; k < ECH; ++k) acc[k] = 0.f;
+    for (int u0 = t; u0 < T; u0 += 64) {
+        const int u = u0 + lane;
+        uint64_t m = __builtin_amdgcn_ballot_w64(u < T && tok[u] == id);
+        while (m) {  // matches in increasing token order
+            const int64_t row = (int64_t)(u0 + __builtin_ctzll(m)) * d;
+            m &= m - 1;
+#pragma unroll
+            for (int k = 0; k < ECH; ++k) {
+                const int c = threadIdx.x + 256 * k;
+                if (c < d) acc[k] += ghat[row + c];
+            }
         }
     }
-    if (c < d)
-        for (int j = 0; j < EVB && v0 + j < V; ++j) gemb[(int64_t)(v0 + j) * d + c] = acc[j][threadIdx.x];
+#pragma unroll
+    for (int k = 0; k < ECH; ++k) {
+        const int c = threadIdx.x + 256 * k;
+        if (c < d) gemb[(int64_t)id * d + c] = acc[k];
+    }
 }
 
 __global__ void __launch_bounds__(256) lm_pos_grad_kernel(const float* __restrict__ ghat, int T, int S, int d,
@@ -1357,9 +1369,11 @@ hipError_t lm_ghat(const float* rew, int K, int T, int w, float scale, uint32_t 
 
 hipError_t lm_embed_grads(const float* ghat, const int32_t* tok, int T, int S, int V, int d, float* gemb, float* gpos,
                           hipStream_t s) {
-    hipLaunchKernelGGL(lm_embed_grad_kernel, dim3((unsigned)((V + EVB - 1) / EVB), (unsigned)((d + 255) / 256)),
-                       dim3(256), 0, s, ghat, tok, T, V, d, gemb);
-    hipError_t e = hipGetLastError();
+    if (d > 256 * ECH) return hipErrorInvalidValue;
+    hipError_t e = hipMemsetAsync(gemb, 0, (size_t)V * d * sizeof(float), s);  // rows no token names
+    if (e != hipSuccess) return e;
+    if (T > 0) hipLaunchKernelGGL(lm_embed_grad_kernel, dim3((unsigned)T), dim3(256), 0, s, ghat, tok, T, V, d, gemb);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(lm_pos_grad_kernel, dim3(blocks((int64_t)S * d)), dim3(256), 0, s, ghat, T, S, d, gpos);
     return hipGetLastError();
