@@ -621,17 +621,18 @@ __global__ void __launch_bounds__(256) attn_csum_kernel(const float* __restrict_
 }
 
 // ---- g_hat_t = -(1/(K sigma)) sum_i r_t^(i) a_t^(i) ------------------------------
-// One workgroup per token.  With fewer than 128 channel quads, the draws are spread over
-// G = 128 / (d / 4) thread groups (group g takes draws g, g + G, ...) and the groups'
-// sums are added in a fixed order through LDS.
-__global__ void __launch_bounds__(128) attn_reduce_kernel(AttnKArgs A, int K, const float* __restrict__ rew,
+// One workgroup of ART threads per token.  With fewer than ART channel quads, the draws are
+// spread over G = ART / (d / 4) thread groups (group g takes draws g, g + G, ...) and the
+// groups' sums are added in a fixed order through LDS.
+constexpr int ART = 256;
+__global__ void __launch_bounds__(ART) attn_reduce_kernel(AttnKArgs A, int K, const float* __restrict__ rew,
                                                           float gscale, float* __restrict__ ghat) {
-    __shared__ float4 part[128];
+    __shared__ float4 part[ART];
     const int t = blockIdx.x;
     const int nqd = A.d / 4;
     const uint32_t tok = A.tok0 + (uint32_t)t;
-    if (nqd < 128) {
-        const int G = 128 / nqd, g = threadIdx.x / nqd, qd = threadIdx.x % nqd;
+    if (nqd < ART) {
+        const int G = ART / nqd, g = threadIdx.x / nqd, qd = threadIdx.x % nqd;
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
         if (g < G)
             for (int i = g; i < K; i += G) {
@@ -656,7 +657,7 @@ __global__ void __launch_bounds__(128) attn_reduce_kernel(AttnKArgs A, int K, co
         }
         return;
     }
-    for (int qd = threadIdx.x; qd < nqd; qd += 128) {
+    for (int qd = threadIdx.x; qd < nqd; qd += ART) {
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
         for (int i = 0; i < K; ++i) {
             const float r = rew[(int64_t)i * A.T + t];
@@ -769,7 +770,7 @@ hipError_t launch_attn_v_ghat(int64_t T, int64_t d, int64_t K, float sigma, uint
     A.T = (int)T; A.d = (int)d;
     A.k0 = (uint32_t)seed; A.k1 = (uint32_t)(seed >> 32);
     A.layer = layer; A.tok0 = token_offset; A.draw0 = draw_offset;
-    hipLaunchKernelGGL(attn_reduce_kernel, dim3((unsigned)T), dim3(128), 0, stream, A, (int)K, rew,
+    hipLaunchKernelGGL(attn_reduce_kernel, dim3((unsigned)T), dim3(ART), 0, stream, A, (int)K, rew,
                        -1.0f / ((float)K * sigma), ghat);
     return hipGetLastError();
 }
