@@ -933,6 +933,42 @@ __global__ void __launch_bounds__(256) lm_head_reward_kernel(const float* __rest
     if (lane == 0) rew[r] = zy - log1pf(ps);
 }
 
+// The same rewards with 16 lanes per row (4 rows per wave) for d = 64 or 128 and at most 16
+// segments: CPL channels per lane, sums over the lane group by DPP row operations.
+__device__ __forceinline__ float row16_total(float v) {
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));   // quad: lane ^ 1
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));   // quad: lane ^ 2
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));  // half-row mirror
+    return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true));  // row mirror
+}
+
+template <int CPL>
+__global__ void __launch_bounds__(256) lm_head_reward16_kernel(const float* __restrict__ du,
+                                                               const float* __restrict__ whead,
+                                                               const int32_t* __restrict__ labels,
+                                                               const float* __restrict__ part, int T, int V, int nseg,
+                                                               int64_t rows, float* __restrict__ rew) {
+    constexpr int D = 16 * CPL;
+    const int64_t r = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
+    if (r >= rows) return;  // whole 16-lane rows: the DPP sums stay within live rows
+    const int li = threadIdx.x & 15, t = (int)(r % T), y = min(max(labels[t], 0), V - 1);
+    const float* a = du + r * D + CPL * li;
+    const float* w = whead + (int64_t)y * D + CPL * li;
+    float zy = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; c += 4) {
+        const float4 av = *reinterpret_cast<const float4*>(a + c), wv = *reinterpret_cast<const float4*>(w + c);
+        zy = fmaf(av.x, wv.x, zy);
+        zy = fmaf(av.y, wv.y, zy);
+        zy = fmaf(av.z, wv.z, zy);
+        zy = fmaf(av.w, wv.w, zy);
+    }
+    float ps = li < nseg ? part[r * nseg + li] : 0.f;
+    zy = row16_total(zy);
+    ps = row16_total(ps);
+    if (li == 0) rew[r] = zy - log1pf(ps);
+}
+
 // ---- change of the attention output (bf16x3 MFMA) ---------------------------------
 // One workgroup: draw i, sequence b, head h, 64 queries; wave w takes queries 32 (w >> 1)
 // and, of every 64-key tile, keys 32 (w & 1).  Per key tile:
@@ -1404,8 +1440,17 @@ hipError_t lm_head_delta(const float* du, const uint16_t* whi, const uint16_t* w
 
 hipError_t lm_head_reward(const float* du, const float* whead, const int32_t* labels, const float* part, int T, int V,
                           int d, int nseg, int64_t rows, float* rew, hipStream_t s) {
-    hipLaunchKernelGGL(lm_head_reward_kernel, dim3(blocks(rows, 4)), dim3(256), 0, s, du, whead, labels, part, T, V, d,
-                       nseg, rows, rew);
+    if (nseg <= 16 && (d == 64 || d == 128)) {
+        if (d == 64)
+            hipLaunchKernelGGL(lm_head_reward16_kernel<4>, dim3(blocks(rows, 16)), dim3(256), 0, s, du, whead, labels,
+                               part, T, V, nseg, rows, rew);
+        else
+            hipLaunchKernelGGL(lm_head_reward16_kernel<8>, dim3(blocks(rows, 16)), dim3(256), 0, s, du, whead, labels,
+                               part, T, V, nseg, rows, rew);
+    } else {
+        hipLaunchKernelGGL(lm_head_reward_kernel, dim3(blocks(rows, 4)), dim3(256), 0, s, du, whead, labels, part, T, V,
+                           d, nseg, rows, rew);
+    }
     return hipGetLastError();
 }
 
