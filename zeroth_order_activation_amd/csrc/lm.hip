@@ -135,37 +135,40 @@ __global__ void __launch_bounds__(256) lm_layernorm_kernel(const float* __restri
     }
 }
 
-// Causal attention of FQ = 8 queries x one head per workgroup (one wave): the 8 lanes of
-// a query split its keys (lane r takes keys r mod 8) and hold all 64 channels, so a dot
+// Causal attention of FQ = 4 queries x one head per workgroup (one wave): the 16 lanes of
+// a query split its keys (lane r takes keys r mod 16) and hold all 64 channels, so a dot
 // product needs no other lane.  Each lane keeps an online softmax over its keys (running
-// maximum, sum and output) and the 8 lanes merge once at the end.  The key and value tiles
+// maximum, sum and output) and the 16 lanes merge once at the end.  The key and value tiles
 // up to the queries' own 64-key tile are staged in LDS, rows padded to 68 floats so that
-// the 8 lanes of a query read 8 consecutive rows at one column in distinct banks.  The raw
+// the 16 lanes of a query read 16 consecutive rows at one column in distinct banks.  The raw
 // logits go to the probability cache during the pass and become probabilities once the
 // log-sum-exp is known: each lane rewrites the keys it wrote.
-constexpr int FQ = 8;
+constexpr int FQ = 4;   // queries per workgroup
+constexpr int FQL = 16; // lanes per query
 constexpr int FKP = 68;
 
-// over the 8 lanes of an aligned octet: row half-mirror (lane i with 7 - i), then quad xor 1 and 2
-__device__ __forceinline__ float oct_total(float v) {
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));
+// over the 16 lanes of a row: quad xor 1 and 2, then the half-row and row mirrors
+__device__ __forceinline__ float row16_sum(float v) {
     v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
-    return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));
+    return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true));
 }
-__device__ __forceinline__ float oct_max(float v) {
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true)));
+__device__ __forceinline__ float row16_max(float v) {
     v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true)));
-    return fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true)));
+    return fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true)));
 }
 
-__global__ void __launch_bounds__(8 * FQ) lm_attn_fwd_kernel(const float* __restrict__ q, const float* __restrict__ k,
+__global__ void __launch_bounds__(FQL * FQ) lm_attn_fwd_kernel(const float* __restrict__ q, const float* __restrict__ k,
                                                              const float* __restrict__ v, int T, int S, int H,
                                                              float* __restrict__ o, float* __restrict__ lse,
                                                              float* __restrict__ pc) {
     __shared__ __align__(16) float Ks[64][FKP];
     __shared__ __align__(16) float Vs[64][FKP];
     const int nqt = S / FQ, qt = blockIdx.x % nqt, bh = blockIdx.x / nqt, b = bh / H, h = bh % H;
-    const int d = 64 * H, ql = threadIdx.x >> 3, r = threadIdx.x & 7;
+    const int d = 64 * H, ql = threadIdx.x / FQL, r = threadIdx.x % FQL;
     const int query = qt * FQ + ql, q64 = (qt * FQ) / 64;  // the queries' 64-key tile
     const int64_t s0 = (int64_t)b * S, row = s0 + query;
     float qv[64];  // the query scaled by 1/8 (exact)
@@ -191,10 +194,10 @@ __global__ void __launch_bounds__(8 * FQ) lm_attn_fwd_kernel(const float* __rest
             *reinterpret_cast<float4*>(&Vs[rr][c4]) = *reinterpret_cast<const float4*>(v + src);
         }
         __syncthreads();
-        float dl[8], tm = -INFINITY;
+        float dl[64 / FQL], tm = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int j = 8 * i + r, key = kt * 64 + j;
+        for (int i = 0; i < 64 / FQL; ++i) {
+            const int j = FQL * i + r, key = kt * 64 + j;
             float dot = 0.f;
 #pragma unroll
             for (int c4 = 0; c4 < 16; ++c4) {
@@ -214,8 +217,8 @@ __global__ void __launch_bounds__(8 * FQ) lm_attn_fwd_kernel(const float* __rest
         for (int c = 0; c < 64; ++c) acc[c] *= sc;
         m = mn;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int j = 8 * i + r;
+        for (int i = 0; i < 64 / FQL; ++i) {
+            const int j = FQL * i + r;
             const float p = dl[i] > -INFINITY ? __expf(dl[i] - m) : 0.f;
             s += p;
 #pragma unroll
@@ -228,11 +231,11 @@ __global__ void __launch_bounds__(8 * FQ) lm_attn_fwd_kernel(const float* __rest
             }
         }
     }
-    // merge the 8 lanes: lane 0 holds key 0, so the maximum is finite
-    const float M = oct_max(m), sc = __expf(m - M);  // 0 for a lane whose keys were all masked
-    s = oct_total(s * sc);
+    // merge the query's lanes: lane 0 holds key 0, so the maximum is finite
+    const float M = row16_max(m), sc = __expf(m - M);  // 0 for a lane whose keys were all masked
+    s = row16_sum(s * sc);
 #pragma unroll
-    for (int c = 0; c < 64; ++c) acc[c] = oct_total(acc[c] * sc);
+    for (int c = 0; c < 64; ++c) acc[c] = row16_sum(acc[c] * sc);
     const float inv = 1.0f / s, l = M + logf(s);
     if (r == 0) {
 #pragma unroll
@@ -245,8 +248,8 @@ __global__ void __launch_bounds__(8 * FQ) lm_attn_fwd_kernel(const float* __rest
     // pc[((b H + h) S + query) S + key]
     for (int kt = 0; kt <= q64; ++kt)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int key = kt * 64 + 8 * i + r;
+        for (int i = 0; i < 64 / FQL; ++i) {
+            const int key = kt * 64 + FQL * i + r;
             prow[key] = key <= query ? __expf(prow[key] - l) : 0.f;
         }
 }
@@ -1284,7 +1287,7 @@ hipError_t lm_layernorm(const float* x, int64_t R, int d, float eps, float* u, f
 
 hipError_t lm_attn_fwd(const float* q, const float* k, const float* v, int T, int S, int H, float* o, float* lse,
                        float* pc, hipStream_t s) {
-    hipLaunchKernelGGL(lm_attn_fwd_kernel, dim3((unsigned)((T / S) * H * (S / FQ))), dim3(8 * FQ), 0, s, q, k, v, T,
+    hipLaunchKernelGGL(lm_attn_fwd_kernel, dim3((unsigned)((T / S) * H * (S / FQ))), dim3(FQL * FQ), 0, s, q, k, v, T,
                        S, H, o, lse, pc);
     return hipGetLastError();
 }
