@@ -43,6 +43,8 @@ CASES = [
     (50, 192, 3, 1, 64, 64, 2, 3, 2, 1e-2, 0),     # d = 192: the head change by GEMM + loss-change kernel
     (100, 128, 2, 2, 128, 64, 2, 11, 5, 1e-2, 3),  # chunks of 3 draws (11 = 3+3+3+2, 10 members = 3+3+3+1)
     (130, 64, 1, 3, 64, 192, 1, 3, 2, 1e-2, 0),    # three blocks, three query tiles per sequence
+    (60, 256, 4, 1, 64, 64, 1, 2, 1, 1e-2, 0),     # d = 256: the 32-lane LayerNorm-change rows
+    (60, 512, 8, 1, 64, 64, 1, 2, 1, 1e-2, 0),     # d = 512: the 64-lane LayerNorm-change rows
 ]
 
 # the limits the library accepts, one at a time
