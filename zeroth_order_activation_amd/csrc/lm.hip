@@ -499,24 +499,32 @@ __device__ __forceinline__ float expm1_s(float x) {
 // cached Phi(h), phi(h) of the clean pass; the difference of Phi by Simpson's rule on the
 // density for |D_h| < 1/4 (error below |D_h|^5 max|phi''''| / 2880), else by complementary
 // error functions of one sign (no cancellation in either).
+// One thread: entry j of the draws' rows for GDD draws (blockIdx.y GDD on): the cached h,
+// Phi(h), phi(h) of the entry are read once for all of them
+constexpr int GDD = 8;
+
 __global__ void __launch_bounds__(256) lm_gelu_delta_kernel(const float* __restrict__ hc,
                                                             const float* __restrict__ cdf,
                                                             const float* __restrict__ pdf,
                                                             const float* __restrict__ dh, int64_t per_draw,
-                                                            int64_t count, float* __restrict__ dm) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= count) return;
-    const int64_t j = i % per_draw;
-    const float h = hc[j], e = dh[i], h1 = h + e;
-    float dphi;
-    if (fabsf(e) < 0.25f) {
-        dphi = e * (1.0f / 6.0f) * (pdf[j] + 4.0f * phi_pdf(h + 0.5f * e) + phi_pdf(h1));
-    } else if (h + 0.5f * e > 0.f) {  // upper tail: 1 - Phi by erfc
-        dphi = 0.5f * (erfcf(h * 0.70710678118654752f) - erfcf(h1 * 0.70710678118654752f));
-    } else {
-        dphi = 0.5f * (erfcf(-h1 * 0.70710678118654752f) - erfcf(-h * 0.70710678118654752f));
+                                                            int kc, float* __restrict__ dm) {
+    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (j >= per_draw) return;
+    const float h = hc[j], c = cdf[j], q = pdf[j];
+    const int d0 = blockIdx.y * GDD, dn = min(GDD, kc - d0);
+    for (int dd = 0; dd < dn; ++dd) {
+        const int64_t i = (int64_t)(d0 + dd) * per_draw + j;
+        const float e = dh[i], h1 = h + e;
+        float dphi;
+        if (fabsf(e) < 0.25f) {
+            dphi = e * (1.0f / 6.0f) * (q + 4.0f * phi_pdf(h + 0.5f * e) + phi_pdf(h1));
+        } else if (h + 0.5f * e > 0.f) {  // upper tail: 1 - Phi by erfc
+            dphi = 0.5f * (erfcf(h * 0.70710678118654752f) - erfcf(h1 * 0.70710678118654752f));
+        } else {
+            dphi = 0.5f * (erfcf(-h1 * 0.70710678118654752f) - erfcf(-h * 0.70710678118654752f));
+        }
+        dm[i] = fmaf(e, c, (e + h) * dphi);
     }
-    dm[i] = fmaf(e, cdf[j], (e + h) * dphi);
 }
 
 // dx += alpha db, plus for an ES member (es_sigma > 0) the change of the scalar:
@@ -1353,8 +1361,11 @@ hipError_t lm_attn_delta(const float* q, const float* k, const float* v, const f
 
 hipError_t lm_gelu_delta(const float* h, const float* cdf, const float* pdf, const float* dh, int64_t per_draw,
                          int64_t count, float* dm, hipStream_t s) {
-    hipLaunchKernelGGL(lm_gelu_delta_kernel, dim3(blocks(count)), dim3(256), 0, s, h, cdf, pdf, dh, per_draw, count,
-                       dm);
+    if (per_draw <= 0 || count % per_draw != 0) return hipErrorInvalidValue;
+    const int64_t kc = count / per_draw;
+    if (kc == 0) return hipSuccess;
+    hipLaunchKernelGGL(lm_gelu_delta_kernel, dim3(blocks(per_draw), (unsigned)((kc + GDD - 1) / GDD)), dim3(256), 0, s,
+                       h, cdf, pdf, dh, per_draw, (int)kc, dm);
     return hipGetLastError();
 }
 
