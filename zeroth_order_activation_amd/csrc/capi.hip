@@ -689,7 +689,7 @@ hipError_t lm_clean_forward(const LmRun& R) {
     LM_TRY(dust::lm_layernorm(R.f(L.X[D.L]), T, d, D.eps, R.f(L.UF), R.f(L.MUF), R.f(L.RSF), st));
     LM_TRY(dust::lm_gemm_nt(R.f(L.UF), p + R.P.head, R.f(L.Z), T, D.V, d, nullptr, false, st));
     if (L.fused)
-        LM_TRY(dust::lm_split(p + R.P.head, D.V, L.vp, d, reinterpret_cast<uint16_t*>(R.ws + L.HBHI),
+        LM_TRY(dust::lm_split_frag(p + R.P.head, D.V, L.vp, d, reinterpret_cast<uint16_t*>(R.ws + L.HBHI),
                               reinterpret_cast<uint16_t*>(R.ws + L.HBLO), st));
     return dust::lm_ce(R.f(L.Z), R.lab, T, (int)D.V, R.f(L.LSEZ), R.f(L.CE), L.fused ? R.f(L.PP) : nullptr,
                        (int)L.vp, st);

@@ -739,6 +739,29 @@ __global__ void __launch_bounds__(256) lm_split_kernel(const float* __restrict__
     lo[i] = bf16_pair(a - __uint_as_float(h << 16), b - __uint_as_float(h & 0xFFFF0000u));
 }
 
+// hi/lo bf16 parts of W [rows, K] in MFMA fragment order: 16-byte unit u = ((vb KS + ks) 64 + lane)
+// (KS = K / 16) holds channels 16 ks + 8 (lane >> 5) + [0, 8) of row 32 vb + (lane & 31), so a
+// wave's fragment load of one 32-row block and channel step reads 1 KB contiguous; rows past
+// `rows` are zero
+__global__ void __launch_bounds__(256) lm_split_frag_kernel(const float* __restrict__ W, int64_t rows, int64_t rows_p,
+                                                            int K, uint4* __restrict__ hi, uint4* __restrict__ lo) {
+    const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int KS = K / 16;
+    if (u >= rows_p * K / 8) return;
+    const int lane = (int)(u & 63), ks = (int)((u >> 6) % KS);
+    const int64_t vb = (u >> 6) / KS, row = vb * 32 + (lane & 31);
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+    if (row < rows) {
+        const float* src = W + row * K + 16 * ks + 8 * (lane >> 5);
+        a = *reinterpret_cast<const float4*>(src);
+        b = *reinterpret_cast<const float4*>(src + 4);
+    }
+    uint4 h, l;
+    split8(a, b, h, l);
+    hi[u] = h;
+    lo[u] = l;
+}
+
 // expm1 of 16 values: the degree-6 Taylor polynomial (relative truncation below 5e-8
 // for |x| < 1/4); waves holding a larger |x| take exp(x) - 1 for those values.
 __device__ __forceinline__ void expm1_x16(float (&x)[16]) {
@@ -838,12 +861,13 @@ __global__ void __launch_bounds__(64 * HW) lm_head_delta_kernel(const float* __r
     const int vb = sg * vseg, ve = min(Vp, vb + vseg);
     for (int v0 = vb + 32 * w; v0 < ve; v0 += 32 * HW) {
         uint4 ahi[KS], alo[KS];  // W_head rows v0 + (lane & 31), channels 16 ks + 8 hf + [0, 8)
-        const uint16_t* bh = whi + (int64_t)(v0 + (lane & 31)) * D + 8 * hf;
-        const uint16_t* bl = wlo + (int64_t)(v0 + (lane & 31)) * D + 8 * hf;
+        // the parts are stored in fragment order: unit ((v0 / 32) KS + ks) 64 + lane
+        const uint4* bh = reinterpret_cast<const uint4*>(whi) + (int64_t)(v0 / 32) * KS * 64 + lane;
+        const uint4* bl = reinterpret_cast<const uint4*>(wlo) + (int64_t)(v0 / 32) * KS * 64 + lane;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            ahi[ks] = *reinterpret_cast<const uint4*>(bh + 16 * ks);
-            alo[ks] = *reinterpret_cast<const uint4*>(bl + 16 * ks);
+            ahi[ks] = bh[ks * 64];
+            alo[ks] = bl[ks * 64];
         }
         float pv[2][16];  // p of this lane's token (column) at the 16 vocabulary rows it holds, per token half
 #pragma unroll
@@ -1429,6 +1453,14 @@ hipError_t lm_embed_grads(const float* ghat, const int32_t* tok, int T, int S, i
     return hipGetLastError();
 }
 
+hipError_t lm_split_frag(const float* W, int64_t rows, int64_t rows_p, int K, uint16_t* hi, uint16_t* lo,
+                        hipStream_t s) {
+    if (K % 16 != 0 || rows_p % 32 != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(lm_split_frag_kernel, dim3(blocks(rows_p * K / 8)), dim3(256), 0, s, W, rows, rows_p, K,
+                       reinterpret_cast<uint4*>(hi), reinterpret_cast<uint4*>(lo));
+    return hipGetLastError();
+}
+
 hipError_t lm_split(const float* W, int64_t rows, int64_t rows_p, int K, uint16_t* hi, uint16_t* lo, hipStream_t s) {
     hipLaunchKernelGGL(lm_split_kernel, dim3(blocks(rows_p * K / 2)), dim3(256), 0, s, W, rows, rows_p, K,
                        reinterpret_cast<uint32_t*>(hi), reinterpret_cast<uint32_t*>(lo));
@@ -1437,6 +1469,8 @@ hipError_t lm_split(const float* W, int64_t rows, int64_t rows_p, int K, uint16_
 
 hipError_t lm_head_delta(const float* du, const uint16_t* whi, const uint16_t* wlo, const float* prob, int d, int kc,
                          int T, int Vp, int vseg, int nseg, float* part, hipStream_t s) {
+    // W_head's parts are in fragment order over whole 32-row blocks
+    if (T % 64 != 0 || Vp % 32 != 0 || vseg % 32 != 0) return hipErrorInvalidValue;
     const int64_t npairs = (int64_t)(T / 64) * nseg, ngr = (kc + HDG - 1) / HDG;
     const dim3 grid((unsigned)(8 * ngr * ((npairs + 7) / 8)));
     bool timed;

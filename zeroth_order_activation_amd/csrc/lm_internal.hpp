@@ -33,6 +33,9 @@ hipError_t lm_ce(const float* z, const int32_t* labels, int T, int V, float* lse
 hipError_t lm_gemm_x3(const float* A, const uint16_t* Bh, const uint16_t* Bl, float* C, int64_t M, int64_t N,
                       int64_t K, hipStream_t s, int64_t pw = 0, int64_t ps = 0);
 hipError_t lm_split(const float* W, int64_t rows, int64_t rows_p, int K, uint16_t* hi, uint16_t* lo, hipStream_t s);
+// the same parts in MFMA fragment order (16-byte unit ((row / 32) (K / 16) + k / 16) 64 + lane), for the head change
+hipError_t lm_split_frag(const float* W, int64_t rows, int64_t rows_p, int K, uint16_t* hi, uint16_t* lo,
+                        hipStream_t s);
 hipError_t lm_head_delta(const float* du, const uint16_t* whi, const uint16_t* wlo, const float* prob, int d, int kc,
                          int T, int Vp, int vseg, int nseg, float* part, hipStream_t s);
 hipError_t lm_head_reward(const float* du, const float* whead, const int32_t* labels, const float* part, int T, int V,
