@@ -1203,16 +1203,23 @@ __global__ void __launch_bounds__(256) lm_attn_delta_kernel(const float* __restr
 }
 
 // ---- change rows times a weight on bf16x3 MFMA: C = A B^T ----------------------------
-// A [M, K] fp32 (change rows, split into bf16 parts as they are read), B [N, K] given as
-// bf16 parts Bh, Bl (the weight split once per step).  Workgroup tile 128 rows x 128
-// columns, 4 waves of 64 x 64 (2 x 2 MFMA blocks); B's parts go through LDS in chunks
-// of 64 channels, A's fragments come from global memory.  M % 128 == 0 or the rows past
-// M are not stored; columns past N read zero weights and are not stored; K % XK == 0.
+// A [M, K] fp32 (change rows), B [N, K] given as bf16 parts Bh, Bl (the weight split once
+// per step).  Workgroup tile 128 rows x 128 columns, 4 waves of 64 x 64 (2 x 2 MFMA
+// blocks), over chunks of XK channels.  A chunk's rows are read whole (8 lanes per 128-byte
+// row piece), split into bf16 parts once and staged in LDS beside B's parts; the next
+// chunk's loads are in flight while this chunk's MFMAs run.  Rows past M are read clamped
+// and not stored; columns past N read zero weights and are not stored; K % XK == 0.
 constexpr int XT = 128, XK = 32;
+
+// LDS slot of 8-channel piece p of A row `row`: any 8 consecutive rows reading one piece hit
+// distinct 16-byte bank groups (rows are 64 bytes, 4 pieces)
+__device__ __forceinline__ int x3_slot(int row, int p) { return p ^ ((row >> 1) & 3); }
 
 __global__ void __launch_bounds__(256) lm_gemm_x3_kernel(const float* __restrict__ A, const uint16_t* __restrict__ Bh,
                                                          const uint16_t* __restrict__ Bl, float* __restrict__ C,
                                                          int M, int N, int K, int pw, int64_t ps) {
+    __shared__ __align__(16) uint4 AH[XT][XK / 8];      // [row][slot]
+    __shared__ __align__(16) uint4 AL[XT][XK / 8];
     __shared__ __align__(16) uint4 SH[XT][XK / 8 + 1];  // [column][8-channel piece], padded
     __shared__ __align__(16) uint4 SL[XT][XK / 8 + 1];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w & 1, wn = w >> 1, hf = lane >> 5;
@@ -1224,43 +1231,66 @@ __global__ void __launch_bounds__(256) lm_gemm_x3_kernel(const float* __restrict
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = hf32x16{};
-    // this lane's A rows (clamped to M - 1: rows past M are computed but never stored)
-    const float* arow[2];
+    // staging roles: A rows (threadIdx >> 3) + 32 u, channels 4 aq + [0, 4) of the chunk;
+    // B units f = threadIdx + 256 u: column f / 4, piece f % 4
+    constexpr int AU = XT * XK / 4 / 256, BU = XT * (XK / 8) / 256;
+    const int aq = threadIdx.x & 7;
+    const float* asrc[AU];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int64_t r = min(m0 + 64 * wm + 32 * i + (lane & 31), (int64_t)M - 1);
-        arow[i] = A + r * K + 8 * hf;
+    for (int u = 0; u < AU; ++u) {
+        const int64_t r = min(m0 + (threadIdx.x >> 3) + 32 * u, (int64_t)M - 1);
+        asrc[u] = A + r * K + 4 * aq;
     }
-    for (int k0 = 0; k0 < K; k0 += XK) {
-        // this chunk's A values, in flight while the weight parts are staged
-        float4 av[2][XK / 16][2];
+    float4 ar[AU];
+    uint4 bhr[BU], blr[BU];
+    auto load = [&](int k0) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int u = 0; u < AU; ++u) ar[u] = *reinterpret_cast<const float4*>(asrc[u] + k0);
 #pragma unroll
-            for (int ks = 0; ks < XK / 16; ++ks) {
-                av[i][ks][0] = *reinterpret_cast<const float4*>(arow[i] + k0 + 16 * ks);
-                av[i][ks][1] = *reinterpret_cast<const float4*>(arow[i] + k0 + 16 * ks + 4);
-            }
-        __syncthreads();  // the previous chunk's weight parts are used up
-        // 128 columns x XK / 8 pieces of 8 channels, hi and lo
-#pragma unroll
-        for (int u = 0; u < XT * (XK / 8) / 256; ++u) {
-            const int f = threadIdx.x + 256 * u, col = f / (XK / 8), pc = f % (XK / 8);
-            const int64_t n = n0 + col;
-            uint4 h = make_uint4(0u, 0u, 0u, 0u), l = h;
+        for (int u = 0; u < BU; ++u) {
+            const int f = threadIdx.x + 256 * u;
+            const int64_t n = n0 + f / (XK / 8);
+            bhr[u] = blr[u] = make_uint4(0u, 0u, 0u, 0u);
             if (n < N) {
-                h = *reinterpret_cast<const uint4*>(Bh + n * K + k0 + 8 * pc);
-                l = *reinterpret_cast<const uint4*>(Bl + n * K + k0 + 8 * pc);
+                bhr[u] = *reinterpret_cast<const uint4*>(Bh + n * K + k0 + 8 * (f % (XK / 8)));
+                blr[u] = *reinterpret_cast<const uint4*>(Bl + n * K + k0 + 8 * (f % (XK / 8)));
             }
-            SH[col][pc] = h;
-            SL[col][pc] = l;
         }
-        __syncthreads();
+    };
+    auto store = [&]() {
+#pragma unroll
+        for (int u = 0; u < AU; ++u) {
+            const int row = (threadIdx.x >> 3) + 32 * u;
+            const float x[4] = {ar[u].x, ar[u].y, ar[u].z, ar[u].w};
+            const uint32_t h0 = bf16_pair(x[0], x[1]), h1 = bf16_pair(x[2], x[3]);
+            const uint32_t l0 = bf16_pair(x[0] - __uint_as_float(h0 << 16), x[1] - __uint_as_float(h0 & 0xFFFF0000u));
+            const uint32_t l1 = bf16_pair(x[2] - __uint_as_float(h1 << 16), x[3] - __uint_as_float(h1 & 0xFFFF0000u));
+            const int sl = x3_slot(row, aq >> 1), half = aq & 1;
+            reinterpret_cast<uint2*>(&AH[row][sl])[half] = make_uint2(h0, h1);
+            reinterpret_cast<uint2*>(&AL[row][sl])[half] = make_uint2(l0, l1);
+        }
+#pragma unroll
+        for (int u = 0; u < BU; ++u) {
+            const int f = threadIdx.x + 256 * u;
+            SH[f / (XK / 8)][f % (XK / 8)] = bhr[u];
+            SL[f / (XK / 8)][f % (XK / 8)] = blr[u];
+        }
+    };
+    load(0);
+    store();
+    __syncthreads();
+    for (int k0 = 0; k0 < K; k0 += XK) {
+        const bool more = k0 + XK < K;
+        if (more) load(k0 + XK);  // in flight during this chunk's MFMAs
 #pragma unroll
         for (int ks = 0; ks < XK / 16; ++ks) {
             uint4 ah[2], al[2], bh[2], bl[2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) split8(av[i][ks][0], av[i][ks][1], ah[i], al[i]);
+            for (int i = 0; i < 2; ++i) {
+                const int row = 64 * wm + 32 * i + (lane & 31), sl = x3_slot(row, 2 * ks + hf);
+                ah[i] = AH[row][sl];
+                al[i] = AL[row][sl];
+            }
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int col = 64 * wn + 32 * j + (lane & 31);
@@ -1275,6 +1305,11 @@ __global__ void __launch_bounds__(256) lm_gemm_x3_kernel(const float* __restrict
                     acc[i][j] = mfma_bf16(ah[i], bl[j], acc[i][j]);
                     acc[i][j] = mfma_bf16(ah[i], bh[j], acc[i][j]);
                 }
+        }
+        if (more) {
+            __syncthreads();  // this chunk's parts are used up
+            store();
+            __syncthreads();
         }
     }
     // D[row][col]: lane holds column lane & 31 and rows (r & 3) + 8 (r >> 2) + 4 hf; column
