@@ -1215,7 +1215,7 @@ constexpr int XT = 128, XK = 32;
 // distinct 16-byte bank groups (rows are 64 bytes, 4 pieces)
 __device__ __forceinline__ int x3_slot(int row, int p) { return p ^ ((row >> 1) & 3); }
 
-__global__ void __launch_bounds__(256) lm_gemm_x3_kernel(const float* __restrict__ A, const uint16_t* __restrict__ Bh,
+__global__ void __launch_bounds__(256, 3) lm_gemm_x3_kernel(const float* __restrict__ A, const uint16_t* __restrict__ Bh,
                                                          const uint16_t* __restrict__ Bl, float* __restrict__ C,
                                                          int M, int N, int K, int pw, int64_t ps) {
     __shared__ __align__(16) uint4 AH[XT][XK / 8];      // [row][slot]
