@@ -503,27 +503,43 @@ __device__ __forceinline__ float expm1_s(float x) {
 // Phi(h), phi(h) of the entry are read once for all of them
 constexpr int GDD = 8;
 
-__global__ void __launch_bounds__(256) lm_gelu_delta_kernel(const float* __restrict__ hc,
-                                                            const float* __restrict__ cdf,
-                                                            const float* __restrict__ pdf,
-                                                            const float* __restrict__ dh, int64_t per_draw,
-                                                            int kc, float* __restrict__ dm) {
+__device__ __forceinline__ float gelu_change(float h, float c, float q, float e) {
+    const float h1 = h + e;
+    float dphi;
+    if (fabsf(e) < 0.25f) {
+        dphi = e * (1.0f / 6.0f) * (q + 4.0f * phi_pdf(h + 0.5f * e) + phi_pdf(h1));
+    } else if (h + 0.5f * e > 0.f) {  // upper tail: 1 - Phi by erfc
+        dphi = 0.5f * (erfcf(h * 0.70710678118654752f) - erfcf(h1 * 0.70710678118654752f));
+    } else {
+        dphi = 0.5f * (erfcf(-h1 * 0.70710678118654752f) - erfcf(-h * 0.70710678118654752f));
+    }
+    return fmaf(e, c, (e + h) * dphi);
+}
+
+// Four consecutive entries per thread (per_draw % 4 == 0), their cached h, Phi(h), phi(h)
+// read once for GDD draws, every draw's change loaded before any is computed.
+__global__ void __launch_bounds__(256) lm_gelu_delta_kernel(const float4* __restrict__ hc,
+                                                            const float4* __restrict__ cdf,
+                                                            const float4* __restrict__ pdf,
+                                                            const float4* __restrict__ dh, int64_t per_draw4,
+                                                            int kc, float4* __restrict__ dm) {
     const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (j >= per_draw) return;
-    const float h = hc[j], c = cdf[j], q = pdf[j];
+    if (j >= per_draw4) return;
     const int d0 = blockIdx.y * GDD, dn = min(GDD, kc - d0);
-    for (int dd = 0; dd < dn; ++dd) {
-        const int64_t i = (int64_t)(d0 + dd) * per_draw + j;
-        const float e = dh[i], h1 = h + e;
-        float dphi;
-        if (fabsf(e) < 0.25f) {
-            dphi = e * (1.0f / 6.0f) * (q + 4.0f * phi_pdf(h + 0.5f * e) + phi_pdf(h1));
-        } else if (h + 0.5f * e > 0.f) {  // upper tail: 1 - Phi by erfc
-            dphi = 0.5f * (erfcf(h * 0.70710678118654752f) - erfcf(h1 * 0.70710678118654752f));
-        } else {
-            dphi = 0.5f * (erfcf(-h1 * 0.70710678118654752f) - erfcf(-h * 0.70710678118654752f));
-        }
-        dm[i] = fmaf(e, c, (e + h) * dphi);
+    float4 e[GDD];
+#pragma unroll
+    for (int dd = 0; dd < GDD; ++dd)
+        if (dd < dn) e[dd] = dh[(int64_t)(d0 + dd) * per_draw4 + j];
+    const float4 h = hc[j], c = cdf[j], q = pdf[j];
+#pragma unroll
+    for (int dd = 0; dd < GDD; ++dd) {
+        if (dd >= dn) break;
+        float4 r;
+        r.x = gelu_change(h.x, c.x, q.x, e[dd].x);
+        r.y = gelu_change(h.y, c.y, q.y, e[dd].y);
+        r.z = gelu_change(h.z, c.z, q.z, e[dd].z);
+        r.w = gelu_change(h.w, c.w, q.w, e[dd].w);
+        dm[(int64_t)(d0 + dd) * per_draw4 + j] = r;
     }
 }
 
@@ -1420,11 +1436,13 @@ hipError_t lm_attn_delta(const float* q, const float* k, const float* v, const f
 
 hipError_t lm_gelu_delta(const float* h, const float* cdf, const float* pdf, const float* dh, int64_t per_draw,
                          int64_t count, float* dm, hipStream_t s) {
-    if (per_draw <= 0 || count % per_draw != 0) return hipErrorInvalidValue;
+    if (per_draw <= 0 || per_draw % 4 != 0 || count % per_draw != 0) return hipErrorInvalidValue;
     const int64_t kc = count / per_draw;
     if (kc == 0) return hipSuccess;
-    hipLaunchKernelGGL(lm_gelu_delta_kernel, dim3(blocks(per_draw), (unsigned)((kc + GDD - 1) / GDD)), dim3(256), 0, s,
-                       h, cdf, pdf, dh, per_draw, (int)kc, dm);
+    hipLaunchKernelGGL(lm_gelu_delta_kernel, dim3(blocks(per_draw / 4), (unsigned)((kc + GDD - 1) / GDD)), dim3(256), 0,
+                       s, reinterpret_cast<const float4*>(h), reinterpret_cast<const float4*>(cdf),
+                       reinterpret_cast<const float4*>(pdf), reinterpret_cast<const float4*>(dh), per_draw / 4, (int)kc,
+                       reinterpret_cast<float4*>(dm));
     return hipGetLastError();
 }
 
