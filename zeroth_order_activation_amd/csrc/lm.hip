@@ -444,6 +444,10 @@ __global__ void __launch_bounds__(256) lm_residual_ln_delta8_kernel(float* __res
     const float* bp = db + row * D + 8 * li;
     const float4 d0 = *reinterpret_cast<const float4*>(dp), d1 = *reinterpret_cast<const float4*>(dp + 4);
     const float4 y0 = *reinterpret_cast<const float4*>(bp), y1 = *reinterpret_cast<const float4*>(bp + 4);
+    // the token's cached LayerNorm input and statistics, in flight with the change rows
+    const float mm = mu[t], r = rs[t];
+    const float* xp = x + (int64_t)t * D + 8 * li;
+    const float4 x0 = *reinterpret_cast<const float4*>(xp), x1 = *reinterpret_cast<const float4*>(xp + 4);
     const float y[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
     float c[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
 #pragma unroll
@@ -461,9 +465,6 @@ __global__ void __launch_bounds__(256) lm_residual_ln_delta8_kernel(float* __res
     *reinterpret_cast<float4*>(dp) = make_float4(c[0], c[1], c[2], c[3]);
     *reinterpret_cast<float4*>(dp + 4) = make_float4(c[4], c[5], c[6], c[7]);
     // the LayerNorm change of the updated row
-    const float mm = mu[t], r = rs[t];
-    const float* xp = x + (int64_t)t * D + 8 * li;
-    const float4 x0 = *reinterpret_cast<const float4*>(xp), x1 = *reinterpret_cast<const float4*>(xp + 4);
     const float xc[8] = {x0.x - mm, x0.y - mm, x0.z - mm, x0.w - mm, x1.x - mm, x1.y - mm, x1.z - mm, x1.w - mm};
     float s = 0.f;
 #pragma unroll
