@@ -1092,10 +1092,12 @@ __global__ void __launch_bounds__(256) lm_attn_delta_kernel(const float* __restr
     const float* prow = pc + ((int64_t)bh * S + query) * S;
     for (int kt = 0; kt <= qt; ++kt) {
         __syncthreads();  // the previous tile's transposed values are used up
-        // v and D_v of the 64 keys, transposed into bf16 parts: unit = 2 keys x 4 channels
+        // v and D_v of the 64 keys, transposed into bf16 parts: unit = 2 keys x 4 channels.
+        // A wave takes 8 key pairs x 8 channel quads (each row read is one 128-byte line), so
+        // its transposed 4-byte writes land on 32 distinct banks per half-wave
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int f = threadIdx.x + 256 * u, kp = f >> 4, c4 = (f & 15) * 4;
+            const int f = threadIdx.x + 256 * u, kp = (f >> 3) & 31, c4 = ((f & 7) + 8 * (f >> 8)) * 4;
             const int64_t r0 = s0 + kt * 64 + 2 * kp;
             const float4 va = *reinterpret_cast<const float4*>(v + r0 * d + h * 64 + c4);
             const float4 vb = *reinterpret_cast<const float4*>(v + (r0 + 1) * d + h * 64 + c4);
