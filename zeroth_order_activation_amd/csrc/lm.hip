@@ -625,15 +625,24 @@ __global__ void __launch_bounds__(256) lm_ghat_kernel(const float* __restrict__ 
 // order.  Rows no token names keep the zero written before.  Ids outside [0, V) add nothing.
 constexpr int ECH = 4;  // channels per thread: d <= 1024
 
+constexpr int EMB_G = 8;  // matching rows gathered per load wait in the embedding gradient
+
 __global__ void __launch_bounds__(256) lm_embed_grad_kernel(const float* __restrict__ ghat,
                                                             const int32_t* __restrict__ tok, int T, int V, int d,
                                                             float* __restrict__ gemb) {
     const int t = blockIdx.x, lane = threadIdx.x & 63;
     const int id = tok[t];
     if (id < 0 || id >= V) return;
-    for (int u0 = 0; u0 < t; u0 += 64) {  // the same answer in every wave: the workgroup leaves together
-        const int u = u0 + lane;
-        if (__builtin_amdgcn_ballot_w64(u < t && tok[u] == id)) return;
+    // an earlier token with this id owns the row; 4 chunks of 64 tokens per load wait (the
+    // same answer in every wave: the workgroup leaves together)
+    for (int u0 = 0; u0 < t; u0 += 256) {
+        bool seen = false;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int u = u0 + 64 * q + lane;
+            seen |= u < t && tok[u] == id;
+        }
+        if (__builtin_amdgcn_ballot_w64(seen)) return;
     }
     float acc[ECH];
 #pragma unroll
@@ -641,14 +650,30 @@ __global__ void __launch_bounds__(256) lm_embed_grad_kernel(const float* __restr
     for (int u0 = t; u0 < T; u0 += 64) {
         const int u = u0 + lane;
         uint64_t m = __builtin_amdgcn_ballot_w64(u < T && tok[u] == id);
-        while (m) {  // matches in increasing token order
-            const int64_t row = (int64_t)(u0 + __builtin_ctzll(m)) * d;
-            m &= m - 1;
+        while (m) {  // matches in increasing token order, up to EMB_G rows loaded per wait
+            int rows[EMB_G];
+            int nr = 0;
 #pragma unroll
-            for (int k = 0; k < ECH; ++k) {
-                const int c = threadIdx.x + 256 * k;
-                if (c < d) acc[k] += ghat[row + c];
+            for (int j = 0; j < EMB_G; ++j) {
+                rows[j] = m ? u0 + __builtin_ctzll(m) : -1;
+                if (m) {
+                    m &= m - 1;
+                    ++nr;
+                }
             }
+            float v[EMB_G][ECH];
+#pragma unroll
+            for (int j = 0; j < EMB_G; ++j)
+#pragma unroll
+                for (int k = 0; k < ECH; ++k) {
+                    const int c = threadIdx.x + 256 * k;
+                    v[j][k] = (j < nr && c < d) ? ghat[(int64_t)rows[j] * d + c] : 0.f;
+                }
+#pragma unroll
+            for (int j = 0; j < EMB_G; ++j)
+#pragma unroll
+                for (int k = 0; k < ECH; ++k)
+                    if (j < nr) acc[k] += v[j][k];
         }
     }
 #pragma unroll
