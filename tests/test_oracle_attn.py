@@ -143,3 +143,52 @@ def test_query_and_key_estimates_are_unbiased():
         slope = float((g * ga).sum() / (ga * ga).sum())
         print(f"{proj}: slope on the autograd gradient {slope:.3f}, cosine {oracle.cosine(g, ga):.3f}")
         assert abs(slope - 1.0) < 0.08
+
+
+def _token_subset(B, S, rng, extra):
+    """First, a middle and the last token of every sequence, plus ``extra`` random ones."""
+    toks = set()
+    for b in range(B):
+        toks.update({b * S, b * S + S // 2, b * S + S - 1})
+    toks.update(int(t) for t in rng.choice(B * S, extra, replace=False))
+    return sorted(toks)
+
+
+def test_token_subset_checker_equals_the_full_estimator():
+    # attn_estimate_tokens recomputes only the attention rows a token's reward needs;
+    # row for row it must give attn_estimate's rewards and estimates, for each
+    # projection, on tokens at both ends and inside each sequence (an off-by-one in
+    # the span of later queries, or a wrong causal slice, breaks the first or last).
+    B, S, H, dh = 3, 6, 2, 4
+    q, k, v, e = _inputs(B, S, H, dh, 10)
+    K, sigma, t0, d0 = 3, 4e-2, 5, 2
+    toks = _token_subset(B, S, np.random.default_rng(0), 3)
+    for proj in ("q", "k", "v"):
+        g, rew = oracle.attn_estimate(proj, q, k, v, e, S, H, K, sigma, SEED, 6, token_offset=t0, draw_offset=d0)
+        gs, rs = oracle.attn_estimate_tokens(proj, q, k, v, e, S, H, K, sigma, SEED, 6, toks,
+                                             token_offset=t0, draw_offset=d0)
+        np.testing.assert_allclose(rs, rew[:, toks], rtol=1e-10, atol=1e-14)
+        np.testing.assert_allclose(gs, g[toks], rtol=1e-10, atol=1e-14)
+
+
+def test_token_subset_checker_against_torch_attention():
+    # The same subset checker against rewards formed directly from torch's causal
+    # attention on the perturbed projection: keys and values sum the output change
+    # over the token's own and every later query of its sequence, queries take their own.
+    B, S, H, dh = 2, 7, 3, 4
+    q, k, v, e = _inputs(B, S, H, dh, 11)
+    K, sigma, t0, d0 = 2, 3e-2, 0, 4
+    toks = _token_subset(B, S, np.random.default_rng(1), 2)
+    a = oracle.noise_block(SEED, 7, d0, K, t0, B * S, H * dh)
+    o = _torch_attn(q, k, v, B, S, H).numpy()
+    for proj in ("q", "k", "v"):
+        _, rs = oracle.attn_estimate_tokens(proj, q, k, v, e, S, H, K, sigma, SEED, 7, toks,
+                                            token_offset=t0, draw_offset=d0)
+        for i in range(K):
+            pert = [q, k, v]
+            pert["qkv".index(proj)] = pert["qkv".index(proj)] + sigma * a[i]
+            c = np.sum(e * (_torch_attn(*pert, B, S, H).numpy() - o), axis=1)
+            for j, t in enumerate(toks):
+                end = (t // S + 1) * S
+                ref = -c[t] if proj == "q" else -c[t:end].sum()
+                assert abs(rs[i, j] - ref) <= 1e-9 * max(1.0, abs(ref)), (proj, i, t, rs[i, j], ref)

@@ -100,3 +100,52 @@ def test_additivity_and_token_sampling():
     gs, rs, _ = oracle.linear_estimate(*args, K, 1e-2, EPS, SEED, 0, tokens=[5, 1])
     np.testing.assert_allclose(gs, g[[5, 1]], rtol=1e-13, atol=1e-13)
     np.testing.assert_allclose(rs, r[:, [5, 1]], rtol=1e-13, atol=1e-15)
+
+
+def _torch_quantized_ce(htilde64, x, labels, w2, wh, eps):
+    """The bf16 downstream written with torch: GELU in fp64, its output cast to fp32 and
+    then to bf16; W2 product and residual in fp64; LayerNorm in fp64, its output cast
+    to fp32 and then to bf16; head product and cross-entropy in fp64."""
+    bf = torch.bfloat16
+    m = F.gelu(torch.from_numpy(htilde64)).to(torch.float32).to(bf).to(torch.float64)
+    yv = torch.from_numpy(x.astype(np.float64)) + m @ torch.from_numpy(w2).T
+    f = F.layer_norm(yv, (yv.shape[1],), eps=eps).to(torch.float32).to(bf).to(torch.float64)
+    z = f @ torch.from_numpy(wh).T
+    return F.cross_entropy(z, torch.from_numpy(labels).long(), reduction="none").numpy()
+
+
+def test_bf16_rounding_points_match_explicit_torch_casts():
+    # The rounding points of the quantised downstream: the GELU output and the
+    # LayerNorm output, each taken to fp32 and then to bf16 (round to nearest even).
+    # Rounding h~ instead of GELU(h~), or rounding before the LayerNorm, moves the
+    # losses by about a bf16 step (1e-3 relative), far above this test's 1e-12.
+    c = _case(T=24, d=32, n=128, V=64, seed=7)
+    w2, wh = _w(c)
+    rng = np.random.default_rng(8)
+    h = c["h"].astype(np.float64) + 0.3 * rng.standard_normal(c["h"].shape)
+    ce = oracle.mlp_downstream_ce(h, c["x_res"].astype(np.float64), c["labels"], w2, wh, EPS, quantize=True)
+    ref = _torch_quantized_ce(h, c["x_res"], c["labels"], w2, wh, EPS)
+    np.testing.assert_allclose(ce, ref, rtol=1e-12, atol=1e-12)
+    # and the rounding matters at this size: the unrounded loss differs
+    ce_exact = oracle.mlp_downstream_ce(h, c["x_res"].astype(np.float64), c["labels"], w2, wh, EPS, quantize=False)
+    assert np.abs(ce_exact - ref).max() > 1e-6
+
+
+def test_quantised_rewards_are_torch_loss_differences():
+    # Every reward of the quantised estimator: the clean row through the bf16 downstream
+    # minus the perturbed row, h~ = h + sigma a rounded to fp32 first (an fp32 tensor,
+    # like the cached h), both written with torch's casts.
+    c = _case(T=5, d=16, n=64, V=40, seed=9)
+    w2, wh = _w(c)
+    K, sigma, t0, d0 = 4, 2e-2, 3, 6
+    g, rew, ce0 = oracle.linear_estimate(c["h"], c["x_res"], c["w2_bf16"], c["w_head_bf16"], c["labels"], K, sigma,
+                                         EPS, SEED, 0, token_offset=t0, draw_offset=d0)
+    a = oracle.noise_block(SEED, 0, d0, K, t0, 5, 64)
+    h = c["h"].astype(np.float64)
+    clean = _torch_quantized_ce(h, c["x_res"], c["labels"], w2, wh, EPS)
+    np.testing.assert_allclose(ce0, clean, rtol=1e-12, atol=1e-12)
+    for i in range(K):
+        ht = (h + sigma * a[i]).astype(np.float32).astype(np.float64)
+        r = clean - _torch_quantized_ce(ht, c["x_res"], c["labels"], w2, wh, EPS)
+        np.testing.assert_allclose(rew[i], r, rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(g, -np.einsum("kt,ktn->tn", rew, a) / (K * sigma), rtol=1e-12, atol=1e-14)
