@@ -13,8 +13,11 @@ synthetic inputs already resident in HBM:
   * MLP-linear workloads (3, 5): GEMM1 with the noise/GELU prologue and the
     LayerNorm epilogue, GEMM2 with the log-sum-exp epilogue, the loss combine,
     the noise-regenerating reduce and the outer product.
-The default workload is the fp32 LM head with T=4096 tokens (2x2048), d=512,
-V=8192, K=256 draws, sigma=1e-2.
+The default workload is the 243M-shape LM head: bf16 cached logits, T=8192 tokens
+(4x2048), d=1024, V=50304, K=16 full-vocabulary draws, sigma=5e-3.  The same JSON
+line also carries, under "mlp_linear", the MLP-linear estimator (T=4096, d=512,
+n=2048, V=8192, K=64) measured in the same process (skip with --no-mlp-line), and,
+under "alu_probe", the sustained vector-ALU rate of the head's instruction mix.
 
 Prints one JSON line: token-draws/s (T*K per step), per-stage times from HIP
 events on the call's stream, the roofline of the dominant kernel and the oracle
@@ -156,9 +159,9 @@ def write_traffic(args):
     cmds = [prof.format(c="FETCH_SIZE", n="copy_fetch", a=f"--copy-calibration {args.copy_calibration}"),
             prof.format(c="WRITE_SIZE", n="copy_write", a=f"--copy-calibration {args.copy_calibration}"),
             prof.format(c="FETCH_SIZE", n=f"fetch_w{args.workload}",
-                        a=f"{wl} --steps 1 --warmup 0 --no-cpu-baseline --no-alignment"),
+                        a=f"{wl} --steps 1 --warmup 0 --no-cpu-baseline --no-alignment --no-mlp-line --no-alu-probe"),
             prof.format(c="WRITE_SIZE", n=f"write_w{args.workload}",
-                        a=f"{wl} --steps 1 --warmup 0 --no-cpu-baseline --no-alignment"),
+                        a=f"{wl} --steps 1 --warmup 0 --no-cpu-baseline --no-alignment --no-mlp-line --no-alu-probe"),
             f"python bench.py {wl} --traffic-from DIR --copy-calibration {args.copy_calibration}"]
     out = {"kernel": kernel, "workload": args.workload, "subset_m": args.subset, "commands": cmds,
            "copy_bytes": copy_bytes,
@@ -189,7 +192,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", type=int, default=2, choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--workload", type=int, default=4, choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--draws", type=int, default=1024, help="K for workload 5")
     ap.add_argument("--subset", type=int, default=0, metavar="M",
                     help="LM-head workloads: perturb a window of M vocabulary channels per draw (plus the "
@@ -197,6 +200,11 @@ def parse():
     ap.add_argument("--attn-proj", default="v", choices=("q", "k", "v"),
                     help="workload 6: the attention projection whose output is perturbed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mlp-line", action="store_true",
+                    help="with the default 243M-shape head workload: skip the MLP-linear (workload 3) measurement "
+                         "that the same JSON line carries under 'mlp_linear'")
+    ap.add_argument("--no-alu-probe", action="store_true",
+                    help="skip the vector-ALU issue-rate probe (the measured peak of the head's instruction mix)")
     ap.add_argument("--no-alignment", action="store_true",
                     help="MLP-linear workloads: skip the cosine to the backprop gradient")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -277,6 +285,34 @@ def timed(dust, torch, step, nstage, steps):
     return wall, ev
 
 
+class KernelTimer:
+    """HIP events around every launch of chosen library kernels (the library records
+    them on the stream it launches on), for per-launch durations."""
+
+    def __init__(self, dust, torch, names, capacity):
+        self.dust, self.names = dust, names
+        stream = torch.cuda.current_stream()
+        self.ev = {n: ([torch.cuda.Event(enable_timing=True) for _ in range(capacity)],
+                       [torch.cuda.Event(enable_timing=True) for _ in range(capacity)]) for n in names}
+        for a, b in self.ev.values():
+            for e in a + b:
+                e.record(stream)
+        torch.cuda.synchronize()
+
+    def __enter__(self):
+        for n, (a, b) in self.ev.items():
+            self.dust.set_kernel_events(n, a, b)
+        return self
+
+    def __exit__(self, *exc):
+        self.ms = {}
+        for n, (a, b) in self.ev.items():
+            cnt = self.dust.kernel_event_count(n)
+            self.dust.set_kernel_events(n, None, None)
+            self.ms[n] = [self.dust.event_elapsed_ms(a[j], b[j]) for j in range(cnt)]
+        return False
+
+
 def run_head(args, c, dust, torch):
     T, V, d, K, sigma = c["T"], c["V"], c["d"], c["K"], c["sigma"]
     if "logits" in c:
@@ -305,10 +341,17 @@ def run_head(args, c, dust, torch):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    wall, ev = timed(dust, torch, step, 2, args.steps)
+    kern = "head_subset" if m and m // 4 < (V + 3) // 4 else "head"
+    names = ["outer"] + ([kern] if kern == "head" else [])
+    with KernelTimer(dust, torch, names, args.steps) as kt:
+        wall, ev = timed(dust, torch, step, 2, args.steps)
     est_ms = float(np.mean([dust.event_elapsed_ms(e[0], e[1]) for e in ev]))
     outer_ms = float(np.mean([dust.event_elapsed_ms(e[1], e[2]) for e in ev]))
     ms_per_step = wall * 1e3 / args.steps
+    # the estimator kernel's own launches (HIP events around each on the call's stream);
+    # the subset estimator's passes are timed together by the stage events
+    kern_ms = float(np.mean(kt.ms["head"])) if kt.ms.get("head") else est_ms
+    outer_main_ms = float(np.mean(kt.ms["outer"])) if kt.ms.get("outer") else None
     deg = head_taylor_degree(sigma)
     ops = head_lane_ops_per_channel_draw(deg)
     # channels perturbed per (token, draw): the vocabulary, or the window (the label,
@@ -317,7 +360,7 @@ def run_head(args, c, dust, torch):
     covers = not m or m // 4 >= nq
     per_draw = V if covers else m
     kernel = "head_estimate_kernel" if covers else "head_subset_kernel"
-    achieved = T * K * per_draw * ops / (est_ms / 1e3) / 1e9
+    achieved = T * K * per_draw * ops / (kern_ms / 1e3) / 1e9
     lb = 4 if "logits" in c else 2
     # bytes every step must move at least once: logits read, g_hat written and read back,
     # x read, grad_w written, labels read
@@ -331,12 +374,23 @@ def run_head(args, c, dust, torch):
                      "peak": VALU_PEAK_GOPS, "unit": "G lane-ops/s", "frac": achieved / VALU_PEAK_GOPS,
                      "traffic": load_traffic(kernel, args.workload, 0 if covers else m),
                      "lane_ops_per_channel_draw": ops, "taylor_degree": deg,
-                     "channel_draws_per_launch": T * K * per_draw, "kernel_ms": est_ms,
-                     "algorithmic_bytes_per_launch": kern_bytes},
+                     "channel_draws_per_launch": T * K * per_draw, "kernel_ms": kern_ms,
+                     "kernel_ms_source": "HIP events around each launch of the estimator kernel"
+                     if kern_ms is not est_ms else "HIP stage events around the estimator passes",
+                     "algorithmic_bytes_per_launch": kern_bytes,
+                     "hbm_GBps": kern_bytes / (kern_ms / 1e3) / 1e9,
+                     "hbm_frac": kern_bytes / (kern_ms / 1e3) / 1e9 / HBM_PEAK_GBS},
         "hbm": {"algorithmic_bytes_per_step": alg_bytes, "GBps": alg_bytes / (ms_per_step / 1e3) / 1e9,
                 "frac": alg_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS,
-                "estimator_kernel_GBps": kern_bytes / (est_ms / 1e3) / 1e9},
+                "estimator_kernel_GBps": kern_bytes / (kern_ms / 1e3) / 1e9},
     }
+    if outer_main_ms is not None:
+        fl = 2.0 * T * V * d
+        out["outer_product"] = {"kernel": "outer_x3_kernel", "ms_main_kernel": outer_main_ms,
+                                "ms_stage": outer_ms, "flops": fl,
+                                "issued_bf16_TFLOPs": 3 * fl / (outer_ms / 1e3) / 1e12,
+                                "frac_bf16_peak_issued": 3 * fl / (outer_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                                "note": "G_W = G^T X as three bf16 products (hi/lo pairs) with fp32 accumulation"}
     return ms_per_step, out
 
 
@@ -624,33 +678,41 @@ def run_linear(args, c, K, dust, torch):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    wall, ev = timed(dust, torch, step, 4, args.steps)
-    # events: 0 start, 1 after g_hat, 2 after outer, 3 after (last) gemm1, 4 after (last) gemm2
     rows = T * (K + 1)
-    single_chunk = rows * d * 2 <= (512 << 20)
+    nchunks = -(-rows * d * 2 // (512 << 20)) + 2
+    with KernelTimer(dust, torch, ["mlp_gemm1", "mlp_gemm2"], args.steps * nchunks) as kt:
+        wall, ev = timed(dust, torch, step, 4, args.steps)
+    # events: 0 start, 1 after g_hat, 2 after outer, 3 after (last) gemm1, 4 after (last) gemm2
     ms_per_step = wall * 1e3 / args.steps
     fl1 = 2.0 * rows * n * d
     fl2 = 2.0 * rows * d * V
+    # per step: the sum of every row chunk's launch (HIP events around each launch)
+    g1 = float(np.sum(kt.ms["mlp_gemm1"])) / args.steps
+    g2 = float(np.sum(kt.ms["mlp_gemm2"])) / args.steps
+    launches = len(kt.ms["mlp_gemm1"]) // args.steps
+    red = float(np.mean([dust.event_elapsed_ms(e[4], e[1]) for e in ev]))
+    outer = float(np.mean([dust.event_elapsed_ms(e[1], e[2]) for e in ev]))
     out = {"dtype": "bf16 GEMM operands with fp32 accumulate in the downstream; fp32 noise, rewards, g_hat, G_W"}
-    if single_chunk:
-        g1 = float(np.mean([dust.event_elapsed_ms(e[0], e[3]) for e in ev]))
-        g2 = float(np.mean([dust.event_elapsed_ms(e[3], e[4]) for e in ev]))
-        red = float(np.mean([dust.event_elapsed_ms(e[4], e[1]) for e in ev]))
-        outer = float(np.mean([dust.event_elapsed_ms(e[1], e[2]) for e in ev]))
-        out["stages_ms"] = {"gemm1_noise_gelu_w2_ln": g1, "gemm2_head_logsumexp": g2, "combine_and_reduce": red,
-                            "outer_product": outer}
-        out["roofline"] = {"bound": "mfma", "kernel": "mlp_gemm2_kernel", "achieved": fl2 / (g2 / 1e3) / 1e12,
-                           "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                           "frac": fl2 / (g2 / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-                           "traffic": load_traffic("mlp_gemm2_kernel", args.workload),
-                           "flop_per_launch": fl2, "kernel_ms": g2,
-                           "algorithmic_bytes_per_launch": rows * d * 2 + V * d * 2 + rows * 4
-                           + (V + 255) // 256 * rows * 8}
-        out["mfma_downstream"] = {"gemm1_TFLOPs": fl1 / (g1 / 1e3) / 1e12, "gemm2_TFLOPs": fl2 / (g2 / 1e3) / 1e12,
-                                  "both_frac_of_peak": (fl1 + fl2) / ((g1 + g2) / 1e3) / 1e12
-                                  / MFMA_BF16_PEAK_TFLOPS}
-    else:
-        out["mfma_downstream"] = {"both_TFLOPs_whole_step": (fl1 + fl2) / (ms_per_step / 1e3) / 1e12}
+    out["stages_ms"] = {"gemm1_noise_gelu_w2_ln": g1, "gemm2_head_logsumexp": g2,
+                        "combine_and_reduce_last_chunk": red, "outer_product": outer}
+    both = (fl1 + fl2) / ((g1 + g2) / 1e3) / 1e12
+    out["roofline"] = {"bound": "mfma", "kernel": "mlp_gemm1_kernel + mlp_gemm2_kernel", "achieved": both,
+                       "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": both / MFMA_BF16_PEAK_TFLOPS,
+                       "traffic": None, "flop_per_step": fl1 + fl2, "kernel_ms": g1 + g2,
+                       "launches_per_step": 2 * launches,
+                       "note": "the two downstream GEMMs together: their algorithmic flops (2 rows n d + 2 rows d V, "
+                               "rows = T (K + 1)) over the sum of their launch durations (HIP events around each "
+                               "launch, every row chunk)"}
+    out["mfma_downstream"] = {
+        "mlp_gemm1_kernel": {"TFLOPs": fl1 / (g1 / 1e3) / 1e12, "frac": fl1 / (g1 / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                             "ms_per_step": g1, "flop_per_step": fl1},
+        "mlp_gemm2_kernel": {"TFLOPs": fl2 / (g2 / 1e3) / 1e12, "frac": fl2 / (g2 / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                             "ms_per_step": g2, "flop_per_step": fl2,
+                             "traffic": load_traffic("mlp_gemm2_kernel", args.workload),
+                             "algorithmic_bytes_per_step": rows * d * 2 + V * d * 2 + rows * 4
+                             + (V + 255) // 256 * rows * 8},
+        "launches_per_step_each": launches,
+    }
     # bytes the step must move at least once: its inputs and G_W (F stays on chip in
     # principle; its HBM round trip is not counted)
     alg_bytes = 4 * T * (d + n + d) + 2 * d * n + 2 * V * d + 4 * T + 4 * n * d
@@ -687,17 +749,93 @@ def main():
         with torch.no_grad():
             return (torch.from_numpy(X).cuda() @ torch.from_numpy(W).cuda().T).cpu().numpy()
 
-    c = synth.workload(args.workload, matmul=gpu_matmul)
-    name = WORKLOAD_NAMES[args.workload]
+    out = measure(args, args.workload, dust, torch, synth, gpu_matmul)
+    head_default = out["config"].get("V") == 50304 and not args.subset
+    if out.pop("_kind") == "head" and not args.no_alu_probe:
+        probe = alu_probe(torch)
+        if probe is not None:
+            out["alu_probe"] = probe
+            r = out["roofline"]
+            mix = probe["head_mix"]["channel_draws_per_s"]
+            r["peak_measured_mix_G_lane_ops"] = probe["head_mix"]["G_lane_ops_per_s"]
+            r["frac_of_measured_mix"] = (r["channel_draws_per_launch"] / (r["kernel_ms"] / 1e3)) / mix
+            r["measured_mix_note"] = ("the estimator's channel-draws/s over those of the probe that runs the same "
+                                      "per-channel-draw arithmetic (Philox, Box-Muller, degree-4 expm1 term, running "
+                                      "sums) from registers only")
+    if args.workload == 4 and head_default and not args.no_mlp_line:
+        print("bench: 243M-shape head done; MLP-linear workload 3 next", file=sys.stderr, flush=True)
+        mlp = measure(args, 3, dust, torch, synth, gpu_matmul)
+        mlp.pop("_kind")
+        for k in ("n_gpus", "higher_is_better", "scaling", "data", "warmup", "steps"):
+            mlp.pop(k, None)
+        out["mlp_linear"] = mlp
+    print(json.dumps(out), flush=True)
+
+
+def alu_probe(torch):
+    """Sustained vector-ALU rates on this chip: each probe loop's vector instructions
+    (counted from its own assembly at build time) x 64 lanes x waves x trips, over the
+    time of a launch that fills every CU many times over."""
+    lib_path = os.path.join(ROOT, "zeroth_order_activation_amd", "libdust_probe.so")
+    cnt_path = os.path.join(ROOT, "zeroth_order_activation_amd", "libdust_probe.json")
+    if not (os.path.exists(lib_path) and os.path.exists(cnt_path)):
+        print("bench: libdust_probe.so not built; no ALU probe", file=sys.stderr, flush=True)
+        return None
+    import ctypes
+    L = ctypes.CDLL(lib_path)
+    L.dust_probe_valu_mix.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    L.dust_probe_valu_mix.restype = ctypes.c_int
+    with open(cnt_path) as f:
+        per_trip = {int(k): v for k, v in json.load(f)["valu_per_loop_trip"].items()}
+    blocks = N_CU * 32
+    gin = torch.rand(2048, device="cuda") + 0.5
+    gout = torch.empty(blocks * 256, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    names = {0: "fma_f32", 1: "mad_u64_u32_and_xor", 2: "log_sqrt_sin_cos_mul", 3: "head_mix"}
+    iters = {0: 2048, 1: 1024, 2: 2048, 3: 32}
+    res = {}
+    for mix in (0, 1, 2, 3):
+        for rep in range(2):  # the first launch warms up; the second is timed
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            rc = L.dust_probe_valu_mix(mix, blocks, iters[mix], ctypes.c_void_p(gin.data_ptr()),
+                                       ctypes.c_void_p(gout.data_ptr()), stream)
+            b.record()
+            torch.cuda.synchronize()
+            if rc != 0:
+                raise RuntimeError(f"probe mix {mix} failed: {rc}")
+        ms = a.elapsed_time(b)
+        waves = blocks * 4
+        lane_ops = per_trip[mix] * 64 * waves * iters[mix]
+        res[names[mix]] = {"valu_per_loop_trip": per_trip[mix], "ms": ms,
+                           "G_lane_ops_per_s": lane_ops / (ms / 1e3) / 1e9,
+                           "frac_of_unit_count_peak": lane_ops / (ms / 1e3) / 1e9 / VALU_PEAK_GOPS}
+    # the head mix: 8 channel quads = 32 channel-draws per lane and loop trip
+    res["head_mix"]["channel_draws_per_s"] = 32 * 256 * blocks * iters[3] / (res["head_mix"]["ms"] / 1e3)
+    res["head_mix"]["valu_per_channel_draw"] = per_trip[3] / 32
+    res["note"] = ("register-only loops over 8192 workgroups of 256 lanes; rates are vector instructions x 64 lanes "
+                   "per second (one issue slot per instruction), against 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz")
+    return res
+
+
+def measure(args, wid, dust, torch, synth, gpu_matmul):
+    """One workload: its timed steps, roofline and (unless --no-cpu-baseline) the oracle
+    timed on the host cores.  Returns the JSON object of its line."""
+    print(f"bench: workload {wid}: inputs", file=sys.stderr, flush=True)
+    args = argparse.Namespace(**{**vars(args), "workload": wid})
+    c = synth.workload(wid, matmul=gpu_matmul)
+    name = WORKLOAD_NAMES[wid]
     if args.subset and c["kind"] != "head":
         sys.exit("--subset applies to the LM-head workloads (1, 2, 4)")
+    sub = args.subset
     if c["kind"] == "head":
         K = c["K"]
         ms, extra = run_head(args, c, dust, torch)
         cfg = {"workload": name, "T": c["T"], "V": c["V"], "d": c["d"], "K": K, "sigma": c["sigma"]}
-        if args.subset:
-            cfg["workload"] = name + f"; vocabulary subset: window of {args.subset} channels per draw + label"
-            cfg["subset_m"] = args.subset
+        if sub:
+            cfg["workload"] = name + f"; vocabulary subset: window of {sub} channels per draw + label"
+            cfg["subset_m"] = sub
     elif c["kind"] == "lm":
         ms, td, extra = run_lm(args, c, dust, torch)
         cfg = {"workload": name, "T": c["T"], "V": c["V"], "d": c["d"], "H": c["H"], "L": c["L"], "n": c["n"],
@@ -715,7 +853,8 @@ def main():
         name = name.format(K=K)
         ms, extra = run_linear(args, c, K, dust, torch)
         cfg = {"workload": name, "T": c["T"], "d": c["d"], "n": c["n"], "V": c["V"], "K": K, "sigma": c["sigma"]}
-    cfg.update({"noise_seed": c["seed_noise"], "layer": c["layer"], "data_seed": 1000 + args.workload})
+    print(f"bench: workload {wid}: {ms:.3f} ms per step", file=sys.stderr, flush=True)
+    cfg.update({"noise_seed": c["seed_noise"], "layer": c["layer"], "data_seed": 1000 + wid})
     out = {
         "metric": "token-draws/sec per Dust gradient estimate; % of HBM BW / MFMA peak",
         "value": (td if c["kind"] == "lm" else c["T"] * K) / (ms / 1e3),
@@ -730,14 +869,15 @@ def main():
         "dtype": extra.pop("dtype"),
         "data": "synthetic (seeded; stands in for FineWeb)",
         "config": cfg,
+        "_kind": c["kind"],
     }
     out.update(extra)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = (cpu_baseline_lm(c, args.cpu_seconds) if c["kind"] == "lm"
-                               else cpu_baseline_head(c, args.cpu_seconds, args.subset) if c["kind"] == "head"
+                               else cpu_baseline_head(c, args.cpu_seconds, sub) if c["kind"] == "head"
                                else cpu_baseline_attn(c, args.cpu_seconds, args.attn_proj) if c["kind"] == "attn_v"
                                else cpu_baseline_linear(c, K, args.cpu_seconds))
-    print(json.dumps(out), flush=True)
+    return out
 
 
 if __name__ == "__main__":

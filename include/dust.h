@@ -32,6 +32,13 @@
  *     access, but the result is then meaningless.  With DUST_DEBUG_CHECKS=1 in
  *     the environment the labels are copied back and checked (synchronising).
  *   - Results are bitwise deterministic run to run (no floating-point atomics).
+ *   - State: the library holds no state between calls apart from two kinds of
+ *     thread-local data: the error message (dust_last_error) and the profiling
+ *     hooks a caller sets with dust_set_stage_event / dust_set_kernel_events
+ *     (event handles recorded on the call's stream; cleared by passing NULL).
+ *   - Token and draw ids: token_offset is 64-bit in every signature, but the
+ *     noise counter holds token and draw ids in one 32-bit Philox word each, so
+ *     token_offset + T <= 2^32 and draw_offset + K <= 2^32 (else DUST_E_INVALID).
  *
  * Noise stream (the pages say only "independent Gaussian noise per token";
  * this library fixes one stream so that results are reproducible):
@@ -54,7 +61,7 @@
 extern "C" {
 #endif
 
-#define DUST_ABI_VERSION 1
+#define DUST_ABI_VERSION 2
 
 typedef enum {
     DUST_OK = 0,
@@ -94,7 +101,10 @@ dust_status dust_set_stage_event(int stage, void *event);
  * first `capacity` launches (hipEvent_t handles owned by the caller; the arrays are
  * copied).  kernel 0 = the small-LM step's GEMM of change rows (C = A B^T on bf16x3
  * MFMA), 1 = its fused head change, 2 = the main pass of dust_estimate_attn (query, key
- * or value kernel).
+ * or value kernel), 3 = dust_estimate_linear's GEMM1 (F = LN(x + W2 GELU(.))), once per
+ * row chunk, 4 = its GEMM2 (the head product and log-sum-exp), once per row chunk,
+ * 5 = dust_estimate_head's per-token estimator kernel, 6 = the main product kernel of
+ * the bf16-pair outer product (the first pass over whole rounds of output tiles).
  * dust_kernel_event_count(kernel) returns how many launches were recorded since the
  * hook was set (-1 for an unknown kernel).  NULL arrays or capacity <= 0 clear it.
  */
@@ -111,8 +121,18 @@ int dust_kernel_event_count(int kernel);
  * Requires draw_offset + K <= 2^32 and token_offset + T <= 2^32.
  */
 dust_status dust_noise(uint64_t seed, uint32_t layer, uint32_t draw_offset, int64_t K,
-                       uint32_t token_offset, int64_t T, int64_t n,
+                       uint64_t token_offset, int64_t T, int64_t n,
                        uint32_t *raw, float *gauss, void *stream);
+
+/*
+ * Noise of one (draw, token): the Gaussian values a[0..n) and, optionally, the raw
+ * Philox words behind them, exactly as every estimator draws them for that draw id,
+ * token id and layer.  The same stream as dust_noise with K = T = 1.
+ *   raw   : uint32 [4*ceil(n/4)] or NULL;  gauss : float [n] or NULL (not both NULL).
+ *   token < 2^32 (DUST_E_INVALID otherwise); n >= 1.
+ */
+dust_status dust_debug_noise(uint64_t seed, uint32_t layer, uint32_t draw, uint64_t token, int64_t n,
+                             uint32_t *raw, float *gauss, void *stream);
 
 /*
  * Weight-gradient outer product  grad_w = ghat^T x  =  sum_t ghat_t x_t^T
@@ -144,7 +164,7 @@ size_t dust_head_workspace_bytes(int64_t T, int64_t V, int64_t d, int64_t K);
 dust_status dust_estimate_head(const void *logits, int logits_dtype, const float *x,
                                const int32_t *labels, int64_t T, int64_t V, int64_t d,
                                int64_t K, float sigma, uint64_t seed, uint32_t layer,
-                               uint32_t token_offset, uint32_t draw_offset,
+                               uint64_t token_offset, uint32_t draw_offset,
                                float *grad_w, float *ghat, float *rewards,
                                void *workspace, size_t workspace_bytes, void *stream);
 
@@ -177,7 +197,7 @@ size_t dust_head_subset_workspace_bytes(int64_t T, int64_t V, int64_t d, int64_t
 dust_status dust_estimate_head_subset(const void *logits, int logits_dtype, const float *x,
                                       const int32_t *labels, int64_t T, int64_t V, int64_t d,
                                       int64_t K, int64_t m, float sigma, uint64_t seed, uint32_t layer,
-                                      uint32_t token_offset, uint32_t draw_offset,
+                                      uint64_t token_offset, uint32_t draw_offset,
                                       float *grad_w, float *ghat, float *rewards,
                                       void *workspace, size_t workspace_bytes, void *stream);
 
@@ -198,7 +218,8 @@ dust_status dust_estimate_head_subset(const void *logits, int logits_dtype, cons
  *   w2     : bf16 bits [d, n];   w_head : bf16 bits [V, d]
  *   labels : int32 [T]
  *   grad_w : OUT float [n, d];  ghat : OUT float [T, n] or NULL;  rewards : OUT float [K, T] or NULL.
- * Supported: d in {256, 512}, n a multiple of 32, V >= 1.
+ * Supported: d in {256, 512}, n a multiple of 32, V >= 1, V*d < 2^31 and n*d < 2^31
+ * (DUST_E_UNSUPPORTED otherwise).
  * Workspace: dust_linear_workspace_bytes(T, d, n, V, K) bytes.
  */
 size_t dust_linear_workspace_bytes(int64_t T, int64_t d, int64_t n, int64_t V, int64_t K);
@@ -206,7 +227,7 @@ dust_status dust_estimate_linear(const float *u, const float *h, const float *x_
                                  const uint16_t *w2, const uint16_t *w_head, const int32_t *labels,
                                  int64_t T, int64_t d, int64_t n, int64_t V, int64_t K,
                                  float sigma, float ln_eps, uint64_t seed, uint32_t layer,
-                                 uint32_t token_offset, uint32_t draw_offset,
+                                 uint64_t token_offset, uint32_t draw_offset,
                                  float *grad_w, float *ghat, float *rewards,
                                  void *workspace, size_t workspace_bytes, void *stream);
 
@@ -247,13 +268,13 @@ typedef enum { DUST_ATTN_Q = 0, DUST_ATTN_K = 1, DUST_ATTN_V = 2 } dust_attn_pro
 size_t dust_attn_workspace_bytes(int proj, int64_t T, int64_t S, int64_t d, int64_t H, int64_t K);
 dust_status dust_estimate_attn(int proj, const float *q, const float *k, const float *v, const float *e,
                                const float *u, int64_t T, int64_t S, int64_t d, int64_t H, int64_t K,
-                               float sigma, uint64_t seed, uint32_t layer, uint32_t token_offset,
+                               float sigma, uint64_t seed, uint32_t layer, uint64_t token_offset,
                                uint32_t draw_offset, float *grad_w, float *ghat, float *rewards,
                                void *workspace, size_t workspace_bytes, void *stream);
 size_t dust_attn_v_workspace_bytes(int64_t T, int64_t S, int64_t d, int64_t H, int64_t K);
 dust_status dust_estimate_attn_v(const float *q, const float *k, const float *e, const float *u,
                                  int64_t T, int64_t S, int64_t d, int64_t H, int64_t K, float sigma,
-                                 uint64_t seed, uint32_t layer, uint32_t token_offset,
+                                 uint64_t seed, uint32_t layer, uint64_t token_offset,
                                  uint32_t draw_offset, float *grad_w, float *ghat, float *rewards,
                                  void *workspace, size_t workspace_bytes, void *stream);
 

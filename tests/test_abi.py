@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     assert {"dust_estimate_head", "dust_noise", "dust_outer_product", "dust_last_error"} <= names
     for n in sorted(names):
         assert hasattr(L, n), n
-    assert L.dust_abi_version() == 1
+    assert L.dust_abi_version() == 2
 
 
 def _head(**kw):
@@ -57,6 +57,7 @@ def _head(**kw):
     (dict(sigma=float("nan")), 1, "sigma"),
     (dict(sigma=float("inf")), 1, "sigma"),
     (dict(tok=2**32 - 2), 1, "token counter"),
+    (dict(tok=2**40), 1, "token counter"),    # a 64-bit id past the 32-bit counter word
     (dict(draw=2**32 - 1), 1, "draw counter"),
     (dict(V=70000), 2, "65536"),
     (dict(V=40000, dt=0), 2, "LDS"),
@@ -131,6 +132,28 @@ def test_outer_and_noise_reject_bad_arguments():
     assert L.dust_noise(1, 0, 0, 1, 0, 1, 4, None, None, None) == 1
     assert L.dust_noise(1, 0, 2**32 - 1, 2, 0, 1, 4, None, FAKE, None) == 1
     assert L.dust_noise(1, 0, 0, 0, 0, 1, 4, None, FAKE, None) == 1
+    assert L.dust_noise(1, 0, 0, 1, 2**33, 1, 4, None, FAKE, None) == 1
+    # the single-(draw, token) export
+    assert L.dust_debug_noise(1, 0, 0, 0, 4, None, None, None) == 1
+    assert L.dust_debug_noise(1, 0, 0, 0, 0, None, FAKE, None) == 1
+    assert L.dust_debug_noise(1, 0, 0, 2**32, 4, None, FAKE, None) == 1
+    assert "2^32" in L.dust_last_error().decode()
+
+
+def test_linear_rejects_oversized_weights_on_host():
+    L = dust.lib()
+
+    def call(V, d=512, n=2048):
+        st = L.dust_estimate_linear(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, d, n, V, 2, ctypes.c_float(0.01),
+                                    ctypes.c_float(1e-5), 1, 0, 0, 0, FAKE, None, None, None, 0, None)
+        return st, L.dust_last_error().decode()
+
+    st, err = call(V=(1 << 31) // 512)  # V*d = 2^31: the W_head offsets would wrap
+    assert st == 2 and "2^31" in err, err
+    st, err = call(V=8192, d=256, n=(1 << 31) // 256)
+    assert st == 2, err
+    st, err = call(V=(1 << 31) // 512 - 1)  # the largest accepted vocabulary: fails only on the workspace
+    assert st == 3, err
 
 
 def test_workspace_queries():

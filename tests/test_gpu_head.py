@@ -89,11 +89,14 @@ def test_workload1_full_parity():
     assert rel_l2(rew.cpu().numpy(), orew) < TOL_REW
 
 
-@pytest.mark.parametrize("wid,ntok", [(2, 12), (4, 6)])
-def test_named_workload_full_size(wid, ntok):
-    """Full-size workload in the benchmark's configuration (g_hat kept in the workspace)."""
+@pytest.mark.parametrize("wid", [2, 4])
+def test_named_workload_whole(wid):
+    """Full-size workload in the benchmark's configuration (g_hat kept in the workspace):
+    every reward, every g_hat element and the whole G_W against the oracle run on the
+    same inputs."""
     c = synth.workload(wid, matmul=gpu_matmul)
     T, V, K, sigma = c["T"], c["V"], c["K"], c["sigma"]
+    print(f"workload {wid}: GPU estimate", flush=True)
     z, x, y = logits_to_device(c), dev(c["x"]), dev(c["labels"])
     gw_bench = dust.estimate_head(z, x, y, K, sigma, c["seed_noise"], c["layer"])
     ghat = torch.empty((T, V), dtype=torch.float32, device="cuda")
@@ -101,23 +104,15 @@ def test_named_workload_full_size(wid, ntok):
     gw = dust.estimate_head(z, x, y, K, sigma, c["seed_noise"], c["layer"], ghat=ghat, rewards=rew)
     torch.cuda.synchronize()
     assert torch.equal(gw, gw_bench)  # same result with or without the g_hat output
-    toks = np.random.default_rng(wid).choice(T, ntok, replace=False)
-    toks[0] = int(np.argmax(c["labels"] > 0))  # include a token whose label is not 0
-    zv = logits_values({k: (v[toks] if k in ("logits", "logits_bf16") else v) for k, v in c.items()})
-    og_rows = []
-    for t in toks:  # tokens one by one, with their global token ids
-        g1, r1, _ = oracle.head_estimate(zv[list(toks).index(t)][None], c["labels"][[t]], K, sigma,
-                                         c["seed_noise"], c["layer"], token_offset=int(t))
-        og_rows.append((g1[0], r1[:, 0]))
-    gh = ghat[toks].cpu().numpy()
-    rw = rew[:, toks].cpu().numpy()
-    e_g = rel_l2(gh, np.stack([g for g, _ in og_rows]))
-    e_r = rel_l2(rw, np.stack([r for _, r in og_rows], axis=1))
-    rows = np.random.default_rng(wid + 1).choice(V, 64, replace=False)
-    ref_rows = ghat[:, rows].cpu().numpy().astype(np.float64).T @ c["x"].astype(np.float64)
-    e_w = rel_l2(gw[rows].cpu().numpy(), ref_rows)
-    print(f"workload {wid}: sampled ghat {e_g:.2e} rewards {e_r:.2e}; grad_w rows vs G^T X {e_w:.2e}")
-    assert e_g < TOL_GHAT and e_r < TOL_REW and e_w < 6e-5  # bf16-pair outer product
+    del z
+    print(f"workload {wid}: oracle on every token", flush=True)
+    og, orew, _ = oracle.head_estimate(logits_values(c), c["labels"], K, sigma, c["seed_noise"], c["layer"])
+    e_r = rel_l2(rew.cpu().numpy(), orew)
+    e_g = rel_l2(ghat.cpu().numpy(), og)
+    del ghat
+    e_w = rel_l2(gw.cpu().numpy(), oracle.grad_w(og, c["x"]))
+    print(f"workload {wid}: rewards {e_r:.2e}, g_hat {e_g:.2e}, grad_w {e_w:.2e} (relative L2 against the oracle)")
+    assert e_r < TOL_REW and e_g < TOL_GHAT and e_w < TOL_GW
 
 
 def test_deterministic_and_split_invariants():

@@ -54,14 +54,16 @@ def _oracle(c, K, sigma, seed, layer, tok0=0, draw0=0, tokens=None):
                                   c["ln_eps"], seed, layer, tok0, draw0, tokens=tokens)
 
 
+# K chosen so that every case has at least 1000 rewards: the relative L2 bars on
+# rewards, g_hat and G_W then apply to every case.
 SMALL = [
     # T, d, n, V, K, sigma
-    (8, 256, 64, 40, 3, 1e-2),
-    (37, 512, 128, 1000, 4, 1e-2),     # ragged vocabulary tile, ragged row tiles
-    (70, 256, 96, 300, 5, 2e-2),
-    (130, 512, 256, 2048, 2, 1e-2),
-    (8, 256, 32, 777, 3, 1e-2),        # the narrowest layer accepted (n = 32), ragged vocabulary
-    (4, 512, 64, 50304, 2, 1e-2),      # a 50304-entry vocabulary (197 tiles of 256)
+    (8, 256, 64, 40, 125, 1e-2),
+    (37, 512, 128, 1000, 28, 1e-2),    # ragged vocabulary tile, ragged row tiles
+    (70, 256, 96, 300, 15, 2e-2),
+    (130, 512, 256, 2048, 8, 1e-2),
+    (8, 256, 32, 777, 125, 1e-2),      # the narrowest layer accepted (n = 32), ragged vocabulary
+    (4, 512, 64, 50304, 250, 1e-2),    # a 50304-entry vocabulary (197 tiles of 256)
 ]
 
 
@@ -74,26 +76,42 @@ def test_linear_small_cases(T, d, n, V, K, sigma):
     st = check_quantized_rewards(rew.cpu().numpy(), orew, oce0)
     gh = ghat.cpu().numpy()
     _check_reduction(c, gh, rew.cpu().numpy(), range(T), K, sigma, seed, layer, tok0, draw0)
-    e_w = rel_l2(gw.cpu().numpy(), gh.astype(np.float64).T @ c["u"].astype(np.float64))
-    print(f"T={T} d={d} n={n} V={V} K={K}: rewards {st}; grad_w vs G^T U {e_w:.2e}")
+    u64 = c["u"].astype(np.float64)
+    e_w = rel_l2(gw.cpu().numpy(), gh.astype(np.float64).T @ u64)
+    e_go = rel_l2(gh, og)
+    e_wo = rel_l2(gw.cpu().numpy(), oracle.grad_w(og, u64))
+    print(f"T={T} d={d} n={n} V={V} K={K}: rewards {st}; g_hat vs oracle {e_go:.2e}; "
+          f"grad_w vs oracle {e_wo:.2e}; grad_w vs G^T U {e_w:.2e}")
     assert e_w < 1e-5
+    assert e_go < TOL_GW and e_wo < TOL_GW
 
 
-@pytest.mark.parametrize("wid,K,ntok", [(3, 64, 16), (5, 256, 4)])
+@pytest.mark.parametrize("wid,K,ntok", [(3, 64, 16), (5, 256, 4), (5, 1024, 8), (5, 4096, 3), (5, 16384, 2)])
 def test_named_workload_full_size(wid, K, ntok):
+    """Full-size workload in the benchmark's configuration; sampled tokens against the
+    oracle (every draw of each), all grad_w rows against the identity G_W = G^T U, and
+    sampled rows of the oracle's G_W restricted to the sampled tokens."""
     c = synth.workload(wid)
     T, n, sigma = c["T"], c["n"], c["sigma"]
+    print(f"workload {wid} K={K}: GPU estimate", flush=True)
     gw, ghat, rew = _run(c, K, sigma, c["seed_noise"], c["layer"])
-    toks = np.random.default_rng(wid).choice(T, ntok, replace=False)
+    toks = np.random.default_rng(wid + K).choice(T, ntok, replace=False)
     og, orew, oce0 = _oracle(c, K, sigma, c["seed_noise"], c["layer"], tokens=toks)
     rw = rew[:, toks].cpu().numpy()
     st = check_quantized_rewards(rw, orew, oce0)
-    _check_reduction(c, ghat[toks].cpu().numpy(), rw, toks, K, sigma, c["seed_noise"], c["layer"])
-    rows = np.random.default_rng(wid + 1).choice(n, 64, replace=False)
-    ref = ghat[:, rows].cpu().numpy().astype(np.float64).T @ c["u"].astype(np.float64)
-    e_w = rel_l2(gw[rows].cpu().numpy(), ref)
-    print(f"workload {wid} K={K}: sampled rewards {st}; grad_w rows vs G^T U {e_w:.2e}")
+    gh_s = ghat[toks].cpu().numpy()
+    _check_reduction(c, gh_s, rw, toks, K, sigma, c["seed_noise"], c["layer"])
+    e_go = rel_l2(gh_s, og)
+    u64 = c["u"].astype(np.float64)
+    # the sampled tokens' share of G_W: their g_hat rows against the oracle's
+    e_wo = rel_l2(gh_s.astype(np.float64).T @ u64[toks], og.T @ u64[toks])
+    gw_h = gw.cpu().numpy()
+    ref = ghat.cpu().numpy().astype(np.float64).T @ u64
+    e_w = rel_l2(gw_h, ref)
+    print(f"workload {wid} K={K}: sampled rewards {st}; g_hat vs oracle {e_go:.2e}; "
+          f"sampled tokens' G_W vs oracle {e_wo:.2e}; grad_w vs G^T U {e_w:.2e}")
     assert e_w < 6e-5  # bf16-pair outer product
+    assert e_go < TOL_GW and e_wo < TOL_GW
 
 
 def test_linear_deterministic_additive_and_chunked():

@@ -15,7 +15,9 @@ from gpu_cases import dev, rel_l2
 
 pytestmark = pytest.mark.gpu
 
-GAUSS_ABS_TOL = 2e-5
+# the Box-Muller spec in fp32 against fp64: about 6e-7 at most measured (hardware
+# log2/sqrt/sin/cos); the bar is the one fixed for the noise stream
+GAUSS_ABS_TOL = 2e-6
 
 
 @pytest.mark.parametrize("seed,layer,d0,K,t0,T,n", [
@@ -39,6 +41,21 @@ def test_noise_gaussians_match_oracle():
     print(f"gaussian max abs err {err.max():.3e}, rms {np.sqrt((err ** 2).mean()):.3e}")
     assert err.max() < GAUSS_ABS_TOL
     assert np.abs(g).max() <= 5.7684
+
+
+@pytest.mark.parametrize("seed,layer,draw,token,n", [
+    (0x4455535400000004, 1, 0, 0, 1),
+    (0x4455535400000002, 3, 17, 123456, 1001),
+    (0xFFFFFFFFFFFFFFFF, 2**32 - 1, 2**32 - 1, 2**32 - 1, 64),
+])
+def test_debug_noise_is_the_oracle_stream(seed, layer, draw, token, n):
+    g, w = dust.debug_noise(seed, layer, draw, token, n, raw=True)
+    np.testing.assert_array_equal(w.cpu().numpy().view(np.uint32), oracle.noise_raw(seed, layer, draw, token, n))
+    err = np.abs(g.cpu().numpy().astype(np.float64) - oracle.noise(seed, layer, draw, token, n))
+    assert err.max() < GAUSS_ABS_TOL, err.max()
+    # the same values as the batched export at that (draw, token)
+    gb = dust.noise(seed, layer, draw, 1, token, 1, n)[0, 0]
+    assert torch.equal(g, gb)
 
 
 def outer_tol(T, n, d):

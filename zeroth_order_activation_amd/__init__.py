@@ -51,7 +51,9 @@ def lib():
         L.dust_set_stage_event.restype = ctypes.c_int
         L.dust_set_stage_event.argtypes = [ctypes.c_int, _vp]
         L.dust_noise.restype = ctypes.c_int
-        L.dust_noise.argtypes = [_u64, _u32, _u32, _i64, _u32, _i64, _i64, _vp, _vp, _vp]
+        L.dust_noise.argtypes = [_u64, _u32, _u32, _i64, _u64, _i64, _i64, _vp, _vp, _vp]
+        L.dust_debug_noise.restype = ctypes.c_int
+        L.dust_debug_noise.argtypes = [_u64, _u32, _u32, _u64, _i64, _vp, _vp, _vp]
         L.dust_outer_workspace_bytes.restype = ctypes.c_size_t
         L.dust_outer_workspace_bytes.argtypes = [_i64, _i64, _i64]
         L.dust_outer_product.restype = ctypes.c_int
@@ -60,29 +62,29 @@ def lib():
         L.dust_head_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64]
         L.dust_estimate_head.restype = ctypes.c_int
         L.dust_estimate_head.argtypes = [_vp, ctypes.c_int, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _u64, _u32,
-                                         _u32, _u32, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+                                         _u64, _u32, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.dust_head_subset_workspace_bytes.restype = ctypes.c_size_t
         L.dust_head_subset_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64]
         L.dust_estimate_head_subset.restype = ctypes.c_int
         L.dust_estimate_head_subset.argtypes = [_vp, ctypes.c_int, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32,
-                                                _u64, _u32, _u32, _u32, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+                                                _u64, _u32, _u64, _u32, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.dust_attn_workspace_bytes.restype = ctypes.c_size_t
         L.dust_attn_workspace_bytes.argtypes = [ctypes.c_int, _i64, _i64, _i64, _i64, _i64]
         L.dust_estimate_attn.restype = ctypes.c_int
         L.dust_estimate_attn.argtypes = [ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32,
-                                         ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
+                                         ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_uint32,
                                          _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.dust_attn_v_workspace_bytes.restype = ctypes.c_size_t
         L.dust_attn_v_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _i64]
         L.dust_estimate_attn_v.restype = ctypes.c_int
         L.dust_estimate_attn_v.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32,
-                                           ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
+                                           ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_uint32,
                                            _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.dust_linear_workspace_bytes.restype = ctypes.c_size_t
         L.dust_linear_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, _i64]
         L.dust_estimate_linear.restype = ctypes.c_int
         L.dust_estimate_linear.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32,
-                                           _f32, _u64, _u32, _u32, _u32, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+                                           _f32, _u64, _u32, _u64, _u32, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.dust_set_kernel_events.restype = ctypes.c_int
         L.dust_set_kernel_events.argtypes = [ctypes.c_int, _vp, _vp, ctypes.c_int]
         L.dust_kernel_event_count.restype = ctypes.c_int
@@ -151,7 +153,8 @@ def set_stage_event(stage: int, event) -> None:
 _hip = None
 
 
-TIMED_KERNELS = {"lm_gemm": 0, "lm_head": 1, "attn_main": 2}
+TIMED_KERNELS = {"lm_gemm": 0, "lm_head": 1, "attn_main": 2, "mlp_gemm1": 3, "mlp_gemm2": 4, "head": 5,
+                 "outer": 6}
 
 
 def set_kernel_events(kernel: str, starts, ends) -> None:
@@ -193,6 +196,14 @@ def noise(seed: int, layer: int, draw_offset: int, K: int, token_offset: int, T:
     g = torch.empty((K, T, n), dtype=torch.float32, device=device)
     w = torch.empty((K, T, 4 * ((n + 3) // 4)), dtype=torch.int32, device=device) if raw else None
     _check(lib().dust_noise(seed, layer, draw_offset, K, token_offset, T, n, _p(w), _p(g), _stream(g)))
+    return (g, w.view(torch.uint32) if hasattr(torch, "uint32") else w) if raw else g
+
+
+def debug_noise(seed: int, layer: int, draw: int, token: int, n: int, device="cuda", raw: bool = False):
+    """The noise a[n] of one (draw, token) (and the raw Philox words if ``raw``)."""
+    g = torch.empty((n,), dtype=torch.float32, device=device)
+    w = torch.empty((4 * ((n + 3) // 4),), dtype=torch.int32, device=device) if raw else None
+    _check(lib().dust_debug_noise(seed, layer, draw, token, n, _p(w), _p(g), _stream(g)))
     return (g, w.view(torch.uint32) if hasattr(torch, "uint32") else w) if raw else g
 
 

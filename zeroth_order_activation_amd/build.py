@@ -60,5 +60,64 @@ def build(extra=(), jobs: int | None = None, verbose: bool = False) -> str:
     return LIB
 
 
+PROBE_SRC = os.path.join(PKG, "probe", "valu_mix.hip")
+PROBE_LIB = os.path.join(PKG, "libdust_probe.so")
+PROBE_COUNTS = os.path.join(PKG, "libdust_probe.json")
+PROBE_KERNELS = {"mix_fma_kernel": 0, "mix_mad64_kernel": 1, "mix_trans_kernel": 2, "mix_head_kernel": 3}
+
+
+def loop_valu_counts(asm: str) -> dict:
+    """{kernel name: [vector instructions of each innermost loop body]} from gfx950
+    assembly: a loop runs from its 'Inner Loop Header' label to the branch back to it."""
+    import re
+    out, fn, lines, i = {}, None, asm.split("\n"), 0
+    while i < len(lines):
+        f = re.match(r"^(_Z\w+):", lines[i])
+        if f:
+            fn = f.group(1)
+        m = re.match(r"^(\.LBB\w+):.*Inner Loop Header", lines[i])
+        if m and fn:
+            lab, n, j = m.group(1), 0, i + 1
+            while j < len(lines) and not re.match(r"^\s+s_cbranch\w*\s+" + re.escape(lab) + r"\s*$", lines[j]):
+                t = lines[j].split()
+                n += bool(t) and t[0].startswith("v_")
+                j += 1
+            out.setdefault(fn, []).append(n)
+            i = j
+        i += 1
+    return out
+
+
+def build_probe() -> str:
+    """libdust_probe.so (the vector-ALU issue-rate probes the benchmark times) and
+    libdust_probe.json (the vector instructions per loop trip of each probe, counted
+    from the same source's assembly)."""
+    import json
+    os.makedirs(BUILD, exist_ok=True)
+    asm = os.path.join(BUILD, "valu_mix.s")
+    r = subprocess.run([HIPCC, *CFLAGS, "--cuda-device-only", "-S", PROBE_SRC, "-o", asm], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed on {PROBE_SRC}:\n{r.stderr}")
+    counts = loop_valu_counts(open(asm).read())
+    per_mix = {}
+    for name, n in counts.items():
+        for k, mix in PROBE_KERNELS.items():
+            if k in name:
+                if len(n) != 1:
+                    raise RuntimeError(f"{k}: expected one loop, found {len(n)}")
+                per_mix[mix] = n[0]
+    if sorted(per_mix) != sorted(PROBE_KERNELS.values()):
+        raise RuntimeError(f"probe loops not found in the assembly: {counts}")
+    tmp = PROBE_LIB + ".tmp"
+    r = subprocess.run([HIPCC, *CFLAGS, "-shared", PROBE_SRC, "-o", tmp], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {PROBE_SRC}:\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    with open(PROBE_COUNTS, "w") as f:
+        json.dump({"valu_per_loop_trip": {str(k): v for k, v in sorted(per_mix.items())}}, f)
+    return PROBE_LIB
+
+
 if __name__ == "__main__":
     build(extra=sys.argv[1:], verbose=True)
+    build_probe()

@@ -56,7 +56,7 @@ constexpr size_t kAlign = 256;
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // Checks shared by the estimators.  Returns DUST_OK or a failure with message.
-dust_status check_common(int64_t T, int64_t K, float sigma, uint32_t token_offset, uint32_t draw_offset) {
+dust_status check_common(int64_t T, int64_t K, float sigma, uint64_t token_offset, uint32_t draw_offset) {
     if (T <= 0 || T > (int64_t)INT32_MAX) return fail(DUST_E_INVALID, "T must be in [1, 2^31): got %lld", (long long)T);
     if (K <= 0 || K > (int64_t)INT32_MAX) return fail(DUST_E_INVALID, "K must be in [1, 2^31): got %lld", (long long)K);
     if (!std::isfinite(sigma) || !(sigma > 0.f)) return fail(DUST_E_INVALID, "sigma must be finite and > 0: got %g", (double)sigma);
@@ -118,7 +118,7 @@ int dust_kernel_event_count(int kernel) {
     return kernel >= 0 && kernel < dust::kTimedKernels ? dust::g_kernel_events[kernel].count : -1;
 }
 
-dust_status dust_noise(uint64_t seed, uint32_t layer, uint32_t draw_offset, int64_t K, uint32_t token_offset,
+dust_status dust_noise(uint64_t seed, uint32_t layer, uint32_t draw_offset, int64_t K, uint64_t token_offset,
                        int64_t T, int64_t n, uint32_t* raw, float* gauss, void* stream) {
     if (!raw && !gauss) return fail(DUST_E_INVALID, "dust_noise: raw and gauss are both NULL");
     if (T <= 0 || K <= 0 || n <= 0) return fail(DUST_E_INVALID, "dust_noise: K, T, n must be >= 1");
@@ -127,9 +127,21 @@ dust_status dust_noise(uint64_t seed, uint32_t layer, uint32_t draw_offset, int6
     const int64_t threads = K * T * ((n + 3) / 4);
     if (K > (int64_t)INT32_MAX || T > (int64_t)INT32_MAX || threads > ((int64_t)1 << 32) - 256)
         return fail(DUST_E_UNSUPPORTED, "dust_noise: K*T*ceil(n/4) must stay below 2^32");
-    hipError_t e = dust::launch_noise_export(seed, layer, draw_offset, K, token_offset, T, n, raw, gauss,
+    hipError_t e = dust::launch_noise_export(seed, layer, draw_offset, K, (uint32_t)token_offset, T, n, raw, gauss,
                                              static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return device_fail("dust_noise launch", e);
+    return ok();
+}
+
+dust_status dust_debug_noise(uint64_t seed, uint32_t layer, uint32_t draw, uint64_t token, int64_t n,
+                             uint32_t* raw, float* gauss, void* stream) {
+    if (!raw && !gauss) return fail(DUST_E_INVALID, "dust_debug_noise: raw and gauss are both NULL");
+    if (n <= 0) return fail(DUST_E_INVALID, "dust_debug_noise: n must be >= 1");
+    if (token >= (1ull << 32)) return fail(DUST_E_INVALID, "dust_debug_noise: token must be below 2^32");
+    if (n > ((int64_t)1 << 32) - 1024) return fail(DUST_E_UNSUPPORTED, "dust_debug_noise: n too large");
+    hipError_t e = dust::launch_noise_export(seed, layer, draw, 1, (uint32_t)token, 1, n, raw, gauss,
+                                             static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_fail("dust_debug_noise launch", e);
     return ok();
 }
 
@@ -167,7 +179,7 @@ static bool head_pairs_path(int64_t T, int64_t V, int64_t d) { return dust::oute
 // g_hat = -(1/(K sigma)) sqrt(2 ln 2) sum r a'.
 static dust::HeadArgs head_args(const void* logits, const int32_t* labels, float* ghat, float* rewards, int64_t T,
                                 int64_t V, int64_t K, float sigma, const dust::HeadPlan& plan, uint64_t seed,
-                                uint32_t layer, uint32_t token_offset, uint32_t draw_offset) {
+                                uint32_t layer, uint64_t token_offset, uint32_t draw_offset) {
     dust::HeadArgs A{};
     A.logits = logits;
     A.labels = labels;
@@ -190,7 +202,7 @@ static dust::HeadArgs head_args(const void* logits, const int32_t* labels, float
     A.k0 = (uint32_t)seed;
     A.k1 = (uint32_t)(seed >> 32);
     A.layer = layer;
-    A.tok0 = token_offset;
+    A.tok0 = (uint32_t)token_offset;
     A.draw0 = draw_offset;
     return A;
 }
@@ -203,7 +215,7 @@ size_t dust_head_workspace_bytes(int64_t T, int64_t V, int64_t d, int64_t K) {
 
 dust_status dust_estimate_head(const void* logits, int logits_dtype, const float* x, const int32_t* labels,
                                int64_t T, int64_t V, int64_t d, int64_t K, float sigma, uint64_t seed,
-                               uint32_t layer, uint32_t token_offset, uint32_t draw_offset, float* grad_w,
+                               uint32_t layer, uint64_t token_offset, uint32_t draw_offset, float* grad_w,
                                float* ghat, float* rewards, void* workspace, size_t workspace_bytes,
                                void* stream) {
     if (!logits || !x || !labels || !grad_w)
@@ -271,7 +283,7 @@ size_t dust_head_subset_workspace_bytes(int64_t T, int64_t V, int64_t d, int64_t
 
 dust_status dust_estimate_head_subset(const void* logits, int logits_dtype, const float* x, const int32_t* labels,
                                       int64_t T, int64_t V, int64_t d, int64_t K, int64_t m, float sigma,
-                                      uint64_t seed, uint32_t layer, uint32_t token_offset, uint32_t draw_offset,
+                                      uint64_t seed, uint32_t layer, uint64_t token_offset, uint32_t draw_offset,
                                       float* grad_w, float* ghat, float* rewards, void* workspace,
                                       size_t workspace_bytes, void* stream) {
     if (m < 4 || m % 4 != 0)
@@ -338,7 +350,7 @@ size_t dust_linear_workspace_bytes(int64_t T, int64_t d, int64_t n, int64_t V, i
 dust_status dust_estimate_linear(const float* u, const float* h, const float* x_res, const uint16_t* w2,
                                  const uint16_t* w_head, const int32_t* labels, int64_t T, int64_t d, int64_t n,
                                  int64_t V, int64_t K, float sigma, float ln_eps, uint64_t seed, uint32_t layer,
-                                 uint32_t token_offset, uint32_t draw_offset, float* grad_w, float* ghat,
+                                 uint64_t token_offset, uint32_t draw_offset, float* grad_w, float* ghat,
                                  float* rewards, void* workspace, size_t workspace_bytes, void* stream) {
     if (!u || !h || !x_res || !w2 || !w_head || !labels || !grad_w)
         return fail(DUST_E_INVALID, "dust_estimate_linear: u, h, x_res, w2, w_head, labels and grad_w must be non-NULL");
@@ -355,6 +367,9 @@ dust_status dust_estimate_linear(const float* u, const float* h, const float* x_
     if (n % 32 != 0) return fail(DUST_E_UNSUPPORTED, "dust_estimate_linear: n must be a multiple of 32 (got %lld)", (long long)n);
     if (V > (int64_t)INT32_MAX / 2 || n > (int64_t)INT32_MAX / 4)
         return fail(DUST_E_UNSUPPORTED, "dust_estimate_linear: V or n too large");
+    if (V * d >= ((int64_t)1 << 31) || n * d >= ((int64_t)1 << 31))
+        return fail(DUST_E_UNSUPPORTED, "dust_estimate_linear: V*d and n*d must stay below 2^31 (W_head and W2 "
+                                        "element offsets are 32-bit)");
     if (T * (K + 1) > ((int64_t)1 << 40)) return fail(DUST_E_UNSUPPORTED, "dust_estimate_linear: T*(K+1) too large");
     const dust::MlpLayout L = dust::mlp_layout(T, d, n, V, K);
     if (workspace == nullptr || workspace_bytes < L.total)
@@ -382,7 +397,7 @@ dust_status dust_estimate_linear(const float* u, const float* h, const float* x_
     A.k0 = (uint32_t)seed;
     A.k1 = (uint32_t)(seed >> 32);
     A.layer = layer;
-    A.tok0 = token_offset;
+    A.tok0 = (uint32_t)token_offset;
     A.draw0 = draw_offset;
     A.stage_event = g_stage_event[0];
     A.gemm1_event = g_stage_event[2];
@@ -410,7 +425,7 @@ size_t dust_attn_v_workspace_bytes(int64_t T, int64_t S, int64_t d, int64_t H, i
 
 dust_status dust_estimate_attn(int proj, const float* q, const float* k, const float* v, const float* e,
                                const float* u, int64_t T, int64_t S, int64_t d, int64_t H, int64_t K, float sigma,
-                               uint64_t seed, uint32_t layer, uint32_t token_offset, uint32_t draw_offset,
+                               uint64_t seed, uint32_t layer, uint64_t token_offset, uint32_t draw_offset,
                                float* grad_w, float* ghat, float* rewards, void* workspace, size_t workspace_bytes,
                                void* stream) {
     if (proj != DUST_ATTN_Q && proj != DUST_ATTN_K && proj != DUST_ATTN_V)
@@ -442,11 +457,11 @@ dust_status dust_estimate_attn(int proj, const float* q, const float* k, const f
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     float* rew = rewards ? rewards : reinterpret_cast<float*>(ws + L.off_rew);
     float* g = ghat ? ghat : reinterpret_cast<float*>(ws + L.off_ghat);
-    hipError_t err = dust::launch_attn_rewards(proj, q, k, v, e, T, S, d, H, K, sigma, seed, layer, token_offset,
+    hipError_t err = dust::launch_attn_rewards(proj, q, k, v, e, T, S, d, H, K, sigma, seed, layer, (uint32_t)token_offset,
                                                draw_offset, rew, ws, L, st);
     if (err != hipSuccess) return device_fail("dust_estimate_attn: attention passes", err);
     if ((err = record_stage(2, st)) != hipSuccess) return device_fail("dust_estimate_attn: stage event", err);
-    err = dust::launch_attn_v_ghat(T, d, K, sigma, seed, layer, token_offset, draw_offset, rew, g, st);
+    err = dust::launch_attn_v_ghat(T, d, K, sigma, seed, layer, (uint32_t)token_offset, draw_offset, rew, g, st);
     if (err != hipSuccess) return device_fail("dust_estimate_attn: reduction launch", err);
     if ((err = record_stage(0, st)) != hipSuccess) return device_fail("dust_estimate_attn: stage event", err);
     err = dust::launch_outer(g, u, T, d, d, grad_w, ws + L.off_outer, L.total - L.off_outer, st, false);
@@ -457,7 +472,7 @@ dust_status dust_estimate_attn(int proj, const float* q, const float* k, const f
 
 dust_status dust_estimate_attn_v(const float* q, const float* k, const float* e, const float* u, int64_t T,
                                  int64_t S, int64_t d, int64_t H, int64_t K, float sigma, uint64_t seed,
-                                 uint32_t layer, uint32_t token_offset, uint32_t draw_offset, float* grad_w,
+                                 uint32_t layer, uint64_t token_offset, uint32_t draw_offset, float* grad_w,
                                  float* ghat, float* rewards, void* workspace, size_t workspace_bytes,
                                  void* stream) {
     return dust_estimate_attn(DUST_ATTN_V, q, k, nullptr, e, u, T, S, d, H, K, sigma, seed, layer, token_offset,

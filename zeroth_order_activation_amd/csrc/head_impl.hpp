@@ -31,6 +31,7 @@
 
 #include "dust_device.hpp"
 #include "dust_internal.hpp"
+#include "launch_events.hpp"
 
 namespace dust {
 
@@ -384,8 +385,12 @@ hipError_t launch_head_variant(const HeadPlan& plan, const HeadArgs& args, hipSt
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)plan.lds);
         if (e != hipSuccess) return e;
     }
+    bool timed = false;
+    hipError_t e = launch_timer_begin(kTimedHead, stream, timed);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(args.T), dim3(NT), plan.lds, stream, args);
-    return hipGetLastError();
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return launch_timer_end(kTimedHead, stream, timed);
 }
 
 // Dispatch over the compiled variants for one logits type.

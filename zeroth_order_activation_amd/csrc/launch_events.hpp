@@ -7,7 +7,16 @@
 namespace dust {
 
 // kernels that can be timed launch by launch
-enum TimedKernel { kTimedLmGemm = 0, kTimedLmHead = 1, kTimedAttnMain = 2, kTimedKernels = 3 };
+enum TimedKernel {
+    kTimedLmGemm = 0,
+    kTimedLmHead = 1,
+    kTimedAttnMain = 2,
+    kTimedMlpGemm1 = 3,
+    kTimedMlpGemm2 = 4,
+    kTimedHead = 5,
+    kTimedOuter = 6,
+    kTimedKernels = 7
+};
 
 struct LaunchEvents {
     hipEvent_t* starts = nullptr;

@@ -29,6 +29,7 @@
 // D[i][j] in lane j + 32*((i/4)%2), register (i%4) + 4*(i/8).
 #include "dust_device.hpp"
 #include "dust_internal.hpp"
+#include "launch_events.hpp"
 
 namespace dust {
 
@@ -637,16 +638,21 @@ hipError_t launch_mlp(const MlpArgs& A, const MlpLayout& L, unsigned char* ws, f
     for (int64_t g0 = 0; g0 < total; g0 += L.chunk) {
         const int64_t nrows = (total - g0) < L.chunk ? (total - g0) : L.chunk;
         const unsigned b1 = (unsigned)((nrows + G1_ROWS - 1) / G1_ROWS);
+        bool timed = false;
+        if ((e = launch_timer_begin(kTimedMlpGemm1, stream, timed)) != hipSuccess) return e;
         if (A.d == 512)
             hipLaunchKernelGGL(mlp_gemm1_kernel<512>, dim3(b1), dim3(G1_NT), 0, stream, A, g0, nrows, F);
         else
             hipLaunchKernelGGL(mlp_gemm1_kernel<256>, dim3(b1), dim3(G1_NT), 0, stream, A, g0, nrows, F);
         if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = launch_timer_end(kTimedMlpGemm1, stream, timed)) != hipSuccess) return e;
         if (A.gemm1_event && (e = hipEventRecord(A.gemm1_event, stream)) != hipSuccess) return e;
         const int64_t nrt = (nrows + G2_TR - 1) / G2_TR;
+        if ((e = launch_timer_begin(kTimedMlpGemm2, stream, timed)) != hipSuccess) return e;
         hipLaunchKernelGGL(mlp_gemm2_kernel, dim3((unsigned)(nrt * L.nvt)), dim3(G2_NT), 0, stream, A, g0, nrows,
                            L.nvt, F, part, zy, offset);
         if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = launch_timer_end(kTimedMlpGemm2, stream, timed)) != hipSuccess) return e;
         if (A.gemm2_event && (e = hipEventRecord(A.gemm2_event, stream)) != hipSuccess) return e;
         hipLaunchKernelGGL(mlp_combine_kernel, dim3((unsigned)((nrows + 255) / 256)), dim3(256), 0, stream, g0, nrows,
                            L.nvt, part, zy, ce);

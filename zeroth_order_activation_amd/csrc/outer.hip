@@ -25,6 +25,7 @@
 
 #include "dust_device.hpp"
 #include "dust_internal.hpp"
+#include "launch_events.hpp"
 
 namespace dust {
 
@@ -465,9 +466,12 @@ hipError_t launch_outer(const float* ghat, const float* x, int64_t T, int64_t n,
         const int64_t nnt = (d + YT - 1) / YT, nmt = (n + YT - 1) / YT;
         const int64_t nmt8 = (p.mA + 7) / 8 * 8;  // M-tiles rounded up to whole XCD groups
         const dim3 grid((unsigned)(nmt8 * nnt), 1, (unsigned)p.splits);
+        bool timed = false;
+        if ((e = launch_timer_begin(kTimedOuter, stream, timed)) != hipSuccess) return e;
         hipLaunchKernelGGL(outer_x3_kernel, grid, dim3(YNT), 0, stream, ah, al, bh, bl, std::min(n, p.mA * YT), d, p.Mp,
                            p.Np, p.Tp, p.tchunk, part, (int64_t)0, n * d, (int64_t)0);
         if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = launch_timer_end(kTimedOuter, stream, timed)) != hipSuccess) return e;
         if (p.mA < nmt) {  // the last round's M-tiles, their tokens split
             float* tpart = reinterpret_cast<float*>(ws + p.off_tail);
             const int64_t rows = n - p.mA * YT, tcount = rows * d;
