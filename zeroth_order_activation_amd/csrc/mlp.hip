@@ -233,11 +233,13 @@ __global__ void __launch_bounds__(G1_NT, 1) mlp_gemm1_kernel(MlpArgs A, int64_t 
 
     // ---- epilogue: residual add, LayerNorm over D, bf16 ---------------------
     // lane holds rows j = row0 + rb*32 + lane%32; for each, features
-    // fg*32 + drow(r, lane).  y = x + o is formed in fp32; the LayerNorm
-    // statistics and the normalised value are computed in fp64 and rounded to
-    // fp32 once before the bf16 rounding.  The reduction buffer reuses the slabs.
+    // fg*32 + drow(r, lane).  y = x + o, the LayerNorm statistics and the
+    // normalised value are computed in fp64 and rounded to fp32 once before the
+    // bf16 rounding: an fp32 y would carry half an ulp of y into (y - mean),
+    // which for entries near the mean decides their bf16 rounding far more often
+    // than the accumulation error of o does.  The reduction buffer reuses the slabs.
     double* red = reinterpret_cast<double*>(&Bs[0][0]);   // [G1_WAVES][G1_ROWS]
-    float y[RB][16];
+    double y[RB][16];
     double s[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -250,12 +252,12 @@ __global__ void __launch_bounds__(G1_NT, 1) mlp_gemm1_kernel(MlpArgs A, int64_t 
             const float4 o = tot[rb * 4 + r4][tid];
             const int ff = fg * 32 + 8 * r4 + 4 * (lane >> 5);
             const float4 xv = *reinterpret_cast<const float4*>(A.x_res + t * D + ff);
-            y[rb][4 * r4 + 0] = o.x + xv.x;
-            y[rb][4 * r4 + 1] = o.y + xv.y;
-            y[rb][4 * r4 + 2] = o.z + xv.z;
-            y[rb][4 * r4 + 3] = o.w + xv.w;
+            y[rb][4 * r4 + 0] = (double)o.x + (double)xv.x;
+            y[rb][4 * r4 + 1] = (double)o.y + (double)xv.y;
+            y[rb][4 * r4 + 2] = (double)o.z + (double)xv.z;
+            y[rb][4 * r4 + 3] = (double)o.w + (double)xv.w;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) s[rb] += (double)y[rb][4 * r4 + c];
+            for (int c = 0; c < 4; ++c) s[rb] += y[rb][4 * r4 + c];
         }
         s[rb] += __shfl_xor(s[rb], 32, 64);
     }
@@ -280,7 +282,7 @@ __global__ void __launch_bounds__(G1_NT, 1) mlp_gemm1_kernel(MlpArgs A, int64_t 
         double v = 0.0;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const double dv = (double)y[rb][r] - mean[rb];
+            const double dv = y[rb][r] - mean[rb];
             v = fma(dv, dv, v);
         }
         v += __shfl_xor(v, 32, 64);
@@ -300,7 +302,7 @@ __global__ void __launch_bounds__(G1_NT, 1) mlp_gemm1_kernel(MlpArgs A, int64_t 
             const int ff = fg * 32 + 8 * r4 + 4 * (lane >> 5);
             float o[4];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) o[c] = (float)(((double)y[rb][4 * r4 + c] - mean[rb]) * rstd);
+            for (int c = 0; c < 4; ++c) o[c] = (float)((y[rb][4 * r4 + c] - mean[rb]) * rstd);
             *reinterpret_cast<uint2*>(frow + ff) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
         }
     }
