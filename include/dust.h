@@ -169,6 +169,25 @@ dust_status dust_estimate_head(const void *logits, int logits_dtype, const float
                                void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * dust_estimate_head without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, outputs, checks and kernels as
+ * dust_estimate_head; its scratch is a static device array of the library, one per GPU,
+ * of dust_head_noalloc_max_bytes() bytes (64 MiB), held from the library's first use of
+ * that GPU until the process ends.  The call allocates nothing (no hipMalloc, no
+ * allocating library routine).  A shape whose dust_head_workspace_bytes exceeds that
+ * size (ignoring the g_hat rows when `ghat` is passed) is rejected with
+ * DUST_E_UNSUPPORTED before anything is enqueued.  Calls on one GPU share the array:
+ * calls that overlap on one GPU (other streams, other threads) race; serialize them.
+ */
+dust_status dust_estimate_head_noalloc(const void *logits, int logits_dtype, const float *x,
+                                       const int32_t *labels, int64_t T, int64_t V, int64_t d,
+                                       int64_t K, float sigma, uint64_t seed, uint32_t layer,
+                                       uint64_t token_offset, uint32_t draw_offset,
+                                       float *grad_w, float *ghat, float *rewards, void *stream);
+size_t dust_head_noalloc_max_bytes(void);
+
+/*
  * Vocabulary-subset LM-head estimator (TL;DR page, section 1, "reducing
  * interference": the head is evaluated on part of the vocabulary per draw).
  * The pages give no subset rule.  Here, per (token, draw), the perturbed set S is

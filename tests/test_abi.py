@@ -156,6 +156,21 @@ def test_linear_rejects_oversized_weights_on_host():
     assert st == 3, err
 
 
+def test_head_noalloc_rejects_on_host():
+    L = dust.lib()
+    assert L.dust_head_noalloc_max_bytes() == 64 << 20
+
+    def call(T, V, d, ghat=None, logits=FAKE):
+        st = L.dust_estimate_head_noalloc(logits, 1, FAKE, FAKE, T, V, d, 4, ctypes.c_float(0.01), 1, 1, 0, 0, FAKE,
+                                          ghat, None, None)
+        return st, L.dust_last_error().decode()
+
+    st, err = call(4096, 8192, 512)  # 128 MiB of g_hat rows alone
+    assert st == 2 and "static scratch" in err, err
+    st, err = call(4, 8, 2, logits=None)
+    assert st == 1 and "non-NULL" in err, err
+
+
 def test_workspace_queries():
     L = dust.lib()
     # large product (bf16-pair outer product): the estimator writes the g_hat

@@ -63,6 +63,11 @@ def lib():
         L.dust_estimate_head.restype = ctypes.c_int
         L.dust_estimate_head.argtypes = [_vp, ctypes.c_int, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _u64, _u32,
                                          _u64, _u32, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.dust_estimate_head_noalloc.restype = ctypes.c_int
+        L.dust_estimate_head_noalloc.argtypes = [_vp, ctypes.c_int, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _u64,
+                                                 _u32, _u64, _u32, _vp, _vp, _vp, _vp]
+        L.dust_head_noalloc_max_bytes.restype = ctypes.c_size_t
+        L.dust_head_noalloc_max_bytes.argtypes = []
         L.dust_head_subset_workspace_bytes.restype = ctypes.c_size_t
         L.dust_head_subset_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64]
         L.dust_estimate_head_subset.restype = ctypes.c_int
@@ -252,6 +257,30 @@ def estimate_head(logits, x, labels, K: int, sigma: float, seed: int, layer: int
                                     token_offset, draw_offset, _p(grad_w), _p(ghat), _p(rewards), _p(ws), nb,
                                     _stream(logits)))
     return grad_w
+
+
+def estimate_head_noalloc(logits, x, labels, K: int, sigma: float, seed: int, layer: int,
+                          token_offset: int = 0, draw_offset: int = 0, *, grad_w, ghat=None, rewards=None):
+    """dust_estimate_head_noalloc: the LM-head estimator with the library's static
+    scratch instead of a workspace.  The caller passes every output (``grad_w`` [V,d]
+    and optionally ``ghat`` [T,V], ``rewards`` [K,T]); nothing is allocated here."""
+    _dev_tensor(logits, "logits", (torch.float32, torch.bfloat16))
+    _dev_tensor(x, "x", (torch.float32,))
+    _dev_tensor(labels, "labels", (torch.int32,))
+    _dev_tensor(grad_w, "grad_w", (torch.float32,))
+    T, V = logits.shape
+    d = x.shape[1]
+    if x.shape[0] != T or labels.numel() != T or tuple(grad_w.shape) != (V, d):
+        raise ValueError("logits, x, labels and grad_w disagree on T, V or d")
+    dt = F32 if logits.dtype == torch.float32 else BF16
+    _check(lib().dust_estimate_head_noalloc(_p(logits), dt, _p(x), _p(labels), T, V, d, K, sigma, seed, layer,
+                                            token_offset, draw_offset, _p(grad_w), _p(ghat), _p(rewards),
+                                            _stream(logits)))
+    return grad_w
+
+
+def head_noalloc_max_bytes() -> int:
+    return int(lib().dust_head_noalloc_max_bytes())
 
 
 def head_subset_workspace_bytes(T: int, V: int, d: int, K: int) -> int:

@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -80,6 +81,39 @@ dust_status check_labels(const int32_t* labels, int64_t T, int64_t V, hipStream_
 }
 
 size_t head_ghat_bytes(int64_t T, int64_t V) { return round_up((size_t)T * (size_t)V * sizeof(float)); }
+
+}  // namespace
+
+// Scratch of dust_estimate_head_noalloc: one array per GPU, part of the code object,
+// so no call allocates.  Host code never uses the array's name as an address (on the
+// host it is only a stand-in for the symbol); it uses the device address that
+// hipGetSymbolAddress returns, fetched once per device with that device current.
+#define DUST_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+static __device__ __align__(256) unsigned char scratch[DUST_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first call there).
+dust_status scratch_for_current_device(const char* fn, void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return device_fail(fn, e);
+    if (dev < 0 || dev >= kMaxDevices) return fail(DUST_E_UNSUPPORTED, "%s: device %d beyond %d", fn, dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return device_fail("hipGetSymbolAddress(scratch)", e);
+        if (!p) return fail(DUST_E_DEVICE, "%s: hipGetSymbolAddress(scratch) gave NULL", fn);
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return DUST_OK;
+}
 
 }  // namespace
 
@@ -213,25 +247,45 @@ size_t dust_head_workspace_bytes(int64_t T, int64_t V, int64_t d, int64_t K) {
     return (head_pairs_path(T, V, d) ? 0 : head_ghat_bytes(T, V)) + dust::outer_workspace_bytes(T, V, d);
 }
 
+// The host checks of dust_estimate_head (and of its no-allocation variant), in order;
+// `fn` names the entry point in the messages.  Touches no device.
+static dust_status head_checks(const char* fn, const void* logits, int logits_dtype, const float* x,
+                               const int32_t* labels, int64_t T, int64_t V, int64_t d, int64_t K, float sigma,
+                               uint64_t token_offset, uint32_t draw_offset, const float* grad_w, const float* ghat,
+                               const float* rewards, const void* workspace, dust::HeadPlan* plan) {
+    if (!logits || !x || !labels || !grad_w)
+        return fail(DUST_E_INVALID, "%s: logits, x, labels and grad_w must be non-NULL", fn);
+    if (logits_dtype != DUST_F32 && logits_dtype != DUST_BF16)
+        return fail(DUST_E_UNSUPPORTED, "%s: logits_dtype %d is not DUST_F32 or DUST_BF16", fn, logits_dtype);
+    if (!aligned16(logits) || !aligned16(x) || !aligned16(labels) || !aligned16(grad_w) ||
+        (ghat && !aligned16(ghat)) || (rewards && !aligned16(rewards)) || (workspace && !aligned16(workspace)))
+        return fail(DUST_E_INVALID, "%s: every pointer must be 16-byte aligned", fn);
+    dust_status s = check_common(T, K, sigma, token_offset, draw_offset);
+    if (s != DUST_OK) return s;
+    if (V <= 0) return fail(DUST_E_INVALID, "%s: V must be >= 1", fn);
+    if (d <= 0) return fail(DUST_E_INVALID, "%s: d must be >= 1", fn);
+    if (V > 65535LL * 128 || d > 65535LL * 128) return fail(DUST_E_UNSUPPORTED, "%s: V or d too large", fn);
+    *plan = dust::plan_head(V, logits_dtype, sigma);
+    if (!plan->ok) return fail(DUST_E_UNSUPPORTED, "%s: %s", fn, plan->why);
+    return DUST_OK;
+}
+
+// Workspace bytes one dust_estimate_head call needs (the g_hat rows only when the
+// caller passes no ghat and the outer product does not take the bf16-pair path).
+static size_t head_need_bytes(int64_t T, int64_t V, int64_t d, bool have_ghat) {
+    const size_t ghat_ws = (have_ghat || head_pairs_path(T, V, d)) ? 0 : head_ghat_bytes(T, V);
+    return ghat_ws + dust::outer_workspace_bytes(T, V, d);
+}
+
 dust_status dust_estimate_head(const void* logits, int logits_dtype, const float* x, const int32_t* labels,
                                int64_t T, int64_t V, int64_t d, int64_t K, float sigma, uint64_t seed,
                                uint32_t layer, uint64_t token_offset, uint32_t draw_offset, float* grad_w,
                                float* ghat, float* rewards, void* workspace, size_t workspace_bytes,
                                void* stream) {
-    if (!logits || !x || !labels || !grad_w)
-        return fail(DUST_E_INVALID, "dust_estimate_head: logits, x, labels and grad_w must be non-NULL");
-    if (logits_dtype != DUST_F32 && logits_dtype != DUST_BF16)
-        return fail(DUST_E_UNSUPPORTED, "dust_estimate_head: logits_dtype %d is not DUST_F32 or DUST_BF16", logits_dtype);
-    if (!aligned16(logits) || !aligned16(x) || !aligned16(labels) || !aligned16(grad_w) ||
-        (ghat && !aligned16(ghat)) || (rewards && !aligned16(rewards)) || (workspace && !aligned16(workspace)))
-        return fail(DUST_E_INVALID, "dust_estimate_head: every pointer must be 16-byte aligned");
-    dust_status s = check_common(T, K, sigma, token_offset, draw_offset);
+    dust::HeadPlan plan{};
+    dust_status s = head_checks("dust_estimate_head", logits, logits_dtype, x, labels, T, V, d, K, sigma,
+                                token_offset, draw_offset, grad_w, ghat, rewards, workspace, &plan);
     if (s != DUST_OK) return s;
-    if (V <= 0) return fail(DUST_E_INVALID, "dust_estimate_head: V must be >= 1");
-    if (d <= 0) return fail(DUST_E_INVALID, "dust_estimate_head: d must be >= 1");
-    if (V > 65535LL * 128 || d > 65535LL * 128) return fail(DUST_E_UNSUPPORTED, "dust_estimate_head: V or d too large");
-    const dust::HeadPlan plan = dust::plan_head(V, logits_dtype, sigma);
-    if (!plan.ok) return fail(DUST_E_UNSUPPORTED, "dust_estimate_head: %s", plan.why);
 
     const bool pairs = head_pairs_path(T, V, d);
     const size_t ghat_ws = (ghat || pairs) ? 0 : head_ghat_bytes(T, V);
@@ -266,6 +320,29 @@ dust_status dust_estimate_head(const void* logits, int logits_dtype, const float
     if ((e = record_stage(1, st)) != hipSuccess) return device_fail("dust_estimate_head: stage event", e);
     return ok();
 }
+
+dust_status dust_estimate_head_noalloc(const void* logits, int logits_dtype, const float* x, const int32_t* labels,
+                                       int64_t T, int64_t V, int64_t d, int64_t K, float sigma, uint64_t seed,
+                                       uint32_t layer, uint64_t token_offset, uint32_t draw_offset, float* grad_w,
+                                       float* ghat, float* rewards, void* stream) {
+    const char* fn = "dust_estimate_head_noalloc";
+    dust::HeadPlan plan{};
+    dust_status s = head_checks(fn, logits, logits_dtype, x, labels, T, V, d, K, sigma, token_offset, draw_offset,
+                                grad_w, ghat, rewards, nullptr, &plan);
+    if (s != DUST_OK) return s;
+    const size_t need = head_need_bytes(T, V, d, ghat != nullptr);
+    if (need > DUST_NOALLOC_SCRATCH_BYTES)
+        return fail(DUST_E_UNSUPPORTED, "%s: this shape needs %zu bytes of scratch; the static scratch holds %zu "
+                    "(use dust_estimate_head with a workspace)", fn, need, DUST_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if ((s = scratch_for_current_device(fn, &ws)) != DUST_OK) return s;
+    // Nothing in the workspace has to start at zero: every byte the kernels read is
+    // written earlier in the same call (as for a workspace fresh from an allocator).
+    return dust_estimate_head(logits, logits_dtype, x, labels, T, V, d, K, sigma, seed, layer, token_offset,
+                              draw_offset, grad_w, ghat, rewards, ws, DUST_NOALLOC_SCRATCH_BYTES, stream);
+}
+
+size_t dust_head_noalloc_max_bytes(void) { return DUST_NOALLOC_SCRATCH_BYTES; }
 
 // bytes of K*T floats or ints, padded to 256
 static size_t kt_bytes(int64_t T, int64_t K) { return ((size_t)T * (size_t)K * 4 + 255) & ~(size_t)255; }
