@@ -86,7 +86,23 @@ def test_linear_small_cases(T, d, n, V, K, sigma):
     assert e_go < TOL_GW and e_wo < TOL_GW
 
 
-@pytest.mark.parametrize("wid,K,ntok", [(3, 64, 16), (5, 256, 4), (5, 1024, 8), (5, 4096, 3), (5, 16384, 2)])
+def test_workload3_whole():
+    """The MLP-linear workload at full size in the benchmark's configuration: every
+    reward, every g_hat row and the whole G_W against the oracle run on all tokens."""
+    c = synth.workload(3)
+    K, sigma = c["K"], c["sigma"]
+    print("workload 3: GPU estimate", flush=True)
+    gw, ghat, rew = _run(c, K, sigma, c["seed_noise"], c["layer"])
+    print("workload 3: oracle on every token", flush=True)
+    og, orew, oce0 = _oracle(c, K, sigma, c["seed_noise"], c["layer"])
+    st = check_quantized_rewards(rew.cpu().numpy(), orew, oce0)
+    e_go = rel_l2(ghat.cpu().numpy(), og)
+    e_wo = rel_l2(gw.cpu().numpy(), oracle.grad_w(og, c["u"]))
+    print(f"workload 3 K={K}: rewards {st}; g_hat vs oracle {e_go:.2e}; grad_w vs oracle {e_wo:.2e}")
+    assert e_go < TOL_GW and e_wo < TOL_GW
+
+
+@pytest.mark.parametrize("wid,K,ntok", [(5, 256, 16), (5, 1024, 8), (5, 4096, 3), (5, 16384, 2)])
 def test_named_workload_full_size(wid, K, ntok):
     """Full-size workload in the benchmark's configuration; sampled tokens against the
     oracle (every draw of each), all grad_w rows against the identity G_W = G^T U, and

@@ -96,6 +96,16 @@ __device__ __forceinline__ f32x4 gauss4(uint32_t token, uint32_t quad, uint32_t 
     return a;
 }
 
+// The Gaussians divided by sqrt(2 ln 2) (any counter).
+__device__ __forceinline__ f32x4 gauss4_unscaled(uint32_t token, uint32_t quad, uint32_t draw, uint32_t layer,
+                                                 uint32_t k0, uint32_t k1) {
+    const u32x4 w = philox4x32_10(token, quad, draw, layer, k0, k1);
+    f32x4 a;
+    box_muller_unscaled(w.x, w.y, a.v[0], a.v[1]);
+    box_muller_unscaled(w.z, w.w, a.v[2], a.v[3]);
+    return a;
+}
+
 // The same Gaussians divided by sqrt(2 ln 2), for a wave whose token, draw and
 // layer are uniform.
 __device__ __forceinline__ f32x4 gauss4_unscaled_uniform(uint32_t token, uint32_t quad, uint32_t draw,

@@ -309,6 +309,401 @@ __global__ void __launch_bounds__(G1_NT, 1) mlp_gemm1_kernel(MlpArgs A, int64_t 
 }
 
 // ---------------------------------------------------------------------------
+// gemm1, Taylor form (small sigma).  The same F = bf16(LN(x + W2 bf16(GELU(h~))))
+// with h~ = h + sigma a, for the draw rows, but GELU(h~) = h~ Phi(h~) is formed
+// from the token's cached Phi(h), phi(h) (computed once per call, in fp64, by
+// mlp_phi_kernel) through the exact identity
+//     Phi(h + delta) - Phi(h) = phi(h) I(h, delta),  I = int_0^delta exp(-h s - s^2/2) ds,
+// with I by its Taylor series to delta^5:
+//     I = delta (1 + delta (e1 + delta (e2 + delta (e3 + delta e4)))),
+//     e1 = -h/2, e2 = (h^2 - 1)/6, e3 = -h (h^2 - 3)/24, e4 = (h^4 - 6 h^2 + 3)/120.
+// The host takes this form when |delta| <= sigma sqrt(48 ln 2) <= 1/16; then for
+// h >= -3.5 the dropped delta^6 term is below one fp32 ulp of Phi(h~) and the
+// fp32 value of GELU(h~) is within 3 ulps of the exact one.  Entries within 8 ulps
+// of a bf16 tie, and entries with h < -3.5 (Phi small), are re-evaluated in fp64
+// as 0.5 h~ (1 + erf(h~/sqrt 2)), so every bf16 decision is the one the exactly
+// rounded GELU takes.  Per entry this costs about a dozen VALU operations where
+// the library erf costs about forty.
+//
+// Workgroup: 64 rows = 8 tokens x 8 draws, all D features, 16 waves (4 per SIMD)
+// in two roles, so that neither pays for the other's registers: waves 0-7 run the
+// MFMAs (wave c owns features [c D/8, (c+1) D/8) of every row), waves 8-15 make the
+// B operand.  A k-step's slab (64 rows x 128 channels, bf16, double-buffered in
+// LDS) is generated by wave 8 + p for token p: lane l makes channel quad l%32 for
+// the 4 draws of parity l/32, two at a time (their Philox chains run side by
+// side), and the cached h, Phi(h), phi(h) and the series coefficients of that quad
+// serve all of them.  While the MFMA waves multiply slab k, the generation waves
+// make slab k+1; each SIMD holds two waves of each role, so the MFMAs of one run
+// under the VALU work of the other.  W2 is read in MFMA fragment order
+// (mlp_w2frag_kernel), one contiguous 1 KB per wave and fragment.  The accumulator
+// is added into an fp32 running total in LDS every 128 channels; the epilogue is
+// mlp_gemm1_kernel's fp64 residual and LayerNorm.
+// ---------------------------------------------------------------------------
+constexpr int GT_TB = 8;          // tokens per workgroup
+constexpr int GT_DB = 8;          // draws per workgroup
+constexpr int GT_ROWS = GT_TB * GT_DB;
+constexpr int GT_KS = 128;        // channels per k-step (32 quads)
+constexpr float GT_FAR = -3.5f;   // h below this: fp64 evaluation
+constexpr double GT_MAX_DELTA = 0.0625;
+
+bool mlp_taylor_ok(float sigma) { return (double)sigma * 5.7683 <= GT_MAX_DELTA; }
+
+// Phi(h), phi(h) of every cached entry, in fp64, rounded to fp32 once.
+__global__ void __launch_bounds__(256) mlp_phi_kernel(const float* __restrict__ h, int64_t count,
+                                                      float* __restrict__ Pt, float* __restrict__ pt) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= count) return;
+    const double x = (double)h[i];
+    Pt[i] = (float)(0.5 * erfc(-x * 0.70710678118654752440));
+    pt[i] = (float)(exp(-0.5 * x * x) * 0.39894228040143267794);
+}
+
+// W2 [D][n] bf16 -> fragment order [D/32][n/16][64 lanes][8]: lane l of the A
+// fragment of feature block fb, sub-step s holds W2[32 fb + l%32][16 s + 8 (l/32) .. +8].
+__global__ void __launch_bounds__(256) mlp_w2frag_kernel(const uint16_t* __restrict__ w2, int D, int n,
+                                                         uint16_t* __restrict__ w2f) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // one 16-byte piece
+    const int nsub = n / 16;
+    if (i >= (int64_t)(D / 32) * nsub * 64) return;
+    const int lane = (int)(i & 63);
+    const int64_t fs = i >> 6;
+    const int s = (int)(fs % nsub), fb = (int)(fs / nsub);
+    const int f = fb * 32 + (lane & 31);
+    const int c = s * 16 + 8 * (lane >> 5);
+    *reinterpret_cast<uint4*>(w2f + i * 8) = *reinterpret_cast<const uint4*>(w2 + (int64_t)f * n + c);
+}
+
+// GELU of one entry in fp64, rounded to fp32 once (the rare exact path).
+__device__ __attribute__((noinline)) float gelu_exact(float x) {
+    const double xd = (double)x;
+    return (float)(0.5 * xd * (1.0 + erf(xd * 0.70710678118654752440)));
+}
+
+// Slab layout: 64 rows of 128 bf16 (16 pieces of 16 bytes); piece p of row r is
+// stored at p ^ (r & 15): sixteen lanes reading one piece of sixteen consecutive
+// rows, and sixteen lanes writing the 16 pieces of one row, touch every bank once.
+__device__ __forceinline__ int gt_swz(int row, int piece) { return row * GT_KS + ((piece ^ (row & 15)) << 3); }
+
+template <int D>
+__global__ void __launch_bounds__(1024, 1) mlp_gemm1t_kernel(MlpArgs A, float sig_u, const uint16_t* __restrict__ w2f,
+                                                            const float* __restrict__ Pt, const float* __restrict__ pt,
+                                                            int64_t g0, int first_slot, int nslots, int ntiles,
+                                                            uint16_t* __restrict__ F) {
+    constexpr int NC = 8;                       // MFMA waves (waves 0-7); waves 8-15 generate
+    constexpr int FB = D / 256;                 // 32-feature blocks per MFMA wave (2 or 1)
+    constexpr int NV = FB * 2 * 16;             // accumulator values per MFMA lane
+    constexpr int FLUSH = 1;                    // k-steps (128 channels) per accumulator restart
+    __shared__ __align__(16) uint16_t Bs[2][GT_ROWS * GT_KS];   // 2 x 16 KB
+    __shared__ __align__(16) float4 tot[NV / 4][NC * 64];       // running totals, lane-interleaved
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const bool mfma_wave = w < NC;              // wave-uniform role
+    const int T = A.T, n = A.n;
+    // tiles (token block, draw block), draw block fastest; each XCD (workgroup id
+    // mod 8) takes a contiguous run of tiles, so the draw blocks of a token block
+    // share that XCD's L2 for the token's h, Phi(h), phi(h)
+    const int per_xcd = (ntiles + 7) / 8;
+    const int tile = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+    if (tile >= ntiles) return;
+    const int nsb = (nslots + GT_DB - 1) / GT_DB;
+    const int tb = tile / nsb, sb = tile % nsb;
+    const int slot_base = sb * GT_DB;           // first draw slot of this tile (launch-relative)
+    const int nks = (n + GT_KS - 1) / GT_KS;
+    const int nfull = n / GT_KS;
+
+    // ===== generation waves: wave 8 + p makes token tb*8 + p; lane l channel quad
+    //       l%32 of each k-step for the draws of parity l/32, two at a time ======
+    const int pw = w - NC;
+    const int gt = tb * GT_TB + (pw & 7);
+    const bool tok_ok = gt < T;
+    const int tt = tok_ok ? gt : T - 1;
+    const int gq = lane & 31, par = lane >> 5;
+    const float* hrow = A.h + (int64_t)tt * n;
+    const float* Prow = Pt + (int64_t)tt * n;
+    const float* prow = pt + (int64_t)tt * n;
+    const uint32_t tok = A.tok0 + (uint32_t)tt;
+    const int64_t slot_g0 = g0 / T + first_slot + slot_base;   // g / T of the tile's draw slot 0
+    struct In { float4 h, P, p; };
+    auto load_in = [&](int ks) -> In {
+        int c0 = ks * GT_KS + 4 * gq;
+        c0 = c0 < n ? c0 : n - 4;
+        return In{*reinterpret_cast<const float4*>(hrow + c0), *reinterpret_cast<const float4*>(Prow + c0),
+                  *reinterpret_cast<const float4*>(prow + c0)};
+    };
+    // the generation state of one k-step: per channel h, Phi, phi, the series
+    // coefficients, and which entries take the fp64 path whatever the draw
+    float gh[4], gP[4], gp[4], e1[4], e2[4], e3[4], e4[4];
+    uint32_t far_mask = 0;
+    bool gen_live = false;
+    auto setup = [&](int ks, const In& in) {
+        const float hv[4] = {in.h.x, in.h.y, in.h.z, in.h.w};
+        const float Pv[4] = {in.P.x, in.P.y, in.P.z, in.P.w};
+        const float pv[4] = {in.p.x, in.p.y, in.p.z, in.p.w};
+        far_mask = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float x = hv[c], x2 = x * x;
+            gh[c] = x; gP[c] = Pv[c]; gp[c] = pv[c];
+            e1[c] = -0.5f * x;
+            e2[c] = fmaf(x2, 1.0f / 6.0f, -1.0f / 6.0f);
+            e3[c] = x * fmaf(x2, -1.0f / 24.0f, 3.0f / 24.0f);
+            e4[c] = fmaf(x2, fmaf(x2, 1.0f / 120.0f, -6.0f / 120.0f), 3.0f / 120.0f);
+            far_mask |= (x < GT_FAR ? 1u : 0u) << c;
+        }
+        gen_live = tok_ok && ks * GT_KS + 4 * gq < n;
+    };
+    // draws j + par and j + 2 + par of the lane's quad (two Philox chains side by
+    // side): rows (draw, token) of slab buf
+    auto gen_pair = [&](int ks, int j, int buf) {
+        const uint32_t q = (uint32_t)(ks * (GT_KS / 4) + gq);
+        f32x4 a[2];
+        float v[2][4];
+        bool slow = far_mask != 0;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const uint32_t draw = A.draw0 + (uint32_t)(slot_g0 + j + 2 * k + par - 1);
+            a[k] = gauss4_unscaled(tok, q, draw, A.layer, A.k0, A.k1);
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const float ht = fmaf(sig_u, a[k].v[c], gh[c]);   // the noise is drawn divided by sqrt(2 ln 2)
+                const float dl = ht - gh[c];
+                float t = fmaf(dl, e4[c], e3[c]);
+                t = fmaf(dl, t, e2[c]);
+                t = fmaf(dl, t, e1[c]);
+                t = fmaf(dl, t, 1.0f);
+                const float Pn = fmaf(gp[c], dl * t, gP[c]);
+                v[k][c] = ht * Pn;
+                // within 8 fp32 ulps of a bf16 tie (the low half of the bits in [0x7FF8, 0x8007])
+                slow |= ((__float_as_uint(v[k][c]) + 8u) & 0xFFF0u) == 0x8000u;
+            }
+        if (__builtin_amdgcn_ballot_w64(slow)) {   // rare: fp64 for the entries that need it
+            if (slow) {
+#pragma unroll 1
+                for (int e = 0; e < 8; ++e) {
+                    const int c = e & 3;
+                    float ve = 0.f, ae = 0.f, he = 0.f;
+#pragma unroll
+                    for (int q2 = 0; q2 < 8; ++q2)   // select without dynamic register indexing
+                        if (q2 == e) { ve = v[q2 >> 2][q2 & 3]; ae = a[q2 >> 2].v[q2 & 3]; he = gh[q2 & 3]; }
+                    if (((__float_as_uint(ve) + 8u) & 0xFFF0u) == 0x8000u || ((far_mask >> c) & 1u)) {
+                        ve = gelu_exact(fmaf(sig_u, ae, he));
+#pragma unroll
+                        for (int q2 = 0; q2 < 8; ++q2)
+                            if (q2 == e) v[q2 >> 2][q2 & 3] = ve;
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int jj = j + 2 * k + par;
+            const bool ok = gen_live && slot_base + jj < nslots;
+            const uint2 pk = ok ? make_uint2(pack_bf16x2(v[k][0], v[k][1]), pack_bf16x2(v[k][2], v[k][3]))
+                                : make_uint2(0, 0);
+            const int row = jj * GT_TB + (pw & 7);
+            *reinterpret_cast<uint2*>(&Bs[buf][gt_swz(row, gq >> 1) + 4 * (gq & 1)]) = pk;
+        }
+    };
+
+    // ===== MFMA waves: wave c owns features [fbase, fbase + 32 FB) of every row ===
+    const int fbase = w * (32 * FB);
+    const int nsub_total = n / 16;
+    const uint4* w2fw = reinterpret_cast<const uint4*>(w2f) + ((int64_t)(fbase / 32) * nsub_total) * 64 + lane;
+    const f32x16_t zero = {};
+    f32x16_t acc[FB][2];
+#pragma unroll
+    for (int fb = 0; fb < FB; ++fb) acc[fb][0] = acc[fb][1] = zero;
+    // the accumulator restarts every k-step (128 channels) after being added into
+    // the fp32 running total: sums of 2048 products in groups of 128 carry about
+    // half the rounding error of one chain, which shows in the bf16 decisions of f
+    auto flush = [&]() {
+#pragma unroll
+        for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    float4 o = tot[(fb * 2 + rb) * 4 + r4][tid];
+                    o.x += acc[fb][rb][4 * r4]; o.y += acc[fb][rb][4 * r4 + 1];
+                    o.z += acc[fb][rb][4 * r4 + 2]; o.w += acc[fb][rb][4 * r4 + 3];
+                    tot[(fb * 2 + rb) * 4 + r4][tid] = o;
+                }
+                acc[fb][rb] = zero;
+            }
+    };
+    // B fragment of sub-step s, row block rb: row 32 rb + lane%32, logical piece
+    // 2 s + lane/32, stored at piece (2 s + lane/32) ^ (lane & 15) = 2 (s ^ m) + c
+    // with m = (lane & 15) >> 1 and c = (lane/32) ^ (lane & 1); row block 1 is 8 KB
+    // further
+    const int rd_base = (lane & 31) * (GT_KS * 2) + (((lane >> 5) ^ (lane & 1)) << 4);
+    const int mk = (lane & 15) >> 1;
+    auto load_a = [&](int sub, uint4 (&af)[FB]) {
+#pragma unroll
+        for (int fb = 0; fb < FB; ++fb) af[fb] = w2fw[((int64_t)fb * nsub_total + sub) * 64];
+    };
+    auto mfma_sub = [&](const unsigned char* slab, int s_local, const uint4 (&af)[FB]) {
+        const int off = rd_base + (((s_local ^ mk) & 7) << 5);
+        uint4 bfr[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) bfr[rb] = *reinterpret_cast<const uint4*>(slab + off + rb * 32 * GT_KS * 2);
+#pragma unroll
+        for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) acc[fb][rb] = mfma32(af[fb], bfr[rb], acc[fb][rb]);
+    };
+
+    // The two roles run separate loops that meet the same barriers (one after the
+    // prologue, one per k-step, three in the epilogue), so that each role's
+    // registers are live only in its own loop.
+    if (!mfma_wave) {
+        In in_next = load_in(0);
+        setup(0, in_next);
+        if (nks > 1) in_next = load_in(1);
+        gen_pair(0, 0, 0);
+        gen_pair(0, 4, 0);
+        __syncthreads();
+#pragma unroll 1
+        for (int ks = 0; ks < nks; ++ks) {
+            if (ks + 1 < nks) {
+                setup(ks + 1, in_next);
+                if (ks + 2 < nks) in_next = load_in(ks + 2);
+                gen_pair(ks + 1, 0, (ks & 1) ^ 1);
+                gen_pair(ks + 1, 4, (ks & 1) ^ 1);
+            }
+            __syncthreads();
+        }
+        __syncthreads();   // the epilogue's three barriers
+        __syncthreads();
+        __syncthreads();
+        return;
+    }
+
+#pragma unroll
+    for (int r4 = 0; r4 < NV / 4; ++r4) tot[r4][tid] = make_float4(0.f, 0.f, 0.f, 0.f);
+    uint4 fr[2][FB];
+    load_a(0, fr[0]);
+    load_a(1, fr[1]);
+    __syncthreads();
+    // one k-step of the MFMA waves on slab ks (fragments two sub-steps ahead);
+    // FULL: all 128 channels exist
+    auto kstep = [&](int ks, auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        const int buf = ks & 1;
+        const bool more = ks + 1 < nks;
+        const int nsub = FULL ? GT_KS / 16 : (n - ks * GT_KS) / 16;   // even: n is a multiple of 32
+        const unsigned char* slab = reinterpret_cast<const unsigned char*>(&Bs[buf][0]);
+#pragma unroll
+        for (int s2 = 0; s2 < GT_KS / 16; s2 += 2) {
+            if (FULL || s2 < nsub) {
+                const int g = ks * (GT_KS / 16) + s2;
+                mfma_sub(slab, s2, fr[0]);
+                if (g + 2 < nsub_total) load_a(g + 2, fr[0]);
+                mfma_sub(slab, s2 + 1, fr[1]);
+                if (g + 3 < nsub_total) load_a(g + 3, fr[1]);
+            }
+        }
+        if ((ks + 1) % FLUSH == 0 || !more) flush();
+        __syncthreads();
+    };
+#pragma unroll 1
+    for (int ks = 0; ks < nfull; ++ks) kstep(ks, std::integral_constant<bool, true>{});
+    if (nfull < nks) kstep(nfull, std::integral_constant<bool, false>{});
+
+    // ---- epilogue (MFMA waves): residual add, LayerNorm over D, bf16, all in
+    // fp64.  Lane holds rows 32 rb + lane%32
+    // and features fbase + 32 fb + drow(r, lane).
+    double* red = reinterpret_cast<double*>(&Bs[0][0]);   // [NC waves][64 rows]
+    auto yv = [&](int fb, int rb, int r4, const float4& xv, double (&y)[4]) {
+        const float4 o = tot[(fb * 2 + rb) * 4 + r4][tid];
+        y[0] = (double)o.x + (double)xv.x; y[1] = (double)o.y + (double)xv.y;
+        y[2] = (double)o.z + (double)xv.z; y[3] = (double)o.w + (double)xv.w;
+    };
+    auto xrow_of = [&](int rb) {
+        const int r = rb * 32 + (lane & 31);
+        const int t = tb * GT_TB + (r % GT_TB);
+        return A.x_res + (int64_t)(t < T ? t : T - 1) * D;
+    };
+    auto row_total = [&](int r) {
+        double v = 0.0;
+#pragma unroll
+        for (int k = 0; k < NC; ++k) v += red[k * GT_ROWS + r];
+        return v;
+    };
+    double mean[2] = {0.0, 0.0};
+    {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            const float* xrow = xrow_of(rb);
+            double sv = 0.0;
+#pragma unroll
+            for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    double y[4];
+                    yv(fb, rb, r4, *reinterpret_cast<const float4*>(xrow + fbase + fb * 32 + 8 * r4 + 4 * (lane >> 5)),
+                       y);
+                    sv += (y[0] + y[1]) + (y[2] + y[3]);
+                }
+            sv += __shfl_xor(sv, 32, 64);
+            if (lane < 32) red[w * GT_ROWS + rb * 32 + lane] = sv;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) mean[rb] = row_total(rb * 32 + (lane & 31)) * (1.0 / D);
+    __syncthreads();
+    {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            const float* xrow = xrow_of(rb);
+            double v = 0.0;
+#pragma unroll
+            for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    double y[4];
+                    yv(fb, rb, r4, *reinterpret_cast<const float4*>(xrow + fbase + fb * 32 + 8 * r4 + 4 * (lane >> 5)),
+                       y);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const double dv = y[c] - mean[rb];
+                        v = fma(dv, dv, v);
+                    }
+                }
+            v += __shfl_xor(v, 32, 64);
+            if (lane < 32) red[w * GT_ROWS + rb * 32 + lane] = v;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const int r = rb * 32 + (lane & 31);
+        const int t = tb * GT_TB + (r % GT_TB);
+        const int slot = slot_base + r / GT_TB;
+        const double var = row_total(r) * (1.0 / D);
+        const double rstd = 1.0 / sqrt(var + (double)A.ln_eps);
+        if (t >= T || slot >= nslots) continue;
+        const float* xrow = A.x_res + (int64_t)t * D;
+        uint16_t* frow = F + ((int64_t)(first_slot + slot) * T + t) * D;
+#pragma unroll
+        for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int ff = fbase + fb * 32 + 8 * r4 + 4 * (lane >> 5);
+                double y[4];
+                yv(fb, rb, r4, *reinterpret_cast<const float4*>(xrow + ff), y);
+                float o[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) o[c] = (float)((y[c] - mean[rb]) * rstd);
+                *reinterpret_cast<uint2*>(frow + ff) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // gemm2: per (vocab tile of 256, row): partial log-sum-exp of z = W_head F
 // and the label logit.  Workgroup tile 256 vocab x 256 rows, 8 waves of
 // 128 vocab x 64 rows (4 x 2 MFMA blocks, 128 accumulators); both operands
@@ -615,6 +1010,8 @@ MlpLayout mlp_layout(int64_t T, int64_t d, int64_t n, int64_t V, int64_t K) {
     L.off_wnorm = off; off += al256((size_t)((V + 255) / 256 + 1) * sizeof(float));
     L.off_ce = off;   off += al256((size_t)T * (K + 1) * sizeof(float));
     L.off_ghat = off; off += al256((size_t)T * n * sizeof(float));
+    L.off_w2f = off;  off += al256((size_t)d * n * 2);
+    L.off_phi = off;  off += 2 * al256((size_t)T * n * sizeof(float));
     L.off_outer = off;
     off += outer_workspace_bytes(T, n, d);
     L.total = off;
@@ -637,16 +1034,56 @@ hipError_t launch_mlp(const MlpArgs& A, const MlpLayout& L, unsigned char* ws, f
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(mlp_wnorm_final_kernel, dim3(1), dim3(256), 0, stream, wnorm, nwb, A.d, offset);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    for (int64_t g0 = 0; g0 < total; g0 += L.chunk) {
-        const int64_t nrows = (total - g0) < L.chunk ? (total - g0) : L.chunk;
+    // small sigma: GELU of the draw rows from the cached Phi(h), phi(h) by the
+    // series (mlp_gemm1t_kernel); the clean rows, and every row at larger sigma,
+    // through mlp_gemm1_kernel's library erf
+    const bool taylor = mlp_taylor_ok(A.sigma);
+    const uint16_t* w2f = reinterpret_cast<const uint16_t*>(ws + L.off_w2f);
+    float* Pt = reinterpret_cast<float*>(ws + L.off_phi);
+    float* pt = reinterpret_cast<float*>(ws + L.off_phi + al256((size_t)A.T * A.n * sizeof(float)));
+    const float sig_u = (float)((double)A.sigma * (double)kSqrt2Ln2);
+    if (taylor) {
+        const int64_t cnt = (int64_t)A.T * A.n;
+        hipLaunchKernelGGL(mlp_phi_kernel, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, stream, A.h, cnt, Pt,
+                           pt);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        const int64_t pieces = (int64_t)(A.d / 32) * (A.n / 16) * 64;
+        hipLaunchKernelGGL(mlp_w2frag_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, stream, A.w2, A.d,
+                           A.n, const_cast<uint16_t*>(w2f));
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    auto gemm1_direct = [&](int64_t g0, int64_t nrows) {
         const unsigned b1 = (unsigned)((nrows + G1_ROWS - 1) / G1_ROWS);
-        bool timed = false;
-        if ((e = launch_timer_begin(kTimedMlpGemm1, stream, timed)) != hipSuccess) return e;
         if (A.d == 512)
             hipLaunchKernelGGL(mlp_gemm1_kernel<512>, dim3(b1), dim3(G1_NT), 0, stream, A, g0, nrows, F);
         else
             hipLaunchKernelGGL(mlp_gemm1_kernel<256>, dim3(b1), dim3(G1_NT), 0, stream, A, g0, nrows, F);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        return hipGetLastError();
+    };
+    auto gemm1_taylor = [&](int64_t g0, int first_slot, int nslots) {
+        const int ntiles = ((A.T + GT_TB - 1) / GT_TB) * ((nslots + GT_DB - 1) / GT_DB);
+        const unsigned grid = (unsigned)((ntiles + 7) / 8 * 8);
+        if (A.d == 512)
+            hipLaunchKernelGGL(mlp_gemm1t_kernel<512>, dim3(grid), dim3(1024), 0, stream, A, sig_u, w2f, Pt, pt, g0,
+                               first_slot, nslots, ntiles, F);
+        else
+            hipLaunchKernelGGL(mlp_gemm1t_kernel<256>, dim3(grid), dim3(1024), 0, stream, A, sig_u, w2f, Pt, pt, g0,
+                               first_slot, nslots, ntiles, F);
+        return hipGetLastError();
+    };
+    for (int64_t g0 = 0; g0 < total; g0 += L.chunk) {
+        const int64_t nrows = (total - g0) < L.chunk ? (total - g0) : L.chunk;
+        bool timed = false;
+        if ((e = launch_timer_begin(kTimedMlpGemm1, stream, timed)) != hipSuccess) return e;
+        if (!taylor) {
+            if ((e = gemm1_direct(g0, nrows)) != hipSuccess) return e;
+        } else {
+            // a chunk is a whole number of slots of T rows; slot 0 of the first is the clean rows
+            const int first = g0 == 0 ? 1 : 0;
+            const int nslots = (int)(nrows / A.T) - first;
+            if (first && (e = gemm1_direct(0, A.T)) != hipSuccess) return e;
+            if (nslots > 0 && (e = gemm1_taylor(g0, first, nslots)) != hipSuccess) return e;
+        }
         if ((e = launch_timer_end(kTimedMlpGemm1, stream, timed)) != hipSuccess) return e;
         if (A.gemm1_event && (e = hipEventRecord(A.gemm1_event, stream)) != hipSuccess) return e;
         const int64_t nrt = (nrows + G2_TR - 1) / G2_TR;
