@@ -173,6 +173,39 @@ def write_traffic(args):
     print(json.dumps(out))
 
 
+def trace_summary(args):
+    """Markdown summary of a rocprofv3 --kernel-trace --stats --output-format csv folder
+    (the kernel stats table and each library kernel's launch shape), printed to stdout."""
+    import csv
+    import glob
+    d = args.trace_summary
+    stats = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    trace = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if not stats:
+        sys.exit(f"no kernel_stats.csv under {d}")
+    print("| kernel | calls | total us | average us | min us | max us | % |")
+    print("|---|---:|---:|---:|---:|---:|---:|")
+    for r in csv.DictReader(open(stats[0])):
+        nm = r["Name"] if len(r["Name"]) <= 100 else r["Name"][:97] + "..."
+        print(f"| `{nm}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e3:.1f} | {float(r['AverageNs']) / 1e3:.1f} "
+              f"| {float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f} |")
+    if trace:
+        seen = {}
+        for r in csv.DictReader(open(trace[0])):
+            nm = r.get("Kernel_Name", "")
+            if "dust" not in nm or nm in seen:
+                continue
+            seen[nm] = (f"grid {r.get('Grid_Size', '?')}, workgroup {r.get('Workgroup_Size', '?')}, "
+                        f"VGPR {r.get('VGPR_Count', r.get('Arch_VGPR_Count', '?'))}, "
+                        f"AGPR {r.get('Accum_VGPR_Count', '?')}, LDS {r.get('LDS_Block_Size', r.get('Lds_Size', '?'))} B, "
+                        f"scratch {r.get('Scratch_Size', r.get('Private_Segment_Size', '?'))} B")
+        print()
+        print("Launch shape of each library kernel:")
+        print()
+        for nm, shape in seen.items():
+            print(f"- `{nm[:110]}`: {shape}")
+
+
 WORKLOAD_NAMES = {
     1: "LM-head estimator fp32 logits: T=256, d=64, V=512, K=64, sigma=1e-2, uniform labels",
     2: "LM-head estimator fp32 logits: T=4096 (2x2048), d=512, V=8192, K=256, sigma=1e-2, Zipf(1.1) labels",
@@ -210,6 +243,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB (to scale HBM traffic counters) and exit")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="print a markdown summary of the rocprofv3 --kernel-trace --stats csv output under DIR "
+                         "and exit")
     ap.add_argument("--traffic-from", metavar="DIR",
                     help="with --copy-calibration MIB: read the rocprofv3 --pmc folders DIR/fetch_wN, "
                          "DIR/write_wN (this workload) and DIR/copy_fetch, DIR/copy_write, and write the "
@@ -732,6 +768,9 @@ def main():
         sys.exit(2)
     if args.traffic_from:
         write_traffic(args)
+        return
+    if args.trace_summary:
+        trace_summary(args)
         return
     import torch
     if args.copy_calibration:

@@ -27,6 +27,8 @@
 // v_mfma_f32_32x32x16_bf16 operand layout (checked on the device): A[i][k] in
 // lane i + 32*(k/8) element k%8; B[k][j] in lane j + 32*(k/8) element k%8;
 // D[i][j] in lane j + 32*((i/4)%2), register (i%4) + 4*(i/8).
+#include <algorithm>
+
 #include "dust_device.hpp"
 #include "dust_internal.hpp"
 #include "launch_events.hpp"
@@ -379,325 +381,381 @@ __device__ __attribute__((noinline)) float gelu_exact(float x) {
     return (float)(0.5 * xd * (1.0 + erf(xd * 0.70710678118654752440)));
 }
 
-// Slab layout: 64 rows of 128 bf16 (16 pieces of 16 bytes); piece p of row r is
-// stored at p ^ (r & 15): sixteen lanes reading one piece of sixteen consecutive
-// rows, and sixteen lanes writing the 16 pieces of one row, touch every bank once.
-__device__ __forceinline__ int gt_swz(int row, int piece) { return row * GT_KS + ((piece ^ (row & 15)) << 3); }
-
-template <int D>
-__global__ void __launch_bounds__(1024, 1) mlp_gemm1t_kernel(MlpArgs A, float sig_u, const uint16_t* __restrict__ w2f,
-                                                            const float* __restrict__ Pt, const float* __restrict__ pt,
-                                                            int64_t g0, int first_slot, int nslots, int ntiles,
-                                                            uint16_t* __restrict__ F) {
-    constexpr int NC = 8;                       // MFMA waves (waves 0-7); waves 8-15 generate
-    constexpr int FB = D / 256;                 // 32-feature blocks per MFMA wave (2 or 1)
-    constexpr int NV = FB * 2 * 16;             // accumulator values per MFMA lane
-    constexpr int FLUSH = 1;                    // k-steps (128 channels) per accumulator restart
-    __shared__ __align__(16) uint16_t Bs[2][GT_ROWS * GT_KS];   // 2 x 16 KB
-    __shared__ __align__(16) float4 tot[NV / 4][NC * 64];       // running totals, lane-interleaved
-
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const bool mfma_wave = w < NC;              // wave-uniform role
+// ---- kernel A: M = bf16(GELU(h + sigma a)) of the draw rows -----------------
+// One wave per (token, 256-channel block): lane l holds channel quad l of the
+// block, its cached h, Phi(h), phi(h) and the series coefficients, and makes the
+// quad for every draw slot of the launch, two draws at a time (token, draw and
+// layer are uniform across the wave, so the first Philox rounds stay scalar).  Each
+// draw's 512 bytes of the wave are one contiguous store into row (slot T + t) of M.
+constexpr int GA_NT = 256;
+__global__ void __launch_bounds__(GA_NT) mlp_gelu_rows_kernel(MlpArgs A, float sig_u, const float* __restrict__ Pt,
+                                                             const float* __restrict__ pt, int64_t g0, int first_slot,
+                                                             int nslots, uint16_t* __restrict__ M) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wid = (int64_t)blockIdx.x * (GA_NT / 64) + (threadIdx.x >> 6);
     const int T = A.T, n = A.n;
-    // tiles (token block, draw block), draw block fastest; each XCD (workgroup id
-    // mod 8) takes a contiguous run of tiles, so the draw blocks of a token block
-    // share that XCD's L2 for the token's h, Phi(h), phi(h)
-    const int per_xcd = (ntiles + 7) / 8;
-    const int tile = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
-    if (tile >= ntiles) return;
-    const int nsb = (nslots + GT_DB - 1) / GT_DB;
-    const int tb = tile / nsb, sb = tile % nsb;
-    const int slot_base = sb * GT_DB;           // first draw slot of this tile (launch-relative)
-    const int nks = (n + GT_KS - 1) / GT_KS;
-    const int nfull = n / GT_KS;
-
-    // ===== generation waves: wave 8 + p makes token tb*8 + p; lane l channel quad
-    //       l%32 of each k-step for the draws of parity l/32, two at a time ======
-    const int pw = w - NC;
-    const int gt = tb * GT_TB + (pw & 7);
-    const bool tok_ok = gt < T;
-    const int tt = tok_ok ? gt : T - 1;
-    const int gq = lane & 31, par = lane >> 5;
-    const float* hrow = A.h + (int64_t)tt * n;
-    const float* Prow = Pt + (int64_t)tt * n;
-    const float* prow = pt + (int64_t)tt * n;
-    const uint32_t tok = A.tok0 + (uint32_t)tt;
-    const int64_t slot_g0 = g0 / T + first_slot + slot_base;   // g / T of the tile's draw slot 0
-    struct In { float4 h, P, p; };
-    auto load_in = [&](int ks) -> In {
-        int c0 = ks * GT_KS + 4 * gq;
-        c0 = c0 < n ? c0 : n - 4;
-        return In{*reinterpret_cast<const float4*>(hrow + c0), *reinterpret_cast<const float4*>(Prow + c0),
-                  *reinterpret_cast<const float4*>(prow + c0)};
-    };
-    // the generation state of one k-step: per channel h, Phi, phi, the series
-    // coefficients, and which entries take the fp64 path whatever the draw
-    float gh[4], gP[4], gp[4], e1[4], e2[4], e3[4], e4[4];
+    const int ncb = (n + 255) / 256;
+    if (wid >= (int64_t)T * ncb) return;
+    const int t = (int)(wid / ncb), cb = (int)(wid % ncb);
+    const int c0 = cb * 256 + 4 * lane;
+    const bool live = c0 < n;
+    const int cc = live ? c0 : n - 4;
+    const float4 h4 = *reinterpret_cast<const float4*>(A.h + (int64_t)t * n + cc);
+    const float4 P4 = *reinterpret_cast<const float4*>(Pt + (int64_t)t * n + cc);
+    const float4 p4 = *reinterpret_cast<const float4*>(pt + (int64_t)t * n + cc);
+    const float gh[4] = {h4.x, h4.y, h4.z, h4.w};
+    const float gP[4] = {P4.x, P4.y, P4.z, P4.w};
+    const float gp[4] = {p4.x, p4.y, p4.z, p4.w};
+    float e1[4], e2[4], e3[4], e4[4];
     uint32_t far_mask = 0;
-    bool gen_live = false;
-    auto setup = [&](int ks, const In& in) {
-        const float hv[4] = {in.h.x, in.h.y, in.h.z, in.h.w};
-        const float Pv[4] = {in.P.x, in.P.y, in.P.z, in.P.w};
-        const float pv[4] = {in.p.x, in.p.y, in.p.z, in.p.w};
-        far_mask = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const float x = gh[c], x2 = x * x;
+        e1[c] = -0.5f * x;
+        e2[c] = fmaf(x2, 1.0f / 6.0f, -1.0f / 6.0f);
+        e3[c] = x * fmaf(x2, -1.0f / 24.0f, 3.0f / 24.0f);
+        e4[c] = fmaf(x2, fmaf(x2, 1.0f / 120.0f, -6.0f / 120.0f), 3.0f / 120.0f);
+        far_mask |= (x < GT_FAR ? 1u : 0u) << c;
+    }
+    const uint32_t tok = A.tok0 + (uint32_t)t;
+    const uint32_t q = (uint32_t)(c0 >> 2);
+    const int64_t slot_g0 = g0 / T + first_slot;   // g / T of launch slot 0
+    uint16_t* mrow0 = M + ((int64_t)first_slot * T + t) * n + cc;
+    auto gelu4 = [&](const f32x4& a, float (&v)[4], bool& slow) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const float x = hv[c], x2 = x * x;
-            gh[c] = x; gP[c] = Pv[c]; gp[c] = pv[c];
-            e1[c] = -0.5f * x;
-            e2[c] = fmaf(x2, 1.0f / 6.0f, -1.0f / 6.0f);
-            e3[c] = x * fmaf(x2, -1.0f / 24.0f, 3.0f / 24.0f);
-            e4[c] = fmaf(x2, fmaf(x2, 1.0f / 120.0f, -6.0f / 120.0f), 3.0f / 120.0f);
-            far_mask |= (x < GT_FAR ? 1u : 0u) << c;
+            const float ht = fmaf(sig_u, a.v[c], gh[c]);   // the noise is drawn divided by sqrt(2 ln 2)
+            const float dl = ht - gh[c];
+            float tt = fmaf(dl, e4[c], e3[c]);
+            tt = fmaf(dl, tt, e2[c]);
+            tt = fmaf(dl, tt, e1[c]);
+            tt = fmaf(dl, tt, 1.0f);
+            const float Pn = fmaf(gp[c], dl * tt, gP[c]);
+            v[c] = ht * Pn;
+            // within 8 fp32 ulps of a bf16 tie (the low half of the bits in [0x7FF8, 0x8007])
+            slow |= ((__float_as_uint(v[c]) + 8u) & 0xFFF0u) == 0x8000u;
         }
-        gen_live = tok_ok && ks * GT_KS + 4 * gq < n;
     };
-    // draws j + par and j + 2 + par of the lane's quad (two Philox chains side by
-    // side): rows (draw, token) of slab buf
-    auto gen_pair = [&](int ks, int j, int buf) {
-        const uint32_t q = (uint32_t)(ks * (GT_KS / 4) + gq);
-        f32x4 a[2];
-        float v[2][4];
-        bool slow = far_mask != 0;
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const uint32_t draw = A.draw0 + (uint32_t)(slot_g0 + j + 2 * k + par - 1);
-            a[k] = gauss4_unscaled(tok, q, draw, A.layer, A.k0, A.k1);
-        }
-#pragma unroll
-        for (int k = 0; k < 2; ++k)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const float ht = fmaf(sig_u, a[k].v[c], gh[c]);   // the noise is drawn divided by sqrt(2 ln 2)
-                const float dl = ht - gh[c];
-                float t = fmaf(dl, e4[c], e3[c]);
-                t = fmaf(dl, t, e2[c]);
-                t = fmaf(dl, t, e1[c]);
-                t = fmaf(dl, t, 1.0f);
-                const float Pn = fmaf(gp[c], dl * t, gP[c]);
-                v[k][c] = ht * Pn;
-                // within 8 fp32 ulps of a bf16 tie (the low half of the bits in [0x7FF8, 0x8007])
-                slow |= ((__float_as_uint(v[k][c]) + 8u) & 0xFFF0u) == 0x8000u;
-            }
-        if (__builtin_amdgcn_ballot_w64(slow)) {   // rare: fp64 for the entries that need it
-            if (slow) {
+    auto fix4 = [&](const f32x4& a, float (&v)[4]) {   // the rare fp64 path
 #pragma unroll 1
-                for (int e = 0; e < 8; ++e) {
-                    const int c = e & 3;
-                    float ve = 0.f, ae = 0.f, he = 0.f;
+        for (int c = 0; c < 4; ++c) {
+            float ve = 0.f, ae = 0.f, he = 0.f;
 #pragma unroll
-                    for (int q2 = 0; q2 < 8; ++q2)   // select without dynamic register indexing
-                        if (q2 == e) { ve = v[q2 >> 2][q2 & 3]; ae = a[q2 >> 2].v[q2 & 3]; he = gh[q2 & 3]; }
-                    if (((__float_as_uint(ve) + 8u) & 0xFFF0u) == 0x8000u || ((far_mask >> c) & 1u)) {
-                        ve = gelu_exact(fmaf(sig_u, ae, he));
+            for (int c2 = 0; c2 < 4; ++c2)   // select without dynamic register indexing
+                if (c2 == c) { ve = v[c2]; ae = a.v[c2]; he = gh[c2]; }
+            if (((__float_as_uint(ve) + 8u) & 0xFFF0u) == 0x8000u || ((far_mask >> c) & 1u)) {
+                ve = gelu_exact(fmaf(sig_u, ae, he));
 #pragma unroll
-                        for (int q2 = 0; q2 < 8; ++q2)
-                            if (q2 == e) v[q2 >> 2][q2 & 3] = ve;
-                    }
-                }
+                for (int c2 = 0; c2 < 4; ++c2)
+                    if (c2 == c) v[c2] = ve;
             }
         }
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int jj = j + 2 * k + par;
-            const bool ok = gen_live && slot_base + jj < nslots;
-            const uint2 pk = ok ? make_uint2(pack_bf16x2(v[k][0], v[k][1]), pack_bf16x2(v[k][2], v[k][3]))
-                                : make_uint2(0, 0);
-            const int row = jj * GT_TB + (pw & 7);
-            *reinterpret_cast<uint2*>(&Bs[buf][gt_swz(row, gq >> 1) + 4 * (gq & 1)]) = pk;
-        }
     };
+    auto store = [&](int s, const float (&v)[4]) {
+        if (live)
+            *reinterpret_cast<uint2*>(mrow0 + (int64_t)s * T * n) =
+                make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+    };
+#pragma unroll 1
+    for (int s = 0; s < nslots; s += 2) {
+        const bool two = s + 1 < nslots;   // uniform
+        const uint32_t d0 = A.draw0 + (uint32_t)(slot_g0 + s - 1);
+        const f32x4 a0 = gauss4_unscaled_uniform(tok, q, d0, A.layer, A.k0, A.k1);
+        const f32x4 a1 = gauss4_unscaled_uniform(tok, q, d0 + 1u, A.layer, A.k0, A.k1);
+        float v0[4], v1[4];
+        bool slow0 = far_mask != 0, slow1 = far_mask != 0;
+        gelu4(a0, v0, slow0);
+        gelu4(a1, v1, slow1);
+        if (__builtin_amdgcn_ballot_w64(slow0 || slow1)) {
+            if (slow0) fix4(a0, v0);
+            if (slow1) fix4(a1, v1);
+        }
+        store(s, v0);
+        if (two) store(s + 1, v1);
+    }
+}
 
-    // ===== MFMA waves: wave c owns features [fbase, fbase + 32 FB) of every row ===
-    const int fbase = w * (32 * FB);
+// ---- kernel B: F = bf16(LN(x + W2 M)) for 64 consecutive chunk rows ----------
+// 8 waves (2 per SIMD); wave c owns features [c D/8, (c+1) D/8) of the 64 rows.
+// M moves by direct global->LDS loads into a 4-stage ring of 64 x 128-channel
+// slabs (row r's 16-byte piece p stored at p ^ (r & 15), the swizzle applied on
+// the global side since a direct load puts lane l at slot l), three k-steps in
+// flight; W2 fragments come in fragment order straight from global memory two
+// sub-steps ahead.  The accumulator is added into an fp32 running total in
+// registers every 128 channels (groups of 128 of the 2048 products: about half
+// the rounding error of one chain, which shows in the bf16 decisions of f); the
+// residual and the LayerNorm are formed in fp64.
+// s_waitcnt immediate that waits until at most n vector-memory operations are
+// outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt at
+// their maxima, i.e. not waited for)
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+constexpr int GB_ROWS = 64;
+constexpr int GB_KS = 128;
+constexpr int GB_NT = 512;
+constexpr int GB_STAGES = 4;
+
+// FAST (n a multiple of 512: whole groups of four full k-steps): every k-step has
+// the same shape with no branches -- the W2 fragment and M slab loads past the end
+// re-read the last valid ones -- so the compiler tracks the outstanding loads
+// exactly and waits for a W2 fragment alone, not for the M slab loads issued after
+// it (at a branch join it waits for everything).
+template <int D, bool FAST>
+__global__ void __launch_bounds__(GB_NT, 1) mlp_w2ln_kernel(MlpArgs A, const uint16_t* __restrict__ w2f,
+                                                           const uint16_t* __restrict__ M, int64_t g0, int64_t nrows,
+                                                           uint16_t* __restrict__ F) {
+    constexpr int FB = D / 256;                 // 32-feature blocks per wave (2 or 1)
+    // the four ring stages as separate LDS objects: the compiler can then tell that
+    // reads of one stage do not alias direct loads still in flight into another,
+    // and does not drain those loads before each read
+    __shared__ __align__(16) uint16_t Ms0[GB_ROWS * GB_KS], Ms1[GB_ROWS * GB_KS], Ms2[GB_ROWS * GB_KS],
+        Ms3[GB_ROWS * GB_KS];
+    __shared__ double red[8][GB_ROWS];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int T = A.T, n = A.n;
+    const int64_t r0 = (int64_t)blockIdx.x * GB_ROWS;
+    const int nks = (n + GB_KS - 1) / GB_KS;   // the last k-step may hold 32..96 channels
     const int nsub_total = n / 16;
+
+    // direct loads: each k-step's slab is 64 rows x 16 pieces = 1024 pieces, two
+    // per lane; lane slot s = 64 (2 w + j) + lane holds row s/16, stored piece
+    // s%16, i.e. logical piece (s%16) ^ (row & 15) of that row (rows past the
+    // chunk read zero, channels past n re-read valid ones; both are masked).
+    // The loads go through a buffer resource over this block's rows (bytes past the
+    // chunk's last row read as zero) rather than through global addresses: the
+    // compiler counts a global load into LDS as a possible flat access and then
+    // waits for every outstanding load before any use of a loaded register.
+    const int vrows = (int)min<int64_t>(GB_ROWS, nrows - r0);
+    const __amdgpu_buffer_rsrc_t mres =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(M + r0 * n), (short)0, vrows * n * 2, 0x00020000);
+    int rowoff[2], soff[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int slot = 64 * (2 * w + j) + lane;
+        rowoff[j] = (slot >> 4) * n;
+        soff[j] = 64 * (2 * w + j) * 8;   // element offset of this wave's 64 slots
+    }
+
+    // B fragment of sub-step s, row block rb: row 32 rb + lane%32, logical piece
+    // 2 s + lane/32 at stored piece 2 (s ^ m) + c (m = (lane & 15) >> 1,
+    // c = (lane/32) ^ (lane & 1)); row block 1 is 8 KB further
+    const int rd_base = (lane & 31) * (GB_KS * 2) + (((lane >> 5) ^ (lane & 1)) << 4);
+    const int mk = (lane & 15) >> 1;
+    const int fbase = w * (32 * FB);
     const uint4* w2fw = reinterpret_cast<const uint4*>(w2f) + ((int64_t)(fbase / 32) * nsub_total) * 64 + lane;
+    auto load_a = [&](int sub, uint4 (&af)[FB]) {
+#pragma unroll
+        for (int fb = 0; fb < FB; ++fb) af[fb] = w2fw[((int64_t)fb * nsub_total + sub) * 64];
+    };
     const f32x16_t zero = {};
     f32x16_t acc[FB][2];
+    float tot[FB][2][16];
 #pragma unroll
-    for (int fb = 0; fb < FB; ++fb) acc[fb][0] = acc[fb][1] = zero;
-    // the accumulator restarts every k-step (128 channels) after being added into
-    // the fp32 running total: sums of 2048 products in groups of 128 carry about
-    // half the rounding error of one chain, which shows in the bf16 decisions of f
-    auto flush = [&]() {
+    for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            acc[fb][rb] = zero;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) tot[fb][rb][r] = 0.f;
+        }
+    // M slab loads: piece p of k-step ks; past n a piece re-reads the row's
+    // first piece of the k-step (its channels are never multiplied)
+    auto issue_ks = [&](int ks, uint16_t* dst) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int slot = 64 * (2 * w + j) + lane;
+            const int piece = (slot & 15) ^ ((slot >> 4) & 15);
+            const int c = ks * GB_KS + 8 * piece;
+            const int voff = 2 * (rowoff[j] + (c < n ? c : ks * GB_KS));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(mres, (__attribute__((address_space(3))) void*)(dst + soff[j]), 16,
+                                                     voff, 0, 0, 0);
+        }
+    };
+    // W2 fragments are loaded PF sub-steps ahead of their MFMAs (one L2 round trip
+    // takes about as long as PF sub-steps of MFMAs).  Order of the vector-memory
+    // operations: fragments of sub-steps 0 .. PF-1, slabs 0, 1, 2; then per
+    // iteration ks: the fragments of sub-steps 8 ks + PF .. 8 ks + PF + 7 (8 FB
+    // loads when they all exist), then slab ks + 3 (2 loads).  Slab ks has landed
+    // once at most the operations issued after it are outstanding: 4 (ks = 0),
+    // 8 FB + 4 (ks = 1), 16 FB + 4 (ks >= 2), when all of those were issued;
+    // otherwise the wait is for everything.
+    constexpr int PF = 4;
+    uint4 fr[PF][FB];
+#pragma unroll
+    for (int k = 0; k < PF; ++k)
+        if (k < nsub_total) load_a(k, fr[k]);
+    if (0 < nks) issue_ks(0, Ms0);
+    if (1 < nks) issue_ks(1, Ms1);
+    if (2 < nks) issue_ks(2, Ms2);
+    // k-step ks on stage `cur`; the slab of ks + 3 goes into `nxt` (the stage read
+    // by k-step ks - 1, which every wave has finished at this k-step's barrier)
+    auto kstep = [&](int ks, const uint16_t* cur, uint16_t* nxt) {
+        if (ks == 0 && nks >= 3) __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
+        else if (ks == 1 && nks >= 4) __builtin_amdgcn_s_waitcnt(vmcnt_imm(8 * FB + 4));
+        else if (ks >= 2 && ks + 2 < nks) __builtin_amdgcn_s_waitcnt(vmcnt_imm(16 * FB + 4));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        // a barrier without the full memory wait that __syncthreads adds (which
+        // would drain the later slabs' loads as well); the memory clobber keeps
+        // the compiler from moving LDS accesses across it
+        asm volatile("s_barrier" ::: "memory");
+        const unsigned char* slab = reinterpret_cast<const unsigned char*>(cur);
+        const int nsub = min(GB_KS, n - ks * GB_KS) / 16;
+#pragma unroll
+        for (int s = 0; s < GB_KS / 16; ++s) {
+            if (s < nsub) {
+                const int g = ks * (GB_KS / 16) + s;
+                const int off = rd_base + (((s ^ mk) & 7) << 5);
+                uint4 bfr[2];
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+                    bfr[rb] = *reinterpret_cast<const uint4*>(slab + off + rb * 32 * GB_KS * 2);
+#pragma unroll
+                for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+                    for (int rb = 0; rb < 2; ++rb) acc[fb][rb] = mfma32(fr[s % PF][fb], bfr[rb], acc[fb][rb]);
+                if (g + PF < nsub_total) load_a(g + PF, fr[s % PF]);
+            }
+        }
+        if (ks + GB_STAGES - 1 < nks) issue_ks(ks + GB_STAGES - 1, nxt);
 #pragma unroll
         for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    float4 o = tot[(fb * 2 + rb) * 4 + r4][tid];
-                    o.x += acc[fb][rb][4 * r4]; o.y += acc[fb][rb][4 * r4 + 1];
-                    o.z += acc[fb][rb][4 * r4 + 2]; o.w += acc[fb][rb][4 * r4 + 3];
-                    tot[(fb * 2 + rb) * 4 + r4][tid] = o;
-                }
+                for (int r = 0; r < 16; ++r) tot[fb][rb][r] += acc[fb][rb][r];
                 acc[fb][rb] = zero;
             }
     };
-    // B fragment of sub-step s, row block rb: row 32 rb + lane%32, logical piece
-    // 2 s + lane/32, stored at piece (2 s + lane/32) ^ (lane & 15) = 2 (s ^ m) + c
-    // with m = (lane & 15) >> 1 and c = (lane/32) ^ (lane & 1); row block 1 is 8 KB
-    // further
-    const int rd_base = (lane & 31) * (GT_KS * 2) + (((lane >> 5) ^ (lane & 1)) << 4);
-    const int mk = (lane & 15) >> 1;
-    auto load_a = [&](int sub, uint4 (&af)[FB]) {
+    if (FAST) {
+        // branch-free k-step: slab ks + 3 and the fragments PF sub-steps ahead are
+        // loaded unconditionally (clamped to the last ones), so every k-step issues
+        // 8 FB + 2 loads and, from the third on, slab ks has landed once at most
+        // 16 FB + 4 operations are outstanding
+        auto kfast = [&](int ks, const uint16_t* cur, uint16_t* nxt, int wait) {
+            if (wait == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
+            else if (wait == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(8 * FB + 4));
+            else __builtin_amdgcn_s_waitcnt(vmcnt_imm(16 * FB + 4));
+            asm volatile("s_barrier" ::: "memory");
+            const unsigned char* slab = reinterpret_cast<const unsigned char*>(cur);
 #pragma unroll
-        for (int fb = 0; fb < FB; ++fb) af[fb] = w2fw[((int64_t)fb * nsub_total + sub) * 64];
+            for (int s = 0; s < GB_KS / 16; ++s) {
+                const int g = ks * (GB_KS / 16) + s;
+                const int off = rd_base + (((s ^ mk) & 7) << 5);
+                uint4 bfr[2];
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+                    bfr[rb] = *reinterpret_cast<const uint4*>(slab + off + rb * 32 * GB_KS * 2);
+#pragma unroll
+                for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+                    for (int rb = 0; rb < 2; ++rb) acc[fb][rb] = mfma32(fr[s % PF][fb], bfr[rb], acc[fb][rb]);
+                load_a(min(g + PF, nsub_total - 1), fr[s % PF]);
+            }
+            issue_ks(min(ks + GB_STAGES - 1, nks - 1), nxt);
+#pragma unroll
+            for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) tot[fb][rb][r] += acc[fb][rb][r];
+                    acc[fb][rb] = zero;
+                }
+        };
+        kfast(0, Ms0, Ms3, 0);
+        kfast(1, Ms1, Ms0, 1);
+        kfast(2, Ms2, Ms1, 2);
+        kfast(3, Ms3, Ms2, 2);
+        for (int ks = 4; ks < nks; ks += GB_STAGES) {
+            kfast(ks, Ms0, Ms3, 2);
+            kfast(ks + 1, Ms1, Ms0, 2);
+            kfast(ks + 2, Ms2, Ms1, 2);
+            kfast(ks + 3, Ms3, Ms2, 2);
+        }
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the loads past the end
+    } else {
+        for (int ks = 0; ks < nks; ks += GB_STAGES) {
+            kstep(ks, Ms0, Ms3);
+            if (ks + 1 < nks) kstep(ks + 1, Ms1, Ms0);
+            if (ks + 2 < nks) kstep(ks + 2, Ms2, Ms1);
+            if (ks + 3 < nks) kstep(ks + 3, Ms3, Ms2);
+        }
+    }
+    __syncthreads();   // the epilogue reuses nothing of the ring, but every wave leaves the loop together
+
+    // ---- epilogue: residual add, LayerNorm over D, bf16 (fp64) ---------------
+    // lane holds rows 32 rb + lane%32 and features fbase + 32 fb + drow(r, lane)
+    auto xrow_of = [&](int rb) {
+        const int64_t row = min(r0 + rb * 32 + (lane & 31), nrows - 1);
+        return A.x_res + ((g0 + row) % T) * D;
     };
-    auto mfma_sub = [&](const unsigned char* slab, int s_local, const uint4 (&af)[FB]) {
-        const int off = rd_base + (((s_local ^ mk) & 7) << 5);
-        uint4 bfr[2];
+    double mean[2];
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) bfr[rb] = *reinterpret_cast<const uint4*>(slab + off + rb * 32 * GT_KS * 2);
+    for (int rb = 0; rb < 2; ++rb) {
+        const float* xrow = xrow_of(rb);
+        double sv = 0.0;
 #pragma unroll
         for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) acc[fb][rb] = mfma32(af[fb], bfr[rb], acc[fb][rb]);
-    };
-
-    // The two roles run separate loops that meet the same barriers (one after the
-    // prologue, one per k-step, three in the epilogue), so that each role's
-    // registers are live only in its own loop.
-    if (!mfma_wave) {
-        In in_next = load_in(0);
-        setup(0, in_next);
-        if (nks > 1) in_next = load_in(1);
-        gen_pair(0, 0, 0);
-        gen_pair(0, 4, 0);
-        __syncthreads();
-#pragma unroll 1
-        for (int ks = 0; ks < nks; ++ks) {
-            if (ks + 1 < nks) {
-                setup(ks + 1, in_next);
-                if (ks + 2 < nks) in_next = load_in(ks + 2);
-                gen_pair(ks + 1, 0, (ks & 1) ^ 1);
-                gen_pair(ks + 1, 4, (ks & 1) ^ 1);
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const float4 xv = *reinterpret_cast<const float4*>(xrow + fbase + fb * 32 + 8 * r4 + 4 * (lane >> 5));
+                const float xs[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) sv += (double)tot[fb][rb][4 * r4 + c] + (double)xs[c];
             }
-            __syncthreads();
-        }
-        __syncthreads();   // the epilogue's three barriers
-        __syncthreads();
-        __syncthreads();
-        return;
-    }
-
-#pragma unroll
-    for (int r4 = 0; r4 < NV / 4; ++r4) tot[r4][tid] = make_float4(0.f, 0.f, 0.f, 0.f);
-    uint4 fr[2][FB];
-    load_a(0, fr[0]);
-    load_a(1, fr[1]);
-    __syncthreads();
-    // one k-step of the MFMA waves on slab ks (fragments two sub-steps ahead);
-    // FULL: all 128 channels exist
-    auto kstep = [&](int ks, auto full_tag) {
-        constexpr bool FULL = decltype(full_tag)::value;
-        const int buf = ks & 1;
-        const bool more = ks + 1 < nks;
-        const int nsub = FULL ? GT_KS / 16 : (n - ks * GT_KS) / 16;   // even: n is a multiple of 32
-        const unsigned char* slab = reinterpret_cast<const unsigned char*>(&Bs[buf][0]);
-#pragma unroll
-        for (int s2 = 0; s2 < GT_KS / 16; s2 += 2) {
-            if (FULL || s2 < nsub) {
-                const int g = ks * (GT_KS / 16) + s2;
-                mfma_sub(slab, s2, fr[0]);
-                if (g + 2 < nsub_total) load_a(g + 2, fr[0]);
-                mfma_sub(slab, s2 + 1, fr[1]);
-                if (g + 3 < nsub_total) load_a(g + 3, fr[1]);
-            }
-        }
-        if ((ks + 1) % FLUSH == 0 || !more) flush();
-        __syncthreads();
-    };
-#pragma unroll 1
-    for (int ks = 0; ks < nfull; ++ks) kstep(ks, std::integral_constant<bool, true>{});
-    if (nfull < nks) kstep(nfull, std::integral_constant<bool, false>{});
-
-    // ---- epilogue (MFMA waves): residual add, LayerNorm over D, bf16, all in
-    // fp64.  Lane holds rows 32 rb + lane%32
-    // and features fbase + 32 fb + drow(r, lane).
-    double* red = reinterpret_cast<double*>(&Bs[0][0]);   // [NC waves][64 rows]
-    auto yv = [&](int fb, int rb, int r4, const float4& xv, double (&y)[4]) {
-        const float4 o = tot[(fb * 2 + rb) * 4 + r4][tid];
-        y[0] = (double)o.x + (double)xv.x; y[1] = (double)o.y + (double)xv.y;
-        y[2] = (double)o.z + (double)xv.z; y[3] = (double)o.w + (double)xv.w;
-    };
-    auto xrow_of = [&](int rb) {
-        const int r = rb * 32 + (lane & 31);
-        const int t = tb * GT_TB + (r % GT_TB);
-        return A.x_res + (int64_t)(t < T ? t : T - 1) * D;
-    };
-    auto row_total = [&](int r) {
-        double v = 0.0;
-#pragma unroll
-        for (int k = 0; k < NC; ++k) v += red[k * GT_ROWS + r];
-        return v;
-    };
-    double mean[2] = {0.0, 0.0};
-    {
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-            const float* xrow = xrow_of(rb);
-            double sv = 0.0;
-#pragma unroll
-            for (int fb = 0; fb < FB; ++fb)
-#pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    double y[4];
-                    yv(fb, rb, r4, *reinterpret_cast<const float4*>(xrow + fbase + fb * 32 + 8 * r4 + 4 * (lane >> 5)),
-                       y);
-                    sv += (y[0] + y[1]) + (y[2] + y[3]);
-                }
-            sv += __shfl_xor(sv, 32, 64);
-            if (lane < 32) red[w * GT_ROWS + rb * 32 + lane] = sv;
-        }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) mean[rb] = row_total(rb * 32 + (lane & 31)) * (1.0 / D);
-    __syncthreads();
-    {
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-            const float* xrow = xrow_of(rb);
-            double v = 0.0;
-#pragma unroll
-            for (int fb = 0; fb < FB; ++fb)
-#pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    double y[4];
-                    yv(fb, rb, r4, *reinterpret_cast<const float4*>(xrow + fbase + fb * 32 + 8 * r4 + 4 * (lane >> 5)),
-                       y);
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const double dv = y[c] - mean[rb];
-                        v = fma(dv, dv, v);
-                    }
-                }
-            v += __shfl_xor(v, 32, 64);
-            if (lane < 32) red[w * GT_ROWS + rb * 32 + lane] = v;
-        }
+        sv += __shfl_xor(sv, 32, 64);
+        if (lane < 32) red[w][rb * 32 + lane] = sv;
     }
     __syncthreads();
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-        const int r = rb * 32 + (lane & 31);
-        const int t = tb * GT_TB + (r % GT_TB);
-        const int slot = slot_base + r / GT_TB;
-        const double var = row_total(r) * (1.0 / D);
-        const double rstd = 1.0 / sqrt(var + (double)A.ln_eps);
-        if (t >= T || slot >= nslots) continue;
-        const float* xrow = A.x_res + (int64_t)t * D;
-        uint16_t* frow = F + ((int64_t)(first_slot + slot) * T + t) * D;
+        double v = 0.0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v += red[k][rb * 32 + (lane & 31)];
+        mean[rb] = v * (1.0 / D);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const float* xrow = xrow_of(rb);
+        double v = 0.0;
+#pragma unroll
+        for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const float4 xv = *reinterpret_cast<const float4*>(xrow + fbase + fb * 32 + 8 * r4 + 4 * (lane >> 5));
+                const float xs[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const double dv = (double)tot[fb][rb][4 * r4 + c] + (double)xs[c] - mean[rb];
+                    v = fma(dv, dv, v);
+                }
+            }
+        v += __shfl_xor(v, 32, 64);
+        if (lane < 32) red[w][rb * 32 + lane] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const int64_t row = r0 + rb * 32 + (lane & 31);
+        double v = 0.0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v += red[k][rb * 32 + (lane & 31)];
+        const double rstd = 1.0 / sqrt(v * (1.0 / D) + (double)A.ln_eps);
+        if (row >= nrows) continue;
+        const float* xrow = xrow_of(rb);
+        uint16_t* frow = F + row * D;
 #pragma unroll
         for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 const int ff = fbase + fb * 32 + 8 * r4 + 4 * (lane >> 5);
-                double y[4];
-                yv(fb, rb, r4, *reinterpret_cast<const float4*>(xrow + ff), y);
+                const float4 xv = *reinterpret_cast<const float4*>(xrow + ff);
+                const float xs[4] = {xv.x, xv.y, xv.z, xv.w};
                 float o[4];
 #pragma unroll
-                for (int c = 0; c < 4; ++c) o[c] = (float)((y[c] - mean[rb]) * rstd);
+                for (int c = 0; c < 4; ++c)
+                    o[c] = (float)(((double)tot[fb][rb][4 * r4 + c] + (double)xs[c] - mean[rb]) * rstd);
                 *reinterpret_cast<uint2*>(frow + ff) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
             }
     }
@@ -988,10 +1046,16 @@ __global__ void __launch_bounds__(256) mlp_reduce_kernel(MlpArgs A, const float*
 }
 
 // ---------------------------------------------------------------------------
-size_t mlp_chunk_rows(int64_t T, int64_t K, int64_t d) {
-    // F of one chunk (bf16 rows of d) kept to at most 512 MiB; a whole number of token blocks.
+// The GELU operand M of one chunk (bf16 rows of n) is kept to at most 2 GiB and F
+// (bf16 rows of d) to 512 MiB; a chunk is a whole number of token blocks.  A block
+// of T rows whose M exceeds 1 GiB runs the chunk through mlp_gemm1_kernel instead
+// (no M is stored).
+static bool mlp_m_path(int64_t T, int64_t n) { return T * n * 2 <= ((int64_t)1 << 30); }
+
+size_t mlp_chunk_rows(int64_t T, int64_t K, int64_t d, int64_t n) {
     const int64_t total = T * (K + 1);
     int64_t cap = ((int64_t)512 << 20) / (2 * d);
+    if (mlp_m_path(T, n)) cap = std::min<int64_t>(cap, ((int64_t)2 << 30) / (2 * n));
     cap = cap / T * T;
     if (cap < T) cap = T;
     return (size_t)(total < cap ? total : cap);
@@ -1001,7 +1065,7 @@ static size_t al256(size_t v) { return (v + 255) / 256 * 256; }
 
 MlpLayout mlp_layout(int64_t T, int64_t d, int64_t n, int64_t V, int64_t K) {
     MlpLayout L{};
-    L.chunk = (int64_t)mlp_chunk_rows(T, K, d);
+    L.chunk = (int64_t)mlp_chunk_rows(T, K, d, n);
     L.nvt = (int)((V + G2_TV - 1) / G2_TV);
     size_t off = 0;
     L.off_f = off;    off += al256((size_t)L.chunk * d * 2);
@@ -1012,6 +1076,7 @@ MlpLayout mlp_layout(int64_t T, int64_t d, int64_t n, int64_t V, int64_t K) {
     L.off_ghat = off; off += al256((size_t)T * n * sizeof(float));
     L.off_w2f = off;  off += al256((size_t)d * n * 2);
     L.off_phi = off;  off += 2 * al256((size_t)T * n * sizeof(float));
+    L.off_m = off;    off += mlp_m_path(T, n) ? al256((size_t)L.chunk * n * 2) : 0;
     L.off_outer = off;
     off += outer_workspace_bytes(T, n, d);
     L.total = off;
@@ -1034,13 +1099,15 @@ hipError_t launch_mlp(const MlpArgs& A, const MlpLayout& L, unsigned char* ws, f
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(mlp_wnorm_final_kernel, dim3(1), dim3(256), 0, stream, wnorm, nwb, A.d, offset);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    // small sigma: GELU of the draw rows from the cached Phi(h), phi(h) by the
-    // series (mlp_gemm1t_kernel); the clean rows, and every row at larger sigma,
-    // through mlp_gemm1_kernel's library erf
-    const bool taylor = mlp_taylor_ok(A.sigma);
+    // small sigma: M = bf16(GELU(h + sigma a)) of every row from the cached Phi(h),
+    // phi(h) by the series (mlp_gelu_rows_kernel), then F = bf16(LN(x + W2 M)) on
+    // MFMA (mlp_w2ln_kernel); larger sigma (or an M block beyond 1 GiB): both in
+    // mlp_gemm1_kernel with the library erf
+    const bool taylor = mlp_taylor_ok(A.sigma) && mlp_m_path(A.T, A.n);
     const uint16_t* w2f = reinterpret_cast<const uint16_t*>(ws + L.off_w2f);
     float* Pt = reinterpret_cast<float*>(ws + L.off_phi);
     float* pt = reinterpret_cast<float*>(ws + L.off_phi + al256((size_t)A.T * A.n * sizeof(float)));
+    uint16_t* M = reinterpret_cast<uint16_t*>(ws + L.off_m);
     const float sig_u = (float)((double)A.sigma * (double)kSqrt2Ln2);
     if (taylor) {
         const int64_t cnt = (int64_t)A.T * A.n;
@@ -1060,15 +1127,25 @@ hipError_t launch_mlp(const MlpArgs& A, const MlpLayout& L, unsigned char* ws, f
             hipLaunchKernelGGL(mlp_gemm1_kernel<256>, dim3(b1), dim3(G1_NT), 0, stream, A, g0, nrows, F);
         return hipGetLastError();
     };
-    auto gemm1_taylor = [&](int64_t g0, int first_slot, int nslots) {
-        const int ntiles = ((A.T + GT_TB - 1) / GT_TB) * ((nslots + GT_DB - 1) / GT_DB);
-        const unsigned grid = (unsigned)((ntiles + 7) / 8 * 8);
-        if (A.d == 512)
-            hipLaunchKernelGGL(mlp_gemm1t_kernel<512>, dim3(grid), dim3(1024), 0, stream, A, sig_u, w2f, Pt, pt, g0,
-                               first_slot, nslots, ntiles, F);
+    // the GELU rows of slots [first_slot, first_slot + nslots) of the chunk at g0;
+    // the clean slot (zero noise) with s = 0
+    auto gelu_rows = [&](int64_t g0, int first_slot, int nslots, float s) {
+        const int64_t waves = (int64_t)A.T * ((A.n + 255) / 256);
+        hipLaunchKernelGGL(mlp_gelu_rows_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(GA_NT), 0, stream, A, s, Pt, pt,
+                           g0, first_slot, nslots, M);
+        return hipGetLastError();
+    };
+    auto w2ln = [&](int64_t g0, int64_t nrows) {
+        const unsigned b = (unsigned)((nrows + GB_ROWS - 1) / GB_ROWS);
+        const bool fast = A.n % (GB_STAGES * GB_KS) == 0;
+        if (A.d == 512 && fast)
+            hipLaunchKernelGGL((mlp_w2ln_kernel<512, true>), dim3(b), dim3(GB_NT), 0, stream, A, w2f, M, g0, nrows, F);
+        else if (A.d == 512)
+            hipLaunchKernelGGL((mlp_w2ln_kernel<512, false>), dim3(b), dim3(GB_NT), 0, stream, A, w2f, M, g0, nrows, F);
+        else if (fast)
+            hipLaunchKernelGGL((mlp_w2ln_kernel<256, true>), dim3(b), dim3(GB_NT), 0, stream, A, w2f, M, g0, nrows, F);
         else
-            hipLaunchKernelGGL(mlp_gemm1t_kernel<256>, dim3(grid), dim3(1024), 0, stream, A, sig_u, w2f, Pt, pt, g0,
-                               first_slot, nslots, ntiles, F);
+            hipLaunchKernelGGL((mlp_w2ln_kernel<256, false>), dim3(b), dim3(GB_NT), 0, stream, A, w2f, M, g0, nrows, F);
         return hipGetLastError();
     };
     for (int64_t g0 = 0; g0 < total; g0 += L.chunk) {
@@ -1081,8 +1158,9 @@ hipError_t launch_mlp(const MlpArgs& A, const MlpLayout& L, unsigned char* ws, f
             // a chunk is a whole number of slots of T rows; slot 0 of the first is the clean rows
             const int first = g0 == 0 ? 1 : 0;
             const int nslots = (int)(nrows / A.T) - first;
-            if (first && (e = gemm1_direct(0, A.T)) != hipSuccess) return e;
-            if (nslots > 0 && (e = gemm1_taylor(g0, first, nslots)) != hipSuccess) return e;
+            if (first && (e = gelu_rows(0, 0, 1, 0.0f)) != hipSuccess) return e;
+            if (nslots > 0 && (e = gelu_rows(g0, first, nslots, sig_u)) != hipSuccess) return e;
+            if ((e = w2ln(g0, nrows)) != hipSuccess) return e;
         }
         if ((e = launch_timer_end(kTimedMlpGemm1, stream, timed)) != hipSuccess) return e;
         if (A.gemm1_event && (e = hipEventRecord(A.gemm1_event, stream)) != hipSuccess) return e;
