@@ -48,6 +48,15 @@ __device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, const
 // Row of the D layout held by register r of a lane (within a 32x32 block).
 __device__ __forceinline__ int drow(int r, int lane) { return (r & 3) + 8 * (r >> 2) + 4 * (lane >> 5); }
 
+// Tiled layout of the bf16 LayerNorm output F (and of the repacked W_head): tiles
+// of 256 rows, each split into 32-feature slabs of 256 x 32 contiguous elements
+// (16 KB), so that one k-step of the head GEMM reads each operand as one
+// contiguous 16 KB block.  The row count is padded to a whole tile.
+constexpr int FT_ROWS = 256, FT_KS = 32;
+__device__ __forceinline__ int64_t ftile_off(int64_t row, int f, int D) {
+    return ((row / FT_ROWS) * (D / FT_KS) + f / FT_KS) * (FT_ROWS * FT_KS) + (row % FT_ROWS) * FT_KS + f % FT_KS;
+}
+
 // GELU(x) = x Phi(x) (exact erf form), as the fp32 value whose bf16 rounding
 // (nearest even) is taken next.  That decision only depends on the fp32
 // evaluation when the value is not within a few ulps of a bf16 tie; in that
@@ -298,14 +307,14 @@ __global__ void __launch_bounds__(G1_NT, 1) mlp_gemm1_kernel(MlpArgs A, int64_t 
         const double var = row_total(lr) * (1.0 / D);
         const double rstd = 1.0 / sqrt(var + (double)A.ln_eps);
         if (row >= nrows) continue;
-        uint16_t* frow = F + row * D;
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
             const int ff = fg * 32 + 8 * r4 + 4 * (lane >> 5);
             float o[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) o[c] = (float)((y[rb][4 * r4 + c] - mean[rb]) * rstd);
-            *reinterpret_cast<uint2*>(frow + ff) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+            *reinterpret_cast<uint2*>(F + ftile_off(row, ff, D)) =
+                make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
         }
     }
 }
@@ -744,7 +753,6 @@ __global__ void __launch_bounds__(GB_NT, 1) mlp_w2ln_kernel(MlpArgs A, const uin
         const double rstd = 1.0 / sqrt(v * (1.0 / D) + (double)A.ln_eps);
         if (row >= nrows) continue;
         const float* xrow = xrow_of(rb);
-        uint16_t* frow = F + row * D;
 #pragma unroll
         for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
@@ -756,7 +764,8 @@ __global__ void __launch_bounds__(GB_NT, 1) mlp_w2ln_kernel(MlpArgs A, const uin
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
                     o[c] = (float)(((double)tot[fb][rb][4 * r4 + c] + (double)xs[c] - mean[rb]) * rstd);
-                *reinterpret_cast<uint2*>(frow + ff) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+                *reinterpret_cast<uint2*>(F + ftile_off(row, ff, D)) =
+                    make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
             }
     }
 }
@@ -764,14 +773,14 @@ __global__ void __launch_bounds__(GB_NT, 1) mlp_w2ln_kernel(MlpArgs A, const uin
 // ---------------------------------------------------------------------------
 // gemm2: per (vocab tile of 256, row): partial log-sum-exp of z = W_head F
 // and the label logit.  Workgroup tile 256 vocab x 256 rows, 8 waves of
-// 128 vocab x 64 rows (4 x 2 MFMA blocks, 128 accumulators); both operands
-// go straight from global memory into double-buffered LDS in 64-wide k-steps,
-// and each wave reads the fragments of the next 16-channel sub-step while the
+// 128 vocab x 64 rows (4 x 2 MFMA blocks, 128 accumulators).  Both operands go
+// from global memory straight into a four-stage LDS ring in 32-wide k-steps
+// (buffer loads into LDS, three k-steps in flight ahead of the one computed);
+// each wave reads the fragments of the next 16-channel sub-step while the
 // current sub-step's MFMAs issue.  A 128 x 128 wave tile would read a third
-// less LDS per MFMA, but its 256 accumulators leave one wave per SIMD, which
-// measured slower.
+// less LDS per MFMA, but its 256 accumulators leave one wave per SIMD.
 // ---------------------------------------------------------------------------
-constexpr int G2_TV = 256, G2_TR = 256, G2_KS = 64;
+constexpr int G2_TV = FT_ROWS, G2_TR = FT_ROWS, G2_KS = FT_KS, G2_STAGES = 4;
 constexpr int G2_VB = 4, G2_RB = 2;   // MFMA blocks per wave (vocab, rows): 128 x 64
 constexpr int G2_WAVES = 8;           // 2 vocab halves x 4 row quarters
 constexpr int G2_NT = 64 * G2_WAVES;
@@ -781,6 +790,28 @@ constexpr int G2_WR = G2_RB * 32;     // rows per wave
 // max_v |w_v| <= 40, every term exp(z - C) lies in [e^-80, 1]: no overflow,
 // no underflow, so the running maximum (and its second pass) can be skipped.
 constexpr float G2_FIXED_MAX = 40.0f;
+
+// LDS element offset of 16-byte piece `piece` (0..3) of tile row `row` in a
+// 32-channel k-step slab: rows are 64 bytes apart and the piece is XORed with
+// (row / 4) % 4, so the 16 lanes of one row-group read 16 distinct 16-byte bank
+// groups.
+__device__ __forceinline__ int swz32(int row, int piece) { return row * 32 + ((piece ^ ((row >> 2) & 3)) << 3); }
+
+// W_head [V][d] -> tiled layout (ftile_off), rows past V zero.
+__global__ void __launch_bounds__(256) mlp_wtile_kernel(const uint16_t* __restrict__ w, int V, int D, int nvt,
+                                                        uint16_t* __restrict__ wt) {
+    const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 16-byte piece of the tiled array
+    if (p >= (int64_t)nvt * FT_ROWS * D / 8) return;
+    const int64_t e = p * 8;
+    const int64_t slab = e / (FT_ROWS * FT_KS);
+    const int within = (int)(e % (FT_ROWS * FT_KS));
+    const int nks = D / FT_KS;
+    const int v = (int)(slab / nks) * FT_ROWS + within / FT_KS;
+    const int f = (int)(slab % nks) * FT_KS + within % FT_KS;
+    uint4 q = make_uint4(0u, 0u, 0u, 0u);
+    if (v < V) q = *reinterpret_cast<const uint4*>(w + (int64_t)v * D + f);
+    *reinterpret_cast<uint4*>(wt + e) = q;
+}
 
 
 // Largest row norm of W_head, as an fp32 upper bound (one workgroup per 256
@@ -824,12 +855,13 @@ __global__ void __launch_bounds__(256) mlp_wnorm_final_kernel(const float* __res
 }
 
 __global__ void __launch_bounds__(G2_NT, 1) mlp_gemm2_kernel(MlpArgs A, int64_t g0, int64_t nrows, int nvt,
+                                                            const uint16_t* __restrict__ Wt,
                                                             const uint16_t* __restrict__ F, float2* __restrict__ part,
                                                             float* __restrict__ zy, const float* __restrict__ offset) {
-    // two buffers per operand as separate LDS objects: reads from one provably
-    // do not alias direct loads in flight into the other
-    __shared__ __align__(16) uint16_t As0[G2_TV * G2_KS], As1[G2_TV * G2_KS];
-    __shared__ __align__(16) uint16_t Bs0[G2_TR * G2_KS], Bs1[G2_TR * G2_KS];
+    // the ring stages as separate LDS objects: reads of one provably do not
+    // alias loads in flight into another
+    __shared__ __align__(16) uint16_t As0[G2_TV * G2_KS], As1[G2_TV * G2_KS], As2[G2_TV * G2_KS], As3[G2_TV * G2_KS];
+    __shared__ __align__(16) uint16_t Bs0[G2_TR * G2_KS], Bs1[G2_TR * G2_KS], Bs2[G2_TR * G2_KS], Bs3[G2_TR * G2_KS];
     __shared__ float2 red[2][G2_TR];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -843,31 +875,34 @@ __global__ void __launch_bounds__(G2_NT, 1) mlp_gemm2_kernel(MlpArgs A, int64_t 
     const int64_t r0 = rt * G2_TR;
     const int D = A.d, V = A.V;
 
-    // Each operand tile is 256 rows x 64 k = 2048 pieces of 16 bytes, loaded
-    // straight from global memory into LDS (no register staging).  A direct
-    // load puts lane l of a wave at LDS slot base + l, so the swizzle is applied
-    // on the global side: the lane whose slot s = 8 row + p' holds logical piece
-    // p' ^ ((row >> 1) & 7) of that row.  Rows past V or past the chunk read a
-    // clamped, valid row (those columns are masked and those rows discarded
-    // below), so every load is unconditional.
-    constexpr int NL = 2048 / G2_NT;   // loads per lane per operand and k-step
-    int offa[NL], offb[NL];            // element offsets of this lane's pieces (k-step 0)
+    // Both operands are in the tiled layout: the k-step slab of a tile is 256 rows
+    // x 64 bytes, contiguous.  Each slab is 1024 pieces of 16 bytes, two per lane.
+    // A load into LDS puts lane l of a wave at LDS slot base + l, so the swizzle
+    // is applied on the global side: slot s = 4 row + p' holds logical piece
+    // p' ^ ((row >> 2) & 3) of that row.  The W_head tiles are zero past V; the
+    // rows of the last F tile past the chunk hold stale values, which only reach
+    // those rows' outputs, discarded below.
+    constexpr int NL = G2_TV * 4 / G2_NT;   // loads per lane per operand and k-step
+    const __amdgpu_buffer_rsrc_t ares =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Wt + (int64_t)vt * G2_TV * D), (short)0, G2_TV * D * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t bres =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(F + rt * G2_TR * D), (short)0, G2_TR * D * 2, 0x00020000);
+    int voff[NL];   // byte offsets of this lane's pieces within a slab (same for both operands)
 #pragma unroll
     for (int jj = 0; jj < NL; ++jj) {
         const int slot = (jj * G2_WAVES + w) * 64 + lane;
-        const int row = slot >> 3, piece = (slot & 7) ^ ((row >> 1) & 7);
-        const int v = min(v0 + row, V - 1);
-        const int64_t rr = min(r0 + (int64_t)row, nrows - 1);
-        offa[jj] = v * D + 8 * piece;
-        offb[jj] = (int)(rr - r0) * D + 8 * piece;
+        const int row = slot >> 2, piece = (slot & 3) ^ ((row >> 2) & 3);
+        voff[jj] = row * (G2_KS * 2) + 16 * piece;
     }
-    const uint16_t* Fr = F + r0 * D;
-    auto issue_loads = [&](int ks, uint16_t* as, uint16_t* bs) {
+    auto issue_ks = [&](int ks, uint16_t* as, uint16_t* bs) {
 #pragma unroll
         for (int jj = 0; jj < NL; ++jj) {
             const int base = (jj * G2_WAVES + w) * 64 * 8;  // element offset of this wave's 64 slots
-            __builtin_amdgcn_global_load_lds(A.w_head + offa[jj] + ks * G2_KS, as + base, 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(Fr + offb[jj] + ks * G2_KS, bs + base, 16, 0, 0);
+            const int off = voff[jj] + ks * (G2_TV * G2_KS * 2);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ares, (__attribute__((address_space(3))) void*)(as + base), 16, off,
+                                                     0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(bres, (__attribute__((address_space(3))) void*)(bs + base), 16, off,
+                                                     0, 0, 0);
         }
     };
 
@@ -879,56 +914,72 @@ __global__ void __launch_bounds__(G2_NT, 1) mlp_gemm2_kernel(MlpArgs A, int64_t 
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // One k-step on (as, bs) while the next tile lands in (as_n, bs_n).  The
-    // fragments of 16-channel sub-step kk + 1 are read while sub-step kk's
-    // MFMAs issue (one LDS read per MFMA), so LDS latency hides behind MFMA work.
     auto read_frags = [&](const uint16_t* as, const uint16_t* bs, int kk, uint4 (&a)[G2_VB], uint4 (&b)[G2_RB]) {
         const int piece = kk * 2 + (lane >> 5);
 #pragma unroll
         for (int i = 0; i < G2_VB; ++i)
-            a[i] = *reinterpret_cast<const uint4*>(&as[swz(wv * 128 + i * 32 + (lane & 31), piece)]);
+            a[i] = *reinterpret_cast<const uint4*>(&as[swz32(wv * 128 + i * 32 + (lane & 31), piece)]);
 #pragma unroll
         for (int j = 0; j < G2_RB; ++j)
-            b[j] = *reinterpret_cast<const uint4*>(&bs[swz(wr * G2_WR + j * 32 + (lane & 31), piece)]);
+            b[j] = *reinterpret_cast<const uint4*>(&bs[swz32(wr * G2_WR + j * 32 + (lane & 31), piece)]);
     };
-    auto kstep = [&](int ks, const uint16_t* as, const uint16_t* bs, uint16_t* as_n, uint16_t* bs_n, bool more) {
-        if (more) issue_loads(ks + 1, as_n, bs_n);
-        uint4 af[2][G2_VB], bfr[2][G2_RB];
-        read_frags(as, bs, 0, af[0], bfr[0]);
+    // k-step ks works on stage ks % 4 (its second sub-step; the first one's
+    // fragments were read during k-step ks - 1) and reads the first sub-step of
+    // slab ks + 1 from stage (ks + 1) % 4, so it starts once slab ks + 1 has
+    // landed: only the 2 NL loads of slab ks + 2 may be outstanding.  Past its
+    // barrier every wave has finished k-step ks - 1, so stage (ks + 3) % 4 takes
+    // slab ks + 3 (clamped to the last one: every k-step issues the same loads).
+    const int nks = D / G2_KS;   // a multiple of 4: D is 256 or 512
+    uint4 af[2][G2_VB], bfr[2][G2_RB];
+    auto kstep = [&](int ks, const uint16_t* as, const uint16_t* bs, const uint16_t* as1, const uint16_t* bs1,
+                     uint16_t* as_n, uint16_t* bs_n) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NL));
+        // a barrier without the full memory wait that __syncthreads adds; the
+        // memory clobber keeps LDS accesses on their side of it
+        asm volatile("s_barrier" ::: "memory");
+        issue_ks(min(ks + G2_STAGES - 1, nks - 1), as_n, bs_n);
+        read_frags(as, bs, 1, af[1], bfr[1]);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            if (kk < 3) read_frags(as, bs, kk + 1, af[(kk + 1) & 1], bfr[(kk + 1) & 1]);
+        for (int i = 0; i < G2_VB; ++i)
 #pragma unroll
-            for (int i = 0; i < G2_VB; ++i)
+            for (int j = 0; j < G2_RB; ++j) acc[i][j] = mfma32(af[0][i], bfr[0][j], acc[i][j]);
+        read_frags(as1, bs1, 0, af[0], bfr[0]);   // past the last k-step: a stage of valid data, unused
 #pragma unroll
-                for (int j = 0; j < G2_RB; ++j) acc[i][j] = mfma32(af[kk & 1][i], bfr[kk & 1][j], acc[i][j]);
-        }
-        // order: direct loads, the first sub-step's reads, then per sub-step
-        // its MFMAs interleaved with the next sub-step's reads
-        __builtin_amdgcn_sched_group_barrier(0x020, 2 * NL, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, G2_VB + G2_RB, 0);
+        for (int i = 0; i < G2_VB; ++i)
 #pragma unroll
-        for (int kk = 0; kk < 3; ++kk) {
+            for (int j = 0; j < G2_RB; ++j) acc[i][j] = mfma32(af[1][i], bfr[1][j], acc[i][j]);
+        // each sub-step's MFMAs interleaved with the fragment reads of the next
+        // one, the loads spread between MFMAs (a wave issues in order: a burst of
+        // loads waiting for the address unit would hold back the MFMAs behind it)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
 #pragma unroll
             for (int q = 0; q < G2_VB + G2_RB; ++q) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, G2_VB * G2_RB - (G2_VB + G2_RB), 0);
+#pragma unroll
+            for (int q = 0; q < NL; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, G2_VB * G2_RB - (G2_VB + G2_RB) - NL, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, G2_VB * G2_RB, 0);
-        __builtin_amdgcn_s_waitcnt(0);  // the next tile's direct loads have landed
-        __syncthreads();
     };
 
-    const int nks = D / G2_KS;  // even: D is 256 or 512
-    issue_loads(0, As0, Bs0);
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
-    __syncthreads();
-    for (int ks = 0; ks < nks; ks += 2) {
-        kstep(ks, As0, Bs0, As1, Bs1, true);
-        kstep(ks + 1, As1, Bs1, As0, Bs0, ks + 2 < nks);
+    issue_ks(0, As0, Bs0);
+    issue_ks(1, As1, Bs1);
+    issue_ks(2, As2, Bs2);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * NL));   // slab 0
+    asm volatile("s_barrier" ::: "memory");
+    read_frags(As0, Bs0, 0, af[0], bfr[0]);
+    for (int ks = 0; ks < nks; ks += G2_STAGES) {
+        kstep(ks, As0, Bs0, As1, Bs1, As3, Bs3);
+        kstep(ks + 1, As1, Bs1, As2, Bs2, As0, Bs0);
+        kstep(ks + 2, As2, Bs2, As3, Bs3, As1, Bs1);
+        kstep(ks + 3, As3, Bs3, As0, Bs0, As2, Bs2);
     }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the clamped loads past the end
 
     // ---- epilogue: per row, log-sum-exp over this tile's vocabulary ---------
     // lane holds rows j = wr*G2_WR + rb*32 + lane%32, vocab v0 + wv*128 + vb*32 + drow(r, lane)
@@ -1068,7 +1119,8 @@ MlpLayout mlp_layout(int64_t T, int64_t d, int64_t n, int64_t V, int64_t K) {
     L.chunk = (int64_t)mlp_chunk_rows(T, K, d, n);
     L.nvt = (int)((V + G2_TV - 1) / G2_TV);
     size_t off = 0;
-    L.off_f = off;    off += al256((size_t)L.chunk * d * 2);
+    L.off_f = off;    off += al256((size_t)((L.chunk + FT_ROWS - 1) / FT_ROWS) * FT_ROWS * d * 2);
+    L.off_wt = off;   off += al256((size_t)L.nvt * G2_TV * d * 2);
     L.off_part = off; off += al256((size_t)L.chunk * L.nvt * sizeof(float2));
     L.off_zy = off;   off += al256((size_t)L.chunk * sizeof(float));
     L.off_wnorm = off; off += al256((size_t)((V + 255) / 256 + 1) * sizeof(float));
@@ -1098,6 +1150,11 @@ hipError_t launch_mlp(const MlpArgs& A, const MlpLayout& L, unsigned char* ws, f
     hipLaunchKernelGGL(mlp_wnorm_kernel, dim3((unsigned)nwb), dim3(256), 0, stream, A.w_head, A.V, A.d, wnorm);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(mlp_wnorm_final_kernel, dim3(1), dim3(256), 0, stream, wnorm, nwb, A.d, offset);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    uint16_t* Wt = reinterpret_cast<uint16_t*>(ws + L.off_wt);
+    const int64_t wpieces = (int64_t)L.nvt * G2_TV * A.d / 8;
+    hipLaunchKernelGGL(mlp_wtile_kernel, dim3((unsigned)((wpieces + 255) / 256)), dim3(256), 0, stream, A.w_head, A.V,
+                       A.d, L.nvt, Wt);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // small sigma: M = bf16(GELU(h + sigma a)) of every row from the cached Phi(h),
     // phi(h) by the series (mlp_gelu_rows_kernel), then F = bf16(LN(x + W2 M)) on
@@ -1167,7 +1224,7 @@ hipError_t launch_mlp(const MlpArgs& A, const MlpLayout& L, unsigned char* ws, f
         const int64_t nrt = (nrows + G2_TR - 1) / G2_TR;
         if ((e = launch_timer_begin(kTimedMlpGemm2, stream, timed)) != hipSuccess) return e;
         hipLaunchKernelGGL(mlp_gemm2_kernel, dim3((unsigned)(nrt * L.nvt)), dim3(G2_NT), 0, stream, A, g0, nrows,
-                           L.nvt, F, part, zy, offset);
+                           L.nvt, Wt, F, part, zy, offset);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = launch_timer_end(kTimedMlpGemm2, stream, timed)) != hipSuccess) return e;
         if (A.gemm2_event && (e = hipEventRecord(A.gemm2_event, stream)) != hipSuccess) return e;
