@@ -854,7 +854,7 @@ __global__ void __launch_bounds__(256) mlp_wnorm_final_kernel(const float* __res
     }
 }
 
-__global__ void __launch_bounds__(G2_NT, 1) mlp_gemm2_kernel(MlpArgs A, int64_t g0, int64_t nrows, int nvt,
+__global__ void __launch_bounds__(G2_NT, 1) mlp_gemm2_kernel(MlpArgs A, int64_t g0, int64_t nrows, int64_t nrt, int nvt,
                                                             const uint16_t* __restrict__ Wt,
                                                             const uint16_t* __restrict__ F, float2* __restrict__ part,
                                                             float* __restrict__ zy, const float* __restrict__ offset) {
@@ -866,11 +866,24 @@ __global__ void __launch_bounds__(G2_NT, 1) mlp_gemm2_kernel(MlpArgs A, int64_t 
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wv = w & 1, wr = w >> 1;
-    // vocab tile fastest: with a tile count that is a multiple of 8, each XCD
-    // keeps revisiting the same eighth of W_head, which then stays in its L2,
-    // and the workgroups sharing a row tile on one XCD run back to back.
-    const int vt = blockIdx.x % nvt;
-    const int64_t rt = blockIdx.x / nvt;
+    // XCD-aware order (workgroup b runs on XCD b % 8).  With a vocabulary tile
+    // count that is a multiple of 4, the vocabulary is split into 4 groups; XCDs
+    // 2g and 2g + 1 take group g, alternating over the row tiles, and on one XCD
+    // the group's tiles of a row tile run back to back.  Each F tile then leaves
+    // HBM 4 times (once per group) and each XCD keeps a quarter of W_head in its
+    // L2.  Otherwise: vocabulary tile fastest.
+    int vt;
+    int64_t rt;
+    if ((nvt & 3) == 0) {
+        const int x = blockIdx.x & 7, gv = nvt >> 2;
+        const int64_t i = blockIdx.x >> 3;
+        rt = 2 * (i / gv) + (x & 1);
+        vt = (x >> 1) * gv + (int)(i % gv);
+        if (rt >= nrt) return;   // the odd row tile's empty twin (whole workgroup)
+    } else {
+        vt = blockIdx.x % nvt;
+        rt = blockIdx.x / nvt;
+    }
     const int v0 = vt * G2_TV;
     const int64_t r0 = rt * G2_TR;
     const int D = A.d, V = A.V;
@@ -1223,8 +1236,9 @@ hipError_t launch_mlp(const MlpArgs& A, const MlpLayout& L, unsigned char* ws, f
         if (A.gemm1_event && (e = hipEventRecord(A.gemm1_event, stream)) != hipSuccess) return e;
         const int64_t nrt = (nrows + G2_TR - 1) / G2_TR;
         if ((e = launch_timer_begin(kTimedMlpGemm2, stream, timed)) != hipSuccess) return e;
-        hipLaunchKernelGGL(mlp_gemm2_kernel, dim3((unsigned)(nrt * L.nvt)), dim3(G2_NT), 0, stream, A, g0, nrows,
-                           L.nvt, Wt, F, part, zy, offset);
+        const int64_t nb2 = (L.nvt & 3) == 0 ? 2 * L.nvt * ((nrt + 1) / 2) : nrt * L.nvt;
+        hipLaunchKernelGGL(mlp_gemm2_kernel, dim3((unsigned)nb2), dim3(G2_NT), 0, stream, A, g0, nrows, nrt, L.nvt, Wt,
+                           F, part, zy, offset);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = launch_timer_end(kTimedMlpGemm2, stream, timed)) != hipSuccess) return e;
         if (A.gemm2_event && (e = hipEventRecord(A.gemm2_event, stream)) != hipSuccess) return e;
