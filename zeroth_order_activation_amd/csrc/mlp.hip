@@ -519,7 +519,7 @@ __global__ void __launch_bounds__(GB_NT, 1) mlp_w2ln_kernel(MlpArgs A, const uin
     // and does not drain those loads before each read
     __shared__ __align__(16) uint16_t Ms0[GB_ROWS * GB_KS], Ms1[GB_ROWS * GB_KS], Ms2[GB_ROWS * GB_KS],
         Ms3[GB_ROWS * GB_KS];
-    __shared__ double red[8][GB_ROWS];
+    __shared__ double red[2][8][GB_ROWS];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int T = A.T, n = A.n;
@@ -637,28 +637,33 @@ __global__ void __launch_bounds__(GB_NT, 1) mlp_w2ln_kernel(MlpArgs A, const uin
             }
     };
     if (FAST) {
-        // branch-free k-step: slab ks + 3 and the fragments PF sub-steps ahead are
-        // loaded unconditionally (clamped to the last ones), so every k-step issues
-        // 8 FB + 2 loads and, from the third on, slab ks has landed once at most
-        // 16 FB + 4 operations are outstanding
-        auto kfast = [&](int ks, const uint16_t* cur, uint16_t* nxt, int wait) {
-            if (wait == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
-            else if (wait == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(8 * FB + 4));
-            else __builtin_amdgcn_s_waitcnt(vmcnt_imm(16 * FB + 4));
+        // Branch-free k-steps: every one issues the same 8 FB + 2 loads (the
+        // fragments PF sub-steps ahead and slab ks + 3, both clamped to the last
+        // ones), so the waits are exact.  K-step ks reads the first sub-step of
+        // slab ks + 1 during its last sub-step (the fragments of the next sub-step
+        // are always read while the current one's MFMAs issue), so it starts once
+        // slab ks + 1 has landed: then at most the 8 FB + 2 loads of k-step ks - 1
+        // (the 2 of slab 2 before k-step 0) are outstanding.
+        uint4 bq[2][2];
+        auto read_b = [&](const uint16_t* st, int s, uint4 (&b)[2]) {
+            const unsigned char* slab = reinterpret_cast<const unsigned char*>(st);
+            const int off = rd_base + (((s ^ mk) & 7) << 5);
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) b[rb] = *reinterpret_cast<const uint4*>(slab + off + rb * 32 * GB_KS * 2);
+        };
+        auto kfast = [&](int ks, const uint16_t* cur, const uint16_t* nx1, uint16_t* nxt, bool first) {
+            if (first) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2));
+            else __builtin_amdgcn_s_waitcnt(vmcnt_imm(8 * FB + 2));
             asm volatile("s_barrier" ::: "memory");
-            const unsigned char* slab = reinterpret_cast<const unsigned char*>(cur);
 #pragma unroll
             for (int s = 0; s < GB_KS / 16; ++s) {
                 const int g = ks * (GB_KS / 16) + s;
-                const int off = rd_base + (((s ^ mk) & 7) << 5);
-                uint4 bfr[2];
-#pragma unroll
-                for (int rb = 0; rb < 2; ++rb)
-                    bfr[rb] = *reinterpret_cast<const uint4*>(slab + off + rb * 32 * GB_KS * 2);
+                if (s + 1 < GB_KS / 16) read_b(cur, s + 1, bq[(s + 1) & 1]);
+                else read_b(nx1, 0, bq[0]);
 #pragma unroll
                 for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
-                    for (int rb = 0; rb < 2; ++rb) acc[fb][rb] = mfma32(fr[s % PF][fb], bfr[rb], acc[fb][rb]);
+                    for (int rb = 0; rb < 2; ++rb) acc[fb][rb] = mfma32(fr[s % PF][fb], bq[s & 1][rb], acc[fb][rb]);
                 load_a(min(g + PF, nsub_total - 1), fr[s % PF]);
             }
             issue_ks(min(ks + GB_STAGES - 1, nks - 1), nxt);
@@ -671,15 +676,18 @@ __global__ void __launch_bounds__(GB_NT, 1) mlp_w2ln_kernel(MlpArgs A, const uin
                     acc[fb][rb] = zero;
                 }
         };
-        kfast(0, Ms0, Ms3, 0);
-        kfast(1, Ms1, Ms0, 1);
-        kfast(2, Ms2, Ms1, 2);
-        kfast(3, Ms3, Ms2, 2);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));   // slab 0
+        asm volatile("s_barrier" ::: "memory");
+        read_b(Ms0, 0, bq[0]);
+        kfast(0, Ms0, Ms1, Ms3, true);
+        kfast(1, Ms1, Ms2, Ms0, false);
+        kfast(2, Ms2, Ms3, Ms1, false);
+        kfast(3, Ms3, Ms0, Ms2, false);
         for (int ks = 4; ks < nks; ks += GB_STAGES) {
-            kfast(ks, Ms0, Ms3, 2);
-            kfast(ks + 1, Ms1, Ms0, 2);
-            kfast(ks + 2, Ms2, Ms1, 2);
-            kfast(ks + 3, Ms3, Ms2, 2);
+            kfast(ks, Ms0, Ms1, Ms3, false);
+            kfast(ks + 1, Ms1, Ms2, Ms0, false);
+            kfast(ks + 2, Ms2, Ms3, Ms1, false);
+            kfast(ks + 3, Ms3, Ms0, Ms2, false);
         }
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the loads past the end
     } else {
@@ -693,77 +701,71 @@ __global__ void __launch_bounds__(GB_NT, 1) mlp_w2ln_kernel(MlpArgs A, const uin
     __syncthreads();   // the epilogue reuses nothing of the ring, but every wave leaves the loop together
 
     // ---- epilogue: residual add, LayerNorm over D, bf16 (fp64) ---------------
-    // lane holds rows 32 rb + lane%32 and features fbase + 32 fb + drow(r, lane)
-    auto xrow_of = [&](int rb) {
+    // lane holds rows 32 rb + lane%32 and features fbase + 32 fb + drow(r, lane).
+    // The residual values are loaded once, into the registers the accumulators
+    // held.  One pass takes the shifted sums S1 = sum (y - c), S2 = sum (y - c)^2
+    // with c = x[row][0] (the same for every lane of the row): mean = c + S1 / D
+    // and var = S2 / D - (S1 / D)^2, without cancellation as c lies within the
+    // row's values.
+    float xv[FB][2][16];
+    double csh[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
         const int64_t row = min(r0 + rb * 32 + (lane & 31), nrows - 1);
-        return A.x_res + ((g0 + row) % T) * D;
-    };
-    double mean[2];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        const float* xrow = xrow_of(rb);
-        double sv = 0.0;
+        const float* xrow = A.x_res + ((g0 + row) % T) * D;
+        csh[rb] = (double)xrow[0];
 #pragma unroll
         for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
-                const float4 xv = *reinterpret_cast<const float4*>(xrow + fbase + fb * 32 + 8 * r4 + 4 * (lane >> 5));
-                const float xs[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-                for (int c = 0; c < 4; ++c) sv += (double)tot[fb][rb][4 * r4 + c] + (double)xs[c];
+                const float4 q = *reinterpret_cast<const float4*>(xrow + fbase + fb * 32 + 8 * r4 + 4 * (lane >> 5));
+                xv[fb][rb][4 * r4 + 0] = q.x;
+                xv[fb][rb][4 * r4 + 1] = q.y;
+                xv[fb][rb][4 * r4 + 2] = q.z;
+                xv[fb][rb][4 * r4 + 3] = q.w;
             }
-        sv += __shfl_xor(sv, 32, 64);
-        if (lane < 32) red[w][rb * 32 + lane] = sv;
     }
-    __syncthreads();
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-        double v = 0.0;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) v += red[k][rb * 32 + (lane & 31)];
-        mean[rb] = v * (1.0 / D);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        const float* xrow = xrow_of(rb);
-        double v = 0.0;
+        double s1 = 0.0, s2 = 0.0;
 #pragma unroll
         for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const float4 xv = *reinterpret_cast<const float4*>(xrow + fbase + fb * 32 + 8 * r4 + 4 * (lane >> 5));
-                const float xs[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const double dv = (double)tot[fb][rb][4 * r4 + c] + (double)xs[c] - mean[rb];
-                    v = fma(dv, dv, v);
-                }
+            for (int r = 0; r < 16; ++r) {
+                const double dv = ((double)tot[fb][rb][r] + (double)xv[fb][rb][r]) - csh[rb];
+                s1 += dv;
+                s2 = fma(dv, dv, s2);
             }
-        v += __shfl_xor(v, 32, 64);
-        if (lane < 32) red[w][rb * 32 + lane] = v;
+        s1 += __shfl_xor(s1, 32, 64);
+        s2 += __shfl_xor(s2, 32, 64);
+        if (lane < 32) {
+            red[0][w][rb * 32 + lane] = s1;
+            red[1][w][rb * 32 + lane] = s2;
+        }
     }
     __syncthreads();
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
         const int64_t row = r0 + rb * 32 + (lane & 31);
-        double v = 0.0;
+        double s1 = 0.0, s2 = 0.0;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v += red[k][rb * 32 + (lane & 31)];
-        const double rstd = 1.0 / sqrt(v * (1.0 / D) + (double)A.ln_eps);
+        for (int k = 0; k < 8; ++k) {
+            s1 += red[0][k][rb * 32 + (lane & 31)];
+            s2 += red[1][k][rb * 32 + (lane & 31)];
+        }
+        const double m1 = s1 * (1.0 / D);
+        const double mean = csh[rb] + m1;
+        const double rstd = 1.0 / sqrt(fma(-m1, m1, s2 * (1.0 / D)) + (double)A.ln_eps);
         if (row >= nrows) continue;
-        const float* xrow = xrow_of(rb);
 #pragma unroll
         for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 const int ff = fbase + fb * 32 + 8 * r4 + 4 * (lane >> 5);
-                const float4 xv = *reinterpret_cast<const float4*>(xrow + ff);
-                const float xs[4] = {xv.x, xv.y, xv.z, xv.w};
                 float o[4];
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                    o[c] = (float)(((double)tot[fb][rb][4 * r4 + c] + (double)xs[c] - mean[rb]) * rstd);
+                    o[c] = (float)((((double)tot[fb][rb][4 * r4 + c] + (double)xv[fb][rb][4 * r4 + c]) - mean) * rstd);
                 *reinterpret_cast<uint2*>(F + ftile_off(row, ff, D)) =
                     make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
             }
