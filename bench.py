@@ -807,6 +807,10 @@ def main():
         mlp.pop("_kind")
         for k in ("n_gpus", "higher_is_better", "scaling", "data", "warmup", "steps"):
             mlp.pop(k, None)
+        if "alu_probe" in out:
+            sus = out["alu_probe"]["mfma_bf16"]["TFLOP_per_s"]
+            mlp["roofline"]["peak_measured_mfma_TFLOPs"] = sus
+            mlp["roofline"]["frac_of_measured_mfma"] = mlp["roofline"]["achieved"] / sus
         out["mlp_linear"] = mlp
     print(json.dumps(out), flush=True)
 
@@ -853,6 +857,22 @@ def alu_probe(torch):
     # the head mix: 8 channel quads = 32 channel-draws per lane and loop trip
     res["head_mix"]["channel_draws_per_s"] = 32 * 256 * blocks * iters[3] / (res["head_mix"]["ms"] / 1e3)
     res["head_mix"]["valu_per_channel_draw"] = per_trip[3] / 32
+    # the matrix cores: 8 independent v_mfma_f32_32x32x16_bf16 chains per wave on non-zero data
+    mf_iters = 64
+    for rep in range(2):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        rc = L.dust_probe_valu_mix(4, blocks, mf_iters, ctypes.c_void_p(gin.data_ptr()),
+                                   ctypes.c_void_p(gout.data_ptr()), stream)
+        b.record()
+        torch.cuda.synchronize()
+        if rc != 0:
+            raise RuntimeError(f"probe mix 4 failed: {rc}")
+    ms = a.elapsed_time(b)
+    tf = 2.0 * 32 * 32 * 16 * 8 * mf_iters * blocks * 4 / (ms / 1e3) / 1e12
+    res["mfma_bf16"] = {"ms": ms, "TFLOP_per_s": tf, "frac_of_peak": tf / MFMA_BF16_PEAK_TFLOPS,
+                        "note": "register-only loop of v_mfma_f32_32x32x16_bf16, 8 independent accumulators per "
+                                "wave, operands from random data: the sustained matrix-core rate"}
     res["note"] = ("register-only loops over 8192 workgroups of 256 lanes; rates are vector instructions x 64 lanes "
                    "per second (one issue slot per instruction), against 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz")
     return res

@@ -14,6 +14,9 @@
 //          Box-Muller, the degree-4 expm1 polynomial weighted by p, and the
 //          running sums of r a -- without the per-draw reduction, barrier and
 //          reward, and without memory traffic.
+//   mix 4  v_mfma_f32_32x32x16_bf16 only: eight independent accumulators per
+//          wave, operands taken from `in` (the sustained matrix-core rate with
+//          non-trivial data; rated in flops, not lane-ops).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -127,9 +130,42 @@ __global__ void __launch_bounds__(kNT) mix_head_kernel(const float* __restrict__
     out[blockIdx.x * kNT + tid] = s;
 }
 
+typedef __bf16 pbf16x8_t __attribute__((ext_vector_type(8)));
+typedef float pf32x16_t __attribute__((ext_vector_type(16)));
+
+__global__ void __launch_bounds__(kNT) mix_mfma_kernel(const float* __restrict__ in, float* __restrict__ out, int iters) {
+    const int lane = threadIdx.x & 63;
+    uint32_t ua[4], ub[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {   // bf16 pairs from the upper halves of two floats
+        ua[k] = (__float_as_uint(in[(2 * (lane + 8 * k)) & 1023]) >> 16) |
+                (__float_as_uint(in[(2 * (lane + 8 * k) + 1) & 1023]) & 0xFFFF0000u);
+        ub[k] = (__float_as_uint(in[(2 * (lane + 8 * k) + 512) & 1023]) >> 16) |
+                (__float_as_uint(in[(2 * (lane + 8 * k) + 513) & 1023]) & 0xFFFF0000u);
+    }
+    pbf16x8_t a, b;
+    __builtin_memcpy(&a, ua, 16);
+    __builtin_memcpy(&b, ub, 16);
+    pf32x16_t acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i], 0, 0, 0);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s += acc[i][r];
+    out[blockIdx.x * kNT + threadIdx.x] = s;
+}
+
 }  // namespace
 
-// Runs mix `mix` (0..3) over `blocks` workgroups of 256 lanes with `iters` loop
+// Runs mix `mix` (0..4) over `blocks` workgroups of 256 lanes with `iters` loop
 // trips; `in` holds at least 1028 floats, `out` blocks*256 floats (device memory).
 // Returns 0, or -1 for an unknown mix, or the HIP error of the launch.
 extern "C" int dust_probe_valu_mix(int mix, int blocks, int iters, const float* in, float* out, void* stream) {
@@ -140,6 +176,7 @@ extern "C" int dust_probe_valu_mix(int mix, int blocks, int iters, const float* 
         case 1: hipLaunchKernelGGL(mix_mad64_kernel, dim3(blocks), dim3(kNT), 0, s, in, out, iters); break;
         case 2: hipLaunchKernelGGL(mix_trans_kernel, dim3(blocks), dim3(kNT), 0, s, in, out, iters); break;
         case 3: hipLaunchKernelGGL(mix_head_kernel, dim3(blocks), dim3(kNT), 0, s, in, out, iters, 0x12345678u, 0x9abcdef0u); break;
+        case 4: hipLaunchKernelGGL(mix_mfma_kernel, dim3(blocks), dim3(kNT), 0, s, in, out, iters); break;
         default: return -1;
     }
     return (int)hipGetLastError();
