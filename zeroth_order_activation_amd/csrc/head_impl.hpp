@@ -279,6 +279,8 @@ __global__ void __launch_bounds__(NT, (NT == 256 ? 4 : 1)) head_estimate_kernel(
     const bool owner = (qy % NT) == (uint32_t)tid && y < (uint32_t)V;
 
     const uint32_t tok = A.tok0 + (uint32_t)t;
+    // some lane of this wave holds a quad of the row in the last quad row (uniform)
+    const bool tail_live = wid * 64 + (Q - 1) * NT < nq;
     float acc[QR > 0 ? QR : 1][4];
 #pragma unroll
     for (int j = 0; j < QR; ++j)
@@ -296,7 +298,13 @@ __global__ void __launch_bounds__(NT, (NT == 256 ? 4 : 1)) head_estimate_kernel(
 #pragma unroll
         for (int j = 0; j < Q; ++j) {
             // quads past the row have probability 0: they add nothing to S, and
-            // their running sums are never stored
+            // their running sums are never stored; a wave whose lanes are all past
+            // the row in the last quad row skips it
+            if (j == Q - 1 && !tail_live) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) a[j][c] = 0.f;
+                continue;
+            }
             const int q = tid + j * NT;
             const f32x4 g = gauss4_unscaled_uniform(tok, (uint32_t)q, draw, A.layer, A.k0, A.k1);
             f32x4 pz;
@@ -330,6 +338,7 @@ __global__ void __launch_bounds__(NT, (NT == 256 ? 4 : 1)) head_estimate_kernel(
             for (int c = 0; c < 4; ++c) acc[j][c] = fmaf(r, a[j][c], acc[j][c]);
 #pragma unroll
         for (int j = QR; j < Q; ++j) {  // only this lane touches its slots: no barrier needed
+            if (j == Q - 1 && !tail_live) continue;
             float4 o = accl[(j - QR) * NT + tid];
             o.x = fmaf(r, a[j][0], o.x); o.y = fmaf(r, a[j][1], o.y);
             o.z = fmaf(r, a[j][2], o.z); o.w = fmaf(r, a[j][3], o.w);
