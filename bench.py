@@ -67,11 +67,12 @@ def head_lane_ops_per_channel_draw(deg):
 
 
 def head_taylor_degree(sigma):
-    """The library's choice: the lowest of 4, 6 whose dropped terms stay below 8e-9
-    for |sigma a| <= 5.7683 sigma (else the library expm1, counted as degree 6)."""
+    """The library's choice: the lowest of 3, 4, 6 whose dropped terms stay below
+    2e-5 sigma for |sigma a| <= 5.7683 sigma (else the library expm1, counted as
+    degree 6)."""
     xm = sigma * 5.7683
-    for D in (4, 6):
-        if xm ** (D + 1) / math.factorial(D + 1) * math.exp(xm) <= 8e-9:
+    for D in (3, 4, 6):
+        if xm ** (D + 1) / math.factorial(D + 1) * math.exp(xm) <= 2e-5 * sigma:
             return D
     return 6
 

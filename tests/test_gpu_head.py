@@ -41,11 +41,12 @@ SMALL = [
     (20, 2050, 9, 4, 1e-2, "bf16", "zipf"),      # Q = 4, ragged bf16
     (24, 8192, 32, 4, 1e-2, "f32", "zipf"),      # Q = 8, p in registers
     (8, 8193, 16, 3, 1e-2, "bf16", "zipf"),      # LDS row, 1024 lanes, Q = 4
-    (6, 20000, 8, 2, 5e-3, "f32", "zipf"),       # LDS row fp32, Q = 8
-    (4, 50304, 8, 2, 5e-3, "bf16", "zipf"),      # 768 lanes, Q = 17
+    (6, 20000, 8, 2, 5e-3, "f32", "zipf"),       # LDS row fp32, Q = 8, degree-3 polynomial
+    (4, 50304, 8, 2, 5e-3, "bf16", "zipf"),      # 1024 lanes, Q = 13 (3 running sums in LDS), degree 3
     (3, 60001, 8, 2, 5e-3, "bf16", "zipf"),      # 1024 lanes, Q = 16
     (9, 500, 8, 3, 0.1, "f32", "uniform"),       # large sigma: library expm1 variant
-    (11, 3000, 8, 3, 0.02, "f32", "zipf"),       # degree-6 polynomial
+    (11, 3000, 8, 3, 0.02, "f32", "zipf"),       # degree-4 polynomial at sigma 2e-2
+    (11, 3000, 8, 3, 0.04, "f32", "zipf"),       # degree-6 polynomial
     (5, 20000, 8, 2, 0.5, "bf16", "zipf"),       # large sigma, LDS row
     (3, 32768, 8, 2, 5e-3, "f32", "zipf"),       # the widest fp32 row accepted
     (3, 65536, 8, 2, 5e-3, "bf16", "zipf"),      # the widest bf16 row accepted

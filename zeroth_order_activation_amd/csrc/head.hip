@@ -43,14 +43,18 @@ HeadPlan plan_head(int64_t V, int logits_dtype, float sigma) {
         p.why = "vocabulary larger than 65536 is not supported";
     }
     // Taylor degree of expm1(x), x = sigma a, |x| <= sigma*5.7683: the dropped
-    // terms move S = sum_v p_v expm1(x_v) by at most |x|^(D+1)/(D+1)! e^|x|.
+    // terms move S = sum_v p_v expm1(x_v) by at most |x|^(D+1)/(D+1)! e^|x|, which
+    // moves a reward (of size ~sigma) by at most as much.  The lowest degree whose
+    // bound stays below 2e-5 sigma is taken (the typical change is many orders of
+    // magnitude smaller: |a| reaches 5.77 with probability ~1e-7).
     const double xm = (double)sigma * kMaxAbsNoise;
     auto rem = [&](int D) {
         double f = 1.0;
         for (int k = 2; k <= D + 1; ++k) f *= k;
         return std::pow(xm, D + 1) / f * std::exp(xm);
     };
-    p.deg = rem(4) <= 8e-9 ? 4 : rem(6) <= 8e-9 ? 6 : 0;
+    const double tol = 2e-5 * (double)sigma;
+    p.deg = rem(3) <= tol ? 3 : rem(4) <= tol ? 4 : rem(6) <= tol ? 6 : 0;
     if (p.pmode == 1) p.lds = (size_t)p.nt * p.q * (logits_dtype == 0 ? 16 : 8) + (size_t)p.ql * p.nt * 16;
     return p;
 }

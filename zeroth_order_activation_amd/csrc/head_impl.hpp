@@ -11,10 +11,10 @@
 // is exactly  log1p(S) - sigma a_y,  S = sum_v p_v expm1(sigma a_v),  which
 // avoids subtracting two losses of size ln V in fp32.  |a| <= sqrt(48 ln 2)
 // by construction of the noise, so for small sigma expm1 is a short Taylor
-// polynomial of degree DEG (4 or 6) in x = sigma a; the host picks the degree
-// so that the dropped terms move S by less than 8e-9 (since sum p = 1, that
-// bound is |x|max^(DEG+1)/(DEG+1)! e^|x|max); larger sigma uses the library
-// expm1 (DEG = 0).  The noise is generated divided by sqrt(2 ln 2) (one
+// polynomial of degree DEG (3, 4 or 6) in x = sigma a; the host picks the
+// lowest degree whose dropped terms move S by less than 2e-5 sigma (since
+// sum p = 1, that bound is |x|max^(DEG+1)/(DEG+1)! e^|x|max); larger sigma uses
+// the library expm1 (DEG = 0).  The noise is generated divided by sqrt(2 ln 2) (one
 // product fewer per pair); the host folds that factor into sigma and the
 // final scale.
 //
@@ -407,7 +407,8 @@ template <int LT>
 hipError_t dispatch_head(const HeadPlan& P, const HeadArgs& A, hipStream_t s) {
 #define DUST_HEAD_CASE(NT_, Q_, PM_, QL_)                                                  \
     if (P.nt == NT_ && P.q == Q_ && P.pmode == PM_ && P.ql == QL_) {                        \
-        return P.deg == 4   ? launch_head_variant<NT_, Q_, LT, PM_, 4, QL_>(P, A, s)         \
+        return P.deg == 3   ? launch_head_variant<NT_, Q_, LT, PM_, 3, QL_>(P, A, s)         \
+               : P.deg == 4 ? launch_head_variant<NT_, Q_, LT, PM_, 4, QL_>(P, A, s)         \
                : P.deg == 6 ? launch_head_variant<NT_, Q_, LT, PM_, 6, QL_>(P, A, s)         \
                             : launch_head_variant<NT_, Q_, LT, PM_, 0, QL_>(P, A, s);        \
     }

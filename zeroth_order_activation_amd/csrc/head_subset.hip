@@ -505,13 +505,16 @@ int head_subset_qw(int64_t m, int64_t V) {
 hipError_t launch_head_subset(const HeadPlan& plan, int logits_dtype, const HeadArgs& A, int64_t m, float* rew_ws,
                               int* off_ws, hipStream_t stream) {
     const int64_t nq = (A.V + 3) / 4, mq = m / 4 < nq ? m / 4 : nq;
+    // the subset kernels come in degrees 4 and 6: degree 3 runs as 4 (a smaller
+    // truncation, same coefficients)
+    const int pdeg = plan.deg == 3 ? 4 : plan.deg;
     if (A.V > kSubsetLdsMaxV) {  // two passes
         const float winv = (float)((double)nq / (double)mq);
         float* rew = A.rewards ? A.rewards : rew_ws;
         const size_t lds = head_subset_wide_lds_bytes(A.V, logits_dtype);
         hipError_t e = hipErrorInvalidConfiguration;
 #define DUST_WIDE_CASE(LT_, DEG_)                                                                      \
-        if (logits_dtype == LT_ && plan.deg == DEG_) {                                                \
+        if (logits_dtype == LT_ && pdeg == DEG_) {                                                \
             auto k = head_subset_rewards_kernel<LT_, DEG_>;                                            \
             if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),                             \
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess) \
@@ -534,7 +537,7 @@ hipError_t launch_head_subset(const HeadPlan& plan, int logits_dtype, const Head
     const float winv = (float)((double)nq / (double)mq);
     hipError_t e = hipErrorInvalidConfiguration;
 #define DUST_SUBSET_CASE(LT_, DEG_, QW_)                                                               \
-    if (logits_dtype == LT_ && plan.deg == DEG_ && qw == QW_) {                                        \
+    if (logits_dtype == LT_ && pdeg == DEG_ && qw == QW_) {                                        \
         auto k = head_subset_kernel<LT_, DEG_, QW_, SH>;                                                   \
         if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),                                 \
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess) \
