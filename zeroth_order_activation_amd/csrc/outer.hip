@@ -42,6 +42,9 @@ constexpr int BM = 128, BN = 128, BK = 16, NTH = 256;
 // four different quarters of the 64 banks.
 constexpr int YT = 256, YK = 32, YWAVES = 8, YNT = 64 * YWAVES;
 __device__ __forceinline__ int yswz(int row, int piece) { return row * YT + ((piece ^ ((row & 3) << 2)) << 3); }
+// s_waitcnt immediate that waits until at most n vector-memory operations are
+// outstanding (expcnt and lgkmcnt left unconstrained)
+constexpr int vmcnt_imm_o(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 constexpr double kSplitMinFlop = 4e9;
 
 struct OuterPlan {
@@ -276,17 +279,25 @@ __device__ __forceinline__ uint4 tr_frag(const uint16_t* p) {  // p = tile + lan
 }
 
 // out[m][n] = sum_k Ah[k][m] Bh[k][n] + Ah Bl + Al Bh over the tokens k of this
-// split.  256 x 256 tiles, 8 waves of 128 (m) x 64 (n).  Each k-step moves the
-// four [32 x 256] pair tiles straight from global memory into LDS (16-byte
-// direct loads; the swizzle is applied on the global side, since a direct load
-// puts lane l at slot base + l), double-buffered in two separate LDS objects
-// so reads of one never wait on loads in flight into the other.
+// split.  256 x 256 tiles, 8 waves of 128 (m) x 64 (n).  The four [16 x 256] pair
+// tiles of each 16-token k-step go straight from global memory into a four-stage
+// LDS ring (buffer loads into LDS; the swizzle is applied on the global side,
+// since such a load puts lane l at slot base + l), three k-steps ahead; the
+// fragments of k-step ks + 1 are read while k-step ks's MFMAs issue.
+constexpr int YK2 = 16, PL2 = YK2 * YT;   // tokens per k-step; elements of one plane of a stage
+
+struct PairFrags {
+    uint4 ah[4], al[4], bh[2], bl[2];
+};
+
 __global__ void __launch_bounds__(YNT, 1) outer_x3_kernel(const uint16_t* __restrict__ Ah, const uint16_t* __restrict__ Al,
                                                          const uint16_t* __restrict__ Bh, const uint16_t* __restrict__ Bl,
                                                          int64_t M, int64_t N, int64_t Mp, int64_t Np, int64_t Tp,
                                                          int64_t tchunk, float* __restrict__ out, int64_t mt0,
                                                          int64_t zs, int64_t orow0) {
-    __shared__ __align__(16) uint16_t L0[4 * YK * YT], L1[4 * YK * YT];  // [plane][token][column], 64 KB each
+    // the ring stages as separate LDS objects ([plane][token][column], 32 KB each):
+    // reads of one provably do not alias loads in flight into another
+    __shared__ __align__(16) uint16_t S0[4 * PL2], S1[4 * PL2], S2[4 * PL2], S3[4 * PL2];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w & 1, wn = w >> 1;
     // XCD-aware tile order: workgroups are dealt round-robin to the 8 XCDs, so
@@ -300,29 +311,27 @@ __global__ void __launch_bounds__(YNT, 1) outer_x3_kernel(const uint16_t* __rest
     const int64_t m0 = mt * YT, n0 = nt * YT;
     const int64_t kb0 = (int64_t)blockIdx.z * tchunk;
     const int64_t ke = (kb0 + tchunk < Tp) ? kb0 + tchunk : Tp;
+    const int nks = (int)((ke - kb0) / YK2);   // tchunk and Tp are whole 32-token steps
 
-    // direct loads: 4 planes x 32 rows x 32 pieces = 4096 slots, 8 per lane;
-    // load jj of wave w fills slots (8 jj + w) * 64 .. + 63, all of plane
-    // (8 jj + w) / 16, rows 2 ((8 jj + w) % 16) + lane / 32.  The lane's source
-    // offset only depends on jj % 2 and on the plane pitch.
-    constexpr int NL = 4 * YK * (YT / 8) / YNT;
-    int offl[2][2];  // [plane is B][jj % 2]
+    // one load per lane and plane: wave w fills rows 2w, 2w + 1 of the plane; slot
+    // p' of a row holds logical piece p' ^ 4 (row & 3)
+    constexpr int NL = 4;
+    const int lrow = 2 * w + (lane >> 5);
+    const int lpiece = (lane & 31) ^ ((lrow & 3) << 2);
+    const int dsto = w * 64 * 8;   // element offset of this wave's 64 slots in a plane
+    auto issue_ks = [&](int ks, uint16_t* dst) {
+        const int64_t kb = kb0 + (int64_t)ks * YK2;
 #pragma unroll
-    for (int pb = 0; pb < 2; ++pb)
-#pragma unroll
-        for (int odd = 0; odd < 2; ++odd) {
-            const int row = (odd * 8 + w) * 2 + (lane >> 5);
-            const int piece = (lane & 31) ^ ((row & 3) << 2);
-            const int64_t ld = pb ? Np : Mp, c0 = pb ? n0 : m0;
-            offl[pb][odd] = (int)(row * ld + c0 + 8 * piece);
-        }
-    auto issue_loads = [&](int64_t kb, uint16_t* dst) {
-#pragma unroll
-        for (int jj = 0; jj < NL; ++jj) {
-            const int blk = jj * YWAVES + w, plane = blk >> 4;  // plane = jj / 2 (8 waves)
-            const uint16_t* base = plane == 0 ? Ah : plane == 1 ? Al : plane == 2 ? Bh : Bl;
-            const int64_t ld = plane < 2 ? Mp : Np;
-            __builtin_amdgcn_global_load_lds(base + kb * ld + offl[plane >= 2][jj & 1], dst + blk * 64 * 8, 16, 0, 0);
+        for (int pl = 0; pl < 4; ++pl) {
+            const uint16_t* base = pl == 0 ? Ah : pl == 1 ? Al : pl == 2 ? Bh : Bl;
+            const int64_t ld = pl < 2 ? Mp : Np;
+            const int64_t c0 = pl < 2 ? m0 : n0;
+            // a resource over this k-step's rows of the plane (offsets stay 32-bit)
+            const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(base + kb * ld + c0), (short)0, (int)(YK2 * ld * 2), 0x00020000);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                r, (__attribute__((address_space(3))) void*)(dst + pl * PL2 + dsto), 16,
+                (int)(lrow * ld * 2 + lpiece * 16), 0, 0, 0);
         }
     };
 
@@ -334,69 +343,65 @@ __global__ void __launch_bounds__(YNT, 1) outer_x3_kernel(const uint16_t* __rest
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    constexpr int PL = YK * YT;  // elements per plane tile
-    int oa[4], ob[2];            // lane offsets of the A and B column blocks
+    int oa[4], ob[2];  // lane offsets of the A and B column blocks
 #pragma unroll
     for (int i = 0; i < 4; ++i) oa[i] = tr_lane_off(wm * 128 + 32 * i, lane);
 #pragma unroll
     for (int j = 0; j < 2; ++j) ob[j] = tr_lane_off(wn * 64 + 32 * j, lane);
-    auto read_frags = [&](const uint16_t* t, int kk, uint4 (&ah)[4], uint4 (&al)[4], uint4 (&bh)[2], uint4 (&bl)[2]) {
+    auto read_frags = [&](const uint16_t* t, PairFrags& f) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            ah[i] = tr_frag(t + oa[i] + 16 * kk * YT);
-            al[i] = tr_frag(t + PL + oa[i] + 16 * kk * YT);
+            f.ah[i] = tr_frag(t + oa[i]);
+            f.al[i] = tr_frag(t + PL2 + oa[i]);
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            bh[j] = tr_frag(t + 2 * PL + ob[j] + 16 * kk * YT);
-            bl[j] = tr_frag(t + 3 * PL + ob[j] + 16 * kk * YT);
+            f.bh[j] = tr_frag(t + 2 * PL2 + ob[j]);
+            f.bl[j] = tr_frag(t + 3 * PL2 + ob[j]);
         }
     };
-    auto kstep = [&](int64_t kb, const uint16_t* cur, uint16_t* nxt, bool more) {
-        if (more) issue_loads(kb + YK, nxt);
-        uint4 ah[4], al[4], bh[2], bl[2], nbh[2], nbl[2];
-        read_frags(cur, 0, ah, al, bh, bl);
-        auto pass = [&](const uint4 (&a)[4], const uint4 (&b)[2]) {
+    // k-step ks: MFMAs on the fragments of slab ks (read during k-step ks - 1),
+    // while the fragments of slab ks + 1 are read from its stage; it starts once
+    // slab ks + 1 has landed (only the NL loads of slab ks + 2 outstanding).  Past
+    // its barrier every wave has finished k-step ks - 1, so the stage of slab
+    // ks - 1 takes slab ks + 3 (clamped to the last one: every k-step issues the
+    // same loads).
+    auto kstep = [&](int ks, const uint16_t* nx1, uint16_t* wr, PairFrags& cur, PairFrags& nxt) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm_o(NL));
+        asm volatile("s_barrier" ::: "memory");
+        issue_ks(min(ks + 3, nks - 1), wr);
+        read_frags(nx1, nxt);   // past the last k-step: a stage of valid data, unused
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) acc[i][j] = mfma_bf16(a[i], b[j], acc[i][j]);
-        };
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            nbh[j] = tr_frag(cur + 2 * PL + ob[j] + 16 * YT);
-            nbl[j] = tr_frag(cur + 3 * PL + ob[j] + 16 * YT);
-        }
-        pass(al, bh);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) al[i] = tr_frag(cur + PL + oa[i] + 16 * YT);
-        pass(ah, bl);
-        pass(ah, bh);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ah[i] = tr_frag(cur + oa[i] + 16 * YT);
-        pass(al, nbh);
-        pass(ah, nbl);
-        pass(ah, nbh);
-        // order: direct loads, the first sub-step's 24 reads, the B reads of the
-        // second, then the passes with the A reads in between
+            for (int j = 0; j < 2; ++j) {
+                acc[i][j] = mfma_bf16(cur.al[i], cur.bh[j], acc[i][j]);
+                acc[i][j] = mfma_bf16(cur.ah[i], cur.bl[j], acc[i][j]);
+                acc[i][j] = mfma_bf16(cur.ah[i], cur.bh[j], acc[i][j]);
+            }
+        // the loads first, then one fragment read between consecutive MFMAs
         __builtin_amdgcn_sched_group_barrier(0x020, NL, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 24 + 8, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 24, 0);
-        __builtin_amdgcn_s_waitcnt(0);  // the next tile's direct loads have landed
-        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 24; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
     };
 
-    issue_loads(kb0, L0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int64_t kb = kb0; kb < ke; kb += 2 * YK) {
-        kstep(kb, L0, L1, kb + YK < ke);
-        if (kb + YK < ke) kstep(kb + YK, L1, L0, kb + 2 * YK < ke);
+    PairFrags fa, fb;
+    issue_ks(0, S0);
+    issue_ks(min(1, nks - 1), S1);
+    issue_ks(min(2, nks - 1), S2);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm_o(2 * NL));   // slab 0
+    asm volatile("s_barrier" ::: "memory");
+    read_frags(S0, fa);
+    for (int ks = 0; ks < nks; ks += 4) {
+        kstep(ks, S1, S3, fa, fb);
+        if (ks + 1 < nks) kstep(ks + 1, S2, S0, fb, fa);
+        if (ks + 2 < nks) kstep(ks + 2, S3, S1, fa, fb);
+        if (ks + 3 < nks) kstep(ks + 3, S0, S2, fb, fa);
     }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm_o(0));   // the clamped loads past the end
 
     // split z writes plane z (zs floats apart) of rows orow0 on
     float* o = out + (int64_t)blockIdx.z * zs - orow0 * N;
