@@ -293,6 +293,11 @@ __global__ void __launch_bounds__(NT, (NT == 256 ? 4 : 1)) head_estimate_kernel(
 
     for (int i = 0; i < A.K; ++i) {
         const uint32_t draw = A.draw0 + (uint32_t)i;
+        // the lane index, opaque to the compiler inside the draw loop: the per-quad
+        // indices and LDS addresses derived from it are recomputed (one or two
+        // instructions each) instead of hoisted out of the loop and spilled
+        int tl = tid;
+        asm volatile("" : "+v"(tl));
         float a[Q][4];
         float sl = 0.f, ly = 0.f;
 #pragma unroll
@@ -305,7 +310,7 @@ __global__ void __launch_bounds__(NT, (NT == 256 ? 4 : 1)) head_estimate_kernel(
                 for (int c = 0; c < 4; ++c) a[j][c] = 0.f;
                 continue;
             }
-            const int q = tid + j * NT;
+            const int q = tl + j * NT;
             const f32x4 g = gauss4_unscaled_uniform(tok, (uint32_t)q, draw, A.layer, A.k0, A.k1);
             f32x4 pz;
             if (PMODE == 1) pz = lds_quad<LT>(zlds, q);
@@ -339,10 +344,10 @@ __global__ void __launch_bounds__(NT, (NT == 256 ? 4 : 1)) head_estimate_kernel(
 #pragma unroll
         for (int j = QR; j < Q; ++j) {  // only this lane touches its slots: no barrier needed
             if (j == Q - 1 && !tail_live) continue;
-            float4 o = accl[(j - QR) * NT + tid];
+            float4 o = accl[(j - QR) * NT + tl];
             o.x = fmaf(r, a[j][0], o.x); o.y = fmaf(r, a[j][1], o.y);
             o.z = fmaf(r, a[j][2], o.z); o.w = fmaf(r, a[j][3], o.w);
-            accl[(j - QR) * NT + tid] = o;
+            accl[(j - QR) * NT + tl] = o;
         }
         if (tid == 0 && A.rewards) A.rewards[(size_t)i * A.T + t] = r;
     }
