@@ -14,6 +14,8 @@
 // numbered globally: g < T are the clean rows (a = 0, giving CE0), g = T(1+i)+t
 // is draw i of token t.  Rows are processed in chunks; per chunk:
 //   gemm1   F[g] = bf16(LN(x_t + W2 bf16(GELU(h_t + sigma a))))      (MFMA bf16)
+//           small sigma: GELU rows (vector ALU) then W2 + LayerNorm (MFMA);
+//           larger sigma: one kernel with the library erf
 //   gemm2   per (vocab tile, row): max and sum-exp of z = W_head F[g], and the
 //           label logit z[y_t]                                       (MFMA bf16)
 //   combine CE[g] = log-sum-exp over the tiles - z[y_t]
@@ -336,24 +338,13 @@ __global__ void __launch_bounds__(G1_NT, 1) mlp_gemm1_kernel(MlpArgs A, int64_t 
 // rounded GELU takes.  Per entry this costs about a dozen VALU operations where
 // the library erf costs about forty.
 //
-// Workgroup: 64 rows = 8 tokens x 8 draws, all D features, 16 waves (4 per SIMD)
-// in two roles, so that neither pays for the other's registers: waves 0-7 run the
-// MFMAs (wave c owns features [c D/8, (c+1) D/8) of every row), waves 8-15 make the
-// B operand.  A k-step's slab (64 rows x 128 channels, bf16, double-buffered in
-// LDS) is generated by wave 8 + p for token p: lane l makes channel quad l%32 for
-// the 4 draws of parity l/32, two at a time (their Philox chains run side by
-// side), and the cached h, Phi(h), phi(h) and the series coefficients of that quad
-// serve all of them.  While the MFMA waves multiply slab k, the generation waves
-// make slab k+1; each SIMD holds two waves of each role, so the MFMAs of one run
-// under the VALU work of the other.  W2 is read in MFMA fragment order
-// (mlp_w2frag_kernel), one contiguous 1 KB per wave and fragment.  The accumulator
-// is added into an fp32 running total in LDS every 128 channels; the epilogue is
-// mlp_gemm1_kernel's fp64 residual and LayerNorm.
+// The form runs as two kernels per chunk of rows: mlp_gelu_rows_kernel writes
+// M = bf16(GELU(h~)) for every row of the chunk (one wave per token and 256
+// channels, the token's cached h, Phi(h), phi(h) and series coefficients held in
+// registers across its draws, two draws' Philox chains side by side), then
+// mlp_w2ln_kernel forms F = bf16(LN(x + W2 M)) on MFMA.  W2 is read in MFMA
+// fragment order (mlp_w2frag_kernel), one contiguous 1 KB per wave and fragment.
 // ---------------------------------------------------------------------------
-constexpr int GT_TB = 8;          // tokens per workgroup
-constexpr int GT_DB = 8;          // draws per workgroup
-constexpr int GT_ROWS = GT_TB * GT_DB;
-constexpr int GT_KS = 128;        // channels per k-step (32 quads)
 constexpr float GT_FAR = -3.5f;   // h below this: fp64 evaluation
 constexpr double GT_MAX_DELTA = 0.0625;
 
