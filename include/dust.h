@@ -101,8 +101,9 @@ dust_status dust_set_stage_event(int stage, void *event);
  * first `capacity` launches (hipEvent_t handles owned by the caller; the arrays are
  * copied).  kernel 0 = the small-LM step's GEMM of change rows (C = A B^T on bf16x3
  * MFMA), 1 = its fused head change, 2 = the main pass of dust_estimate_attn (query, key
- * or value kernel), 3 = dust_estimate_linear's GEMM1 (F = LN(x + W2 GELU(.))), once per
- * row chunk, 4 = its GEMM2 (the head product and log-sum-exp), once per row chunk,
+ * or value kernel), 3 = dust_estimate_linear's GEMM1 (F = LN(x + W2 GELU(.)): at small
+ * sigma the GELU rows and the W2/LayerNorm kernel together, else the single kernel), once
+ * per row chunk, 4 = its GEMM2 (the head product and log-sum-exp), once per row chunk,
  * 5 = dust_estimate_head's per-token estimator kernel, 6 = the main product kernel of
  * the bf16-pair outer product (the first pass over whole rounds of output tiles).
  * dust_kernel_event_count(kernel) returns how many launches were recorded since the
