@@ -147,40 +147,42 @@ def test_step_updates_parameters_and_momentum():
     assert e_g < TOL and e_m < TOL and e_u < TOL
 
 
-def test_bench_shape_on_sampled_draws():
-    """The 2M-class shape: V 8192, d 128 (2 heads), 2 blocks, n 512, 4 x 256 tokens,
-    K = 64 (one chunk, 16 groups of four draws in the fused head), 32 ES pairs: rewards of
-    sampled draws of every layer-type pass and of sampled ES members against the oracle,
-    draw by draw."""
+def test_bench_shape_whole_estimate():
+    """The 2M-class shape in the benchmark's configuration: V 8192, d 128 (2 heads), 2
+    blocks, n 512, 4 x 256 tokens, K = 64 (one chunk, 16 groups of four draws in the
+    fused head), 32 ES pairs.  Every reward of every pass, every ES member's loss change
+    and every gradient tensor against the oracle's whole step on the same inputs."""
     w = synth.WORKLOADS[7]
-    c, cfg, ocfg, p, tok, lab = _setup(w["V"], w["d"], w["H"], w["L"], w["n"], w["S"], w["B"], seed=1007)
+    V, d, H, L, n, S, B = (w[k] for k in ("V", "d", "H", "L", "n", "S", "B"))
+    c, cfg, ocfg, p, tok, lab = _setup(V, d, H, L, n, S, B, seed=1007)
     K, M, sigma, ses = w["K"], w["M"], w["sigma"], w["sigma_es"]
     hp = dust.lm_hparams(K, M, sigma, ses)
     rew = torch.empty(dust.lm_rewards_count(cfg, hp), dtype=torch.float32, device="cuda")
-    dust.lm_estimate(cfg, hp, p, tok, lab, synth.LM_NOISE_SEED, rewards=rew)
+    print("2M-class shape: GPU estimate", flush=True)
+    G = dust.lm_estimate(cfg, hp, p, tok, lab, synth.LM_NOISE_SEED, rewards=rew)
     torch.cuda.synchronize()
-    r = rew.cpu().numpy()
-    T = w["B"] * w["S"]
+    print("2M-class shape: oracle step", flush=True)
+    sig = dict.fromkeys(lm.ALL_TYPES, sigma)
+    og, info = lm.estimate(ocfg, c["params"], c["tokens"], c["labels"], K, M, sig, ses, synth.LM_NOISE_SEED)
+    T = B * S
     KT = K * T
-    errs = []
-    for j, kind in enumerate(lm.ACT_TYPES):
-        for i in (0, 27, K - 1):  # first, a middle and the last draw
-            orw, _, _ = lm.activation_pass(ocfg, c["params"], c["tokens"], c["labels"], kind, 1, sigma,
-                                           synth.LM_NOISE_SEED, draw_offset=i)
-            e = rel_l2(r[(1 + j) * KT + i * T:(1 + j) * KT + (i + 1) * T], orw[0])
-            errs.append(e)
-            assert e < TOL, (kind, i, e)
-    ce0 = lm.forward(ocfg, c["params"], c["tokens"], c["labels"])[0].sum()
-    base = lm.unpack(ocfg, c["params"])["scal"].astype(np.float64)
-    dl = r[(5 + 3 * w["L"]) * KT:]
-    for jm in (0, 1, 2 * M - 1):
-        eps = oracle.noise(synth.LM_NOISE_SEED, lm.LID_ES, jm // 2, 0, 2 * w["L"])
-        sc = base + (ses if jm % 2 == 0 else -ses) * eps
-        want = lm.forward(ocfg, c["params"], c["tokens"], c["labels"], scal=sc)[0].sum() - ce0
-        e = abs(dl[jm] - want) / abs(want)
-        errs.append(e)
-        assert e < TOL, (jm, e)
-    print(f"2M-class shape: sampled rewards worst rel {max(errs):.2e}")
+    r = rew.cpu().numpy()
+    names = ["head", "emb", "o", "up", "down"] + [f"{k}{l}" for l in range(L) for k in ("q", "k", "v")]
+    worst = 0.0
+    for j, nm in enumerate(names):
+        e = rel_l2(r[j * KT:(j + 1) * KT].reshape(K, T), info["rew_" + nm])
+        worst = max(worst, e)
+        assert e < TOL, (nm, e)
+    dl = r[len(names) * KT:]
+    e_es = rel_l2(dl, np.stack([info["es_plus"], info["es_minus"]], axis=1).reshape(-1))
+    assert e_es < TOL, e_es
+    g = G.cpu().numpy()
+    gw = 0.0
+    for name, sl in _slices(ocfg).items():
+        e = rel_l2(g[sl], og[sl])
+        gw = max(gw, e)
+        assert e < TOL, (name, e)
+    print(f"2M-class shape: every reward {worst:.2e}, ES {e_es:.2e}, every gradient {gw:.2e} (relative L2, worst)")
 
 
 def test_three_steps_follow_the_oracle_trajectory():
