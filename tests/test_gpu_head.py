@@ -1,7 +1,7 @@
 """GPU parity of the LM-head estimator against the oracle.
 
 Small cases (every output element, ragged and degenerate shapes, every kernel
-variant) and the named workloads at full size in the benchmark's launch
+variant), the persistent form on each of its row widths, and the named workloads at full size in the benchmark's launch
 configuration: g_hat rows and rewards of sampled tokens against the oracle,
 every grad_w row sampled against the fp64 identity G_W = G_hat^T X, plus
 determinism and the draw/token split invariants.
@@ -114,6 +114,40 @@ def test_named_workload_whole(wid):
     e_w = rel_l2(gw.cpu().numpy(), oracle.grad_w(og, c["x"]))
     print(f"workload {wid}: rewards {e_r:.2e}, g_hat {e_g:.2e}, grad_w {e_w:.2e} (relative L2 against the oracle)")
     assert e_r < TOL_REW and e_g < TOL_GHAT and e_w < TOL_GW
+
+
+PERSISTENT = [
+    # T, V, d, K, sigma: bf16 rows with V a multiple of 8 and 2 T V d >= 4e9, so that
+    # g_hat goes to the outer product as bf16 pairs only and the persistent form runs
+    (600, 12296, 288, 3, 1e-2),   # Q = 4, degree 4: two full rounds of 256 workgroups, then 88 tokens
+    (270, 24584, 320, 5, 0.5),    # Q = 8, library expm1, odd K
+    (300, 50304, 160, 2, 5e-3),   # Q = 13 (3 running sums in LDS), degree 3
+    (260, 60008, 160, 2, 2e-2),   # Q = 16, degree 4
+    (100, 50304, 400, 4, 4e-2),   # fewer tokens than CUs, degree 6
+]
+
+
+@pytest.mark.parametrize("T,V,d,K,sigma", PERSISTENT)
+def test_persistent_head_form(T, V, d, K, sigma):
+    """The persistent form (each workgroup walks several tokens, the next row loaded
+    into LDS while the pairs are stored) against the oracle, and bit for bit against
+    the one-token-per-workgroup form, which runs when g_hat is also requested."""
+    case = synth.head_case(T, V, d, seed=3 + V, labels="zipf", logits_dtype="bf16")
+    seed, layer, tok0, draw0 = 0x4455535400000000 + T, 2, 11, 7
+    print(f"persistent head T={T} V={V} d={d} K={K} sigma={sigma}", flush=True)
+    z, x, y = logits_to_device(case), dev(case["x"]), dev(case["labels"])
+    rew = torch.empty((K, T), dtype=torch.float32, device="cuda")
+    gw = dust.estimate_head(z, x, y, K, sigma, seed, layer, tok0, draw0, rewards=rew)
+    ghat = torch.empty((T, V), dtype=torch.float32, device="cuda")
+    rew1 = torch.empty((K, T), dtype=torch.float32, device="cuda")
+    gw1 = dust.estimate_head(z, x, y, K, sigma, seed, layer, tok0, draw0, ghat=ghat, rewards=rew1)
+    torch.cuda.synchronize()
+    assert torch.equal(rew, rew1) and torch.equal(gw, gw1)
+    og, orew, _ = oracle.head_estimate(logits_values(case), case["labels"], K, sigma, seed, layer, tok0, draw0)
+    e_r = rel_l2(rew.cpu().numpy(), orew)
+    e_w = rel_l2(gw.cpu().numpy(), oracle.grad_w(og, case["x"]))
+    print(f"  rewards {e_r:.2e}, grad_w {e_w:.2e} (relative L2 against the oracle)")
+    assert e_r < TOL_REW and e_w < TOL_GW
 
 
 def test_deterministic_and_split_invariants():
