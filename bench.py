@@ -81,6 +81,7 @@ def head_taylor_degree(sigma):
 # are unchanged.
 KERNEL_SOURCES = {
     "head_estimate_kernel": ["head_impl.hpp", "head_f32.hip", "head_bf16.hip", "head.hip", "dust_device.hpp"],
+    "head_stream_kernel": ["head_impl.hpp", "head_bf16.hip", "head.hip", "dust_device.hpp"],
     "mlp_gemm2_kernel": ["mlp.hip", "dust_device.hpp", "dust_internal.hpp"],
     "head_subset_kernel": ["head_subset.hip", "dust_device.hpp", "dust_internal.hpp"],
     "attn_v_kernel": ["attn.hip", "dust_device.hpp", "dust_internal.hpp", "launch_events.hpp"],
@@ -89,6 +90,15 @@ KERNEL_SOURCES = {
     "lm_gemm_x3_kernel": ["lm.hip", "lm_internal.hpp", "launch_events.hpp"],
     "lm_head_delta_kernel": ["lm.hip", "lm_internal.hpp", "launch_events.hpp"],
 }
+
+
+def head_kernel_name(T, V, d, logits_bf16):
+    """The estimator kernel the library launches for a whole-row head call that asks for
+    no fp32 g_hat (the benchmark's call): the persistent form for bf16 rows staged in LDS
+    (8192 < V <= 65536, V a multiple of 8) when g_hat goes to the outer product as bf16
+    pairs (2 T V d >= 4e9), else one workgroup per token."""
+    stream = logits_bf16 and 8192 < V <= 65536 and V % 8 == 0 and 2.0 * T * V * d >= 4e9
+    return "head_stream_kernel" if stream else "head_estimate_kernel"
 
 
 def sources_digest(kernel):
@@ -135,7 +145,13 @@ def write_traffic(args):
     """Turn four rocprofv3 --pmc runs (kernel FETCH_SIZE, kernel WRITE_SIZE, and the
     same two counters on a plain copy of --copy-calibration MiB) into the traffic
     file of the workload's dominant kernel."""
-    kernel = ("head_subset_kernel" if args.subset else "head_estimate_kernel") if args.workload in (1, 2, 4) \
+    if args.workload in (1, 2, 4) and not args.subset:
+        import synth
+        w = synth.WORKLOADS[args.workload]
+        head_kernel = head_kernel_name(w["T"], w["V"], w["d"], w["logits_dtype"] == "bf16")
+    else:
+        head_kernel = "head_subset_kernel"
+    kernel = head_kernel if args.workload in (1, 2, 4) \
         else f"attn_{args.attn_proj}_kernel" if args.workload == 6 \
         else "lm_head_delta_kernel" if args.workload == 7 else "mlp_gemm2_kernel"
     copy_bytes = args.copy_calibration << 20
@@ -396,7 +412,7 @@ def run_head(args, c, dust, torch):
     nq = (V + 3) // 4
     covers = not m or m // 4 >= nq
     per_draw = V if covers else m
-    kernel = "head_estimate_kernel" if covers else "head_subset_kernel"
+    kernel = head_kernel_name(T, V, d, "logits" not in c) if covers else "head_subset_kernel"
     achieved = T * K * per_draw * ops / (kern_ms / 1e3) / 1e9
     lb = 4 if "logits" in c else 2
     # bytes every step must move at least once: logits read, g_hat written and read back,

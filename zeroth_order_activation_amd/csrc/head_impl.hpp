@@ -444,10 +444,8 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_barrier" ::: "memory");
 }
 
-// Row (max, sum of exp(z - max)) from per-lane pairs: the wave's maximum and its
-// rescaled sum by DPP (no lane-index arithmetic to keep live), then the waves'
-// pairs merged through LDS.
-// The same statistics with a barrier that does not wait for global memory.
+// The row statistics of block_max_sumexp with a barrier that does not wait for
+// global memory, the wave's slot given as a wave-uniform index.
 template <int NT>
 __device__ __forceinline__ void block_max_sumexp_lds(float& m, float& s, float2* sh, int wid) {
     wave_max_sumexp(m, s);
