@@ -286,9 +286,9 @@ def cpu_baseline_head(case, target_s, subset=0):
         else:
             oracle.head_estimate(z[:ntok], case["labels"][:ntok], K, sigma, case["seed_noise"], case["layer"])
         el = time.perf_counter() - t0
-        if el >= target_s / 3 or ntok >= case["T"]:
+        if el >= 0.7 * target_s or ntok >= case["T"]:
             break
-        ntok = min(case["T"], int(ntok * max(2.0, target_s / max(el, 1e-3))))
+        ntok = min(case["T"], int(ntok * max(2.0, 1.1 * target_s / max(el, 1e-3))))
     return {"value": ntok * K / el, "unit": "token-draws/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"first {ntok} of {case['T']} tokens x all {K} draws "
                       f"({f'window of {subset} channels + label' if subset else 'full vocabulary'}), "
@@ -308,9 +308,9 @@ def cpu_baseline_linear(case, K, target_s):
                                case["sigma"], case["ln_eps"], case["seed_noise"], case["layer"],
                                tokens=np.arange(ntok))
         el = time.perf_counter() - t0
-        if el >= target_s / 3 or ntok >= case["T"]:
+        if el >= 0.7 * target_s or ntok >= case["T"]:
             break
-        ntok = min(case["T"], int(ntok * max(2.0, target_s / max(el, 1e-3))))
+        ntok = min(case["T"], int(ntok * max(2.0, 1.1 * target_s / max(el, 1e-3))))
     draws = f"all {K} draws" if Ku == K else f"the first {Ku} of {K} draws (rate extrapolated: work is linear in K)"
     return {"value": ntok * Ku / el, "unit": "token-draws/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"first {ntok} of {case['T']} tokens x {draws} (clean + perturbed downstream rows), "
@@ -488,9 +488,9 @@ def cpu_baseline_attn(case, target_s, proj):
         oracle.attn_estimate(proj, case["q"], case["k"], case["v"], case["e"], case["S"], case["H"], kd,
                              case["sigma"], case["seed_noise"], case["layer"])
         el = time.perf_counter() - t0
-        if el >= target_s / 3 or kd >= K:
+        if el >= 0.7 * target_s or kd >= K:
             break
-        kd = min(K, int(kd * max(2.0, target_s / max(el, 1e-3))))
+        kd = min(K, int(kd * max(2.0, 1.1 * target_s / max(el, 1e-3))))
     return {"value": case["T"] * kd / el, "unit": "token-draws/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"all {case['T']} tokens x the first {kd} of {K} draws (two causal attentions per draw, "
                       f"numpy fp64; rate extrapolated: work is linear in K), {el:.1f} s"}
@@ -511,9 +511,9 @@ def cpu_baseline_lm(case, target_s):
         lm.estimate(ocfg, case["params"], case["tokens"], case["labels"], kd, kd, sig, case["sigma_es"],
                     case["seed_noise"])
         el = time.perf_counter() - t0
-        if el >= target_s / 3 or kd >= case["K"]:
+        if el >= 0.7 * target_s or kd >= case["K"]:
             break
-        kd = min(case["K"], int(kd * max(2.0, target_s / max(el, 1e-3))))
+        kd = min(case["K"], int(kd * max(2.0, 1.1 * target_s / max(el, 1e-3))))
     td = ((5 + 3 * L) * kd + 2 * kd) * T
     return {"value": td / el, "unit": "token-draws/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"the full step on all {T} tokens with {kd} draws per pass and {kd} ES pairs "
