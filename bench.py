@@ -101,6 +101,12 @@ def head_kernel_name(T, V, d, logits_bf16):
     return "head_stream_kernel" if stream else "head_estimate_kernel"
 
 
+def subset_kernel_name(V):
+    """The subset estimator's kernels: one pass with the row in LDS up to 16384 channels,
+    else a rewards pass and an accumulation pass."""
+    return "head_subset_kernel" if V <= 16384 else "head_subset_rewards_kernel+head_subset_accum_kernel"
+
+
 def sources_digest(kernel):
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
@@ -145,12 +151,16 @@ def write_traffic(args):
     """Turn four rocprofv3 --pmc runs (kernel FETCH_SIZE, kernel WRITE_SIZE, and the
     same two counters on a plain copy of --copy-calibration MiB) into the traffic
     file of the workload's dominant kernel."""
-    if args.workload in (1, 2, 4) and not args.subset:
+    head_kernel = None
+    if args.workload in (1, 2, 4):
         import synth
         w = synth.WORKLOADS[args.workload]
-        head_kernel = head_kernel_name(w["T"], w["V"], w["d"], w["logits_dtype"] == "bf16")
-    else:
-        head_kernel = "head_subset_kernel"
+        if not args.subset:
+            head_kernel = head_kernel_name(w["T"], w["V"], w["d"], w["logits_dtype"] == "bf16")
+        elif w["V"] <= 16384:
+            head_kernel = "head_subset_kernel"
+        else:
+            sys.exit("traffic files cover the one-pass subset kernel only (V <= 16384)")
     kernel = head_kernel if args.workload in (1, 2, 4) \
         else f"attn_{args.attn_proj}_kernel" if args.workload == 6 \
         else "lm_head_delta_kernel" if args.workload == 7 else "mlp_gemm2_kernel"
@@ -212,7 +222,12 @@ def trace_summary(args):
             nm = r.get("Kernel_Name", "")
             if "dust" not in nm or nm in seen:
                 continue
-            seen[nm] = (f"grid {r.get('Grid_Size', '?')}, workgroup {r.get('Workgroup_Size', '?')}, "
+            def dims(key):
+                if key in r:
+                    return r[key]
+                xyz = [r.get(f"{key}_{a}") for a in "XYZ"]
+                return "x".join(v for v in xyz if v) if xyz[0] else "?"
+            seen[nm] = (f"grid {dims('Grid_Size')}, workgroup {dims('Workgroup_Size')}, "
                         f"VGPR {r.get('VGPR_Count', r.get('Arch_VGPR_Count', '?'))}, "
                         f"AGPR {r.get('Accum_VGPR_Count', '?')}, LDS {r.get('LDS_Block_Size', r.get('Lds_Size', '?'))} B, "
                         f"scratch {r.get('Scratch_Size', r.get('Private_Segment_Size', '?'))} B")
@@ -412,7 +427,7 @@ def run_head(args, c, dust, torch):
     nq = (V + 3) // 4
     covers = not m or m // 4 >= nq
     per_draw = V if covers else m
-    kernel = head_kernel_name(T, V, d, "logits" not in c) if covers else "head_subset_kernel"
+    kernel = head_kernel_name(T, V, d, "logits" not in c) if covers else subset_kernel_name(V)
     achieved = T * K * per_draw * ops / (kern_ms / 1e3) / 1e9
     lb = 4 if "logits" in c else 2
     # bytes every step must move at least once: logits read, g_hat written and read back,
