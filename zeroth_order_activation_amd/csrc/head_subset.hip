@@ -337,32 +337,60 @@ __global__ void __launch_bounds__(RNT) head_subset_rewards_kernel(HeadArgs A, in
 
     // ---- clean statistics; the row (plus a spare quad of -inf) goes to LDS ----
     float m = -__builtin_inff();
-    for (int q = tid; q <= nq; q += RNT) {
-        f32x4 z;
-        if ((V & 3) == 0 && q < nq) {
-            if (LT == 0) {
-                const float4 v = reinterpret_cast<const float4*>(row)[q];
-                z.v[0] = v.x; z.v[1] = v.y; z.v[2] = v.z; z.v[3] = v.w;
-            } else {
-                const uint2 v = reinterpret_cast<const uint2*>(row)[q];
-                z.v[0] = __uint_as_float(v.x << 16);
-                z.v[1] = __uint_as_float(v.x & 0xFFFF0000u);
-                z.v[2] = __uint_as_float(v.y << 16);
-                z.v[3] = __uint_as_float(v.y & 0xFFFF0000u);
-            }
-        } else {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) z.v[c] = 4 * q + c < V ? logit_at<LT>(row, 4 * q + c) : -__builtin_inff();
+    if (LT == 1 ? (V & 7) == 0 : (V & 3) == 0) {
+        // rows of whole 16-byte pieces: every piece goes from global memory straight
+        // into LDS (buffer loads into LDS, no registers), all of them in flight at
+        // once; a load into registers per quad, each waited for, left one memory
+        // latency per quad of the row exposed
+        const int rowbytes = V * (LT == 0 ? 4 : 2), npc = rowbytes >> 4;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(row), (short)0,
+                                                                            rowbytes, 0x00020000);
+        const int wbase = __builtin_amdgcn_readfirstlane(tid & ~63) * 16;   // byte offset of the wave's slots
+        for (int i = 0; i * RNT < npc; ++i) {
+            const int P = i * RNT + tid;
+            if (P < npc)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rs, (__attribute__((address_space(3))) void*)(zl + i * RNT * 16 + wbase), 16, P * 16, 0, 0, 0);
         }
+        if (tid == 0) {  // the spare quad
+            if (LT == 0) reinterpret_cast<float4*>(zl)[nq] = make_float4(-__builtin_inff(), -__builtin_inff(),
+                                                                          -__builtin_inff(), -__builtin_inff());
+            else reinterpret_cast<uint2*>(zl)[nq] = make_uint2(0xFF80FF80u, 0xFF80FF80u);
+        }
+        __syncthreads();  // waits for the loads
+        for (int q = tid; q < nq; q += RNT) {
+            const f32x4 z = row_quad<LT>(zl, q);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) m = fmaxf(m, z.v[c]);
-        if (LT == 0) {
-            reinterpret_cast<float4*>(zl)[q] = make_float4(z.v[0], z.v[1], z.v[2], z.v[3]);
-        } else {  // back to bf16 bits: exact (-inf included)
-            uint2 b;
-            b.x = (__float_as_uint(z.v[0]) >> 16) | (__float_as_uint(z.v[1]) & 0xFFFF0000u);
-            b.y = (__float_as_uint(z.v[2]) >> 16) | (__float_as_uint(z.v[3]) & 0xFFFF0000u);
-            reinterpret_cast<uint2*>(zl)[q] = b;
+            for (int c = 0; c < 4; ++c) m = fmaxf(m, z.v[c]);
+        }
+    } else {
+        for (int q = tid; q <= nq; q += RNT) {
+            f32x4 z;
+            if ((V & 3) == 0 && q < nq) {
+                if (LT == 0) {
+                    const float4 v = reinterpret_cast<const float4*>(row)[q];
+                    z.v[0] = v.x; z.v[1] = v.y; z.v[2] = v.z; z.v[3] = v.w;
+                } else {
+                    const uint2 v = reinterpret_cast<const uint2*>(row)[q];
+                    z.v[0] = __uint_as_float(v.x << 16);
+                    z.v[1] = __uint_as_float(v.x & 0xFFFF0000u);
+                    z.v[2] = __uint_as_float(v.y << 16);
+                    z.v[3] = __uint_as_float(v.y & 0xFFFF0000u);
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) z.v[c] = 4 * q + c < V ? logit_at<LT>(row, 4 * q + c) : -__builtin_inff();
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) m = fmaxf(m, z.v[c]);
+            if (LT == 0) {
+                reinterpret_cast<float4*>(zl)[q] = make_float4(z.v[0], z.v[1], z.v[2], z.v[3]);
+            } else {  // back to bf16 bits: exact (-inf included)
+                uint2 b;
+                b.x = (__float_as_uint(z.v[0]) >> 16) | (__float_as_uint(z.v[1]) & 0xFFFF0000u);
+                b.y = (__float_as_uint(z.v[2]) >> 16) | (__float_as_uint(z.v[3]) & 0xFFFF0000u);
+                reinterpret_cast<uint2*>(zl)[q] = b;
+            }
         }
     }
     m = block_reduce_max<RNT>(m, sh);  // its barriers publish the row
@@ -438,6 +466,15 @@ __global__ void __launch_bounds__(BNT) head_subset_accum_kernel(HeadArgs A, int 
         for (int c = 0; c < 4; ++c) acc[k][c] = 0.f;
     // this wave's 64-quad blocks start at wq0 + k BNT
     const int wq0 = sg * BNT * BQS + __builtin_amdgcn_readfirstlane(tid & ~63);
+    // bit k: the blocks [wq0 + k BNT, + 64) that meet a quad range [lo, hi), all
+    // wave-uniform: k BNT < hi - wq0 and k BNT > lo - wq0 - 64
+    auto block_bits = [&](int lo, int hi) -> uint32_t {
+        const int khi = min(BQS, max(0, (hi - wq0 + BNT - 1) >> 8));
+        const int klo = max(0, ((lo - wq0 - 64) >> 8) + 1);   // arithmetic shift: floor
+        return khi > klo ? ((1u << khi) - 1u) & ~((1u << klo) - 1u) : 0u;
+    };
+    static_assert(BNT == 256, "block_bits divides by BNT with a shift");
+    const uint32_t lbits = block_bits(qy, qy + 1);   // the label's block, in every draw
     for (int i = 0; i < A.K; ++i) {
         const int o = woff[(size_t)i * A.T + t];  // wave-uniform
         const float r = rew[(size_t)i * A.T + t];
@@ -445,11 +482,12 @@ __global__ void __launch_bounds__(BNT) head_subset_accum_kernel(HeadArgs A, int 
         const uint32_t draw = A.draw0 + (uint32_t)i;
         // the window as [o, e1) and, when it wraps, [0, e2)
         const int e1 = min(o + mq, nq), e2 = o + mq - nq;
+        // the blocks that the window or the label meet, as one mask built once per
+        // draw: a few scalar instructions, where a test per block cost a dozen
+        const uint32_t hits = block_bits(o, e1) | (e2 > 0 ? block_bits(0, e2) : 0u) | lbits;
 #pragma unroll
         for (int k = 0; k < BQS; ++k) {
-            const int b0 = wq0 + k * BNT;  // wave-uniform: the block [b0, b0 + 64)
-            const bool hit = (b0 < e1 && b0 + 64 > o) || b0 < e2 || (qy >= b0 && qy < b0 + 64);
-            if (hit) {  // scalar test: blocks the window misses cost no vector work
+            if ((hits >> k) & 1u) {  // blocks the window misses cost no vector work
                 const int q = qbase + k * BNT;
                 const bool in = q < nq && ((q >= o && q < e1) || q < e2);
                 const bool lab = q == qy;
