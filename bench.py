@@ -181,7 +181,8 @@ def write_traffic(args):
         factor = copy_bytes / (copy_kib * 1024.0)
         res[ctr] = {"kib_per_dispatch": kib, "dispatches": len(k_runs), "copy_kib": copy_kib,
                     "scale": factor, "bytes": kib * 1024.0 * factor}
-    wl = f"--workload {args.workload}" + (f" --subset {args.subset}" if args.subset else "")
+    wl = (f"--workload {args.workload}" + (f" --subset {args.subset}" if args.subset else "")
+          + (f" --attn-proj {args.attn_proj}" if args.workload == 6 else ""))
     prof = "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 120 rocprofv3 --pmc {c} --output-format csv -d DIR/{n} -o {n} -- python3 $REPO/bench.py {a}"
     cmds = [prof.format(c="FETCH_SIZE", n="copy_fetch", a=f"--copy-calibration {args.copy_calibration}"),
             prof.format(c="WRITE_SIZE", n="copy_write", a=f"--copy-calibration {args.copy_calibration}"),

@@ -279,7 +279,7 @@ dust_status dust_estimate_linear(const float *u, const float *h, const float *x_
  *   u      : float [T, d]  input of the projection (the u_t of G_W)
  *   grad_w : OUT float [d, d];  ghat : OUT float [T, d] or NULL;  rewards : OUT float [K, T] or NULL.
  * Noise counter: (token, channel/4, draw, layer).  Supported: S a multiple of 64 up to
- * 4096, T a multiple of S, d = 64 H.  Stages (dust_set_stage_event): 2 = after the
+ * 4096, T a multiple of S, d = 64 H with 1 <= H <= 16 (else DUST_E_UNSUPPORTED).  Stages (dust_set_stage_event): 2 = after the
  * rewards, 0 = after g_hat, 1 = after G_W.
  * Workspace: dust_attn_workspace_bytes(proj, T, S, d, H, K) bytes.
  * dust_estimate_attn_v is dust_estimate_attn with DUST_ATTN_V (no v argument).

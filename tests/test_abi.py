@@ -101,6 +101,8 @@ def test_attn_v_rejects_bad_arguments_on_host():
         return st, L.dust_last_error().decode()
 
     assert call(d=96, H=2)[0] == 2       # heads of 64 channels only
+    st, err = call(d=64 * 17, H=17)      # at most 16 heads
+    assert st == 2 and "16 heads" in err
     assert call(S=96, T=192)[0] == 2     # sequences of whole 64-token tiles
     assert call(S=8192, T=8192)[0] == 2  # longest sequence 4096
     assert call(T=100)[0] == 1           # T a multiple of S

@@ -134,24 +134,48 @@ struct AttnKArgs {
     uint32_t k0, k1, layer, tok0, draw0;
 };
 
-// expm1 of the 16 logit changes of a lane: the degree-6 Taylor polynomial
-// (truncation below 5e-8 relative for |x| < 1/4); where some lane of the wave
-// holds a larger |x|, those values take exp(x) - 1 (no cancellation there).
-__device__ __forceinline__ void expm1_16(float (&x)[16]) {
+// expm1(s D) for the 16 logit-change inputs D of a lane, x = s D.  The common
+// case is the degree-4 Taylor polynomial with s folded into its coefficients
+// (s, s^2/2, s^3/6, s^4/24: four operations per value, no separate product s D;
+// truncation below 1.3e-7 relative for |x| < 1/16).  Only in a wave where some
+// lane holds |D| >= dlim = (1/16)/s do those values take the degree-6 polynomial
+// (truncation below 5e-8 relative for |x| < 1/4) or, beyond, exp(x) - 1, where
+// no cancellation arises.  At sigma = 1e-2 logit changes are about 1e-2, so that
+// branch practically never runs; the degree-6 form for every value had cost
+// a third more vector instructions per draw.
+struct Expm1Coef {
+    float c1, c2, c3, c4, dlim;
+};
+
+__host__ __device__ inline Expm1Coef expm1_coef(float s) {
+    Expm1Coef c;
+    c.c1 = s;
+    c.c2 = s * s * 0.5f;
+    c.c3 = s * s * s * (1.0f / 6.0f);
+    c.c4 = s * s * s * s * (1.0f / 24.0f);
+    c.dlim = s > 0.f ? 0.0625f / s : __builtin_huge_valf();
+    return c;
+}
+
+__device__ __forceinline__ void expm1_16s(float (&D)[16], const Expm1Coef& cf) {
     bool big = false;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) big |= fabsf(x[r]) >= 0.25f;
+    for (int r = 0; r < 16; ++r) big |= fabsf(D[r]) >= cf.dlim;
     float p[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-        p[r] = x[r] * fmaf(x[r], fmaf(x[r], fmaf(x[r], fmaf(x[r], fmaf(x[r], 1.0f / 720.0f, 1.0f / 120.0f),
-                                                             1.0f / 24.0f), 1.0f / 6.0f), 0.5f), 1.0f);
+    for (int r = 0; r < 16; ++r) p[r] = D[r] * fmaf(D[r], fmaf(D[r], fmaf(D[r], cf.c4, cf.c3), cf.c2), cf.c1);
     if (__builtin_amdgcn_ballot_w64(big)) {  // wave-uniform, rare at small sigma
 #pragma unroll
-        for (int r = 0; r < 16; ++r) p[r] = fabsf(x[r]) < 0.25f ? p[r] : __expf(x[r]) - 1.0f;
+        for (int r = 0; r < 16; ++r) {
+            const float x = D[r] * cf.c1;
+            const float q6 = x * fmaf(x, fmaf(x, fmaf(x, fmaf(x, fmaf(x, 1.0f / 720.0f, 1.0f / 120.0f), 1.0f / 24.0f),
+                                                      1.0f / 6.0f), 0.5f), 1.0f);
+            const float alt = fabsf(x) < 0.25f ? q6 : __expf(x) - 1.0f;
+            p[r] = fabsf(D[r]) >= cf.dlim ? alt : p[r];
+        }
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] = p[r];
+    for (int r = 0; r < 16; ++r) D[r] = p[r];
 }
 
 // ---- clean statistics -------------------------------------------------------
@@ -371,6 +395,7 @@ __global__ void __launch_bounds__(VNT, 1) attn_k_kernel(AttnKArgs A, int kc) {
     const int64_t s0 = (int64_t)b * A.S;
     const int nkt = nqt;
     const float sl2 = kAL2e * 0.125f;
+    const Expm1Coef cf = expm1_coef(A.sdelta);
     uint4 khi[4], klo[4], vhi[4], vlo[4];  // this wave's 32 keys
     load_frags(A.k, A.d, s0 + kt * AT + kh * 32 + (lane & 31), h * ADH, khi, klo);
     load_frags(A.v, A.d, s0 + kt * AT + kh * 32 + (lane & 31), h * ADH, vhi, vlo);
@@ -408,8 +433,8 @@ __global__ void __launch_bounds__(VNT, 1) attn_k_kernel(AttnKArgs A, int kc) {
                     const af32x16_t D = prod_x3c(ahi, alo, qhi, qlo);  // [key][query]: <a_key, q_query>
                     float x[16];
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) x[r] = D[r] * A.sdelta;
-                    expm1_16(x);
+                    for (int r = 0; r < 16; ++r) x[r] = D[r];
+                    expm1_16s(x, cf);
                     float rr = 0.f, mm = 0.f;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
@@ -457,6 +482,7 @@ __global__ void __launch_bounds__(VNT, 1) attn_q_kernel(AttnKArgs A, int kc) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, kh = (w >> 1) & 1, qh = w & 1, grp = w >> 2;
     const int64_t s0 = (int64_t)b * A.S;
     const float sl2 = kAL2e * 0.125f;
+    const Expm1Coef cf = expm1_coef(A.sdelta);
     const int64_t qrow = s0 + qt * AT + qh * 32 + (lane & 31);
     const int query = qt * AT + qh * 32 + (lane & 31);
     uint4 qhi[4], qlo[4], ehi[4], elo[4];  // this wave's 32 queries
@@ -493,8 +519,8 @@ __global__ void __launch_bounds__(VNT, 1) attn_q_kernel(AttnKArgs A, int kc) {
                     const af32x16_t D = prod_x3c(khi, klo, ahi, alo);  // [key][query]: <k_key, a_query>
                     float x[16];
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) x[r] = D[r] * A.sdelta;
-                    expm1_16(x);
+                    for (int r = 0; r < 16; ++r) x[r] = D[r];
+                    expm1_16s(x, cf);
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         rho[dd] = fmaf(P[r], x[r], rho[dd]);
@@ -535,26 +561,34 @@ __global__ void __launch_bounds__(VNT, 1) attn_q_kernel(AttnKArgs A, int kc) {
 // c = sum over heads of (mu - rho <e, o>) / (1 + rho), rho and mu summed over the key
 // tiles up to the token's own and the key halves; written to rew[(i0 + dd) T + t] for
 // the suffix scan.
-__global__ void __launch_bounds__(256) attn_csum_k_kernel(const float* __restrict__ cpart,
-                                                          const float* __restrict__ ob, int T, int S, int H, int i0,
-                                                          int kc, float* __restrict__ rew) {
-    const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (x >= (int64_t)kc * T) return;
-    const int64_t dd = x / T, t = x % T;
-    const int s = (int)(t % S), nkt = S / AT;
-    float c = 0.f;
-    for (int h = 0; h < H; ++h) {
-        float rr = 0.f, mm = 0.f;
-        for (int kt = 0; kt <= s / AT; ++kt)
+// One workgroup per (draw, 64 consecutive tokens), one wave per head (H <= 16):
+// the lanes read consecutive tokens (coalesced), and each head's term meets the
+// others in LDS, added in head order.  One thread per (draw, token) looping over
+// heads and key tiles kept too few loads in flight: 75 us per 16 draws.
+constexpr int kCsumMaxH = 16;
+__global__ void __launch_bounds__(64 * kCsumMaxH) attn_csum_k_kernel(const float* __restrict__ cpart,
+                                                                   const float* __restrict__ ob, int T, int S,
+                                                                   int H, int i0, float* __restrict__ rew) {
+    __shared__ float sh[kCsumMaxH][64];
+    const int lane = threadIdx.x & 63, h = threadIdx.x >> 6;
+    const int64_t x0 = (int64_t)blockIdx.x * 64;   // T is a multiple of 64
+    const int64_t dd = x0 / T, t = x0 % T + lane;
+    const int s = (int)(t % S), nkt = S / AT;      // s / AT: the same for the 64 tokens
+    float rr = 0.f, mm = 0.f;
+    for (int kt = 0; kt <= s / AT; ++kt)
 #pragma unroll
-            for (int kh = 0; kh < 2; ++kh) {
-                const float* pp = cpart + ((((dd * nkt + kt) * H + h) * 2 + kh) * 2) * T + t;
-                rr += pp[0];
-                mm += pp[T];
-            }
-        c += (mm - rr * ob[t * H + h]) / (1.0f + rr);
+        for (int kh = 0; kh < 2; ++kh) {
+            const float* pp = cpart + ((((dd * nkt + kt) * H + h) * 2 + kh) * 2) * T + t;
+            rr += pp[0];
+            mm += pp[T];
+        }
+    sh[h][lane] = (mm - rr * ob[t * H + h]) / (1.0f + rr);
+    __syncthreads();
+    if (h == 0) {
+        float c = 0.f;
+        for (int g = 0; g < H; ++g) c += sh[g][lane];
+        rew[(i0 + dd) * T + t] = c;
     }
-    rew[(i0 + dd) * T + t] = c;
 }
 
 // ---- in place: rew_t = -scale sum_{s >= t, same sequence} c_s (one workgroup per
@@ -603,21 +637,28 @@ __global__ void __launch_bounds__(256) attn_heads_q_kernel(const float* __restri
     rew[(i0 + dd) * T + t] = r;
 }
 
-// ---- value projection: c_t = sum over key tiles, heads and key halves of the partials
-// (one thread per draw and token), written to rew[(i0 + dd) T + t] for the suffix scan
-__global__ void __launch_bounds__(256) attn_csum_kernel(const float* __restrict__ cpart, int T, int S, int H, int i0,
-                                                        int kc, float* __restrict__ rew) {
-    const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (x >= (int64_t)kc * T) return;
-    const int64_t dd = x / T, t = x % T;
+// ---- value projection: c_t = sum over heads, key tiles and key halves of the
+// partials, written to rew[(i0 + dd) T + t] for the suffix scan.  Laid out as the
+// key projection's sum: one workgroup per (draw, 64 tokens), one wave per head.
+__global__ void __launch_bounds__(64 * kCsumMaxH) attn_csum_kernel(const float* __restrict__ cpart, int T, int S,
+                                                                 int H, int i0, float* __restrict__ rew) {
+    __shared__ float sh[kCsumMaxH][64];
+    const int lane = threadIdx.x & 63, h = threadIdx.x >> 6;
+    const int64_t x0 = (int64_t)blockIdx.x * 64;
+    const int64_t dd = x0 / T, t = x0 % T + lane;
     const int s = (int)(t % S), nkt = S / AT;
     float c = 0.f;
-    for (int kt = 0; kt <= s / AT; ++kt)
-        for (int h = 0; h < H; ++h) {
-            const float* pp = cpart + (((dd * nkt + kt) * H + h) * 2) * T + t;
-            c += pp[0] + pp[T];
-        }
-    rew[(i0 + dd) * T + t] = c;
+    for (int kt = 0; kt <= s / AT; ++kt) {
+        const float* pp = cpart + (((dd * nkt + kt) * H + h) * 2) * T + t;
+        c += pp[0] + pp[T];
+    }
+    sh[h][lane] = c;
+    __syncthreads();
+    if (h == 0) {
+        float tot = 0.f;
+        for (int g = 0; g < H; ++g) tot += sh[g][lane];
+        rew[(i0 + dd) * T + t] = tot;
+    }
 }
 
 // ---- g_hat_t = -(1/(K sigma)) sum_i r_t^(i) a_t^(i) ------------------------------
@@ -741,16 +782,16 @@ hipError_t launch_attn_rewards(int proj, const float* q, const float* k, const f
             hipLaunchKernelGGL(attn_q_kernel, g2, dim3(VNT), 0, stream, Ai, kc);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         if ((err = launch_timer_end(kTimedAttnMain, stream, timed)) != hipSuccess) return err;
-        const unsigned nthr = (unsigned)((kc * T + 255) / 256);
+        const unsigned nblk = (unsigned)(kc * T / 64);   // one workgroup per (draw, 64 tokens)
         if (proj == 2) {
-            hipLaunchKernelGGL(attn_csum_kernel, dim3(nthr), dim3(256), 0, stream, A.cpart, (int)T, (int)S, (int)H,
-                               (int)i0, kc, rew);
+            hipLaunchKernelGGL(attn_csum_kernel, dim3(nblk), dim3((unsigned)(64 * H)), 0, stream, A.cpart, (int)T,
+                               (int)S, (int)H, (int)i0, rew);
             if ((err = hipGetLastError()) != hipSuccess) return err;
             hipLaunchKernelGGL(attn_suffix_scan_kernel, dim3((unsigned)(kc * nb)), dim3(256), 0, stream, rew, (int)T,
                                (int)S, (int)i0, sigma);
         } else if (proj == 1) {
-            hipLaunchKernelGGL(attn_csum_k_kernel, dim3(nthr), dim3(256), 0, stream, A.cpart, A.ob, (int)T, (int)S,
-                               (int)H, (int)i0, kc, rew);
+            hipLaunchKernelGGL(attn_csum_k_kernel, dim3(nblk), dim3((unsigned)(64 * H)), 0, stream, A.cpart, A.ob,
+                               (int)T, (int)S, (int)H, (int)i0, rew);
             if ((err = hipGetLastError()) != hipSuccess) return err;
             hipLaunchKernelGGL(attn_suffix_scan_kernel, dim3((unsigned)(kc * nb)), dim3(256), 0, stream, rew, (int)T,
                                (int)S, (int)i0, 1.0f);

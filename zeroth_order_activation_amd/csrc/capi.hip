@@ -521,6 +521,7 @@ dust_status dust_estimate_attn(int proj, const float* q, const float* k, const f
         return fail(DUST_E_INVALID, "dust_estimate_attn: T (%lld) must be a multiple of S (%lld)", (long long)T,
                     (long long)S);
     if (d != 64 * H) return fail(DUST_E_UNSUPPORTED, "dust_estimate_attn: heads of 64 channels only (d = 64 H)");
+    if (H > 16) return fail(DUST_E_UNSUPPORTED, "dust_estimate_attn: at most 16 heads (got %lld)", (long long)H);
     if (S % 64 != 0 || S > 4096)
         return fail(DUST_E_UNSUPPORTED, "dust_estimate_attn: S must be a multiple of 64 up to 4096 (got %lld)",
                     (long long)S);
