@@ -347,9 +347,6 @@ size_t dust_head_noalloc_max_bytes(void) { return DUST_NOALLOC_SCRATCH_BYTES; }
 // bytes of K*T floats or ints, padded to 256
 static size_t kt_bytes(int64_t T, int64_t K) { return ((size_t)T * (size_t)K * 4 + 255) & ~(size_t)255; }
 
-// dynamic LDS a workgroup of the wide-row subset rewards pass may take
-static constexpr size_t kMaxWideLds = 160 * 1024 - 1024;
-
 size_t dust_head_subset_workspace_bytes(int64_t T, int64_t V, int64_t d, int64_t K) {
     // the full estimator's layout (which a covering window runs); rows wider
     // than LDS add the rewards and window offsets of every (draw, token)
@@ -386,8 +383,6 @@ dust_status dust_estimate_head_subset(const void* logits, int logits_dtype, cons
     const dust::HeadPlan plan = dust::plan_head(V, logits_dtype, sigma);  // the Taylor degree and the row limits
     if (!plan.ok) return fail(DUST_E_UNSUPPORTED, "dust_estimate_head_subset: %s", plan.why);
     const bool wide = V > dust::kSubsetLdsMaxV;
-    if (wide && dust::head_subset_wide_lds_bytes(V, logits_dtype) > kMaxWideLds)
-        return fail(DUST_E_UNSUPPORTED, "dust_estimate_head_subset: the logit row does not fit in LDS");
     const bool pairs = head_pairs_path(T, V, d);
     const size_t ghat_ws = (ghat || pairs) ? 0 : head_ghat_bytes(T, V);
     const size_t outer_ws = dust::outer_workspace_bytes(T, V, d);

@@ -47,7 +47,6 @@ hipError_t launch_head(const HeadPlan& plan, int logits_dtype, const HeadArgs& a
 // rewards (unless the caller keeps them) and K T ints of window offsets
 constexpr int64_t kSubsetLdsMaxV = 16384;
 size_t head_subset_lds_bytes(int64_t V);
-size_t head_subset_wide_lds_bytes(int64_t V, int logits_dtype);
 int head_subset_qw(int64_t m, int64_t V);
 hipError_t launch_head_subset(const HeadPlan& plan, int logits_dtype, const HeadArgs& args, int64_t m,
                               float* rew_ws, int* off_ws, hipStream_t stream);

@@ -291,114 +291,83 @@ __global__ void __launch_bounds__(GL * H) head_subset_kernel(HeadArgs A, int mq,
 // ---- rows beyond LDS (V > 16384): a rewards pass, then an accumulation pass ----
 //
 // The probabilities and the running sums of a wide row do not fit in LDS
-// together.  The rewards pass keeps only the logit row (in its own type) in
-// LDS and recomputes p per window channel; every wave works on whole draws
-// (wave w: draws w, w + 16, ... of a chunk), so the wave's own reduction gives
-// S and the draw loop has no barrier.  It writes r and the window offset o of
-// every (draw, token).  The accumulation pass gives each workgroup one
+// together.  The rewards pass recomputes p per window channel from the logits
+// in global memory (below); every wave works on whole draws, so the wave's own
+// reduction gives S and the draw loop has no barrier.  It writes r and the
+// window offset o of every (draw, token).  The accumulation pass gives each workgroup one
 // vocabulary segment of one token with the running sums in registers (lane l
 // owns quads l, l + 256, ... of the segment); per draw it regenerates the
 // noise of the segment's quads that lie in the window (and of the label quad),
 // skipping 64-quad blocks the window misses, and adds r a / pi.  The noise is
 // generated twice, once per pass.
-constexpr int RNT = 1024;  // rewards pass: lanes per workgroup
+constexpr int RNT = 256;   // rewards pass: lanes per workgroup
 constexpr int BNT = 256;   // accumulation pass: lanes per workgroup
 constexpr int BQS = 8;     // accumulation pass: quads per lane (segments of BNT * BQS quads)
 
+// Quad q of a row as fp32, -inf past V (the spare quad q = nq included).
 template <int LT>
-__device__ __forceinline__ f32x4 row_quad(const unsigned char* zl, int q) {  // quad q of the LDS row, as fp32
-    f32x4 r;
-    if (LT == 0) {
-        const float4 v = reinterpret_cast<const float4*>(zl)[q];
-        r.v[0] = v.x; r.v[1] = v.y; r.v[2] = v.z; r.v[3] = v.w;
+__device__ __forceinline__ f32x4 global_quad(const void* row, int q, int V) {
+    f32x4 z;
+    if ((V & 3) == 0 && 4 * q < V) {  // whole quads: one aligned load
+        if (LT == 0) {
+            const float4 v = reinterpret_cast<const float4*>(row)[q];
+            z.v[0] = v.x; z.v[1] = v.y; z.v[2] = v.z; z.v[3] = v.w;
+        } else {
+            const uint2 v = reinterpret_cast<const uint2*>(row)[q];
+            z.v[0] = __uint_as_float(v.x << 16);
+            z.v[1] = __uint_as_float(v.x & 0xFFFF0000u);
+            z.v[2] = __uint_as_float(v.y << 16);
+            z.v[3] = __uint_as_float(v.y & 0xFFFF0000u);
+        }
     } else {
-        const uint2 v = reinterpret_cast<const uint2*>(zl)[q];
-        r.v[0] = __uint_as_float(v.x << 16);
-        r.v[1] = __uint_as_float(v.x & 0xFFFF0000u);
-        r.v[2] = __uint_as_float(v.y << 16);
-        r.v[3] = __uint_as_float(v.y & 0xFFFF0000u);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) z.v[c] = 4 * q + c < V ? logit_at<LT>(row, 4 * q + c) : -__builtin_inff();
     }
-    return r;
+    return z;
 }
 
-__host__ __device__ constexpr size_t wide_row_bytes(int nq, int lt) {  // LDS row, padded to 16 bytes
-    return (((size_t)(nq + 1) * (lt == 0 ? 16 : 8)) + 15) & ~(size_t)15;
-}
+// Rewards pass of the wide rows: one workgroup of RNT lanes per token and no row
+// in LDS, so that several tokens share a CU and hide each other's memory
+// latency.  The statistics stream the row twice (maximum, then the sum of
+// exponentials; the second read mostly hits the caches), RB quads per lane in
+// flight at a time.  Each wave takes whole draws (wave w: draws w, w + 4, ...)
+// and reads its window's logits from global memory, four quads per lane at once;
+// its own DPP reduction gives S, so the draw loop has no barrier.  It writes r
+// and the window offset of every (draw, token).  A 1024-lane workgroup per token
+// with the row staged in LDS (100 KB at the 243M shape: one token per CU) took
+// 0.79 ms per launch there.
+constexpr int RB = 8;   // quads per lane and batch of the statistics' loads
 
 template <int LT, int DEG>
 __global__ void __launch_bounds__(RNT) head_subset_rewards_kernel(HeadArgs A, int mq, float* __restrict__ rew,
                                                                    int* __restrict__ woff) {
-    extern __shared__ __align__(16) unsigned char zl[];
+    __shared__ float4 DR[SKC];
     __shared__ float sh[RNT / 64];
     const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int V = A.V, nq = (V + 3) >> 2;
-    float4* DR = reinterpret_cast<float4*>(zl + wide_row_bytes(nq, LT));
     const void* row = reinterpret_cast<const unsigned char*>(A.logits) + (size_t)t * V * (LT == 0 ? 4 : 2);
 
-    // ---- clean statistics; the row (plus a spare quad of -inf) goes to LDS ----
+    // ---- clean statistics, streamed ----
     float m = -__builtin_inff();
-    if (LT == 1 ? (V & 7) == 0 : (V & 3) == 0) {
-        // rows of whole 16-byte pieces: every piece goes from global memory straight
-        // into LDS (buffer loads into LDS, no registers), all of them in flight at
-        // once; a load into registers per quad, each waited for, left one memory
-        // latency per quad of the row exposed
-        const int rowbytes = V * (LT == 0 ? 4 : 2), npc = rowbytes >> 4;
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(row), (short)0,
-                                                                            rowbytes, 0x00020000);
-        const int wbase = __builtin_amdgcn_readfirstlane(tid & ~63) * 16;   // byte offset of the wave's slots
-        for (int i = 0; i * RNT < npc; ++i) {
-            const int P = i * RNT + tid;
-            if (P < npc)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rs, (__attribute__((address_space(3))) void*)(zl + i * RNT * 16 + wbase), 16, P * 16, 0, 0, 0);
-        }
-        if (tid == 0) {  // the spare quad
-            if (LT == 0) reinterpret_cast<float4*>(zl)[nq] = make_float4(-__builtin_inff(), -__builtin_inff(),
-                                                                          -__builtin_inff(), -__builtin_inff());
-            else reinterpret_cast<uint2*>(zl)[nq] = make_uint2(0xFF80FF80u, 0xFF80FF80u);
-        }
-        __syncthreads();  // waits for the loads
-        for (int q = tid; q < nq; q += RNT) {
-            const f32x4 z = row_quad<LT>(zl, q);
+    for (int q0 = tid; q0 < nq; q0 += RB * RNT) {
+        f32x4 z[RB];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) m = fmaxf(m, z.v[c]);
-        }
-    } else {
-        for (int q = tid; q <= nq; q += RNT) {
-            f32x4 z;
-            if ((V & 3) == 0 && q < nq) {
-                if (LT == 0) {
-                    const float4 v = reinterpret_cast<const float4*>(row)[q];
-                    z.v[0] = v.x; z.v[1] = v.y; z.v[2] = v.z; z.v[3] = v.w;
-                } else {
-                    const uint2 v = reinterpret_cast<const uint2*>(row)[q];
-                    z.v[0] = __uint_as_float(v.x << 16);
-                    z.v[1] = __uint_as_float(v.x & 0xFFFF0000u);
-                    z.v[2] = __uint_as_float(v.y << 16);
-                    z.v[3] = __uint_as_float(v.y & 0xFFFF0000u);
-                }
-            } else {
+        for (int u = 0; u < RB; ++u) z[u] = global_quad<LT>(row, min(q0 + u * RNT, nq), V);
 #pragma unroll
-                for (int c = 0; c < 4; ++c) z.v[c] = 4 * q + c < V ? logit_at<LT>(row, 4 * q + c) : -__builtin_inff();
-            }
+        for (int u = 0; u < RB; ++u)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) m = fmaxf(m, z.v[c]);
-            if (LT == 0) {
-                reinterpret_cast<float4*>(zl)[q] = make_float4(z.v[0], z.v[1], z.v[2], z.v[3]);
-            } else {  // back to bf16 bits: exact (-inf included)
-                uint2 b;
-                b.x = (__float_as_uint(z.v[0]) >> 16) | (__float_as_uint(z.v[1]) & 0xFFFF0000u);
-                b.y = (__float_as_uint(z.v[2]) >> 16) | (__float_as_uint(z.v[3]) & 0xFFFF0000u);
-                reinterpret_cast<uint2*>(zl)[q] = b;
-            }
-        }
+            for (int c = 0; c < 4; ++c) m = fmaxf(m, z[u].v[c]);
     }
-    m = block_reduce_max<RNT>(m, sh);  // its barriers publish the row
+    m = block_reduce_max<RNT>(m, sh);
     float s = 0.f;
-    for (int q = tid; q < nq; q += RNT) {
-        const f32x4 z = row_quad<LT>(zl, q);
+    for (int q0 = tid; q0 < nq; q0 += RB * RNT) {
+        f32x4 z[RB];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) s += __expf(z.v[c] - m);
+        for (int u = 0; u < RB; ++u) z[u] = global_quad<LT>(row, min(q0 + u * RNT, nq), V);
+#pragma unroll
+        for (int u = 0; u < RB; ++u)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) s += __expf(z[u].v[c] - m);
     }
     s = block_reduce_sum<RNT>(s, sh);
     const float lse2 = (m + __logf(s)) * kL2e;
@@ -406,7 +375,7 @@ __global__ void __launch_bounds__(RNT) head_subset_rewards_kernel(HeadArgs A, in
     const uint32_t y = (uint32_t)A.labels[t];
     const int qy = (int)(y >> 2), cy = (int)(y & 3u);
     const uint32_t tok = A.tok0 + (uint32_t)t;
-    const float py = __builtin_amdgcn_exp2f(fmaf(row_quad<LT>(zl, qy).v[cy], kL2e, -lse2));
+    const float py = __builtin_amdgcn_exp2f(fmaf(logit_at<LT>(row, y), kL2e, -lse2));
 
     for (int i0 = 0; i0 < A.K; i0 += SKC) {
         const int kc = min(SKC, A.K - i0);
@@ -428,19 +397,28 @@ __global__ void __launch_bounds__(RNT) head_subset_rewards_kernel(HeadArgs A, in
             const uint32_t draw = A.draw0 + (uint32_t)(i0 + ii);
             const float4 dr = DR[ii];
             const int o = __builtin_amdgcn_readfirstlane(__float_as_int(dr.x));
-            float sl = 0.f;
-            for (int j0 = 0; j0 < mq; j0 += 64) {
-                const int j = j0 + lane;
-                int q = o + j;
-                q = q >= nq ? q - nq : q;
-                q = j < mq ? q : nq;  // past the window: the spare quad
-                const f32x4 g = gauss4_unscaled_uniform(tok, (uint32_t)q, draw, A.layer, A.k0, A.k1);
-                const f32x4 z = row_quad<LT>(zl, q);
+            float sl[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int j0 = 0; j0 < mq; j0 += 256) {
+                int q[4];
+                f32x4 z[4];
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    sl = fmaf(__builtin_amdgcn_exp2f(fmaf(z.v[c], kL2e, -lse2)), em1s<DEG>(g.v[c], A), sl);
+                for (int u = 0; u < 4; ++u) {
+                    const int j = j0 + 64 * u + lane;
+                    int qq = o + j;
+                    qq = qq >= nq ? qq - nq : qq;
+                    q[u] = j < mq ? qq : nq;  // past the window: the spare quad (probability 0)
+                    z[u] = global_quad<LT>(row, q[u], V);
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const f32x4 g = gauss4_unscaled_uniform(tok, (uint32_t)q[u], draw, A.layer, A.k0, A.k1);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        sl[u] = fmaf(__builtin_amdgcn_exp2f(fmaf(z[u].v[c], kL2e, -lse2)), em1s<DEG>(g.v[c], A),
+                                     sl[u]);
+                }
             }
-            const float S = wave_total(sl) + dr.y;
+            const float S = wave_total((sl[0] + sl[1]) + (sl[2] + sl[3])) + dr.y;
             const float r = A.sigma * dr.z - log1p_uniform(S * A.smul);
             if (lane == 0) {
                 rew[(size_t)(i0 + ii) * A.T + t] = r;
@@ -529,9 +507,6 @@ __global__ void __launch_bounds__(BNT) head_subset_accum_kernel(HeadArgs A, int 
 // P and ACC hold 4 (nq + 1) floats each, DR SKC float4s.
 size_t head_subset_lds_bytes(int64_t V) { return (size_t)(8 * ((V + 3) / 4 + 1) + 4 * SKC) * sizeof(float); }
 
-size_t head_subset_wide_lds_bytes(int64_t V, int logits_dtype) {
-    return wide_row_bytes((int)((V + 3) / 4), logits_dtype) + (size_t)SKC * 16;
-}
 
 int head_subset_qw(int64_t m, int64_t V) {
     const int64_t nq = (V + 3) / 4, mq = m / 4 < nq ? m / 4 : nq;
@@ -549,15 +524,11 @@ hipError_t launch_head_subset(const HeadPlan& plan, int logits_dtype, const Head
     if (A.V > kSubsetLdsMaxV) {  // two passes
         const float winv = (float)((double)nq / (double)mq);
         float* rew = A.rewards ? A.rewards : rew_ws;
-        const size_t lds = head_subset_wide_lds_bytes(A.V, logits_dtype);
         hipError_t e = hipErrorInvalidConfiguration;
 #define DUST_WIDE_CASE(LT_, DEG_)                                                                      \
         if (logits_dtype == LT_ && pdeg == DEG_) {                                                \
-            auto k = head_subset_rewards_kernel<LT_, DEG_>;                                            \
-            if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),                             \
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess) \
-                return e;                                                                              \
-            hipLaunchKernelGGL(k, dim3(A.T), dim3(RNT), lds, stream, A, (int)mq, rew, off_ws);         \
+            hipLaunchKernelGGL((head_subset_rewards_kernel<LT_, DEG_>), dim3(A.T), dim3(RNT), 0, stream, A, \
+                               (int)mq, rew, off_ws);                                                  \
             e = hipGetLastError();                                                                     \
         }
         DUST_WIDE_CASE(0, 4) DUST_WIDE_CASE(0, 6) DUST_WIDE_CASE(0, 0)
