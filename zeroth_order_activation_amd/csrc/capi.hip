@@ -386,7 +386,7 @@ dust_status dust_estimate_head_subset(const void* logits, int logits_dtype, cons
     const bool pairs = head_pairs_path(T, V, d);
     const size_t ghat_ws = (ghat || pairs) ? 0 : head_ghat_bytes(T, V);
     const size_t outer_ws = dust::outer_workspace_bytes(T, V, d);
-    const size_t kt_ws = wide ? kt_bytes(T, K) : 0;  // rewards, then window offsets
+    const size_t kt_ws = wide ? kt_bytes(T, K) : 0;  // twice: the (reward, window offset) pairs
     const size_t need = ghat_ws + outer_ws + 2 * kt_ws;
     if (need > 0 && (workspace == nullptr || workspace_bytes < need))
         return fail(DUST_E_WORKSPACE, "dust_estimate_head_subset: workspace of %zu bytes needed, %zu given", need,
@@ -403,9 +403,8 @@ dust_status dust_estimate_head_subset(const void* logits, int logits_dtype, cons
     A.ghi = pr.hi;
     A.glo = pr.lo;
     A.ldp = pr.ld;
-    float* rew_ws = wide ? reinterpret_cast<float*>(ws + ghat_ws + outer_ws) : nullptr;
-    int* off_ws = wide ? reinterpret_cast<int*>(ws + ghat_ws + outer_ws + kt_ws) : nullptr;
-    hipError_t e = dust::launch_head_subset(plan, logits_dtype, A, m, rew_ws, off_ws, st);
+    float2* ro_ws = wide ? reinterpret_cast<float2*>(ws + ghat_ws + outer_ws) : nullptr;   // 2 kt_ws >= 8 K T
+    hipError_t e = dust::launch_head_subset(plan, logits_dtype, A, m, ro_ws, st);
     if (e != hipSuccess) return device_fail("dust_estimate_head_subset: estimator launch", e);
     if ((e = record_stage(0, st)) != hipSuccess) return device_fail("dust_estimate_head_subset: stage event", e);
     e = dust::launch_outer(g, x, T, V, d, grad_w, ows, outer_ws, st, pr.hi != nullptr);

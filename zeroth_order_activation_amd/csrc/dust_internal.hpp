@@ -43,13 +43,13 @@ HeadPlan plan_head(int64_t V, int logits_dtype, float sigma);
 hipError_t launch_head(const HeadPlan& plan, int logits_dtype, const HeadArgs& args, hipStream_t stream);
 // vocabulary-subset estimator (head_subset.hip)
 // rows of up to kSubsetLdsMaxV channels run in one pass with the row in LDS;
-// wider ones in two (rewards, then accumulation), which need K T floats of
-// rewards (unless the caller keeps them) and K T ints of window offsets
+// wider ones in two (rewards, then accumulation), which pass K T pairs of
+// (reward, window offset) through the workspace
 constexpr int64_t kSubsetLdsMaxV = 16384;
 size_t head_subset_lds_bytes(int64_t V);
 int head_subset_qw(int64_t m, int64_t V);
 hipError_t launch_head_subset(const HeadPlan& plan, int logits_dtype, const HeadArgs& args, int64_t m,
-                              float* rew_ws, int* off_ws, hipStream_t stream);
+                              float2* ro_ws, hipStream_t stream);
 
 // ---- grad_w = ghat^T x (fp32 MFMA) --------------------------------------
 size_t outer_workspace_bytes(int64_t T, int64_t n, int64_t d);

@@ -333,14 +333,15 @@ __device__ __forceinline__ f32x4 global_quad(const void* row, int q, int V) {
 // flight at a time.  Each wave takes whole draws (wave w: draws w, w + 4, ...)
 // and reads its window's logits from global memory, four quads per lane at once;
 // its own DPP reduction gives S, so the draw loop has no barrier.  It writes r
-// and the window offset of every (draw, token).  A 1024-lane workgroup per token
+// and the window offset of every (draw, token) as one pair, token-major, so the
+// accumulation pass reads a token's pairs as one contiguous run (and r into the
+// caller's [K, T] rewards when asked for).  A 1024-lane workgroup per token
 // with the row staged in LDS (100 KB at the 243M shape: one token per CU) took
 // 0.79 ms per launch there.
 constexpr int RB = 8;   // quads per lane and batch of the statistics' loads
 
 template <int LT, int DEG>
-__global__ void __launch_bounds__(RNT) head_subset_rewards_kernel(HeadArgs A, int mq, float* __restrict__ rew,
-                                                                   int* __restrict__ woff) {
+__global__ void __launch_bounds__(RNT) head_subset_rewards_kernel(HeadArgs A, int mq, float2* __restrict__ ro) {
     __shared__ float4 DR[SKC];
     __shared__ float sh[RNT / 64];
     const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -421,16 +422,16 @@ __global__ void __launch_bounds__(RNT) head_subset_rewards_kernel(HeadArgs A, in
             const float S = wave_total((sl[0] + sl[1]) + (sl[2] + sl[3])) + dr.y;
             const float r = A.sigma * dr.z - log1p_uniform(S * A.smul);
             if (lane == 0) {
-                rew[(size_t)(i0 + ii) * A.T + t] = r;
-                woff[(size_t)(i0 + ii) * A.T + t] = o;
+                ro[(size_t)t * A.K + i0 + ii] = make_float2(r, __int_as_float(o));
+                if (A.rewards) A.rewards[(size_t)(i0 + ii) * A.T + t] = r;
             }
         }
     }
 }
 
 __global__ void __launch_bounds__(BNT) head_subset_accum_kernel(HeadArgs A, int mq, float winv, int nseg,
-                                                                const float* __restrict__ rew,
-                                                                const int* __restrict__ woff) {
+                                                                const float2* __restrict__ ro) {
+    __shared__ float2 dro[SKC];   // (r, window offset) of a chunk of draws
     const int t = blockIdx.x / nseg, sg = blockIdx.x % nseg, tid = threadIdx.x;
     const int V = A.V, nq = (V + 3) >> 2;
     const int qbase = sg * BNT * BQS + tid;
@@ -453,11 +454,19 @@ __global__ void __launch_bounds__(BNT) head_subset_accum_kernel(HeadArgs A, int 
     };
     static_assert(BNT == 256, "block_bits divides by BNT with a shift");
     const uint32_t lbits = block_bits(qy, qy + 1);   // the label's block, in every draw
-    for (int i = 0; i < A.K; ++i) {
-        const int o = woff[(size_t)i * A.T + t];  // wave-uniform
-        const float r = rew[(size_t)i * A.T + t];
+    // the token's (r, o) pairs staged in LDS by chunk: one coalesced read, where a
+    // scalar load per draw left each wave waiting on a chain of load latencies
+    for (int i0 = 0; i0 < A.K; i0 += SKC) {
+      const int kc = min(SKC, A.K - i0);
+      __syncthreads();  // the previous chunk fully read
+      for (int i = tid; i < kc; i += BNT) dro[i] = ro[(size_t)t * A.K + i0 + i];
+      __syncthreads();
+      for (int i = 0; i < kc; ++i) {
+        const float2 pr = dro[i];  // one address for the whole wave
+        const int o = __builtin_amdgcn_readfirstlane(__float_as_int(pr.y));
+        const float r = pr.x;
         const float rw = r * winv;
-        const uint32_t draw = A.draw0 + (uint32_t)i;
+        const uint32_t draw = A.draw0 + (uint32_t)(i0 + i);
         // the window as [o, e1) and, when it wraps, [0, e2)
         const int e1 = min(o + mq, nq), e2 = o + mq - nq;
         // the blocks that the window or the label meet, as one mask built once per
@@ -477,6 +486,7 @@ __global__ void __launch_bounds__(BNT) head_subset_accum_kernel(HeadArgs A, int 
                 }
             }
         }
+      }
     }
     float* out = A.ghat ? A.ghat + (size_t)t * V : nullptr;
     uint16_t* ohi = A.ghi ? A.ghi + (size_t)t * A.ldp : nullptr;
@@ -515,20 +525,19 @@ int head_subset_qw(int64_t m, int64_t V) {
     return 0;
 }
 
-hipError_t launch_head_subset(const HeadPlan& plan, int logits_dtype, const HeadArgs& A, int64_t m, float* rew_ws,
-                              int* off_ws, hipStream_t stream) {
+hipError_t launch_head_subset(const HeadPlan& plan, int logits_dtype, const HeadArgs& A, int64_t m, float2* ro_ws,
+                              hipStream_t stream) {
     const int64_t nq = (A.V + 3) / 4, mq = m / 4 < nq ? m / 4 : nq;
     // the subset kernels come in degrees 4 and 6: degree 3 runs as 4 (a smaller
     // truncation, same coefficients)
     const int pdeg = plan.deg == 3 ? 4 : plan.deg;
     if (A.V > kSubsetLdsMaxV) {  // two passes
         const float winv = (float)((double)nq / (double)mq);
-        float* rew = A.rewards ? A.rewards : rew_ws;
         hipError_t e = hipErrorInvalidConfiguration;
 #define DUST_WIDE_CASE(LT_, DEG_)                                                                      \
         if (logits_dtype == LT_ && pdeg == DEG_) {                                                \
             hipLaunchKernelGGL((head_subset_rewards_kernel<LT_, DEG_>), dim3(A.T), dim3(RNT), 0, stream, A, \
-                               (int)mq, rew, off_ws);                                                  \
+                               (int)mq, ro_ws);                                                        \
             e = hipGetLastError();                                                                     \
         }
         DUST_WIDE_CASE(0, 4) DUST_WIDE_CASE(0, 6) DUST_WIDE_CASE(0, 0)
@@ -538,7 +547,7 @@ hipError_t launch_head_subset(const HeadPlan& plan, int logits_dtype, const Head
         const int64_t nqo = A.ghi ? std::max<int64_t>(nq, (A.ldp + 3) / 4) : nq;
         const int nseg = (int)((nqo + BNT * BQS - 1) / (BNT * BQS));
         hipLaunchKernelGGL(head_subset_accum_kernel, dim3((unsigned)(A.T * nseg)), dim3(BNT), 0, stream, A, (int)mq,
-                           winv, nseg, rew, off_ws);
+                           winv, nseg, ro_ws);
         return hipGetLastError();
     }
     const int qw = head_subset_qw(m, A.V);
