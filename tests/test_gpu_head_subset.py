@@ -2,7 +2,8 @@
 
 Small cases element by element (fp32 and bf16 logits, ragged V, a one-quad window,
 windows spanning several quads per lane, the degree-6 polynomial, the widest row of
-the one-pass kernel), rows wider than LDS (the rewards + accumulation passes), a
+the one-pass kernel, more draws than one chunk), rows wider than LDS (the rewards +
+accumulation passes, also over two chunks of draws), a
 window covering the vocabulary (bitwise the full estimator), the full-size
 4096 x 8192 shape with m = 1024 and the 243M-shape head with m = 4096 on sampled
 tokens, and determinism.
@@ -39,12 +40,14 @@ SMALL = [
     (5, 16384, 8, 3, 8192, 1e-2, "f32"),    # largest V, 8 quads per lane
     (6, 9000, 8, 4, 16000, 1e-2, "bf16"),   # 4000 >= 2250 quads: the window covers, full estimator path
     (8, 300, 8, 9, 120, 0.1, "f32"),        # library expm1 (large sigma)
+    (2, 4097, 8, 600, 256, 1e-2, "bf16"),   # more draws than one chunk of per-draw terms (512)
     # rows wider than the one-pass kernel's LDS: rewards pass + accumulation pass
     (5, 20000, 8, 7, 2048, 1e-2, "f32"),
     (4, 50304, 8, 5, 4096, 5e-3, "bf16"),   # the 243M-shape vocabulary
     (3, 40001, 8, 3, 4, 1e-2, "bf16"),      # ragged, one-quad window
     (6, 30000, 8, 9, 1000, 0.1, "f32"),     # library expm1, window not a multiple of 64 quads
     (5, 65536, 8, 4, 60000, 5e-3, "bf16"),  # widest bf16 row, window almost everything
+    (2, 20000, 8, 600, 1024, 1e-2, "bf16"), # two chunks of draws in both passes
 ]
 
 
