@@ -302,7 +302,7 @@ __global__ void __launch_bounds__(GL * H) head_subset_kernel(HeadArgs A, int mq,
 // generated twice, once per pass.
 constexpr int RNT = 256;   // rewards pass: lanes per workgroup
 constexpr int BNT = 256;   // accumulation pass: lanes per workgroup
-constexpr int BQS = 8;     // accumulation pass: quads per lane (segments of BNT * BQS quads)
+constexpr int BQS = 8;    // accumulation pass: quads per lane (segments of BNT * BQS quads)
 
 // Quad q of a row as fp32, -inf past V (the spare quad q = nq included).
 template <int LT>
@@ -453,7 +453,15 @@ __global__ void __launch_bounds__(BNT) head_subset_accum_kernel(HeadArgs A, int 
         return khi > klo ? ((1u << khi) - 1u) & ~((1u << klo) - 1u) : 0u;
     };
     static_assert(BNT == 256, "block_bits divides by BNT with a shift");
-    const uint32_t lbits = block_bits(qy, qy + 1);   // the label's block, in every draw
+    // the label channel carries weight r in every draw: its running sum is kept
+    // apart (accy, on the lane that owns it) and replaces that channel's window
+    // sum at the end; per-block label tests in the draw loop had kept one scalar
+    // mask per block live across it (scalar registers spilled)
+    const int dy = qy - wq0;
+    const bool lwave = dy >= 0 && dy < BQS * BNT && (dy & (BNT - 1)) < 64;   // wave-uniform
+    const int ky = dy >> 8;
+    const bool lowner = lwave && (threadIdx.x & 63) == (dy & 63);
+    float accy = 0.f;
     // the token's (r, o) pairs staged in LDS by chunk: one coalesced read, where a
     // scalar load per draw left each wave waiting on a chain of load latencies
     for (int i0 = 0; i0 < A.K; i0 += SKC) {
@@ -471,32 +479,40 @@ __global__ void __launch_bounds__(BNT) head_subset_accum_kernel(HeadArgs A, int 
         const int e1 = min(o + mq, nq), e2 = o + mq - nq;
         // the blocks that the window or the label meet, as one mask built once per
         // draw: a few scalar instructions, where a test per block cost a dozen
-        const uint32_t hits = block_bits(o, e1) | (e2 > 0 ? block_bits(0, e2) : 0u) | lbits;
+        const uint32_t hits = block_bits(o, e1) | (e2 > 0 ? block_bits(0, e2) : 0u);
+        if (lwave) {  // the label's noise, the same counter as its block's
+            const f32x4 gy = gauss4_unscaled_uniform(tok, (uint32_t)qy, draw, A.layer, A.k0, A.k1);
+            const float ay = cy == 0 ? gy.v[0] : cy == 1 ? gy.v[1] : cy == 2 ? gy.v[2] : gy.v[3];
+            accy = fmaf(r, ay, accy);
+        }
 #pragma unroll
         for (int k = 0; k < BQS; ++k) {
             if ((hits >> k) & 1u) {  // blocks the window misses cost no vector work
                 const int q = qbase + k * BNT;
                 const bool in = q < nq && ((q >= o && q < e1) || q < e2);
-                const bool lab = q == qy;
                 const f32x4 g = gauss4_unscaled_uniform(tok, (uint32_t)q, draw, A.layer, A.k0, A.k1);
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const float w = (lab && c == cy) ? r : (in ? rw : 0.f);  // label weight 1, window nq/mq
-                    acc[k][c] = fmaf(w, g.v[c], acc[k][c]);
-                }
+                for (int c = 0; c < 4; ++c) acc[k][c] = fmaf(in ? rw : 0.f, g.v[c], acc[k][c]);   // window: nq/mq
             }
         }
       }
     }
-    float* out = A.ghat ? A.ghat + (size_t)t * V : nullptr;
-    uint16_t* ohi = A.ghi ? A.ghi + (size_t)t * A.ldp : nullptr;
-    uint16_t* olo = A.ghi ? A.glo + (size_t)t * A.ldp : nullptr;
+    // the output rows formed here, opaque to the compiler: addresses derived from
+    // them are not hoisted into scalar registers that would live across the draws
+    uint64_t ob = (uint64_t)(uintptr_t)A.ghat, hb = (uint64_t)(uintptr_t)A.ghi, lb = (uint64_t)(uintptr_t)A.glo;
+    asm volatile("" : "+s"(ob), "+s"(hb), "+s"(lb));
+    float* out = ob ? reinterpret_cast<float*>(ob) + (size_t)t * V : nullptr;
+    uint16_t* ohi = hb ? reinterpret_cast<uint16_t*>(hb) + (size_t)t * A.ldp : nullptr;
+    uint16_t* olo = hb ? reinterpret_cast<uint16_t*>(lb) + (size_t)t * A.ldp : nullptr;
 #pragma unroll
     for (int k = 0; k < BQS; ++k) {
         const int q = qbase + k * BNT;
         float v[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) v[c] = 4 * q + c < V ? acc[k][c] * A.gscale : 0.f;
+        for (int c = 0; c < 4; ++c) {
+            const float a = (lowner && k == ky && c == cy) ? accy : acc[k][c];   // the label: weight 1
+            v[c] = 4 * q + c < V ? a * A.gscale : 0.f;
+        }
         if (ohi && 4 * (int64_t)q < A.ldp) {
             uint2 h, l;
             h.x = pack_bf16_pair(v[0], v[1]);
