@@ -239,6 +239,29 @@ def trace_summary(args):
             print(f"- `{nm[:110]}`: {shape}")
 
 
+def counter_summary(dirs):
+    """Markdown table of rocprofv3 --pmc runs: per library kernel, each counter summed
+    over the rows of a dispatch (the per-XCD and per-SE instances), averaged over the
+    kernel's dispatches."""
+    per = {}
+    for d in dirs:
+        for (disp, name), ctrs in _counter_sums(d).items():
+            if "dust" not in name:
+                continue
+            nm = name.split("(")[0]
+            for c, v in ctrs.items():
+                per.setdefault(nm, {}).setdefault(c, []).append(v)
+    for nm, ctrs in per.items():
+        print(f"### `{nm}`")
+        print()
+        print("| counter | per dispatch | dispatches |")
+        print("|---|---:|---:|")
+        for c in sorted(ctrs):
+            v = ctrs[c]
+            print(f"| {c} | {sum(v) / len(v):.4g} | {len(v)} |")
+        print()
+
+
 WORKLOAD_NAMES = {
     1: "LM-head estimator fp32 logits: T=256, d=64, V=512, K=64, sigma=1e-2, uniform labels",
     2: "LM-head estimator fp32 logits: T=4096 (2x2048), d=512, V=8192, K=256, sigma=1e-2, Zipf(1.1) labels",
@@ -276,6 +299,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB (to scale HBM traffic counters) and exit")
+    ap.add_argument("--counter-summary", metavar="DIR", nargs="+",
+                    help="print each library kernel's rocprofv3 --pmc counters (csv output under the DIRs), "
+                         "summed over a dispatch and averaged over dispatches, as markdown, and exit")
     ap.add_argument("--trace-summary", metavar="DIR",
                     help="print a markdown summary of the rocprofv3 --kernel-trace --stats csv output under DIR "
                          "and exit")
@@ -808,6 +834,9 @@ def main():
         return
     if args.trace_summary:
         trace_summary(args)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
         return
     import torch
     if args.copy_calibration:
