@@ -857,7 +857,9 @@ __global__ void __launch_bounds__(G2_NT, 1) mlp_gemm2_kernel(MlpArgs A, int64_t 
     __shared__ __align__(16) uint16_t Bs0[G2_TR * G2_KS], Bs1[G2_TR * G2_KS], Bs2[G2_TR * G2_KS], Bs3[G2_TR * G2_KS];
     __shared__ float2 red[2][G2_TR];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    // the wave index as a scalar: the LDS destinations of the loads into LDS (M0)
+    // then come from scalar arithmetic, not from a read of the first lane per load
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wv = w & 1, wr = w >> 1;
     // XCD-aware order (workgroup b runs on XCD b % 8).  With a vocabulary tile
     // count that is a multiple of 4, the vocabulary is split into 4 groups; XCDs
