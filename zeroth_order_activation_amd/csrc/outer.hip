@@ -298,7 +298,8 @@ __global__ void __launch_bounds__(YNT, 1) outer_x3_kernel(const uint16_t* __rest
     // the ring stages as separate LDS objects ([plane][token][column], 32 KB each):
     // reads of one provably do not alias loads in flight into another
     __shared__ __align__(16) uint16_t S0[4 * PL2], S1[4 * PL2], S2[4 * PL2], S3[4 * PL2];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    // the wave index as a scalar: the loads into LDS take M0 from scalar arithmetic
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = w & 1, wn = w >> 1;
     // XCD-aware tile order: workgroups are dealt round-robin to the 8 XCDs, so
     // block b runs on XCD b % 8.  All N-tiles of one M-tile go to the same XCD
