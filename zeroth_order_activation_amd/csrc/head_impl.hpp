@@ -730,8 +730,10 @@ hipError_t dispatch_head(const HeadPlan& P, const HeadArgs& A, hipStream_t s) {
     DUST_HEAD_CASE(256, 8, 0, 0)
     DUST_HEAD_CASE(1024, 4, 1, 0)
     DUST_HEAD_CASE(1024, 8, 1, 0)
-    DUST_HEAD_CASE(1024, 13, 1, 3)
-    DUST_HEAD_CASE(1024, 16, 1, 0)
+    if constexpr (LT == 1) {  // rows past 32768 channels: bf16 only (an fp32 row would not fit in LDS)
+        DUST_HEAD_CASE(1024, 13, 1, 3)
+        DUST_HEAD_CASE(1024, 16, 1, 0)
+    }
 #undef DUST_HEAD_CASE
     return hipErrorInvalidConfiguration;
 }
